@@ -1,0 +1,186 @@
+"""Throughput of one tensor-parallel rank's transformer-layer training step on one MI355X.
+
+A step is the rank's whole share of the layer's forward and backward pass:
+column-parallel QKV projection, causal attention over its heads, row-parallel
+output projection, the reduce share standing in for the all-reduce, column-parallel
+fc1 with GeLU, row-parallel fc2, reduce share; then the backward of all of it
+(dgrad and wgrad of every linear, bias gradients, attention backward) with its
+two reduce shares.  The reduce shares are the rank's reduce-scatter rows
+[rank*S/t, (rank+1)*S/t) over its own partial and t-1 resident peer partials.
+
+Prints one JSON line.  Default workload: rank 0 of a 7B-class layer at TP=4
+(hidden 4096, 32 heads, ffn 16384, seq 4096, micro-batch 1, bf16).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+PEAK_BF16_TFLOPS = 2516.6  # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="7b-tp4")
+    ap.add_argument("--rank", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample-seq", type=int, default=2048)
+    return ap.parse_args()
+
+
+def cpu_baseline(shape, rank, sample_seq):
+    """The oracle (fp64 numpy, as it stands) on a bounded sample: the same rank's
+    forward + backward over the first sample_seq tokens."""
+    import synth
+    from oracle import layer as L
+    from oracle import shard as S
+
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        cores = len(os.sched_getaffinity(0))
+    sub = synth.LayerShape(hidden=shape.hidden, heads=shape.heads, ffn=shape.ffn, seq=sample_seq,
+                           micro_batch=1, tp=shape.tp)
+    inp = synth.layer_inputs(sub, tp=shape.tp, rank=rank)
+    f = {k: synth.bf16_bits_to_f64(v) for k, v in inp.items()}
+    hh = synth.bf16_bits_to_f64(synth.layer_tensor(sub, "h"))
+    dh = synth.bf16_bits_to_f64(synth.layer_tensor(sub, "dh"))
+    lh = shape.heads // shape.tp
+    t0 = time.perf_counter()
+    att = S.rank_attn_forward(f, f["x"], lh)
+    mlp = S.rank_mlp_forward(f, hh)
+    S.rank_mlp_backward(f, f["dy"], hh, mlp["z"], mlp["a"])
+    S.rank_attn_backward(f, dh, f["x"], att["qkv"], lh)
+    dt = time.perf_counter() - t0
+    flops = L.layer_flops(shape.hidden, shape.heads, shape.ffn, sample_seq, 1, shape.tp)["total"]
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"rank {rank} shard forward+backward on the first {sample_seq} of {shape.seq} tokens "
+                      f"(fp64 numpy), {dt:.2f} s"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (collectives are replaced by an "
+              "on-device reduce); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import synth
+    from megatron_tensor_transformer_layer_amd import mtl_reduce
+    from megatron_tensor_transformer_layer_amd.layer import RankState, bf16_dev, empty_bf16
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    shape = synth.WORKLOADS[args.workload]
+    t, r = shape.tp, args.rank
+    inp = synth.layer_inputs(shape, tp=t, rank=r)
+    st = RankState(shape, t, r, inp)
+    D = st.D
+    x = bf16_dev(inp["x"])
+    dy = bf16_dev(inp["dy"])
+    b_o = bf16_dev(inp["b_o"])
+    b2 = bf16_dev(inp["b2"])
+    g = torch.Generator(device="cuda").manual_seed(1234)
+    # partial sums the other t-1 ranks would contribute to this rank's reduce-scatter share
+    peers = {k: [torch.randn(D.S, D.h, device="cuda", generator=g).to(torch.bfloat16) for _ in range(t - 1)]
+             for k in ("attn", "mlp", "dh", "dx")}
+    h = empty_bf16(D.S, D.h)
+    y = empty_bf16(D.S, D.h)
+    dh = empty_bf16(D.S, D.h)
+    dx = empty_bf16(D.S, D.h)
+    r0, r1 = r * D.S // t, (r + 1) * D.S // t
+
+    # rows of H / dH outside this rank's share come from the all-gather; fill them once
+    st.attn_fwd(x)
+    mtl_reduce([st.p_attn] + peers["attn"], b_o, None, h, D.S, D.h)
+    st.mlp_fwd(h)
+    st.mlp_bwd(dy, h)
+    mtl_reduce([st.p_dh] + peers["dh"], None, None, dh, D.S, D.h)
+    torch.cuda.synchronize()
+
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+    mlp_ev = []
+
+    def step(record=False):
+        st.attn_fwd(x)
+        mtl_reduce([st.p_attn] + peers["attn"], b_o, None, h, D.S, D.h, r0, r1)
+        if record:
+            e0, e1 = ev(), ev()
+            e0.record()
+        st.mlp_fwd(h)
+        if record:
+            e1.record()
+            mlp_ev.append((e0, e1))
+        mtl_reduce([st.p_mlp] + peers["mlp"], b2, None, y, D.S, D.h, r0, r1)
+        st.mlp_bwd(dy, h)
+        mtl_reduce([st.p_dh] + peers["dh"], None, None, dh, D.S, D.h, r0, r1)
+        st.attn_bwd(dh, x)
+        mtl_reduce([st.p_dx] + peers["dx"], None, None, dx, D.S, D.h, r0, r1)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    step_ev = [(ev(), ev()) for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step_ev[i][0].record()
+        step(record=True)
+        step_ev[i][1].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    from oracle.layer import layer_flops  # FLOP count only (closed form)
+    fl = layer_flops(shape.hidden, shape.heads, shape.ffn, shape.seq, shape.micro_batch, t)
+    ms = wall / args.steps * 1e3
+    per_step = np.array([a.elapsed_time(b) for a, b in step_ev])
+    mlp_ms = np.array([a.elapsed_time(b) for a, b in mlp_ev])
+    # dominant kernel: the bf16 MFMA GEMM; mtl_mlp_fwd is exactly two GEMM launches of
+    # shape S x f/t x h and S x h x f/t (2*S*h*f/t FLOP each)
+    gemm_flop = 2.0 * D.S * D.h * D.f_l
+    gemm_launch_s = float(np.mean(mlp_ms)) / 2 / 1e3
+    achieved = gemm_flop / gemm_launch_s / 1e12
+    out = {
+        "metric": "TFLOP/s per TP-shard layer fwd+bwd (bf16) and % of MI355X MFMA peak",
+        "value": round(fl["total"] / (ms / 1e3) / 1e12, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) activations, N(0,0.02) weights)",
+        "config": {"workload": f"{args.workload}: rank {r} of TP={t}, hidden {shape.hidden}, heads {shape.heads} "
+                               f"({shape.heads // t} local), ffn {shape.ffn} ({shape.ffn // t} local), "
+                               f"seq {shape.seq}, micro-batch {shape.micro_batch}",
+                   "global_batch": shape.micro_batch, "seq_len": shape.seq, "parallelism": f"tp{t}-rank{r}-of-1gpu"},
+        "pct_of_peak": round(100 * fl["total"] / (ms / 1e3) / 1e12 / PEAK_BF16_TFLOPS, 2),
+        "step_ms_p50": round(float(np.percentile(per_step, 50)), 4),
+        "step_ms_p95": round(float(np.percentile(per_step, 95)), 4),
+        "flop_per_step": fl["total"],
+        "roofline": {"bound": "mfma", "kernel": "gemm_bf16_kernel (fc1/fc2 forward, 256x256 tiles)",
+                     "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(shape, r, min(args.cpu_sample_seq, shape.seq))
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,139 @@
+"""Python binding of libmtl.so -- argument marshalling only.
+
+Every function here has the name of the C entry point it calls (include/mtl.h
+documents each one).  Tensor arguments may be torch tensors (their
+``data_ptr()`` is passed) or integer device addresses; ``stream`` defaults to
+torch's current stream on the current device.  A non-OK status raises
+``MtlError``.  Every step of the computation runs in the library's HIP kernels;
+there is no fallback path: if libmtl.so is missing, loading fails loudly.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libmtl.so")
+HEADER = os.path.join(os.path.dirname(HERE), "include", "mtl.h")
+
+MTL_OK, MTL_E_NULL, MTL_E_DIVISIBILITY, MTL_E_RANK, MTL_E_SHAPE = 0, 1, 2, 3, 4
+MTL_E_ALIGN, MTL_E_WORKSPACE, MTL_E_UNSUPPORTED, MTL_E_HIP = 5, 6, 7, 8
+MTL_PREC_BF16, MTL_PREC_FP8_HYBRID = 0, 1
+MTL_F_RESIDUAL, MTL_F_WGRAD_ACCUM = 1, 2
+
+
+class MtlError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: status {status} ({status_text(status)})")
+
+
+class LayerCfg(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in
+                ("hidden", "heads", "ffn", "seq", "micro_batch", "tp", "rank", "precision", "flags")]
+
+
+_P = ctypes.c_void_p
+_I32, _I64, _SZ = ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+_CFG = ctypes.POINTER(LayerCfg)
+_SIGS = {
+    "mtl_status_str": (ctypes.c_char_p, [ctypes.c_int]),
+    "mtl_validate": (ctypes.c_int, [_CFG]),
+    "mtl_workspace_bytes": (ctypes.c_int, [_CFG, ctypes.POINTER(_SZ)]),
+    "mtl_attn_fwd": (ctypes.c_int, [_CFG, _P, _P, _P, _P, _P, _P, _P, _P, _P]),
+    "mtl_reduce": (ctypes.c_int, [_I32, ctypes.POINTER(_P), _P, _P, _P, _I64, _I64, _I64, _I64, _P]),
+    "mtl_mlp_fwd": (ctypes.c_int, [_CFG, _P, _P, _P, _P, _P, _P, _P, _P]),
+    "mtl_mlp_bwd": (ctypes.c_int, [_CFG, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
+    "mtl_attn_bwd": (ctypes.c_int, [_CFG, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
+}
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libmtl.so (built in-tree by ``megatron_tensor_transformer_layer_amd.build``)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is not built; run python -m megatron_tensor_transformer_layer_amd.build")
+        l = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGS.items():
+            f = getattr(l, name)
+            f.restype = res
+            f.argtypes = args
+        _lib = l
+    return _lib
+
+
+def status_text(status: int) -> str:
+    try:
+        return lib().mtl_status_str(status).decode()
+    except Exception:  # pragma: no cover - library missing
+        return "?"
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _stream(stream):
+    if stream is not None:
+        return stream if isinstance(stream, int) else stream.cuda_stream
+    import torch
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _check(status: int, where: str):
+    if status != MTL_OK:
+        raise MtlError(status, where)
+
+
+def make_cfg(hidden, heads, ffn, seq, micro_batch=1, tp=1, rank=0, precision=MTL_PREC_BF16, flags=0) -> LayerCfg:
+    return LayerCfg(hidden, heads, ffn, seq, micro_batch, tp, rank, precision, flags)
+
+
+def mtl_validate(cfg: LayerCfg) -> int:
+    """Returns the status code (does not raise)."""
+    return lib().mtl_validate(ctypes.byref(cfg))
+
+
+def mtl_workspace_bytes(cfg: LayerCfg) -> int:
+    n = _SZ(0)
+    _check(lib().mtl_workspace_bytes(ctypes.byref(cfg), ctypes.byref(n)), "mtl_workspace_bytes")
+    return n.value
+
+
+def mtl_attn_fwd(cfg, x, w_qkv, b_qkv, w_o, qkv, o, lse, partial, stream=None):
+    _check(lib().mtl_attn_fwd(ctypes.byref(cfg), _ptr(x), _ptr(w_qkv), _ptr(b_qkv), _ptr(w_o), _ptr(qkv), _ptr(o),
+                              _ptr(lse), _ptr(partial), _stream(stream)), "mtl_attn_fwd")
+
+
+def mtl_reduce(partials, bias, residual, out, rows, cols, row_begin=0, row_end=None, stream=None):
+    t = len(partials)
+    arr = (_P * t)(*[_ptr(p) for p in partials])
+    _check(lib().mtl_reduce(t, arr, _ptr(bias), _ptr(residual), _ptr(out), rows, cols, row_begin,
+                            rows if row_end is None else row_end, _stream(stream)), "mtl_reduce")
+
+
+def mtl_mlp_fwd(cfg, h, w1, b1, w2, z, a, partial, stream=None):
+    _check(lib().mtl_mlp_fwd(ctypes.byref(cfg), _ptr(h), _ptr(w1), _ptr(b1), _ptr(w2), _ptr(z), _ptr(a),
+                             _ptr(partial), _stream(stream)), "mtl_mlp_fwd")
+
+
+def mtl_mlp_bwd(cfg, dy, h, z, a, w1, w2, dh_partial, dw1, db1, dw2, db2, scratch, scratch_bytes=None, stream=None):
+    nbytes = scratch.numel() * scratch.element_size() if scratch_bytes is None else scratch_bytes
+    _check(lib().mtl_mlp_bwd(ctypes.byref(cfg), _ptr(dy), _ptr(h), _ptr(z), _ptr(a), _ptr(w1), _ptr(w2),
+                             _ptr(dh_partial), _ptr(dw1), _ptr(db1), _ptr(dw2), _ptr(db2), _ptr(scratch), nbytes,
+                             _stream(stream)), "mtl_mlp_bwd")
+
+
+def mtl_attn_bwd(cfg, dh, x, qkv, o, lse, w_qkv, w_o, dx_partial, dw_qkv, db_qkv, dw_o, db_o, scratch,
+                 scratch_bytes=None, stream=None):
+    nbytes = scratch.numel() * scratch.element_size() if scratch_bytes is None else scratch_bytes
+    _check(lib().mtl_attn_bwd(ctypes.byref(cfg), _ptr(dh), _ptr(x), _ptr(qkv), _ptr(o), _ptr(lse), _ptr(w_qkv),
+                              _ptr(w_o), _ptr(dx_partial), _ptr(dw_qkv), _ptr(db_qkv), _ptr(dw_o), _ptr(db_o),
+                              _ptr(scratch), nbytes, _stream(stream)), "mtl_attn_bwd")

@@ -1,0 +1,76 @@
+// Device-side building blocks shared by the gfx950 kernels: vector types,
+// bf16 packing, the MFMA wrappers, LDS tile swizzle and the 8x8 register
+// transpose used to turn mn-contiguous global tiles into k-contiguous LDS tiles.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mtl {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// ---------------------------------------------------------------- bf16 <-> fp32
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) { return __uint_as_float(((uint32_t)h) << 16); }
+
+// fp32 -> bf16 bits, round to nearest even (NaN kept quiet).
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
+}
+
+// ---------------------------------------------------------------- MFMA
+// v_mfma_f32_32x32x16_bf16: D[32x32] += A[32x16] * B[16x32].
+// Operand a: lane l supplies row (l % 32) with 8 k-values; operand b: lane l
+// supplies column (l % 32) with 8 k-values.  The k-slot -> k mapping only has to
+// agree between a and b.  Result: lane l, register r holds
+// D[8*(r/4) + 4*(l/32) + r%4][l % 32].
+__device__ __forceinline__ f32x16 mfma32(const u32x4& a, const u32x4& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c,
+                                                 0, 0, 0);
+}
+
+// ---------------------------------------------------------------- LDS tiles
+// A k-contiguous tile of R rows x 64 bf16 (128 B per row) is stored as eight
+// 16-byte chunks per row, chunk c of row r at physical chunk c ^ (r & 7): eight
+// consecutive rows reading the same logical chunk hit eight distinct bank groups.
+__device__ __forceinline__ uint32_t swz(uint32_t row, uint32_t chunk) {
+  return row * 128u + ((chunk ^ (row & 7u)) << 4);
+}
+
+// ---------------------------------------------------------------- 8x8 transpose
+// in[r] holds 8 bf16 of row r (element e in dword e/2, low half for even e).
+// out[i] receives column i: element r of out[i] = in[r] element i.
+__device__ __forceinline__ void transpose8x8(const u32x4 (&in)[8], u32x4 (&out)[8]) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const uint32_t sel = (i & 1) ? 0x07060302u : 0x05040100u;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      out[i][j] = __builtin_amdgcn_perm(in[2 * j + 1][i >> 1], in[2 * j][i >> 1], sel);
+    }
+  }
+}
+
+// ---------------------------------------------------------------- GeLU
+// Exact GeLU z * Phi(z) with Phi from the device erf (ROCm's OCML), and its
+// derivative Phi(z) + z * phi(z).
+__device__ __forceinline__ float gelu_f(float z) { return 0.5f * z * (1.0f + erff(z * 0.70710678118654752f)); }
+__device__ __forceinline__ float gelu_grad_f(float z) {
+  const float cdf = 0.5f * (1.0f + erff(z * 0.70710678118654752f));
+  const float pdf = 0.39894228040143268f * __expf(-0.5f * z * z);
+  return cdf + z * pdf;
+}
+
+}  // namespace mtl

@@ -1,0 +1,136 @@
+// HBM-streaming reductions for gfx950.
+//
+// reduce_partials: the on-device stand-in for the tensor-parallel all-reduce
+// that follows a row-parallel linear: out = sum_i partial_i (+ bias) (+ residual),
+// summed in fp32 in rank order, written bf16.  Every lane moves 16 bytes per
+// load; the grid is a multiple of the 256 CUs and strides over the row range.
+//
+// colsum_bf16: the bias gradients of the four linears are column sums of a
+// [rows, cols] bf16 gradient.  Deterministic two-stage sum: stage 1 gives each
+// wave 512 columns x 64 rows (16-byte loads, fp32 accumulate) and writes one
+// partial row to the workspace; stage 2 adds the partial rows in order.
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace mtl {
+
+constexpr int MAX_PARTIALS = 16;
+
+struct ReduceArgs {
+  const uint16_t* p[MAX_PARTIALS];
+  const uint16_t* bias;
+  const uint16_t* residual;
+  uint16_t* out;
+  int t;
+  int64_t cols;  // multiple of 8
+  int64_t begin, count;  // element range (row_begin*cols, rows*cols)
+};
+
+__global__ __launch_bounds__(256) void reduce_partials_kernel(ReduceArgs a) {
+  const int64_t nvec = a.count / 8;
+  for (int64_t v = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; v < nvec; v += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t e = a.begin + v * 8;
+    float s[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    for (int i = 0; i < a.t; ++i) {
+      const u32x4 x = *reinterpret_cast<const u32x4*>(a.p[i] + e);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        s[2 * j] += bf16_lo(x[j]);
+        s[2 * j + 1] += bf16_hi(x[j]);
+      }
+    }
+    if (a.bias) {
+      const u32x4 x = *reinterpret_cast<const u32x4*>(a.bias + (e % a.cols));
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        s[2 * j] += bf16_lo(x[j]);
+        s[2 * j + 1] += bf16_hi(x[j]);
+      }
+    }
+    if (a.residual) {
+      const u32x4 x = *reinterpret_cast<const u32x4*>(a.residual + e);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        s[2 * j] += bf16_lo(x[j]);
+        s[2 * j + 1] += bf16_hi(x[j]);
+      }
+    }
+    u32x4 o;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) o[j] = pack_bf16x2(s[2 * j], s[2 * j + 1]);
+    *reinterpret_cast<u32x4*>(a.out + e) = o;
+  }
+}
+
+hipError_t reduce_partials(int t, const uint16_t* const* partials, const uint16_t* bias, const uint16_t* residual,
+                           uint16_t* out, int64_t cols, int64_t row_begin, int64_t row_end, hipStream_t s) {
+  if (t < 1 || t > MAX_PARTIALS) return hipErrorInvalidValue;
+  ReduceArgs a{};
+  for (int i = 0; i < t; ++i) a.p[i] = partials[i];
+  a.bias = bias;
+  a.residual = residual;
+  a.out = out;
+  a.t = t;
+  a.cols = cols;
+  a.begin = row_begin * cols;
+  a.count = (row_end - row_begin) * cols;
+  if (a.count <= 0) return hipSuccess;
+  const int64_t nvec = a.count / 8;
+  int64_t blocks = (nvec + 255) / 256;
+  if (blocks > 2048) blocks = 2048;
+  hipLaunchKernelGGL(reduce_partials_kernel, dim3((unsigned)blocks), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+constexpr int CS_ROWS = 64;  // rows per stage-1 chunk
+constexpr int CS_COLS = 512; // columns per stage-1 wave
+
+size_t colsum_ws_floats(int64_t rows, int64_t cols) {
+  return (size_t)((rows + CS_ROWS - 1) / CS_ROWS) * (size_t)cols;
+}
+
+__global__ __launch_bounds__(64) void colsum_stage1(const uint16_t* __restrict__ x, int64_t rows, int64_t cols,
+                                                     int64_t ld, float* __restrict__ ws) {
+  const int64_t c = (int64_t)blockIdx.x * CS_COLS + threadIdx.x * 8;
+  const int64_t r0 = (int64_t)blockIdx.y * CS_ROWS;
+  if (c >= cols) return;
+  float s[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  const int64_t r1 = min(rows, r0 + CS_ROWS);
+  for (int64_t r = r0; r < r1; ++r) {
+    const u32x4 v = *reinterpret_cast<const u32x4*>(x + r * ld + c);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      s[2 * j] += bf16_lo(v[j]);
+      s[2 * j + 1] += bf16_hi(v[j]);
+    }
+  }
+  float* w = ws + (int64_t)blockIdx.y * cols + c;
+  *reinterpret_cast<f32x4*>(w) = f32x4{s[0], s[1], s[2], s[3]};
+  *reinterpret_cast<f32x4*>(w + 4) = f32x4{s[4], s[5], s[6], s[7]};
+}
+
+__global__ __launch_bounds__(256) void colsum_stage2(const float* __restrict__ ws, int64_t chunks, int64_t cols,
+                                                      float* __restrict__ out, int accumulate) {
+  const int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (c >= cols) return;
+  float s = 0.f;
+  for (int64_t k = 0; k < chunks; ++k) s += ws[k * cols + c];
+  out[c] = accumulate ? out[c] + s : s;
+}
+
+hipError_t colsum_bf16(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld, float* out, bool accumulate,
+                       float* ws, hipStream_t s) {
+  if (cols <= 0) return hipSuccess;
+  const int64_t chunks = (rows + CS_ROWS - 1) / CS_ROWS;
+  if (chunks > 0) {
+    dim3 g1((unsigned)((cols + CS_COLS - 1) / CS_COLS), (unsigned)chunks);
+    hipLaunchKernelGGL(colsum_stage1, g1, dim3(64), 0, s, x, rows, cols, ld, ws);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL(colsum_stage2, dim3((unsigned)((cols + 255) / 256)), dim3(256), 0, s, ws, chunks, cols, out,
+                     accumulate ? 1 : 0);
+  return hipGetLastError();
+}
+
+}  // namespace mtl

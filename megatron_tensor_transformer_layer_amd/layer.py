@@ -1,0 +1,140 @@
+"""Device buffers and the call sequence of a tensor-parallel layer step.
+
+Plumbing only: allocates torch device tensors, passes their addresses to the
+C entry points (see ``__init__``) in the order a training step needs them, and
+converts bf16 bit patterns to and from host arrays.  No arithmetic of the layer
+happens here.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+
+import numpy as np
+import torch
+
+from . import (MTL_PREC_BF16, make_cfg, mtl_attn_bwd, mtl_attn_fwd, mtl_mlp_bwd, mtl_mlp_fwd, mtl_reduce,
+               mtl_workspace_bytes)
+
+DEV = "cuda"
+
+
+def bf16_dev(bits: np.ndarray, device=DEV) -> torch.Tensor:
+    """bf16 bit patterns (uint16) -> bfloat16 device tensor (same bits)."""
+    t = torch.from_numpy(np.ascontiguousarray(bits).view(np.int16))
+    return t.to(device).view(torch.bfloat16)
+
+
+def host_f64(t: torch.Tensor) -> np.ndarray:
+    return t.detach().float().cpu().numpy().astype(np.float64)
+
+
+def empty_bf16(*shape, device=DEV):
+    return torch.empty(*shape, dtype=torch.bfloat16, device=device)
+
+
+def zeros_f32(*shape, device=DEV):
+    return torch.zeros(*shape, dtype=torch.float32, device=device)
+
+
+@dataclass
+class Dims:
+    S: int
+    h: int
+    heads_l: int
+    d: int
+    f_l: int
+
+    @property
+    def qkv_l(self):
+        return 3 * self.heads_l * self.d
+
+    @property
+    def o_l(self):
+        return self.heads_l * self.d
+
+
+def dims_of(hidden, heads, ffn, seq, micro_batch, tp) -> Dims:
+    return Dims(S=seq * micro_batch, h=hidden, heads_l=heads // tp, d=hidden // heads, f_l=ffn // tp)
+
+
+class RankState:
+    """All device buffers of one TP rank: shard weights, saved activations,
+    partial outputs, gradients and scratch."""
+
+    def __init__(self, shape, tp: int, rank: int, shard: dict, flags: int = 0, device=DEV):
+        self.cfg = make_cfg(shape.hidden, shape.heads, shape.ffn, shape.seq, shape.micro_batch, tp, rank,
+                            MTL_PREC_BF16, flags)
+        D = self.D = dims_of(shape.hidden, shape.heads, shape.ffn, shape.seq, shape.micro_batch, tp)
+        self.w = {k: bf16_dev(shard[k], device) for k in ("w_qkv", "b_qkv", "w_o", "w1", "b1", "w2")}
+        self.qkv = empty_bf16(D.S, D.qkv_l, device=device)
+        self.o = empty_bf16(D.S, D.o_l, device=device)
+        self.lse = torch.empty(D.heads_l, D.S, dtype=torch.float32, device=device)
+        self.z = empty_bf16(D.S, D.f_l, device=device)
+        self.a = empty_bf16(D.S, D.f_l, device=device)
+        self.p_attn = empty_bf16(D.S, D.h, device=device)
+        self.p_mlp = empty_bf16(D.S, D.h, device=device)
+        self.p_dh = empty_bf16(D.S, D.h, device=device)
+        self.p_dx = empty_bf16(D.S, D.h, device=device)
+        self.dw_qkv = zeros_f32(D.h, D.qkv_l, device=device)
+        self.db_qkv = zeros_f32(D.qkv_l, device=device)
+        self.dw_o = zeros_f32(D.o_l, D.h, device=device)
+        self.db_o = zeros_f32(D.h, device=device)
+        self.dw1 = zeros_f32(D.h, D.f_l, device=device)
+        self.db1 = zeros_f32(D.f_l, device=device)
+        self.dw2 = zeros_f32(D.f_l, D.h, device=device)
+        self.db2 = zeros_f32(D.h, device=device)
+        self.scratch_bytes = mtl_workspace_bytes(self.cfg)
+        self.scratch = torch.empty(self.scratch_bytes, dtype=torch.uint8, device=device)
+
+    def attn_fwd(self, x):
+        mtl_attn_fwd(self.cfg, x, self.w["w_qkv"], self.w["b_qkv"], self.w["w_o"], self.qkv, self.o, self.lse,
+                     self.p_attn)
+
+    def mlp_fwd(self, h):
+        mtl_mlp_fwd(self.cfg, h, self.w["w1"], self.w["b1"], self.w["w2"], self.z, self.a, self.p_mlp)
+
+    def mlp_bwd(self, dy, h, want_db2=True):
+        mtl_mlp_bwd(self.cfg, dy, h, self.z, self.a, self.w["w1"], self.w["w2"], self.p_dh, self.dw1, self.db1,
+                    self.dw2, self.db2 if want_db2 else None, self.scratch)
+
+    def attn_bwd(self, dh, x, want_db_o=True):
+        mtl_attn_bwd(self.cfg, dh, x, self.qkv, self.o, self.lse, self.w["w_qkv"], self.w["w_o"], self.p_dx,
+                     self.dw_qkv, self.db_qkv, self.dw_o, self.db_o if want_db_o else None, self.scratch)
+
+
+def run_sharded_layer(shape, tp: int, shards: list, x_bits, b_o_bits, b2_bits, dy_bits, residual: bool = False,
+                      device=DEV) -> dict:
+    """Run the whole layer as tp rank shards plus the four full reductions on
+    one device; returns host fp64 copies of every output."""
+    ranks = [RankState(shape, tp, r, shards[r], device=device) for r in range(tp)]
+    D = ranks[0].D
+    x = bf16_dev(x_bits, device)
+    b_o = bf16_dev(b_o_bits, device)
+    b2 = bf16_dev(b2_bits, device)
+    dy = bf16_dev(dy_bits, device)
+    h = empty_bf16(D.S, D.h, device=device)
+    y = empty_bf16(D.S, D.h, device=device)
+    dh = empty_bf16(D.S, D.h, device=device)
+    dx = empty_bf16(D.S, D.h, device=device)
+    for r in ranks:
+        r.attn_fwd(x)
+    mtl_reduce([r.p_attn for r in ranks], b_o, x if residual else None, h, D.S, D.h)
+    for r in ranks:
+        r.mlp_fwd(h)
+    mtl_reduce([r.p_mlp for r in ranks], b2, h if residual else None, y, D.S, D.h)
+    for r in ranks:
+        r.mlp_bwd(dy, h)
+    mtl_reduce([r.p_dh for r in ranks], None, dy if residual else None, dh, D.S, D.h)
+    for r in ranks:
+        r.attn_bwd(dh, x)
+    mtl_reduce([r.p_dx for r in ranks], None, dh if residual else None, dx, D.S, D.h)
+    torch.cuda.synchronize()
+    cat = lambda key, axis: np.concatenate([host_f64(getattr(r, key)) for r in ranks], axis=axis)
+    return dict(
+        y=host_f64(y), h=host_f64(h), dh=host_f64(dh), dx=host_f64(dx),
+        qkv=cat("qkv", 1), o=cat("o", 1), lse=cat("lse", 0), z=cat("z", 1), a=cat("a", 1),
+        dw_qkv=cat("dw_qkv", 1), db_qkv=cat("db_qkv", 0), dw_o=cat("dw_o", 0), dw1=cat("dw1", 1),
+        db1=cat("db1", 0), dw2=cat("dw2", 0),
+        db_o=host_f64(ranks[0].db_o), db2=host_f64(ranks[0].db2),
+        db_o_all=[host_f64(r.db_o) for r in ranks], db2_all=[host_f64(r.db2) for r in ranks],
+    )

@@ -26,3 +26,14 @@ def pytest_collection_modifyitems(config, items):
     for item in items:
         if "gpu" in item.keywords:
             item.add_marker(skip)
+
+
+@pytest.fixture(scope="session")
+def mtl():
+    """The binding, with libmtl.so loaded (built first if nothing is built)."""
+    import megatron_tensor_transformer_layer_amd as m
+    if not os.path.exists(m.LIB_PATH):
+        from megatron_tensor_transformer_layer_amd import build
+        build.build(verbose=False)
+    m.lib()
+    return m

@@ -1,0 +1,102 @@
+"""The C-ABI library on a host without a GPU: it loads, exports every entry
+point the header declares, and its host-side validation returns the documented
+status codes before any launch."""
+import ctypes
+import json
+import os
+import re
+
+import pytest
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _declared(header):
+    text = open(header).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(mtl_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol(mtl):
+    names = _declared(mtl.HEADER)
+    assert "mtl_attn_fwd" in names and "mtl_reduce" in names
+    lib = mtl.lib()
+    for n in names:
+        assert hasattr(lib, n), n
+    # every declared entry point has a Python binding of the same name
+    for n in names:
+        if n not in ("mtl_status_str",):
+            assert hasattr(mtl, n), n
+
+
+def test_validate_divisibility_cases_from_the_pages(mtl):
+    cases = json.load(open(os.path.join(GOLDEN, "divisibility.json")))
+    for c in cases["dense"]:
+        d = c["hidden"] // c["heads"] if c["hidden"] % c["heads"] == 0 else 0
+        cfg = mtl.make_cfg(c["hidden"], c["heads"], c["ffn"], 512, 1, c["tp"], 0)
+        st = mtl.mtl_validate(cfg)
+        if not c["ok"]:
+            assert st == mtl.MTL_E_DIVISIBILITY, c
+        elif d in (64, 128):
+            assert st == mtl.MTL_OK, c
+        else:  # legal split, head size outside what the kernels are built for
+            assert st == mtl.MTL_E_SHAPE, c
+
+
+def test_validate_codes(mtl):
+    ok = dict(hidden=4096, heads=32, ffn=16384, seq=4096, micro_batch=1, tp=4, rank=0)
+    assert mtl.mtl_validate(mtl.make_cfg(**ok)) == mtl.MTL_OK
+    bad = [
+        (dict(rank=4), mtl.MTL_E_RANK), (dict(rank=-1), mtl.MTL_E_RANK),
+        (dict(ffn=16382), mtl.MTL_E_DIVISIBILITY), (dict(heads=30), mtl.MTL_E_DIVISIBILITY),
+        (dict(seq=0), mtl.MTL_E_SHAPE), (dict(hidden=0), mtl.MTL_E_SHAPE),
+        (dict(hidden=3072, heads=32), mtl.MTL_E_SHAPE),  # d = 96
+        (dict(ffn=4 * 1028), mtl.MTL_E_SHAPE),  # ffn/tp = 1028, not a multiple of 8
+    ]
+    for change, want in bad:
+        assert mtl.mtl_validate(mtl.make_cfg(**{**ok, **change})) == want, change
+    c = mtl.make_cfg(**ok)
+    c.precision = 7
+    assert mtl.mtl_validate(c) == mtl.MTL_E_UNSUPPORTED
+    c = mtl.make_cfg(**ok)
+    c.flags = 64
+    assert mtl.mtl_validate(c) == mtl.MTL_E_UNSUPPORTED
+    assert mtl.lib().mtl_validate(None) == mtl.MTL_E_NULL
+
+
+def test_workspace_bytes(mtl):
+    cfg = mtl.make_cfg(4096, 32, 16384, 4096, 1, 4, 0)
+    n = mtl.mtl_workspace_bytes(cfg)
+    S, f_l, qkv_l = 4096, 4096, 3072
+    assert n >= S * f_l * 2 and n >= S * qkv_l * 2
+    assert n < 1 << 30
+    with pytest.raises(mtl.MtlError) as e:
+        mtl.mtl_workspace_bytes(mtl.make_cfg(4096, 32, 16384, 4096, 1, 4, 9))
+    assert e.value.status == mtl.MTL_E_RANK
+
+
+def test_errors_before_launch(mtl):
+    """NULL, misaligned and too-small-scratch arguments are refused on the host:
+    nothing touches the (fake, never dereferenced) addresses."""
+    cfg = mtl.make_cfg(256, 2, 512, 64, 1, 2, 0)
+    P = 1 << 20  # a fake, aligned address
+    lib = mtl.lib()
+    st = lib.mtl_attn_fwd(ctypes.byref(cfg), None, P, P, P, P, P, P, P, None)
+    assert st == mtl.MTL_E_NULL
+    st = lib.mtl_attn_fwd(ctypes.byref(cfg), P + 2, P, P, P, P, P, P, P, None)
+    assert st == mtl.MTL_E_ALIGN
+    st = lib.mtl_mlp_bwd(ctypes.byref(cfg), P, P, P, P, P, P, P, P, P, P, None, P, 16, None)
+    assert st == mtl.MTL_E_WORKSPACE
+    st = lib.mtl_attn_bwd(ctypes.byref(cfg), P, P, P, P, P, P, P, P, P, P, P, None, P, 16, None)
+    assert st == mtl.MTL_E_WORKSPACE
+    arr = (ctypes.c_void_p * 2)(P, P)
+    assert lib.mtl_reduce(2, arr, None, None, P, 64, 12, 0, 64, None) == mtl.MTL_E_SHAPE  # cols % 8
+    assert lib.mtl_reduce(2, arr, None, None, P, 64, 16, 0, 65, None) == mtl.MTL_E_SHAPE
+    assert lib.mtl_reduce(0, arr, None, None, P, 64, 16, 0, 64, None) == mtl.MTL_E_SHAPE
+    assert lib.mtl_reduce(2, arr, None, None, P, 64, 16, 0, 64, None) == mtl.MTL_E_UNSUPPORTED  # out aliases
+    assert lib.mtl_reduce(2, None, None, None, P, 64, 16, 0, 64, None) == mtl.MTL_E_NULL
+
+
+def test_status_strings(mtl):
+    for s in range(9):
+        assert mtl.status_text(s) not in ("", "unknown status")
