@@ -64,13 +64,30 @@ __device__ __forceinline__ void transpose8x8(const u32x4 (&in)[8], u32x4 (&out)[
 }
 
 // ---------------------------------------------------------------- GeLU
-// Exact GeLU z * Phi(z) with Phi from the device erf (ROCm's OCML), and its
-// derivative Phi(z) + z * phi(z).
-__device__ __forceinline__ float gelu_f(float z) { return 0.5f * z * (1.0f + erff(z * 0.70710678118654752f)); }
+// Exact-form GeLU z * Phi(z) and its derivative Phi(z) + z * phi(z).  The normal
+// CDF uses the rational approximation of erfc in Abramowitz & Stegun (1964),
+// formula 7.1.26 (|error of erf| <= 1.5e-7): erfc(x) = poly(t) * exp(-x^2),
+// t = 1 / (1 + p x), x >= 0.  With x = |z| / sqrt(2), exp(-x^2) = exp(-z^2 / 2)
+// is also the unnormalised normal density, so one exp serves both Phi and phi.
+__device__ __forceinline__ void normal_cdf_pdf(float z, float& cdf, float& pdf) {
+  const float x = fabsf(z) * 0.70710678118654752f;
+  const float t = __builtin_amdgcn_rcpf(1.0f + 0.3275911f * x);
+  const float poly =
+      t * (0.254829592f + t * (-0.284496736f + t * (1.421413741f + t * (-1.453152027f + t * 1.061405429f))));
+  const float e = __expf(-x * x);
+  const float half_erfc = 0.5f * poly * e;
+  cdf = z >= 0.f ? 1.0f - half_erfc : half_erfc;
+  pdf = 0.39894228040143268f * e;
+}
+__device__ __forceinline__ float gelu_f(float z) {
+  float c, p;
+  normal_cdf_pdf(z, c, p);
+  return z * c;
+}
 __device__ __forceinline__ float gelu_grad_f(float z) {
-  const float cdf = 0.5f * (1.0f + erff(z * 0.70710678118654752f));
-  const float pdf = 0.39894228040143268f * __expf(-0.5f * z * z);
-  return cdf + z * pdf;
+  float c, p;
+  normal_cdf_pdf(z, c, p);
+  return c + z * p;
 }
 
 }  // namespace mtl

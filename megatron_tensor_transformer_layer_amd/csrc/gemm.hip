@@ -6,87 +6,154 @@
 // (A k, B k) for dgrad and (A mn, B mn) for wgrad when weights are stored
 // [in, out] row-major.
 //
-// Design (CDNA4): 256 threads = 4 wave64s in a 2x2 grid; a BMxBN tile per
-// workgroup, K stepped 64 at a time through a double-buffered LDS stage of
-// k-contiguous rows (16-byte chunks XOR-swizzled by row).  mn-contiguous
-// operands are read as 8(k) x 8(mn) blocks and transposed in registers with
-// v_perm_b32 before the LDS write, so the MFMA operand reads are always one
-// ds_read_b128 per lane.  The MFMA is issued with the operands swapped
-// (B fragment as "a", A fragment as "b") so that each lane ends up owning 4
-// consecutive output columns of one row: the epilogue stores 8 or 16 bytes per
-// lane.  Tile order is XCD-aware: the 8 XCDs each take a contiguous block of
-// tiles (grouped 4 tile-rows at a time) so A/B panels are reused inside one L2.
+// Design (CDNA4):
+//  * 256 threads = 4 wave64s in a 2x2 grid, a BM x BN tile per workgroup, K in
+//    slabs of 64, v_mfma_f32_32x32x16_bf16.
+//  * Global -> LDS with global_load_lds_dwordx4: every wave instruction fills
+//    1 KB of LDS directly (no VGPR staging, no VALU).  Two LDS stages, each a
+//    separate LDS object so the compiler knows a DMA into one never aliases a
+//    read of the other; the slab kt+1 streams in while slab kt is multiplied.
+//  * A k-contiguous operand is kept as [rows][64] with its 16-byte chunks XOR
+//    swizzled by row; fragments are one ds_read_b128 per lane.
+//  * An mn-contiguous operand is kept in its global layout [64][rows] (64-byte
+//    groups XOR-swizzled by k so that the reads below hit distinct banks) and read with
+//    two ds_read_b64_tr_b16: within each 16-lane group, lanes 4R..4R+3 name row
+//    R of a 4 x 16 block and lane i receives its column i, i.e. four
+//    consecutive k of one m (or n).  No register transposes.
+//  * Fragments of the next 16-deep k step are read while the MFMAs of the
+//    current one run.
+//  * The MFMA is issued with the operands swapped (B fragment as "a") so that
+//    each lane owns 4 consecutive output columns of one row: the epilogue
+//    stores 8 or 16 bytes per lane.
+//  * Tile order is XCD-aware: the 8 XCDs each take a contiguous run of tiles
+//    (grouped 4 tile-rows at a time) so A/B panels are reused inside one L2.
+//  * Tails: rows/columns past M or N load a clamped in-bounds row (those
+//    outputs are never stored); k past K loads a clamped address and the slab
+//    is zero-filled in LDS before use.
 #include "common.hpp"
 #include "kernels.hpp"
 
+#define LDS_AS __attribute__((address_space(3)))
+#define GLB_AS __attribute__((address_space(1)))
+
 namespace mtl {
 
-template <int ROWS, bool KCONTIG>
-struct TileLoader {
-  // k-contiguous: ROWS x 64 tile, thread t loads chunk t%8 of rows t/8 + 32 i.
-  // mn-contiguous: ROWS/8 x 8 blocks of 8x8, block b = t + 256 i: kg = b%8, mg = b/8.
-  static constexpr int NK = ROWS / 32;
-  static constexpr int NB = (ROWS + 255) / 256;
-  static constexpr int NREG = KCONTIG ? NK : NB * 8;
-  u32x4 r[NREG];
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 
-  __device__ __forceinline__ void load(const uint16_t* __restrict__ base, int64_t ld, int row0, int nrows, int k0,
-                                       int K) {
-    const int t = threadIdx.x;
-    if constexpr (KCONTIG) {
-      const int c = t & 7;
-      const int kk = k0 + c * 8;
+__device__ __forceinline__ u32x2 read_tr(const LDS_AS char* p) {
+  return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4*)p));
+}
+
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+// A raw buffer resource over [base, base + bytes): loads past the end return 0.
+__device__ __forceinline__ i32x4 make_rsrc(const void* base, uint32_t bytes) {
+  const uint64_t b = reinterpret_cast<uint64_t>(base);
+  return i32x4{(int)(uint32_t)b, (int)(uint32_t)(b >> 32), (int)bytes, 0x00020000};
+}
+
+// 16 bytes per lane from buffer offset voff + soff into LDS at lds + 16*lane
+// (buffer_load_dwordx4 ... lds; the LDS base travels in M0).  Issued as inline
+// assembly so that the compiler does not fence every later LDS read on it: the
+// caller waits (vmcnt) before the barrier that publishes the slab.  M0 is
+// saved and restored; s_nop covers the M0 -> LDS-DMA hazard.
+__device__ __forceinline__ void dma16(i32x4 rsrc, uint32_t voff, uint32_t soff, uint32_t lds) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %2, %3, %4 offen lds\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(lds), "v"(voff), "s"(rsrc), "s"(soff)
+      : "memory");
+}
+
+// LDS swizzles, for gfx950's 64 x 4-byte banks (ds_read_b128 serves 16 lanes per
+// cycle, ds_read_b64_tr_b16 32 lanes per cycle):
+//  * k-contiguous tiles ([rows][64], 128-byte rows): 16-byte chunk c of row r is
+//    stored at c ^ ((r >> 1) & 7), so the 16 rows of one cycle (two rows per
+//    256-byte bank line) use 16 distinct bank quads;
+//  * mn-contiguous tiles ([64][rows]): the 64-byte group of row k is XORed with
+//    k & 3, so the 4 rows a transpose read touches per cycle fall in 4 different
+//    64-byte bank windows.  For 192-wide tiles (24 chunks, 384-byte rows, which
+//    already alternate bank halves) only bit 2 of the chunk is flipped, by
+//    (k >> 1) & 1, which keeps the map a bijection on the row.
+__device__ __forceinline__ int kc_swz(int row) { return (row >> 1) & 7; }
+template <int ROWS>
+__device__ __forceinline__ int mn_swz(int k) {
+  if constexpr (ROWS % 256 == 0 || ROWS == 128) return (k & 3) << 2;
+  else return ((k >> 1) & 1) << 2;
+}
+
+template <int ROWS, bool KC>
+struct Operand {
+  static constexpr int BYTES = ROWS * 128;     // one 64-deep slab
+  static constexpr int INSTR = BYTES / 1024;   // wave instructions per slab
+  static constexpr int PER_WAVE = INSTR / 4;
+  static constexpr int ROWB = ROWS * 2;        // row bytes of the mn-contiguous layout
+  static constexpr int READS = KC ? 1 : 2;     // LDS read instructions per fragment
+
+  // Issue the DMA of slab [k0, k0+64) of rows [row0, row0+ROWS) into lds.
+  // k-contiguous: wave instruction I fills rows 8I..8I+7, lane -> (row 8I + l/8,
+  // physical chunk l%8 = logical chunk ^ kc_swz(row)).
+  // mn-contiguous: lds byte o = 1024 I + 16 l is (k = o / ROWB, physical chunk
+  // (o % ROWB)/16 = logical chunk ^ mn_swz(k)).
+  static __device__ __forceinline__ void load(i32x4 rs, int64_t ld, int row0, int k0, LDS_AS char* lds) {
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 #pragma unroll
-      for (int i = 0; i < NK; ++i) {
-        const int row = row0 + (t >> 3) + 32 * i;
-        if (row < nrows && kk < K) {
-          r[i] = *reinterpret_cast<const u32x4*>(base + (int64_t)row * ld + kk);
-        } else {
-          r[i] = u32x4{0, 0, 0, 0};
-        }
+    for (int q = 0; q < PER_WAVE; ++q) {
+      const int I = wave * PER_WAVE + q;
+      // The whole offset goes in the VGPR operand: the raw-buffer range check
+      // (which turns reads past the end into zeros) does not cover soffset.
+      uint32_t voff;
+      if constexpr (KC) {
+        const int row = I * 8 + (lane >> 3);
+        const int c = (lane & 7) ^ kc_swz(row);
+        voff = (uint32_t)(((int64_t)(row0 + row) * ld + k0 + c * 8) * 2);
+      } else {
+        const int o = I * 1024 + lane * 16;
+        const int k = o / ROWB;
+        const int c = ((o % ROWB) >> 4) ^ mn_swz<ROWS>(k);
+        voff = (uint32_t)(((int64_t)(k0 + k) * ld + row0 + c * 8) * 2);
       }
-    } else {
+      dma16(rs, voff, 0u, (uint32_t)(uintptr_t)(lds + I * 1024));
+    }
+  }
+
+  // k-contiguous operand of a slab with kvalid < 64 valid k (after its DMA has
+  // landed): zero the chunks past K, which hold the next row's values.
+  static __device__ __forceinline__ void zero_tail(LDS_AS char* lds, int kvalid) {
+    if constexpr (KC) {
+      const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 #pragma unroll
-      for (int i = 0; i < NB; ++i) {
-        const int b = t + 256 * i;
-        const int kg = b & 7, mg = b >> 3;
-        const int col = row0 + mg * 8;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const int k = k0 + kg * 8 + j;
-          if (b < ROWS && col < nrows && k < K) {
-            r[i * 8 + j] = *reinterpret_cast<const u32x4*>(base + (int64_t)k * ld + col);
-          } else {
-            r[i * 8 + j] = u32x4{0, 0, 0, 0};
-          }
-        }
+      for (int q = 0; q < PER_WAVE; ++q) {
+        const int I = wave * PER_WAVE + q;
+        const int c = (lane & 7) ^ kc_swz(I * 8 + (lane >> 3));
+        if (c * 8 >= kvalid) *reinterpret_cast<LDS_AS u32x4*>(lds + I * 1024 + lane * 16) = u32x4{0, 0, 0, 0};
       }
     }
   }
 
-  __device__ __forceinline__ void store(char* lds) {
-    const int t = threadIdx.x;
-    if constexpr (KCONTIG) {
-      const int c = t & 7;
-#pragma unroll
-      for (int i = 0; i < NK; ++i) {
-        const int row = (t >> 3) + 32 * i;
-        *reinterpret_cast<u32x4*>(lds + swz(row, c)) = r[i];
-      }
+  // Operand fragment of 32-row block r32 at k step kk (16 deep): lane l holds
+  // row (l % 32) and k = kk*16 + (l/32)*8 + j, j = 0..7.
+  static __device__ __forceinline__ u32x4 frag(const LDS_AS char* lds, int r32, int kk, int lane) {
+    if constexpr (KC) {
+      const int row = r32 * 32 + (lane & 31);
+      const int c = kk * 2 + (lane >> 5);
+      return *reinterpret_cast<const LDS_AS u32x4*>(lds + row * 128 + ((c ^ kc_swz(row)) << 4));
     } else {
-#pragma unroll
-      for (int i = 0; i < NB; ++i) {
-        const int b = t + 256 * i;
-        if (b < ROWS) {
-          const int kg = b & 7, mg = b >> 3;
-          u32x4 in[8], out[8];
-#pragma unroll
-          for (int j = 0; j < 8; ++j) in[j] = r[i * 8 + j];
-          transpose8x8(in, out);
-#pragma unroll
-          for (int j = 0; j < 8; ++j) *reinterpret_cast<u32x4*>(lds + swz(mg * 8 + j, kg)) = out[j];
-        }
-      }
+      // lanes 4R..4R+3 of each 16-lane group g name row k = kk*16 + (g/2)*8 + R
+      // (+4 for the second read), columns r32*32 + (g%2)*16 + 4*(l%4) .. +3
+      const int g = lane >> 4, R = (lane >> 2) & 3, c4 = lane & 3;
+      const int chunk = (r32 * 4 + (g & 1) * 2 + (c4 >> 1)) ^ mn_swz<ROWS>(R);
+      const int lanepart = (g >> 1) * 8 * ROWB + R * ROWB + (chunk << 4) + (c4 & 1) * 8;
+      const LDS_AS char* p = lds + lanepart + kk * 16 * ROWB;
+      const u32x2 lo = read_tr(p);
+      const u32x2 hi = read_tr(p + 4 * ROWB);
+      return u32x4{lo[0], lo[1], hi[0], hi[1]};
     }
   }
 };
@@ -98,12 +165,78 @@ __device__ __forceinline__ int tile_index(int w, int ntiles) {
   return w;
 }
 
+template <int BM, int BN, bool A_K, bool B_K>
+struct Mainloop {
+  static constexpr int WM = BM / 2, WN = BN / 2;
+  static constexpr int TM = WM / 32, TN = WN / 32;
+  using OA = Operand<BM, A_K>;
+  using OB = Operand<BN, B_K>;
+  static constexpr int STAGE = OA::BYTES + OB::BYTES;
+
+  static __device__ __forceinline__ void issue(const GemmArgs& p, i32x4 ra, i32x4 rb, int m0, int n0, int k0,
+                                               LDS_AS char* st) {
+    OA::load(ra, p.lda, m0, k0, st);
+    OB::load(rb, p.ldb, n0, k0, st + OA::BYTES);
+    __builtin_amdgcn_sched_barrier(0);  // keep the DMA issue ahead of the MFMA work
+  }
+  static __device__ __forceinline__ void settle(const GemmArgs& p, int k0, LDS_AS char* st) {
+    // wait for this thread's DMAs; clear the k tail of a partial last slab
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    const int kvalid = p.K - k0;
+    if (kvalid < 64) {
+      OA::zero_tail(st, kvalid);
+      OB::zero_tail(st + OA::BYTES, kvalid);
+    }
+  }
+  static __device__ __forceinline__ void compute(const LDS_AS char* st, int wm, int wn, int lane,
+                                                 f32x16 (&acc)[TM][TN]) {
+    const LDS_AS char* sa = st;
+    const LDS_AS char* sb = st + OA::BYTES;
+    u32x4 fa[2][TM], fb[2][TN];
+#pragma unroll
+    for (int i = 0; i < TM; ++i) fa[0][i] = OA::frag(sa, wm * TM + i, 0, lane);
+#pragma unroll
+    for (int j = 0; j < TN; ++j) fb[0][j] = OB::frag(sb, wn * TN + j, 0, lane);
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      const int cur = kk & 1, nxt = cur ^ 1;
+      if (kk < 3) {
+#pragma unroll
+        for (int i = 0; i < TM; ++i) fa[nxt][i] = OA::frag(sa, wm * TM + i, kk + 1, lane);
+#pragma unroll
+        for (int j = 0; j < TN; ++j) fb[nxt][j] = OB::frag(sb, wn * TN + j, kk + 1, lane);
+      }
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j) acc[i][j] = mfma32(fb[cur][j], fa[cur][i], acc[i][j]);
+    }
+    // Schedule: the first step's fragment reads, then for every step its MFMAs
+    // with the next step's fragment reads interleaved one for one, so LDS
+    // latency hides behind MFMA issue.
+    constexpr int NR = TM * (OA::READS) + TN * (OB::READS);  // LDS reads per step
+    constexpr int NM = TM * TN;                               // MFMAs per step
+    __builtin_amdgcn_sched_group_barrier(0x100, NR, 0);
+#pragma unroll
+    for (int kk = 0; kk < 3; ++kk) {
+#pragma unroll
+      for (int x = 0; x < NM; ++x) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        if (x < NR) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, NM, 0);
+  }
+};
+
 template <int BM, int BN, bool A_K, bool B_K, int EPI>
 __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmArgs p) {
-  constexpr int WM = BM / 2, WN = BN / 2;
-  constexpr int TM = WM / 32, TN = WN / 32;
-  constexpr int A_BYTES = BM * 128, B_BYTES = BN * 128;
-  __shared__ __attribute__((aligned(16))) char smem[2 * (A_BYTES + B_BYTES)];
+  using ML = Mainloop<BM, BN, A_K, B_K>;
+  constexpr int WM = ML::WM, WN = ML::WN, TM = ML::TM, TN = ML::TN;
+  __shared__ __attribute__((aligned(1024))) char st0_[ML::STAGE];
+  __shared__ __attribute__((aligned(1024))) char st1_[ML::STAGE];
+  LDS_AS char* st0 = (LDS_AS char*)st0_;
+  LDS_AS char* st1 = (LDS_AS char*)st1_;
 
   const int tiles_m = (p.M + BM - 1) / BM, tiles_n = (p.N + BN - 1) / BN;
   const int ntiles = tiles_m * tiles_n;
@@ -120,93 +253,150 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmArgs p) {
   const int wave = threadIdx.x >> 6;
   const int wm = wave >> 1, wn = wave & 1;
 
-  TileLoader<BM, A_K> la;
-  TileLoader<BN, B_K> lb;
-
   f32x16 acc[TM][TN];
 #pragma unroll
   for (int i = 0; i < TM; ++i)
 #pragma unroll
     for (int j = 0; j < TN; ++j) acc[i][j] = f32x16{};
 
+  // Buffer resources: k-contiguous operands end after their last row (M or N),
+  // mn-contiguous ones after row K, so everything past the matrix reads as 0.
+  const i32x4 ra = make_rsrc(p.a, (uint32_t)((A_K ? (int64_t)p.M : (int64_t)p.K) * p.lda * 2));
+  const i32x4 rb = make_rsrc(p.b, (uint32_t)((B_K ? (int64_t)p.N : (int64_t)p.K) * p.ldb * 2));
   const int nk = (p.K + 63) / 64;
-  la.load(p.a, p.lda, m0, p.M, 0, p.K);
-  lb.load(p.b, p.ldb, n0, p.N, 0, p.K);
-  la.store(smem);
-  lb.store(smem + A_BYTES);
+  ML::issue(p, ra, rb, m0, n0, 0, st0);
+  ML::settle(p, 0, st0);
   __syncthreads();
-
-  const int lrow = lane & 31, lgrp = lane >> 5;
-  for (int kt = 0; kt < nk; ++kt) {
-    char* sa = smem + (kt & 1) * (A_BYTES + B_BYTES);
-    char* sb = sa + A_BYTES;
-    if (kt + 1 < nk) {
-      la.load(p.a, p.lda, m0, p.M, (kt + 1) * 64, p.K);
-      lb.load(p.b, p.ldb, n0, p.N, (kt + 1) * 64, p.K);
-    }
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      u32x4 af[TM], bfr[TN];
-#pragma unroll
-      for (int i = 0; i < TM; ++i)
-        af[i] = *reinterpret_cast<const u32x4*>(sa + swz(wm * WM + i * 32 + lrow, kk * 2 + lgrp));
-#pragma unroll
-      for (int j = 0; j < TN; ++j)
-        bfr[j] = *reinterpret_cast<const u32x4*>(sb + swz(wn * WN + j * 32 + lrow, kk * 2 + lgrp));
-#pragma unroll
-      for (int i = 0; i < TM; ++i)
-#pragma unroll
-        for (int j = 0; j < TN; ++j) acc[i][j] = mfma32(bfr[j], af[i], acc[i][j]);
-    }
-    if (kt + 1 < nk) {
-      char* na = smem + ((kt + 1) & 1) * (A_BYTES + B_BYTES);
-      la.store(na);
-      lb.store(na + A_BYTES);
-    }
+  // Two slabs per trip (stage 0 then stage 1), so each LDS stage is a fixed
+  // object; an odd last slab is finished after the loop.
+  int kt = 0;
+  for (; kt + 1 < nk; kt += 2) {
+    ML::issue(p, ra, rb, m0, n0, (kt + 1) * 64, st1);
+    ML::compute(st0, wm, wn, lane, acc);
+    ML::settle(p, (kt + 1) * 64, st1);
+    __syncthreads();
+    const bool more = kt + 2 < nk;
+    if (more) ML::issue(p, ra, rb, m0, n0, (kt + 2) * 64, st0);
+    ML::compute(st1, wm, wn, lane, acc);
+    if (more) ML::settle(p, (kt + 2) * 64, st0);
     __syncthreads();
   }
+  if (kt < nk) ML::compute(st0, wm, wn, lane, acc);
+  const int lrow = lane & 31, lgrp = lane >> 5;
 
-  // Epilogue: lane owns row m, columns n..n+3 for each (i, j, g).
+  // ---- epilogue ----------------------------------------------------------
+  // Lane (lrow, lgrp) holds, for every (i, j, g), row i*32 + lrow and columns
+  // j*32 + 8g + 4*lgrp .. +3 of the wave's WM x WN sub-tile.  Values are first
+  // finished in registers (bias, GeLU), then written to the wave's own slice of
+  // the (now idle) LDS stages and read back row by row, so every global store
+  // is 16 bytes per lane over whole rows.  fp32 results go in passes of IPP
+  // row blocks.
+  __syncthreads();  // all waves are done with the last slab
+  LDS_AS char* region = (wave < 2 ? st0 : st1) + (wave & 1) * (ML::STAGE / 2);
+  constexpr int REGION = ML::STAGE / 2;
+  constexpr bool HAS_BIAS = (EPI == EPI_BF16_BIAS || EPI == EPI_BIAS_GELU);
+  constexpr bool F32OUT = (EPI == EPI_F32 || EPI == EPI_F32_ACC);
+  // GeLU' is applied in the row phase against the stored z, so its products
+  // are staged in fp32 too.
+  constexpr bool F32STAGE = F32OUT || EPI == EPI_DGELU;
+  constexpr int E = F32STAGE ? 4 : 2;
+  constexpr int RB = WN * E;                 // bytes per staged row
+  constexpr int CPR = RB / 16;               // 16-byte chunks per row
+  constexpr int IPP = (REGION / (32 * RB)) < TM ? (REGION / (32 * RB)) : TM;
+  static_assert(IPP >= 1, "epilogue staging does not fit");
+  const int mw = m0 + wm * WM, nw = n0 + wn * WN;
+
+  float bias_v[TN][4][4];
+  if constexpr (HAS_BIAS) {
+    u32x2 braw[TN][4];
 #pragma unroll
-  for (int i = 0; i < TM; ++i) {
-    const int m = m0 + wm * WM + i * 32 + lrow;
-    if (m >= p.M) continue;
-#pragma unroll
-    for (int j = 0; j < TN; ++j) {
+    for (int j = 0; j < TN; ++j)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        const int n = n0 + wn * WN + j * 32 + 8 * g + 4 * lgrp;
-        if (n >= p.N) continue;
-        float v[4] = {acc[i][j][4 * g + 0], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]};
-        if constexpr (EPI == EPI_F32 || EPI == EPI_F32_ACC) {
-          float* c = reinterpret_cast<float*>(p.c) + (int64_t)m * p.ldc + n;
-          f32x4 o = {v[0], v[1], v[2], v[3]};
-          if constexpr (EPI == EPI_F32_ACC) o += *reinterpret_cast<const f32x4*>(c);
-          *reinterpret_cast<f32x4*>(c) = o;
-        } else {
-          if constexpr (EPI == EPI_BF16_BIAS || EPI == EPI_BIAS_GELU) {
-            const u32x2 bb = *reinterpret_cast<const u32x2*>(p.bias + n);
-            v[0] += bf16_lo(bb[0]);
-            v[1] += bf16_hi(bb[0]);
-            v[2] += bf16_lo(bb[1]);
-            v[3] += bf16_hi(bb[1]);
+        const int n = nw + j * 32 + 8 * g + 4 * lgrp;
+        braw[j][g] = n < p.N ? *reinterpret_cast<const u32x2*>(p.bias + n) : u32x2{0, 0};
+      }
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        bias_v[j][g][0] = bf16_lo(braw[j][g][0]);
+        bias_v[j][g][1] = bf16_hi(braw[j][g][0]);
+        bias_v[j][g][2] = bf16_lo(braw[j][g][1]);
+        bias_v[j][g][3] = bf16_hi(braw[j][g][1]);
+      }
+  }
+
+  // out selects the output: 0 -> C, 1 -> C2 (GeLU of the biased sum).
+#pragma unroll
+  for (int out = 0; out < (EPI == EPI_BIAS_GELU ? 2 : 1); ++out) {
+#pragma unroll
+    for (int i0 = 0; i0 < TM; i0 += IPP) {
+      // register phase
+#pragma unroll
+      for (int ii = 0; ii < IPP; ++ii) {
+        const int i = i0 + ii;
+        const int rl = ii * 32 + lrow;
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            float v[4] = {acc[i][j][4 * g + 0], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]};
+            if constexpr (HAS_BIAS) {
+#pragma unroll
+              for (int e = 0; e < 4; ++e) v[e] += bias_v[j][g][e];
+            }
+            if (out == 1) {
+#pragma unroll
+              for (int e = 0; e < 4; ++e) v[e] = gelu_f(v[e]);
+            }
+            const int col = j * 32 + 8 * g + 4 * lgrp;
+            if constexpr (F32STAGE) {
+              const int ch = col / 4;
+              const int pc = (ch + rl) % CPR;
+              *reinterpret_cast<LDS_AS f32x4*>(region + rl * RB + pc * 16) = f32x4{v[0], v[1], v[2], v[3]};
+            } else {
+              const int ch = col / 8;
+              const int pc = (ch + rl) % CPR;
+              *reinterpret_cast<LDS_AS u32x2*>(region + rl * RB + pc * 16 + (col & 7) * 2) =
+                  u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+            }
           }
-          if constexpr (EPI == EPI_DGELU) {
-            const u32x2 zz = *reinterpret_cast<const u32x2*>(p.aux + (int64_t)m * p.ld_aux + n);
-            v[0] *= gelu_grad_f(bf16_lo(zz[0]));
-            v[1] *= gelu_grad_f(bf16_hi(zz[0]));
-            v[2] *= gelu_grad_f(bf16_lo(zz[1]));
-            v[3] *= gelu_grad_f(bf16_hi(zz[1]));
-          }
-          uint16_t* c = reinterpret_cast<uint16_t*>(p.c) + (int64_t)m * p.ldc + n;
-          *reinterpret_cast<u32x2*>(c) = u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
-          if constexpr (EPI == EPI_BIAS_GELU) {
-            uint16_t* c2 = reinterpret_cast<uint16_t*>(p.c2) + (int64_t)m * p.ldc2 + n;
-            *reinterpret_cast<u32x2*>(c2) = u32x2{pack_bf16x2(gelu_f(v[0]), gelu_f(v[1])),
-                                                  pack_bf16x2(gelu_f(v[2]), gelu_f(v[3]))};
+      }
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      // row phase: chunk idx of the IPP*32 staged rows
+      constexpr int TOTAL = IPP * 32 * CPR;
+#pragma unroll
+      for (int it = 0; it < (TOTAL + 63) / 64; ++it) {
+        const int idx = it * 64 + lane;
+        if (TOTAL % 64 == 0 || idx < TOTAL) {
+          const int rl = idx / CPR, ch = idx % CPR;
+          const int pc = (ch + rl) % CPR;
+          const u32x4 val = *reinterpret_cast<const LDS_AS u32x4*>(region + rl * RB + pc * 16);
+          const int m = mw + i0 * 32 + rl;
+          const int n = nw + ch * (16 / E);
+          if (m < p.M && n < p.N) {
+            if constexpr (F32OUT) {
+              float* c = reinterpret_cast<float*>(p.c) + (int64_t)m * p.ldc + n;
+              f32x4 o = __builtin_bit_cast(f32x4, val);
+              if constexpr (EPI == EPI_F32_ACC) o += *reinterpret_cast<const f32x4*>(c);
+              *reinterpret_cast<f32x4*>(c) = o;
+            } else if constexpr (EPI == EPI_DGELU) {
+              const f32x4 d = __builtin_bit_cast(f32x4, val);
+              const u32x2 z = *reinterpret_cast<const u32x2*>(p.aux + (int64_t)m * p.ld_aux + n);
+              uint16_t* c = reinterpret_cast<uint16_t*>(p.c) + (int64_t)m * p.ldc + n;
+              *reinterpret_cast<u32x2*>(c) = u32x2{pack_bf16x2(d[0] * gelu_grad_f(bf16_lo(z[0])),
+                                                               d[1] * gelu_grad_f(bf16_hi(z[0]))),
+                                                   pack_bf16x2(d[2] * gelu_grad_f(bf16_lo(z[1])),
+                                                               d[3] * gelu_grad_f(bf16_hi(z[1])))};
+            } else {
+              uint16_t* c = reinterpret_cast<uint16_t*>(out == 0 ? p.c : p.c2) + (int64_t)m * (out == 0 ? p.ldc : p.ldc2) + n;
+              *reinterpret_cast<u32x4*>(c) = val;
+            }
           }
         }
       }
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     }
   }
 }
@@ -229,6 +419,12 @@ static hipError_t launch_layout(const GemmArgs& p, hipStream_t s) {
 
 hipError_t gemm_bf16(const GemmArgs& p, GemmLayout layout, int epi, hipStream_t s) {
   if (p.M <= 0 || p.N <= 0) return hipSuccess;
+  // Operands are addressed through raw buffer resources with 32-bit byte
+  // offsets; a tile may run up to 256 rows (or 64 k) past the matrix.
+  const bool a_k = layout != GEMM_WGRAD, b_k = layout == GEMM_DGRAD;
+  const int64_t a_rows = (a_k ? (int64_t)p.M : (int64_t)p.K) + 256, b_rows = (b_k ? (int64_t)p.N : (int64_t)p.K) + 256;
+  if (a_rows * p.lda * 2 >= ((int64_t)1 << 32) || b_rows * p.ldb * 2 >= ((int64_t)1 << 32)) return hipErrorInvalidValue;
+  if (p.K <= 0) return hipErrorInvalidValue;
   switch (layout) {
     case GEMM_FWD:  // A k-contig, B n-contig
       if (epi == EPI_BF16) return launch_layout<true, false, EPI_BF16>(p, s);

@@ -7,8 +7,9 @@
 //
 // colsum_bf16: the bias gradients of the four linears are column sums of a
 // [rows, cols] bf16 gradient.  Deterministic two-stage sum: stage 1 gives each
-// wave 512 columns x 64 rows (16-byte loads, fp32 accumulate) and writes one
-// partial row to the workspace; stage 2 adds the partial rows in order.
+// 256-thread block 512 columns x 128 rows (16-byte loads, fp32 accumulate, the
+// four waves combined in a fixed order) and writes one partial row to the
+// workspace; stage 2 adds the partial rows in order.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -82,38 +83,59 @@ hipError_t reduce_partials(int t, const uint16_t* const* partials, const uint16_
   return hipGetLastError();
 }
 
-constexpr int CS_ROWS = 64;  // rows per stage-1 chunk
-constexpr int CS_COLS = 512; // columns per stage-1 wave
+constexpr int CS_ROWS = 128;  // rows per stage-1 block (32 per wave)
+constexpr int CS_COLS = 512;  // columns per stage-1 block (8 per lane)
 
 size_t colsum_ws_floats(int64_t rows, int64_t cols) {
   return (size_t)((rows + CS_ROWS - 1) / CS_ROWS) * (size_t)cols;
 }
 
-__global__ __launch_bounds__(64) void colsum_stage1(const uint16_t* __restrict__ x, int64_t rows, int64_t cols,
-                                                     int64_t ld, float* __restrict__ ws) {
-  const int64_t c = (int64_t)blockIdx.x * CS_COLS + threadIdx.x * 8;
+// Stage 1: block (column slab, row chunk); wave w sums rows r0+w, r0+w+4, ...
+// of its 512 columns; the four wave sums are added in wave order through LDS.
+__global__ __launch_bounds__(256) void colsum_stage1(const uint16_t* __restrict__ x, int64_t rows, int64_t cols,
+                                                      int64_t ld, float* __restrict__ ws) {
+  __shared__ f32x4 part[3][64][2];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t c = (int64_t)blockIdx.x * CS_COLS + lane * 8;
   const int64_t r0 = (int64_t)blockIdx.y * CS_ROWS;
-  if (c >= cols) return;
-  float s[8] = {0, 0, 0, 0, 0, 0, 0, 0};
   const int64_t r1 = min(rows, r0 + CS_ROWS);
-  for (int64_t r = r0; r < r1; ++r) {
-    const u32x4 v = *reinterpret_cast<const u32x4*>(x + r * ld + c);
+  float s[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  if (c < cols) {
+#pragma unroll 4
+    for (int64_t r = r0 + wave; r < r1; r += 4) {
+      const u32x4 v = *reinterpret_cast<const u32x4*>(x + r * ld + c);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      s[2 * j] += bf16_lo(v[j]);
-      s[2 * j + 1] += bf16_hi(v[j]);
+      for (int j = 0; j < 4; ++j) {
+        s[2 * j] += bf16_lo(v[j]);
+        s[2 * j + 1] += bf16_hi(v[j]);
+      }
     }
   }
-  float* w = ws + (int64_t)blockIdx.y * cols + c;
-  *reinterpret_cast<f32x4*>(w) = f32x4{s[0], s[1], s[2], s[3]};
-  *reinterpret_cast<f32x4*>(w + 4) = f32x4{s[4], s[5], s[6], s[7]};
+  if (wave > 0) {
+    part[wave - 1][lane][0] = f32x4{s[0], s[1], s[2], s[3]};
+    part[wave - 1][lane][1] = f32x4{s[4], s[5], s[6], s[7]};
+  }
+  __syncthreads();
+  if (wave == 0 && c < cols) {
+#pragma unroll
+    for (int w = 0; w < 3; ++w) {
+      const f32x4 a = part[w][lane][0], b = part[w][lane][1];
+      s[0] += a[0]; s[1] += a[1]; s[2] += a[2]; s[3] += a[3];
+      s[4] += b[0]; s[5] += b[1]; s[6] += b[2]; s[7] += b[3];
+    }
+    float* w = ws + (int64_t)blockIdx.y * cols + c;
+    *reinterpret_cast<f32x4*>(w) = f32x4{s[0], s[1], s[2], s[3]};
+    *reinterpret_cast<f32x4*>(w + 4) = f32x4{s[4], s[5], s[6], s[7]};
+  }
 }
 
-__global__ __launch_bounds__(256) void colsum_stage2(const float* __restrict__ ws, int64_t chunks, int64_t cols,
-                                                      float* __restrict__ out, int accumulate) {
+// Stage 2: one thread per column adds the chunk partials in chunk order.
+__global__ __launch_bounds__(64) void colsum_stage2(const float* __restrict__ ws, int64_t chunks, int64_t cols,
+                                                     float* __restrict__ out, int accumulate) {
   const int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (c >= cols) return;
   float s = 0.f;
+#pragma unroll 8
   for (int64_t k = 0; k < chunks; ++k) s += ws[k * cols + c];
   out[c] = accumulate ? out[c] + s : s;
 }
@@ -124,11 +146,11 @@ hipError_t colsum_bf16(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld
   const int64_t chunks = (rows + CS_ROWS - 1) / CS_ROWS;
   if (chunks > 0) {
     dim3 g1((unsigned)((cols + CS_COLS - 1) / CS_COLS), (unsigned)chunks);
-    hipLaunchKernelGGL(colsum_stage1, g1, dim3(64), 0, s, x, rows, cols, ld, ws);
+    hipLaunchKernelGGL(colsum_stage1, g1, dim3(256), 0, s, x, rows, cols, ld, ws);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL(colsum_stage2, dim3((unsigned)((cols + 255) / 256)), dim3(256), 0, s, ws, chunks, cols, out,
+  hipLaunchKernelGGL(colsum_stage2, dim3((unsigned)((cols + 63) / 64)), dim3(64), 0, s, ws, chunks, cols, out,
                      accumulate ? 1 : 0);
   return hipGetLastError();
 }
