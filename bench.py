@@ -33,8 +33,57 @@ def parse():
     ap.add_argument("--workload", default="7b-tp4")
     ap.add_argument("--rank", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-sample-seq", type=int, default=2048)
+    ap.add_argument("--cpu-sample-seq", type=int, default=4096)
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="run only a plain device copy of known size (for scaling HBM byte counters)")
     return ap.parse_args()
+
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+GEMM_SRC = os.path.join(HERE, "megatron_tensor_transformer_layer_amd", "csrc", "gemm.hip")
+TRAFFIC_FILE = os.path.join(HERE, "profiles", "gemm_bf16_mlp_fwd_7b-tp4_traffic.txt")
+COPY_BYTES = 64 << 20  # one 32 Mi-element bf16 tensor read and written
+
+
+def gemm_source_hash() -> str:
+    import hashlib
+    with open(GEMM_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def stored_traffic(workload: str):
+    """Counter-derived HBM bytes per GEMM launch, from the committed rocprofv3
+    summary; None when there is none or when gemm.hip has changed since."""
+    if not os.path.exists(TRAFFIC_FILE) or workload != "7b-tp4":
+        return None
+    fields = {}
+    for line in open(TRAFFIC_FILE):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            fields[k.strip()] = v.strip()
+    if fields.get("gemm_source_sha256_16") != gemm_source_hash():
+        return None
+    try:
+        return float(fields["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def calibrate_copy():
+    """A plain copy of COPY_BYTES/2 bytes through the library (mtl_reduce with a
+    single partial, no bias, no residual): reads and writes exactly that many bytes."""
+    import torch
+    from megatron_tensor_transformer_layer_amd import mtl_reduce
+    n = COPY_BYTES // 2 // 2
+    rows, cols = n // 4096, 4096
+    src = torch.randn(rows, cols, device="cuda").to(torch.bfloat16)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        mtl_reduce([src], None, None, dst, rows, cols)
+    torch.cuda.synchronize()
+    assert torch.equal(src, dst)
+    print(json.dumps({"copy_kernel": "reduce_partials_kernel (t=1)", "bytes_read": rows * cols * 2,
+                      "bytes_written": rows * cols * 2, "launches": 3}), flush=True)
 
 
 def cpu_baseline(shape, rank, sample_seq):
@@ -75,6 +124,9 @@ def main():
               "on-device reduce); run with --gpus 1", file=sys.stderr)
         sys.exit(2)
 
+    if args.calibrate_copy:
+        calibrate_copy()
+        return
     import torch
     import synth
     from megatron_tensor_transformer_layer_amd import mtl_reduce
@@ -172,9 +224,12 @@ def main():
         "step_ms_p50": round(float(np.percentile(per_step, 50)), 4),
         "step_ms_p95": round(float(np.percentile(per_step, 95)), 4),
         "flop_per_step": fl["total"],
-        "roofline": {"bound": "mfma", "kernel": "gemm_bf16_kernel (fc1/fc2 forward, 256x256 tiles)",
+        "roofline": {"bound": "mfma",
+                     "kernel": "gemm_bf16_kernel, 256x256 tiles: the two launches of mtl_mlp_fwd "
+                               "(fc1 + bias + GeLU, fc2), %d x %d x %d each" % (D.S, D.f_l, D.h),
                      "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None},
+                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": stored_traffic(args.workload),
+                     "gemm_launch_us": round(gemm_launch_s * 1e6, 2)},
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:

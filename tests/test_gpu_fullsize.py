@@ -1,0 +1,97 @@
+"""Parity at the full workload sizes, in the launch configuration bench.py times.
+
+One TP rank's shard of a 7B-class layer (hidden 4096, 32 heads, ffn 16384,
+seq 4096, TP=4) and of a 96-layer-GPT-shaped layer (hidden 8192, 64 heads, ffn
+32768, seq 4096, TP=8), rank 0.  Each block call of the C ABI is fed seeded
+synthetic inputs (x and dY, plus independent H and dH for the MLP and
+attention halves) and compared with the fp64 oracle of the rank's share:
+QKV, attention output and log-sum-exp, the attention-input gradient and the
+bias gradients in full; the large GEMM outputs on sampled rows (activations)
+or sampled columns (weight gradients), which the oracle computes one by one.
+"""
+import numpy as np
+import pytest
+
+import synth
+from oracle import layer as L
+from tests.parity_util import assert_bf16, f64
+
+ROWS = [0, 1, 63, 64, 127, 1000, 2047, 2048, 3001, 4095]
+COLS = [0, 1, 7, 8, 255, 256, 511, 1023]
+
+
+def _cols(n):
+    rng = np.random.default_rng(5)
+    extra = rng.choice(n, 8, replace=False).tolist()
+    return sorted(set([c for c in COLS if c < n] + [n - 1] + extra))
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("workload", ["7b-tp4", "gpt96l-tp8"])
+def test_rank_shard_full_size(mtl, workload):
+    import torch
+    from megatron_tensor_transformer_layer_amd.layer import RankState, bf16_dev, host_f64
+
+    shape = synth.WORKLOADS[workload]
+    t = shape.tp
+    print(f"workload {workload} rank 0 of tp {t}", flush=True)
+    inp = synth.layer_inputs(shape, tp=t, rank=0)
+    hb = synth.layer_tensor(shape, "h")
+    dhb = synth.layer_tensor(shape, "dh")
+    st = RankState(shape, t, 0, inp)
+    x, dy, h, dh = bf16_dev(inp["x"]), bf16_dev(inp["dy"]), bf16_dev(hb), bf16_dev(dhb)
+    st.attn_fwd(x)
+    st.mlp_fwd(h)
+    st.mlp_bwd(dy, h)
+    st.attn_bwd(dh, x)
+    torch.cuda.synchronize()
+    g = {k: host_f64(getattr(st, k)) for k in ("qkv", "o", "lse", "z", "a", "p_attn", "p_mlp", "p_dh", "p_dx",
+                                               "dw_qkv", "db_qkv", "dw_o", "db_o", "dw1", "db1", "dw2", "db2")}
+    del st
+    torch.cuda.empty_cache()
+
+    p = {k: f64(inp[k]) for k in ("w_qkv", "b_qkv", "w_o", "w1", "b1", "w2")}
+    X, DY, H, DH = f64(inp["x"]), f64(inp["dy"]), f64(hb), f64(dhb)
+    lh = shape.heads // t
+    rows = ROWS
+
+    # attention forward: qkv, o, lse in full; the partial on sampled rows
+    qkv = X @ p["w_qkv"] + p["b_qkv"]
+    assert_bf16("qkv", g["qkv"], qkv)
+    o, lse = L.attention_forward(qkv, lh)
+    assert_bf16("o", g["o"], o)
+    assert_bf16("lse", g["lse"], lse)
+    assert_bf16("attn partial[rows]", g["p_attn"][rows], o[rows] @ p["w_o"])
+
+    # MLP forward on sampled rows
+    z_r = H[rows] @ p["w1"] + p["b1"]
+    a_r = L.gelu(z_r)
+    assert_bf16("z[rows]", g["z"][rows], z_r)
+    assert_bf16("a[rows]", g["a"][rows], a_r)
+    assert_bf16("mlp partial[rows]", g["p_mlp"][rows], a_r @ p["w2"])
+
+    # MLP backward: dgrad partial on sampled rows, weight gradients on sampled columns
+    dz_r = (DY[rows] @ p["w2"].T) * L.gelu_grad(z_r)
+    assert_bf16("dh partial[rows]", g["p_dh"][rows], dz_r @ p["w1"].T)
+    z_full = H @ p["w1"] + p["b1"]
+    a_full = L.gelu(z_full)
+    ch = _cols(shape.hidden)
+    assert_bf16("dw2[:, cols]", g["dw2"][:, ch], a_full.T @ DY[:, ch])
+    cf = _cols(shape.ffn // t)
+    dz_c = (DY @ p["w2"][cf].T) * L.gelu_grad(z_full[:, cf])
+    assert_bf16("dw1[:, cols]", g["dw1"][:, cf], H.T @ dz_c)
+    dz_full = (DY @ p["w2"].T) * L.gelu_grad(z_full)
+    assert_bf16("db1", g["db1"], dz_full.sum(axis=0))
+    assert_bf16("db2", g["db2"], DY.sum(axis=0))
+    del z_full, a_full, dz_full
+
+    # attention backward: dqkv in full (through dx partial rows and its weight gradient)
+    do = DH @ p["w_o"].T
+    dqkv = L.attention_backward(qkv, do, lh)
+    co = _cols(shape.hidden)
+    assert_bf16("dw_o[:, cols]", g["dw_o"][:, co], o.T @ DH[:, co])
+    assert_bf16("db_o", g["db_o"], DH.sum(axis=0))
+    cq = _cols(3 * shape.hidden // t)
+    assert_bf16("dw_qkv[:, cols]", g["dw_qkv"][:, cq], X.T @ dqkv[:, cq])
+    assert_bf16("db_qkv", g["db_qkv"], dqkv.sum(axis=0))
+    assert_bf16("dx partial[rows]", g["p_dx"][rows], dqkv[rows] @ p["w_qkv"].T)
