@@ -8,72 +8,24 @@
 // Layout: Q, K, V of head n are columns [n*3d, n*3d+d), [+d, +2d), [+2d, +3d) of
 // the head-interleaved QKV tensor; O is [tokens, heads*d].
 //
-// CDNA4 design.  All products use v_mfma_f32_32x32x16_bf16.  Scores are formed
-// transposed where the softmax is a row operation (S^T = K Q^T): a lane then owns
-// one query and 16 of the 32 keys of a block, so the row max / row sum are
+// CDNA4 design.  All products use v_mfma_f32_32x32x16_bf16.  Where the softmax
+// is a row operation the scores are formed transposed (S^T = K Q^T): a lane then
+// owns one query and 16 of the 32 keys of a block, so row max / row sum are
 // in-register reductions plus one exchange with lane l^32, and the bf16 P values
 // in the accumulator registers are directly the "b" operand of the next MFMA
 // (the k-slot order of that MFMA is chosen to match the accumulator layout).
-// The "a" operand that pairs with it (V^T, K^T, Q^T or dO^T) is staged in LDS
-// transposed, built with an 8x8 register transpose on the global->LDS path.
-// The backward is two deterministic passes (dK/dV per key block, dQ per query
-// block): no floating-point atomics, bit-identical run to run.
+// The "a" operand that pairs with them (V^T, K^T, Q^T or dO^T) is read straight
+// from the natural-layout tile with ds_read_b64_tr_b16.  Tiles arrive by LDS
+// DMA (buffer_load ... lds) in their global layout, with swizzles that keep
+// every access pattern free of bank conflicts on the 64-bank LDS.  Causal work
+// is balanced by pairing mirrored blocks inside a workgroup; the backward is one
+// fused deterministic pass (no floating-point atomics, bit-identical run to run).
 #include "common.hpp"
 #include "kernels.hpp"
 
 namespace mtl {
 
-// Row swizzle for tiles read both row-wise (lanes = 32 consecutive rows) and
-// written as 8-row blocks: physical chunk = chunk ^ ((row ^ row>>3) & 7).
-__device__ __forceinline__ uint32_t swa(uint32_t row, uint32_t chunk, uint32_t row_bytes) {
-  return row * row_bytes + ((chunk ^ ((row ^ (row >> 3)) & 7u)) << 4);
-}
-
 constexpr float LOG2E = 1.4426950408889634f;
-
-// Load an 8 (rows) x 8 (cols) bf16 block from global memory: rows r0..r0+7
-// (row stride ld, rows >= nrows read as zero), columns c0..c0+7.
-__device__ __forceinline__ void load_block8(const uint16_t* __restrict__ base, int64_t ld, int r0, int nrows,
-                                            int c0, u32x4 (&v)[8]) {
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const int r = r0 + j;
-    v[j] = (r < nrows) ? *reinterpret_cast<const u32x4*>(base + (int64_t)r * ld + c0) : u32x4{0, 0, 0, 0};
-  }
-}
-
-// Write a loaded 8x8 block (rows rg*8.., cols cg*8..) into a natural tile
-// [rows][D] (row bytes 2D) and/or a transposed tile [D][64] (row bytes 128).
-template <int D>
-__device__ __forceinline__ void store_block8(const u32x4 (&v)[8], int rg, int cg, char* nat, char* tr) {
-  if (nat) {
-#pragma unroll
-    for (int j = 0; j < 8; ++j) *reinterpret_cast<u32x4*>(nat + swa(rg * 8 + j, cg, 2 * D)) = v[j];
-  }
-  if (tr) {
-    u32x4 t[8];
-    transpose8x8(v, t);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) *reinterpret_cast<u32x4*>(tr + swa(cg * 8 + i, rg, 128)) = t[i];
-  }
-}
-
-// a-operand fragment from a natural tile: row (l%32 + row0), k-step ks.
-template <int D>
-__device__ __forceinline__ u32x4 frag_nat(const char* tile, int row0, int ks, int lane) {
-  return *reinterpret_cast<const u32x4*>(tile + swa(row0 + (lane & 31), ks * 2 + (lane >> 5), 2 * D));
-}
-
-// a-operand fragment from a transposed tile [D][64]: row = dim (l%32 + dim0);
-// k-slots j map to columns ks*16 + 8*(j/4) + 4*(l/32) + j%4, matching the
-// accumulator layout of a 32x32 MFMA result used as the b operand.
-__device__ __forceinline__ u32x4 frag_tr(const char* tile, int dim0, int ks, int lane) {
-  const int row = dim0 + (lane & 31);
-  const int g = lane >> 5;
-  const u32x2 lo = *reinterpret_cast<const u32x2*>(tile + swa(row, ks * 2, 128) + 8 * g);
-  const u32x2 hi = *reinterpret_cast<const u32x2*>(tile + swa(row, ks * 2 + 1, 128) + 8 * g);
-  return u32x4{lo[0], lo[1], hi[0], hi[1]};
-}
 
 // b-operand from registers r = 8*half .. 8*half+7 of an fp32 32x32 accumulator.
 __device__ __forceinline__ u32x4 pack_half(const f32x16& p, int half) {
@@ -85,92 +37,114 @@ __device__ __forceinline__ u32x4 pack_half(const f32x16& p, int half) {
 __device__ __forceinline__ float xor32(float v) { return __shfl_xor(v, 32); }
 
 // ============================================================== forward
-// Workgroup: 128 queries (4 waves x 32) of one head; key blocks of 64.
+// Work item: 64 queries of one head.  A workgroup (4 waves) takes the mirrored
+// pair of items (p, n-1-p) one after the other, so every workgroup sees the same
+// number of causal key blocks (n+1 of 64 keys).  Within an item, wave w handles
+// queries (w & 1)*32 .. +31 and the key blocks of parity w >> 1; the two
+// parities' online-softmax states are merged through LDS at the end of the item.
+// K and V tiles of two key blocks per stage arrive by LDS DMA in their global
+// layout; V^T fragments for the P.V product are read with ds_read_b64_tr_b16.
+template <int D>
+struct FwdTiles {
+  static constexpr int RB = 2 * D;              // bytes per key row
+  static constexpr int TILE = 64 * RB;          // one 64-key K or V tile
+  static constexpr int STAGE = 4 * TILE;        // K(even) V(even) K(odd) V(odd)
+  static constexpr int PER_TILE = TILE / 1024;  // DMA wave instructions per tile
+  static constexpr int PER_WAVE = 4 * PER_TILE / 4;
+  // 64-bank swizzles: K rows are read 16 rows per cycle (ds_read_b128), V rows
+  // 4 at a time by the transpose read; both maps are bijections on a row.
+  static __device__ __forceinline__ int kswz(int row) { return D == 128 ? (row & 15) : ((row >> 1) & 7); }
+  static __device__ __forceinline__ int vswz(int row) { return D == 128 ? ((row & 3) << 2) : (((row >> 1) & 1) << 2); }
+
+  // DMA the K and V tiles of key blocks kb0 and kb0+1 (64 keys each).
+  static __device__ __forceinline__ void load(i32x4 rs, int64_t ld, int64_t tok0, int colq, int kb0, LDS_AS char* st) {
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+#pragma unroll
+    for (int q = 0; q < PER_WAVE; ++q) {
+      const int I = wave * PER_WAVE + q;
+      const int tile = I / PER_TILE;            // 0 K even, 1 V even, 2 K odd, 3 V odd
+      const int o = (I % PER_TILE) * 1024 + lane * 16;
+      const int row = o / RB;
+      const int pc = (o % RB) >> 4;
+      const bool isv = tile & 1;
+      const int c = pc ^ (isv ? vswz(row) : kswz(row));
+      const int key = (kb0 + (tile >> 1)) * 64 + row;
+      const uint32_t voff = (uint32_t)(((tok0 + key) * ld + colq + (isv ? 2 * D : D) + c * 8) * 2);
+      dma16(rs, voff, 0u, lds_addr(st + I * 1024));
+    }
+  }
+  // a-operand fragment of K (rows = keys row0 + l%32, 8 dims of k step ks)
+  static __device__ __forceinline__ u32x4 kfrag(const LDS_AS char* k, int row0, int ks, int lane) {
+    const int row = row0 + (lane & 31);
+    const int c = ks * 2 + (lane >> 5);
+    return *reinterpret_cast<const LDS_AS u32x4*>(k + row * RB + ((c ^ kswz(row)) << 4));
+  }
+  // a-operand fragment of V^T (rows = dims i*32 + l%32); its k slots are keys
+  // ks*16 + 8*(j/4) + 4*(l/32) + j%4, the order of a 32x32 accumulator's rows.
+  static __device__ __forceinline__ u32x4 vfrag(const LDS_AS char* v, int i, int ks, int lane) {
+    const int G = lane >> 4, R = (lane >> 2) & 3, c4 = lane & 3;
+    const int key = ks * 16 + 4 * (G >> 1) + R;
+    const int dim = i * 32 + (G & 1) * 16 + 4 * c4;
+    const LDS_AS char* p = v + key * RB + (((dim >> 3) ^ vswz(key)) << 4) + ((dim & 7) >> 2) * 8;
+    const u32x2 lo = read_tr(p);
+    const u32x2 hi = read_tr(p + 8 * RB);
+    return u32x4{lo[0], lo[1], hi[0], hi[1]};
+  }
+};
+
 template <int D>
 __global__ __launch_bounds__(256, 1) void attn_fwd_kernel(AttnArgs a) {
-  constexpr int KS = D / 16;       // k-steps over the head dimension
-  constexpr int DB = D / 32;       // 32-row blocks of the head dimension
-  constexpr int KT = 64 * 2 * D;   // bytes of the natural K tile
-  constexpr int VT = D * 128;      // bytes of the transposed V tile
-  __shared__ __attribute__((aligned(16))) char smem[2 * (KT + VT)];
+  using T = FwdTiles<D>;
+  constexpr int KS = D / 16;
+  constexpr int DB = D / 32;
+  __shared__ __attribute__((aligned(1024))) char st0_[T::STAGE];
+  __shared__ __attribute__((aligned(1024))) char st1_[T::STAGE];
+  LDS_AS char* st0 = (LDS_AS char*)st0_;
+  LDS_AS char* st1 = (LDS_AS char*)st1_;
 
-  const int nqb = (a.seq + 127) / 128;
-  const int qb = nqb - 1 - blockIdx.x;  // heaviest blocks first
   const int n = blockIdx.y, b = blockIdx.z;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, g = lane >> 5;
-  const int tid = threadIdx.x;
+  const int qsub = wave & 1, kpar = wave >> 1;
+  const int64_t tokens = (int64_t)a.seq * a.batch;
   const int64_t tok0 = (int64_t)b * a.seq;
-  const uint16_t* qbase = a.qkv + tok0 * a.ld_qkv + (int64_t)n * 3 * D;
-  const uint16_t* kbase = qbase + D;
-  const uint16_t* vbase = qbase + 2 * D;
-
-  const int q0 = qb * 128;
-  const int qw = q0 + wave * 32;     // this wave's first query
-  const int q = qw + (lane & 31);    // this lane's query
+  const int colq = n * 3 * D;
+  const uint16_t* qbase = a.qkv + tok0 * a.ld_qkv + colq;
   const float c = a.scale * LOG2E;
+  const i32x4 rs = make_rsrc(a.qkv, (uint32_t)(tokens * a.ld_qkv * 2));
+  const int nitems = (a.seq + 63) / 64;
+  const int nkb_all = (a.seq + 63) / 64;
 
-  // Q fragments (b operand): lane -> query, 8 dims per k-step.
-  u32x4 qf[KS];
+  for (int side = 0; side < 2; ++side) {
+    const int item = side == 0 ? (int)blockIdx.x : nitems - 1 - (int)blockIdx.x;
+    if (side == 1 && item == (int)blockIdx.x) break;
+    const int q0 = item * 64;
+    const int qw = q0 + qsub * 32;
+    const int q = qw + (lane & 31);
+    const bool qok = q < a.seq;
+    const int nkb = min(item + 1, nkb_all);
+    const int niter = (nkb + 1) / 2;
+
+    u32x4 qf[KS];
 #pragma unroll
-  for (int ks = 0; ks < KS; ++ks)
-    qf[ks] = (q < a.seq) ? *reinterpret_cast<const u32x4*>(qbase + (int64_t)q * a.ld_qkv + ks * 16 + g * 8)
-                         : u32x4{0, 0, 0, 0};
-
-  f32x16 o[DB];
+    for (int ks = 0; ks < KS; ++ks)
+      qf[ks] = qok ? *reinterpret_cast<const u32x4*>(qbase + (int64_t)q * a.ld_qkv + ks * 16 + g * 8)
+                   : u32x4{0, 0, 0, 0};
+    f32x16 o[DB];
 #pragma unroll
-  for (int i = 0; i < DB; ++i) o[i] = f32x16{};
-  float m = -INFINITY, l = 0.f;
+    for (int i = 0; i < DB; ++i) o[i] = f32x16{};
+    float m = -INFINITY, l = 0.f;
 
-  // Loader roles: K natural tile as 16-byte chunks; V^T via 8x8 blocks.
-  constexpr int KCH = 64 * D / 8;               // 16-byte chunks in the K tile
-  constexpr int KPT = KCH / 256;                // chunks per thread
-  constexpr int VBL = 64 * D / 64;              // 8x8 blocks in the V tile
-  u32x4 kreg[KPT];
-  u32x4 vreg[8];
-  const int kmax = min(a.seq, q0 + 128);        // keys needed by this block
-  const int nkb = (kmax + 63) / 64;
-
-  auto gload = [&](int kb) {
-    const int k0 = kb * 64;
-#pragma unroll
-    for (int i = 0; i < KPT; ++i) {
-      const int ch = tid + 256 * i;
-      const int r = ch / (D / 8), cc = ch % (D / 8);
-      const int key = k0 + r;
-      kreg[i] = key < a.seq ? *reinterpret_cast<const u32x4*>(kbase + (int64_t)key * a.ld_qkv + cc * 8)
-                            : u32x4{0, 0, 0, 0};
-    }
-    if (tid < VBL) load_block8(vbase, a.ld_qkv, k0 + (tid & 7) * 8, a.seq, (tid >> 3) * 8, vreg);
-  };
-  auto lstore = [&](int buf) {
-    char* kt = smem + buf * (KT + VT);
-    char* vt = kt + KT;
-#pragma unroll
-    for (int i = 0; i < KPT; ++i) {
-      const int ch = tid + 256 * i;
-      const int r = ch / (D / 8), cc = ch % (D / 8);
-      *reinterpret_cast<u32x4*>(kt + swa(r, cc, 2 * D)) = kreg[i];
-    }
-    if (tid < VBL) store_block8<D>(vreg, tid & 7, tid >> 3, nullptr, vt);
-  };
-
-  gload(0);
-  lstore(0);
-  __syncthreads();
-
-  for (int kb = 0; kb < nkb; ++kb) {
-    const char* kt = smem + (kb & 1) * (KT + VT);
-    const char* vt = kt + KT;
-    if (kb + 1 < nkb) gload(kb + 1);
-    const int k0 = kb * 64;
-    if (k0 <= qw + 31) {
-      // S^T blocks: keys k0 + 32*sb + row, query = lane column.
+    // one key block from the K and V tiles of this wave's parity in stage st
+    auto block = [&](const LDS_AS char* st, int kb) {
+      const LDS_AS char* kt = st + kpar * 2 * T::TILE;
+      const LDS_AS char* vt = kt + T::TILE;
+      const int k0 = kb * 64;
       f32x16 s[2] = {f32x16{}, f32x16{}};
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
+      for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
-        for (int sb = 0; sb < 2; ++sb) s[sb] = mfma32(frag_nat<D>(kt, sb * 32, ks, lane), qf[ks], s[sb]);
-      }
+        for (int sb = 0; sb < 2; ++sb) s[sb] = mfma32(T::kfrag(kt, sb * 32, ks, lane), qf[ks], s[sb]);
       const bool diag = (k0 + 63 > qw);
       float mx = m;
 #pragma unroll
@@ -184,47 +158,85 @@ __global__ __launch_bounds__(256, 1) void attn_fwd_kernel(AttnArgs a) {
       mx = fmaxf(mx, xor32(mx));
       const float alpha = exp2f((m - mx) * c);
       const float mc = mx * c;
-      float rs = 0.f;
+      float rsum = 0.f;
 #pragma unroll
       for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const float p = exp2f(s[sb][r] * c - mc);
-          s[sb][r] = p;
-          rs += p;
+          const float pv = exp2f(s[sb][r] * c - mc);
+          s[sb][r] = pv;
+          rsum += pv;
         }
-      l = l * alpha + rs;
+      l = l * alpha + rsum;
       m = mx;
 #pragma unroll
       for (int i = 0; i < DB; ++i) o[i] *= alpha;
-      // O^T[dim][q] += V^T[dim][key] P^T[key][q]
 #pragma unroll
-      for (int sb = 0; sb < 2; ++sb)
+      for (int ks = 0; ks < 4; ++ks) {
+        const u32x4 pb = pack_half(s[ks >> 1], ks & 1);
 #pragma unroll
-        for (int hf = 0; hf < 2; ++hf) {
-          const u32x4 pb = pack_half(s[sb], hf);
-#pragma unroll
-          for (int i = 0; i < DB; ++i) o[i] = mfma32(frag_tr(vt, i * 32, sb * 2 + hf, lane), pb, o[i]);
-        }
-    }
-    if (kb + 1 < nkb) lstore((kb + 1) & 1);
-    __syncthreads();
-  }
-
-  const float lt = l + xor32(l);
-  if (q < a.seq) {
-    const float inv = 1.f / lt;
-    uint16_t* orow = a.o + (tok0 + q) * a.ld_o + (int64_t)n * D;
-#pragma unroll
-    for (int i = 0; i < DB; ++i)
-#pragma unroll
-      for (int gg = 0; gg < 4; ++gg) {
-        const int dim = i * 32 + 8 * gg + 4 * g;
-        *reinterpret_cast<u32x2*>(orow + dim) =
-            u32x2{pack_bf16x2(o[i][4 * gg] * inv, o[i][4 * gg + 1] * inv),
-                  pack_bf16x2(o[i][4 * gg + 2] * inv, o[i][4 * gg + 3] * inv)};
+        for (int i = 0; i < DB; ++i) o[i] = mfma32(T::vfrag(vt, i, ks, lane), pb, o[i]);
       }
-    if (g == 0) a.lse[(int64_t)n * (a.seq * a.batch) + tok0 + q] = m * a.scale + logf(lt);
+    };
+
+    T::load(rs, a.ld_qkv, tok0, colq, 0, st0);
+    wait_dma();
+    __syncthreads();
+    for (int it = 0; it < niter; it += 2) {
+      const bool more1 = it + 1 < niter;
+      if (more1) T::load(rs, a.ld_qkv, tok0, colq, 2 * (it + 1), st1);
+      {
+        const int kb = 2 * it + kpar;
+        if (kb < nkb && kb * 64 <= qw + 31) block(st0, kb);
+      }
+      if (more1) wait_dma();
+      __syncthreads();
+      if (more1) {
+        const bool more2 = it + 2 < niter;
+        if (more2) T::load(rs, a.ld_qkv, tok0, colq, 2 * (it + 2), st0);
+        const int kb = 2 * (it + 1) + kpar;
+        if (kb < nkb && kb * 64 <= qw + 31) block(st1, kb);
+        if (more2) wait_dma();
+        __syncthreads();
+      }
+    }
+
+    // merge the odd-parity waves' state into the even ones (stage 0 is free)
+    float* mg = reinterpret_cast<float*>((char*)st0_) + qsub * (2 + 16 * DB) * 64;
+    if (kpar == 1) {
+      mg[lane] = m;
+      mg[64 + lane] = l;
+#pragma unroll
+      for (int i = 0; i < DB; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mg[(2 + i * 16 + r) * 64 + lane] = o[i][r];
+    }
+    __syncthreads();
+    if (kpar == 0) {
+      const float m2 = mg[lane], l2 = mg[64 + lane];
+      const float mt = fmaxf(m, m2);
+      const float a1 = exp2f((m - mt) * c), a2 = exp2f((m2 - mt) * c);
+      const float lp = l * a1 + l2 * a2;
+      const float lt = lp + xor32(lp);
+      if (qok) {
+        const float inv = 1.f / lt;
+        uint16_t* orow = a.o + (tok0 + q) * a.ld_o + (int64_t)n * D;
+#pragma unroll
+        for (int i = 0; i < DB; ++i) {
+          float v[16];
+#pragma unroll
+          for (int r = 0; r < 16; ++r) v[r] = (o[i][r] * a1 + mg[(2 + i * 16 + r) * 64 + lane] * a2) * inv;
+#pragma unroll
+          for (int gg = 0; gg < 4; ++gg) {
+            const int dim = i * 32 + 8 * gg + 4 * g;
+            *reinterpret_cast<u32x2*>(orow + dim) =
+                u32x2{pack_bf16x2(v[4 * gg], v[4 * gg + 1]), pack_bf16x2(v[4 * gg + 2], v[4 * gg + 3])};
+          }
+        }
+        if (g == 0) a.lse[(int64_t)n * tokens + tok0 + q] = mt * a.scale + logf(lt);
+      }
+    }
+    __syncthreads();  // the next item's DMA reuses stage 0
   }
 }
 
@@ -249,282 +261,277 @@ __global__ __launch_bounds__(256) void attn_delta_kernel(AttnArgs a) {
   if (lane == 0) a.delta[(int64_t)n * tokens + tok] = acc;
 }
 
-// ============================================================== backward: dK, dV
-// Workgroup: 128 keys (4 waves x 32) of one head; query blocks of 64.
+// ============================================================== backward
+// One fused, balanced, deterministic pass.  Workgroup w (4 waves) computes
+//   part 1: dK and dV of key block w (64 keys), over query blocks w .. n-1;
+//   part 2: dQ of query block w (64 queries), over key blocks 0 .. w;
+// (n - w) + (w + 1) = n + 1 block steps for every workgroup.  Each 64 x 64 block
+// step is split in 32 x 32 quarters over the waves; the two partial sums of each
+// output quarter are added through LDS at the end of a part (fixed order, no
+// atomics).  One LDS stage of <= 65 KB and <= 256 VGPRs let two workgroups share
+// a CU.  Tiles arrive by LDS DMA in their global layout; Q, dO and K tiles are
+// read both row-wise (ds_read_b128) and transposed (ds_read_b64_tr_b16).
 template <int D>
-__global__ __launch_bounds__(256, 1) void attn_bwd_kv_kernel(AttnArgs a) {
+struct BwdTiles {
+  static constexpr int RB = 2 * D;
+  static constexpr int TILE = 64 * RB;
+  static constexpr int PER_TILE = TILE / 1024;
+  // one swizzle that keeps both access patterns bank-conflict free on 64 banks
+  static __device__ __forceinline__ int swz(int r) {
+    return D == 128 ? (((r & 3) << 2) | ((r >> 2) & 3)) : ((((r >> 1) & 1) << 2) | ((r >> 2) & 3));
+  }
+  // DMA of ntiles 64-row tiles: tile i = rows [row0, row0+64) of column block
+  // cols[i] of src[i] (row stride ld[i]) into dst + i*TILE.
+  static __device__ __forceinline__ void load(int ntiles, const i32x4* rs, const int64_t* ld, const int64_t* col,
+                                              int64_t row0, LDS_AS char* dst) {
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int per_wave = ntiles * PER_TILE / 4;
+    for (int q = 0; q < per_wave; ++q) {
+      const int I = wave * per_wave + q;
+      const int t = I / PER_TILE;
+      const int o = (I % PER_TILE) * 1024 + lane * 16;
+      const int row = o / RB;
+      const int c = ((o % RB) >> 4) ^ swz(row);
+      const uint32_t voff = (uint32_t)(((row0 + row) * ld[t] + col[t] + c * 8) * 2);
+      dma16(rs[t], voff, 0u, lds_addr(dst + I * 1024));
+    }
+  }
+  // row fragment: rows row0 + l%32, 8 columns of k step ks
+  static __device__ __forceinline__ u32x4 rfrag(const LDS_AS char* t, int row0, int ks, int lane) {
+    const int row = row0 + (lane & 31);
+    const int c = ks * 2 + (lane >> 5);
+    return *reinterpret_cast<const LDS_AS u32x4*>(t + row * RB + ((c ^ swz(row)) << 4));
+  }
+  // transposed fragment: rows = columns i*32 + l%32 of the tile; k slots = tile
+  // rows r0 + ks*16 + 8*(j/4) + 4*(l/32) + j%4 (a 32x32 accumulator's row order)
+  static __device__ __forceinline__ u32x4 tfrag(const LDS_AS char* t, int r0, int i, int ks, int lane) {
+    const int G = lane >> 4, R = (lane >> 2) & 3, c4 = lane & 3;
+    const int row = r0 + ks * 16 + 4 * (G >> 1) + R;
+    const int col = i * 32 + (G & 1) * 16 + 4 * c4;
+    const int off = ((col & 7) >> 2) * 8;
+    const u32x2 lo = read_tr(t + row * RB + (((col >> 3) ^ swz(row)) << 4) + off);
+    const u32x2 hi = read_tr(t + (row + 8) * RB + (((col >> 3) ^ swz(row + 8)) << 4) + off);
+    return u32x4{lo[0], lo[1], hi[0], hi[1]};
+  }
+};
+
+template <int D>
+__global__ __launch_bounds__(256, 2) void attn_bwd_kernel(AttnArgs a) {
+  using T = BwdTiles<D>;
   constexpr int KS = D / 16;
   constexpr int DB = D / 32;
-  constexpr int NT = 64 * 2 * D;  // natural [64][D] tile bytes
-  constexpr int TT = D * 128;     // transposed [D][64] tile bytes
-  constexpr int STAGE = 2 * NT + 2 * TT + 2 * 64 * 4;
-  __shared__ __attribute__((aligned(16))) char smem[2 * STAGE];
+  // part 1: [K | V | Q | dO] tiles + LSE, D; part 2: [K | V] tiles
+  __shared__ __attribute__((aligned(1024))) char sm_[4 * T::TILE + 2 * 64 * 4];
+  LDS_AS char* sm = (LDS_AS char*)sm_;
+  LDS_AS char* tK = sm;
+  LDS_AS char* tV = sm + T::TILE;
+  LDS_AS char* tQ = sm + 2 * T::TILE;
+  LDS_AS char* tO = sm + 3 * T::TILE;
+  float* sl = reinterpret_cast<float*>(sm_ + 4 * T::TILE);  // [0,64) lse*log2e, [64,128) delta
 
-  const int nkb = (a.seq + 127) / 128;
-  const int kb = blockIdx.x;  // key blocks near the start see the most queries; launch order as is
-  const int n = blockIdx.y, b = blockIdx.z;
+  const int w = blockIdx.x, n = blockIdx.y, b = blockIdx.z;
+  const int nblk = (a.seq + 63) / 64;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, g = lane >> 5;
   const int tid = threadIdx.x;
   const int64_t tokens = (int64_t)a.seq * a.batch;
   const int64_t tok0 = (int64_t)b * a.seq;
-  const uint16_t* qbase = a.qkv + tok0 * a.ld_qkv + (int64_t)n * 3 * D;
-  const uint16_t* kbase = qbase + D;
-  const uint16_t* vbase = qbase + 2 * D;
-  const uint16_t* dobase = a.dout + tok0 * a.ld_o + (int64_t)n * D;
+  const int64_t colq = (int64_t)n * 3 * D, colo = (int64_t)n * D;
+  const float c = a.scale * LOG2E;
+  const i32x4 rq = make_rsrc(a.qkv, (uint32_t)(tokens * a.ld_qkv * 2));
+  const i32x4 ro = make_rsrc(a.dout, (uint32_t)(tokens * a.ld_o * 2));
   const float* lse = a.lse_in + (int64_t)n * tokens + tok0;
   const float* dlt = a.delta + (int64_t)n * tokens + tok0;
-  const float c = a.scale * LOG2E;
-  (void)nkb;
 
-  const int k0 = kb * 128;
-  const int kw = k0 + wave * 32;
-  const int key = kw + (lane & 31);
-
-  // K and V fragments (b operands): lane -> key, 8 dims per k-step.
-  u32x4 kf[KS], vf[KS];
-#pragma unroll
-  for (int ks = 0; ks < KS; ++ks) {
-    const bool ok = key < a.seq;
-    kf[ks] = ok ? *reinterpret_cast<const u32x4*>(kbase + (int64_t)key * a.ld_qkv + ks * 16 + g * 8) : u32x4{0, 0, 0, 0};
-    vf[ks] = ok ? *reinterpret_cast<const u32x4*>(vbase + (int64_t)key * a.ld_qkv + ks * 16 + g * 8) : u32x4{0, 0, 0, 0};
-  }
-  f32x16 dv[DB], dk[DB];
-#pragma unroll
-  for (int i = 0; i < DB; ++i) {
-    dv[i] = f32x16{};
-    dk[i] = f32x16{};
-  }
-
-  // Loader: threads 0..127 take Q blocks, 128..255 dO blocks (8x8 each); the
-  // block count per tensor is 64*D/64 = D (64 or 128).
-  u32x4 reg[8];
-  float sreg = 0.f;
-  const int which = tid >> 7, bt = tid & 127;
-  const bool active = bt < D;
-  const int qstart = (k0 / 64);
-  const int nqb = (a.seq + 63) / 64;
-
-  auto gload = [&](int qb) {
-    const int qq0 = qb * 64;
-    if (active) {
-      const uint16_t* src = which ? dobase : qbase;
-      const int64_t ld = which ? a.ld_o : a.ld_qkv;
-      load_block8(src, ld, qq0 + (bt & 7) * 8, a.seq, (bt >> 3) * 8, reg);
+  // ---------------------------------------------------------------- part 1
+  {
+    const int kh = wave & 1, qh = wave >> 1;
+    const int k0 = w * 64;
+    const int kw = k0 + kh * 32;
+    const int key = kw + (lane & 31);
+    {
+      const i32x4 rs[2] = {rq, rq};
+      const int64_t ld[2] = {a.ld_qkv, a.ld_qkv};
+      const int64_t col[2] = {colq + D, colq + 2 * D};
+      T::load(2, rs, ld, col, tok0 + k0, tK);
     }
-    if (tid < 128) {
-      const int qq = qq0 + (tid & 63);
-      const float* srcf = (tid < 64) ? lse : dlt;
-      sreg = qq < a.seq ? srcf[qq] : 0.f;
+    f32x16 dk[DB], dv[DB];
+#pragma unroll
+    for (int i = 0; i < DB; ++i) {
+      dk[i] = f32x16{};
+      dv[i] = f32x16{};
     }
-  };
-  auto lstore = [&](int buf) {
-    char* st = smem + buf * STAGE;
-    char* qn = st;
-    char* don = st + NT;
-    char* qt = st + 2 * NT;
-    char* dot = qt + TT;
-    float* sf = reinterpret_cast<float*>(dot + TT);
-    if (active) store_block8<D>(reg, bt & 7, bt >> 3, which ? don : qn, which ? dot : qt);
-    if (tid < 128) sf[tid] = sreg;
-  };
-
-  if (qstart < nqb) {
-    gload(qstart);
-    lstore(0);
-  }
-  __syncthreads();
-  for (int qb = qstart; qb < nqb; ++qb) {
-    const int buf = (qb - qstart) & 1;
-    const char* st = smem + buf * STAGE;
-    const char* qn = st;
-    const char* don = st + NT;
-    const char* qt = st + 2 * NT;
-    const char* dot = qt + TT;
-    const float* sl = reinterpret_cast<const float*>(dot + TT);  // [0,64) lse, [64,128) delta
-    if (qb + 1 < nqb) gload(qb + 1);
-    const int qq0 = qb * 64;
-    if (qq0 + 63 >= kw) {
-      // S[q][key] and dP[q][key]: rows = queries (2 blocks of 32), column = key.
-      f32x16 s[2] = {f32x16{}, f32x16{}}, dp[2] = {f32x16{}, f32x16{}};
+    for (int qb = w; qb < nblk; ++qb) {
+      const int q0 = qb * 64;
+      {
+        const i32x4 rs[2] = {rq, ro};
+        const int64_t ld[2] = {a.ld_qkv, a.ld_o};
+        const int64_t col[2] = {colq, colo};
+        T::load(2, rs, ld, col, tok0 + q0, tQ);
+      }
+      if (tid < 128) {
+        const int qq = q0 + (tid & 63);
+        sl[tid] = qq < a.seq ? (tid < 64 ? lse[qq] * LOG2E : dlt[qq]) : 0.f;
+      }
+      wait_dma();
+      __syncthreads();
+      const int qw = q0 + qh * 32;
+      if (qw + 31 >= kw) {
+        // S[q][key], dP[q][key]: rows = this wave's 32 queries, column = key
+        f32x16 sc = f32x16{}, dp = f32x16{};
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks)
-#pragma unroll
-        for (int sb = 0; sb < 2; ++sb) {
-          s[sb] = mfma32(frag_nat<D>(qn, sb * 32, ks, lane), kf[ks], s[sb]);
-          dp[sb] = mfma32(frag_nat<D>(don, sb * 32, ks, lane), vf[ks], dp[sb]);
+        for (int ks = 0; ks < KS; ++ks) {
+          sc = mfma32(T::rfrag(tQ, qh * 32, ks, lane), T::rfrag(tK, kh * 32, ks, lane), sc);
+          dp = mfma32(T::rfrag(tO, qh * 32, ks, lane), T::rfrag(tV, kh * 32, ks, lane), dp);
         }
 #pragma unroll
-      for (int sb = 0; sb < 2; ++sb)
-#pragma unroll
         for (int r4 = 0; r4 < 4; ++r4) {
-          const int qi = sb * 32 + 8 * r4 + 4 * g;  // local query of registers 4*r4 .. 4*r4+3
-          const f32x4 L = *reinterpret_cast<const f32x4*>(sl + qi);
-          const f32x4 Dl = *reinterpret_cast<const f32x4*>(sl + 64 + qi);
+          const int ql = qh * 32 + 8 * r4 + 4 * g;  // local query of registers 4*r4 ..
+          const f32x4 L = *reinterpret_cast<const f32x4*>(sl + ql);
+          const f32x4 Dl = *reinterpret_cast<const f32x4*>(sl + 64 + ql);
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int r = 4 * r4 + e;
-            const int qg = qq0 + qi + e;
-            float p = exp2f(s[sb][r] * c - L[e] * LOG2E);
-            if (key > qg) p = 0.f;
-            s[sb][r] = p;
-            dp[sb][r] = p * (dp[sb][r] - Dl[e]);
+            const int qg = q0 + ql + e;
+            float pv = exp2f(sc[r] * c - L[e]);
+            if (key > qg || qg >= a.seq) pv = 0.f;
+            sc[r] = pv;
+            dp[r] = pv * (dp[r] - Dl[e]);
           }
         }
-      // dV^T[dim][key] += dO^T[dim][q] P[q][key]; dK^T += Q^T dS
-#pragma unroll
-      for (int sb = 0; sb < 2; ++sb)
+        // dV^T[dim][key] += dO^T P ; dK^T[dim][key] += Q^T dS  (k = this wave's 32 queries)
 #pragma unroll
         for (int hf = 0; hf < 2; ++hf) {
-          const u32x4 pb = pack_half(s[sb], hf);
-          const u32x4 sbf = pack_half(dp[sb], hf);
+          const u32x4 pb = pack_half(sc, hf);
+          const u32x4 sb = pack_half(dp, hf);
 #pragma unroll
           for (int i = 0; i < DB; ++i) {
-            dv[i] = mfma32(frag_tr(dot, i * 32, sb * 2 + hf, lane), pb, dv[i]);
-            dk[i] = mfma32(frag_tr(qt, i * 32, sb * 2 + hf, lane), sbf, dk[i]);
+            dv[i] = mfma32(T::tfrag(tO, qh * 32, i, hf, lane), pb, dv[i]);
+            dk[i] = mfma32(T::tfrag(tQ, qh * 32, i, hf, lane), sb, dk[i]);
           }
         }
-    }
-    if (qb + 1 < nqb) lstore(buf ^ 1);
-    __syncthreads();
-  }
-
-  if (key < a.seq) {
-    uint16_t* kout = a.dqkv + (tok0 + key) * a.ld_qkv + (int64_t)n * 3 * D + D;
-    uint16_t* vout = kout + D;
-#pragma unroll
-    for (int i = 0; i < DB; ++i)
-#pragma unroll
-      for (int gg = 0; gg < 4; ++gg) {
-        const int dim = i * 32 + 8 * gg + 4 * g;
-        const f32x16& K = dk[i];
-        const f32x16& V = dv[i];
-        *reinterpret_cast<u32x2*>(kout + dim) =
-            u32x2{pack_bf16x2(K[4 * gg] * a.scale, K[4 * gg + 1] * a.scale),
-                  pack_bf16x2(K[4 * gg + 2] * a.scale, K[4 * gg + 3] * a.scale)};
-        *reinterpret_cast<u32x2*>(vout + dim) =
-            u32x2{pack_bf16x2(V[4 * gg], V[4 * gg + 1]), pack_bf16x2(V[4 * gg + 2], V[4 * gg + 3])};
       }
-  }
-}
-
-// ============================================================== backward: dQ
-// Workgroup: 128 queries (4 waves x 32) of one head; key blocks of 64.
-template <int D>
-__global__ __launch_bounds__(256, 1) void attn_bwd_q_kernel(AttnArgs a) {
-  constexpr int KS = D / 16;
-  constexpr int DB = D / 32;
-  constexpr int NT = 64 * 2 * D;
-  constexpr int TT = D * 128;
-  constexpr int STAGE = 2 * NT + TT;  // K natural, V natural, K^T
-  __shared__ __attribute__((aligned(16))) char smem[2 * STAGE];
-
-  const int nqb = (a.seq + 127) / 128;
-  const int qb = nqb - 1 - blockIdx.x;
-  const int n = blockIdx.y, b = blockIdx.z;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, g = lane >> 5;
-  const int tid = threadIdx.x;
-  const int64_t tokens = (int64_t)a.seq * a.batch;
-  const int64_t tok0 = (int64_t)b * a.seq;
-  const uint16_t* qbase = a.qkv + tok0 * a.ld_qkv + (int64_t)n * 3 * D;
-  const uint16_t* kbase = qbase + D;
-  const uint16_t* vbase = qbase + 2 * D;
-  const uint16_t* dobase = a.dout + tok0 * a.ld_o + (int64_t)n * D;
-  const float c = a.scale * LOG2E;
-
-  const int q0 = qb * 128;
-  const int qw = q0 + wave * 32;
-  const int q = qw + (lane & 31);
-  const bool qok = q < a.seq;
-
-  u32x4 qf[KS], df[KS];
-#pragma unroll
-  for (int ks = 0; ks < KS; ++ks) {
-    qf[ks] = qok ? *reinterpret_cast<const u32x4*>(qbase + (int64_t)q * a.ld_qkv + ks * 16 + g * 8) : u32x4{0, 0, 0, 0};
-    df[ks] = qok ? *reinterpret_cast<const u32x4*>(dobase + (int64_t)q * a.ld_o + ks * 16 + g * 8) : u32x4{0, 0, 0, 0};
-  }
-  const float L2 = qok ? a.lse_in[(int64_t)n * tokens + tok0 + q] * LOG2E : 0.f;
-  const float Dq = qok ? a.delta[(int64_t)n * tokens + tok0 + q] : 0.f;
-
-  f32x16 dq[DB];
-#pragma unroll
-  for (int i = 0; i < DB; ++i) dq[i] = f32x16{};
-
-  u32x4 reg[8];
-  const int which = tid >> 7, bt = tid & 127;
-  const bool active = bt < D;
-  const int kmax = min(a.seq, q0 + 128);
-  const int nkb = (kmax + 63) / 64;
-
-  auto gload = [&](int kb) {
-    if (active) load_block8(which ? vbase : kbase, a.ld_qkv, kb * 64 + (bt & 7) * 8, a.seq, (bt >> 3) * 8, reg);
-  };
-  auto lstore = [&](int buf) {
-    char* st = smem + buf * STAGE;
-    if (active) {
-      if (which == 0) store_block8<D>(reg, bt & 7, bt >> 3, st, st + 2 * NT);
-      else store_block8<D>(reg, bt & 7, bt >> 3, st + NT, nullptr);
+      __syncthreads();
     }
-  };
-
-  gload(0);
-  lstore(0);
-  __syncthreads();
-  for (int kb = 0; kb < nkb; ++kb) {
-    const char* st = smem + (kb & 1) * STAGE;
-    const char* kn = st;
-    const char* vn = st + NT;
-    const char* kt = st + 2 * NT;
-    if (kb + 1 < nkb) gload(kb + 1);
-    const int k0 = kb * 64;
-    if (k0 <= qw + 31) {
-      f32x16 s[2] = {f32x16{}, f32x16{}}, dp[2] = {f32x16{}, f32x16{}};
+    // add the qh = 1 partials to qh = 0 through LDS (the tiles are free now)
+    float* mg = reinterpret_cast<float*>(sm_) + kh * (2 * DB * 16 * 64);
+    if (qh == 1) {
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks)
-#pragma unroll
-        for (int sb = 0; sb < 2; ++sb) {
-          s[sb] = mfma32(frag_nat<D>(kn, sb * 32, ks, lane), qf[ks], s[sb]);
-          dp[sb] = mfma32(frag_nat<D>(vn, sb * 32, ks, lane), df[ks], dp[sb]);
-        }
-#pragma unroll
-      for (int sb = 0; sb < 2; ++sb)
+      for (int i = 0; i < DB; ++i)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int key = k0 + sb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
-          float p = exp2f(s[sb][r] * c - L2);
-          if (key > q) p = 0.f;
-          dp[sb][r] = p * (dp[sb][r] - Dq);
-        }
-#pragma unroll
-      for (int sb = 0; sb < 2; ++sb)
-#pragma unroll
-        for (int hf = 0; hf < 2; ++hf) {
-          const u32x4 sbf = pack_half(dp[sb], hf);
-#pragma unroll
-          for (int i = 0; i < DB; ++i) dq[i] = mfma32(frag_tr(kt, i * 32, sb * 2 + hf, lane), sbf, dq[i]);
+          mg[(i * 16 + r) * 64 + lane] = dk[i][r];
+          mg[((DB + i) * 16 + r) * 64 + lane] = dv[i][r];
         }
     }
-    if (kb + 1 < nkb) lstore((kb + 1) & 1);
+    __syncthreads();
+    if (qh == 0 && key < a.seq) {
+      uint16_t* kout = a.dqkv + (tok0 + key) * a.ld_qkv + colq + D;
+      uint16_t* vout = kout + D;
+#pragma unroll
+      for (int i = 0; i < DB; ++i)
+#pragma unroll
+        for (int gg = 0; gg < 4; ++gg) {
+          const int dim = i * 32 + 8 * gg + 4 * g;
+          float kv[4], vv[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int r = 4 * gg + e;
+            kv[e] = (dk[i][r] + mg[(i * 16 + r) * 64 + lane]) * a.scale;
+            vv[e] = dv[i][r] + mg[((DB + i) * 16 + r) * 64 + lane];
+          }
+          *reinterpret_cast<u32x2*>(kout + dim) = u32x2{pack_bf16x2(kv[0], kv[1]), pack_bf16x2(kv[2], kv[3])};
+          *reinterpret_cast<u32x2*>(vout + dim) = u32x2{pack_bf16x2(vv[0], vv[1]), pack_bf16x2(vv[2], vv[3])};
+        }
+    }
     __syncthreads();
   }
 
-  if (qok) {
-    uint16_t* qout = a.dqkv + (tok0 + q) * a.ld_qkv + (int64_t)n * 3 * D;
+  // ---------------------------------------------------------------- part 2
+  {
+    const int qh = wave & 1, kh = wave >> 1;
+    const int q0 = w * 64;
+    const int qw = q0 + qh * 32;
+    const int q = qw + (lane & 31);
+    const bool qok = q < a.seq;
+    const uint16_t* qrow = a.qkv + (tok0 + q) * a.ld_qkv + colq;
+    const uint16_t* orow = a.dout + (tok0 + q) * a.ld_o + colo;
+    u32x4 qf[KS], df[KS];
 #pragma unroll
-    for (int i = 0; i < DB; ++i)
+    for (int ks = 0; ks < KS; ++ks) {
+      qf[ks] = qok ? *reinterpret_cast<const u32x4*>(qrow + ks * 16 + g * 8) : u32x4{0, 0, 0, 0};
+      df[ks] = qok ? *reinterpret_cast<const u32x4*>(orow + ks * 16 + g * 8) : u32x4{0, 0, 0, 0};
+    }
+    const float L2 = qok ? lse[q] * LOG2E : 0.f;
+    const float Dq = qok ? dlt[q] : 0.f;
+    f32x16 dq[DB];
 #pragma unroll
-      for (int gg = 0; gg < 4; ++gg) {
-        const int dim = i * 32 + 8 * gg + 4 * g;
-        *reinterpret_cast<u32x2*>(qout + dim) =
-            u32x2{pack_bf16x2(dq[i][4 * gg] * a.scale, dq[i][4 * gg + 1] * a.scale),
-                  pack_bf16x2(dq[i][4 * gg + 2] * a.scale, dq[i][4 * gg + 3] * a.scale)};
+    for (int i = 0; i < DB; ++i) dq[i] = f32x16{};
+    for (int kb = 0; kb <= w; ++kb) {
+      const int k0 = kb * 64;
+      {
+        const i32x4 rs[2] = {rq, rq};
+        const int64_t ld[2] = {a.ld_qkv, a.ld_qkv};
+        const int64_t col[2] = {colq + D, colq + 2 * D};
+        T::load(2, rs, ld, col, tok0 + k0, tK);
       }
+      wait_dma();
+      __syncthreads();
+      const int kw = k0 + kh * 32;
+      if (kw <= qw + 31) {
+        // S^T[key][q], dP^T[key][q]: rows = this wave's 32 keys, column = query
+        f32x16 sc = f32x16{}, dp = f32x16{};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          sc = mfma32(T::rfrag(tK, kh * 32, ks, lane), qf[ks], sc);
+          dp = mfma32(T::rfrag(tV, kh * 32, ks, lane), df[ks], dp);
+        }
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int kk = kw + 8 * (r >> 2) + 4 * g + (r & 3);
+          float pv = exp2f(sc[r] * c - L2);
+          if (kk > q || !qok) pv = 0.f;
+          dp[r] = pv * (dp[r] - Dq);
+        }
+        // dQ^T[dim][q] += K^T dS^T (k = this wave's 32 keys)
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf) {
+          const u32x4 sb = pack_half(dp, hf);
+#pragma unroll
+          for (int i = 0; i < DB; ++i) dq[i] = mfma32(T::tfrag(tK, kh * 32, i, hf, lane), sb, dq[i]);
+        }
+      }
+      __syncthreads();
+    }
+    float* mg = reinterpret_cast<float*>(sm_) + qh * (DB * 16 * 64);
+    if (kh == 1) {
+#pragma unroll
+      for (int i = 0; i < DB; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mg[(i * 16 + r) * 64 + lane] = dq[i][r];
+    }
+    __syncthreads();
+    if (kh == 0 && qok) {
+      uint16_t* qout = a.dqkv + (tok0 + q) * a.ld_qkv + colq;
+#pragma unroll
+      for (int i = 0; i < DB; ++i)
+#pragma unroll
+        for (int gg = 0; gg < 4; ++gg) {
+          const int dim = i * 32 + 8 * gg + 4 * g;
+          float v[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v[e] = (dq[i][4 * gg + e] + mg[(i * 16 + 4 * gg + e) * 64 + lane]) * a.scale;
+          *reinterpret_cast<u32x2*>(qout + dim) = u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+        }
+    }
   }
 }
 
 // ============================================================== launchers
 template <int D>
 static hipError_t fwd_d(const AttnArgs& a, hipStream_t s) {
-  dim3 grid((a.seq + 127) / 128, a.heads, a.batch);
+  const int nitems = (a.seq + 63) / 64;
+  dim3 grid((nitems + 1) / 2, a.heads, a.batch);
   hipLaunchKernelGGL(attn_fwd_kernel<D>, grid, dim3(256), 0, s, a);
   return hipGetLastError();
 }
@@ -535,11 +542,8 @@ static hipError_t bwd_d(const AttnArgs& a, hipStream_t s) {
   hipLaunchKernelGGL(attn_delta_kernel<D>, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  dim3 grid((a.seq + 127) / 128, a.heads, a.batch);
-  hipLaunchKernelGGL(attn_bwd_kv_kernel<D>, grid, dim3(256), 0, s, a);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(attn_bwd_q_kernel<D>, grid, dim3(256), 0, s, a);
+  dim3 grid((a.seq + 63) / 64, a.heads, a.batch);
+  hipLaunchKernelGGL(attn_bwd_kernel<D>, grid, dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

@@ -33,42 +33,7 @@
 #include "common.hpp"
 #include "kernels.hpp"
 
-#define LDS_AS __attribute__((address_space(3)))
-#define GLB_AS __attribute__((address_space(1)))
-
 namespace mtl {
-
-typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-
-__device__ __forceinline__ u32x2 read_tr(const LDS_AS char* p) {
-  return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4*)p));
-}
-
-typedef int i32x4 __attribute__((ext_vector_type(4)));
-
-// A raw buffer resource over [base, base + bytes): loads past the end return 0.
-__device__ __forceinline__ i32x4 make_rsrc(const void* base, uint32_t bytes) {
-  const uint64_t b = reinterpret_cast<uint64_t>(base);
-  return i32x4{(int)(uint32_t)b, (int)(uint32_t)(b >> 32), (int)bytes, 0x00020000};
-}
-
-// 16 bytes per lane from buffer offset voff + soff into LDS at lds + 16*lane
-// (buffer_load_dwordx4 ... lds; the LDS base travels in M0).  Issued as inline
-// assembly so that the compiler does not fence every later LDS read on it: the
-// caller waits (vmcnt) before the barrier that publishes the slab.  M0 is
-// saved and restored; s_nop covers the M0 -> LDS-DMA hazard.
-__device__ __forceinline__ void dma16(i32x4 rsrc, uint32_t voff, uint32_t soff, uint32_t lds) {
-  uint32_t saved;
-  asm volatile(
-      "s_mov_b32 %0, m0\n\t"
-      "s_mov_b32 m0, %1\n\t"
-      "s_nop 0\n\t"
-      "buffer_load_dwordx4 %2, %3, %4 offen lds\n\t"
-      "s_mov_b32 m0, %0"
-      : "=&s"(saved)
-      : "s"(lds), "v"(voff), "s"(rsrc), "s"(soff)
-      : "memory");
-}
 
 // LDS swizzles, for gfx950's 64 x 4-byte banks (ds_read_b128 serves 16 lanes per
 // cycle, ds_read_b64_tr_b16 32 lanes per cycle):
