@@ -86,7 +86,9 @@ const char* mtl_status_str(mtl_status s);
  * tutorial's section 2.2: 3 heads on TP 8 is an error; section 4.2: 768/12 on
  * TP 2 is legal); 0 <= rank < tp; d = hidden/heads in {64, 128} and
  * (ffn/tp) % 8 == 0 (MTL_E_SHAPE otherwise: the attention kernels are built for
- * those head sizes and the GEMMs move 16-byte vectors); tp <= 16. */
+ * those head sizes and the GEMMs move 16-byte vectors); tp <= 16; every GEMM
+ * operand under 4 GiB: (max(S, w) + 256) * w * 2 < 2^32 bytes with
+ * w = max(h, 3h/t, f/t). */
 mtl_status mtl_validate(const mtl_layer_cfg* cfg);
 
 /* Bytes of device scratch the backward calls need (*scratch_bytes) for this
@@ -149,6 +151,92 @@ mtl_status mtl_attn_bwd(const mtl_layer_cfg* cfg, const void* dh, const void* x,
                         const float* lse, const void* w_qkv, const void* w_o, void* dx_partial, float* dw_qkv,
                         float* db_qkv, float* dw_o, float* db_o, void* scratch, size_t scratch_bytes,
                         mtl_stream_t stream);
+
+/* ------------------------------------------------------------------------
+ * MoE expert block of one expert-parallel rank.
+ *
+ * The site summary's MoE deploy step (navi2ai.com/sites/1106, step 6) runs 256
+ * experts with a top-8 router on expert-parallel size 16, and the guide's table
+ * of parallel strategies (ai.lansai.wang/82226) names the grouped GEMM as the
+ * MoE compute path.  The pages print no router formula; this library reads it
+ * as: the k largest fp32 logits of a token (ties to the lower expert id, slots
+ * in decreasing-logit order), gates = softmax over those k logits, no capacity
+ * limit (dropless), rank r of ep owning experts [r*E/ep, (r+1)*E/ep).  The
+ * rank's assignments are grouped by expert with tokens ascending; each expert
+ * is GeLU(x W1_e) W2_e without biases; a token's output is the gate-weighted
+ * sum of its local experts' rows in slot order -- the rank's partial of the
+ * combine (the all-to-all that brings the other ranks' experts is not part of
+ * this library).
+ *
+ * Sizes: T = tokens, h = hidden, f = ffn, E = experts, k = topk,
+ * E_l = E/ep local experts, N = number of local assignments (offsets[E_l]),
+ * N_max = T * min(k, E_l) -- the most N can be, which sizes every per-row
+ * buffer (rows past N are never touched).  Expert weights are stored
+ * w1 [E_l, h, f] and w2 [E_l, f, h] bf16; their gradients fp32 of the same shape.
+ * Integer outputs (ids, counts, offsets, permutation) are exact and
+ * deterministic; so is every floating-point output from run to run.
+ * ---------------------------------------------------------------------- */
+
+/* --num-experts, --moe-router-topk, --expert-model-parallel-size and this
+ * process's EP rank; tokens = micro-batch x sequence length. */
+typedef struct mtl_moe_cfg {
+  int32_t tokens, hidden, ffn, experts, topk, ep, rank;
+  int32_t precision; /* MTL_PREC_BF16 only */
+  int32_t flags;     /* MTL_F_WGRAD_ACCUM or 0 */
+} mtl_moe_cfg;
+
+/* Host-only check; makes no HIP call.  Every size > 0; experts % ep == 0
+ * (MTL_E_DIVISIBILITY); 0 <= rank < ep (MTL_E_RANK); hidden % 8 == 0,
+ * ffn % 8 == 0, experts <= 1024, topk <= min(experts, 64), tokens * topk < 2^31,
+ * (max(N_max, w) + 256) * w * 2 < 2^32 bytes with w = max(h, f) (MTL_E_SHAPE). */
+mtl_status mtl_moe_validate(const mtl_moe_cfg* cfg);
+
+/* N_max = tokens * min(topk, experts/ep): rows of xp, z, a, ye and of the
+ * backward scratch; and the backward's scratch bytes.  Either output may be NULL. */
+mtl_status mtl_moe_sizes(const mtl_moe_cfg* cfg, int64_t* max_rows, size_t* scratch_bytes);
+
+/* Router selection: logits [T, E] fp32 -> topk_idx [T, k] int32, gates [T, k]
+ * fp32 (softmax of the selected logits, computed in fp32).  Logits must not be NaN. */
+mtl_status mtl_moe_route(const mtl_moe_cfg* cfg, const float* logits, int32_t* topk_idx, float* gates,
+                         mtl_stream_t stream);
+
+/* Stable grouping of this rank's assignments by local expert:
+ *   counts   [E_l]     assignments per local expert
+ *   offsets  [E_l + 1] exclusive prefix sum; offsets[E_l] = N
+ *   perm_token, perm_slot [N_max]: row i < N is assignment (token, slot)
+ *   slot_row [T, k]    inverse map: the row of (t, s), or -1 when the slot's
+ *                      expert is not on this rank
+ * topk_idx [T, k] int32 with every id in [0, E). */
+mtl_status mtl_moe_permute(const mtl_moe_cfg* cfg, const int32_t* topk_idx, int32_t* counts, int32_t* offsets,
+                           int32_t* perm_token, int32_t* perm_slot, int32_t* slot_row, mtl_stream_t stream);
+
+/* Expert forward (grouped GEMMs over the E_l local experts):
+ *   xp = x[perm_token]                     [N_max, h] bf16 (saved)
+ *   z  = xp_e . w1_e per expert            [N_max, f] bf16 (saved)
+ *   a  = GeLU(z)                           [N_max, f] bf16 (saved, GeLU of fp32 z)
+ *   ye = a_e . w2_e per expert             [N_max, h] bf16 (saved, not gate-scaled)
+ *   y_partial[t] = sum over local slots s of t, ascending, of gates[t,s] * ye[row]
+ *                                          [T, h] bf16 (zero rows for tokens with no local expert)
+ * x [T, h] bf16; the routing arrays are those of mtl_moe_route/permute. */
+mtl_status mtl_moe_fwd(const mtl_moe_cfg* cfg, const void* x, const int32_t* offsets, const int32_t* perm_token,
+                       const int32_t* slot_row, const float* gates, const void* w1, const void* w2, void* xp, void* z,
+                       void* a, void* ye, void* y_partial, mtl_stream_t stream);
+
+/* Expert backward given dy = dL/dY [T, h] bf16:
+ *   dye       = gates[t,s] * dy[t] per row       (scratch)
+ *   dgates    = <ye[row], dy[t]>                 [T, k] fp32, 0 on non-local slots
+ *   dz        = (dye_e . w2_e^T) * GeLU'(z)      (scratch)
+ *   dw2[e]    = a_e^T . dye_e                    [E_l, f, h] fp32
+ *   dw1[e]    = xp_e^T . dz_e                    [E_l, h, f] fp32 (zero for an expert with no rows)
+ *   dx_partial[t] = sum over local slots of t, ascending, of (dz_e . w1_e^T)[row]
+ *                                                [T, h] bf16
+ * The gradient through the gate softmax into the logits is not computed here.
+ * With MTL_F_WGRAD_ACCUM, dw1/dw2 are added to. */
+mtl_status mtl_moe_bwd(const mtl_moe_cfg* cfg, const void* dy, const int32_t* offsets, const int32_t* perm_token,
+                       const int32_t* perm_slot, const int32_t* slot_row, const float* gates, const void* xp,
+                       const void* z, const void* a, const void* ye, const void* w1, const void* w2, void* dx_partial,
+                       float* dw1, float* dw2, float* dgates, void* scratch, size_t scratch_bytes,
+                       mtl_stream_t stream);
 
 #ifdef __cplusplus
 }

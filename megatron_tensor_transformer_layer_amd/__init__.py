@@ -33,9 +33,15 @@ class LayerCfg(ctypes.Structure):
                 ("hidden", "heads", "ffn", "seq", "micro_batch", "tp", "rank", "precision", "flags")]
 
 
+class MoeCfg(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in
+                ("tokens", "hidden", "ffn", "experts", "topk", "ep", "rank", "precision", "flags")]
+
+
 _P = ctypes.c_void_p
 _I32, _I64, _SZ = ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
 _CFG = ctypes.POINTER(LayerCfg)
+_MCFG = ctypes.POINTER(MoeCfg)
 _SIGS = {
     "mtl_status_str": (ctypes.c_char_p, [ctypes.c_int]),
     "mtl_validate": (ctypes.c_int, [_CFG]),
@@ -45,6 +51,12 @@ _SIGS = {
     "mtl_mlp_fwd": (ctypes.c_int, [_CFG, _P, _P, _P, _P, _P, _P, _P, _P]),
     "mtl_mlp_bwd": (ctypes.c_int, [_CFG, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "mtl_attn_bwd": (ctypes.c_int, [_CFG, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
+    "mtl_moe_validate": (ctypes.c_int, [_MCFG]),
+    "mtl_moe_sizes": (ctypes.c_int, [_MCFG, ctypes.POINTER(_I64), ctypes.POINTER(_SZ)]),
+    "mtl_moe_route": (ctypes.c_int, [_MCFG, _P, _P, _P, _P]),
+    "mtl_moe_permute": (ctypes.c_int, [_MCFG, _P, _P, _P, _P, _P, _P, _P]),
+    "mtl_moe_fwd": (ctypes.c_int, [_MCFG] + [_P] * 13),
+    "mtl_moe_bwd": (ctypes.c_int, [_MCFG] + [_P] * 17 + [_SZ, _P]),
 }
 
 _lib = None
@@ -137,3 +149,44 @@ def mtl_attn_bwd(cfg, dh, x, qkv, o, lse, w_qkv, w_o, dx_partial, dw_qkv, db_qkv
     _check(lib().mtl_attn_bwd(ctypes.byref(cfg), _ptr(dh), _ptr(x), _ptr(qkv), _ptr(o), _ptr(lse), _ptr(w_qkv),
                               _ptr(w_o), _ptr(dx_partial), _ptr(dw_qkv), _ptr(db_qkv), _ptr(dw_o), _ptr(db_o),
                               _ptr(scratch), nbytes, _stream(stream)), "mtl_attn_bwd")
+
+
+def make_moe_cfg(tokens, hidden, ffn, experts, topk, ep=1, rank=0, precision=MTL_PREC_BF16, flags=0) -> MoeCfg:
+    return MoeCfg(tokens, hidden, ffn, experts, topk, ep, rank, precision, flags)
+
+
+def mtl_moe_validate(cfg: MoeCfg) -> int:
+    """Returns the status code (does not raise)."""
+    return lib().mtl_moe_validate(ctypes.byref(cfg))
+
+
+def mtl_moe_sizes(cfg: MoeCfg):
+    """Returns (max_rows, scratch_bytes)."""
+    rows, n = _I64(0), _SZ(0)
+    _check(lib().mtl_moe_sizes(ctypes.byref(cfg), ctypes.byref(rows), ctypes.byref(n)), "mtl_moe_sizes")
+    return rows.value, n.value
+
+
+def mtl_moe_route(cfg, logits, topk_idx, gates, stream=None):
+    _check(lib().mtl_moe_route(ctypes.byref(cfg), _ptr(logits), _ptr(topk_idx), _ptr(gates), _stream(stream)),
+           "mtl_moe_route")
+
+
+def mtl_moe_permute(cfg, topk_idx, counts, offsets, perm_token, perm_slot, slot_row, stream=None):
+    _check(lib().mtl_moe_permute(ctypes.byref(cfg), _ptr(topk_idx), _ptr(counts), _ptr(offsets), _ptr(perm_token),
+                                 _ptr(perm_slot), _ptr(slot_row), _stream(stream)), "mtl_moe_permute")
+
+
+def mtl_moe_fwd(cfg, x, offsets, perm_token, slot_row, gates, w1, w2, xp, z, a, ye, y_partial, stream=None):
+    _check(lib().mtl_moe_fwd(ctypes.byref(cfg), _ptr(x), _ptr(offsets), _ptr(perm_token), _ptr(slot_row),
+                             _ptr(gates), _ptr(w1), _ptr(w2), _ptr(xp), _ptr(z), _ptr(a), _ptr(ye), _ptr(y_partial),
+                             _stream(stream)), "mtl_moe_fwd")
+
+
+def mtl_moe_bwd(cfg, dy, offsets, perm_token, perm_slot, slot_row, gates, xp, z, a, ye, w1, w2, dx_partial, dw1,
+                dw2, dgates, scratch, scratch_bytes=None, stream=None):
+    nbytes = scratch.numel() * scratch.element_size() if scratch_bytes is None else scratch_bytes
+    _check(lib().mtl_moe_bwd(ctypes.byref(cfg), _ptr(dy), _ptr(offsets), _ptr(perm_token), _ptr(perm_slot),
+                             _ptr(slot_row), _ptr(gates), _ptr(xp), _ptr(z), _ptr(a), _ptr(ye), _ptr(w1), _ptr(w2),
+                             _ptr(dx_partial), _ptr(dw1), _ptr(dw2), _ptr(dgates), _ptr(scratch), nbytes,
+                             _stream(stream)), "mtl_moe_bwd")

@@ -4,6 +4,8 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
+
 #include "kernels.hpp"
 
 using namespace mtl;
@@ -127,6 +129,12 @@ mtl_status mtl_validate(const mtl_layer_cfg* c) {
   if ((c->ffn / c->tp) % 8 != 0) return MTL_E_SHAPE;
   if (c->tp > 16) return MTL_E_SHAPE;
   if ((int64_t)c->seq * c->micro_batch > (int64_t)1 << 30) return MTL_E_SHAPE;
+  {
+    // every GEMM operand is addressed with 32-bit byte offsets
+    const Dims d = dims_of(c);
+    const int64_t w = std::max({d.h, d.qkv_l, d.f_l});
+    if ((std::max(d.S, w) + 256) * w * 2 >= ((int64_t)1 << 32)) return MTL_E_SHAPE;
+  }
   if (c->precision != MTL_PREC_BF16) return MTL_E_UNSUPPORTED;
   if (c->flags & ~(MTL_F_RESIDUAL | MTL_F_WGRAD_ACCUM)) return MTL_E_UNSUPPORTED;
   return MTL_OK;
@@ -288,6 +296,221 @@ mtl_status mtl_attn_bwd(const mtl_layer_cfg* c, const void* dh, const void* x, c
   MTL_TRY(colsum_bf16(ws.dqkv, d.S, d.qkv_l, d.qkv_l, db_qkv, accum, ws.ws, s));
   g = gemm(ws.dqkv, d.qkv_l, w_qkv, d.qkv_l, d.S, d.h, d.qkv_l, dx_partial, d.h);
   MTL_TRY(gemm_bf16(g, GEMM_DGRAD, EPI_BF16, s));
+  return MTL_OK;
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------- MoE
+
+namespace {
+
+struct MoeDims {
+  int64_t T, h, f, E, k, El, e_lo, nmax;
+};
+
+MoeDims moe_dims(const mtl_moe_cfg* c) {
+  MoeDims d;
+  d.T = c->tokens;
+  d.h = c->hidden;
+  d.f = c->ffn;
+  d.E = c->experts;
+  d.k = c->topk;
+  d.El = c->experts / c->ep;
+  d.e_lo = (int64_t)c->rank * d.El;
+  d.nmax = d.T * (d.k < d.El ? d.k : d.El);
+  return d;
+}
+
+struct MoeScratch {
+  uint16_t* dye;  // [N_max, h]; reused for dxp once the wgrads have read dye
+  uint16_t* dz;   // [N_max, f]
+};
+
+size_t moe_scratch(const MoeDims& d, MoeScratch* s, char* base) {
+  size_t off = 0;
+  if (s) s->dye = reinterpret_cast<uint16_t*>(base + off);
+  off += up(d.nmax * d.h * 2);
+  if (s) s->dz = reinterpret_cast<uint16_t*>(base + off);
+  off += up(d.nmax * d.f * 2);
+  return off;
+}
+
+GemmArgs grouped(const MoeDims& d, GemmGroupMode mode, const int32_t* offsets, int64_t stride_b, int64_t stride_c) {
+  GemmArgs g{};
+  g.offsets = offsets;
+  g.groups = (int)d.El;
+  g.group_mode = mode;
+  g.stride_b = stride_b;
+  g.stride_c = stride_c;
+  return g;
+}
+
+}  // namespace
+
+extern "C" {
+
+mtl_status mtl_moe_validate(const mtl_moe_cfg* c) {
+  if (!c) return MTL_E_NULL;
+  if (c->tokens <= 0 || c->hidden <= 0 || c->ffn <= 0 || c->experts <= 0 || c->topk <= 0 || c->ep <= 0)
+    return MTL_E_SHAPE;
+  if (c->experts % c->ep != 0) return MTL_E_DIVISIBILITY;
+  if (c->rank < 0 || c->rank >= c->ep) return MTL_E_RANK;
+  if (c->hidden % 8 != 0 || c->ffn % 8 != 0) return MTL_E_SHAPE;
+  if (c->experts > 1024 || c->topk > c->experts || c->topk > 64) return MTL_E_SHAPE;
+  if ((int64_t)c->tokens * c->topk >= ((int64_t)1 << 31)) return MTL_E_SHAPE;
+  {
+    // every grouped-GEMM operand is addressed with 32-bit byte offsets
+    const MoeDims d = moe_dims(c);
+    const int64_t w = std::max(d.h, d.f);
+    if ((std::max(d.nmax, w) + 256) * w * 2 >= ((int64_t)1 << 32)) return MTL_E_SHAPE;
+  }
+  if (c->precision != MTL_PREC_BF16) return MTL_E_UNSUPPORTED;
+  if (c->flags & ~MTL_F_WGRAD_ACCUM) return MTL_E_UNSUPPORTED;
+  return MTL_OK;
+}
+
+mtl_status mtl_moe_sizes(const mtl_moe_cfg* c, int64_t* max_rows, size_t* scratch_bytes) {
+  mtl_status st = mtl_moe_validate(c);
+  if (st != MTL_OK) return st;
+  const MoeDims d = moe_dims(c);
+  if (max_rows) *max_rows = d.nmax;
+  if (scratch_bytes) *scratch_bytes = moe_scratch(d, nullptr, nullptr);
+  return MTL_OK;
+}
+
+mtl_status mtl_moe_route(const mtl_moe_cfg* c, const float* logits, int32_t* topk_idx, float* gates,
+                         mtl_stream_t stream) {
+  mtl_status st = mtl_moe_validate(c);
+  if (st != MTL_OK) return st;
+  if ((st = check_ptrs(logits, topk_idx, gates)) != MTL_OK) return st;
+  return hip_status(moe_route(logits, c->tokens, c->experts, c->topk, topk_idx, gates,
+                              reinterpret_cast<hipStream_t>(stream)));
+}
+
+mtl_status mtl_moe_permute(const mtl_moe_cfg* c, const int32_t* topk_idx, int32_t* counts, int32_t* offsets,
+                           int32_t* perm_token, int32_t* perm_slot, int32_t* slot_row, mtl_stream_t stream) {
+  mtl_status st = mtl_moe_validate(c);
+  if (st != MTL_OK) return st;
+  if ((st = check_ptrs(topk_idx, counts, offsets, perm_token, perm_slot, slot_row)) != MTL_OK) return st;
+  const MoeDims d = moe_dims(c);
+  return hip_status(moe_permute(topk_idx, (int)d.T, (int)d.k, (int)d.e_lo, (int)d.El, counts, offsets, perm_token,
+                                perm_slot, slot_row, reinterpret_cast<hipStream_t>(stream)));
+}
+
+mtl_status mtl_moe_fwd(const mtl_moe_cfg* c, const void* x, const int32_t* offsets, const int32_t* perm_token,
+                       const int32_t* slot_row, const float* gates, const void* w1, const void* w2, void* xp, void* z,
+                       void* a, void* ye, void* y_partial, mtl_stream_t stream) {
+  mtl_status st = mtl_moe_validate(c);
+  if (st != MTL_OK) return st;
+  if ((st = check_ptrs(x, offsets, perm_token, slot_row, gates, w1, w2, xp, z, a, ye, y_partial)) != MTL_OK) return st;
+  const MoeDims d = moe_dims(c);
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+
+  MTL_TRY(moe_gather(static_cast<const uint16_t*>(x), perm_token, offsets, (int)d.El, d.nmax, d.h,
+                     static_cast<uint16_t*>(xp), s));
+  // z = xp_e . w1_e, a = GeLU(z)   (the grid covers N_max rows; M carries N_max)
+  GemmArgs g = grouped(d, GROUP_M, offsets, d.h * d.f, 0);
+  g.a = static_cast<const uint16_t*>(xp);
+  g.lda = d.h;
+  g.b = static_cast<const uint16_t*>(w1);
+  g.ldb = d.f;
+  g.M = (int)d.nmax;
+  g.N = (int)d.f;
+  g.K = (int)d.h;
+  g.c = z;
+  g.ldc = d.f;
+  g.c2 = a;
+  g.ldc2 = d.f;
+  MTL_TRY(gemm_bf16(g, GEMM_FWD, EPI_BIAS_GELU, s));
+  // ye = a_e . w2_e
+  g = grouped(d, GROUP_M, offsets, d.f * d.h, 0);
+  g.a = static_cast<const uint16_t*>(a);
+  g.lda = d.f;
+  g.b = static_cast<const uint16_t*>(w2);
+  g.ldb = d.h;
+  g.M = (int)d.nmax;
+  g.N = (int)d.h;
+  g.K = (int)d.f;
+  g.c = ye;
+  g.ldc = d.h;
+  MTL_TRY(gemm_bf16(g, GEMM_FWD, EPI_BF16, s));
+  MTL_TRY(moe_combine(static_cast<const uint16_t*>(ye), slot_row, gates, (int)d.T, (int)d.k, d.h,
+                      static_cast<uint16_t*>(y_partial), s));
+  return MTL_OK;
+}
+
+mtl_status mtl_moe_bwd(const mtl_moe_cfg* c, const void* dy, const int32_t* offsets, const int32_t* perm_token,
+                       const int32_t* perm_slot, const int32_t* slot_row, const float* gates, const void* xp,
+                       const void* z, const void* a, const void* ye, const void* w1, const void* w2, void* dx_partial,
+                       float* dw1, float* dw2, float* dgates, void* scratch, size_t scratch_bytes,
+                       mtl_stream_t stream) {
+  mtl_status st = mtl_moe_validate(c);
+  if (st != MTL_OK) return st;
+  if ((st = check_ptrs(dy, offsets, perm_token, perm_slot, slot_row, gates, xp, z, a, ye, w1, w2, dx_partial, dw1,
+                       dw2, dgates, scratch)) != MTL_OK)
+    return st;
+  const MoeDims d = moe_dims(c);
+  MoeScratch ws;
+  if (scratch_bytes < moe_scratch(d, &ws, static_cast<char*>(scratch))) return MTL_E_WORKSPACE;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const int wepi = (c->flags & MTL_F_WGRAD_ACCUM) ? EPI_F32_ACC : EPI_F32;
+
+  MTL_TRY(moe_combine_bwd(static_cast<const uint16_t*>(dy), static_cast<const uint16_t*>(ye), perm_token, perm_slot,
+                          slot_row, offsets, (int)d.El, d.nmax, gates, (int)d.T, (int)d.k, d.h, ws.dye, dgates, s));
+  // dz = (dye_e . w2_e^T) * GeLU'(z)
+  GemmArgs g = grouped(d, GROUP_M, offsets, d.f * d.h, 0);
+  g.a = ws.dye;
+  g.lda = d.h;
+  g.b = static_cast<const uint16_t*>(w2);
+  g.ldb = d.h;
+  g.M = (int)d.nmax;
+  g.N = (int)d.f;
+  g.K = (int)d.h;
+  g.c = ws.dz;
+  g.ldc = d.f;
+  g.aux = static_cast<const uint16_t*>(z);
+  g.ld_aux = d.f;
+  MTL_TRY(gemm_bf16(g, GEMM_DGRAD, EPI_DGELU, s));
+  // dw2[e] = a_e^T . dye_e   (K = the expert's rows; K carries N_max for the range check)
+  g = grouped(d, GROUP_K, offsets, 0, d.f * d.h);
+  g.a = static_cast<const uint16_t*>(a);
+  g.lda = d.f;
+  g.b = ws.dye;
+  g.ldb = d.h;
+  g.M = (int)d.f;
+  g.N = (int)d.h;
+  g.K = (int)d.nmax;
+  g.c = dw2;
+  g.ldc = d.h;
+  MTL_TRY(gemm_bf16(g, GEMM_WGRAD, wepi, s));
+  // dw1[e] = xp_e^T . dz_e
+  g = grouped(d, GROUP_K, offsets, 0, d.h * d.f);
+  g.a = static_cast<const uint16_t*>(xp);
+  g.lda = d.h;
+  g.b = ws.dz;
+  g.ldb = d.f;
+  g.M = (int)d.h;
+  g.N = (int)d.f;
+  g.K = (int)d.nmax;
+  g.c = dw1;
+  g.ldc = d.f;
+  MTL_TRY(gemm_bf16(g, GEMM_WGRAD, wepi, s));
+  // dxp = dz_e . w1_e^T into the dye buffer (dye is dead after dw2), then the
+  // slot-ordered scatter-add into dx_partial
+  uint16_t* dxp = ws.dye;
+  g = grouped(d, GROUP_M, offsets, d.h * d.f, 0);
+  g.a = ws.dz;
+  g.lda = d.f;
+  g.b = static_cast<const uint16_t*>(w1);
+  g.ldb = d.f;
+  g.M = (int)d.nmax;
+  g.N = (int)d.h;
+  g.K = (int)d.f;
+  g.c = dxp;
+  g.ldc = d.h;
+  MTL_TRY(gemm_bf16(g, GEMM_DGRAD, EPI_BF16, s));
+  MTL_TRY(moe_combine(dxp, slot_row, nullptr, (int)d.T, (int)d.k, d.h, static_cast<uint16_t*>(dx_partial), s));
   return MTL_OK;
 }
 

@@ -202,16 +202,54 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmArgs p) {
   __shared__ __attribute__((aligned(1024))) char st1_[ML::STAGE];
   LDS_AS char* st0 = (LDS_AS char*)st0_;
   LDS_AS char* st1 = (LDS_AS char*)st1_;
+  constexpr int OUT_BYTES = (EPI == EPI_F32 || EPI == EPI_F32_ACC) ? 4 : 2;
 
-  const int tiles_m = (p.M + BM - 1) / BM, tiles_n = (p.N + BN - 1) / BN;
-  const int ntiles = tiles_m * tiles_n;
-  const int t = tile_index(blockIdx.x, ntiles);
-  constexpr int GM = 4;
-  const int group = GM * tiles_n;
-  const int first_m = (t / group) * GM;
-  const int gm = min(tiles_m - first_m, GM);
-  const int tm = first_m + (t % group) % gm;
-  const int tn = (t % group) / gm;
+  int tm, tn;
+  if (p.offsets == nullptr) {
+    const int tiles_m = (p.M + BM - 1) / BM, tiles_n = (p.N + BN - 1) / BN;
+    const int ntiles = tiles_m * tiles_n;
+    const int t = tile_index(blockIdx.x, ntiles);
+    constexpr int GM = 4;
+    const int group = GM * tiles_n;
+    const int first_m = (t / group) * GM;
+    const int gm = min(tiles_m - first_m, GM);
+    tm = first_m + (t % group) % gm;
+    tn = (t % group) / gm;
+  } else if (p.group_mode == GROUP_M) {
+    // find this workgroup's expert among the per-expert row-tile counts
+    const int tiles_n = (p.N + BN - 1) / BN;
+    int w = blockIdx.x, e = -1;
+    for (int gi = 0; gi < p.groups; ++gi) {
+      const int rows = p.offsets[gi + 1] - p.offsets[gi];
+      const int span = ((rows + BM - 1) / BM) * tiles_n;
+      if (w < span) {
+        e = gi;
+        break;
+      }
+      w -= span;
+    }
+    if (e < 0) return;  // beyond the grouped rows: nothing to do
+    const int r0 = p.offsets[e];
+    p.M = p.offsets[e + 1] - r0;
+    p.a += (int64_t)r0 * p.lda;
+    p.b += (int64_t)e * p.stride_b;
+    p.c = reinterpret_cast<char*>(p.c) + (int64_t)r0 * p.ldc * OUT_BYTES;
+    if (p.c2) p.c2 = reinterpret_cast<uint16_t*>(p.c2) + (int64_t)r0 * p.ldc2;
+    if (p.aux) p.aux += (int64_t)r0 * p.ld_aux;
+    tm = w / tiles_n;
+    tn = w % tiles_n;
+  } else {
+    const int tiles_m = (p.M + BM - 1) / BM, tiles_n = (p.N + BN - 1) / BN;
+    const int per = tiles_m * tiles_n;
+    const int e = blockIdx.x / per, w = blockIdx.x % per;
+    const int r0 = p.offsets[e];
+    p.K = p.offsets[e + 1] - r0;
+    p.a += (int64_t)r0 * p.lda;
+    p.b += (int64_t)r0 * p.ldb;
+    p.c = reinterpret_cast<char*>(p.c) + (int64_t)e * p.stride_c * OUT_BYTES;
+    tm = w / tiles_n;
+    tn = w % tiles_n;
+  }
   const int m0 = tm * BM, n0 = tn * BN;
 
   const int lane = threadIdx.x & 63;
@@ -279,7 +317,7 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmArgs p) {
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const int n = nw + j * 32 + 8 * g + 4 * lgrp;
-        braw[j][g] = n < p.N ? *reinterpret_cast<const u32x2*>(p.bias + n) : u32x2{0, 0};
+        braw[j][g] = (p.bias && n < p.N) ? *reinterpret_cast<const u32x2*>(p.bias + n) : u32x2{0, 0};
       }
 #pragma unroll
     for (int j = 0; j < TN; ++j)
@@ -368,18 +406,32 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmArgs p) {
 
 template <int BM, int BN, bool A_K, bool B_K, int EPI>
 static hipError_t launch_cfg(const GemmArgs& p, hipStream_t s) {
-  const int tiles = ((p.M + BM - 1) / BM) * ((p.N + BN - 1) / BN);
-  hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, A_K, B_K, EPI>), dim3(tiles), dim3(256), 0, s, p);
+  int64_t tiles;
+  if (p.offsets == nullptr) {
+    tiles = (int64_t)((p.M + BM - 1) / BM) * ((p.N + BN - 1) / BN);
+  } else if (p.group_mode == GROUP_M) {
+    // p.M carries the maximum number of grouped rows
+    tiles = ((int64_t)(p.M + BM - 1) / BM + p.groups) * ((p.N + BN - 1) / BN);
+  } else {
+    tiles = (int64_t)p.groups * ((p.M + BM - 1) / BM) * ((p.N + BN - 1) / BN);
+  }
+  if (tiles <= 0) return hipSuccess;
+  hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, A_K, B_K, EPI>), dim3((unsigned)tiles), dim3(256), 0, s, p);
   return hipGetLastError();
 }
 
 template <bool A_K, bool B_K, int EPI>
 static hipError_t launch_layout(const GemmArgs& p, hipStream_t s) {
+  if (p.offsets) return launch_cfg<256, 256, A_K, B_K, EPI>(p, s);  // expert GEMMs are large
   const long t256 = (long)((p.M + 255) / 256) * ((p.N + 255) / 256);
   const long t192 = (long)((p.M + 255) / 256) * ((p.N + 191) / 192);
   if (t256 >= 240) return launch_cfg<256, 256, A_K, B_K, EPI>(p, s);
   if (t192 >= 240 && p.N % 192 == 0) return launch_cfg<256, 192, A_K, B_K, EPI>(p, s);
   return launch_cfg<128, 128, A_K, B_K, EPI>(p, s);
+}
+
+int64_t gemm_group_m_grid(int64_t max_rows, int groups, int N) {
+  return ((max_rows + 255) / 256 + groups) * ((N + 255) / 256);
 }
 
 hipError_t gemm_bf16(const GemmArgs& p, GemmLayout layout, int epi, hipStream_t s) {
@@ -389,7 +441,7 @@ hipError_t gemm_bf16(const GemmArgs& p, GemmLayout layout, int epi, hipStream_t 
   const bool a_k = layout != GEMM_WGRAD, b_k = layout == GEMM_DGRAD;
   const int64_t a_rows = (a_k ? (int64_t)p.M : (int64_t)p.K) + 256, b_rows = (b_k ? (int64_t)p.N : (int64_t)p.K) + 256;
   if (a_rows * p.lda * 2 >= ((int64_t)1 << 32) || b_rows * p.ldb * 2 >= ((int64_t)1 << 32)) return hipErrorInvalidValue;
-  if (p.K <= 0) return hipErrorInvalidValue;
+  if (p.K <= 0 && !(p.offsets && p.group_mode == GROUP_K)) return hipErrorInvalidValue;
   switch (layout) {
     case GEMM_FWD:  // A k-contig, B n-contig
       if (epi == EPI_BF16) return launch_layout<true, false, EPI_BF16>(p, s);

@@ -10,7 +10,7 @@ namespace mtl {
 enum GemmEpi : int {
   EPI_BF16 = 0,       // C = acc                      (bf16)
   EPI_BF16_BIAS = 1,  // C = acc + bias[n]            (bf16)
-  EPI_BIAS_GELU = 2,  // C = acc + bias[n]; C2 = GeLU(C) (both bf16)
+  EPI_BIAS_GELU = 2,  // C = acc + bias[n]; C2 = GeLU(C) (both bf16); bias may be null
   EPI_DGELU = 3,      // C = acc * GeLU'(aux[m][n])   (bf16, aux bf16)
   EPI_F32 = 4,        // C = acc                      (fp32)
   EPI_F32_ACC = 5,    // C += acc                     (fp32)
@@ -34,7 +34,21 @@ struct GemmArgs {
   int64_t ldc2;
   const uint16_t* aux;   // GeLU input Z (EPI_DGELU)
   int64_t ld_aux;
+  // Grouped (MoE experts): group e owns rows [offsets[e], offsets[e+1]).
+  //  GROUP_M: those rows of A, C (and C2, aux) form expert e's M; B advances by
+  //           stride_b elements per group; N and K are fixed.
+  //  GROUP_K: those rows of A and B form expert e's K (A and B mn-contiguous);
+  //           C advances by stride_c elements per group; M and N are fixed.
+  const int32_t* offsets;  // nullptr = one plain GEMM
+  int groups;
+  int group_mode;
+  int64_t stride_b, stride_c;
 };
+
+enum GemmGroupMode : int { GROUP_M = 0, GROUP_K = 1 };
+
+// Workgroups needed by a GROUP_M launch with at most max_rows grouped rows.
+int64_t gemm_group_m_grid(int64_t max_rows, int groups, int N);
 
 // Requirements (checked by the caller): K % 8 == 0 when an operand is
 // k-contiguous, M % 8 == 0 when A is mn-contiguous, N % 8 == 0 always,
@@ -71,5 +85,25 @@ hipError_t reduce_partials(int t, const uint16_t* const* partials, const uint16_
 size_t colsum_ws_floats(int64_t rows, int64_t cols);
 hipError_t colsum_bf16(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld, float* out, bool accumulate,
                        float* ws, hipStream_t s);
+
+// ---------------------------------------------------------------- MoE data movement
+// Top-k expert ids per token (descending logit, ties to the lower id) and the
+// softmax of the selected logits.  E <= 1024, k <= min(E, 64).
+hipError_t moe_route(const float* logits, int T, int E, int k, int32_t* idx, float* gates, hipStream_t s);
+// Stable grouping of the (token, slot) entries whose expert lies in
+// [e_lo, e_lo + E_l): counts[E_l], offsets[E_l + 1], ptok/pslot[N] and the
+// inverse slot_row[T*k] (row of the entry, or -1 when its expert is not local).
+hipError_t moe_permute(const int32_t* idx, int T, int k, int e_lo, int E_l, int32_t* counts, int32_t* offsets,
+                       int32_t* ptok, int32_t* pslot, int32_t* slot_row, hipStream_t s);
+// xp[i] = x[ptok[i]] for i < offsets[E_l] (max_rows bounds the grid).
+hipError_t moe_gather(const uint16_t* x, const int32_t* ptok, const int32_t* offsets, int E_l, int64_t max_rows,
+                      int64_t h, uint16_t* xp, hipStream_t s);
+// out[t] = sum_{s ascending, slot_row[t,s] >= 0} (gates ? gates[t,s] : 1) * rows[slot_row[t,s]].
+hipError_t moe_combine(const uint16_t* rows, const int32_t* slot_row, const float* gates, int T, int k, int64_t h,
+                       uint16_t* out, hipStream_t s);
+// dye[i] = gates[t,s] * dy[t]; dgates[t,s] = <ye[i], dy[t]> (0 for non-local slots).
+hipError_t moe_combine_bwd(const uint16_t* dy, const uint16_t* ye, const int32_t* ptok, const int32_t* pslot,
+                           const int32_t* slot_row, const int32_t* offsets, int E_l, int64_t max_rows,
+                           const float* gates, int T, int k, int64_t h, uint16_t* dye, float* dgates, hipStream_t s);
 
 }  // namespace mtl

@@ -1,0 +1,273 @@
+// MoE routing and data movement for one expert-parallel rank, gfx950.
+//
+// Readings (the site summary's MoE deploy step gives 256 experts, a top-8
+// router and EP 16 but no formula): the k largest fp32 logits per token, ties to
+// the lower expert id, in slot order of decreasing logit; gates are the softmax
+// over the k selected logits; rank r of ep owns experts [r*E/ep, (r+1)*E/ep);
+// its assignments are grouped by expert with tokens ascending (a stable order),
+// dropless.  The expert GEMMs run on the grouped modes of gemm_bf16.
+//
+// Every kernel here is deterministic: selection is exact comparison of the
+// given fp32 values, the permutation is a scan, and every sum runs in a fixed
+// order (slot order for the combine and the scatter of dX).
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace mtl {
+
+// ---------------------------------------------------------------- route
+// One wave per token; lane l holds logits l, l+64, ... (E <= 1024).  Round r
+// of k picks the largest untaken logit (lowest id among equals) by a wave
+// butterfly; lane r keeps it, so slot r's id and gate are written by lane r.
+__global__ __launch_bounds__(256) void moe_route_kernel(const float* __restrict__ logits, int T, int E, int k,
+                                                        int32_t* __restrict__ idx, float* __restrict__ gates) {
+  const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (t >= T) return;
+  const float* row = logits + t * E;
+  constexpr int PER = 16;
+  float v[PER];
+  uint32_t taken = 0;
+#pragma unroll
+  for (int j = 0; j < PER; ++j) {
+    const int e = lane + 64 * j;
+    v[j] = e < E ? row[e] : -INFINITY;
+    if (e >= E) taken |= 1u << j;
+  }
+  float mine_v = -INFINITY;
+  int mine_i = 0;
+  for (int r = 0; r < k; ++r) {
+    float bv = -INFINITY;
+    int bi = 0x7fffffff;
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      const int e = lane + 64 * j;
+      if (!(taken & (1u << j)) && (v[j] > bv || (v[j] == bv && e < bi))) {
+        bv = v[j];
+        bi = e;
+      }
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+      const float ov = __shfl_xor(bv, off);
+      const int oi = __shfl_xor(bi, off);
+      if (ov > bv || (ov == bv && oi < bi)) {
+        bv = ov;
+        bi = oi;
+      }
+    }
+    if ((bi & 63) == lane) taken |= 1u << (bi >> 6);
+    if (lane == r) {
+      mine_v = bv;
+      mine_i = bi;
+    }
+  }
+  // softmax over the k selected logits; slot 0 holds the largest
+  const float top = __shfl(mine_v, 0);
+  const float ex = lane < k ? expf(mine_v - top) : 0.f;
+  float z = ex;
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) z += __shfl_xor(z, off);
+  if (lane < k) {
+    idx[t * k + lane] = mine_i;
+    gates[t * k + lane] = ex / z;
+  }
+}
+
+hipError_t moe_route(const float* logits, int T, int E, int k, int32_t* idx, float* gates, hipStream_t s) {
+  if (T <= 0) return hipSuccess;
+  hipLaunchKernelGGL(moe_route_kernel, dim3((unsigned)((T + 3) / 4)), dim3(256), 0, s, logits, T, E, k, idx, gates);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------- permute
+// One workgroup of 1024 threads; thread t owns a contiguous chunk of the
+// (token, slot) entries.  For each local expert in turn: count the chunk's
+// matches, exclusive-scan the counts over threads, write the matches in entry
+// order.  Entry order is (token, slot), so tokens ascend within an expert.
+__device__ __forceinline__ int block_exclusive_scan(int v, int* sh, int& total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int x = v;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int y = __shfl_up(x, off);
+    if (lane >= off) x += y;
+  }
+  if (lane == 63) sh[wave] = x;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int acc = 0;
+    for (int w = 0; w < 16; ++w) {
+      const int c = sh[w];
+      sh[w] = acc;
+      acc += c;
+    }
+    sh[16] = acc;
+  }
+  __syncthreads();
+  const int excl = sh[wave] + x - v;
+  total = sh[16];
+  __syncthreads();
+  return excl;
+}
+
+__global__ __launch_bounds__(1024) void moe_permute_kernel(const int32_t* __restrict__ idx, int T, int k, int e_lo,
+                                                            int E_l, int32_t* __restrict__ counts,
+                                                            int32_t* __restrict__ offsets, int32_t* __restrict__ ptok,
+                                                            int32_t* __restrict__ pslot, int32_t* __restrict__ slot_row) {
+  __shared__ int sh[17];
+  const int64_t n = (int64_t)T * k;
+  const int64_t chunk = (n + 1023) / 1024;
+  const int64_t b0 = threadIdx.x * chunk, b1 = min(n, b0 + chunk);
+  for (int64_t j = b0; j < b1; ++j) slot_row[j] = -1;
+  int base = 0;
+  for (int e = 0; e < E_l; ++e) {
+    const int ex = e_lo + e;
+    int c = 0;
+    for (int64_t j = b0; j < b1; ++j) c += (idx[j] == ex);
+    int total;
+    const int excl = block_exclusive_scan(c, sh, total);
+    int pos = base + excl;
+    for (int64_t j = b0; j < b1; ++j) {
+      if (idx[j] == ex) {
+        ptok[pos] = (int32_t)(j / k);
+        pslot[pos] = (int32_t)(j % k);
+        slot_row[j] = pos;
+        ++pos;
+      }
+    }
+    if (threadIdx.x == 0) {
+      counts[e] = total;
+      offsets[e] = base;
+    }
+    base += total;
+  }
+  if (threadIdx.x == 0) offsets[E_l] = base;
+}
+
+hipError_t moe_permute(const int32_t* idx, int T, int k, int e_lo, int E_l, int32_t* counts, int32_t* offsets,
+                       int32_t* ptok, int32_t* pslot, int32_t* slot_row, hipStream_t s) {
+  hipLaunchKernelGGL(moe_permute_kernel, dim3(1), dim3(1024), 0, s, idx, T, k, e_lo, E_l, counts, offsets, ptok, pslot,
+                     slot_row);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------- gather
+// xp[i] = x[ptok[i]] for i < offsets[E_l]; 16 bytes per thread.
+__global__ __launch_bounds__(256) void moe_gather_kernel(const uint16_t* __restrict__ x, const int32_t* __restrict__ ptok,
+                                                          const int32_t* __restrict__ offsets, int E_l, int64_t max_rows,
+                                                          int64_t h, uint16_t* __restrict__ xp) {
+  const int64_t nv = h / 8;
+  const int64_t v = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t i = v / nv, c = v % nv;
+  if (i >= max_rows || i >= offsets[E_l]) return;
+  const int64_t t = ptok[i];
+  *reinterpret_cast<u32x4*>(xp + i * h + c * 8) = *reinterpret_cast<const u32x4*>(x + t * h + c * 8);
+}
+
+hipError_t moe_gather(const uint16_t* x, const int32_t* ptok, const int32_t* offsets, int E_l, int64_t max_rows,
+                      int64_t h, uint16_t* xp, hipStream_t s) {
+  const int64_t nthreads = max_rows * (h / 8);
+  if (nthreads <= 0) return hipSuccess;
+  hipLaunchKernelGGL(moe_gather_kernel, dim3((unsigned)((nthreads + 255) / 256)), dim3(256), 0, s, x, ptok, offsets,
+                     E_l, max_rows, h, xp);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------- combine and dX scatter
+// out[t] = sum over slots s (ascending) with slot_row[t,s] >= 0 of
+//          (gates ? gates[t,s] : 1) * rows[slot_row[t,s]]; fp32 sum, bf16 out.
+__global__ __launch_bounds__(256) void moe_combine_kernel(const uint16_t* __restrict__ rows,
+                                                           const int32_t* __restrict__ slot_row,
+                                                           const float* __restrict__ gates, int T, int k, int64_t h,
+                                                           uint16_t* __restrict__ out) {
+  const int64_t nv = h / 8;
+  const int64_t v = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t t = v / nv, c = v % nv;
+  if (t >= T) return;
+  float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  for (int s = 0; s < k; ++s) {
+    const int32_t r = slot_row[t * k + s];
+    if (r < 0) continue;
+    const float g = gates ? gates[t * k + s] : 1.f;
+    const u32x4 x = *reinterpret_cast<const u32x4*>(rows + (int64_t)r * h + c * 8);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      acc[2 * j] += g * bf16_lo(x[j]);
+      acc[2 * j + 1] += g * bf16_hi(x[j]);
+    }
+  }
+  u32x4 o;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) o[j] = pack_bf16x2(acc[2 * j], acc[2 * j + 1]);
+  *reinterpret_cast<u32x4*>(out + t * h + c * 8) = o;
+}
+
+hipError_t moe_combine(const uint16_t* rows, const int32_t* slot_row, const float* gates, int T, int k, int64_t h,
+                       uint16_t* out, hipStream_t s) {
+  const int64_t nthreads = (int64_t)T * (h / 8);
+  if (nthreads <= 0) return hipSuccess;
+  hipLaunchKernelGGL(moe_combine_kernel, dim3((unsigned)((nthreads + 255) / 256)), dim3(256), 0, s, rows, slot_row,
+                     gates, T, k, h, out);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------- combine backward
+// For every local assignment row i (token t, slot s): dye[i] = g[t,s] * dy[t]
+// and dgates[t,s] = <ye[i], dy[t]> (fp32, one wave per row, fixed lane order);
+// dgates of slots whose expert is not local are zero.
+__global__ __launch_bounds__(256) void moe_gate_grad_zero_kernel(const int32_t* __restrict__ slot_row, int64_t n,
+                                                                  float* __restrict__ dgates) {
+  const int64_t j = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (j < n && slot_row[j] < 0) dgates[j] = 0.f;
+}
+
+__global__ __launch_bounds__(256) void moe_combine_bwd_kernel(const uint16_t* __restrict__ dy,
+                                                               const uint16_t* __restrict__ ye,
+                                                               const int32_t* __restrict__ ptok,
+                                                               const int32_t* __restrict__ pslot,
+                                                               const int32_t* __restrict__ offsets, int E_l,
+                                                               int64_t max_rows, const float* __restrict__ gates, int k,
+                                                               int64_t h, uint16_t* __restrict__ dye,
+                                                               float* __restrict__ dgates) {
+  const int64_t i = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (i >= max_rows || i >= offsets[E_l]) return;
+  const int64_t t = ptok[i];
+  const int s = pslot[i];
+  const float g = gates[t * k + s];
+  float dot = 0.f;
+  for (int64_t c = lane; c < h / 8; c += 64) {
+    const u32x4 d = *reinterpret_cast<const u32x4*>(dy + t * h + c * 8);
+    const u32x4 y = *reinterpret_cast<const u32x4*>(ye + i * h + c * 8);
+    u32x4 o;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float d0 = bf16_lo(d[j]), d1 = bf16_hi(d[j]);
+      dot += bf16_lo(y[j]) * d0 + bf16_hi(y[j]) * d1;
+      o[j] = pack_bf16x2(g * d0, g * d1);
+    }
+    *reinterpret_cast<u32x4*>(dye + i * h + c * 8) = o;
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) dot += __shfl_xor(dot, off);
+  if (lane == 0) dgates[t * k + s] = dot;
+}
+
+hipError_t moe_combine_bwd(const uint16_t* dy, const uint16_t* ye, const int32_t* ptok, const int32_t* pslot,
+                           const int32_t* slot_row, const int32_t* offsets, int E_l, int64_t max_rows,
+                           const float* gates, int T, int k, int64_t h, uint16_t* dye, float* dgates, hipStream_t s) {
+  const int64_t n = (int64_t)T * k;
+  if (n > 0) {
+    hipLaunchKernelGGL(moe_gate_grad_zero_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, slot_row, n,
+                       dgates);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (max_rows <= 0) return hipSuccess;
+  hipLaunchKernelGGL(moe_combine_bwd_kernel, dim3((unsigned)((max_rows + 3) / 4)), dim3(256), 0, s, dy, ye, ptok,
+                     pslot, offsets, E_l, max_rows, gates, k, h, dye, dgates);
+  return hipGetLastError();
+}
+
+}  // namespace mtl

@@ -1,0 +1,67 @@
+"""Device buffers and the call sequence of one expert-parallel rank's MoE block.
+
+Plumbing only: allocates torch device tensors and passes their addresses to
+the C entry points (see ``__init__``) in the order a training step needs them.
+No arithmetic of the block happens here.
+"""
+from __future__ import annotations
+
+import torch
+
+from . import (MTL_PREC_BF16, make_moe_cfg, mtl_moe_bwd, mtl_moe_fwd, mtl_moe_permute, mtl_moe_route,
+               mtl_moe_sizes)
+
+DEV = "cuda"
+
+
+class MoeRank:
+    """Routing tables, saved activations, outputs, gradients and scratch of one
+    EP rank.  ``w1`` [E/ep, h, f] and ``w2`` [E/ep, f, h] are bf16 device tensors."""
+
+    def __init__(self, tokens, hidden, ffn, experts, topk, ep, rank, w1, w2, flags=0, device=DEV):
+        self.cfg = make_moe_cfg(tokens, hidden, ffn, experts, topk, ep, rank, MTL_PREC_BF16, flags)
+        self.max_rows, self.scratch_bytes = mtl_moe_sizes(self.cfg)
+        T, h, f, k, El, N = tokens, hidden, ffn, topk, experts // ep, self.max_rows
+        i32 = dict(dtype=torch.int32, device=device)
+        bf = dict(dtype=torch.bfloat16, device=device)
+        f32 = dict(dtype=torch.float32, device=device)
+        self.w1, self.w2 = w1, w2
+        self.idx = torch.empty(T, k, **i32)
+        self.gates = torch.empty(T, k, **f32)
+        self.counts = torch.empty(El, **i32)
+        self.offsets = torch.empty(El + 1, **i32)
+        self.perm_token = torch.empty(N, **i32)
+        self.perm_slot = torch.empty(N, **i32)
+        self.slot_row = torch.empty(T, k, **i32)
+        self.xp = torch.empty(N, h, **bf)
+        self.z = torch.empty(N, f, **bf)
+        self.a = torch.empty(N, f, **bf)
+        self.ye = torch.empty(N, h, **bf)
+        self.y = torch.empty(T, h, **bf)
+        self.dx = torch.empty(T, h, **bf)
+        self.dw1 = torch.zeros(El, h, f, **f32)
+        self.dw2 = torch.zeros(El, f, h, **f32)
+        self.dgates = torch.empty(T, k, **f32)
+        self.scratch = torch.empty(self.scratch_bytes, dtype=torch.uint8, device=device)
+
+    def route(self, logits):
+        mtl_moe_route(self.cfg, logits, self.idx, self.gates)
+
+    def permute(self):
+        mtl_moe_permute(self.cfg, self.idx, self.counts, self.offsets, self.perm_token, self.perm_slot,
+                        self.slot_row)
+
+    def forward(self, x):
+        mtl_moe_fwd(self.cfg, x, self.offsets, self.perm_token, self.slot_row, self.gates, self.w1, self.w2,
+                    self.xp, self.z, self.a, self.ye, self.y)
+
+    def backward(self, dy):
+        mtl_moe_bwd(self.cfg, dy, self.offsets, self.perm_token, self.perm_slot, self.slot_row, self.gates,
+                    self.xp, self.z, self.a, self.ye, self.w1, self.w2, self.dx, self.dw1, self.dw2, self.dgates,
+                    self.scratch)
+
+    def step(self, logits, x, dy):
+        self.route(logits)
+        self.permute()
+        self.forward(x)
+        self.backward(dy)

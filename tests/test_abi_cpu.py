@@ -100,3 +100,50 @@ def test_errors_before_launch(mtl):
 def test_status_strings(mtl):
     for s in range(9):
         assert mtl.status_text(s) not in ("", "unknown status")
+
+
+def test_moe_validate_codes(mtl):
+    cases = json.load(open(os.path.join(GOLDEN, "divisibility.json")))
+    for c in cases["moe"]:
+        cfg = mtl.make_moe_cfg(4096, 7168, 18432, c["experts"], c["topk"], c["ep"], 0)
+        st = mtl.mtl_moe_validate(cfg)
+        assert st == (mtl.MTL_OK if c["ok"] else mtl.MTL_E_DIVISIBILITY), c
+    ok = dict(tokens=4096, hidden=7168, ffn=18432, experts=256, topk=8, ep=16, rank=0)
+    assert mtl.mtl_moe_validate(mtl.make_moe_cfg(**ok)) == mtl.MTL_OK
+    bad = [
+        (dict(rank=16), mtl.MTL_E_RANK), (dict(rank=-1), mtl.MTL_E_RANK),
+        (dict(experts=250), mtl.MTL_E_DIVISIBILITY),
+        (dict(tokens=0), mtl.MTL_E_SHAPE), (dict(topk=0), mtl.MTL_E_SHAPE),
+        (dict(hidden=7170), mtl.MTL_E_SHAPE), (dict(ffn=18436), mtl.MTL_E_SHAPE),
+        (dict(experts=2048, ep=16), mtl.MTL_E_SHAPE),  # more experts than the router kernel holds
+        (dict(experts=4, ep=1, topk=5), mtl.MTL_E_SHAPE),  # k > E
+        (dict(tokens=1 << 20), mtl.MTL_E_SHAPE),  # grouped rows x 18432 past 4 GiB
+    ]
+    for change, want in bad:
+        assert mtl.mtl_moe_validate(mtl.make_moe_cfg(**{**ok, **change})) == want, change
+    c = mtl.make_moe_cfg(**ok)
+    c.precision = mtl.MTL_PREC_FP8_HYBRID
+    assert mtl.mtl_moe_validate(c) == mtl.MTL_E_UNSUPPORTED
+    assert mtl.lib().mtl_moe_validate(None) == mtl.MTL_E_NULL
+
+
+def test_moe_sizes(mtl):
+    # N_max = T * min(k, E/ep): every one of a token's k slots can be local
+    rows, scratch = mtl.mtl_moe_sizes(mtl.make_moe_cfg(4096, 7168, 18432, 256, 8, 16, 0))
+    assert rows == 4096 * 8
+    assert scratch >= rows * (7168 + 18432) * 2
+    # fewer local experts than k bounds the rows by T * E/ep
+    rows, _ = mtl.mtl_moe_sizes(mtl.make_moe_cfg(100, 64, 128, 8, 4, 4, 1))
+    assert rows == 100 * 2
+
+
+def test_moe_errors_before_launch(mtl):
+    cfg = mtl.make_moe_cfg(64, 128, 256, 8, 2, 2, 0)
+    P = 1 << 20
+    lib = mtl.lib()
+    assert lib.mtl_moe_route(ctypes.byref(cfg), P, None, P, None) == mtl.MTL_E_NULL
+    assert lib.mtl_moe_permute(ctypes.byref(cfg), P, P, P, P, P + 4, P, None) == mtl.MTL_E_ALIGN
+    args = [P] * 12
+    args[3] = None
+    assert lib.mtl_moe_fwd(ctypes.byref(cfg), *args, None) == mtl.MTL_E_NULL
+    assert lib.mtl_moe_bwd(ctypes.byref(cfg), *([P] * 17), 16, None) == mtl.MTL_E_WORKSPACE
