@@ -9,7 +9,9 @@ two reduce shares.  The reduce shares are the rank's reduce-scatter rows
 [rank*S/t, (rank+1)*S/t) over its own partial and t-1 resident peer partials.
 
 Prints one JSON line.  Default workload: rank 0 of a 7B-class layer at TP=4
-(hidden 4096, 32 heads, ffn 16384, seq 4096, micro-batch 1, bf16).
+(hidden 4096, 32 heads, ffn 16384, seq 4096, micro-batch 1, bf16).  With
+--workload moe-256e-top8-ep16 the step is one expert-parallel rank's MoE
+expert block instead (route, permute, grouped expert GEMMs, combine, backward).
 """
 from __future__ import annotations
 
@@ -117,6 +119,122 @@ def cpu_baseline(shape, rank, sample_seq):
                       f"(fp64 numpy), {dt:.2f} s"}
 
 
+def moe_cpu_baseline(shape, rank, sample_tokens, sample_ffn):
+    """The MoE oracle (fp64 numpy, as it stands) on a bounded sample of the
+    workload: the first sample_tokens tokens, routed as in the full run, with
+    every expert's ffn width cut to sample_ffn."""
+    import synth
+    from oracle import moe as M
+
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        cores = len(os.sched_getaffinity(0))
+    sub = synth.MoeShape(tokens=sample_tokens, hidden=shape.hidden, ffn=sample_ffn, experts=shape.experts,
+                         topk=shape.topk, ep=shape.ep, zipf_s=shape.zipf_s)
+    lo, hi = M.local_range(shape.experts, shape.ep, rank)
+    w1 = np.stack([synth.bf16_bits_to_f64(synth.moe_expert_weight(sub, "moe_w1", e)) for e in range(lo, hi)])
+    w2 = np.stack([synth.bf16_bits_to_f64(synth.moe_expert_weight(sub, "moe_w2", e)) for e in range(lo, hi)])
+    logits = synth.moe_logits(shape)[:sample_tokens]
+    x = synth.bf16_bits_to_f64(synth.moe_tokens(sub, 0, "moe_x"))
+    dy = synth.bf16_bits_to_f64(synth.moe_tokens(sub, 0, "moe_dy"))
+    t0 = time.perf_counter()
+    fwd = M.moe_forward(x, w1, w2, logits, shape.topk, shape.ep, rank)
+    M.moe_backward(x, w1, w2, fwd, dy)
+    dt = time.perf_counter() - t0
+    flops = M.moe_flops(fwd["counts"], shape.hidden, sample_ffn)
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"EP rank {rank} expert block forward+backward on the first {sample_tokens} of {shape.tokens} "
+                      f"tokens ({int(fwd['offsets'][-1])} local assignments) with ffn cut to {sample_ffn} "
+                      f"(fp64 numpy), {dt:.2f} s"}
+
+
+def moe_main(args):
+    """One EP rank's MoE expert block: route, permute, grouped fc1+GeLU, fc2,
+    combine, and the backward (combine', grouped dgrad and wgrad, dX scatter)."""
+    import torch
+    import synth
+    from megatron_tensor_transformer_layer_amd.layer import bf16_dev
+    from megatron_tensor_transformer_layer_amd.moe import MoeRank
+    from oracle.moe import moe_flops  # FLOP count only (closed form)
+
+    shape = synth.MOE_WORKLOADS[args.workload]
+    r, El = args.rank, shape.experts // shape.ep
+    lo = r * El
+    w1 = torch.stack([synth.moe_expert_weight_device(shape, "moe_w1", lo + e) for e in range(El)])
+    w2 = torch.stack([synth.moe_expert_weight_device(shape, "moe_w2", lo + e) for e in range(El)])
+    st = MoeRank(shape.tokens, shape.hidden, shape.ffn, shape.experts, shape.topk, shape.ep, r, w1, w2)
+    logits = torch.from_numpy(synth.moe_logits(shape)).cuda()
+    x = bf16_dev(synth.moe_tokens(shape, 0, "moe_x"))
+    dy = bf16_dev(synth.moe_tokens(shape, 0, "moe_dy"))
+    st.step(logits, x, dy)
+    torch.cuda.synchronize()
+    counts = st.counts.cpu().numpy()
+
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+    fwd_ev = []
+
+    def step(record=False):
+        st.route(logits)
+        st.permute()
+        if record:
+            e0, e1 = ev(), ev()
+            e0.record()
+        st.forward(x)
+        if record:
+            e1.record()
+            fwd_ev.append((e0, e1))
+        st.backward(dy)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step(record=True)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = wall / args.steps * 1e3
+    fl = moe_flops(counts, shape.hidden, shape.ffn)
+    n = int(counts.sum())
+    fwd_ms = float(np.mean([a.elapsed_time(b) for a, b in fwd_ev]))
+    # mtl_moe_fwd = gather + two grouped GEMM launches (2*N*h*f FLOP each) + combine;
+    # the per-launch rate below charges the gather and combine to the GEMMs
+    gemm_launch_s = fwd_ms / 2 / 1e3
+    achieved = 2.0 * n * shape.hidden * shape.ffn / gemm_launch_s / 1e12
+    out = {
+        "metric": "TFLOP/s per EP-rank MoE expert block fwd+bwd (bf16) and % of MI355X MFMA peak",
+        "value": round(fl / (ms / 1e3) / 1e12, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (Zipf(%.1f) router logits, N(0,1) tokens, N(0,0.02) expert weights)" % shape.zipf_s,
+        "config": {"workload": f"{args.workload}: EP rank {r} of {shape.ep}, {El} of {shape.experts} experts, "
+                               f"top-{shape.topk}, hidden {shape.hidden}, ffn {shape.ffn}, {shape.tokens} tokens; "
+                               f"{n} local assignments, per-expert rows {counts.min()}..{counts.max()}",
+                   "global_batch": 1, "seq_len": shape.tokens, "parallelism": f"ep{shape.ep}-rank{r}-of-1gpu"},
+        "pct_of_peak": round(100 * fl / (ms / 1e3) / 1e12 / PEAK_BF16_TFLOPS, 2),
+        "flop_per_step": fl,
+        "roofline": {"bound": "mfma",
+                     "kernel": "gemm_bf16_kernel grouped over experts, 256x256 tiles: the two launches of "
+                               "mtl_moe_fwd (fc1 + GeLU, fc2), gather and combine included",
+                     "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "gemm_launch_us": round(gemm_launch_s * 1e6, 2)},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = moe_cpu_baseline(shape, r, 512, shape.ffn // 16)
+    print(json.dumps(out), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -135,6 +253,9 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
+    if args.workload in synth.MOE_WORKLOADS:
+        moe_main(args)
+        return
     shape = synth.WORKLOADS[args.workload]
     t, r = shape.tp, args.rank
     inp = synth.layer_inputs(shape, tp=t, rank=r)

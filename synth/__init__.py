@@ -213,3 +213,19 @@ def moe_expert_weight(shape: MoeShape, name: str, expert: int, seed: int = 0) ->
     else:
         raise KeyError(name)
     return bf16_round_bits(_normal(seed, name, expert, shp, WEIGHT_STD))
+
+
+def moe_expert_weight_device(shape: MoeShape, name: str, expert: int, seed: int = 0, device="cuda"):
+    """A full-size expert weight drawn on the device (torch's Philox generator),
+    N(0, WEIGHT_STD) rounded to bf16: a fast stand-in for experts whose values
+    no check reads.  Not the numbers of moe_expert_weight."""
+    import torch
+    if name == "moe_w1":
+        shp = (shape.hidden, shape.ffn)
+    elif name == "moe_w2":
+        shp = (shape.ffn, shape.hidden)
+    else:
+        raise KeyError(name)
+    g = torch.Generator(device=device)
+    g.manual_seed((seed * 1_000_003 + _TID[name]) * 4099 + expert)
+    return (torch.randn(shp, generator=g, device=device, dtype=torch.float32) * WEIGHT_STD).to(torch.bfloat16)
