@@ -62,6 +62,8 @@ typedef enum mtl_status {
 } mtl_status;
 
 enum { MTL_PREC_BF16 = 0, MTL_PREC_FP8_HYBRID = 1 };
+enum { MTL_FP8_E4M3 = 0, MTL_FP8_E5M2 = 1 };
+#define MTL_FP8_AMAX_SCRATCH 4096 /* bytes of scratch mtl_fp8_amax needs */
 
 enum {
   MTL_F_RESIDUAL = 1,   /* mtl_reduce callers add residuals; recorded for validation only */
@@ -88,11 +90,14 @@ const char* mtl_status_str(mtl_status s);
  * (ffn/tp) % 8 == 0 (MTL_E_SHAPE otherwise: the attention kernels are built for
  * those head sizes and the GEMMs move 16-byte vectors); tp <= 16; every GEMM
  * operand under 4 GiB: (max(S, w) + 256) * w * 2 < 2^32 bytes with
- * w = max(h, 3h/t, f/t). */
+ * w = max(h, 3h/t, f/t).  precision MTL_PREC_BF16 or MTL_PREC_FP8_HYBRID; the
+ * latter also needs S % 16 == 0 and (ffn/tp) % 16 == 0 (fp8 GEMMs contract over
+ * 16-byte chunks of codes). */
 mtl_status mtl_validate(const mtl_layer_cfg* cfg);
 
-/* Bytes of device scratch the backward calls need (*scratch_bytes) for this
- * configuration.  The forward calls need none. */
+/* Bytes of device scratch (*scratch_bytes) that suffice for every call of this
+ * configuration.  In bf16 the forward calls need none (their scratch may be
+ * NULL); in fp8 every call needs it for the operands' codes. */
 mtl_status mtl_workspace_bytes(const mtl_layer_cfg* cfg, size_t* scratch_bytes);
 
 /* Attention half of the rank's forward (column-parallel QKV, causal attention
@@ -101,9 +106,16 @@ mtl_status mtl_workspace_bytes(const mtl_layer_cfg* cfg, size_t* scratch_bytes);
  *   o       = attention(qkv)             [S, h/t]  bf16 (saved)
  *   lse     = row log-sum-exp of scaled scores, [heads/t, S] fp32 (saved)
  *   partial = o . w_o                    [S, h]    bf16, this rank's partial sum
- * x [S, h] bf16. */
+ * x [S, h] bf16.  scratch: see mtl_workspace_bytes (NULL allowed in bf16).
+ *
+ * fp8 (MTL_PREC_FP8_HYBRID, the site summary's --fp8-format hybrid): each GEMM
+ * operand is quantised per tensor (mtl_fp8_amax + mtl_fp8_cast) -- E4M3 for
+ * activations and weights, E5M2 for gradients -- the product accumulates in
+ * fp32 and is multiplied by both operands' 1/s in the epilogue; outputs, bias,
+ * GeLU, attention and the reductions stay bf16/fp32 as in the bf16 path. */
 mtl_status mtl_attn_fwd(const mtl_layer_cfg* cfg, const void* x, const void* w_qkv, const void* b_qkv,
-                        const void* w_o, void* qkv, void* o, float* lse, void* partial, mtl_stream_t stream);
+                        const void* w_o, void* qkv, void* o, float* lse, void* partial, void* scratch,
+                        size_t scratch_bytes, mtl_stream_t stream);
 
 /* The all-reduce stand-in (tutorial section 2.2: the row-parallel outputs are
  * summed across the t ranks):
@@ -121,9 +133,10 @@ mtl_status mtl_reduce(int32_t t, const void* const* partials, const void* bias, 
  *   z       = h . w1 + b1     [S, f/t] bf16 (saved)
  *   a       = GeLU(z)         [S, f/t] bf16 (saved; GeLU of the fp32 z)
  *   partial = a . w2          [S, h]   bf16, this rank's partial sum
- * h [S, h] bf16 is the reduced attention output. */
+ * h [S, h] bf16 is the reduced attention output.  scratch as for mtl_attn_fwd;
+ * in fp8, a is quantised from its bf16 values. */
 mtl_status mtl_mlp_fwd(const mtl_layer_cfg* cfg, const void* h, const void* w1, const void* b1, const void* w2,
-                       void* z, void* a, void* partial, mtl_stream_t stream);
+                       void* z, void* a, void* partial, void* scratch, size_t scratch_bytes, mtl_stream_t stream);
 
 /* MLP backward given dy = dL/dY [S, h] bf16 (every rank holds all of it):
  *   dz         = (dy . w2^T) * GeLU'(z)      (scratch, bf16)
@@ -146,11 +159,32 @@ mtl_status mtl_mlp_bwd(const mtl_layer_cfg* cfg, const void* dy, const void* h, 
  *   dw_qkv     = x^T . dqkv                  [h, 3h/t] fp32
  *   db_qkv     = colsum(dqkv)                [3h/t] fp32
  *   dx_partial = dqkv . w_qkv^T              [S, h] bf16, this rank's partial
- * The attention backward is deterministic (no atomics). */
+ * The attention backward is deterministic (no atomics).  In fp8 the six GEMMs
+ * of mtl_mlp_bwd / mtl_attn_bwd take E5M2 gradients and E4M3 activations and
+ * weights (dgrad: gradient x weight; wgrad: activation^T x gradient); the
+ * bias gradients are column sums of the bf16 gradients. */
 mtl_status mtl_attn_bwd(const mtl_layer_cfg* cfg, const void* dh, const void* x, const void* qkv, const void* o,
                         const float* lse, const void* w_qkv, const void* w_o, void* dx_partial, float* dw_qkv,
                         float* db_qkv, float* dw_o, float* db_o, void* scratch, size_t scratch_bytes,
                         mtl_stream_t stream);
+
+/* fp8 per-tensor scaling (the site summary's --fp8-format hybrid; the pages give
+ * no encoding or scaling rule, read as OCP E4M3 (bias 7, max 448, no infinity)
+ * and E5M2 (bias 15, max 57344) with current scaling).
+ * rec[0..2] = {amax, s, 1/s} for n bf16 values x: amax = max |x| (exact),
+ * s = fmt_max / amax in fp32 with correct rounding (1 when amax is 0, inf or
+ * NaN), 1/s likewise.  rec: 16-byte aligned device floats; scratch >=
+ * MTL_FP8_AMAX_SCRATCH bytes.  Deterministic. */
+mtl_status mtl_fp8_amax(const void* x, int64_t n, int32_t format, float* rec, void* scratch, size_t scratch_bytes,
+                        mtl_stream_t stream);
+
+/* Codes of x [rows, cols] bf16: code = round-to-nearest-even of the fp32
+ * product x*rec[1] onto the format's grid, saturated to +-fmt_max, NaN -> 0x7F.
+ * out [rows, cols] and/or out_t [cols, rows] (the transposed copy a weight
+ * gradient needs) -- either may be NULL, not both.  cols % 8 == 0; rows % 16 == 0
+ * when out_t is given. */
+mtl_status mtl_fp8_cast(const void* x, int64_t rows, int64_t cols, int32_t format, const float* rec, void* out,
+                        void* out_t, mtl_stream_t stream);
 
 /* ------------------------------------------------------------------------
  * MoE expert block of one expert-parallel rank.

@@ -19,6 +19,8 @@ HEADER = os.path.join(os.path.dirname(HERE), "include", "mtl.h")
 MTL_OK, MTL_E_NULL, MTL_E_DIVISIBILITY, MTL_E_RANK, MTL_E_SHAPE = 0, 1, 2, 3, 4
 MTL_E_ALIGN, MTL_E_WORKSPACE, MTL_E_UNSUPPORTED, MTL_E_HIP = 5, 6, 7, 8
 MTL_PREC_BF16, MTL_PREC_FP8_HYBRID = 0, 1
+MTL_FP8_E4M3, MTL_FP8_E5M2 = 0, 1
+MTL_FP8_AMAX_SCRATCH = 4096
 MTL_F_RESIDUAL, MTL_F_WGRAD_ACCUM = 1, 2
 
 
@@ -46,11 +48,13 @@ _SIGS = {
     "mtl_status_str": (ctypes.c_char_p, [ctypes.c_int]),
     "mtl_validate": (ctypes.c_int, [_CFG]),
     "mtl_workspace_bytes": (ctypes.c_int, [_CFG, ctypes.POINTER(_SZ)]),
-    "mtl_attn_fwd": (ctypes.c_int, [_CFG, _P, _P, _P, _P, _P, _P, _P, _P, _P]),
+    "mtl_attn_fwd": (ctypes.c_int, [_CFG, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "mtl_reduce": (ctypes.c_int, [_I32, ctypes.POINTER(_P), _P, _P, _P, _I64, _I64, _I64, _I64, _P]),
-    "mtl_mlp_fwd": (ctypes.c_int, [_CFG, _P, _P, _P, _P, _P, _P, _P, _P]),
+    "mtl_mlp_fwd": (ctypes.c_int, [_CFG, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "mtl_mlp_bwd": (ctypes.c_int, [_CFG, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "mtl_attn_bwd": (ctypes.c_int, [_CFG, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
+    "mtl_fp8_amax": (ctypes.c_int, [_P, _I64, _I32, _P, _P, _SZ, _P]),
+    "mtl_fp8_cast": (ctypes.c_int, [_P, _I64, _I64, _I32, _P, _P, _P, _P]),
     "mtl_moe_validate": (ctypes.c_int, [_MCFG]),
     "mtl_moe_sizes": (ctypes.c_int, [_MCFG, ctypes.POINTER(_I64), ctypes.POINTER(_SZ)]),
     "mtl_moe_route": (ctypes.c_int, [_MCFG, _P, _P, _P, _P]),
@@ -119,9 +123,16 @@ def mtl_workspace_bytes(cfg: LayerCfg) -> int:
     return n.value
 
 
-def mtl_attn_fwd(cfg, x, w_qkv, b_qkv, w_o, qkv, o, lse, partial, stream=None):
+def _nbytes(scratch, scratch_bytes):
+    if scratch_bytes is not None:
+        return scratch_bytes
+    return 0 if scratch is None or isinstance(scratch, int) else scratch.numel() * scratch.element_size()
+
+
+def mtl_attn_fwd(cfg, x, w_qkv, b_qkv, w_o, qkv, o, lse, partial, scratch=None, scratch_bytes=None, stream=None):
     _check(lib().mtl_attn_fwd(ctypes.byref(cfg), _ptr(x), _ptr(w_qkv), _ptr(b_qkv), _ptr(w_o), _ptr(qkv), _ptr(o),
-                              _ptr(lse), _ptr(partial), _stream(stream)), "mtl_attn_fwd")
+                              _ptr(lse), _ptr(partial), _ptr(scratch), _nbytes(scratch, scratch_bytes),
+                              _stream(stream)), "mtl_attn_fwd")
 
 
 def mtl_reduce(partials, bias, residual, out, rows, cols, row_begin=0, row_end=None, stream=None):
@@ -131,9 +142,10 @@ def mtl_reduce(partials, bias, residual, out, rows, cols, row_begin=0, row_end=N
                             rows if row_end is None else row_end, _stream(stream)), "mtl_reduce")
 
 
-def mtl_mlp_fwd(cfg, h, w1, b1, w2, z, a, partial, stream=None):
+def mtl_mlp_fwd(cfg, h, w1, b1, w2, z, a, partial, scratch=None, scratch_bytes=None, stream=None):
     _check(lib().mtl_mlp_fwd(ctypes.byref(cfg), _ptr(h), _ptr(w1), _ptr(b1), _ptr(w2), _ptr(z), _ptr(a),
-                             _ptr(partial), _stream(stream)), "mtl_mlp_fwd")
+                             _ptr(partial), _ptr(scratch), _nbytes(scratch, scratch_bytes), _stream(stream)),
+           "mtl_mlp_fwd")
 
 
 def mtl_mlp_bwd(cfg, dy, h, z, a, w1, w2, dh_partial, dw1, db1, dw2, db2, scratch, scratch_bytes=None, stream=None):
@@ -190,3 +202,13 @@ def mtl_moe_bwd(cfg, dy, offsets, perm_token, perm_slot, slot_row, gates, xp, z,
                              _ptr(slot_row), _ptr(gates), _ptr(xp), _ptr(z), _ptr(a), _ptr(ye), _ptr(w1), _ptr(w2),
                              _ptr(dx_partial), _ptr(dw1), _ptr(dw2), _ptr(dgates), _ptr(scratch), nbytes,
                              _stream(stream)), "mtl_moe_bwd")
+
+
+def mtl_fp8_amax(x, n, fmt, rec, scratch, scratch_bytes=None, stream=None):
+    _check(lib().mtl_fp8_amax(_ptr(x), n, fmt, _ptr(rec), _ptr(scratch), _nbytes(scratch, scratch_bytes),
+                              _stream(stream)), "mtl_fp8_amax")
+
+
+def mtl_fp8_cast(x, rows, cols, fmt, rec, out, out_t=None, stream=None):
+    _check(lib().mtl_fp8_cast(_ptr(x), rows, cols, fmt, _ptr(rec), _ptr(out), _ptr(out_t), _stream(stream)),
+           "mtl_fp8_cast")

@@ -66,37 +66,157 @@ GemmArgs gemm(const void* a, int64_t lda, const void* b, int64_t ldb, int64_t M,
   return g;
 }
 
+// Bump allocation over a caller's scratch buffer (base == nullptr: sizing only).
+struct Bump {
+  char* base;
+  size_t off = 0;
+  template <class T>
+  T* take(size_t bytes) {
+    T* p = base ? reinterpret_cast<T*>(base + off) : nullptr;
+    off += up(bytes);
+    return p;
+  }
+};
+
+// An fp8 copy of one bf16 tensor [rows, cols]: its scale record {amax, s, 1/s}
+// and the row-major codes q and/or the transposed codes qt ([cols, rows]).
+struct Q8 {
+  float* rec;
+  uint8_t* q;
+  uint8_t* qt;
+  int64_t rows, cols;
+  int fmt;
+};
+Q8 q8(Bump& b, int64_t rows, int64_t cols, int fmt, bool normal, bool trans) {
+  Q8 q{};
+  q.rec = b.take<float>(16);
+  q.q = normal ? b.take<uint8_t>(rows * cols) : nullptr;
+  q.qt = trans ? b.take<uint8_t>(rows * cols) : nullptr;
+  q.rows = rows;
+  q.cols = cols;
+  q.fmt = fmt;
+  return q;
+}
+constexpr int E4M3 = 0, E5M2 = 1;
+
+hipError_t quantize(const void* x, const Q8& q, void* amax_ws, hipStream_t s) {
+  hipError_t e = fp8_amax(static_cast<const uint16_t*>(x), q.rows * q.cols, q.fmt, q.rec, amax_ws, s);
+  if (e != hipSuccess) return e;
+  return fp8_cast(static_cast<const uint16_t*>(x), q.rows, q.cols, q.fmt, q.rec, q.q, q.qt, s);
+}
+
+// fp8 GEMM C[M, N] = A . B^T over K, both operands k-contiguous codes.
+hipError_t gemm8(const Q8& a, const uint8_t* a_codes, const Q8& b, const uint8_t* b_codes, int64_t M, int64_t N,
+                 int64_t K, void* c, int64_t ldc, int epi, hipStream_t s, const void* bias = nullptr,
+                 void* c2 = nullptr, const void* aux = nullptr) {
+  GemmArgs g{};
+  g.a = reinterpret_cast<const uint16_t*>(a_codes);
+  g.b = reinterpret_cast<const uint16_t*>(b_codes);
+  g.lda = K;
+  g.ldb = K;
+  g.M = (int)M;
+  g.N = (int)N;
+  g.K = (int)K;
+  g.c = c;
+  g.ldc = ldc;
+  g.bias = static_cast<const uint16_t*>(bias);
+  g.c2 = c2;
+  g.ldc2 = ldc;
+  g.aux = static_cast<const uint16_t*>(aux);
+  g.ld_aux = ldc;
+  g.scale_a = a.rec + 2;
+  g.scale_b = b.rec + 2;
+  return gemm_fp8(g, a.fmt, b.fmt, epi, s);
+}
+
 struct MlpScratch {
   uint16_t* dz;
   float* ws;
+  // fp8 copies
+  Q8 dy, w2, a_t, dz8, h_t, w1;
+  void* amax_ws;
 };
 struct AttnScratch {
   uint16_t* dout;
   uint16_t* dqkv;
   float* delta;
   float* ws;
+  Q8 dh, wo, o_t, dqkv8, x_t, wqkv;
+  void* amax_ws;
+};
+struct AttnFwdScratch {
+  Q8 x, wqkv_t, o, wo_t;
+  void* amax_ws;
+};
+struct MlpFwdScratch {
+  Q8 h, w1_t, a, w2_t;
+  void* amax_ws;
 };
 
-size_t mlp_scratch(const Dims& d, MlpScratch* s, char* base) {
-  size_t off = 0;
-  if (s) s->dz = reinterpret_cast<uint16_t*>(base + off);
-  off += up(d.S * d.f_l * 2);
-  if (s) s->ws = reinterpret_cast<float*>(base + off);
-  off += up(colsum_ws_floats(d.S, d.f_l > d.h ? d.f_l : d.h) * 4);
-  return off;
+inline bool is_fp8(const mtl_layer_cfg* c) { return c->precision == MTL_PREC_FP8_HYBRID; }
+
+size_t mlp_scratch(const mtl_layer_cfg* c, const Dims& d, MlpScratch* s, char* base) {
+  Bump b{base};
+  MlpScratch t{};
+  t.dz = b.take<uint16_t>(d.S * d.f_l * 2);
+  t.ws = b.take<float>(colsum_ws_floats(d.S, d.f_l > d.h ? d.f_l : d.h) * 4);
+  if (is_fp8(c)) {
+    t.dy = q8(b, d.S, d.h, E5M2, true, true);
+    t.w2 = q8(b, d.f_l, d.h, E4M3, true, false);
+    t.a_t = q8(b, d.S, d.f_l, E4M3, false, true);
+    t.dz8 = q8(b, d.S, d.f_l, E5M2, true, true);
+    t.h_t = q8(b, d.S, d.h, E4M3, false, true);
+    t.w1 = q8(b, d.h, d.f_l, E4M3, true, false);
+    t.amax_ws = b.take<char>(fp8_amax_ws_bytes());
+  }
+  if (s) *s = t;
+  return b.off;
 }
 
-size_t attn_scratch(const Dims& d, AttnScratch* s, char* base) {
-  size_t off = 0;
-  if (s) s->dout = reinterpret_cast<uint16_t*>(base + off);
-  off += up(d.S * d.o_l * 2);
-  if (s) s->dqkv = reinterpret_cast<uint16_t*>(base + off);
-  off += up(d.S * d.qkv_l * 2);
-  if (s) s->delta = reinterpret_cast<float*>(base + off);
-  off += up(d.heads_l * d.S * 4);
-  if (s) s->ws = reinterpret_cast<float*>(base + off);
-  off += up(colsum_ws_floats(d.S, d.qkv_l > d.h ? d.qkv_l : d.h) * 4);
-  return off;
+size_t attn_scratch(const mtl_layer_cfg* c, const Dims& d, AttnScratch* s, char* base) {
+  Bump b{base};
+  AttnScratch t{};
+  t.dout = b.take<uint16_t>(d.S * d.o_l * 2);
+  t.dqkv = b.take<uint16_t>(d.S * d.qkv_l * 2);
+  t.delta = b.take<float>(d.heads_l * d.S * 4);
+  t.ws = b.take<float>(colsum_ws_floats(d.S, d.qkv_l > d.h ? d.qkv_l : d.h) * 4);
+  if (is_fp8(c)) {
+    t.dh = q8(b, d.S, d.h, E5M2, true, true);
+    t.wo = q8(b, d.o_l, d.h, E4M3, true, false);
+    t.o_t = q8(b, d.S, d.o_l, E4M3, false, true);
+    t.dqkv8 = q8(b, d.S, d.qkv_l, E5M2, true, true);
+    t.x_t = q8(b, d.S, d.h, E4M3, false, true);
+    t.wqkv = q8(b, d.h, d.qkv_l, E4M3, true, false);
+    t.amax_ws = b.take<char>(fp8_amax_ws_bytes());
+  }
+  if (s) *s = t;
+  return b.off;
+}
+
+size_t attn_fwd_scratch(const mtl_layer_cfg* c, const Dims& d, AttnFwdScratch* s, char* base) {
+  if (!is_fp8(c)) return 0;
+  Bump b{base};
+  AttnFwdScratch t{};
+  t.x = q8(b, d.S, d.h, E4M3, true, false);
+  t.wqkv_t = q8(b, d.h, d.qkv_l, E4M3, false, true);
+  t.o = q8(b, d.S, d.o_l, E4M3, true, false);
+  t.wo_t = q8(b, d.o_l, d.h, E4M3, false, true);
+  t.amax_ws = b.take<char>(fp8_amax_ws_bytes());
+  if (s) *s = t;
+  return b.off;
+}
+
+size_t mlp_fwd_scratch(const mtl_layer_cfg* c, const Dims& d, MlpFwdScratch* s, char* base) {
+  if (!is_fp8(c)) return 0;
+  Bump b{base};
+  MlpFwdScratch t{};
+  t.h = q8(b, d.S, d.h, E4M3, true, false);
+  t.w1_t = q8(b, d.h, d.f_l, E4M3, false, true);
+  t.a = q8(b, d.S, d.f_l, E4M3, true, false);
+  t.w2_t = q8(b, d.f_l, d.h, E4M3, false, true);
+  t.amax_ws = b.take<char>(fp8_amax_ws_bytes());
+  if (s) *s = t;
+  return b.off;
 }
 
 }  // namespace
@@ -135,7 +255,12 @@ mtl_status mtl_validate(const mtl_layer_cfg* c) {
     const int64_t w = std::max({d.h, d.qkv_l, d.f_l});
     if ((std::max(d.S, w) + 256) * w * 2 >= ((int64_t)1 << 32)) return MTL_E_SHAPE;
   }
-  if (c->precision != MTL_PREC_BF16) return MTL_E_UNSUPPORTED;
+  if (c->precision != MTL_PREC_BF16 && c->precision != MTL_PREC_FP8_HYBRID) return MTL_E_UNSUPPORTED;
+  // fp8 GEMMs contract over 16-byte code chunks: every K (h, 3h/t, h/t, f/t, S)
+  // must be a multiple of 16
+  if (c->precision == MTL_PREC_FP8_HYBRID &&
+      (((int64_t)c->seq * c->micro_batch) % 16 != 0 || (c->ffn / c->tp) % 16 != 0))
+    return MTL_E_SHAPE;
   if (c->flags & ~(MTL_F_RESIDUAL | MTL_F_WGRAD_ACCUM)) return MTL_E_UNSUPPORTED;
   return MTL_OK;
 }
@@ -145,22 +270,35 @@ mtl_status mtl_workspace_bytes(const mtl_layer_cfg* c, size_t* scratch_bytes) {
   if (st != MTL_OK) return st;
   if (!scratch_bytes) return MTL_E_NULL;
   const Dims d = dims_of(c);
-  const size_t a = mlp_scratch(d, nullptr, nullptr), b = attn_scratch(d, nullptr, nullptr);
-  *scratch_bytes = a > b ? a : b;
+  *scratch_bytes = std::max({mlp_scratch(c, d, nullptr, nullptr), attn_scratch(c, d, nullptr, nullptr),
+                             attn_fwd_scratch(c, d, nullptr, nullptr), mlp_fwd_scratch(c, d, nullptr, nullptr)});
   return MTL_OK;
 }
 
 mtl_status mtl_attn_fwd(const mtl_layer_cfg* c, const void* x, const void* w_qkv, const void* b_qkv, const void* w_o,
-                        void* qkv, void* o, float* lse, void* partial, mtl_stream_t stream) {
+                        void* qkv, void* o, float* lse, void* partial, void* scratch, size_t scratch_bytes,
+                        mtl_stream_t stream) {
   mtl_status st = mtl_validate(c);
   if (st != MTL_OK) return st;
   if ((st = check_ptrs(x, w_qkv, b_qkv, w_o, qkv, o, lse, partial)) != MTL_OK) return st;
   const Dims d = dims_of(c);
+  AttnFwdScratch ws{};
+  if (is_fp8(c)) {
+    if ((st = check_ptrs(scratch)) != MTL_OK) return st;
+    if (scratch_bytes < attn_fwd_scratch(c, d, &ws, static_cast<char*>(scratch))) return MTL_E_WORKSPACE;
+  }
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
 
-  GemmArgs g = gemm(x, d.h, w_qkv, d.qkv_l, d.S, d.qkv_l, d.h, qkv, d.qkv_l);
-  g.bias = static_cast<const uint16_t*>(b_qkv);
-  MTL_TRY(gemm_bf16(g, GEMM_FWD, EPI_BF16_BIAS, s));
+  // qkv = x . w_qkv + b_qkv
+  if (is_fp8(c)) {
+    MTL_TRY(quantize(x, ws.x, ws.amax_ws, s));
+    MTL_TRY(quantize(w_qkv, ws.wqkv_t, ws.amax_ws, s));
+    MTL_TRY(gemm8(ws.x, ws.x.q, ws.wqkv_t, ws.wqkv_t.qt, d.S, d.qkv_l, d.h, qkv, d.qkv_l, EPI_BF16_BIAS, s, b_qkv));
+  } else {
+    GemmArgs g = gemm(x, d.h, w_qkv, d.qkv_l, d.S, d.qkv_l, d.h, qkv, d.qkv_l);
+    g.bias = static_cast<const uint16_t*>(b_qkv);
+    MTL_TRY(gemm_bf16(g, GEMM_FWD, EPI_BF16_BIAS, s));
+  }
 
   AttnArgs a{};
   a.qkv = static_cast<const uint16_t*>(qkv);
@@ -175,8 +313,15 @@ mtl_status mtl_attn_fwd(const mtl_layer_cfg* c, const void* x, const void* w_qkv
   a.scale = 1.0f / sqrtf((float)d.d);
   MTL_TRY(attention_fwd(a, s));
 
-  g = gemm(o, d.o_l, w_o, d.h, d.S, d.h, d.o_l, partial, d.h);
-  MTL_TRY(gemm_bf16(g, GEMM_FWD, EPI_BF16, s));
+  // partial = o . w_o
+  if (is_fp8(c)) {
+    MTL_TRY(quantize(o, ws.o, ws.amax_ws, s));
+    MTL_TRY(quantize(w_o, ws.wo_t, ws.amax_ws, s));
+    MTL_TRY(gemm8(ws.o, ws.o.q, ws.wo_t, ws.wo_t.qt, d.S, d.h, d.o_l, partial, d.h, EPI_BF16, s));
+  } else {
+    GemmArgs g = gemm(o, d.o_l, w_o, d.h, d.S, d.h, d.o_l, partial, d.h);
+    MTL_TRY(gemm_bf16(g, GEMM_FWD, EPI_BF16, s));
+  }
   return MTL_OK;
 }
 
@@ -199,13 +344,28 @@ mtl_status mtl_reduce(int32_t t, const void* const* partials, const void* bias, 
 }
 
 mtl_status mtl_mlp_fwd(const mtl_layer_cfg* c, const void* h, const void* w1, const void* b1, const void* w2, void* z,
-                       void* a, void* partial, mtl_stream_t stream) {
+                       void* a, void* partial, void* scratch, size_t scratch_bytes, mtl_stream_t stream) {
   mtl_status st = mtl_validate(c);
   if (st != MTL_OK) return st;
   if ((st = check_ptrs(h, w1, b1, w2, z, a, partial)) != MTL_OK) return st;
   const Dims d = dims_of(c);
+  MlpFwdScratch ws{};
+  if (is_fp8(c)) {
+    if ((st = check_ptrs(scratch)) != MTL_OK) return st;
+    if (scratch_bytes < mlp_fwd_scratch(c, d, &ws, static_cast<char*>(scratch))) return MTL_E_WORKSPACE;
+  }
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
 
+  if (is_fp8(c)) {
+    // z = h . w1 + b1, a = GeLU(z); partial = a . w2 (a re-quantised from bf16)
+    MTL_TRY(quantize(h, ws.h, ws.amax_ws, s));
+    MTL_TRY(quantize(w1, ws.w1_t, ws.amax_ws, s));
+    MTL_TRY(gemm8(ws.h, ws.h.q, ws.w1_t, ws.w1_t.qt, d.S, d.f_l, d.h, z, d.f_l, EPI_BIAS_GELU, s, b1, a));
+    MTL_TRY(quantize(a, ws.a, ws.amax_ws, s));
+    MTL_TRY(quantize(w2, ws.w2_t, ws.amax_ws, s));
+    MTL_TRY(gemm8(ws.a, ws.a.q, ws.w2_t, ws.w2_t.qt, d.S, d.h, d.f_l, partial, d.h, EPI_BF16, s));
+    return MTL_OK;
+  }
   GemmArgs g = gemm(h, d.h, w1, d.f_l, d.S, d.f_l, d.h, z, d.f_l);
   g.bias = static_cast<const uint16_t*>(b1);
   g.c2 = a;
@@ -226,11 +386,27 @@ mtl_status mtl_mlp_bwd(const mtl_layer_cfg* c, const void* dy, const void* h, co
   if (db2 && !aligned16(db2)) return MTL_E_ALIGN;
   const Dims d = dims_of(c);
   MlpScratch ws;
-  if (scratch_bytes < mlp_scratch(d, &ws, static_cast<char*>(scratch))) return MTL_E_WORKSPACE;
+  if (scratch_bytes < mlp_scratch(c, d, &ws, static_cast<char*>(scratch))) return MTL_E_WORKSPACE;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   const bool accum = (c->flags & MTL_F_WGRAD_ACCUM) != 0;
   const int wepi = accum ? EPI_F32_ACC : EPI_F32;
 
+  if (is_fp8(c)) {
+    // E5M2 gradients, E4M3 activations and weights; wgrad operands transposed
+    MTL_TRY(quantize(dy, ws.dy, ws.amax_ws, s));
+    MTL_TRY(quantize(w2, ws.w2, ws.amax_ws, s));
+    MTL_TRY(gemm8(ws.dy, ws.dy.q, ws.w2, ws.w2.q, d.S, d.f_l, d.h, ws.dz, d.f_l, EPI_DGELU, s, nullptr, nullptr, z));
+    MTL_TRY(quantize(a, ws.a_t, ws.amax_ws, s));
+    MTL_TRY(gemm8(ws.a_t, ws.a_t.qt, ws.dy, ws.dy.qt, d.f_l, d.h, d.S, dw2, d.h, wepi, s));
+    MTL_TRY(quantize(ws.dz, ws.dz8, ws.amax_ws, s));
+    MTL_TRY(quantize(h, ws.h_t, ws.amax_ws, s));
+    MTL_TRY(gemm8(ws.h_t, ws.h_t.qt, ws.dz8, ws.dz8.qt, d.h, d.f_l, d.S, dw1, d.f_l, wepi, s));
+    MTL_TRY(colsum_bf16(ws.dz, d.S, d.f_l, d.f_l, db1, accum, ws.ws, s));
+    if (db2) MTL_TRY(colsum_bf16(static_cast<const uint16_t*>(dy), d.S, d.h, d.h, db2, accum, ws.ws, s));
+    MTL_TRY(quantize(w1, ws.w1, ws.amax_ws, s));
+    MTL_TRY(gemm8(ws.dz8, ws.dz8.q, ws.w1, ws.w1.q, d.S, d.h, d.f_l, dh_partial, d.h, EPI_BF16, s));
+    return MTL_OK;
+  }
   // dz = (dy . w2^T) * GeLU'(z)
   GemmArgs g = gemm(dy, d.h, w2, d.h, d.S, d.f_l, d.h, ws.dz, d.f_l);
   g.aux = static_cast<const uint16_t*>(z);
@@ -261,17 +437,27 @@ mtl_status mtl_attn_bwd(const mtl_layer_cfg* c, const void* dh, const void* x, c
   if (db_o && !aligned16(db_o)) return MTL_E_ALIGN;
   const Dims d = dims_of(c);
   AttnScratch ws;
-  if (scratch_bytes < attn_scratch(d, &ws, static_cast<char*>(scratch))) return MTL_E_WORKSPACE;
+  if (scratch_bytes < attn_scratch(c, d, &ws, static_cast<char*>(scratch))) return MTL_E_WORKSPACE;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   const bool accum = (c->flags & MTL_F_WGRAD_ACCUM) != 0;
   const int wepi = accum ? EPI_F32_ACC : EPI_F32;
+  const bool f8 = is_fp8(c);
 
-  // do = dh . w_o^T
-  GemmArgs g = gemm(dh, d.h, w_o, d.h, d.S, d.o_l, d.h, ws.dout, d.o_l);
-  MTL_TRY(gemm_bf16(g, GEMM_DGRAD, EPI_BF16, s));
-  // dw_o = o^T . dh
-  g = gemm(o, d.o_l, dh, d.h, d.o_l, d.h, d.S, dw_o, d.h);
-  MTL_TRY(gemm_bf16(g, GEMM_WGRAD, wepi, s));
+  if (f8) {
+    // do = dh . w_o^T ; dw_o = o^T . dh
+    MTL_TRY(quantize(dh, ws.dh, ws.amax_ws, s));
+    MTL_TRY(quantize(w_o, ws.wo, ws.amax_ws, s));
+    MTL_TRY(gemm8(ws.dh, ws.dh.q, ws.wo, ws.wo.q, d.S, d.o_l, d.h, ws.dout, d.o_l, EPI_BF16, s));
+    MTL_TRY(quantize(o, ws.o_t, ws.amax_ws, s));
+    MTL_TRY(gemm8(ws.o_t, ws.o_t.qt, ws.dh, ws.dh.qt, d.o_l, d.h, d.S, dw_o, d.h, wepi, s));
+  } else {
+    // do = dh . w_o^T
+    GemmArgs g = gemm(dh, d.h, w_o, d.h, d.S, d.o_l, d.h, ws.dout, d.o_l);
+    MTL_TRY(gemm_bf16(g, GEMM_DGRAD, EPI_BF16, s));
+    // dw_o = o^T . dh
+    g = gemm(o, d.o_l, dh, d.h, d.o_l, d.h, d.S, dw_o, d.h);
+    MTL_TRY(gemm_bf16(g, GEMM_WGRAD, wepi, s));
+  }
   if (db_o) MTL_TRY(colsum_bf16(static_cast<const uint16_t*>(dh), d.S, d.h, d.h, db_o, accum, ws.ws, s));
 
   AttnArgs at{};
@@ -290,13 +476,48 @@ mtl_status mtl_attn_bwd(const mtl_layer_cfg* c, const void* dh, const void* x, c
   at.dqkv = ws.dqkv;
   MTL_TRY(attention_bwd(at, s));
 
+  if (f8) {
+    // dw_qkv = x^T . dqkv ; dx_partial = dqkv . w_qkv^T
+    MTL_TRY(quantize(ws.dqkv, ws.dqkv8, ws.amax_ws, s));
+    MTL_TRY(quantize(x, ws.x_t, ws.amax_ws, s));
+    MTL_TRY(gemm8(ws.x_t, ws.x_t.qt, ws.dqkv8, ws.dqkv8.qt, d.h, d.qkv_l, d.S, dw_qkv, d.qkv_l, wepi, s));
+    MTL_TRY(colsum_bf16(ws.dqkv, d.S, d.qkv_l, d.qkv_l, db_qkv, accum, ws.ws, s));
+    MTL_TRY(quantize(w_qkv, ws.wqkv, ws.amax_ws, s));
+    MTL_TRY(gemm8(ws.dqkv8, ws.dqkv8.q, ws.wqkv, ws.wqkv.q, d.S, d.h, d.qkv_l, dx_partial, d.h, EPI_BF16, s));
+    return MTL_OK;
+  }
   // dw_qkv = x^T . dqkv ; db_qkv = colsum(dqkv) ; dx_partial = dqkv . w_qkv^T
-  g = gemm(x, d.h, ws.dqkv, d.qkv_l, d.h, d.qkv_l, d.S, dw_qkv, d.qkv_l);
+  GemmArgs g = gemm(x, d.h, ws.dqkv, d.qkv_l, d.h, d.qkv_l, d.S, dw_qkv, d.qkv_l);
   MTL_TRY(gemm_bf16(g, GEMM_WGRAD, wepi, s));
   MTL_TRY(colsum_bf16(ws.dqkv, d.S, d.qkv_l, d.qkv_l, db_qkv, accum, ws.ws, s));
   g = gemm(ws.dqkv, d.qkv_l, w_qkv, d.qkv_l, d.S, d.h, d.qkv_l, dx_partial, d.h);
   MTL_TRY(gemm_bf16(g, GEMM_DGRAD, EPI_BF16, s));
   return MTL_OK;
+}
+
+// ---------------------------------------------------------------- fp8 scaling
+
+mtl_status mtl_fp8_amax(const void* x, int64_t n, int32_t format, float* rec, void* scratch, size_t scratch_bytes,
+                        mtl_stream_t stream) {
+  mtl_status st = check_ptrs(x, rec, scratch);
+  if (st != MTL_OK) return st;
+  if (n <= 0) return MTL_E_SHAPE;
+  if (format != MTL_FP8_E4M3 && format != MTL_FP8_E5M2) return MTL_E_UNSUPPORTED;
+  if (scratch_bytes < fp8_amax_ws_bytes()) return MTL_E_WORKSPACE;
+  return hip_status(fp8_amax(static_cast<const uint16_t*>(x), n, format, rec, scratch,
+                             reinterpret_cast<hipStream_t>(stream)));
+}
+
+mtl_status mtl_fp8_cast(const void* x, int64_t rows, int64_t cols, int32_t format, const float* rec, void* out,
+                        void* out_t, mtl_stream_t stream) {
+  mtl_status st = check_ptrs(x, rec);
+  if (st != MTL_OK) return st;
+  if (!out && !out_t) return MTL_E_NULL;
+  if ((out && !aligned16(out)) || (out_t && !aligned16(out_t))) return MTL_E_ALIGN;
+  if (rows <= 0 || cols <= 0 || cols % 8 != 0 || (out_t && rows % 16 != 0)) return MTL_E_SHAPE;
+  if (format != MTL_FP8_E4M3 && format != MTL_FP8_E5M2) return MTL_E_UNSUPPORTED;
+  return hip_status(fp8_cast(static_cast<const uint16_t*>(x), rows, cols, format, rec, static_cast<uint8_t*>(out),
+                             static_cast<uint8_t*>(out_t), reinterpret_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

@@ -41,6 +41,19 @@ __device__ __forceinline__ f32x16 mfma32(const u32x4& a, const u32x4& b, const f
                                                  0, 0, 0);
 }
 
+// v_mfma_f32_32x32x64_f8f6f4 with OCP fp8 operands: D[32x32] += A[32x64] * B[64x32].
+// Each operand is 32 bytes per lane (lane l: row or column l % 32, 32 k-values);
+// FA / FB select the format of a / b (0 = E4M3, 1 = E5M2).  Same result layout
+// as mfma32.  Scale operands 0 select the unscaled instruction.
+template <int FA, int FB>
+__device__ __forceinline__ f32x16 mfma32_f8(const u32x4& a0, const u32x4& a1, const u32x4& b0, const u32x4& b1,
+                                            const f32x16& c) {
+  typedef int i32x8_t __attribute__((ext_vector_type(8)));
+  const i32x8_t a = {(int)a0[0], (int)a0[1], (int)a0[2], (int)a0[3], (int)a1[0], (int)a1[1], (int)a1[2], (int)a1[3]};
+  const i32x8_t b = {(int)b0[0], (int)b0[1], (int)b0[2], (int)b0[3], (int)b1[0], (int)b1[1], (int)b1[2], (int)b1[3]};
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, FA, FB, 0, 0, 0, 0);
+}
+
 // ---------------------------------------------------------------- LDS tiles
 // A k-contiguous tile of R rows x 64 bf16 (128 B per row) is stored as eight
 // 16-byte chunks per row, chunk c of row r at physical chunk c ^ (r & 7): eight

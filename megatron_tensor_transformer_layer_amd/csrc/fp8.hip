@@ -1,0 +1,169 @@
+// fp8 per-tensor scaling for gfx950: amax and the scaled cast to OCP E4M3 / E5M2.
+//
+// Reading of the site summary's "--fp8-format hybrid" (no encoding or scaling rule
+// is printed): E4M3 for forward operands, E5M2 for gradients, current per-tensor
+// scaling s = fmt_max / amax (1 when amax is 0 or not finite), codes by
+// round-to-nearest-even of the fp32 product x*s onto the format's grid with
+// saturation to +-fmt_max; NaN gives 0x7F.
+//
+// Both kernels stream HBM with 16-byte accesses; amax is a deterministic
+// two-stage max (no atomics): max is order independent, and the magnitudes are
+// compared as bf16 bit patterns (sign cleared), which orders them like the values.
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace mtl {
+
+namespace {
+
+constexpr int AMAX_BLOCKS = 1024;
+
+__global__ __launch_bounds__(256) void amax_stage1(const uint16_t* __restrict__ x, int64_t n,
+                                                   uint32_t* __restrict__ part) {
+  uint32_t m = 0;
+  const int64_t nv = n / 8;
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t v = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; v < nv; v += stride) {
+    const u32x4 q = *reinterpret_cast<const u32x4*>(x + v * 8);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      m = max(m, q[j] & 0x7fffu);
+      m = max(m, (q[j] >> 16) & 0x7fffu);
+    }
+  }
+  // tail of n % 8 elements, block 0 only
+  if (blockIdx.x == 0)
+    for (int64_t i = nv * 8 + threadIdx.x; i < n; i += blockDim.x) m = max(m, (uint32_t)(x[i] & 0x7fffu));
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, off));
+  __shared__ uint32_t sh[4];
+  if ((threadIdx.x & 63) == 0) sh[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) part[blockIdx.x] = max(max(sh[0], sh[1]), max(sh[2], sh[3]));
+}
+
+// rec = {amax, s, 1/s}; s = fmt_max / amax with correctly rounded fp32 division.
+__global__ __launch_bounds__(256) void amax_stage2(const uint32_t* __restrict__ part, int nparts, float fmt_max,
+                                                   float* __restrict__ rec) {
+  uint32_t m = 0;
+  for (int i = threadIdx.x; i < nparts; i += blockDim.x) m = max(m, part[i]);
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, off));
+  __shared__ uint32_t sh[4];
+  if ((threadIdx.x & 63) == 0) sh[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const uint32_t bits = max(max(sh[0], sh[1]), max(sh[2], sh[3]));
+    const float amax = __uint_as_float(bits << 16);
+    const bool usable = amax > 0.f && amax <= 3.4028234663852886e38f;  // false for 0, inf, NaN
+    const float s = usable ? __fdiv_rn(fmt_max, amax) : 1.f;
+    rec[0] = amax;
+    rec[1] = s;
+    rec[2] = __fdiv_rn(1.f, s);
+  }
+}
+
+// Round the fp32 value y to the fp8 grid (M mantissa bits, exponent bias BIAS),
+// nearest-even, saturating to the largest finite code MAXC.
+template <int M, int BIAS, uint32_t MAXC>
+__device__ __forceinline__ uint32_t to_fp8(float y) {
+  const uint32_t u = __float_as_uint(y);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fu;  // NaN
+  const uint32_t sign = (u >> 24) & 0x80u;
+  const uint32_t a = u & 0x7fffffffu;
+  const int e = (int)(a >> 23) - 127;
+  uint32_t code;
+  if (e < 1 - BIAS) {
+    // below the smallest normal: an integer count of the subnormal step
+    // 2^(1 - BIAS - M); exact scaling by a power of two, then RNE
+    code = (uint32_t)rintf(__uint_as_float(a) * __uint_as_float((uint32_t)(127 + M + BIAS - 1) << 23));
+  } else {
+    constexpr int SH = 23 - M;
+    const uint32_t r = a + ((1u << (SH - 1)) - 1u) + ((a >> SH) & 1u);  // RNE on the dropped bits
+    const int e2 = (int)(r >> 23) - 127;
+    code = ((uint32_t)(e2 + BIAS) << M) | ((r >> SH) & ((1u << M) - 1u));
+    code = min(code, MAXC);
+  }
+  return sign | code;
+}
+
+template <int FMT>
+__device__ __forceinline__ uint32_t encode(float y) {
+  if constexpr (FMT == 0) return to_fp8<3, 7, 0x7eu>(y);
+  else return to_fp8<2, 15, 0x7bu>(y);
+}
+
+// Tile of 64 rows x 64 columns per workgroup: each thread converts 16 elements
+// (two 8-element vectors), writes the row-major codes directly and stages them
+// in LDS for the transposed copy, which is written as 16 consecutive rows of one
+// column per thread.
+template <int FMT>
+__global__ __launch_bounds__(256) void cast_kernel(const uint16_t* __restrict__ x, int64_t rows, int64_t cols,
+                                                   const float* __restrict__ rec, uint8_t* __restrict__ out,
+                                                   uint8_t* __restrict__ out_t) {
+  __shared__ uint8_t tile[64][64 + 4];
+  const float s = rec[1];
+  const int64_t r0 = (int64_t)blockIdx.y * 64, c0 = (int64_t)blockIdx.x * 64;
+  const int tr = threadIdx.x >> 3, tc = (threadIdx.x & 7) * 8;
+#pragma unroll
+  for (int pass = 0; pass < 2; ++pass) {
+    const int lr = tr + pass * 32;
+    const int64_t r = r0 + lr, c = c0 + tc;
+    if (r < rows && c < cols) {
+      const u32x4 q = *reinterpret_cast<const u32x4*>(x + r * cols + c);
+      uint32_t w0 = 0, w1 = 0;
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        w0 |= encode<FMT>(__fmul_rn(bf16_lo(q[j]), s)) << (16 * j);
+        w0 |= encode<FMT>(__fmul_rn(bf16_hi(q[j]), s)) << (16 * j + 8);
+        w1 |= encode<FMT>(__fmul_rn(bf16_lo(q[j + 2]), s)) << (16 * j);
+        w1 |= encode<FMT>(__fmul_rn(bf16_hi(q[j + 2]), s)) << (16 * j + 8);
+      }
+      if (out) *reinterpret_cast<u32x2*>(out + r * cols + c) = u32x2{w0, w1};
+      *reinterpret_cast<uint32_t*>(&tile[lr][tc]) = w0;
+      *reinterpret_cast<uint32_t*>(&tile[lr][tc + 4]) = w1;
+    }
+  }
+  if (!out_t) return;
+  __syncthreads();
+  // thread -> column lc, rows seg*16 .. seg*16+15
+  const int lc = threadIdx.x & 63, seg = threadIdx.x >> 6;
+  const int64_t c = c0 + lc, rbase = r0 + seg * 16;
+  if (c < cols && rbase < rows) {
+    u32x4 o;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      uint32_t v = 0;
+#pragma unroll
+      for (int b = 0; b < 4; ++b) v |= (uint32_t)tile[seg * 16 + 4 * w + b][lc] << (8 * b);
+      o[w] = v;
+    }
+    *reinterpret_cast<u32x4*>(out_t + c * rows + rbase) = o;
+  }
+}
+
+}  // namespace
+
+size_t fp8_amax_ws_bytes() { return AMAX_BLOCKS * sizeof(uint32_t); }
+
+hipError_t fp8_amax(const uint16_t* x, int64_t n, int fmt, float* rec, void* ws, hipStream_t s) {
+  const int64_t nv = n / 8;
+  const int blocks = (int)std::max<int64_t>(1, std::min<int64_t>(AMAX_BLOCKS, (nv + 1023) / 1024));
+  uint32_t* part = static_cast<uint32_t*>(ws);
+  hipLaunchKernelGGL(amax_stage1, dim3(blocks), dim3(256), 0, s, x, n, part);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(amax_stage2, dim3(1), dim3(256), 0, s, part, blocks, fmt == 0 ? 448.f : 57344.f, rec);
+  return hipGetLastError();
+}
+
+hipError_t fp8_cast(const uint16_t* x, int64_t rows, int64_t cols, int fmt, const float* rec, uint8_t* out,
+                    uint8_t* out_t, hipStream_t s) {
+  if (rows <= 0 || cols <= 0 || (!out && !out_t)) return hipSuccess;
+  const dim3 grid((unsigned)((cols + 63) / 64), (unsigned)((rows + 63) / 64));
+  if (fmt == 0) hipLaunchKernelGGL(cast_kernel<0>, grid, dim3(256), 0, s, x, rows, cols, rec, out, out_t);
+  else hipLaunchKernelGGL(cast_kernel<1>, grid, dim3(256), 0, s, x, rows, cols, rec, out, out_t);
+  return hipGetLastError();
+}
+
+}  // namespace mtl

@@ -52,15 +52,19 @@ __device__ __forceinline__ int mn_swz(int k) {
   else return ((k >> 1) & 1) << 2;
 }
 
-template <int ROWS, bool KC>
+template <int ROWS, bool KC, int EB = 2>
 struct Operand {
-  static constexpr int BYTES = ROWS * 128;     // one 64-deep slab
+  static_assert(EB == 2 || KC, "fp8 operands are k-contiguous");
+  static constexpr int BYTES = ROWS * 128;     // one slab: 128 bytes of k per row
+  static constexpr int KSLAB = 128 / EB;       // k per slab: 64 bf16 or 128 fp8
+  static constexpr int CHUNK = 16 / EB;        // k per 16-byte chunk
   static constexpr int INSTR = BYTES / 1024;   // wave instructions per slab
   static constexpr int PER_WAVE = INSTR / 4;
   static constexpr int ROWB = ROWS * 2;        // row bytes of the mn-contiguous layout
-  static constexpr int READS = KC ? 1 : 2;     // LDS read instructions per fragment
+  static constexpr int READS = (KC && EB == 2) ? 1 : 2;  // LDS read instructions per fragment
 
-  // Issue the DMA of slab [k0, k0+64) of rows [row0, row0+ROWS) into lds.
+  // Issue the DMA of slab [k0, k0+KSLAB) of rows [row0, row0+ROWS) into lds
+  // (ld and k0 in elements).
   // k-contiguous: wave instruction I fills rows 8I..8I+7, lane -> (row 8I + l/8,
   // physical chunk l%8 = logical chunk ^ kc_swz(row)).
   // mn-contiguous: lds byte o = 1024 I + 16 l is (k = o / ROWB, physical chunk
@@ -77,7 +81,7 @@ struct Operand {
       if constexpr (KC) {
         const int row = I * 8 + (lane >> 3);
         const int c = (lane & 7) ^ kc_swz(row);
-        voff = (uint32_t)(((int64_t)(row0 + row) * ld + k0 + c * 8) * 2);
+        voff = (uint32_t)(((int64_t)(row0 + row) * ld + k0 + c * CHUNK) * EB);
       } else {
         const int o = I * 1024 + lane * 16;
         const int k = o / ROWB;
@@ -88,7 +92,7 @@ struct Operand {
     }
   }
 
-  // k-contiguous operand of a slab with kvalid < 64 valid k (after its DMA has
+  // k-contiguous operand of a slab with kvalid < KSLAB valid k (after its DMA has
   // landed): zero the chunks past K, which hold the next row's values.
   static __device__ __forceinline__ void zero_tail(LDS_AS char* lds, int kvalid) {
     if constexpr (KC) {
@@ -97,9 +101,19 @@ struct Operand {
       for (int q = 0; q < PER_WAVE; ++q) {
         const int I = wave * PER_WAVE + q;
         const int c = (lane & 7) ^ kc_swz(I * 8 + (lane >> 3));
-        if (c * 8 >= kvalid) *reinterpret_cast<LDS_AS u32x4*>(lds + I * 1024 + lane * 16) = u32x4{0, 0, 0, 0};
+        if (c * CHUNK >= kvalid) *reinterpret_cast<LDS_AS u32x4*>(lds + I * 1024 + lane * 16) = u32x4{0, 0, 0, 0};
       }
     }
+  }
+
+  // fp8 fragment of 32-row block r32 at k step kk (64 deep): lane l holds row
+  // (l % 32) and k = kk*64 + (l/32)*32 + j, j = 0..31, as two 16-byte chunks.
+  static __device__ __forceinline__ void frag8(const LDS_AS char* lds, int r32, int kk, int lane, u32x4& lo,
+                                               u32x4& hi) {
+    const int row = r32 * 32 + (lane & 31);
+    const int c = kk * 4 + (lane >> 5) * 2;
+    lo = *reinterpret_cast<const LDS_AS u32x4*>(lds + row * 128 + ((c ^ kc_swz(row)) << 4));
+    hi = *reinterpret_cast<const LDS_AS u32x4*>(lds + row * 128 + (((c + 1) ^ kc_swz(row)) << 4));
   }
 
   // Operand fragment of 32-row block r32 at k step kk (16 deep): lane l holds
@@ -130,12 +144,18 @@ __device__ __forceinline__ int tile_index(int w, int ntiles) {
   return w;
 }
 
-template <int BM, int BN, bool A_K, bool B_K>
+// F8 = 0: bf16 operands.  F8 = 1 + FA + 2*FB: fp8 operands, A in format FA and
+// B in format FB (0 = E4M3, 1 = E5M2), both k-contiguous.
+template <int BM, int BN, bool A_K, bool B_K, int F8 = 0>
 struct Mainloop {
   static constexpr int WM = BM / 2, WN = BN / 2;
   static constexpr int TM = WM / 32, TN = WN / 32;
-  using OA = Operand<BM, A_K>;
-  using OB = Operand<BN, B_K>;
+  static constexpr int EB = F8 ? 1 : 2;
+  static constexpr int FA = F8 ? (F8 - 1) & 1 : 0, FB = F8 ? (F8 - 1) >> 1 : 0;
+  using OA = Operand<BM, A_K, EB>;
+  using OB = Operand<BN, B_K, EB>;
+  static constexpr int KSLAB = OA::KSLAB;
+  static constexpr int KSTEPS = F8 ? 2 : 4;  // MFMA k steps per slab
   static constexpr int STAGE = OA::BYTES + OB::BYTES;
 
   static __device__ __forceinline__ void issue(const GemmArgs& p, i32x4 ra, i32x4 rb, int m0, int n0, int k0,
@@ -148,13 +168,17 @@ struct Mainloop {
     // wait for this thread's DMAs; clear the k tail of a partial last slab
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     const int kvalid = p.K - k0;
-    if (kvalid < 64) {
+    if (kvalid < KSLAB) {
       OA::zero_tail(st, kvalid);
       OB::zero_tail(st + OA::BYTES, kvalid);
     }
   }
   static __device__ __forceinline__ void compute(const LDS_AS char* st, int wm, int wn, int lane,
                                                  f32x16 (&acc)[TM][TN]) {
+    if constexpr (F8 != 0) {
+      compute_f8(st, wm, wn, lane, acc);
+      return;
+    }
     const LDS_AS char* sa = st;
     const LDS_AS char* sb = st + OA::BYTES;
     u32x4 fa[2][TM], fb[2][TN];
@@ -192,11 +216,51 @@ struct Mainloop {
     }
     __builtin_amdgcn_sched_group_barrier(0x008, NM, 0);
   }
+  // fp8: two 64-deep k steps per slab, the same read/MFMA interleave.
+  static __device__ __forceinline__ void compute_f8(const LDS_AS char* st, int wm, int wn, int lane,
+                                                    f32x16 (&acc)[TM][TN]) {
+    const LDS_AS char* sa = st;
+    const LDS_AS char* sb = st + OA::BYTES;
+    u32x4 fa[2][TM][2], fb[2][TN][2];
+#pragma unroll
+    for (int i = 0; i < TM; ++i) OA::frag8(sa, wm * TM + i, 0, lane, fa[0][i][0], fa[0][i][1]);
+#pragma unroll
+    for (int j = 0; j < TN; ++j) OB::frag8(sb, wn * TN + j, 0, lane, fb[0][j][0], fb[0][j][1]);
+#pragma unroll
+    for (int kk = 0; kk < KSTEPS; ++kk) {
+      const int cur = kk & 1, nxt = cur ^ 1;
+      if (kk + 1 < KSTEPS) {
+#pragma unroll
+        for (int i = 0; i < TM; ++i) OA::frag8(sa, wm * TM + i, kk + 1, lane, fa[nxt][i][0], fa[nxt][i][1]);
+#pragma unroll
+        for (int j = 0; j < TN; ++j) OB::frag8(sb, wn * TN + j, kk + 1, lane, fb[nxt][j][0], fb[nxt][j][1]);
+      }
+      // operands swapped as in the bf16 path: the B fragment goes first
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+          acc[i][j] = mfma32_f8<FB, FA>(fb[cur][j][0], fb[cur][j][1], fa[cur][i][0], fa[cur][i][1], acc[i][j]);
+    }
+    constexpr int NR = 2 * (TM + TN);
+    constexpr int NM = TM * TN;
+    __builtin_amdgcn_sched_group_barrier(0x100, NR, 0);
+#pragma unroll
+    for (int kk = 0; kk < KSTEPS - 1; ++kk) {
+#pragma unroll
+      for (int x = 0; x < NM; ++x) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        if (x < NR) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, NM, 0);
+  }
 };
 
-template <int BM, int BN, bool A_K, bool B_K, int EPI>
+template <int BM, int BN, bool A_K, bool B_K, int EPI, int F8 = 0>
 __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmArgs p) {
-  using ML = Mainloop<BM, BN, A_K, B_K>;
+  using ML = Mainloop<BM, BN, A_K, B_K, F8>;
+  constexpr int EB = ML::EB, KSLAB = ML::KSLAB;
   constexpr int WM = ML::WM, WN = ML::WN, TM = ML::TM, TN = ML::TN;
   __shared__ __attribute__((aligned(1024))) char st0_[ML::STAGE];
   __shared__ __attribute__((aligned(1024))) char st1_[ML::STAGE];
@@ -264,9 +328,9 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmArgs p) {
 
   // Buffer resources: k-contiguous operands end after their last row (M or N),
   // mn-contiguous ones after row K, so everything past the matrix reads as 0.
-  const i32x4 ra = make_rsrc(p.a, (uint32_t)((A_K ? (int64_t)p.M : (int64_t)p.K) * p.lda * 2));
-  const i32x4 rb = make_rsrc(p.b, (uint32_t)((B_K ? (int64_t)p.N : (int64_t)p.K) * p.ldb * 2));
-  const int nk = (p.K + 63) / 64;
+  const i32x4 ra = make_rsrc(p.a, (uint32_t)((A_K ? (int64_t)p.M : (int64_t)p.K) * p.lda * EB));
+  const i32x4 rb = make_rsrc(p.b, (uint32_t)((B_K ? (int64_t)p.N : (int64_t)p.K) * p.ldb * EB));
+  const int nk = (p.K + KSLAB - 1) / KSLAB;
   ML::issue(p, ra, rb, m0, n0, 0, st0);
   ML::settle(p, 0, st0);
   __syncthreads();
@@ -274,14 +338,14 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmArgs p) {
   // object; an odd last slab is finished after the loop.
   int kt = 0;
   for (; kt + 1 < nk; kt += 2) {
-    ML::issue(p, ra, rb, m0, n0, (kt + 1) * 64, st1);
+    ML::issue(p, ra, rb, m0, n0, (kt + 1) * KSLAB, st1);
     ML::compute(st0, wm, wn, lane, acc);
-    ML::settle(p, (kt + 1) * 64, st1);
+    ML::settle(p, (kt + 1) * KSLAB, st1);
     __syncthreads();
     const bool more = kt + 2 < nk;
-    if (more) ML::issue(p, ra, rb, m0, n0, (kt + 2) * 64, st0);
+    if (more) ML::issue(p, ra, rb, m0, n0, (kt + 2) * KSLAB, st0);
     ML::compute(st1, wm, wn, lane, acc);
-    if (more) ML::settle(p, (kt + 2) * 64, st0);
+    if (more) ML::settle(p, (kt + 2) * KSLAB, st0);
     __syncthreads();
   }
   if (kt < nk) ML::compute(st0, wm, wn, lane, acc);
@@ -309,6 +373,9 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmArgs p) {
   static_assert(IPP >= 1, "epilogue staging does not fit");
   const int mw = m0 + wm * WM, nw = n0 + wn * WN;
 
+  // fp8: the product of the two operands' dequantisation factors
+  float dq = 1.f;
+  if constexpr (F8 != 0) dq = *p.scale_a * *p.scale_b;
   float bias_v[TN][4][4];
   if constexpr (HAS_BIAS) {
     u32x2 braw[TN][4];
@@ -345,6 +412,10 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmArgs p) {
 #pragma unroll
           for (int g = 0; g < 4; ++g) {
             float v[4] = {acc[i][j][4 * g + 0], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]};
+            if constexpr (F8 != 0) {
+#pragma unroll
+              for (int e = 0; e < 4; ++e) v[e] *= dq;
+            }
             if constexpr (HAS_BIAS) {
 #pragma unroll
               for (int e = 0; e < 4; ++e) v[e] += bias_v[j][g][e];
@@ -404,7 +475,7 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmArgs p) {
   }
 }
 
-template <int BM, int BN, bool A_K, bool B_K, int EPI>
+template <int BM, int BN, bool A_K, bool B_K, int EPI, int F8 = 0>
 static hipError_t launch_cfg(const GemmArgs& p, hipStream_t s) {
   int64_t tiles;
   if (p.offsets == nullptr) {
@@ -416,7 +487,7 @@ static hipError_t launch_cfg(const GemmArgs& p, hipStream_t s) {
     tiles = (int64_t)p.groups * ((p.M + BM - 1) / BM) * ((p.N + BN - 1) / BN);
   }
   if (tiles <= 0) return hipSuccess;
-  hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, A_K, B_K, EPI>), dim3((unsigned)tiles), dim3(256), 0, s, p);
+  hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, A_K, B_K, EPI, F8>), dim3((unsigned)tiles), dim3(256), 0, s, p);
   return hipGetLastError();
 }
 
@@ -456,6 +527,34 @@ hipError_t gemm_bf16(const GemmArgs& p, GemmLayout layout, int epi, hipStream_t 
       if (epi == EPI_F32) return launch_layout<false, false, EPI_F32>(p, s);
       if (epi == EPI_F32_ACC) return launch_layout<false, false, EPI_F32_ACC>(p, s);
       break;
+  }
+  return hipErrorInvalidValue;
+}
+
+template <int EPI, int F8>
+static hipError_t launch_f8(const GemmArgs& p, hipStream_t s) {
+  const long t256 = (long)((p.M + 255) / 256) * ((p.N + 255) / 256);
+  if (t256 >= 240) return launch_cfg<256, 256, true, true, EPI, F8>(p, s);
+  return launch_cfg<128, 128, true, true, EPI, F8>(p, s);
+}
+
+hipError_t gemm_fp8(const GemmArgs& p, int fmt_a, int fmt_b, int epi, hipStream_t s) {
+  if (p.M <= 0 || p.N <= 0) return hipSuccess;
+  if (p.offsets || p.K <= 0 || p.K % 16 || p.lda % 16 || p.ldb % 16 || !p.scale_a || !p.scale_b)
+    return hipErrorInvalidValue;
+  if (((int64_t)p.M + 256) * p.lda >= ((int64_t)1 << 32) || ((int64_t)p.N + 256) * p.ldb >= ((int64_t)1 << 32))
+    return hipErrorInvalidValue;
+  const int f8 = 1 + fmt_a + 2 * fmt_b;
+  if (f8 == 1) {  // forward: E4M3 x E4M3
+    if (epi == EPI_BF16) return launch_f8<EPI_BF16, 1>(p, s);
+    if (epi == EPI_BF16_BIAS) return launch_f8<EPI_BF16_BIAS, 1>(p, s);
+    if (epi == EPI_BIAS_GELU) return launch_f8<EPI_BIAS_GELU, 1>(p, s);
+  } else if (f8 == 2) {  // dgrad: E5M2 gradient x E4M3 weight
+    if (epi == EPI_BF16) return launch_f8<EPI_BF16, 2>(p, s);
+    if (epi == EPI_DGELU) return launch_f8<EPI_DGELU, 2>(p, s);
+  } else if (f8 == 3) {  // wgrad: E4M3 activation x E5M2 gradient
+    if (epi == EPI_F32) return launch_f8<EPI_F32, 3>(p, s);
+    if (epi == EPI_F32_ACC) return launch_f8<EPI_F32_ACC, 3>(p, s);
   }
   return hipErrorInvalidValue;
 }

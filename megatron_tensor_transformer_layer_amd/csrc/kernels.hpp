@@ -43,6 +43,9 @@ struct GemmArgs {
   int groups;
   int group_mode;
   int64_t stride_b, stride_c;
+  // fp8 operands (gemm_fp8): each operand's dequantisation factor 1/s (device scalars)
+  const float* scale_a;
+  const float* scale_b;
 };
 
 enum GemmGroupMode : int { GROUP_M = 0, GROUP_K = 1 };
@@ -54,6 +57,13 @@ int64_t gemm_group_m_grid(int64_t max_rows, int groups, int N);
 // k-contiguous, M % 8 == 0 when A is mn-contiguous, N % 8 == 0 always,
 // 16-byte aligned base pointers and leading dimensions multiple of 8.
 hipError_t gemm_bf16(const GemmArgs& p, GemmLayout layout, int epi, hipStream_t s);
+
+// fp8 GEMM: C = (A . B^T) * (*scale_a) * (*scale_b), fp32 accumulate, with the
+// epilogues above.  A [M][K] and B [N][K] are fp8 codes (both k-contiguous; a, b
+// point at bytes, lda/ldb in bytes), fmt_a/fmt_b 0 = E4M3, 1 = E5M2.  Supported:
+// (E4M3, E4M3) with BF16 / BF16_BIAS / BIAS_GELU, (E5M2, E4M3) with BF16 / DGELU,
+// (E4M3, E5M2) with F32 / F32_ACC.  K % 16 == 0, lda and ldb % 16 == 0, not grouped.
+hipError_t gemm_fp8(const GemmArgs& p, int fmt_a, int fmt_b, int epi, hipStream_t s);
 
 // ---------------------------------------------------------------- attention
 // Causal attention over `heads` heads of a head-interleaved QKV tensor
@@ -85,6 +95,17 @@ hipError_t reduce_partials(int t, const uint16_t* const* partials, const uint16_
 size_t colsum_ws_floats(int64_t rows, int64_t cols);
 hipError_t colsum_bf16(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld, float* out, bool accumulate,
                        float* ws, hipStream_t s);
+
+// ---------------------------------------------------------------- fp8 scaling
+// rec[0..2] = {amax, s, 1/s} of n bf16 values for format fmt (0 = E4M3, 1 = E5M2);
+// ws holds fp8_amax_ws_bytes().
+size_t fp8_amax_ws_bytes();
+hipError_t fp8_amax(const uint16_t* x, int64_t n, int fmt, float* rec, void* ws, hipStream_t s);
+// codes of x [rows, cols] (bf16) scaled by rec[1]: out [rows, cols] and/or
+// out_t [cols, rows] (either may be null).  cols % 8 == 0; rows % 16 == 0 when
+// out_t is given; 16-byte aligned pointers.
+hipError_t fp8_cast(const uint16_t* x, int64_t rows, int64_t cols, int fmt, const float* rec, uint8_t* out,
+                    uint8_t* out_t, hipStream_t s);
 
 // ---------------------------------------------------------------- MoE data movement
 // Top-k expert ids per token (descending logit, ties to the lower id) and the

@@ -61,9 +61,10 @@ class RankState:
     """All device buffers of one TP rank: shard weights, saved activations,
     partial outputs, gradients and scratch."""
 
-    def __init__(self, shape, tp: int, rank: int, shard: dict, flags: int = 0, device=DEV):
+    def __init__(self, shape, tp: int, rank: int, shard: dict, flags: int = 0, device=DEV,
+                 precision: int = MTL_PREC_BF16):
         self.cfg = make_cfg(shape.hidden, shape.heads, shape.ffn, shape.seq, shape.micro_batch, tp, rank,
-                            MTL_PREC_BF16, flags)
+                            precision, flags)
         D = self.D = dims_of(shape.hidden, shape.heads, shape.ffn, shape.seq, shape.micro_batch, tp)
         self.w = {k: bf16_dev(shard[k], device) for k in ("w_qkv", "b_qkv", "w_o", "w1", "b1", "w2")}
         self.qkv = empty_bf16(D.S, D.qkv_l, device=device)
@@ -88,10 +89,11 @@ class RankState:
 
     def attn_fwd(self, x):
         mtl_attn_fwd(self.cfg, x, self.w["w_qkv"], self.w["b_qkv"], self.w["w_o"], self.qkv, self.o, self.lse,
-                     self.p_attn)
+                     self.p_attn, self.scratch)
 
     def mlp_fwd(self, h):
-        mtl_mlp_fwd(self.cfg, h, self.w["w1"], self.w["b1"], self.w["w2"], self.z, self.a, self.p_mlp)
+        mtl_mlp_fwd(self.cfg, h, self.w["w1"], self.w["b1"], self.w["w2"], self.z, self.a, self.p_mlp,
+                    self.scratch)
 
     def mlp_bwd(self, dy, h, want_db2=True):
         mtl_mlp_bwd(self.cfg, dy, h, self.z, self.a, self.w["w1"], self.w["w2"], self.p_dh, self.dw1, self.db1,
@@ -103,10 +105,10 @@ class RankState:
 
 
 def run_sharded_layer(shape, tp: int, shards: list, x_bits, b_o_bits, b2_bits, dy_bits, residual: bool = False,
-                      device=DEV) -> dict:
+                      precision: int = MTL_PREC_BF16, device=DEV) -> dict:
     """Run the whole layer as tp rank shards plus the four full reductions on
     one device; returns host fp64 copies of every output."""
-    ranks = [RankState(shape, tp, r, shards[r], device=device) for r in range(tp)]
+    ranks = [RankState(shape, tp, r, shards[r], device=device, precision=precision) for r in range(tp)]
     D = ranks[0].D
     x = bf16_dev(x_bits, device)
     b_o = bf16_dev(b_o_bits, device)

@@ -81,9 +81,9 @@ def test_errors_before_launch(mtl):
     cfg = mtl.make_cfg(256, 2, 512, 64, 1, 2, 0)
     P = 1 << 20  # a fake, aligned address
     lib = mtl.lib()
-    st = lib.mtl_attn_fwd(ctypes.byref(cfg), None, P, P, P, P, P, P, P, None)
+    st = lib.mtl_attn_fwd(ctypes.byref(cfg), None, P, P, P, P, P, P, P, None, 0, None)
     assert st == mtl.MTL_E_NULL
-    st = lib.mtl_attn_fwd(ctypes.byref(cfg), P + 2, P, P, P, P, P, P, P, None)
+    st = lib.mtl_attn_fwd(ctypes.byref(cfg), P + 2, P, P, P, P, P, P, P, None, 0, None)
     assert st == mtl.MTL_E_ALIGN
     st = lib.mtl_mlp_bwd(ctypes.byref(cfg), P, P, P, P, P, P, P, P, P, P, None, P, 16, None)
     assert st == mtl.MTL_E_WORKSPACE
@@ -147,3 +147,33 @@ def test_moe_errors_before_launch(mtl):
     args[3] = None
     assert lib.mtl_moe_fwd(ctypes.byref(cfg), *args, None) == mtl.MTL_E_NULL
     assert lib.mtl_moe_bwd(ctypes.byref(cfg), *([P] * 17), 16, None) == mtl.MTL_E_WORKSPACE
+
+
+def test_fp8_validate_and_errors_before_launch(mtl):
+    ok = dict(hidden=4096, heads=32, ffn=16384, seq=4096, micro_batch=1, tp=4, rank=0,
+              precision=mtl.MTL_PREC_FP8_HYBRID)
+    assert mtl.mtl_validate(mtl.make_cfg(**ok)) == mtl.MTL_OK
+    # fp8 GEMMs contract over 16-byte code chunks
+    assert mtl.mtl_validate(mtl.make_cfg(**{**ok, "seq": 4088})) == mtl.MTL_E_SHAPE
+    assert mtl.mtl_validate(mtl.make_cfg(**{**ok, "ffn": 4 * 4104})) == mtl.MTL_E_SHAPE
+    assert mtl.mtl_validate(mtl.make_cfg(**{**ok, "seq": 4088, "precision": mtl.MTL_PREC_BF16})) == mtl.MTL_OK
+    # fp8 needs scratch in the forward calls too, for the operands' codes
+    n8 = mtl.mtl_workspace_bytes(mtl.make_cfg(**ok))
+    n16 = mtl.mtl_workspace_bytes(mtl.make_cfg(**{**ok, "precision": mtl.MTL_PREC_BF16}))
+    assert n8 > n16
+    cfg = mtl.make_cfg(**ok)
+    P = 1 << 20
+    lib = mtl.lib()
+    assert lib.mtl_attn_fwd(ctypes.byref(cfg), P, P, P, P, P, P, P, P, None, 0, None) == mtl.MTL_E_NULL
+    assert lib.mtl_attn_fwd(ctypes.byref(cfg), P, P, P, P, P, P, P, P, P, 64, None) == mtl.MTL_E_WORKSPACE
+    assert lib.mtl_mlp_fwd(ctypes.byref(cfg), P, P, P, P, P, P, P, P, 64, None) == mtl.MTL_E_WORKSPACE
+    assert lib.mtl_mlp_bwd(ctypes.byref(cfg), P, P, P, P, P, P, P, P, P, P, None, P, n16, None) == \
+        mtl.MTL_E_WORKSPACE
+    # the standalone amax / cast calls
+    assert lib.mtl_fp8_amax(P, 1024, 0, P, P, 64, None) == mtl.MTL_E_WORKSPACE
+    assert lib.mtl_fp8_amax(P, 0, 0, P, P, mtl.MTL_FP8_AMAX_SCRATCH, None) == mtl.MTL_E_SHAPE
+    assert lib.mtl_fp8_amax(P, 1024, 2, P, P, mtl.MTL_FP8_AMAX_SCRATCH, None) == mtl.MTL_E_UNSUPPORTED
+    assert lib.mtl_fp8_cast(P, 64, 12, 0, P, P, None, None) == mtl.MTL_E_SHAPE  # cols % 8
+    assert lib.mtl_fp8_cast(P, 40, 16, 0, P, None, P, None) == mtl.MTL_E_SHAPE  # transposed needs rows % 16
+    assert lib.mtl_fp8_cast(P, 64, 16, 0, P, None, None, None) == mtl.MTL_E_NULL
+    assert lib.mtl_fp8_cast(P, 64, 16, 0, P, P + 8, None, None) == mtl.MTL_E_ALIGN

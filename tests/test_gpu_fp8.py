@@ -1,0 +1,198 @@
+"""fp8 path on the GPU.
+
+* amax and the scaled cast (E4M3 / E5M2) are bit-exact against the oracle:
+  the scale record {amax, s, 1/s} and every code, on tensors that reach every
+  code point and every rounding tie (all bf16 values within the format's range
+  at scale 1), on Gaussian tensors (s not a power of two), on zeros, and on
+  tensors holding inf and NaN; the transposed copy is the transpose.
+* The whole tensor-parallel layer in fp8 (all shards on one device) against
+  both references: the fp64 layer with quantised GEMM operands (the same
+  recipe in exact arithmetic) within the bf16 bound, and the plain fp64 layer
+  on the unquantised inputs within 8e-2 * max|ref| -- or, for outputs where the
+  recipe's own quantisation error already exceeds that (gradients that pass
+  through several E5M2 operands), within that error plus the bf16 bound.
+"""
+import numpy as np
+import pytest
+
+import synth
+from oracle import fp8 as Q
+from oracle import fp8_layer as F8
+from oracle import layer as L
+from tests.parity_util import BF16_ABS, BF16_REL, FP8_REL, assert_bf16, f64, full_params
+
+FMT = {0: Q.E4M3, 1: Q.E5M2}
+
+
+def _bits_within(limit):
+    """Every finite bf16 bit pattern with |value| <= limit (both signs)."""
+    bits = np.arange(65536, dtype=np.uint16)
+    v = synth.bf16_bits_to_f64(bits)
+    return bits[np.isfinite(v) & (np.abs(v) <= limit)]
+
+
+def _cast_case(name):
+    rng = np.random.default_rng(7)
+    if name == "grid-e4m3":
+        return _bits_within(448.0), 0
+    if name == "grid-e5m2":
+        return _bits_within(57344.0), 1
+    if name in ("gauss-e4m3", "gauss-e5m2"):
+        return synth.bf16_round_bits(rng.standard_normal(4096 * 48) * 3.7), int(name.endswith("e5m2"))
+    if name == "zeros":
+        return np.zeros(4096, np.uint16), 0
+    if name == "inf-nan":
+        b = synth.bf16_round_bits(rng.standard_normal(4096))
+        b[17], b[1000], b[2001] = 0x7F80, 0xFF80, 0x7FC1  # +inf, -inf, NaN
+        return b, 1
+    raise KeyError(name)
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("case", ["grid-e4m3", "grid-e5m2", "gauss-e4m3", "gauss-e5m2", "zeros", "inf-nan"])
+def test_amax_and_cast_bit_exact(mtl, case):
+    import torch
+    from megatron_tensor_transformer_layer_amd.layer import bf16_dev
+    bits, fmt = _cast_case(case)
+    cols = 64
+    n = (len(bits) + 16 * cols - 1) // (16 * cols) * 16 * cols
+    bits = np.concatenate([bits, np.zeros(n - len(bits), np.uint16)])  # pad with zeros: amax unchanged
+    rows = n // cols
+    print(f"cast case {case}: {rows} x {cols}, format {fmt}", flush=True)
+    x = bf16_dev(bits.reshape(rows, cols))
+    rec = torch.zeros(4, dtype=torch.float32, device="cuda")
+    ws = torch.empty(mtl.MTL_FP8_AMAX_SCRATCH, dtype=torch.uint8, device="cuda")
+    out = torch.empty(rows, cols, dtype=torch.uint8, device="cuda")
+    out_t = torch.empty(cols, rows, dtype=torch.uint8, device="cuda")
+    mtl.mtl_fp8_amax(x, rows * cols, fmt, rec, ws)
+    mtl.mtl_fp8_cast(x, rows, cols, fmt, rec, out, out_t)
+    torch.cuda.synchronize()
+    got_rec = rec.cpu().numpy()
+    vals = synth.bf16_bits_to_f32(bits)
+    with np.errstate(invalid="ignore"):
+        amax = Q.amax(vals)
+    codes, s, sinv = Q.quantize(vals, FMT[fmt])
+    if np.isnan(amax):
+        assert np.isnan(got_rec[0])
+    else:
+        assert got_rec[0].tobytes() == np.float32(amax).tobytes()
+    assert got_rec[1].tobytes() == np.float32(s).tobytes()
+    assert got_rec[2].tobytes() == np.float32(sinv).tobytes()
+    got = out.cpu().numpy()
+    assert np.array_equal(got.reshape(-1), codes), np.flatnonzero(got.reshape(-1) != codes)[:10]
+    assert np.array_equal(out_t.cpu().numpy(), got.T)
+
+
+FP8_CASES = {
+    "gpt2-small-tp2": (synth.WORKLOADS["gpt2-small-tp2"], False),
+    # TP=4 with residual connections, 144 tokens (9 row tiles of 16), d = 64
+    "tp4-residual": (synth.LayerShape(hidden=512, heads=8, ffn=1024, seq=144, micro_batch=1, tp=4), True),
+    # d = 128, two micro-batch elements, ffn/t = 272
+    "d128-mb2-tp2": (synth.LayerShape(hidden=256, heads=2, ffn=544, seq=96, micro_batch=2, tp=2), False),
+}
+
+
+def _bf16(t):
+    """The bf16 value the device stores for t (round to nearest even)."""
+    return synth.bf16_bits_to_f64(synth.bf16_round_bits(np.asarray(t, dtype=np.float64)))
+
+
+# The reference with quantised operands, taking each quantisation decision from
+# the bf16 value the device holds (inputs are bf16 already, so this only
+# touches the intermediates A, O, H, dZ, dH, dQKV).
+def _q4(t):
+    return F8.q4(_bf16(t))
+
+
+def _q5(t):
+    return F8.q5(_bf16(t))
+
+
+def _rms(t):
+    return float(np.sqrt(np.mean(np.square(t))))
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("case", list(FP8_CASES))
+def test_fp8_layer_error_is_the_recipe_error(mtl, case):
+    """The whole layer in fp8 against the plain fp64 layer on the unquantised
+    inputs.  Requirement per output: max|diff| <= 8e-2 * max|ref|, or -- where
+    the recipe's own quantisation error (the quantised-operand reference against
+    the plain one) is already larger -- no more than 1.5 times that error; and
+    in RMS no more than 1.25 times the recipe's RMS error plus 1% of the
+    output's RMS.  A device result whose fp8 error is larger than the recipe's
+    (a wrong scale, operand or format) fails the RMS bound by far."""
+    from megatron_tensor_transformer_layer_amd.layer import run_sharded_layer
+    shape, residual = FP8_CASES[case]
+    print(f"fp8 case {case} {shape} residual={residual}", flush=True)
+    full = synth.layer_inputs(shape, seed=0)
+    shards = [synth.layer_inputs(shape, seed=0, tp=shape.tp, rank=r) for r in range(shape.tp)]
+    got = run_sharded_layer(shape, shape.tp, shards, full["x"], full["b_o"], full["b2"], full["dy"], residual,
+                            precision=mtl.MTL_PREC_FP8_HYBRID)
+    p = full_params(full)
+    x, g = f64(full["x"]), f64(full["dy"])
+    fwd = L.layer_forward(p, x, shape.heads, shape.micro_batch, residual)
+    bwd = L.layer_backward(p, x, fwd, g, shape.heads, shape.micro_batch, residual)
+    ref_i = {**{k: fwd[k] for k in ("qkv", "h", "z", "a", "y")}, "dh": bwd["dh"],
+             **{k: bwd[k] for k in ("dx", "dw_qkv", "db_qkv", "dw_o", "db_o", "dw1", "db1", "dw2", "db2")}}
+    q = F8.sharded_layer(p, x, g, shape.heads, shape.tp, shape.micro_batch, residual, fq=_q4, gq=_q5)
+    cat = lambda part, key, axis: np.concatenate([d[key] for d in q[part]], axis=axis)
+    ref_q = dict(y=q["y"], h=q["h"], dh=q["dh"], dx=q["dx"], qkv=cat("att", "qkv", 1), z=cat("mlp", "z", 1),
+                 a=cat("mlp", "a", 1), dw_qkv=cat("attn_bwd", "dw_qkv", 1), db_qkv=cat("attn_bwd", "db_qkv", 0),
+                 dw_o=cat("attn_bwd", "dw_o", 0), dw1=cat("mlp_bwd", "dw1", 1), db1=cat("mlp_bwd", "db1", 0),
+                 dw2=cat("mlp_bwd", "dw2", 0), db_o=q["attn_bwd"][0]["db_o"], db2=q["mlp_bwd"][0]["db2"])
+    bad = []
+    for k, ref in ref_i.items():
+        scale = float(np.max(np.abs(ref)))
+        err = float(np.max(np.abs(got[k] - ref)))
+        recipe = float(np.max(np.abs(ref_q[k] - ref)))
+        rms_err, rms_recipe = _rms(got[k] - ref), _rms(ref_q[k] - ref)
+        print(f"  {k:7s} max|got-ref|/max {err / scale:.4f} (recipe {recipe / scale:.4f})  "
+              f"rms {rms_err / _rms(ref):.4f} (recipe {rms_recipe / _rms(ref):.4f})")
+        if err > max(FP8_REL * scale, 1.5 * recipe) or rms_err > 1.25 * rms_recipe + 0.01 * _rms(ref):
+            bad.append(k)
+    assert not bad, bad
+
+
+@pytest.mark.gpu
+def test_fp8_gemms_on_identical_codes(mtl):
+    """Every fp8 GEMM kind whose operands are call inputs -- so the device and
+    the reference quantise the same bf16 values to the same codes (the cast is
+    bit-exact) -- within the bf16 bound of the quantised-operand reference:
+    fwd E4M3 x E4M3 with bias (qkv) and with bias + GeLU (z, a); dgrad E5M2 x
+    E4M3 with GeLU' (through db1 = colsum(dz)); wgrad E4M3^T x E5M2 (dw2,
+    dw_o).  Each call gets independent inputs, as in a real step."""
+    import torch
+    from megatron_tensor_transformer_layer_amd.layer import RankState, bf16_dev, host_f64
+    shape = synth.WORKLOADS["gpt2-small-tp2"]
+    t, r = shape.tp, 1
+    f_l, o_l = shape.ffn // t, shape.hidden // t
+    inp = synth.layer_inputs(shape, tp=t, rank=r)
+    hb, dhb = synth.layer_tensor(shape, "h"), synth.layer_tensor(shape, "dh")
+    # independent saved activations for the backward calls: Z ~ N(0, 4), A, O ~ N(0, 1)
+    zb = synth.bf16_round_bits(np.tile(f64(synth.layer_tensor(shape, "dh", seed=3)), (1, 2))[:, :f_l] * 2.0)
+    ab = np.tile(synth.layer_tensor(shape, "h", seed=4), (1, 2))[:, :f_l].copy()
+    ob = synth.layer_tensor(shape, "x", seed=6)[:, :o_l].copy()
+    st = RankState(shape, t, r, inp, precision=mtl.MTL_PREC_FP8_HYBRID)
+    x, dy, h, dh = bf16_dev(inp["x"]), bf16_dev(inp["dy"]), bf16_dev(hb), bf16_dev(dhb)
+    st.attn_fwd(x)
+    st.mlp_fwd(h)
+    torch.cuda.synchronize()
+    got = dict(qkv=host_f64(st.qkv), z=host_f64(st.z), a=host_f64(st.a))
+    st.z.copy_(bf16_dev(zb))
+    st.a.copy_(bf16_dev(ab))
+    st.o.copy_(bf16_dev(ob))
+    st.mlp_bwd(dy, h)
+    st.attn_bwd(dh, x)
+    torch.cuda.synchronize()
+    got.update(db1=host_f64(st.db1), dw2=host_f64(st.dw2), dw_o=host_f64(st.dw_o), db_o=host_f64(st.db_o))
+
+    pr = {k: f64(inp[k]) for k in ("w_qkv", "b_qkv", "w_o", "w1", "b1", "w2")}
+    X, DY, H, DH, Z, A, O = (f64(v) for v in (inp["x"], inp["dy"], hb, dhb, zb, ab, ob))
+    fa = F8.rank_attn_forward(pr, X, shape.heads // t)
+    fm = F8.rank_mlp_forward(pr, H)
+    mb = F8.rank_mlp_backward(pr, DY, H, Z, A)
+    ref = dict(qkv=fa["qkv"], z=fm["z"], a=fm["a"], db1=mb["db1"], dw2=mb["dw2"],
+               dw_o=F8.q4(O).T @ F8.q5(DH), db_o=DH.sum(axis=0))
+    for k in ref:
+        assert_bf16(k, got[k], ref[k])
