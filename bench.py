@@ -24,6 +24,7 @@ import time
 import numpy as np
 
 PEAK_BF16_TFLOPS = 2516.6  # MI355X dense bf16 MFMA
+PEAK_FP8_TFLOPS = 5033.2   # MI355X dense fp8 MFMA
 PEAK_HBM_GBS = 8000.0
 
 
@@ -34,6 +35,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="7b-tp4")
     ap.add_argument("--rank", type=int, default=0)
+    ap.add_argument("--precision", choices=("bf16", "fp8"), default="bf16",
+                    help="fp8: the linears' GEMMs on per-tensor scaled E4M3/E5M2 codes (--fp8-format hybrid)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-seq", type=int, default=4096)
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -88,12 +91,15 @@ def calibrate_copy():
                       "bytes_written": rows * cols * 2, "launches": 3}), flush=True)
 
 
-def cpu_baseline(shape, rank, sample_seq):
+def cpu_baseline(shape, rank, sample_seq, fp8=False):
     """The oracle (fp64 numpy, as it stands) on a bounded sample: the same rank's
-    forward + backward over the first sample_seq tokens."""
+    forward + backward over the first sample_seq tokens (for fp8, the reference
+    with quantised GEMM operands)."""
     import synth
     from oracle import layer as L
     from oracle import shard as S
+    if fp8:
+        from oracle import fp8_layer as S  # noqa: F811 -- same rank functions, quantised operands
 
     try:
         from threadpoolctl import threadpool_info
@@ -116,7 +122,7 @@ def cpu_baseline(shape, rank, sample_seq):
     flops = L.layer_flops(shape.hidden, shape.heads, shape.ffn, sample_seq, 1, shape.tp)["total"]
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
             "sample": f"rank {rank} shard forward+backward on the first {sample_seq} of {shape.seq} tokens "
-                      f"(fp64 numpy), {dt:.2f} s"}
+                      f"(fp64 numpy{', fp8 quant-dequant operands' if fp8 else ''}), {dt:.2f} s"}
 
 
 def moe_cpu_baseline(shape, rank, sample_tokens, sample_ffn):
@@ -259,7 +265,9 @@ def main():
     shape = synth.WORKLOADS[args.workload]
     t, r = shape.tp, args.rank
     inp = synth.layer_inputs(shape, tp=t, rank=r)
-    st = RankState(shape, t, r, inp)
+    fp8 = args.precision == "fp8"
+    from megatron_tensor_transformer_layer_amd import MTL_PREC_BF16, MTL_PREC_FP8_HYBRID
+    st = RankState(shape, t, r, inp, precision=MTL_PREC_FP8_HYBRID if fp8 else MTL_PREC_BF16)
     D = st.D
     x = bf16_dev(inp["x"])
     dy = bf16_dev(inp["dy"])
@@ -319,13 +327,22 @@ def main():
     ms = wall / args.steps * 1e3
     per_step = np.array([a.elapsed_time(b) for a, b in step_ev])
     mlp_ms = np.array([a.elapsed_time(b) for a, b in mlp_ev])
-    # dominant kernel: the bf16 MFMA GEMM; mtl_mlp_fwd is exactly two GEMM launches of
-    # shape S x f/t x h and S x h x f/t (2*S*h*f/t FLOP each)
+    # dominant kernel: the MFMA GEMM; in bf16 mtl_mlp_fwd is exactly two GEMM launches
+    # of shape S x f/t x h and S x h x f/t (2*S*h*f/t FLOP each); in fp8 it also
+    # holds the amax + cast of its four operands, charged here to the GEMMs
     gemm_flop = 2.0 * D.S * D.h * D.f_l
     gemm_launch_s = float(np.mean(mlp_ms)) / 2 / 1e3
     achieved = gemm_flop / gemm_launch_s / 1e12
+    peak = PEAK_FP8_TFLOPS if fp8 else PEAK_BF16_TFLOPS
+    kernel = ("gemm_bf16_kernel, 256x256 tiles: the two launches of mtl_mlp_fwd (fc1 + bias + GeLU, fc2), "
+              "%d x %d x %d each" % (D.S, D.f_l, D.h))
+    if fp8:
+        kernel = ("gemm_bf16_kernel fp8 variant (E4M3 x E4M3, v_mfma_f32_32x32x64_f8f6f4), 256x256 tiles: the two "
+                  "GEMMs of mtl_mlp_fwd, %d x %d x %d each, with its four amax+cast passes included"
+                  % (D.S, D.f_l, D.h))
     out = {
-        "metric": "TFLOP/s per TP-shard layer fwd+bwd (bf16) and % of MI355X MFMA peak",
+        "metric": ("TFLOP/s per TP-shard layer fwd+bwd (fp8 hybrid GEMMs) and % of MI355X MFMA peak" if fp8 else
+                   "TFLOP/s per TP-shard layer fwd+bwd (bf16) and % of MI355X MFMA peak"),
         "value": round(fl["total"] / (ms / 1e3) / 1e12, 2),
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -335,26 +352,28 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "fp8" if fp8 else "bf16",
         "data": "synthetic (seeded N(0,1) activations, N(0,0.02) weights)",
         "config": {"workload": f"{args.workload}: rank {r} of TP={t}, hidden {shape.hidden}, heads {shape.heads} "
                                f"({shape.heads // t} local), ffn {shape.ffn} ({shape.ffn // t} local), "
-                               f"seq {shape.seq}, micro-batch {shape.micro_batch}",
+                               f"seq {shape.seq}, micro-batch {shape.micro_batch}"
+                               + (", fp8 hybrid (E4M3 activations/weights, E5M2 gradients, per-tensor current "
+                                  "scaling; attention bf16)" if fp8 else ""),
                    "global_batch": shape.micro_batch, "seq_len": shape.seq, "parallelism": f"tp{t}-rank{r}-of-1gpu"},
-        "pct_of_peak": round(100 * fl["total"] / (ms / 1e3) / 1e12 / PEAK_BF16_TFLOPS, 2),
+        "pct_of_peak": round(100 * fl["total"] / (ms / 1e3) / 1e12 / peak, 2),
+        "pct_of_bf16_peak": round(100 * fl["total"] / (ms / 1e3) / 1e12 / PEAK_BF16_TFLOPS, 2),
         "step_ms_p50": round(float(np.percentile(per_step, 50)), 4),
         "step_ms_p95": round(float(np.percentile(per_step, 95)), 4),
         "flop_per_step": fl["total"],
-        "roofline": {"bound": "mfma",
-                     "kernel": "gemm_bf16_kernel, 256x256 tiles: the two launches of mtl_mlp_fwd "
-                               "(fc1 + bias + GeLU, fc2), %d x %d x %d each" % (D.S, D.f_l, D.h),
-                     "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": stored_traffic(args.workload),
+        "roofline": {"bound": "mfma", "kernel": kernel,
+                     "achieved": round(achieved, 1), "peak": peak, "unit": "TFLOP/s",
+                     "frac": round(achieved / peak, 4),
+                     "traffic": None if fp8 else stored_traffic(args.workload),
                      "gemm_launch_us": round(gemm_launch_s * 1e6, 2)},
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(shape, r, min(args.cpu_sample_seq, shape.seq))
+        out["cpu_baseline"] = cpu_baseline(shape, r, min(args.cpu_sample_seq, shape.seq), fp8)
     print(json.dumps(out), flush=True)
 
 

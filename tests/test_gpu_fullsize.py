@@ -95,3 +95,61 @@ def test_rank_shard_full_size(mtl, workload):
     assert_bf16("dw_qkv[:, cols]", g["dw_qkv"][:, cq], X.T @ dqkv[:, cq])
     assert_bf16("db_qkv", g["db_qkv"], dqkv.sum(axis=0))
     assert_bf16("dx partial[rows]", g["p_dx"][rows], dqkv[rows] @ p["w_qkv"].T)
+
+
+@pytest.mark.gpu
+def test_fp8_rank_shard_full_size(mtl):
+    """The fp8 variant of the 7B-class TP=4 rank 0 shard, in the launch
+    configuration bench.py --precision fp8 times.  Every fp8 GEMM kind is
+    checked where its operands are call inputs (so both sides quantise the same
+    bf16 values to the same codes) against the fp64 product of the dequantised
+    codes: qkv in full, z and a on sampled rows, dw2 and dw_o on sampled
+    columns, db1 (a column sum of the dgrad output dz) on sampled columns."""
+    import torch
+    from oracle import fp8_layer as F8
+    from megatron_tensor_transformer_layer_amd.layer import RankState, bf16_dev, host_f64
+
+    shape = synth.WORKLOADS["7b-tp4"]
+    t = shape.tp
+    f_l, o_l = shape.ffn // t, shape.hidden // t
+    print(f"fp8 workload 7b-tp4 rank 0 of tp {t}", flush=True)
+    inp = synth.layer_inputs(shape, tp=t, rank=0)
+    hb, dhb = synth.layer_tensor(shape, "h"), synth.layer_tensor(shape, "dh")
+    zb = synth.bf16_round_bits(f64(synth.layer_tensor(shape, "dh", seed=3))[:, :f_l] * 2.0)
+    ab = synth.layer_tensor(shape, "h", seed=4)[:, :f_l].copy()
+    ob = synth.layer_tensor(shape, "x", seed=6)[:, :o_l].copy()
+    st = RankState(shape, t, 0, inp, precision=mtl.MTL_PREC_FP8_HYBRID)
+    x, dy, h, dh = bf16_dev(inp["x"]), bf16_dev(inp["dy"]), bf16_dev(hb), bf16_dev(dhb)
+    st.attn_fwd(x)
+    st.mlp_fwd(h)
+    torch.cuda.synchronize()
+    g = dict(qkv=host_f64(st.qkv), z=host_f64(st.z[ROWS]), a=host_f64(st.a[ROWS]))
+    st.z.copy_(bf16_dev(zb))
+    st.a.copy_(bf16_dev(ab))
+    st.o.copy_(bf16_dev(ob))
+    st.mlp_bwd(dy, h)
+    st.attn_bwd(dh, x)
+    torch.cuda.synchronize()
+    g.update(dw2=host_f64(st.dw2), db1=host_f64(st.db1), dw_o=host_f64(st.dw_o), db_o=host_f64(st.db_o))
+    del st
+    torch.cuda.empty_cache()
+    print("device calls done", flush=True)
+
+    q4, q5 = F8.q4, F8.q5
+    p = {k: f64(inp[k]) for k in ("w_qkv", "b_qkv", "w1", "b1", "w2")}
+    Xq = q4(f64(inp["x"]))
+    assert_bf16("qkv", g["qkv"], Xq @ q4(p["w_qkv"]) + p["b_qkv"])
+    del Xq
+    z_r = q4(f64(hb))[ROWS] @ q4(p["w1"]) + p["b1"]
+    assert_bf16("z[rows]", g["z"], z_r)
+    assert_bf16("a[rows]", g["a"], L.gelu(z_r))
+    DYq = q5(f64(inp["dy"]))
+    ch = _cols(shape.hidden)
+    assert_bf16("dw2[:, cols]", g["dw2"][:, ch], q4(f64(ab)).T @ DYq[:, ch])
+    cf = _cols(f_l)
+    dz_c = (DYq @ q4(p["w2"])[cf].T) * L.gelu_grad(f64(zb)[:, cf])
+    assert_bf16("db1[cols]", g["db1"][cf], dz_c.sum(axis=0))
+    del DYq
+    DH = f64(dhb)
+    assert_bf16("dw_o[:, cols]", g["dw_o"][:, ch], q4(f64(ob)).T @ q5(DH)[:, ch])
+    assert_bf16("db_o", g["db_o"], DH.sum(axis=0))
