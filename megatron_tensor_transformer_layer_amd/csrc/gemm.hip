@@ -376,24 +376,15 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmArgs p) {
   // fp8: the product of the two operands' dequantisation factors
   float dq = 1.f;
   if constexpr (F8 != 0) dq = *p.scale_a * *p.scale_b;
-  float bias_v[TN][4][4];
+  // bias kept as packed bf16 (half the registers), widened where it is added
+  u32x2 braw[TN][4];
   if constexpr (HAS_BIAS) {
-    u32x2 braw[TN][4];
 #pragma unroll
     for (int j = 0; j < TN; ++j)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const int n = nw + j * 32 + 8 * g + 4 * lgrp;
         braw[j][g] = (p.bias && n < p.N) ? *reinterpret_cast<const u32x2*>(p.bias + n) : u32x2{0, 0};
-      }
-#pragma unroll
-    for (int j = 0; j < TN; ++j)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        bias_v[j][g][0] = bf16_lo(braw[j][g][0]);
-        bias_v[j][g][1] = bf16_hi(braw[j][g][0]);
-        bias_v[j][g][2] = bf16_lo(braw[j][g][1]);
-        bias_v[j][g][3] = bf16_hi(braw[j][g][1]);
       }
   }
 
@@ -417,8 +408,10 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmArgs p) {
               for (int e = 0; e < 4; ++e) v[e] *= dq;
             }
             if constexpr (HAS_BIAS) {
-#pragma unroll
-              for (int e = 0; e < 4; ++e) v[e] += bias_v[j][g][e];
+              v[0] += bf16_lo(braw[j][g][0]);
+              v[1] += bf16_hi(braw[j][g][0]);
+              v[2] += bf16_lo(braw[j][g][1]);
+              v[3] += bf16_hi(braw[j][g][1]);
             }
             if (out == 1) {
 #pragma unroll
