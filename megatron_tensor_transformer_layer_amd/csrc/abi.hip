@@ -407,22 +407,18 @@ mtl_status mtl_mlp_bwd(const mtl_layer_cfg* c, const void* dy, const void* h, co
     MTL_TRY(gemm8(ws.dz8, ws.dz8.q, ws.w1, ws.w1.q, d.S, d.h, d.f_l, dh_partial, d.h, EPI_BF16, s));
     return MTL_OK;
   }
-  // dz = (dy . w2^T) * GeLU'(z)
+  // dz = (dy . w2^T) * GeLU'(z), with the independent dw2 = a^T . dy in the same launch
   GemmArgs g = gemm(dy, d.h, w2, d.h, d.S, d.f_l, d.h, ws.dz, d.f_l);
   g.aux = static_cast<const uint16_t*>(z);
   g.ld_aux = d.f_l;
-  MTL_TRY(gemm_bf16(g, GEMM_DGRAD, EPI_DGELU, s));
-  // dw2 = a^T . dy
-  g = gemm(a, d.f_l, dy, d.h, d.f_l, d.h, d.S, dw2, d.h);
-  MTL_TRY(gemm_bf16(g, GEMM_WGRAD, wepi, s));
-  // dw1 = h^T . dz
-  g = gemm(h, d.h, ws.dz, d.f_l, d.h, d.f_l, d.S, dw1, d.f_l);
-  MTL_TRY(gemm_bf16(g, GEMM_WGRAD, wepi, s));
+  GemmArgs g2 = gemm(a, d.f_l, dy, d.h, d.f_l, d.h, d.S, dw2, d.h);
+  MTL_TRY(gemm_bf16_pair(g, GEMM_DGRAD, EPI_DGELU, g2, GEMM_WGRAD, wepi, s));
   MTL_TRY(colsum_bf16(ws.dz, d.S, d.f_l, d.f_l, db1, accum, ws.ws, s));
   if (db2) MTL_TRY(colsum_bf16(static_cast<const uint16_t*>(dy), d.S, d.h, d.h, db2, accum, ws.ws, s));
-  // dh_partial = dz . w1^T
-  g = gemm(ws.dz, d.f_l, w1, d.f_l, d.S, d.h, d.f_l, dh_partial, d.h);
-  MTL_TRY(gemm_bf16(g, GEMM_DGRAD, EPI_BF16, s));
+  // dw1 = h^T . dz and dh_partial = dz . w1^T
+  g = gemm(h, d.h, ws.dz, d.f_l, d.h, d.f_l, d.S, dw1, d.f_l);
+  g2 = gemm(ws.dz, d.f_l, w1, d.f_l, d.S, d.h, d.f_l, dh_partial, d.h);
+  MTL_TRY(gemm_bf16_pair(g, GEMM_WGRAD, wepi, g2, GEMM_DGRAD, EPI_BF16, s));
   return MTL_OK;
 }
 
@@ -451,12 +447,10 @@ mtl_status mtl_attn_bwd(const mtl_layer_cfg* c, const void* dh, const void* x, c
     MTL_TRY(quantize(o, ws.o_t, ws.amax_ws, s));
     MTL_TRY(gemm8(ws.o_t, ws.o_t.qt, ws.dh, ws.dh.qt, d.o_l, d.h, d.S, dw_o, d.h, wepi, s));
   } else {
-    // do = dh . w_o^T
+    // do = dh . w_o^T and dw_o = o^T . dh, one launch
     GemmArgs g = gemm(dh, d.h, w_o, d.h, d.S, d.o_l, d.h, ws.dout, d.o_l);
-    MTL_TRY(gemm_bf16(g, GEMM_DGRAD, EPI_BF16, s));
-    // dw_o = o^T . dh
-    g = gemm(o, d.o_l, dh, d.h, d.o_l, d.h, d.S, dw_o, d.h);
-    MTL_TRY(gemm_bf16(g, GEMM_WGRAD, wepi, s));
+    GemmArgs g2 = gemm(o, d.o_l, dh, d.h, d.o_l, d.h, d.S, dw_o, d.h);
+    MTL_TRY(gemm_bf16_pair(g, GEMM_DGRAD, EPI_BF16, g2, GEMM_WGRAD, wepi, s));
   }
   if (db_o) MTL_TRY(colsum_bf16(static_cast<const uint16_t*>(dh), d.S, d.h, d.h, db_o, accum, ws.ws, s));
 
@@ -486,12 +480,11 @@ mtl_status mtl_attn_bwd(const mtl_layer_cfg* c, const void* dh, const void* x, c
     MTL_TRY(gemm8(ws.dqkv8, ws.dqkv8.q, ws.wqkv, ws.wqkv.q, d.S, d.h, d.qkv_l, dx_partial, d.h, EPI_BF16, s));
     return MTL_OK;
   }
-  // dw_qkv = x^T . dqkv ; db_qkv = colsum(dqkv) ; dx_partial = dqkv . w_qkv^T
+  // dw_qkv = x^T . dqkv and dx_partial = dqkv . w_qkv^T, one launch; db_qkv = colsum(dqkv)
   GemmArgs g = gemm(x, d.h, ws.dqkv, d.qkv_l, d.h, d.qkv_l, d.S, dw_qkv, d.qkv_l);
-  MTL_TRY(gemm_bf16(g, GEMM_WGRAD, wepi, s));
+  GemmArgs g2 = gemm(ws.dqkv, d.qkv_l, w_qkv, d.qkv_l, d.S, d.h, d.qkv_l, dx_partial, d.h);
+  MTL_TRY(gemm_bf16_pair(g, GEMM_WGRAD, wepi, g2, GEMM_DGRAD, EPI_BF16, s));
   MTL_TRY(colsum_bf16(ws.dqkv, d.S, d.qkv_l, d.qkv_l, db_qkv, accum, ws.ws, s));
-  g = gemm(ws.dqkv, d.qkv_l, w_qkv, d.qkv_l, d.S, d.h, d.qkv_l, dx_partial, d.h);
-  MTL_TRY(gemm_bf16(g, GEMM_DGRAD, EPI_BF16, s));
   return MTL_OK;
 }
 

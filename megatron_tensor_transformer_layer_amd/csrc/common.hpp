@@ -116,9 +116,11 @@ __device__ __forceinline__ u32x2 read_tr(const LDS_AS char* p) {
 
 // A raw buffer resource over [base, base + bytes): loads past the end return 0
 // (the range check covers the VGPR offset only, not soffset).
+// The words are made wave-uniform explicitly: the DMA takes the resource in SGPRs.
 __device__ __forceinline__ i32x4 make_rsrc(const void* base, uint32_t bytes) {
   const uint64_t b = reinterpret_cast<uint64_t>(base);
-  return i32x4{(int)(uint32_t)b, (int)(uint32_t)(b >> 32), (int)bytes, 0x00020000};
+  return i32x4{__builtin_amdgcn_readfirstlane((int)(uint32_t)b), __builtin_amdgcn_readfirstlane((int)(uint32_t)(b >> 32)),
+               __builtin_amdgcn_readfirstlane((int)bytes), 0x00020000};
 }
 
 // 16 bytes per lane from buffer offset voff + soff into LDS at lds + 16*lane

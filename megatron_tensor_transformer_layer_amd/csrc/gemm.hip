@@ -257,22 +257,20 @@ struct Mainloop {
   }
 };
 
-template <int BM, int BN, bool A_K, bool B_K, int EPI, int F8 = 0>
-__global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmArgs p) {
+// One output tile (workgroup index bid of the GEMM p) with the two LDS stages
+// st0, st1 of the launching kernel.
+template <int BM, int BN, bool A_K, bool B_K, int EPI, int F8>
+__device__ __forceinline__ void gemm_tile(GemmArgs p, const int bid, LDS_AS char* st0, LDS_AS char* st1) {
   using ML = Mainloop<BM, BN, A_K, B_K, F8>;
   constexpr int EB = ML::EB, KSLAB = ML::KSLAB;
   constexpr int WM = ML::WM, WN = ML::WN, TM = ML::TM, TN = ML::TN;
-  __shared__ __attribute__((aligned(1024))) char st0_[ML::STAGE];
-  __shared__ __attribute__((aligned(1024))) char st1_[ML::STAGE];
-  LDS_AS char* st0 = (LDS_AS char*)st0_;
-  LDS_AS char* st1 = (LDS_AS char*)st1_;
   constexpr int OUT_BYTES = (EPI == EPI_F32 || EPI == EPI_F32_ACC) ? 4 : 2;
 
   int tm, tn;
   if (p.offsets == nullptr) {
     const int tiles_m = (p.M + BM - 1) / BM, tiles_n = (p.N + BN - 1) / BN;
     const int ntiles = tiles_m * tiles_n;
-    const int t = tile_index(blockIdx.x, ntiles);
+    const int t = tile_index(bid, ntiles);
     constexpr int GM = 4;
     const int group = GM * tiles_n;
     const int first_m = (t / group) * GM;
@@ -282,7 +280,7 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmArgs p) {
   } else if (p.group_mode == GROUP_M) {
     // find this workgroup's expert among the per-expert row-tile counts
     const int tiles_n = (p.N + BN - 1) / BN;
-    int w = blockIdx.x, e = -1;
+    int w = bid, e = -1;
     for (int gi = 0; gi < p.groups; ++gi) {
       const int rows = p.offsets[gi + 1] - p.offsets[gi];
       const int span = ((rows + BM - 1) / BM) * tiles_n;
@@ -305,7 +303,7 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmArgs p) {
   } else {
     const int tiles_m = (p.M + BM - 1) / BM, tiles_n = (p.N + BN - 1) / BN;
     const int per = tiles_m * tiles_n;
-    const int e = blockIdx.x / per, w = blockIdx.x % per;
+    const int e = bid / per, w = bid % per;
     const int r0 = p.offsets[e];
     p.K = p.offsets[e + 1] - r0;
     p.a += (int64_t)r0 * p.lda;
@@ -469,6 +467,39 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmArgs p) {
 }
 
 template <int BM, int BN, bool A_K, bool B_K, int EPI, int F8 = 0>
+__global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmArgs p) {
+  constexpr int STAGE = Mainloop<BM, BN, A_K, B_K, F8>::STAGE;
+  __shared__ __attribute__((aligned(1024))) char st0_[STAGE];
+  __shared__ __attribute__((aligned(1024))) char st1_[STAGE];
+  gemm_tile<BM, BN, A_K, B_K, EPI, F8>(p, blockIdx.x, (LDS_AS char*)st0_, (LDS_AS char*)st1_);
+}
+
+// A tile configuration of gemm_tile.
+template <int BM_, int BN_, bool A_K_, bool B_K_, int EPI_>
+struct TileCfg {
+  static constexpr int BM = BM_, BN = BN_, EPI = EPI_;
+  static constexpr bool A_K = A_K_, B_K = B_K_;
+  static constexpr int STAGE = Mainloop<BM, BN, A_K, B_K, 0>::STAGE;
+};
+
+// Two independent GEMMs in one launch: workgroups [0, tiles1) take p1, the rest
+// p2.  With one tile per CU, the second GEMM's tiles start as the first GEMM's
+// finish, so the first GEMM's output stores drain under the second's main loop
+// instead of at a kernel boundary.
+template <class C1, class C2>
+__global__ __launch_bounds__(256, 1) void gemm_pair_kernel(GemmArgs p1, GemmArgs p2, int tiles1) {
+  constexpr int STAGE = C1::STAGE > C2::STAGE ? C1::STAGE : C2::STAGE;
+  __shared__ __attribute__((aligned(1024))) char st0_[STAGE];
+  __shared__ __attribute__((aligned(1024))) char st1_[STAGE];
+  const int bid = blockIdx.x;
+  if (bid < tiles1)
+    gemm_tile<C1::BM, C1::BN, C1::A_K, C1::B_K, C1::EPI, 0>(p1, bid, (LDS_AS char*)st0_, (LDS_AS char*)st1_);
+  else
+    gemm_tile<C2::BM, C2::BN, C2::A_K, C2::B_K, C2::EPI, 0>(p2, bid - tiles1, (LDS_AS char*)st0_,
+                                                            (LDS_AS char*)st1_);
+}
+
+template <int BM, int BN, bool A_K, bool B_K, int EPI, int F8 = 0>
 static hipError_t launch_cfg(const GemmArgs& p, hipStream_t s) {
   int64_t tiles;
   if (p.offsets == nullptr) {
@@ -492,6 +523,72 @@ static hipError_t launch_layout(const GemmArgs& p, hipStream_t s) {
   if (t256 >= 240) return launch_cfg<256, 256, A_K, B_K, EPI>(p, s);
   if (t192 >= 240 && p.N % 192 == 0) return launch_cfg<256, 192, A_K, B_K, EPI>(p, s);
   return launch_cfg<128, 128, A_K, B_K, EPI>(p, s);
+}
+
+// Tile shape launch_layout picks for a plain GEMM: 0 = 256x256, 1 = 256x192, 2 = 128x128.
+static int tile_kind(const GemmArgs& p) {
+  const long t256 = (long)((p.M + 255) / 256) * ((p.N + 255) / 256);
+  const long t192 = (long)((p.M + 255) / 256) * ((p.N + 191) / 192);
+  if (t256 >= 240) return 0;
+  if (t192 >= 240 && p.N % 192 == 0) return 1;
+  return 2;
+}
+
+template <class C1, class C2>
+static hipError_t launch_pair(const GemmArgs& p1, const GemmArgs& p2, hipStream_t s) {
+  const int64_t t1 = (int64_t)((p1.M + C1::BM - 1) / C1::BM) * ((p1.N + C1::BN - 1) / C1::BN);
+  const int64_t t2 = (int64_t)((p2.M + C2::BM - 1) / C2::BM) * ((p2.N + C2::BN - 1) / C2::BN);
+  hipLaunchKernelGGL((gemm_pair_kernel<C1, C2>), dim3((unsigned)(t1 + t2)), dim3(256), 0, s, p1, p2, (int)t1);
+  return hipGetLastError();
+}
+
+// The backward's independent pairs: dgrad (+GeLU') with wgrad, wgrad with dgrad.
+template <int EPI_W>
+static hipError_t pair_dispatch(const GemmArgs& p1, GemmLayout l1, int e1, const GemmArgs& p2, GemmLayout l2,
+                                int k1, int k2, hipStream_t s, bool* done) {
+  *done = true;
+  using W256 = TileCfg<256, 256, false, false, EPI_W>;
+  using W192 = TileCfg<256, 192, false, false, EPI_W>;
+  using W128 = TileCfg<128, 128, false, false, EPI_W>;
+  if (l1 == GEMM_DGRAD && l2 == GEMM_WGRAD && k1 == 0 && k2 == 0 && e1 == EPI_DGELU)
+    return launch_pair<TileCfg<256, 256, true, true, EPI_DGELU>, W256>(p1, p2, s);
+  if (l1 == GEMM_DGRAD && l2 == GEMM_WGRAD && k1 == 2 && k2 == 2 && e1 == EPI_BF16)
+    return launch_pair<TileCfg<128, 128, true, true, EPI_BF16>, W128>(p1, p2, s);
+  if (l1 == GEMM_WGRAD && l2 == GEMM_DGRAD && k1 == 0 && k2 == 0)
+    return launch_pair<W256, TileCfg<256, 256, true, true, EPI_BF16>>(p1, p2, s);
+  if (l1 == GEMM_WGRAD && l2 == GEMM_DGRAD && k1 == 1 && k2 == 0)
+    return launch_pair<W192, TileCfg<256, 256, true, true, EPI_BF16>>(p1, p2, s);
+  *done = false;
+  return hipSuccess;
+}
+
+hipError_t gemm_bf16_pair(const GemmArgs& p1, GemmLayout l1, int e1, const GemmArgs& p2, GemmLayout l2, int e2,
+                          hipStream_t s) {
+  // combinations without a fused kernel run as two launches
+  const bool plain = !p1.offsets && !p2.offsets && p1.M > 0 && p1.N > 0 && p1.K > 0 && p2.M > 0 && p2.N > 0 &&
+                     p2.K > 0;
+  const bool wgrad_ok = (l1 == GEMM_WGRAD) ? (e1 == EPI_F32 || e1 == EPI_F32_ACC)
+                                           : (l2 == GEMM_WGRAD && (e2 == EPI_F32 || e2 == EPI_F32_ACC));
+  const bool dgrad_ok = (l1 == GEMM_DGRAD) ? (e1 == EPI_BF16 || e1 == EPI_DGELU) : (l2 == GEMM_DGRAD && e2 == EPI_BF16);
+  const bool fits = [&] {  // the same 32-bit offset bound gemm_bf16 checks
+    for (const GemmArgs* q : {&p1, &p2}) {
+      const bool wg = (q == &p1 ? l1 : l2) == GEMM_WGRAD;
+      const int64_t ar = (wg ? (int64_t)q->K : (int64_t)q->M) + 256, br = (int64_t)(wg ? q->K : q->N) + 256;
+      if (ar * q->lda * 2 >= ((int64_t)1 << 32) || br * q->ldb * 2 >= ((int64_t)1 << 32)) return false;
+    }
+    return true;
+  }();
+  if (plain && wgrad_ok && dgrad_ok && fits && l1 != l2) {
+    const int ew = l1 == GEMM_WGRAD ? e1 : e2;
+    bool done = false;
+    hipError_t e = ew == EPI_F32 ? pair_dispatch<EPI_F32>(p1, l1, e1, p2, l2, tile_kind(p1), tile_kind(p2), s, &done)
+                                 : pair_dispatch<EPI_F32_ACC>(p1, l1, e1, p2, l2, tile_kind(p1), tile_kind(p2), s,
+                                                              &done);
+    if (done) return e;
+  }
+  hipError_t e = gemm_bf16(p1, l1, e1, s);
+  if (e != hipSuccess) return e;
+  return gemm_bf16(p2, l2, e2, s);
 }
 
 int64_t gemm_group_m_grid(int64_t max_rows, int groups, int N) {

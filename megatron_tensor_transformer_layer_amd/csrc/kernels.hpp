@@ -58,6 +58,12 @@ int64_t gemm_group_m_grid(int64_t max_rows, int groups, int N);
 // 16-byte aligned base pointers and leading dimensions multiple of 8.
 hipError_t gemm_bf16(const GemmArgs& p, GemmLayout layout, int epi, hipStream_t s);
 
+// Two independent GEMMs, launched as one kernel where a fused configuration
+// exists (the backward's dgrad/wgrad pairs), else as two launches.  Same
+// requirements as gemm_bf16 for each.
+hipError_t gemm_bf16_pair(const GemmArgs& p1, GemmLayout l1, int e1, const GemmArgs& p2, GemmLayout l2, int e2,
+                          hipStream_t s);
+
 // fp8 GEMM: C = (A . B^T) * (*scale_a) * (*scale_b), fp32 accumulate, with the
 // epilogues above.  A [M][K] and B [N][K] are fp8 codes (both k-contiguous; a, b
 // point at bytes, lda/ldb in bytes), fmt_a/fmt_b 0 = E4M3, 1 = E5M2.  Supported:
