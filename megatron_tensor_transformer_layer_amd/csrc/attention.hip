@@ -146,31 +146,40 @@ __global__ __launch_bounds__(256, 1) void attn_fwd_kernel(AttnArgs a) {
 #pragma unroll
         for (int sb = 0; sb < 2; ++sb) s[sb] = mfma32(T::kfrag(kt, sb * 32, ks, lane), qf[ks], s[sb]);
       const bool diag = (k0 + 63 > qw);
-      float mx = m;
+      // every processed block holds key k0 <= q, so bmax is finite
+      float bmax = -INFINITY;
 #pragma unroll
       for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int key = k0 + sb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
           if (diag && key > q) s[sb][r] = -INFINITY;
-          mx = fmaxf(mx, s[sb][r]);
+          bmax = fmaxf(bmax, s[sb][r]);
         }
-      mx = fmaxf(mx, xor32(mx));
-      const float alpha = exp2f((m - mx) * c);
-      const float mc = mx * c;
+      bmax = fmaxf(bmax, xor32(bmax));
+      // The reference max m moves (and l, o are rescaled) only when some row's
+      // block max exceeds it by more than 2^8 in the exponent; otherwise the
+      // probabilities are taken against the stale m (at most 2^8, exact in the
+      // final normalisation), which spares the accumulator rescale.
+      if (__any((bmax - m) * c > 8.f)) {
+        const float mx = fmaxf(m, bmax);
+        const float alpha = __builtin_amdgcn_exp2f((m - mx) * c);
+        l *= alpha;
+#pragma unroll
+        for (int i = 0; i < DB; ++i) o[i] *= alpha;
+        m = mx;
+      }
+      const float mc = m * c;
       float rsum = 0.f;
 #pragma unroll
       for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const float pv = exp2f(s[sb][r] * c - mc);
+          const float pv = __builtin_amdgcn_exp2f(s[sb][r] * c - mc);
           s[sb][r] = pv;
           rsum += pv;
         }
-      l = l * alpha + rsum;
-      m = mx;
-#pragma unroll
-      for (int i = 0; i < DB; ++i) o[i] *= alpha;
+      l += rsum;
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
         const u32x4 pb = pack_half(s[ks >> 1], ks & 1);
@@ -215,7 +224,7 @@ __global__ __launch_bounds__(256, 1) void attn_fwd_kernel(AttnArgs a) {
     if (kpar == 0) {
       const float m2 = mg[lane], l2 = mg[64 + lane];
       const float mt = fmaxf(m, m2);
-      const float a1 = exp2f((m - mt) * c), a2 = exp2f((m2 - mt) * c);
+      const float a1 = __builtin_amdgcn_exp2f((m - mt) * c), a2 = __builtin_amdgcn_exp2f((m2 - mt) * c);
       const float lp = l * a1 + l2 * a2;
       const float lt = lp + xor32(lp);
       if (qok) {
@@ -393,7 +402,7 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_kernel(AttnArgs a) {
           for (int e = 0; e < 4; ++e) {
             const int r = 4 * r4 + e;
             const int qg = q0 + ql + e;
-            float pv = exp2f(sc[r] * c - L[e]);
+            float pv = __builtin_amdgcn_exp2f(sc[r] * c - L[e]);
             if (key > qg || qg >= a.seq) pv = 0.f;
             sc[r] = pv;
             dp[r] = pv * (dp[r] - Dl[e]);
@@ -489,7 +498,7 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_kernel(AttnArgs a) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int kk = kw + 8 * (r >> 2) + 4 * g + (r & 3);
-          float pv = exp2f(sc[r] * c - L2);
+          float pv = __builtin_amdgcn_exp2f(sc[r] * c - L2);
           if (kk > q || !qok) pv = 0.f;
           dp[r] = pv * (dp[r] - Dq);
         }
