@@ -130,6 +130,7 @@ __global__ __launch_bounds__(256, 1) void attn_fwd_kernel(AttnArgs a) {
     for (int ks = 0; ks < KS; ++ks)
       qf[ks] = qok ? *reinterpret_cast<const u32x4*>(qbase + (int64_t)q * a.ld_qkv + ks * 16 + g * 8)
                    : u32x4{0, 0, 0, 0};
+    wait_loads();
     f32x16 o[DB];
 #pragma unroll
     for (int i = 0; i < DB; ++i) o[i] = f32x16{};
@@ -147,21 +148,28 @@ __global__ __launch_bounds__(256, 1) void attn_fwd_kernel(AttnArgs a) {
         for (int sb = 0; sb < 2; ++sb) s[sb] = mfma32(T::kfrag(kt, sb * 32, ks, lane), qf[ks], s[sb]);
       const bool diag = (k0 + 63 > qw);
       // every processed block holds key k0 <= q, so bmax is finite
+      if (diag) {  // wave-uniform: only the diagonal block is masked
+        asm volatile("" ::: "memory");
+#pragma unroll
+        for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int key = k0 + sb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
+            if (key > q) s[sb][r] = -INFINITY;
+          }
+      }
       float bmax = -INFINITY;
 #pragma unroll
       for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = k0 + sb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
-          if (diag && key > q) s[sb][r] = -INFINITY;
-          bmax = fmaxf(bmax, s[sb][r]);
-        }
+        for (int r = 0; r < 16; ++r) bmax = fmaxf(bmax, s[sb][r]);
       bmax = fmaxf(bmax, xor32(bmax));
       // The reference max m moves (and l, o are rescaled) only when some row's
       // block max exceeds it by more than 2^8 in the exponent; otherwise the
       // probabilities are taken against the stale m (at most 2^8, exact in the
       // final normalisation), which spares the accumulator rescale.
       if (__any((bmax - m) * c > 8.f)) {
+        asm volatile("" ::: "memory");  // keep this a branch, not a select on alpha
         const float mx = fmaxf(m, bmax);
         const float alpha = __builtin_amdgcn_exp2f((m - mx) * c);
         l *= alpha;

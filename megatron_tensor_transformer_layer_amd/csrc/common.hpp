@@ -141,6 +141,12 @@ __device__ __forceinline__ void dma16(i32x4 rsrc, uint32_t voff, uint32_t soff, 
       : "memory");
 }
 __device__ __forceinline__ void wait_dma() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+// Wait for this wave's compiler-visible vector loads with the s_waitcnt builtin
+// (vmcnt 0, expcnt and lgkmcnt untouched), which the compiler's own wait
+// tracking sees: loads completed here are not waited for again later, e.g. at
+// the top of a loop whose body also issues LDS DMA, where a compiler-inserted
+// vmcnt(0) would wait for that DMA too.
+__device__ __forceinline__ void wait_loads() { __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8)); }
 __device__ __forceinline__ uint32_t lds_addr(const LDS_AS void* p) { return (uint32_t)(uintptr_t)p; }
 
 }  // namespace mtl
