@@ -24,6 +24,14 @@ CXXFLAGS = [
 ]
 
 
+# Per-source options.  attention.hip: keep MFMA accumulators in architectural
+# VGPRs (its kernels fit in 256), which spares the AGPR<->VGPR copies the
+# compiler otherwise inserts around the softmax of every key block.
+SOURCE_FLAGS = {
+    "attention.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
+}
+
+
 def sources():
     return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hip"))
 
@@ -37,7 +45,7 @@ def _hipcc() -> str:
 
 def _compile(src: str) -> str:
     obj = os.path.join(OBJ, os.path.basename(src) + ".o")
-    cmd = [_hipcc(), *CXXFLAGS, "-c", src, "-o", obj]
+    cmd = [_hipcc(), *CXXFLAGS, *SOURCE_FLAGS.get(os.path.basename(src), []), "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     err = "\n".join(l for l in r.stderr.splitlines() if "packed-fp32-ops" not in l)
     if r.returncode != 0:

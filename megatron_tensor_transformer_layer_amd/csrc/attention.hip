@@ -103,7 +103,12 @@ __global__ __launch_bounds__(256, 1) void attn_fwd_kernel(AttnArgs a) {
   LDS_AS char* st0 = (LDS_AS char*)st0_;
   LDS_AS char* st1 = (LDS_AS char*)st1_;
 
-  const int n = blockIdx.y, b = blockIdx.z;
+  // one work unit = (mirrored item pair, head, batch element); the units of a
+  // head share its K and V, so a head's units are kept on one XCD
+  const int nitems = (a.seq + 63) / 64;
+  const int npairs = (nitems + 1) / 2;
+  const int u = xcd_index(blockIdx.x, npairs * a.heads * a.batch);
+  const int pair = u % npairs, n = (u / npairs) % a.heads, b = u / (npairs * a.heads);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, g = lane >> 5;
   const int qsub = wave & 1, kpar = wave >> 1;
   const int64_t tokens = (int64_t)a.seq * a.batch;
@@ -112,12 +117,11 @@ __global__ __launch_bounds__(256, 1) void attn_fwd_kernel(AttnArgs a) {
   const uint16_t* qbase = a.qkv + tok0 * a.ld_qkv + colq;
   const float c = a.scale * LOG2E;
   const i32x4 rs = make_rsrc(a.qkv, (uint32_t)(tokens * a.ld_qkv * 2));
-  const int nitems = (a.seq + 63) / 64;
-  const int nkb_all = (a.seq + 63) / 64;
+  const int nkb_all = nitems;
 
   for (int side = 0; side < 2; ++side) {
-    const int item = side == 0 ? (int)blockIdx.x : nitems - 1 - (int)blockIdx.x;
-    if (side == 1 && item == (int)blockIdx.x) break;
+    const int item = side == 0 ? pair : nitems - 1 - pair;
+    if (side == 1 && item == pair) break;
     const int q0 = item * 64;
     const int qw = q0 + qsub * 32;
     const int q = qw + (lane & 31);
@@ -347,8 +351,10 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_kernel(AttnArgs a) {
   LDS_AS char* tO = sm + 3 * T::TILE;
   float* sl = reinterpret_cast<float*>(sm_ + 4 * T::TILE);  // [0,64) lse*log2e, [64,128) delta
 
-  const int w = blockIdx.x, n = blockIdx.y, b = blockIdx.z;
+  // one work unit = (block w, head, batch element), a head's units on one XCD
   const int nblk = (a.seq + 63) / 64;
+  const int u = xcd_index(blockIdx.x, nblk * a.heads * a.batch);
+  const int w = u % nblk, n = (u / nblk) % a.heads, b = u / (nblk * a.heads);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, g = lane >> 5;
   const int tid = threadIdx.x;
   const int64_t tokens = (int64_t)a.seq * a.batch;
@@ -547,9 +553,10 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_kernel(AttnArgs a) {
 // ============================================================== launchers
 template <int D>
 static hipError_t fwd_d(const AttnArgs& a, hipStream_t s) {
-  const int nitems = (a.seq + 63) / 64;
-  dim3 grid((nitems + 1) / 2, a.heads, a.batch);
-  hipLaunchKernelGGL(attn_fwd_kernel<D>, grid, dim3(256), 0, s, a);
+  const int64_t npairs = ((a.seq + 63) / 64 + 1) / 2;
+  const int64_t units = npairs * a.heads * a.batch;
+  if (units > INT32_MAX) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(attn_fwd_kernel<D>, dim3((unsigned)units), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
@@ -559,8 +566,9 @@ static hipError_t bwd_d(const AttnArgs& a, hipStream_t s) {
   hipLaunchKernelGGL(attn_delta_kernel<D>, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  dim3 grid((a.seq + 63) / 64, a.heads, a.batch);
-  hipLaunchKernelGGL(attn_bwd_kernel<D>, grid, dim3(256), 0, s, a);
+  const int64_t units = (int64_t)((a.seq + 63) / 64) * a.heads * a.batch;
+  if (units > INT32_MAX) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(attn_bwd_kernel<D>, dim3((unsigned)units), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

@@ -147,6 +147,13 @@ __device__ __forceinline__ void wait_dma() { asm volatile("s_waitcnt vmcnt(0)" :
 // the top of a loop whose body also issues LDS DMA, where a compiler-inserted
 // vmcnt(0) would wait for that DMA too.
 __device__ __forceinline__ void wait_loads() { __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8)); }
+// Workgroups are dispatched round-robin over the 8 XCDs (workgroup w runs on
+// XCD w % 8); map w to a logical work index so that each XCD takes a
+// contiguous run of the n work units, which then share that XCD's L2.
+__device__ __forceinline__ int xcd_index(int w, int n) {
+  if ((n & 7) == 0) return (w & 7) * (n >> 3) + (w >> 3);
+  return w;
+}
 __device__ __forceinline__ uint32_t lds_addr(const LDS_AS void* p) { return (uint32_t)(uintptr_t)p; }
 
 }  // namespace mtl

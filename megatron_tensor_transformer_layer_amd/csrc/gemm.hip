@@ -137,13 +137,6 @@ struct Operand {
   }
 };
 
-__device__ __forceinline__ int tile_index(int w, int ntiles) {
-  // Workgroups are dispatched round-robin over the 8 XCDs; give each XCD a
-  // contiguous run of logical tiles.
-  if ((ntiles & 7) == 0) return (w & 7) * (ntiles >> 3) + (w >> 3);
-  return w;
-}
-
 // F8 = 0: bf16 operands.  F8 = 1 + FA + 2*FB: fp8 operands, A in format FA and
 // B in format FB (0 = E4M3, 1 = E5M2), both k-contiguous.
 template <int BM, int BN, bool A_K, bool B_K, int F8 = 0>
@@ -270,7 +263,7 @@ __device__ __forceinline__ void gemm_tile(GemmArgs p, const int bid, LDS_AS char
   if (p.offsets == nullptr) {
     const int tiles_m = (p.M + BM - 1) / BM, tiles_n = (p.N + BN - 1) / BN;
     const int ntiles = tiles_m * tiles_n;
-    const int t = tile_index(bid, ntiles);
+    const int t = xcd_index(bid, ntiles);
     constexpr int GM = 4;
     const int group = GM * tiles_n;
     const int first_m = (t / group) * GM;
