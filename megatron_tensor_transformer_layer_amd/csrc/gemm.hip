@@ -63,33 +63,44 @@ struct Operand {
   static constexpr int ROWB = ROWS * 2;        // row bytes of the mn-contiguous layout
   static constexpr int READS = (KC && EB == 2) ? 1 : 2;  // LDS read instructions per fragment
 
-  // Issue the DMA of slab [k0, k0+KSLAB) of rows [row0, row0+ROWS) into lds
-  // (ld and k0 in elements).
-  // k-contiguous: wave instruction I fills rows 8I..8I+7, lane -> (row 8I + l/8,
-  // physical chunk l%8 = logical chunk ^ kc_swz(row)).
+  // DMA of slab [k0, k0+KSLAB) of rows [row0, row0+ROWS) into lds (ld, k0 in
+  // elements).  Wave instruction I of the slab:
+  // k-contiguous: fills rows 8I..8I+7, lane -> (row 8I + l/8, physical chunk
+  // l%8 = logical chunk ^ kc_swz(row)).
   // mn-contiguous: lds byte o = 1024 I + 16 l is (k = o / ROWB, physical chunk
   // (o % ROWB)/16 = logical chunk ^ mn_swz(k)).
-  static __device__ __forceinline__ void load(i32x4 rs, int64_t ld, int row0, int k0, LDS_AS char* lds) {
+  // The per-lane byte offsets of slab 0 are computed once (offsets); slab k0
+  // adds the uniform slab_bytes(k0) to them, as 32-bit sums equal to the full
+  // offset taken mod 2^32.  The whole offset goes in the VGPR operand: the
+  // raw-buffer range check (which turns reads past the end into zeros) does not
+  // cover soffset.
+  static __device__ __forceinline__ void offsets(int64_t ld, int row0, uint32_t (&voff)[PER_WAVE]) {
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 #pragma unroll
     for (int q = 0; q < PER_WAVE; ++q) {
       const int I = wave * PER_WAVE + q;
-      // The whole offset goes in the VGPR operand: the raw-buffer range check
-      // (which turns reads past the end into zeros) does not cover soffset.
-      uint32_t voff;
       if constexpr (KC) {
         const int row = I * 8 + (lane >> 3);
         const int c = (lane & 7) ^ kc_swz(row);
-        voff = (uint32_t)(((int64_t)(row0 + row) * ld + k0 + c * CHUNK) * EB);
+        voff[q] = (uint32_t)(((int64_t)(row0 + row) * ld + c * CHUNK) * EB);
       } else {
         const int o = I * 1024 + lane * 16;
         const int k = o / ROWB;
         const int c = ((o % ROWB) >> 4) ^ mn_swz<ROWS>(k);
-        voff = (uint32_t)(((int64_t)(k0 + k) * ld + row0 + c * 8) * 2);
+        voff[q] = (uint32_t)(((int64_t)k * ld + row0 + c * 8) * 2);
       }
-      dma16(rs, voff, 0u, (uint32_t)(uintptr_t)(lds + I * 1024));
     }
+  }
+  static __device__ __forceinline__ uint32_t slab_bytes(int64_t ld, int k0) {
+    return KC ? (uint32_t)((int64_t)k0 * EB) : (uint32_t)((int64_t)k0 * ld * 2);
+  }
+  static __device__ __forceinline__ void load(i32x4 rs, const uint32_t (&voff)[PER_WAVE], uint32_t kb,
+                                              LDS_AS char* lds) {
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+#pragma unroll
+    for (int q = 0; q < PER_WAVE; ++q)
+      dma16(rs, voff[q] + kb, 0u, (uint32_t)(uintptr_t)(lds + (wave * PER_WAVE + q) * 1024));
   }
 
   // k-contiguous operand of a slab with kvalid < KSLAB valid k (after its DMA has
@@ -151,10 +162,14 @@ struct Mainloop {
   static constexpr int KSTEPS = F8 ? 2 : 4;  // MFMA k steps per slab
   static constexpr int STAGE = OA::BYTES + OB::BYTES;
 
-  static __device__ __forceinline__ void issue(const GemmArgs& p, i32x4 ra, i32x4 rb, int m0, int n0, int k0,
+  // per-lane DMA offsets of slab 0 for both operands
+  struct Dma {
+    uint32_t a[OA::PER_WAVE], b[OB::PER_WAVE];
+  };
+  static __device__ __forceinline__ void issue(const GemmArgs& p, i32x4 ra, i32x4 rb, const Dma& d, int k0,
                                                LDS_AS char* st) {
-    OA::load(ra, p.lda, m0, k0, st);
-    OB::load(rb, p.ldb, n0, k0, st + OA::BYTES);
+    OA::load(ra, d.a, OA::slab_bytes(p.lda, k0), st);
+    OB::load(rb, d.b, OB::slab_bytes(p.ldb, k0), st + OA::BYTES);
     __builtin_amdgcn_sched_barrier(0);  // keep the DMA issue ahead of the MFMA work
   }
   static __device__ __forceinline__ void settle(const GemmArgs& p, int k0, LDS_AS char* st) {
@@ -322,19 +337,22 @@ __device__ __forceinline__ void gemm_tile(GemmArgs p, const int bid, LDS_AS char
   const i32x4 ra = make_rsrc(p.a, (uint32_t)((A_K ? (int64_t)p.M : (int64_t)p.K) * p.lda * EB));
   const i32x4 rb = make_rsrc(p.b, (uint32_t)((B_K ? (int64_t)p.N : (int64_t)p.K) * p.ldb * EB));
   const int nk = (p.K + KSLAB - 1) / KSLAB;
-  ML::issue(p, ra, rb, m0, n0, 0, st0);
+  typename ML::Dma dma;
+  ML::OA::offsets(p.lda, m0, dma.a);
+  ML::OB::offsets(p.ldb, n0, dma.b);
+  ML::issue(p, ra, rb, dma, 0, st0);
   ML::settle(p, 0, st0);
   __syncthreads();
   // Two slabs per trip (stage 0 then stage 1), so each LDS stage is a fixed
   // object; an odd last slab is finished after the loop.
   int kt = 0;
   for (; kt + 1 < nk; kt += 2) {
-    ML::issue(p, ra, rb, m0, n0, (kt + 1) * KSLAB, st1);
+    ML::issue(p, ra, rb, dma, (kt + 1) * KSLAB, st1);
     ML::compute(st0, wm, wn, lane, acc);
     ML::settle(p, (kt + 1) * KSLAB, st1);
     __syncthreads();
     const bool more = kt + 2 < nk;
-    if (more) ML::issue(p, ra, rb, m0, n0, (kt + 2) * KSLAB, st0);
+    if (more) ML::issue(p, ra, rb, dma, (kt + 2) * KSLAB, st0);
     ML::compute(st1, wm, wn, lane, acc);
     if (more) ML::settle(p, (kt + 2) * KSLAB, st0);
     __syncthreads();
