@@ -262,24 +262,36 @@ __global__ __launch_bounds__(256, 1) void attn_fwd_kernel(AttnArgs a) {
 }
 
 // ============================================================== backward: D
-// delta[n][tok] = sum_i dO[tok][n*d+i] * O[tok][n*d+i]; one wave per (token, head).
+// delta[n][tok] = sum_i dO[tok][n*d+i] * O[tok][n*d+i]; eight lanes per
+// (token, head) row, each taking d/8 elements in 16-byte loads.
 template <int D>
 __global__ __launch_bounds__(256) void attn_delta_kernel(AttnArgs a) {
-  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int lane = threadIdx.x & 63;
+  constexpr int V = D / 64;  // 16-byte vectors per lane and tensor (1 or 2)
+  const int64_t row = (int64_t)blockIdx.x * 32 + (threadIdx.x >> 3);
+  const int sub = threadIdx.x & 7;
   const int64_t tokens = (int64_t)a.seq * a.batch;
-  if (row >= tokens * a.heads) return;
-  const int64_t tok = row / a.heads;
-  const int n = row % a.heads;
+  const bool ok = row < tokens * a.heads;
+  const int64_t tok = ok ? row / a.heads : 0;
+  const int n = ok ? (int)(row % a.heads) : 0;
   float acc = 0.f;
-  constexpr int PER = D / 64;  // elements per lane (1 or 2)
-  const uint16_t* po = a.out + tok * a.ld_o + (int64_t)n * D + lane * PER;
-  const uint16_t* pd = a.dout + tok * a.ld_o + (int64_t)n * D + lane * PER;
+  if (ok) {
+    const u32x4* po = reinterpret_cast<const u32x4*>(a.out + tok * a.ld_o + (int64_t)n * D) + sub * V;
+    const u32x4* pd = reinterpret_cast<const u32x4*>(a.dout + tok * a.ld_o + (int64_t)n * D) + sub * V;
+    u32x4 vo[V], vd[V];
 #pragma unroll
-  for (int i = 0; i < PER; ++i) acc += bf16_to_f32(po[i]) * bf16_to_f32(pd[i]);
+    for (int i = 0; i < V; ++i) {
+      vo[i] = po[i];
+      vd[i] = pd[i];
+    }
 #pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) acc += __shfl_xor(acc, off);
-  if (lane == 0) a.delta[(int64_t)n * tokens + tok] = acc;
+    for (int i = 0; i < V; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        acc += bf16_lo(vo[i][j]) * bf16_lo(vd[i][j]) + bf16_hi(vo[i][j]) * bf16_hi(vd[i][j]);
+  }
+#pragma unroll
+  for (int off = 4; off >= 1; off >>= 1) acc += __shfl_xor(acc, off);
+  if (ok && sub == 0) a.delta[(int64_t)n * tokens + tok] = acc;
 }
 
 // ============================================================== backward
@@ -563,7 +575,7 @@ static hipError_t fwd_d(const AttnArgs& a, hipStream_t s) {
 template <int D>
 static hipError_t bwd_d(const AttnArgs& a, hipStream_t s) {
   const int64_t rows = (int64_t)a.seq * a.batch * a.heads;
-  hipLaunchKernelGGL(attn_delta_kernel<D>, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, s, a);
+  hipLaunchKernelGGL(attn_delta_kernel<D>, dim3((unsigned)((rows + 31) / 32)), dim3(256), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int64_t units = (int64_t)((a.seq + 63) / 64) * a.heads * a.batch;

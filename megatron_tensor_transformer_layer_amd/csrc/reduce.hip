@@ -7,9 +7,10 @@
 //
 // colsum_bf16: the bias gradients of the four linears are column sums of a
 // [rows, cols] bf16 gradient.  Deterministic two-stage sum: stage 1 gives each
-// 256-thread block 512 columns x 128 rows (16-byte loads, fp32 accumulate, the
-// four waves combined in a fixed order) and writes one partial row to the
-// workspace; stage 2 adds the partial rows in order.
+// 256-thread block 512 columns x 64 rows (16-byte loads, all 16 of a lane in
+// flight at once, fp32 accumulate, the four waves combined in a fixed order)
+// and writes one partial row to the workspace; stage 2 adds the partial rows,
+// four waves each taking every fourth one, combined in wave order.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -83,7 +84,7 @@ hipError_t reduce_partials(int t, const uint16_t* const* partials, const uint16_
   return hipGetLastError();
 }
 
-constexpr int CS_ROWS = 128;  // rows per stage-1 block (32 per wave)
+constexpr int CS_ROWS = 64;   // rows per stage-1 block (16 per wave)
 constexpr int CS_COLS = 512;  // columns per stage-1 block (8 per lane)
 
 size_t colsum_ws_floats(int64_t rows, int64_t cols) {
@@ -101,15 +102,20 @@ __global__ __launch_bounds__(256) void colsum_stage1(const uint16_t* __restrict_
   const int64_t r1 = min(rows, r0 + CS_ROWS);
   float s[8] = {0, 0, 0, 0, 0, 0, 0, 0};
   if (c < cols) {
-#pragma unroll 4
-    for (int64_t r = r0 + wave; r < r1; r += 4) {
-      const u32x4 v = *reinterpret_cast<const u32x4*>(x + r * ld + c);
+    constexpr int PER = CS_ROWS / 4;  // rows of this wave: r0 + wave + 4i
+    u32x4 v[PER];
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int64_t r = r0 + wave + 4 * i;
+      v[i] = r < r1 ? *reinterpret_cast<const u32x4*>(x + r * ld + c) : u32x4{0, 0, 0, 0};
+    }
+#pragma unroll
+    for (int i = 0; i < PER; ++i)
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        s[2 * j] += bf16_lo(v[j]);
-        s[2 * j + 1] += bf16_hi(v[j]);
+        s[2 * j] += bf16_lo(v[i][j]);
+        s[2 * j + 1] += bf16_hi(v[i][j]);
       }
-    }
   }
   if (wave > 0) {
     part[wave - 1][lane][0] = f32x4{s[0], s[1], s[2], s[3]};
@@ -129,15 +135,33 @@ __global__ __launch_bounds__(256) void colsum_stage1(const uint16_t* __restrict_
   }
 }
 
-// Stage 2: one thread per column adds the chunk partials in chunk order.
-__global__ __launch_bounds__(64) void colsum_stage2(const float* __restrict__ ws, int64_t chunks, int64_t cols,
+// Stage 2: 256 columns per block, 4 per lane; wave w adds chunk partials
+// w, w+4, w+8, ... in order, and the four wave sums are added in wave order.
+__global__ __launch_bounds__(256) void colsum_stage2(const float* __restrict__ ws, int64_t chunks, int64_t cols,
                                                      float* __restrict__ out, int accumulate) {
-  const int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (c >= cols) return;
-  float s = 0.f;
-#pragma unroll 8
-  for (int64_t k = 0; k < chunks; ++k) s += ws[k * cols + c];
-  out[c] = accumulate ? out[c] + s : s;
+  __shared__ f32x4 part[3][64];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t c = (int64_t)blockIdx.x * 256 + lane * 4;
+  f32x4 s = {0.f, 0.f, 0.f, 0.f};
+  if (c < cols) {
+    int64_t k = wave;
+    for (; k + 28 < chunks; k += 32) {  // eight loads in flight
+      f32x4 v[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) v[i] = *reinterpret_cast<const f32x4*>(ws + (k + 4 * i) * cols + c);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) s += v[i];
+    }
+    for (; k < chunks; k += 4) s += *reinterpret_cast<const f32x4*>(ws + k * cols + c);
+  }
+  if (wave > 0) part[wave - 1][lane] = s;
+  __syncthreads();
+  if (wave == 0 && c < cols) {
+#pragma unroll
+    for (int w = 0; w < 3; ++w) s += part[w][lane];
+    f32x4* o = reinterpret_cast<f32x4*>(out + c);
+    *o = accumulate ? *o + s : s;
+  }
 }
 
 hipError_t colsum_bf16(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld, float* out, bool accumulate,
@@ -150,7 +174,7 @@ hipError_t colsum_bf16(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL(colsum_stage2, dim3((unsigned)((cols + 63) / 64)), dim3(64), 0, s, ws, chunks, cols, out,
+  hipLaunchKernelGGL(colsum_stage2, dim3((unsigned)((cols + 255) / 256)), dim3(256), 0, s, ws, chunks, cols, out,
                      accumulate ? 1 : 0);
   return hipGetLastError();
 }
