@@ -159,7 +159,7 @@ size_t mlp_scratch(const mtl_layer_cfg* c, const Dims& d, MlpScratch* s, char* b
   Bump b{base};
   MlpScratch t{};
   t.dz = b.take<uint16_t>(d.S * d.f_l * 2);
-  t.ws = b.take<float>(colsum_ws_floats(d.S, d.f_l > d.h ? d.f_l : d.h) * 4);
+  t.ws = b.take<float>(colsum_ws_floats(d.S, d.f_l + d.h) * 4);
   if (is_fp8(c)) {
     t.dy = q8(b, d.S, d.h, E5M2, true, true);
     t.w2 = q8(b, d.f_l, d.h, E4M3, true, false);
@@ -179,7 +179,7 @@ size_t attn_scratch(const mtl_layer_cfg* c, const Dims& d, AttnScratch* s, char*
   t.dout = b.take<uint16_t>(d.S * d.o_l * 2);
   t.dqkv = b.take<uint16_t>(d.S * d.qkv_l * 2);
   t.delta = b.take<float>(d.heads_l * d.S * 4);
-  t.ws = b.take<float>(colsum_ws_floats(d.S, d.qkv_l > d.h ? d.qkv_l : d.h) * 4);
+  t.ws = b.take<float>(colsum_ws_floats(d.S, d.qkv_l + d.h) * 4);
   if (is_fp8(c)) {
     t.dh = q8(b, d.S, d.h, E5M2, true, true);
     t.wo = q8(b, d.o_l, d.h, E4M3, true, false);
@@ -377,6 +377,20 @@ mtl_status mtl_mlp_fwd(const mtl_layer_cfg* c, const void* h, const void* w1, co
   return MTL_OK;
 }
 
+// db1 = colsum(dz) and, when wanted, db2 = colsum(dy): one pair of launches.
+static hipError_t mlp_bias_grads(const Dims& d, const MlpScratch& ws, const void* dy, float* db1, float* db2,
+                                 bool accum, hipStream_t s) {
+  const ColsumJob jobs[2] = {{ws.dz, d.f_l, db1}, {static_cast<const uint16_t*>(dy), d.h, db2}};
+  return colsum_bf16(jobs, db2 ? 2 : 1, d.S, accum, ws.ws, s);
+}
+
+// db_qkv = colsum(dqkv) and, when wanted, db_o = colsum(dh): one pair of launches.
+static hipError_t attn_bias_grads(const Dims& d, const AttnScratch& ws, const void* dh, float* db_qkv,
+                                  float* db_o, bool accum, hipStream_t s) {
+  const ColsumJob jobs[2] = {{ws.dqkv, d.qkv_l, db_qkv}, {static_cast<const uint16_t*>(dh), d.h, db_o}};
+  return colsum_bf16(jobs, db_o ? 2 : 1, d.S, accum, ws.ws, s);
+}
+
 mtl_status mtl_mlp_bwd(const mtl_layer_cfg* c, const void* dy, const void* h, const void* z, const void* a,
                        const void* w1, const void* w2, void* dh_partial, float* dw1, float* db1, float* dw2,
                        float* db2, void* scratch, size_t scratch_bytes, mtl_stream_t stream) {
@@ -401,8 +415,7 @@ mtl_status mtl_mlp_bwd(const mtl_layer_cfg* c, const void* dy, const void* h, co
     MTL_TRY(quantize(ws.dz, ws.dz8, ws.amax_ws, s));
     MTL_TRY(quantize(h, ws.h_t, ws.amax_ws, s));
     MTL_TRY(gemm8(ws.h_t, ws.h_t.qt, ws.dz8, ws.dz8.qt, d.h, d.f_l, d.S, dw1, d.f_l, wepi, s));
-    MTL_TRY(colsum_bf16(ws.dz, d.S, d.f_l, d.f_l, db1, accum, ws.ws, s));
-    if (db2) MTL_TRY(colsum_bf16(static_cast<const uint16_t*>(dy), d.S, d.h, d.h, db2, accum, ws.ws, s));
+    MTL_TRY(mlp_bias_grads(d, ws, dy, db1, db2, accum, s));
     MTL_TRY(quantize(w1, ws.w1, ws.amax_ws, s));
     MTL_TRY(gemm8(ws.dz8, ws.dz8.q, ws.w1, ws.w1.q, d.S, d.h, d.f_l, dh_partial, d.h, EPI_BF16, s));
     return MTL_OK;
@@ -413,8 +426,7 @@ mtl_status mtl_mlp_bwd(const mtl_layer_cfg* c, const void* dy, const void* h, co
   g.ld_aux = d.f_l;
   GemmArgs g2 = gemm(a, d.f_l, dy, d.h, d.f_l, d.h, d.S, dw2, d.h);
   MTL_TRY(gemm_bf16_pair(g, GEMM_DGRAD, EPI_DGELU, g2, GEMM_WGRAD, wepi, s));
-  MTL_TRY(colsum_bf16(ws.dz, d.S, d.f_l, d.f_l, db1, accum, ws.ws, s));
-  if (db2) MTL_TRY(colsum_bf16(static_cast<const uint16_t*>(dy), d.S, d.h, d.h, db2, accum, ws.ws, s));
+  MTL_TRY(mlp_bias_grads(d, ws, dy, db1, db2, accum, s));
   // dw1 = h^T . dz and dh_partial = dz . w1^T
   g = gemm(h, d.h, ws.dz, d.f_l, d.h, d.f_l, d.S, dw1, d.f_l);
   g2 = gemm(ws.dz, d.f_l, w1, d.f_l, d.S, d.h, d.f_l, dh_partial, d.h);
@@ -452,7 +464,6 @@ mtl_status mtl_attn_bwd(const mtl_layer_cfg* c, const void* dh, const void* x, c
     GemmArgs g2 = gemm(o, d.o_l, dh, d.h, d.o_l, d.h, d.S, dw_o, d.h);
     MTL_TRY(gemm_bf16_pair(g, GEMM_DGRAD, EPI_BF16, g2, GEMM_WGRAD, wepi, s));
   }
-  if (db_o) MTL_TRY(colsum_bf16(static_cast<const uint16_t*>(dh), d.S, d.h, d.h, db_o, accum, ws.ws, s));
 
   AttnArgs at{};
   at.qkv = static_cast<const uint16_t*>(qkv);
@@ -475,16 +486,17 @@ mtl_status mtl_attn_bwd(const mtl_layer_cfg* c, const void* dh, const void* x, c
     MTL_TRY(quantize(ws.dqkv, ws.dqkv8, ws.amax_ws, s));
     MTL_TRY(quantize(x, ws.x_t, ws.amax_ws, s));
     MTL_TRY(gemm8(ws.x_t, ws.x_t.qt, ws.dqkv8, ws.dqkv8.qt, d.h, d.qkv_l, d.S, dw_qkv, d.qkv_l, wepi, s));
-    MTL_TRY(colsum_bf16(ws.dqkv, d.S, d.qkv_l, d.qkv_l, db_qkv, accum, ws.ws, s));
+    MTL_TRY(attn_bias_grads(d, ws, dh, db_qkv, db_o, accum, s));
     MTL_TRY(quantize(w_qkv, ws.wqkv, ws.amax_ws, s));
     MTL_TRY(gemm8(ws.dqkv8, ws.dqkv8.q, ws.wqkv, ws.wqkv.q, d.S, d.h, d.qkv_l, dx_partial, d.h, EPI_BF16, s));
     return MTL_OK;
   }
-  // dw_qkv = x^T . dqkv and dx_partial = dqkv . w_qkv^T, one launch; db_qkv = colsum(dqkv)
+  // dw_qkv = x^T . dqkv and dx_partial = dqkv . w_qkv^T, one launch; then
+  // db_qkv = colsum(dqkv) and db_o = colsum(dh)
   GemmArgs g = gemm(x, d.h, ws.dqkv, d.qkv_l, d.h, d.qkv_l, d.S, dw_qkv, d.qkv_l);
   GemmArgs g2 = gemm(ws.dqkv, d.qkv_l, w_qkv, d.qkv_l, d.S, d.h, d.qkv_l, dx_partial, d.h);
   MTL_TRY(gemm_bf16_pair(g, GEMM_WGRAD, wepi, g2, GEMM_DGRAD, EPI_BF16, s));
-  MTL_TRY(colsum_bf16(ws.dqkv, d.S, d.qkv_l, d.qkv_l, db_qkv, accum, ws.ws, s));
+  MTL_TRY(attn_bias_grads(d, ws, dh, db_qkv, db_o, accum, s));
   return MTL_OK;
 }
 

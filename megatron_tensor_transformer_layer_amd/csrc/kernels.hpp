@@ -96,11 +96,16 @@ hipError_t attention_bwd(const AttnArgs& a, hipStream_t s);
 // out[r, :] = sum_i partials[i][r, :] (+ bias) (+ residual) for r in [row_begin, row_end).
 hipError_t reduce_partials(int t, const uint16_t* const* partials, const uint16_t* bias, const uint16_t* residual,
                            uint16_t* out, int64_t cols, int64_t row_begin, int64_t row_end, hipStream_t s);
-// out[c] (=|+=) sum_r x[r][c], fp32; deterministic two-stage; ws holds
-// colsum_ws_floats(rows, cols) floats.
+// For one or two jobs j: out_j[c] (=|+=) sum_r x_j[r][c] over [rows, cols_j]
+// row-major bf16, fp32, deterministic, two launches for all jobs together;
+// ws holds colsum_ws_floats(rows, cols_0 + cols_1) floats.
+struct ColsumJob {
+  const uint16_t* x;
+  int64_t cols;
+  float* out;
+};
 size_t colsum_ws_floats(int64_t rows, int64_t cols);
-hipError_t colsum_bf16(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld, float* out, bool accumulate,
-                       float* ws, hipStream_t s);
+hipError_t colsum_bf16(const ColsumJob* jobs, int njobs, int64_t rows, bool accumulate, float* ws, hipStream_t s);
 
 // ---------------------------------------------------------------- fp8 scaling
 // rec[0..2] = {amax, s, 1/s} of n bf16 values for format fmt (0 = E4M3, 1 = E5M2);

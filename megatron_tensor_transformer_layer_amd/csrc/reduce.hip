@@ -91,15 +91,30 @@ size_t colsum_ws_floats(int64_t rows, int64_t cols) {
   return (size_t)((rows + CS_ROWS - 1) / CS_ROWS) * (size_t)cols;
 }
 
+// Up to two column sums in one pair of launches (the bias gradients that are
+// ready at the same point of a backward pass).
+struct ColsumArgs {
+  const uint16_t* x[2];
+  float* out[2];
+  float* ws[2];
+  int64_t cols[2];
+  int64_t rows, chunks;
+  int split1, split2;  // stage-1 / stage-2 blocks of job 0
+  int accumulate;
+};
+
 // Stage 1: block (column slab, row chunk); wave w sums rows r0+w, r0+w+4, ...
 // of its 512 columns; the four wave sums are added in wave order through LDS.
-__global__ __launch_bounds__(256) void colsum_stage1(const uint16_t* __restrict__ x, int64_t rows, int64_t cols,
-                                                      int64_t ld, float* __restrict__ ws) {
+__global__ __launch_bounds__(256) void colsum_stage1(ColsumArgs a) {
   __shared__ f32x4 part[3][64][2];
+  const int job = (int)blockIdx.x < a.split1 ? 0 : 1;
+  const int slab = (int)blockIdx.x - (job ? a.split1 : 0);
+  const uint16_t* x = a.x[job];
+  const int64_t cols = a.cols[job];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int64_t c = (int64_t)blockIdx.x * CS_COLS + lane * 8;
+  const int64_t c = (int64_t)slab * CS_COLS + lane * 8;
   const int64_t r0 = (int64_t)blockIdx.y * CS_ROWS;
-  const int64_t r1 = min(rows, r0 + CS_ROWS);
+  const int64_t r1 = min(a.rows, r0 + CS_ROWS);
   float s[8] = {0, 0, 0, 0, 0, 0, 0, 0};
   if (c < cols) {
     constexpr int PER = CS_ROWS / 4;  // rows of this wave: r0 + wave + 4i
@@ -107,7 +122,7 @@ __global__ __launch_bounds__(256) void colsum_stage1(const uint16_t* __restrict_
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
       const int64_t r = r0 + wave + 4 * i;
-      v[i] = r < r1 ? *reinterpret_cast<const u32x4*>(x + r * ld + c) : u32x4{0, 0, 0, 0};
+      v[i] = r < r1 ? *reinterpret_cast<const u32x4*>(x + r * cols + c) : u32x4{0, 0, 0, 0};
     }
 #pragma unroll
     for (int i = 0; i < PER; ++i)
@@ -125,11 +140,11 @@ __global__ __launch_bounds__(256) void colsum_stage1(const uint16_t* __restrict_
   if (wave == 0 && c < cols) {
 #pragma unroll
     for (int w = 0; w < 3; ++w) {
-      const f32x4 a = part[w][lane][0], b = part[w][lane][1];
-      s[0] += a[0]; s[1] += a[1]; s[2] += a[2]; s[3] += a[3];
-      s[4] += b[0]; s[5] += b[1]; s[6] += b[2]; s[7] += b[3];
+      const f32x4 p0 = part[w][lane][0], p1 = part[w][lane][1];
+      s[0] += p0[0]; s[1] += p0[1]; s[2] += p0[2]; s[3] += p0[3];
+      s[4] += p1[0]; s[5] += p1[1]; s[6] += p1[2]; s[7] += p1[3];
     }
-    float* w = ws + (int64_t)blockIdx.y * cols + c;
+    float* w = a.ws[job] + (int64_t)blockIdx.y * cols + c;
     *reinterpret_cast<f32x4*>(w) = f32x4{s[0], s[1], s[2], s[3]};
     *reinterpret_cast<f32x4*>(w + 4) = f32x4{s[4], s[5], s[6], s[7]};
   }
@@ -137,11 +152,14 @@ __global__ __launch_bounds__(256) void colsum_stage1(const uint16_t* __restrict_
 
 // Stage 2: 256 columns per block, 4 per lane; wave w adds chunk partials
 // w, w+4, w+8, ... in order, and the four wave sums are added in wave order.
-__global__ __launch_bounds__(256) void colsum_stage2(const float* __restrict__ ws, int64_t chunks, int64_t cols,
-                                                     float* __restrict__ out, int accumulate) {
+__global__ __launch_bounds__(256) void colsum_stage2(ColsumArgs a) {
   __shared__ f32x4 part[3][64];
+  const int job = (int)blockIdx.x < a.split2 ? 0 : 1;
+  const int blk = (int)blockIdx.x - (job ? a.split2 : 0);
+  const float* ws = a.ws[job];
+  const int64_t cols = a.cols[job], chunks = a.chunks;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int64_t c = (int64_t)blockIdx.x * 256 + lane * 4;
+  const int64_t c = (int64_t)blk * 256 + lane * 4;
   f32x4 s = {0.f, 0.f, 0.f, 0.f};
   if (c < cols) {
     int64_t k = wave;
@@ -159,23 +177,38 @@ __global__ __launch_bounds__(256) void colsum_stage2(const float* __restrict__ w
   if (wave == 0 && c < cols) {
 #pragma unroll
     for (int w = 0; w < 3; ++w) s += part[w][lane];
-    f32x4* o = reinterpret_cast<f32x4*>(out + c);
-    *o = accumulate ? *o + s : s;
+    f32x4* o = reinterpret_cast<f32x4*>(a.out[job] + c);
+    *o = a.accumulate ? *o + s : s;
   }
 }
 
-hipError_t colsum_bf16(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld, float* out, bool accumulate,
-                       float* ws, hipStream_t s) {
-  if (cols <= 0) return hipSuccess;
-  const int64_t chunks = (rows + CS_ROWS - 1) / CS_ROWS;
-  if (chunks > 0) {
-    dim3 g1((unsigned)((cols + CS_COLS - 1) / CS_COLS), (unsigned)chunks);
-    hipLaunchKernelGGL(colsum_stage1, g1, dim3(256), 0, s, x, rows, cols, ld, ws);
+hipError_t colsum_bf16(const ColsumJob* jobs, int njobs, int64_t rows, bool accumulate, float* ws, hipStream_t s) {
+  if (njobs < 1 || njobs > 2) return hipErrorInvalidValue;
+  ColsumArgs a{};
+  a.rows = rows;
+  a.chunks = (rows + CS_ROWS - 1) / CS_ROWS;
+  a.accumulate = accumulate ? 1 : 0;
+  int64_t b1 = 0, b2 = 0, off = 0;
+  for (int j = 0; j < njobs; ++j) {
+    a.x[j] = jobs[j].x;
+    a.out[j] = jobs[j].out;
+    a.cols[j] = jobs[j].cols;
+    a.ws[j] = ws + off;
+    off += a.chunks * jobs[j].cols;
+    b1 += (jobs[j].cols + CS_COLS - 1) / CS_COLS;
+    b2 += (jobs[j].cols + 255) / 256;
+    if (j == 0) {
+      a.split1 = (int)b1;
+      a.split2 = (int)b2;
+    }
+  }
+  if (b1 == 0) return hipSuccess;
+  if (a.chunks > 0) {
+    hipLaunchKernelGGL(colsum_stage1, dim3((unsigned)b1, (unsigned)a.chunks), dim3(256), 0, s, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL(colsum_stage2, dim3((unsigned)((cols + 255) / 256)), dim3(256), 0, s, ws, chunks, cols, out,
-                     accumulate ? 1 : 0);
+  hipLaunchKernelGGL(colsum_stage2, dim3((unsigned)b2), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
