@@ -420,12 +420,14 @@ mtl_status mtl_mlp_bwd(const mtl_layer_cfg* c, const void* dy, const void* h, co
     MTL_TRY(gemm8(ws.dz8, ws.dz8.q, ws.w1, ws.w1.q, d.S, d.h, d.f_l, dh_partial, d.h, EPI_BF16, s));
     return MTL_OK;
   }
-  // dz = (dy . w2^T) * GeLU'(z), with the independent dw2 = a^T . dy in the same launch
+  // dz = (dy . w2^T) * GeLU'(z), with the independent dw2 = a^T . dy in the same
+  // launch; the wgrad tiles go first, so their fp32 output drains under the
+  // dgrad tiles' main loops
   GemmArgs g = gemm(dy, d.h, w2, d.h, d.S, d.f_l, d.h, ws.dz, d.f_l);
   g.aux = static_cast<const uint16_t*>(z);
   g.ld_aux = d.f_l;
   GemmArgs g2 = gemm(a, d.f_l, dy, d.h, d.f_l, d.h, d.S, dw2, d.h);
-  MTL_TRY(gemm_bf16_pair(g, GEMM_DGRAD, EPI_DGELU, g2, GEMM_WGRAD, wepi, s));
+  MTL_TRY(gemm_bf16_pair(g2, GEMM_WGRAD, wepi, g, GEMM_DGRAD, EPI_DGELU, s));
   MTL_TRY(mlp_bias_grads(d, ws, dy, db1, db2, accum, s));
   // dw1 = h^T . dz and dh_partial = dz . w1^T
   g = gemm(h, d.h, ws.dz, d.f_l, d.h, d.f_l, d.S, dw1, d.f_l);
@@ -459,10 +461,10 @@ mtl_status mtl_attn_bwd(const mtl_layer_cfg* c, const void* dh, const void* x, c
     MTL_TRY(quantize(o, ws.o_t, ws.amax_ws, s));
     MTL_TRY(gemm8(ws.o_t, ws.o_t.qt, ws.dh, ws.dh.qt, d.o_l, d.h, d.S, dw_o, d.h, wepi, s));
   } else {
-    // do = dh . w_o^T and dw_o = o^T . dh, one launch
+    // dw_o = o^T . dh and do = dh . w_o^T, one launch (wgrad tiles first)
     GemmArgs g = gemm(dh, d.h, w_o, d.h, d.S, d.o_l, d.h, ws.dout, d.o_l);
     GemmArgs g2 = gemm(o, d.o_l, dh, d.h, d.o_l, d.h, d.S, dw_o, d.h);
-    MTL_TRY(gemm_bf16_pair(g, GEMM_DGRAD, EPI_BF16, g2, GEMM_WGRAD, wepi, s));
+    MTL_TRY(gemm_bf16_pair(g2, GEMM_WGRAD, wepi, g, GEMM_DGRAD, EPI_BF16, s));
   }
 
   AttnArgs at{};

@@ -496,7 +496,8 @@ struct TileCfg {
 // Two independent GEMMs in one launch: workgroups [0, tiles1) take p1, the rest
 // p2.  With one tile per CU, the second GEMM's tiles start as the first GEMM's
 // finish, so the first GEMM's output stores drain under the second's main loop
-// instead of at a kernel boundary.
+// instead of at a kernel boundary.  The weight-gradient GEMM (fp32 output,
+// twice the bytes) is always the first of the pair.
 template <class C1, class C2>
 __global__ __launch_bounds__(256, 1) void gemm_pair_kernel(GemmArgs p1, GemmArgs p2, int tiles1) {
   constexpr int STAGE = C1::STAGE > C2::STAGE ? C1::STAGE : C2::STAGE;
@@ -556,17 +557,17 @@ static hipError_t launch_pair(const GemmArgs& p1, const GemmArgs& p2, hipStream_
 // The backward's independent pairs: dgrad (+GeLU') with wgrad, wgrad with dgrad.
 template <int EPI_W>
 static hipError_t pair_dispatch(const GemmArgs& p1, GemmLayout l1, int e1, const GemmArgs& p2, GemmLayout l2,
-                                int k1, int k2, hipStream_t s, bool* done) {
+                                int e2, int k1, int k2, hipStream_t s, bool* done) {
   *done = true;
   using W256 = TileCfg<256, 256, false, false, EPI_W>;
   using W192 = TileCfg<256, 192, false, false, EPI_W>;
   using W128 = TileCfg<128, 128, false, false, EPI_W>;
-  if (l1 == GEMM_DGRAD && l2 == GEMM_WGRAD && k1 == 0 && k2 == 0 && e1 == EPI_DGELU)
-    return launch_pair<TileCfg<256, 256, true, true, EPI_DGELU>, W256>(p1, p2, s);
-  if (l1 == GEMM_DGRAD && l2 == GEMM_WGRAD && k1 == 2 && k2 == 2 && e1 == EPI_BF16)
-    return launch_pair<TileCfg<128, 128, true, true, EPI_BF16>, W128>(p1, p2, s);
+  if (l1 == GEMM_WGRAD && l2 == GEMM_DGRAD && k1 == 0 && k2 == 0 && e2 == EPI_DGELU)
+    return launch_pair<W256, TileCfg<256, 256, true, true, EPI_DGELU>>(p1, p2, s);
   if (l1 == GEMM_WGRAD && l2 == GEMM_DGRAD && k1 == 0 && k2 == 0)
     return launch_pair<W256, TileCfg<256, 256, true, true, EPI_BF16>>(p1, p2, s);
+  if (l1 == GEMM_WGRAD && l2 == GEMM_DGRAD && k1 == 2 && k2 == 2 && e2 == EPI_BF16)
+    return launch_pair<W128, TileCfg<128, 128, true, true, EPI_BF16>>(p1, p2, s);
   if (l1 == GEMM_WGRAD && l2 == GEMM_DGRAD && k1 == 1 && k2 == 0)
     return launch_pair<W192, TileCfg<256, 256, true, true, EPI_BF16>>(p1, p2, s);
   *done = false;
@@ -580,7 +581,8 @@ hipError_t gemm_bf16_pair(const GemmArgs& p1, GemmLayout l1, int e1, const GemmA
                      p2.K > 0;
   const bool wgrad_ok = (l1 == GEMM_WGRAD) ? (e1 == EPI_F32 || e1 == EPI_F32_ACC)
                                            : (l2 == GEMM_WGRAD && (e2 == EPI_F32 || e2 == EPI_F32_ACC));
-  const bool dgrad_ok = (l1 == GEMM_DGRAD) ? (e1 == EPI_BF16 || e1 == EPI_DGELU) : (l2 == GEMM_DGRAD && e2 == EPI_BF16);
+  const bool dgrad_ok = (l1 == GEMM_DGRAD) ? (e1 == EPI_BF16 || e1 == EPI_DGELU)
+                                           : (l2 == GEMM_DGRAD && (e2 == EPI_BF16 || e2 == EPI_DGELU));
   const bool fits = [&] {  // the same 32-bit offset bound gemm_bf16 checks
     for (const GemmArgs* q : {&p1, &p2}) {
       const bool wg = (q == &p1 ? l1 : l2) == GEMM_WGRAD;
@@ -592,9 +594,9 @@ hipError_t gemm_bf16_pair(const GemmArgs& p1, GemmLayout l1, int e1, const GemmA
   if (plain && wgrad_ok && dgrad_ok && fits && l1 != l2) {
     const int ew = l1 == GEMM_WGRAD ? e1 : e2;
     bool done = false;
-    hipError_t e = ew == EPI_F32 ? pair_dispatch<EPI_F32>(p1, l1, e1, p2, l2, tile_kind(p1), tile_kind(p2), s, &done)
-                                 : pair_dispatch<EPI_F32_ACC>(p1, l1, e1, p2, l2, tile_kind(p1), tile_kind(p2), s,
-                                                              &done);
+    hipError_t e = ew == EPI_F32
+                       ? pair_dispatch<EPI_F32>(p1, l1, e1, p2, l2, e2, tile_kind(p1), tile_kind(p2), s, &done)
+                       : pair_dispatch<EPI_F32_ACC>(p1, l1, e1, p2, l2, e2, tile_kind(p1), tile_kind(p2), s, &done);
     if (done) return e;
   }
   hipError_t e = gemm_bf16(p1, l1, e1, s);
