@@ -186,6 +186,14 @@ mtl_status mtl_fp8_amax(const void* x, int64_t n, int32_t format, float* rec, vo
 mtl_status mtl_fp8_cast(const void* x, int64_t rows, int64_t cols, int32_t format, const float* rec, void* out,
                         void* out_t, mtl_stream_t stream);
 
+/* mtl_fp8_amax over the rows*cols values of x, then mtl_fp8_cast with the
+ * record it wrote, in one launch fewer (the cast finishes the amax): rec and
+ * the codes are bit-identical to the two calls.  Arguments and rules as there
+ * (scratch >= MTL_FP8_AMAX_SCRATCH bytes).  This is how the layer entry points
+ * quantise their GEMM operands. */
+mtl_status mtl_fp8_quantize(const void* x, int64_t rows, int64_t cols, int32_t format, float* rec, void* out,
+                            void* out_t, void* scratch, size_t scratch_bytes, mtl_stream_t stream);
+
 /* ------------------------------------------------------------------------
  * MoE expert block of one expert-parallel rank.
  *

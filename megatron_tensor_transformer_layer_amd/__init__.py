@@ -55,6 +55,7 @@ _SIGS = {
     "mtl_attn_bwd": (ctypes.c_int, [_CFG, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "mtl_fp8_amax": (ctypes.c_int, [_P, _I64, _I32, _P, _P, _SZ, _P]),
     "mtl_fp8_cast": (ctypes.c_int, [_P, _I64, _I64, _I32, _P, _P, _P, _P]),
+    "mtl_fp8_quantize": (ctypes.c_int, [_P, _I64, _I64, _I32, _P, _P, _P, _P, _SZ, _P]),
     "mtl_moe_validate": (ctypes.c_int, [_MCFG]),
     "mtl_moe_sizes": (ctypes.c_int, [_MCFG, ctypes.POINTER(_I64), ctypes.POINTER(_SZ)]),
     "mtl_moe_route": (ctypes.c_int, [_MCFG, _P, _P, _P, _P]),
@@ -212,3 +213,8 @@ def mtl_fp8_amax(x, n, fmt, rec, scratch, scratch_bytes=None, stream=None):
 def mtl_fp8_cast(x, rows, cols, fmt, rec, out, out_t=None, stream=None):
     _check(lib().mtl_fp8_cast(_ptr(x), rows, cols, fmt, _ptr(rec), _ptr(out), _ptr(out_t), _stream(stream)),
            "mtl_fp8_cast")
+
+
+def mtl_fp8_quantize(x, rows, cols, fmt, rec, out, out_t, scratch, scratch_bytes=None, stream=None):
+    _check(lib().mtl_fp8_quantize(_ptr(x), rows, cols, fmt, _ptr(rec), _ptr(out), _ptr(out_t), _ptr(scratch),
+                                  _nbytes(scratch, scratch_bytes), _stream(stream)), "mtl_fp8_quantize")

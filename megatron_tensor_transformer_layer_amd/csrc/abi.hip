@@ -100,9 +100,7 @@ Q8 q8(Bump& b, int64_t rows, int64_t cols, int fmt, bool normal, bool trans) {
 constexpr int E4M3 = 0, E5M2 = 1;
 
 hipError_t quantize(const void* x, const Q8& q, void* amax_ws, hipStream_t s) {
-  hipError_t e = fp8_amax(static_cast<const uint16_t*>(x), q.rows * q.cols, q.fmt, q.rec, amax_ws, s);
-  if (e != hipSuccess) return e;
-  return fp8_cast(static_cast<const uint16_t*>(x), q.rows, q.cols, q.fmt, q.rec, q.q, q.qt, s);
+  return fp8_quantize(static_cast<const uint16_t*>(x), q.rows, q.cols, q.fmt, q.rec, amax_ws, q.q, q.qt, s);
 }
 
 // fp8 GEMM C[M, N] = A . B^T over K, both operands k-contiguous codes.
@@ -525,6 +523,20 @@ mtl_status mtl_fp8_cast(const void* x, int64_t rows, int64_t cols, int32_t forma
   if (format != MTL_FP8_E4M3 && format != MTL_FP8_E5M2) return MTL_E_UNSUPPORTED;
   return hip_status(fp8_cast(static_cast<const uint16_t*>(x), rows, cols, format, rec, static_cast<uint8_t*>(out),
                              static_cast<uint8_t*>(out_t), reinterpret_cast<hipStream_t>(stream)));
+}
+
+mtl_status mtl_fp8_quantize(const void* x, int64_t rows, int64_t cols, int32_t format, float* rec, void* out,
+                            void* out_t, void* scratch, size_t scratch_bytes, mtl_stream_t stream) {
+  mtl_status st = check_ptrs(x, rec, scratch);
+  if (st != MTL_OK) return st;
+  if (!out && !out_t) return MTL_E_NULL;
+  if ((out && !aligned16(out)) || (out_t && !aligned16(out_t))) return MTL_E_ALIGN;
+  if (rows <= 0 || cols <= 0 || cols % 8 != 0 || (out_t && rows % 16 != 0)) return MTL_E_SHAPE;
+  if (format != MTL_FP8_E4M3 && format != MTL_FP8_E5M2) return MTL_E_UNSUPPORTED;
+  if (scratch_bytes < fp8_amax_ws_bytes()) return MTL_E_WORKSPACE;
+  return hip_status(fp8_quantize(static_cast<const uint16_t*>(x), rows, cols, format, rec, scratch,
+                                 static_cast<uint8_t*>(out), static_cast<uint8_t*>(out_t),
+                                 reinterpret_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

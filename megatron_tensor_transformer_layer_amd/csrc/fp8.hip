@@ -42,9 +42,9 @@ __global__ __launch_bounds__(256) void amax_stage1(const uint16_t* __restrict__ 
   if (threadIdx.x == 0) part[blockIdx.x] = max(max(sh[0], sh[1]), max(sh[2], sh[3]));
 }
 
-// rec = {amax, s, 1/s}; s = fmt_max / amax with correctly rounded fp32 division.
-__global__ __launch_bounds__(256) void amax_stage2(const uint32_t* __restrict__ part, int nparts, float fmt_max,
-                                                   float* __restrict__ rec) {
+// Max of the stage-1 partials over a 256-thread block, returned to every
+// thread (a fixed order is not needed: max is order independent).
+__device__ __forceinline__ uint32_t block_max_parts(const uint32_t* __restrict__ part, int nparts) {
   uint32_t m = 0;
   for (int i = threadIdx.x; i < nparts; i += blockDim.x) m = max(m, part[i]);
 #pragma unroll
@@ -52,14 +52,29 @@ __global__ __launch_bounds__(256) void amax_stage2(const uint32_t* __restrict__ 
   __shared__ uint32_t sh[4];
   if ((threadIdx.x & 63) == 0) sh[threadIdx.x >> 6] = m;
   __syncthreads();
+  return max(max(sh[0], sh[1]), max(sh[2], sh[3]));
+}
+
+// The scale record {amax, s, 1/s} of a bf16 magnitude bit pattern;
+// s = fmt_max / amax with correctly rounded fp32 division.
+struct Scale {
+  float amax, s, sinv;
+};
+__device__ __forceinline__ Scale scale_of(uint32_t bits, float fmt_max) {
+  const float amax = __uint_as_float(bits << 16);
+  const bool usable = amax > 0.f && amax <= 3.4028234663852886e38f;  // false for 0, inf, NaN
+  const float s = usable ? __fdiv_rn(fmt_max, amax) : 1.f;
+  return Scale{amax, s, __fdiv_rn(1.f, s)};
+}
+
+__global__ __launch_bounds__(256) void amax_stage2(const uint32_t* __restrict__ part, int nparts, float fmt_max,
+                                                   float* __restrict__ rec) {
+  const uint32_t bits = block_max_parts(part, nparts);
   if (threadIdx.x == 0) {
-    const uint32_t bits = max(max(sh[0], sh[1]), max(sh[2], sh[3]));
-    const float amax = __uint_as_float(bits << 16);
-    const bool usable = amax > 0.f && amax <= 3.4028234663852886e38f;  // false for 0, inf, NaN
-    const float s = usable ? __fdiv_rn(fmt_max, amax) : 1.f;
-    rec[0] = amax;
-    rec[1] = s;
-    rec[2] = __fdiv_rn(1.f, s);
+    const Scale sc = scale_of(bits, fmt_max);
+    rec[0] = sc.amax;
+    rec[1] = sc.s;
+    rec[2] = sc.sinv;
   }
 }
 
@@ -96,21 +111,41 @@ __device__ __forceinline__ uint32_t encode(float y) {
 // Tile of 64 rows x 64 columns per workgroup: each thread converts 16 elements
 // (two 8-element vectors), writes the row-major codes directly and stages them
 // in LDS for the transposed copy, which is written as 16 consecutive rows of one
-// column per thread.
+// column per thread.  The scale comes from rec[1], or -- with part non-null --
+// from the amax stage-1 partials, reduced by every block (its tile loads are
+// issued first), and block (0, 0) writes the record: one launch fewer.
 template <int FMT>
 __global__ __launch_bounds__(256) void cast_kernel(const uint16_t* __restrict__ x, int64_t rows, int64_t cols,
-                                                   const float* __restrict__ rec, uint8_t* __restrict__ out,
+                                                   const float* __restrict__ rec_in, const uint32_t* __restrict__ part,
+                                                   int nparts, float* __restrict__ rec_out, uint8_t* __restrict__ out,
                                                    uint8_t* __restrict__ out_t) {
   __shared__ uint8_t tile[64][64 + 4];
-  const float s = rec[1];
   const int64_t r0 = (int64_t)blockIdx.y * 64, c0 = (int64_t)blockIdx.x * 64;
   const int tr = threadIdx.x >> 3, tc = (threadIdx.x & 7) * 8;
+  u32x4 qv[2];
+#pragma unroll
+  for (int pass = 0; pass < 2; ++pass) {
+    const int64_t r = r0 + tr + pass * 32, c = c0 + tc;
+    qv[pass] = (r < rows && c < cols) ? *reinterpret_cast<const u32x4*>(x + r * cols + c) : u32x4{0, 0, 0, 0};
+  }
+  float s;
+  if (part) {
+    const Scale sc = scale_of(block_max_parts(part, nparts), FMT == 0 ? 448.f : 57344.f);
+    s = sc.s;
+    if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) {
+      rec_out[0] = sc.amax;
+      rec_out[1] = sc.s;
+      rec_out[2] = sc.sinv;
+    }
+  } else {
+    s = rec_in[1];
+  }
 #pragma unroll
   for (int pass = 0; pass < 2; ++pass) {
     const int lr = tr + pass * 32;
     const int64_t r = r0 + lr, c = c0 + tc;
     if (r < rows && c < cols) {
-      const u32x4 q = *reinterpret_cast<const u32x4*>(x + r * cols + c);
+      const u32x4 q = qv[pass];
       uint32_t w0 = 0, w1 = 0;
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
@@ -146,24 +181,50 @@ __global__ __launch_bounds__(256) void cast_kernel(const uint16_t* __restrict__ 
 
 size_t fp8_amax_ws_bytes() { return AMAX_BLOCKS * sizeof(uint32_t); }
 
-hipError_t fp8_amax(const uint16_t* x, int64_t n, int fmt, float* rec, void* ws, hipStream_t s) {
+// Stage 1 of the amax into ws; returns the number of partials written.
+static hipError_t amax_partials(const uint16_t* x, int64_t n, void* ws, hipStream_t s, int* nparts) {
   const int64_t nv = n / 8;
   const int blocks = (int)std::max<int64_t>(1, std::min<int64_t>(AMAX_BLOCKS, (nv + 1023) / 1024));
-  uint32_t* part = static_cast<uint32_t*>(ws);
-  hipLaunchKernelGGL(amax_stage1, dim3(blocks), dim3(256), 0, s, x, n, part);
-  hipError_t e = hipGetLastError();
+  hipLaunchKernelGGL(amax_stage1, dim3(blocks), dim3(256), 0, s, x, n, static_cast<uint32_t*>(ws));
+  *nparts = blocks;
+  return hipGetLastError();
+}
+
+static hipError_t launch_cast(const uint16_t* x, int64_t rows, int64_t cols, int fmt, const float* rec_in,
+                              const uint32_t* part, int nparts, float* rec_out, uint8_t* out, uint8_t* out_t,
+                              hipStream_t s) {
+  const dim3 grid((unsigned)((cols + 63) / 64), (unsigned)((rows + 63) / 64));
+  if (fmt == 0)
+    hipLaunchKernelGGL(cast_kernel<0>, grid, dim3(256), 0, s, x, rows, cols, rec_in, part, nparts, rec_out, out,
+                       out_t);
+  else
+    hipLaunchKernelGGL(cast_kernel<1>, grid, dim3(256), 0, s, x, rows, cols, rec_in, part, nparts, rec_out, out,
+                       out_t);
+  return hipGetLastError();
+}
+
+hipError_t fp8_amax(const uint16_t* x, int64_t n, int fmt, float* rec, void* ws, hipStream_t s) {
+  int nparts = 0;
+  hipError_t e = amax_partials(x, n, ws, s, &nparts);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(amax_stage2, dim3(1), dim3(256), 0, s, part, blocks, fmt == 0 ? 448.f : 57344.f, rec);
+  hipLaunchKernelGGL(amax_stage2, dim3(1), dim3(256), 0, s, static_cast<const uint32_t*>(ws), nparts,
+                     fmt == 0 ? 448.f : 57344.f, rec);
   return hipGetLastError();
 }
 
 hipError_t fp8_cast(const uint16_t* x, int64_t rows, int64_t cols, int fmt, const float* rec, uint8_t* out,
                     uint8_t* out_t, hipStream_t s) {
   if (rows <= 0 || cols <= 0 || (!out && !out_t)) return hipSuccess;
-  const dim3 grid((unsigned)((cols + 63) / 64), (unsigned)((rows + 63) / 64));
-  if (fmt == 0) hipLaunchKernelGGL(cast_kernel<0>, grid, dim3(256), 0, s, x, rows, cols, rec, out, out_t);
-  else hipLaunchKernelGGL(cast_kernel<1>, grid, dim3(256), 0, s, x, rows, cols, rec, out, out_t);
-  return hipGetLastError();
+  return launch_cast(x, rows, cols, fmt, rec, nullptr, 0, nullptr, out, out_t, s);
+}
+
+hipError_t fp8_quantize(const uint16_t* x, int64_t rows, int64_t cols, int fmt, float* rec, void* ws, uint8_t* out,
+                        uint8_t* out_t, hipStream_t s) {
+  if (rows <= 0 || cols <= 0 || (!out && !out_t)) return fp8_amax(x, rows * cols, fmt, rec, ws, s);
+  int nparts = 0;
+  hipError_t e = amax_partials(x, rows * cols, ws, s, &nparts);
+  if (e != hipSuccess) return e;
+  return launch_cast(x, rows, cols, fmt, nullptr, static_cast<const uint32_t*>(ws), nparts, rec, out, out_t, s);
 }
 
 }  // namespace mtl

@@ -117,6 +117,10 @@ hipError_t fp8_amax(const uint16_t* x, int64_t n, int fmt, float* rec, void* ws,
 // out_t is given; 16-byte aligned pointers.
 hipError_t fp8_cast(const uint16_t* x, int64_t rows, int64_t cols, int fmt, const float* rec, uint8_t* out,
                     uint8_t* out_t, hipStream_t s);
+// fp8_amax then fp8_cast (rec written too), with the amax's second stage folded
+// into the cast launch: the same record and codes in one launch fewer.
+hipError_t fp8_quantize(const uint16_t* x, int64_t rows, int64_t cols, int fmt, float* rec, void* ws, uint8_t* out,
+                        uint8_t* out_t, hipStream_t s);
 
 // ---------------------------------------------------------------- MoE data movement
 // Top-k expert ids per token (descending logit, ties to the lower id) and the

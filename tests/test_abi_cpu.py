@@ -177,3 +177,10 @@ def test_fp8_validate_and_errors_before_launch(mtl):
     assert lib.mtl_fp8_cast(P, 40, 16, 0, P, None, P, None) == mtl.MTL_E_SHAPE  # transposed needs rows % 16
     assert lib.mtl_fp8_cast(P, 64, 16, 0, P, None, None, None) == mtl.MTL_E_NULL
     assert lib.mtl_fp8_cast(P, 64, 16, 0, P, P + 8, None, None) == mtl.MTL_E_ALIGN
+    S = mtl.MTL_FP8_AMAX_SCRATCH
+    assert lib.mtl_fp8_quantize(P, 64, 16, 0, P, P, None, P, 64, None) == mtl.MTL_E_WORKSPACE
+    assert lib.mtl_fp8_quantize(P, 64, 12, 0, P, P, None, P, S, None) == mtl.MTL_E_SHAPE
+    assert lib.mtl_fp8_quantize(P, 40, 16, 0, P, None, P, P, S, None) == mtl.MTL_E_SHAPE
+    assert lib.mtl_fp8_quantize(P, 64, 16, 0, P, None, None, P, S, None) == mtl.MTL_E_NULL
+    assert lib.mtl_fp8_quantize(P, 64, 16, 0, P, P, None, None, S, None) == mtl.MTL_E_NULL
+    assert lib.mtl_fp8_quantize(P, 64, 16, 3, P, P, None, P, S, None) == mtl.MTL_E_UNSUPPORTED

@@ -1,6 +1,7 @@
 """fp8 path on the GPU.
 
-* amax and the scaled cast (E4M3 / E5M2) are bit-exact against the oracle:
+* amax and the scaled cast (E4M3 / E5M2), separately and as the one-call
+  quantisation, are bit-exact against the oracle:
   the scale record {amax, s, 1/s} and every code, on tensors that reach every
   code point and every rounding tie (all bf16 values within the format's range
   at scale 1), on Gaussian tensors (s not a power of two), on zeros, and on
@@ -81,6 +82,14 @@ def test_amax_and_cast_bit_exact(mtl, case):
     got = out.cpu().numpy()
     assert np.array_equal(got.reshape(-1), codes), np.flatnonzero(got.reshape(-1) != codes)[:10]
     assert np.array_equal(out_t.cpu().numpy(), got.T)
+    # the one-call quantisation (the cast finishing the amax) gives the same bits
+    rec2 = torch.zeros(4, dtype=torch.float32, device="cuda")
+    out2 = torch.empty_like(out)
+    out2_t = torch.empty_like(out_t)
+    mtl.mtl_fp8_quantize(x, rows, cols, fmt, rec2, out2, out2_t, ws)
+    torch.cuda.synchronize()
+    assert rec2.cpu().numpy()[:3].tobytes() == got_rec[:3].tobytes()
+    assert torch.equal(out2, out) and torch.equal(out2_t, out_t)
 
 
 FP8_CASES = {
