@@ -5,6 +5,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <initializer_list>
 
 #include "kernels.hpp"
 
@@ -99,8 +100,20 @@ Q8 q8(Bump& b, int64_t rows, int64_t cols, int fmt, bool normal, bool trans) {
 }
 constexpr int E4M3 = 0, E5M2 = 1;
 
-hipError_t quantize(const void* x, const Q8& q, void* amax_ws, hipStream_t s) {
-  return fp8_quantize(static_cast<const uint16_t*>(x), q.rows, q.cols, q.fmt, q.rec, amax_ws, q.q, q.qt, s);
+// Quantise 1..3 bf16 tensors (x, its Q8) in one amax launch and one cast launch.
+struct QIn {
+  const void* x;
+  const Q8* q;
+};
+hipError_t quantize(std::initializer_list<QIn> in, void* amax_ws, hipStream_t s) {
+  QuantJob jobs[3];
+  int n = 0;
+  for (const QIn& e : in) {
+    if (n == 3) return hipErrorInvalidValue;
+    jobs[n++] = QuantJob{static_cast<const uint16_t*>(e.x), e.q->rows, e.q->cols, e.q->fmt, e.q->rec, e.q->q,
+                         e.q->qt};
+  }
+  return fp8_quantize_n(jobs, n, amax_ws, s);
 }
 
 // fp8 GEMM C[M, N] = A . B^T over K, both operands k-contiguous codes.
@@ -289,8 +302,7 @@ mtl_status mtl_attn_fwd(const mtl_layer_cfg* c, const void* x, const void* w_qkv
 
   // qkv = x . w_qkv + b_qkv
   if (is_fp8(c)) {
-    MTL_TRY(quantize(x, ws.x, ws.amax_ws, s));
-    MTL_TRY(quantize(w_qkv, ws.wqkv_t, ws.amax_ws, s));
+    MTL_TRY(quantize({{x, &ws.x}, {w_qkv, &ws.wqkv_t}, {w_o, &ws.wo_t}}, ws.amax_ws, s));
     MTL_TRY(gemm8(ws.x, ws.x.q, ws.wqkv_t, ws.wqkv_t.qt, d.S, d.qkv_l, d.h, qkv, d.qkv_l, EPI_BF16_BIAS, s, b_qkv));
   } else {
     GemmArgs g = gemm(x, d.h, w_qkv, d.qkv_l, d.S, d.qkv_l, d.h, qkv, d.qkv_l);
@@ -313,8 +325,7 @@ mtl_status mtl_attn_fwd(const mtl_layer_cfg* c, const void* x, const void* w_qkv
 
   // partial = o . w_o
   if (is_fp8(c)) {
-    MTL_TRY(quantize(o, ws.o, ws.amax_ws, s));
-    MTL_TRY(quantize(w_o, ws.wo_t, ws.amax_ws, s));
+    MTL_TRY(quantize({{o, &ws.o}}, ws.amax_ws, s));
     MTL_TRY(gemm8(ws.o, ws.o.q, ws.wo_t, ws.wo_t.qt, d.S, d.h, d.o_l, partial, d.h, EPI_BF16, s));
   } else {
     GemmArgs g = gemm(o, d.o_l, w_o, d.h, d.S, d.h, d.o_l, partial, d.h);
@@ -356,11 +367,9 @@ mtl_status mtl_mlp_fwd(const mtl_layer_cfg* c, const void* h, const void* w1, co
 
   if (is_fp8(c)) {
     // z = h . w1 + b1, a = GeLU(z); partial = a . w2 (a re-quantised from bf16)
-    MTL_TRY(quantize(h, ws.h, ws.amax_ws, s));
-    MTL_TRY(quantize(w1, ws.w1_t, ws.amax_ws, s));
+    MTL_TRY(quantize({{h, &ws.h}, {w1, &ws.w1_t}, {w2, &ws.w2_t}}, ws.amax_ws, s));
     MTL_TRY(gemm8(ws.h, ws.h.q, ws.w1_t, ws.w1_t.qt, d.S, d.f_l, d.h, z, d.f_l, EPI_BIAS_GELU, s, b1, a));
-    MTL_TRY(quantize(a, ws.a, ws.amax_ws, s));
-    MTL_TRY(quantize(w2, ws.w2_t, ws.amax_ws, s));
+    MTL_TRY(quantize({{a, &ws.a}}, ws.amax_ws, s));
     MTL_TRY(gemm8(ws.a, ws.a.q, ws.w2_t, ws.w2_t.qt, d.S, d.h, d.f_l, partial, d.h, EPI_BF16, s));
     return MTL_OK;
   }
@@ -405,16 +414,12 @@ mtl_status mtl_mlp_bwd(const mtl_layer_cfg* c, const void* dy, const void* h, co
 
   if (is_fp8(c)) {
     // E5M2 gradients, E4M3 activations and weights; wgrad operands transposed
-    MTL_TRY(quantize(dy, ws.dy, ws.amax_ws, s));
-    MTL_TRY(quantize(w2, ws.w2, ws.amax_ws, s));
+    MTL_TRY(quantize({{dy, &ws.dy}, {w2, &ws.w2}, {a, &ws.a_t}}, ws.amax_ws, s));
     MTL_TRY(gemm8(ws.dy, ws.dy.q, ws.w2, ws.w2.q, d.S, d.f_l, d.h, ws.dz, d.f_l, EPI_DGELU, s, nullptr, nullptr, z));
-    MTL_TRY(quantize(a, ws.a_t, ws.amax_ws, s));
     MTL_TRY(gemm8(ws.a_t, ws.a_t.qt, ws.dy, ws.dy.qt, d.f_l, d.h, d.S, dw2, d.h, wepi, s));
-    MTL_TRY(quantize(ws.dz, ws.dz8, ws.amax_ws, s));
-    MTL_TRY(quantize(h, ws.h_t, ws.amax_ws, s));
+    MTL_TRY(quantize({{ws.dz, &ws.dz8}, {h, &ws.h_t}, {w1, &ws.w1}}, ws.amax_ws, s));
     MTL_TRY(gemm8(ws.h_t, ws.h_t.qt, ws.dz8, ws.dz8.qt, d.h, d.f_l, d.S, dw1, d.f_l, wepi, s));
     MTL_TRY(mlp_bias_grads(d, ws, dy, db1, db2, accum, s));
-    MTL_TRY(quantize(w1, ws.w1, ws.amax_ws, s));
     MTL_TRY(gemm8(ws.dz8, ws.dz8.q, ws.w1, ws.w1.q, d.S, d.h, d.f_l, dh_partial, d.h, EPI_BF16, s));
     return MTL_OK;
   }
@@ -453,10 +458,8 @@ mtl_status mtl_attn_bwd(const mtl_layer_cfg* c, const void* dh, const void* x, c
 
   if (f8) {
     // do = dh . w_o^T ; dw_o = o^T . dh
-    MTL_TRY(quantize(dh, ws.dh, ws.amax_ws, s));
-    MTL_TRY(quantize(w_o, ws.wo, ws.amax_ws, s));
+    MTL_TRY(quantize({{dh, &ws.dh}, {w_o, &ws.wo}, {o, &ws.o_t}}, ws.amax_ws, s));
     MTL_TRY(gemm8(ws.dh, ws.dh.q, ws.wo, ws.wo.q, d.S, d.o_l, d.h, ws.dout, d.o_l, EPI_BF16, s));
-    MTL_TRY(quantize(o, ws.o_t, ws.amax_ws, s));
     MTL_TRY(gemm8(ws.o_t, ws.o_t.qt, ws.dh, ws.dh.qt, d.o_l, d.h, d.S, dw_o, d.h, wepi, s));
   } else {
     // dw_o = o^T . dh and do = dh . w_o^T, one launch (wgrad tiles first)
@@ -483,11 +486,9 @@ mtl_status mtl_attn_bwd(const mtl_layer_cfg* c, const void* dh, const void* x, c
 
   if (f8) {
     // dw_qkv = x^T . dqkv ; dx_partial = dqkv . w_qkv^T
-    MTL_TRY(quantize(ws.dqkv, ws.dqkv8, ws.amax_ws, s));
-    MTL_TRY(quantize(x, ws.x_t, ws.amax_ws, s));
+    MTL_TRY(quantize({{ws.dqkv, &ws.dqkv8}, {x, &ws.x_t}, {w_qkv, &ws.wqkv}}, ws.amax_ws, s));
     MTL_TRY(gemm8(ws.x_t, ws.x_t.qt, ws.dqkv8, ws.dqkv8.qt, d.h, d.qkv_l, d.S, dw_qkv, d.qkv_l, wepi, s));
     MTL_TRY(attn_bias_grads(d, ws, dh, db_qkv, db_o, accum, s));
-    MTL_TRY(quantize(w_qkv, ws.wqkv, ws.amax_ws, s));
     MTL_TRY(gemm8(ws.dqkv8, ws.dqkv8.q, ws.wqkv, ws.wqkv.q, d.S, d.h, d.qkv_l, dx_partial, d.h, EPI_BF16, s));
     return MTL_OK;
   }
@@ -534,9 +535,9 @@ mtl_status mtl_fp8_quantize(const void* x, int64_t rows, int64_t cols, int32_t f
   if (rows <= 0 || cols <= 0 || cols % 8 != 0 || (out_t && rows % 16 != 0)) return MTL_E_SHAPE;
   if (format != MTL_FP8_E4M3 && format != MTL_FP8_E5M2) return MTL_E_UNSUPPORTED;
   if (scratch_bytes < fp8_amax_ws_bytes()) return MTL_E_WORKSPACE;
-  return hip_status(fp8_quantize(static_cast<const uint16_t*>(x), rows, cols, format, rec, scratch,
-                                 static_cast<uint8_t*>(out), static_cast<uint8_t*>(out_t),
-                                 reinterpret_cast<hipStream_t>(stream)));
+  const QuantJob job{static_cast<const uint16_t*>(x), rows, cols, format, rec, static_cast<uint8_t*>(out),
+                     static_cast<uint8_t*>(out_t)};
+  return hip_status(fp8_quantize_n(&job, 1, scratch, reinterpret_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

@@ -42,6 +42,57 @@ __global__ __launch_bounds__(256) void amax_stage1(const uint16_t* __restrict__ 
   if (threadIdx.x == 0) part[blockIdx.x] = max(max(sh[0], sh[1]), max(sh[2], sh[3]));
 }
 
+// Stage 1 of up to QMAX tensors in one launch: blocks [first[j], first[j+1])
+// take tensor j (grid-stride over its 8-element vectors) and write its partials.
+constexpr int QMAX = 3;
+constexpr int QBLOCKS = 256;  // stage-1 blocks per tensor of a multi-tensor launch
+struct QuantArgs {
+  const uint16_t* x[QMAX];
+  int64_t rows[QMAX], cols[QMAX];
+  int fmt[QMAX];
+  float* rec[QMAX];
+  uint8_t* out[QMAX];
+  uint8_t* out_t[QMAX];
+  uint32_t* part[QMAX];
+  int nparts[QMAX];
+  int first1[QMAX + 1];  // stage-1 block ranges
+  int first2[QMAX + 1];  // cast block ranges
+  int tiles_x[QMAX];
+  int n;
+};
+
+__device__ __forceinline__ int job_of(const int* first, int n, int b) {
+  int j = 0;
+  while (j + 1 < n && b >= first[j + 1]) ++j;
+  return j;
+}
+
+__global__ __launch_bounds__(256) void amax_stage1_multi(QuantArgs a) {
+  const int j = job_of(a.first1, a.n, (int)blockIdx.x);
+  const int lb = (int)blockIdx.x - a.first1[j], nb = a.first1[j + 1] - a.first1[j];
+  const uint16_t* x = a.x[j];
+  const int64_t n = a.rows[j] * a.cols[j];
+  uint32_t m = 0;
+  const int64_t nv = n / 8;
+  const int64_t stride = (int64_t)nb * blockDim.x;
+  for (int64_t v = (int64_t)lb * blockDim.x + threadIdx.x; v < nv; v += stride) {
+    const u32x4 q = *reinterpret_cast<const u32x4*>(x + v * 8);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      m = max(m, q[k] & 0x7fffu);
+      m = max(m, (q[k] >> 16) & 0x7fffu);
+    }
+  }
+  if (lb == 0)
+    for (int64_t i = nv * 8 + threadIdx.x; i < n; i += blockDim.x) m = max(m, (uint32_t)(x[i] & 0x7fffu));
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, off));
+  __shared__ uint32_t sh[4];
+  if ((threadIdx.x & 63) == 0) sh[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) a.part[j][lb] = max(max(sh[0], sh[1]), max(sh[2], sh[3]));
+}
+
 // Max of the stage-1 partials over a 256-thread block, returned to every
 // thread (a fixed order is not needed: max is order independent).
 __device__ __forceinline__ uint32_t block_max_parts(const uint32_t* __restrict__ part, int nparts) {
@@ -115,12 +166,12 @@ __device__ __forceinline__ uint32_t encode(float y) {
 // from the amax stage-1 partials, reduced by every block (its tile loads are
 // issued first), and block (0, 0) writes the record: one launch fewer.
 template <int FMT>
-__global__ __launch_bounds__(256) void cast_kernel(const uint16_t* __restrict__ x, int64_t rows, int64_t cols,
-                                                   const float* __restrict__ rec_in, const uint32_t* __restrict__ part,
-                                                   int nparts, float* __restrict__ rec_out, uint8_t* __restrict__ out,
-                                                   uint8_t* __restrict__ out_t) {
+__device__ __forceinline__ void cast_tile(const uint16_t* __restrict__ x, int64_t rows, int64_t cols,
+                                          const float* __restrict__ rec_in, const uint32_t* __restrict__ part,
+                                          int nparts, float* __restrict__ rec_out, uint8_t* __restrict__ out,
+                                          uint8_t* __restrict__ out_t, int bx, int by) {
   __shared__ uint8_t tile[64][64 + 4];
-  const int64_t r0 = (int64_t)blockIdx.y * 64, c0 = (int64_t)blockIdx.x * 64;
+  const int64_t r0 = (int64_t)by * 64, c0 = (int64_t)bx * 64;
   const int tr = threadIdx.x >> 3, tc = (threadIdx.x & 7) * 8;
   u32x4 qv[2];
 #pragma unroll
@@ -132,7 +183,7 @@ __global__ __launch_bounds__(256) void cast_kernel(const uint16_t* __restrict__ 
   if (part) {
     const Scale sc = scale_of(block_max_parts(part, nparts), FMT == 0 ? 448.f : 57344.f);
     s = sc.s;
-    if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) {
+    if (bx == 0 && by == 0 && threadIdx.x == 0) {
       rec_out[0] = sc.amax;
       rec_out[1] = sc.s;
       rec_out[2] = sc.sinv;
@@ -177,54 +228,82 @@ __global__ __launch_bounds__(256) void cast_kernel(const uint16_t* __restrict__ 
   }
 }
 
+template <int FMT>
+__global__ __launch_bounds__(256) void cast_kernel(const uint16_t* __restrict__ x, int64_t rows, int64_t cols,
+                                                   const float* __restrict__ rec, uint8_t* __restrict__ out,
+                                                   uint8_t* __restrict__ out_t) {
+  cast_tile<FMT>(x, rows, cols, rec, nullptr, 0, nullptr, out, out_t, blockIdx.x, blockIdx.y);
+}
+
+// The casts of up to QMAX tensors (each finishing its own amax) in one launch.
+__global__ __launch_bounds__(256) void cast_multi_kernel(QuantArgs a) {
+  const int j = job_of(a.first2, a.n, (int)blockIdx.x);
+  const int t = (int)blockIdx.x - a.first2[j];
+  const int bx = t % a.tiles_x[j], by = t / a.tiles_x[j];
+  if (a.fmt[j] == 0)
+    cast_tile<0>(a.x[j], a.rows[j], a.cols[j], nullptr, a.part[j], a.nparts[j], a.rec[j], a.out[j], a.out_t[j], bx,
+                 by);
+  else
+    cast_tile<1>(a.x[j], a.rows[j], a.cols[j], nullptr, a.part[j], a.nparts[j], a.rec[j], a.out[j], a.out_t[j], bx,
+                 by);
+}
+
 }  // namespace
 
 size_t fp8_amax_ws_bytes() { return AMAX_BLOCKS * sizeof(uint32_t); }
 
-// Stage 1 of the amax into ws; returns the number of partials written.
-static hipError_t amax_partials(const uint16_t* x, int64_t n, void* ws, hipStream_t s, int* nparts) {
+hipError_t fp8_amax(const uint16_t* x, int64_t n, int fmt, float* rec, void* ws, hipStream_t s) {
   const int64_t nv = n / 8;
   const int blocks = (int)std::max<int64_t>(1, std::min<int64_t>(AMAX_BLOCKS, (nv + 1023) / 1024));
-  hipLaunchKernelGGL(amax_stage1, dim3(blocks), dim3(256), 0, s, x, n, static_cast<uint32_t*>(ws));
-  *nparts = blocks;
-  return hipGetLastError();
-}
-
-static hipError_t launch_cast(const uint16_t* x, int64_t rows, int64_t cols, int fmt, const float* rec_in,
-                              const uint32_t* part, int nparts, float* rec_out, uint8_t* out, uint8_t* out_t,
-                              hipStream_t s) {
-  const dim3 grid((unsigned)((cols + 63) / 64), (unsigned)((rows + 63) / 64));
-  if (fmt == 0)
-    hipLaunchKernelGGL(cast_kernel<0>, grid, dim3(256), 0, s, x, rows, cols, rec_in, part, nparts, rec_out, out,
-                       out_t);
-  else
-    hipLaunchKernelGGL(cast_kernel<1>, grid, dim3(256), 0, s, x, rows, cols, rec_in, part, nparts, rec_out, out,
-                       out_t);
-  return hipGetLastError();
-}
-
-hipError_t fp8_amax(const uint16_t* x, int64_t n, int fmt, float* rec, void* ws, hipStream_t s) {
-  int nparts = 0;
-  hipError_t e = amax_partials(x, n, ws, s, &nparts);
+  uint32_t* part = static_cast<uint32_t*>(ws);
+  hipLaunchKernelGGL(amax_stage1, dim3(blocks), dim3(256), 0, s, x, n, part);
+  hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(amax_stage2, dim3(1), dim3(256), 0, s, static_cast<const uint32_t*>(ws), nparts,
-                     fmt == 0 ? 448.f : 57344.f, rec);
+  hipLaunchKernelGGL(amax_stage2, dim3(1), dim3(256), 0, s, part, blocks, fmt == 0 ? 448.f : 57344.f, rec);
   return hipGetLastError();
 }
 
 hipError_t fp8_cast(const uint16_t* x, int64_t rows, int64_t cols, int fmt, const float* rec, uint8_t* out,
                     uint8_t* out_t, hipStream_t s) {
   if (rows <= 0 || cols <= 0 || (!out && !out_t)) return hipSuccess;
-  return launch_cast(x, rows, cols, fmt, rec, nullptr, 0, nullptr, out, out_t, s);
+  const dim3 grid((unsigned)((cols + 63) / 64), (unsigned)((rows + 63) / 64));
+  if (fmt == 0) hipLaunchKernelGGL(cast_kernel<0>, grid, dim3(256), 0, s, x, rows, cols, rec, out, out_t);
+  else hipLaunchKernelGGL(cast_kernel<1>, grid, dim3(256), 0, s, x, rows, cols, rec, out, out_t);
+  return hipGetLastError();
 }
 
-hipError_t fp8_quantize(const uint16_t* x, int64_t rows, int64_t cols, int fmt, float* rec, void* ws, uint8_t* out,
-                        uint8_t* out_t, hipStream_t s) {
-  if (rows <= 0 || cols <= 0 || (!out && !out_t)) return fp8_amax(x, rows * cols, fmt, rec, ws, s);
-  int nparts = 0;
-  hipError_t e = amax_partials(x, rows * cols, ws, s, &nparts);
+hipError_t fp8_quantize_n(const QuantJob* jobs, int n, void* ws, hipStream_t s) {
+  if (n < 1 || n > QMAX) return hipErrorInvalidValue;
+  QuantArgs a{};
+  a.n = n;
+  int b1 = 0, b2 = 0;
+  for (int j = 0; j < n; ++j) {
+    const QuantJob& q = jobs[j];
+    if (q.rows <= 0 || q.cols <= 0 || (!q.out && !q.out_t)) return hipErrorInvalidValue;
+    a.x[j] = q.x;
+    a.rows[j] = q.rows;
+    a.cols[j] = q.cols;
+    a.fmt[j] = q.fmt;
+    a.rec[j] = q.rec;
+    a.out[j] = q.out;
+    a.out_t[j] = q.out_t;
+    a.part[j] = static_cast<uint32_t*>(ws) + j * QBLOCKS;
+    const int64_t nv = q.rows * q.cols / 8;
+    const int nb = (int)std::max<int64_t>(1, std::min<int64_t>(QBLOCKS, (nv + 1023) / 1024));
+    a.nparts[j] = nb;
+    a.first1[j] = b1;
+    b1 += nb;
+    a.tiles_x[j] = (int)((q.cols + 63) / 64);
+    a.first2[j] = b2;
+    b2 += a.tiles_x[j] * (int)((q.rows + 63) / 64);
+  }
+  a.first1[n] = b1;
+  a.first2[n] = b2;
+  hipLaunchKernelGGL(amax_stage1_multi, dim3((unsigned)b1), dim3(256), 0, s, a);
+  hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  return launch_cast(x, rows, cols, fmt, nullptr, static_cast<const uint32_t*>(ws), nparts, rec, out, out_t, s);
+  hipLaunchKernelGGL(cast_multi_kernel, dim3((unsigned)b2), dim3(256), 0, s, a);
+  return hipGetLastError();
 }
 
 }  // namespace mtl

@@ -117,10 +117,20 @@ hipError_t fp8_amax(const uint16_t* x, int64_t n, int fmt, float* rec, void* ws,
 // out_t is given; 16-byte aligned pointers.
 hipError_t fp8_cast(const uint16_t* x, int64_t rows, int64_t cols, int fmt, const float* rec, uint8_t* out,
                     uint8_t* out_t, hipStream_t s);
-// fp8_amax then fp8_cast (rec written too), with the amax's second stage folded
-// into the cast launch: the same record and codes in one launch fewer.
-hipError_t fp8_quantize(const uint16_t* x, int64_t rows, int64_t cols, int fmt, float* rec, void* ws, uint8_t* out,
-                        uint8_t* out_t, hipStream_t s);
+// fp8_amax then fp8_cast (rec written too) of 1..3 tensors in two launches:
+// stage 1 of every amax, then every cast, each cast block finishing its
+// tensor's amax from the stage-1 partials.  Each tensor's record and codes are
+// those of fp8_amax + fp8_cast on it alone.  ws holds fp8_amax_ws_bytes().
+// Same shape rules as fp8_cast.
+struct QuantJob {
+  const uint16_t* x;
+  int64_t rows, cols;
+  int fmt;
+  float* rec;
+  uint8_t* out;
+  uint8_t* out_t;
+};
+hipError_t fp8_quantize_n(const QuantJob* jobs, int n, void* ws, hipStream_t s);
 
 // ---------------------------------------------------------------- MoE data movement
 // Top-k expert ids per token (descending logit, ties to the lower id) and the
