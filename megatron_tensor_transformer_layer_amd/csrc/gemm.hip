@@ -9,10 +9,21 @@
 // Design (CDNA4):
 //  * 256 threads = 4 wave64s in a 2x2 grid, a BM x BN tile per workgroup, K in
 //    slabs of 64, v_mfma_f32_32x32x16_bf16.
-//  * Global -> LDS with global_load_lds_dwordx4: every wave instruction fills
-//    1 KB of LDS directly (no VGPR staging, no VALU).  Two LDS stages, each a
-//    separate LDS object so the compiler knows a DMA into one never aliases a
-//    read of the other; the slab kt+1 streams in while slab kt is multiplied.
+//  * bf16: global -> VGPR -> LDS, two slabs ahead.  While slab kt is
+//    multiplied from one LDS stage, slab kt+1 is written from registers into
+//    the other stage (ds_write_b128, interleaved with the MFMAs) and each
+//    register is reloaded with its chunk of slab kt+2 right behind its write,
+//    so a load has a whole slab of MFMAs to land.  The two stage pointers are
+//    passed __restrict__, which lets the scheduler interleave the writes of one
+//    stage with the fragment reads of the other.  (LDS DMA of the same slabs,
+//    one slab ahead, measured 4-8% slower: the DMA stream and the MFMAs
+//    overlapped poorly.)
+//  * fp8: global -> LDS with buffer_load_dwordx4 ... lds: every wave
+//    instruction fills 1 KB of LDS directly.  Two LDS stages, each a separate
+//    LDS object so the compiler knows a DMA into one never aliases a read of
+//    the other; slab kt+1 streams in while slab kt is multiplied.
+//  * Both paths address a chunk by the same per-lane byte offset, computed once
+//    per tile; a slab adds its uniform k offset.
 //  * A k-contiguous operand is kept as [rows][64] with its 16-byte chunks XOR
 //    swizzled by row; fragments are one ds_read_b128 per lane.
 //  * An mn-contiguous operand is kept in its global layout [64][rows] (64-byte
@@ -27,9 +38,10 @@
 //    stores 8 or 16 bytes per lane.
 //  * Tile order is XCD-aware: the 8 XCDs each take a contiguous run of tiles
 //    (grouped 4 tile-rows at a time) so A/B panels are reused inside one L2.
-//  * Tails: rows/columns past M or N load a clamped in-bounds row (those
-//    outputs are never stored); k past K loads a clamped address and the slab
-//    is zero-filled in LDS before use.
+//  * Tails: raw buffer range checks return zeros past an operand's last row;
+//    rows/columns past M or N are never stored; chunks past K of a partial last
+//    slab (which hold the next row's values in the k-contiguous layout) are
+//    zero-filled in LDS before use.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -101,6 +113,18 @@ struct Operand {
 #pragma unroll
     for (int q = 0; q < PER_WAVE; ++q)
       dma16(rs, voff[q] + kb, 0u, (uint32_t)(uintptr_t)(lds + (wave * PER_WAVE + q) * 1024));
+  }
+
+  // Register-staged path: the same per-lane offsets and LDS positions as the DMA.
+  static __device__ __forceinline__ void gload(__amdgpu_buffer_rsrc_t rs, const uint32_t (&voff)[PER_WAVE],
+                                               uint32_t kb, u32x4 (&reg)[PER_WAVE]) {
+#pragma unroll
+    for (int q = 0; q < PER_WAVE; ++q)
+      reg[q] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, (int)(voff[q] + kb), 0, 0));
+  }
+  static __device__ __forceinline__ void lwrite(const u32x4& v, int q, LDS_AS char* lds) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    *reinterpret_cast<LDS_AS u32x4*>(lds + (wave * PER_WAVE + q) * 1024 + lane * 16) = v;
   }
 
   // k-contiguous operand of a slab with kvalid < KSLAB valid k (after its DMA has
@@ -181,6 +205,78 @@ struct Mainloop {
       OB::zero_tail(st + OA::BYTES, kvalid);
     }
   }
+  // Register staging: slab data in flight / waiting to be written to LDS.
+  struct Stg {
+    u32x4 a[OA::PER_WAVE], b[OB::PER_WAVE];
+  };
+  static __device__ __forceinline__ void gload(__amdgpu_buffer_rsrc_t ra, __amdgpu_buffer_rsrc_t rb, const GemmArgs& p,
+                                               const Dma& d, int k0, Stg& g) {
+    OA::gload(ra, d.a, OA::slab_bytes(p.lda, k0), g.a);
+    OB::gload(rb, d.b, OB::slab_bytes(p.ldb, k0), g.b);
+  }
+  static __device__ __forceinline__ void lwrite_all(const Stg& g, LDS_AS char* st) {
+#pragma unroll
+    for (int q = 0; q < OA::PER_WAVE; ++q) OA::lwrite(g.a[q], q, st);
+#pragma unroll
+    for (int q = 0; q < OB::PER_WAVE; ++q) OB::lwrite(g.b[q], q, st + OA::BYTES);
+  }
+  // compute(st) while writing the staged slab into wst and loading slab k1 into
+  // the staging registers, chunk by chunk behind each write.
+  static __device__ __forceinline__ void compute_vs(const LDS_AS char* __restrict__ st, int wm, int wn, int lane,
+                                                    f32x16 (&acc)[TM][TN], Stg& g, LDS_AS char* __restrict__ wst,
+                                                    __amdgpu_buffer_rsrc_t ra, __amdgpu_buffer_rsrc_t rb,
+                                                    const GemmArgs& p, const Dma& d, int k1) {
+    constexpr int NA = OA::PER_WAVE, NB = OB::PER_WAVE, NC = NA + NB;
+    const uint32_t kba = OA::slab_bytes(p.lda, k1), kbb = OB::slab_bytes(p.ldb, k1);
+    const LDS_AS char* sa = st;
+    const LDS_AS char* sb = st + OA::BYTES;
+    u32x4 fa[2][TM], fb[2][TN];
+#pragma unroll
+    for (int i = 0; i < TM; ++i) fa[0][i] = OA::frag(sa, wm * TM + i, 0, lane);
+#pragma unroll
+    for (int j = 0; j < TN; ++j) fb[0][j] = OB::frag(sb, wn * TN + j, 0, lane);
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      const int cur = kk & 1, nxt = cur ^ 1;
+      if (kk < 3) {
+#pragma unroll
+        for (int i = 0; i < TM; ++i) fa[nxt][i] = OA::frag(sa, wm * TM + i, kk + 1, lane);
+#pragma unroll
+        for (int j = 0; j < TN; ++j) fb[nxt][j] = OB::frag(sb, wn * TN + j, kk + 1, lane);
+      }
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j) acc[i][j] = mfma32(fb[cur][j], fa[cur][i], acc[i][j]);
+      // this step's share of the staged chunks: write, then reload for slab k1
+#pragma unroll
+      for (int c = kk * NC / 4; c < (kk + 1) * NC / 4; ++c) {
+        if (c < NA) {
+          OA::lwrite(g.a[c], c, wst);
+          g.a[c] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(ra, (int)(d.a[c] + kba), 0, 0));
+        } else {
+          OB::lwrite(g.b[c - NA], c - NA, wst + OA::BYTES);
+          g.b[c - NA] =
+              __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rb, (int)(d.b[c - NA] + kbb), 0, 0));
+        }
+      }
+    }
+    constexpr int NR = TM * (OA::READS) + TN * (OB::READS);  // LDS reads per step
+    constexpr int NM = TM * TN;                               // MFMAs per step
+    constexpr int NW = NC / 4;                                // LDS writes (and loads) per step
+    __builtin_amdgcn_sched_group_barrier(0x100, NR, 0);
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+#pragma unroll
+      for (int x = 0; x < NM; ++x) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        if (kk < 3 && x < NR) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        if (x >= 2 && x < 2 + NW) __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
+        if (x >= 2 + NW && x < 2 + 2 * NW) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+      }
+    }
+  }
+
   static __device__ __forceinline__ void compute(const LDS_AS char* st, int wm, int wn, int lane,
                                                  f32x16 (&acc)[TM][TN]) {
     if constexpr (F8 != 0) {
@@ -340,6 +436,37 @@ __device__ __forceinline__ void gemm_tile(GemmArgs p, const int bid, LDS_AS char
   typename ML::Dma dma;
   ML::OA::offsets(p.lda, m0, dma.a);
   ML::OB::offsets(p.ldb, n0, dma.b);
+  if constexpr (F8 == 0) {
+    // slab 0 to LDS now; slab 1 in the staging registers; while slab kt is
+    // multiplied, slab kt+1 is written from the registers to the other stage and
+    // slab kt+2 loaded behind it (slabs past K load in-range rows or zeros and
+    // are never read)
+    const __amdgpu_buffer_rsrc_t va = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t*>(p.a), 0, (int)((A_K ? (int64_t)p.M : (int64_t)p.K) * p.lda * EB), 0x00020000);
+    const __amdgpu_buffer_rsrc_t vb = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t*>(p.b), 0, (int)((B_K ? (int64_t)p.N : (int64_t)p.K) * p.ldb * EB), 0x00020000);
+    typename ML::Stg stg;
+    ML::gload(va, vb, p, dma, 0, stg);
+    ML::lwrite_all(stg, st0);
+    ML::gload(va, vb, p, dma, KSLAB, stg);
+    if (p.K < KSLAB) {  // each thread clears the k tail of the chunks it wrote
+      ML::OA::zero_tail(st0, p.K);
+      ML::OB::zero_tail(st0 + ML::OA::BYTES, p.K);
+    }
+    __syncthreads();
+    for (int kt = 0; kt < nk; ++kt) {
+      const bool odd = kt & 1;
+      const LDS_AS char* st = odd ? st1 : st0;
+      LDS_AS char* wst = odd ? st0 : st1;
+      ML::compute_vs(st, wm, wn, lane, acc, stg, wst, va, vb, p, dma, (kt + 2) * KSLAB);
+      const int kv = p.K - (kt + 1) * KSLAB;
+      if (kv > 0 && kv < KSLAB) {
+        ML::OA::zero_tail(wst, kv);
+        ML::OB::zero_tail(wst + ML::OA::BYTES, kv);
+      }
+      __syncthreads();
+    }
+  } else {
   ML::issue(p, ra, rb, dma, 0, st0);
   ML::settle(p, 0, st0);
   __syncthreads();
@@ -358,6 +485,7 @@ __device__ __forceinline__ void gemm_tile(GemmArgs p, const int bid, LDS_AS char
     __syncthreads();
   }
   if (kt < nk) ML::compute(st0, wm, wn, lane, acc);
+  }
   const int lrow = lane & 31, lgrp = lane >> 5;
 
   // ---- epilogue ----------------------------------------------------------
