@@ -9,21 +9,17 @@
 // Design (CDNA4):
 //  * 256 threads = 4 wave64s in a 2x2 grid, a BM x BN tile per workgroup, K in
 //    slabs of 64, v_mfma_f32_32x32x16_bf16.
-//  * bf16: global -> VGPR -> LDS, two slabs ahead.  While slab kt is
-//    multiplied from one LDS stage, slab kt+1 is written from registers into
-//    the other stage (ds_write_b128, interleaved with the MFMAs) and each
-//    register is reloaded with its chunk of slab kt+2 right behind its write,
-//    so a load has a whole slab of MFMAs to land.  The two stage pointers are
-//    passed __restrict__, which lets the scheduler interleave the writes of one
-//    stage with the fragment reads of the other.  (LDS DMA of the same slabs,
-//    one slab ahead, measured 4-8% slower: the DMA stream and the MFMAs
-//    overlapped poorly.)
-//  * fp8: global -> LDS with buffer_load_dwordx4 ... lds: every wave
-//    instruction fills 1 KB of LDS directly.  Two LDS stages, each a separate
-//    LDS object so the compiler knows a DMA into one never aliases a read of
-//    the other; slab kt+1 streams in while slab kt is multiplied.
-//  * Both paths address a chunk by the same per-lane byte offset, computed once
-//    per tile; a slab adds its uniform k offset.
+//  * Global -> VGPR -> LDS, two slabs ahead, in two LDS stages.  While slab kt
+//    is multiplied from one stage, slab kt+1 is written from registers into
+//    the other (ds_write_b128, interleaved with the MFMAs) and each register is
+//    reloaded with its chunk of slab kt+2 right behind its write, so a load has
+//    a whole slab of MFMAs to land.  The two stage pointers are passed
+//    __restrict__, which lets the scheduler interleave the writes of one stage
+//    with the fragment reads of the other.  (LDS DMA of the same slabs, one
+//    slab ahead, measured 4-15% slower: the DMA stream and the MFMAs overlapped
+//    poorly.)
+//  * A lane's chunk offsets are computed once per tile; a slab adds its
+//    uniform k offset.
 //  * A k-contiguous operand is kept as [rows][64] with its 16-byte chunks XOR
 //    swizzled by row; fragments are one ds_read_b128 per lane.
 //  * An mn-contiguous operand is kept in its global layout [64][rows] (64-byte
@@ -75,8 +71,8 @@ struct Operand {
   static constexpr int ROWB = ROWS * 2;        // row bytes of the mn-contiguous layout
   static constexpr int READS = (KC && EB == 2) ? 1 : 2;  // LDS read instructions per fragment
 
-  // DMA of slab [k0, k0+KSLAB) of rows [row0, row0+ROWS) into lds (ld, k0 in
-  // elements).  Wave instruction I of the slab:
+  // Slab [k0, k0+KSLAB) of rows [row0, row0+ROWS) (ld, k0 in elements) moves
+  // as 1 KB wave chunks; chunk I of the slab:
   // k-contiguous: fills rows 8I..8I+7, lane -> (row 8I + l/8, physical chunk
   // l%8 = logical chunk ^ kc_swz(row)).
   // mn-contiguous: lds byte o = 1024 I + 16 l is (k = o / ROWB, physical chunk
@@ -107,15 +103,8 @@ struct Operand {
   static __device__ __forceinline__ uint32_t slab_bytes(int64_t ld, int k0) {
     return KC ? (uint32_t)((int64_t)k0 * EB) : (uint32_t)((int64_t)k0 * ld * 2);
   }
-  static __device__ __forceinline__ void load(i32x4 rs, const uint32_t (&voff)[PER_WAVE], uint32_t kb,
-                                              LDS_AS char* lds) {
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-#pragma unroll
-    for (int q = 0; q < PER_WAVE; ++q)
-      dma16(rs, voff[q] + kb, 0u, (uint32_t)(uintptr_t)(lds + (wave * PER_WAVE + q) * 1024));
-  }
-
-  // Register-staged path: the same per-lane offsets and LDS positions as the DMA.
+  // A wave's chunks of a slab: loaded into registers (gload), written to LDS
+  // (lwrite) at byte (wave*PER_WAVE + q)*1024 + 16*lane of the stage.
   static __device__ __forceinline__ void gload(__amdgpu_buffer_rsrc_t rs, const uint32_t (&voff)[PER_WAVE],
                                                uint32_t kb, u32x4 (&reg)[PER_WAVE]) {
 #pragma unroll
@@ -127,8 +116,9 @@ struct Operand {
     *reinterpret_cast<LDS_AS u32x4*>(lds + (wave * PER_WAVE + q) * 1024 + lane * 16) = v;
   }
 
-  // k-contiguous operand of a slab with kvalid < KSLAB valid k (after its DMA has
-  // landed): zero the chunks past K, which hold the next row's values.
+  // k-contiguous operand of a slab with kvalid < KSLAB valid k (after this
+  // thread's writes of it): zero the chunks past K, which hold the next row's
+  // values.
   static __device__ __forceinline__ void zero_tail(LDS_AS char* lds, int kvalid) {
     if constexpr (KC) {
       const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -186,25 +176,10 @@ struct Mainloop {
   static constexpr int KSTEPS = F8 ? 2 : 4;  // MFMA k steps per slab
   static constexpr int STAGE = OA::BYTES + OB::BYTES;
 
-  // per-lane DMA offsets of slab 0 for both operands
+  // per-lane chunk offsets of slab 0 for both operands
   struct Dma {
     uint32_t a[OA::PER_WAVE], b[OB::PER_WAVE];
   };
-  static __device__ __forceinline__ void issue(const GemmArgs& p, i32x4 ra, i32x4 rb, const Dma& d, int k0,
-                                               LDS_AS char* st) {
-    OA::load(ra, d.a, OA::slab_bytes(p.lda, k0), st);
-    OB::load(rb, d.b, OB::slab_bytes(p.ldb, k0), st + OA::BYTES);
-    __builtin_amdgcn_sched_barrier(0);  // keep the DMA issue ahead of the MFMA work
-  }
-  static __device__ __forceinline__ void settle(const GemmArgs& p, int k0, LDS_AS char* st) {
-    // wait for this thread's DMAs; clear the k tail of a partial last slab
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    const int kvalid = p.K - k0;
-    if (kvalid < KSLAB) {
-      OA::zero_tail(st, kvalid);
-      OB::zero_tail(st + OA::BYTES, kvalid);
-    }
-  }
   // Register staging: slab data in flight / waiting to be written to LDS.
   struct Stg {
     u32x4 a[OA::PER_WAVE], b[OB::PER_WAVE];
@@ -220,13 +195,79 @@ struct Mainloop {
 #pragma unroll
     for (int q = 0; q < OB::PER_WAVE; ++q) OB::lwrite(g.b[q], q, st + OA::BYTES);
   }
+  // One staged chunk c (of the A chunks, then the B chunks): write it into wst,
+  // then reload its register with the chunk of slab k1.
+  static __device__ __forceinline__ void stage_chunk(int c, Stg& g, LDS_AS char* __restrict__ wst,
+                                                     __amdgpu_buffer_rsrc_t ra, __amdgpu_buffer_rsrc_t rb,
+                                                     const Dma& d, uint32_t kba, uint32_t kbb) {
+    constexpr int NA = OA::PER_WAVE;
+    if (c < NA) {
+      OA::lwrite(g.a[c], c, wst);
+      g.a[c] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(ra, (int)(d.a[c] + kba), 0, 0));
+    } else {
+      OB::lwrite(g.b[c - NA], c - NA, wst + OA::BYTES);
+      g.b[c - NA] =
+          __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rb, (int)(d.b[c - NA] + kbb), 0, 0));
+    }
+  }
+  // fp8 form of compute_vs: two 64-deep k steps per slab, half the chunks each.
+  static __device__ __forceinline__ void compute_vs_f8(const LDS_AS char* __restrict__ st, int wm, int wn, int lane,
+                                                       f32x16 (&acc)[TM][TN], Stg& g, LDS_AS char* __restrict__ wst,
+                                                       __amdgpu_buffer_rsrc_t ra, __amdgpu_buffer_rsrc_t rb,
+                                                       const GemmArgs& p, const Dma& d, int k1) {
+    constexpr int NC = OA::PER_WAVE + OB::PER_WAVE;
+    const uint32_t kba = OA::slab_bytes(p.lda, k1), kbb = OB::slab_bytes(p.ldb, k1);
+    const LDS_AS char* sa = st;
+    const LDS_AS char* sb = st + OA::BYTES;
+    u32x4 fa[2][TM][2], fb[2][TN][2];
+#pragma unroll
+    for (int i = 0; i < TM; ++i) OA::frag8(sa, wm * TM + i, 0, lane, fa[0][i][0], fa[0][i][1]);
+#pragma unroll
+    for (int j = 0; j < TN; ++j) OB::frag8(sb, wn * TN + j, 0, lane, fb[0][j][0], fb[0][j][1]);
+#pragma unroll
+    for (int kk = 0; kk < KSTEPS; ++kk) {
+      const int cur = kk & 1, nxt = cur ^ 1;
+      if (kk + 1 < KSTEPS) {
+#pragma unroll
+        for (int i = 0; i < TM; ++i) OA::frag8(sa, wm * TM + i, kk + 1, lane, fa[nxt][i][0], fa[nxt][i][1]);
+#pragma unroll
+        for (int j = 0; j < TN; ++j) OB::frag8(sb, wn * TN + j, kk + 1, lane, fb[nxt][j][0], fb[nxt][j][1]);
+      }
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+          acc[i][j] = mfma32_f8<FB, FA>(fb[cur][j][0], fb[cur][j][1], fa[cur][i][0], fa[cur][i][1], acc[i][j]);
+#pragma unroll
+      for (int c = kk * NC / KSTEPS; c < (kk + 1) * NC / KSTEPS; ++c) stage_chunk(c, g, wst, ra, rb, d, kba, kbb);
+    }
+    constexpr int NR = 2 * (TM + TN);
+    constexpr int NM = TM * TN;
+    constexpr int NW = NC / KSTEPS;
+    __builtin_amdgcn_sched_group_barrier(0x100, NR, 0);
+#pragma unroll
+    for (int kk = 0; kk < KSTEPS; ++kk) {
+#pragma unroll
+      for (int x = 0; x < NM; ++x) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        if (kk + 1 < KSTEPS && x < NR) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        if (x >= 1 && x < 1 + NW / 2) __builtin_amdgcn_sched_group_barrier(0x200, 2, 0);
+        if (x >= 1 + NW / 2 && x < 1 + NW) __builtin_amdgcn_sched_group_barrier(0x020, 2, 0);
+      }
+    }
+  }
+
   // compute(st) while writing the staged slab into wst and loading slab k1 into
   // the staging registers, chunk by chunk behind each write.
   static __device__ __forceinline__ void compute_vs(const LDS_AS char* __restrict__ st, int wm, int wn, int lane,
                                                     f32x16 (&acc)[TM][TN], Stg& g, LDS_AS char* __restrict__ wst,
                                                     __amdgpu_buffer_rsrc_t ra, __amdgpu_buffer_rsrc_t rb,
                                                     const GemmArgs& p, const Dma& d, int k1) {
-    constexpr int NA = OA::PER_WAVE, NB = OB::PER_WAVE, NC = NA + NB;
+    if constexpr (F8 != 0) {
+      compute_vs_f8(st, wm, wn, lane, acc, g, wst, ra, rb, p, d, k1);
+      return;
+    }
+    constexpr int NC = OA::PER_WAVE + OB::PER_WAVE;
     const uint32_t kba = OA::slab_bytes(p.lda, k1), kbb = OB::slab_bytes(p.ldb, k1);
     const LDS_AS char* sa = st;
     const LDS_AS char* sb = st + OA::BYTES;
@@ -250,16 +291,7 @@ struct Mainloop {
         for (int j = 0; j < TN; ++j) acc[i][j] = mfma32(fb[cur][j], fa[cur][i], acc[i][j]);
       // this step's share of the staged chunks: write, then reload for slab k1
 #pragma unroll
-      for (int c = kk * NC / 4; c < (kk + 1) * NC / 4; ++c) {
-        if (c < NA) {
-          OA::lwrite(g.a[c], c, wst);
-          g.a[c] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(ra, (int)(d.a[c] + kba), 0, 0));
-        } else {
-          OB::lwrite(g.b[c - NA], c - NA, wst + OA::BYTES);
-          g.b[c - NA] =
-              __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rb, (int)(d.b[c - NA] + kbb), 0, 0));
-        }
-      }
+      for (int c = kk * NC / 4; c < (kk + 1) * NC / 4; ++c) stage_chunk(c, g, wst, ra, rb, d, kba, kbb);
     }
     constexpr int NR = TM * (OA::READS) + TN * (OB::READS);  // LDS reads per step
     constexpr int NM = TM * TN;                               // MFMAs per step
@@ -430,62 +462,40 @@ __device__ __forceinline__ void gemm_tile(GemmArgs p, const int bid, LDS_AS char
 
   // Buffer resources: k-contiguous operands end after their last row (M or N),
   // mn-contiguous ones after row K, so everything past the matrix reads as 0.
-  const i32x4 ra = make_rsrc(p.a, (uint32_t)((A_K ? (int64_t)p.M : (int64_t)p.K) * p.lda * EB));
-  const i32x4 rb = make_rsrc(p.b, (uint32_t)((B_K ? (int64_t)p.N : (int64_t)p.K) * p.ldb * EB));
+  const __amdgpu_buffer_rsrc_t va = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(p.a), 0, (int)((A_K ? (int64_t)p.M : (int64_t)p.K) * p.lda * EB), 0x00020000);
+  const __amdgpu_buffer_rsrc_t vb = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(p.b), 0, (int)((B_K ? (int64_t)p.N : (int64_t)p.K) * p.ldb * EB), 0x00020000);
   const int nk = (p.K + KSLAB - 1) / KSLAB;
   typename ML::Dma dma;
   ML::OA::offsets(p.lda, m0, dma.a);
   ML::OB::offsets(p.ldb, n0, dma.b);
-  if constexpr (F8 == 0) {
-    // slab 0 to LDS now; slab 1 in the staging registers; while slab kt is
-    // multiplied, slab kt+1 is written from the registers to the other stage and
-    // slab kt+2 loaded behind it (slabs past K load in-range rows or zeros and
-    // are never read)
-    const __amdgpu_buffer_rsrc_t va = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint16_t*>(p.a), 0, (int)((A_K ? (int64_t)p.M : (int64_t)p.K) * p.lda * EB), 0x00020000);
-    const __amdgpu_buffer_rsrc_t vb = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint16_t*>(p.b), 0, (int)((B_K ? (int64_t)p.N : (int64_t)p.K) * p.ldb * EB), 0x00020000);
-    typename ML::Stg stg;
-    ML::gload(va, vb, p, dma, 0, stg);
-    ML::lwrite_all(stg, st0);
-    ML::gload(va, vb, p, dma, KSLAB, stg);
-    if (p.K < KSLAB) {  // each thread clears the k tail of the chunks it wrote
-      ML::OA::zero_tail(st0, p.K);
-      ML::OB::zero_tail(st0 + ML::OA::BYTES, p.K);
-    }
-    __syncthreads();
-    for (int kt = 0; kt < nk; ++kt) {
-      const bool odd = kt & 1;
-      const LDS_AS char* st = odd ? st1 : st0;
-      LDS_AS char* wst = odd ? st0 : st1;
-      ML::compute_vs(st, wm, wn, lane, acc, stg, wst, va, vb, p, dma, (kt + 2) * KSLAB);
-      const int kv = p.K - (kt + 1) * KSLAB;
-      if (kv > 0 && kv < KSLAB) {
-        ML::OA::zero_tail(wst, kv);
-        ML::OB::zero_tail(wst + ML::OA::BYTES, kv);
-      }
-      __syncthreads();
-    }
-  } else {
-  ML::issue(p, ra, rb, dma, 0, st0);
-  ML::settle(p, 0, st0);
+  // Slab 0 goes to LDS now and slab 1 into the staging registers.  While slab
+  // kt is multiplied, slab kt+1 is written from the registers into the other
+  // stage and slab kt+2 is loaded behind it (slabs past K load in-range rows or
+  // zeros and are never read); the last slab is multiplied alone.
+  typename ML::Stg stg;
+  ML::gload(va, vb, p, dma, 0, stg);
+  ML::lwrite_all(stg, st0);
+  if (nk > 1) ML::gload(va, vb, p, dma, KSLAB, stg);
+  if (p.K < KSLAB) {  // each thread clears the k tail of the chunks it wrote
+    ML::OA::zero_tail(st0, p.K);
+    ML::OB::zero_tail(st0 + ML::OA::BYTES, p.K);
+  }
   __syncthreads();
-  // Two slabs per trip (stage 0 then stage 1), so each LDS stage is a fixed
-  // object; an odd last slab is finished after the loop.
-  int kt = 0;
-  for (; kt + 1 < nk; kt += 2) {
-    ML::issue(p, ra, rb, dma, (kt + 1) * KSLAB, st1);
-    ML::compute(st0, wm, wn, lane, acc);
-    ML::settle(p, (kt + 1) * KSLAB, st1);
-    __syncthreads();
-    const bool more = kt + 2 < nk;
-    if (more) ML::issue(p, ra, rb, dma, (kt + 2) * KSLAB, st0);
-    ML::compute(st1, wm, wn, lane, acc);
-    if (more) ML::settle(p, (kt + 2) * KSLAB, st0);
+  for (int kt = 0; kt + 1 < nk; ++kt) {
+    const bool odd = kt & 1;
+    const LDS_AS char* st = odd ? st1 : st0;
+    LDS_AS char* wst = odd ? st0 : st1;
+    ML::compute_vs(st, wm, wn, lane, acc, stg, wst, va, vb, p, dma, (kt + 2) * KSLAB);
+    const int kv = p.K - (kt + 1) * KSLAB;
+    if (kv < KSLAB) {
+      ML::OA::zero_tail(wst, kv);
+      ML::OB::zero_tail(wst + ML::OA::BYTES, kv);
+    }
     __syncthreads();
   }
-  if (kt < nk) ML::compute(st0, wm, wn, lane, acc);
-  }
+  if (nk > 0) ML::compute((nk - 1) & 1 ? st1 : st0, wm, wn, lane, acc);  // K = 0 (an empty expert): acc = 0
   const int lrow = lane & 31, lgrp = lane >> 5;
 
   // ---- epilogue ----------------------------------------------------------
