@@ -244,6 +244,7 @@ struct Mainloop {
     constexpr int NR = 2 * (TM + TN);
     constexpr int NM = TM * TN;
     constexpr int NW = NC / KSTEPS;
+    constexpr int STEP = NM / (2 * NW) > 0 ? NM / (2 * NW) : 1;
     __builtin_amdgcn_sched_group_barrier(0x100, NR, 0);
 #pragma unroll
     for (int kk = 0; kk < KSTEPS; ++kk) {
@@ -251,8 +252,10 @@ struct Mainloop {
       for (int x = 0; x < NM; ++x) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
         if (kk + 1 < KSTEPS && x < NR) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-        if (x >= 1 && x < 1 + NW / 2) __builtin_amdgcn_sched_group_barrier(0x200, 2, 0);
-        if (x >= 1 + NW / 2 && x < 1 + NW) __builtin_amdgcn_sched_group_barrier(0x020, 2, 0);
+        if (x % STEP == STEP - 1) {  // writes and reloads spread over the MFMAs
+          if ((x / STEP) & 1) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+          else __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
+        }
       }
     }
   }
@@ -296,6 +299,7 @@ struct Mainloop {
     constexpr int NR = TM * (OA::READS) + TN * (OB::READS);  // LDS reads per step
     constexpr int NM = TM * TN;                               // MFMAs per step
     constexpr int NW = NC / 4;                                // LDS writes (and loads) per step
+    constexpr int STEP = NM / (2 * NW) > 0 ? NM / (2 * NW) : 1;
     __builtin_amdgcn_sched_group_barrier(0x100, NR, 0);
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
@@ -303,8 +307,12 @@ struct Mainloop {
       for (int x = 0; x < NM; ++x) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
         if (kk < 3 && x < NR) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-        if (x >= 2 && x < 2 + NW) __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
-        if (x >= 2 + NW && x < 2 + 2 * NW) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+        // the step's chunk writes and reloads spread evenly over its MFMAs,
+        // each reload right after its chunk's write
+        if (x % STEP == STEP - 1) {
+          if ((x / STEP) & 1) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+          else __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
+        }
       }
     }
   }
