@@ -140,20 +140,6 @@ __device__ __forceinline__ void dma16(i32x4 rsrc, uint32_t voff, uint32_t soff, 
       : "s"(lds), "v"(voff), "s"(rsrc), "s"(soff)
       : "memory");
 }
-// 4 bytes per lane from buffer offset voff + soff into LDS at lds + 4*lane
-// (buffer_load_dword ... lds), with the same M0 handling as dma16.
-__device__ __forceinline__ void dma4(i32x4 rsrc, uint32_t voff, uint32_t soff, uint32_t lds) {
-  uint32_t saved;
-  asm volatile(
-      "s_mov_b32 %0, m0\n\t"
-      "s_mov_b32 m0, %1\n\t"
-      "s_nop 0\n\t"
-      "buffer_load_dword %2, %3, %4 offen lds\n\t"
-      "s_mov_b32 m0, %0"
-      : "=&s"(saved)
-      : "s"(lds), "v"(voff), "s"(rsrc), "s"(soff)
-      : "memory");
-}
 __device__ __forceinline__ void wait_dma() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 // Wait for this wave's compiler-visible vector loads with the s_waitcnt builtin
 // (vmcnt 0, expcnt and lgkmcnt untouched), which the compiler's own wait

@@ -177,7 +177,7 @@ struct Mainloop {
   static constexpr int STAGE = OA::BYTES + OB::BYTES;
 
   // per-lane chunk offsets of slab 0 for both operands
-  struct Dma {
+  struct Offs {
     uint32_t a[OA::PER_WAVE], b[OB::PER_WAVE];
   };
   // Register staging: slab data in flight / waiting to be written to LDS.
@@ -185,7 +185,7 @@ struct Mainloop {
     u32x4 a[OA::PER_WAVE], b[OB::PER_WAVE];
   };
   static __device__ __forceinline__ void gload(__amdgpu_buffer_rsrc_t ra, __amdgpu_buffer_rsrc_t rb, const GemmArgs& p,
-                                               const Dma& d, int k0, Stg& g) {
+                                               const Offs& d, int k0, Stg& g) {
     OA::gload(ra, d.a, OA::slab_bytes(p.lda, k0), g.a);
     OB::gload(rb, d.b, OB::slab_bytes(p.ldb, k0), g.b);
   }
@@ -199,7 +199,7 @@ struct Mainloop {
   // then reload its register with the chunk of slab k1.
   static __device__ __forceinline__ void stage_chunk(int c, Stg& g, LDS_AS char* __restrict__ wst,
                                                      __amdgpu_buffer_rsrc_t ra, __amdgpu_buffer_rsrc_t rb,
-                                                     const Dma& d, uint32_t kba, uint32_t kbb) {
+                                                     const Offs& d, uint32_t kba, uint32_t kbb) {
     constexpr int NA = OA::PER_WAVE;
     if (c < NA) {
       OA::lwrite(g.a[c], c, wst);
@@ -214,7 +214,7 @@ struct Mainloop {
   static __device__ __forceinline__ void compute_vs_f8(const LDS_AS char* __restrict__ st, int wm, int wn, int lane,
                                                        f32x16 (&acc)[TM][TN], Stg& g, LDS_AS char* __restrict__ wst,
                                                        __amdgpu_buffer_rsrc_t ra, __amdgpu_buffer_rsrc_t rb,
-                                                       const GemmArgs& p, const Dma& d, int k1) {
+                                                       const GemmArgs& p, const Offs& d, int k1) {
     constexpr int NC = OA::PER_WAVE + OB::PER_WAVE;
     const uint32_t kba = OA::slab_bytes(p.lda, k1), kbb = OB::slab_bytes(p.ldb, k1);
     const LDS_AS char* sa = st;
@@ -265,7 +265,7 @@ struct Mainloop {
   static __device__ __forceinline__ void compute_vs(const LDS_AS char* __restrict__ st, int wm, int wn, int lane,
                                                     f32x16 (&acc)[TM][TN], Stg& g, LDS_AS char* __restrict__ wst,
                                                     __amdgpu_buffer_rsrc_t ra, __amdgpu_buffer_rsrc_t rb,
-                                                    const GemmArgs& p, const Dma& d, int k1) {
+                                                    const GemmArgs& p, const Offs& d, int k1) {
     if constexpr (F8 != 0) {
       compute_vs_f8(st, wm, wn, lane, acc, g, wst, ra, rb, p, d, k1);
       return;
@@ -475,17 +475,17 @@ __device__ __forceinline__ void gemm_tile(GemmArgs p, const int bid, LDS_AS char
   const __amdgpu_buffer_rsrc_t vb = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint16_t*>(p.b), 0, (int)((B_K ? (int64_t)p.N : (int64_t)p.K) * p.ldb * EB), 0x00020000);
   const int nk = (p.K + KSLAB - 1) / KSLAB;
-  typename ML::Dma dma;
-  ML::OA::offsets(p.lda, m0, dma.a);
-  ML::OB::offsets(p.ldb, n0, dma.b);
+  typename ML::Offs off;
+  ML::OA::offsets(p.lda, m0, off.a);
+  ML::OB::offsets(p.ldb, n0, off.b);
   // Slab 0 goes to LDS now and slab 1 into the staging registers.  While slab
   // kt is multiplied, slab kt+1 is written from the registers into the other
   // stage and slab kt+2 is loaded behind it (slabs past K load in-range rows or
   // zeros and are never read); the last slab is multiplied alone.
   typename ML::Stg stg;
-  ML::gload(va, vb, p, dma, 0, stg);
+  ML::gload(va, vb, p, off, 0, stg);
   ML::lwrite_all(stg, st0);
-  if (nk > 1) ML::gload(va, vb, p, dma, KSLAB, stg);
+  if (nk > 1) ML::gload(va, vb, p, off, KSLAB, stg);
   if (p.K < KSLAB) {  // each thread clears the k tail of the chunks it wrote
     ML::OA::zero_tail(st0, p.K);
     ML::OB::zero_tail(st0 + ML::OA::BYTES, p.K);
@@ -495,7 +495,7 @@ __device__ __forceinline__ void gemm_tile(GemmArgs p, const int bid, LDS_AS char
     const bool odd = kt & 1;
     const LDS_AS char* st = odd ? st1 : st0;
     LDS_AS char* wst = odd ? st0 : st1;
-    ML::compute_vs(st, wm, wn, lane, acc, stg, wst, va, vb, p, dma, (kt + 2) * KSLAB);
+    ML::compute_vs(st, wm, wn, lane, acc, stg, wst, va, vb, p, off, (kt + 2) * KSLAB);
     const int kv = p.K - (kt + 1) * KSLAB;
     if (kv < KSLAB) {
       ML::OA::zero_tail(wst, kv);
