@@ -509,7 +509,7 @@ __device__ __forceinline__ void gemm_tile(GemmArgs p, const int bid, LDS_AS char
   // ---- epilogue ----------------------------------------------------------
   // Lane (lrow, lgrp) holds, for every (i, j, g), row i*32 + lrow and columns
   // j*32 + 8g + 4*lgrp .. +3 of the wave's WM x WN sub-tile.  Values are first
-  // finished in registers (bias, GeLU), then written to the wave's own slice of
+  // finished in registers (bias, GeLU, GeLU'), then written to the wave's own slice of
   // the (now idle) LDS stages and read back row by row, so every global store
   // is 16 bytes per lane over whole rows.  fp32 results go in passes of IPP
   // row blocks.
@@ -518,9 +518,7 @@ __device__ __forceinline__ void gemm_tile(GemmArgs p, const int bid, LDS_AS char
   constexpr int REGION = ML::STAGE / 2;
   constexpr bool HAS_BIAS = (EPI == EPI_BF16_BIAS || EPI == EPI_BIAS_GELU);
   constexpr bool F32OUT = (EPI == EPI_F32 || EPI == EPI_F32_ACC);
-  // GeLU' is applied in the row phase against the stored z, so its products
-  // are staged in fp32 too.
-  constexpr bool F32STAGE = F32OUT || EPI == EPI_DGELU;
+  constexpr bool F32STAGE = F32OUT;
   constexpr int E = F32STAGE ? 4 : 2;
   constexpr int RB = WN * E;                 // bytes per staged row
   constexpr int CPR = RB / 16;               // 16-byte chunks per row
@@ -553,6 +551,19 @@ __device__ __forceinline__ void gemm_tile(GemmArgs p, const int bid, LDS_AS char
       for (int ii = 0; ii < IPP; ++ii) {
         const int i = i0 + ii;
         const int rl = ii * 32 + lrow;
+        // GeLU': this row block's z, in the accumulator layout (4 columns per load)
+        u32x2 zr[TN][4];
+        if constexpr (EPI == EPI_DGELU) {
+          const int m = mw + i * 32 + lrow;
+#pragma unroll
+          for (int j = 0; j < TN; ++j)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+              const int n = nw + j * 32 + 8 * g + 4 * lgrp;
+              zr[j][g] = (m < p.M && n < p.N) ? *reinterpret_cast<const u32x2*>(p.aux + (int64_t)m * p.ld_aux + n)
+                                              : u32x2{0, 0};
+            }
+        }
 #pragma unroll
         for (int j = 0; j < TN; ++j)
 #pragma unroll
@@ -571,6 +582,12 @@ __device__ __forceinline__ void gemm_tile(GemmArgs p, const int bid, LDS_AS char
             if (out == 1) {
 #pragma unroll
               for (int e = 0; e < 4; ++e) v[e] = gelu_f(v[e]);
+            }
+            if constexpr (EPI == EPI_DGELU) {
+              v[0] *= gelu_grad_f(bf16_lo(zr[j][g][0]));
+              v[1] *= gelu_grad_f(bf16_hi(zr[j][g][0]));
+              v[2] *= gelu_grad_f(bf16_lo(zr[j][g][1]));
+              v[3] *= gelu_grad_f(bf16_hi(zr[j][g][1]));
             }
             const int col = j * 32 + 8 * g + 4 * lgrp;
             if constexpr (F32STAGE) {
@@ -603,14 +620,6 @@ __device__ __forceinline__ void gemm_tile(GemmArgs p, const int bid, LDS_AS char
               f32x4 o = __builtin_bit_cast(f32x4, val);
               if constexpr (EPI == EPI_F32_ACC) o += *reinterpret_cast<const f32x4*>(c);
               *reinterpret_cast<f32x4*>(c) = o;
-            } else if constexpr (EPI == EPI_DGELU) {
-              const f32x4 d = __builtin_bit_cast(f32x4, val);
-              const u32x2 z = *reinterpret_cast<const u32x2*>(p.aux + (int64_t)m * p.ld_aux + n);
-              uint16_t* c = reinterpret_cast<uint16_t*>(p.c) + (int64_t)m * p.ldc + n;
-              *reinterpret_cast<u32x2*>(c) = u32x2{pack_bf16x2(d[0] * gelu_grad_f(bf16_lo(z[0])),
-                                                               d[1] * gelu_grad_f(bf16_hi(z[0]))),
-                                                   pack_bf16x2(d[2] * gelu_grad_f(bf16_lo(z[1])),
-                                                               d[3] * gelu_grad_f(bf16_hi(z[1])))};
             } else {
               uint16_t* c = reinterpret_cast<uint16_t*>(out == 0 ? p.c : p.c2) + (int64_t)m * (out == 0 ? p.ldc : p.ldc2) + n;
               *reinterpret_cast<u32x4*>(c) = val;
