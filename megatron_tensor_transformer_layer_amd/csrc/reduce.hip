@@ -28,17 +28,33 @@ struct ReduceArgs {
   int64_t begin, count;  // element range (row_begin*cols, rows*cols)
 };
 
+// T > 0: exactly T partials, whose loads are all issued before the first add;
+// T == 0: a.t partials, one at a time.  The sum is in rank order either way.
+template <int T>
 __global__ __launch_bounds__(256) void reduce_partials_kernel(ReduceArgs a) {
   const int64_t nvec = a.count / 8;
   for (int64_t v = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; v < nvec; v += (int64_t)gridDim.x * blockDim.x) {
     const int64_t e = a.begin + v * 8;
     float s[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-    for (int i = 0; i < a.t; ++i) {
-      const u32x4 x = *reinterpret_cast<const u32x4*>(a.p[i] + e);
+    if constexpr (T > 0) {
+      u32x4 x[T];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        s[2 * j] += bf16_lo(x[j]);
-        s[2 * j + 1] += bf16_hi(x[j]);
+      for (int i = 0; i < T; ++i) x[i] = *reinterpret_cast<const u32x4*>(a.p[i] + e);
+#pragma unroll
+      for (int i = 0; i < T; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          s[2 * j] += bf16_lo(x[i][j]);
+          s[2 * j + 1] += bf16_hi(x[i][j]);
+        }
+    } else {
+      for (int i = 0; i < a.t; ++i) {
+        const u32x4 x = *reinterpret_cast<const u32x4*>(a.p[i] + e);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          s[2 * j] += bf16_lo(x[j]);
+          s[2 * j + 1] += bf16_hi(x[j]);
+        }
       }
     }
     if (a.bias) {
@@ -80,7 +96,13 @@ hipError_t reduce_partials(int t, const uint16_t* const* partials, const uint16_
   const int64_t nvec = a.count / 8;
   int64_t blocks = (nvec + 255) / 256;
   if (blocks > 2048) blocks = 2048;
-  hipLaunchKernelGGL(reduce_partials_kernel, dim3((unsigned)blocks), dim3(256), 0, s, a);
+  switch (t) {
+    case 1: hipLaunchKernelGGL(reduce_partials_kernel<1>, dim3((unsigned)blocks), dim3(256), 0, s, a); break;
+    case 2: hipLaunchKernelGGL(reduce_partials_kernel<2>, dim3((unsigned)blocks), dim3(256), 0, s, a); break;
+    case 4: hipLaunchKernelGGL(reduce_partials_kernel<4>, dim3((unsigned)blocks), dim3(256), 0, s, a); break;
+    case 8: hipLaunchKernelGGL(reduce_partials_kernel<8>, dim3((unsigned)blocks), dim3(256), 0, s, a); break;
+    default: hipLaunchKernelGGL(reduce_partials_kernel<0>, dim3((unsigned)blocks), dim3(256), 0, s, a); break;
+  }
   return hipGetLastError();
 }
 
