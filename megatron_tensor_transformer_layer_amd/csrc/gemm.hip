@@ -27,8 +27,10 @@
 //    two ds_read_b64_tr_b16: within each 16-lane group, lanes 4R..4R+3 name row
 //    R of a 4 x 16 block and lane i receives its column i, i.e. four
 //    consecutive k of one m (or n).  No register transposes.
-//  * Fragments of the next 16-deep k step are read while the MFMAs of the
-//    current one run.
+//  * The MFMA stream runs one k step behind the fragment reads: step kk's
+//    fragments are read while step kk-1's MFMAs issue, across slab boundaries
+//    too, so after each slab's barrier the previous slab's last MFMAs (whose
+//    fragments are already in registers) cover the first LDS reads.
 //  * The MFMA is issued with the operands swapped (B fragment as "a") so that
 //    each lane owns 4 consecutive output columns of one row: the epilogue
 //    stores 8 or 16 bytes per lane.
@@ -210,195 +212,102 @@ struct Mainloop {
           __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rb, (int)(d.b[c - NA] + kbb), 0, 0));
     }
   }
-  // fp8 form of compute_vs: two 64-deep k steps per slab, half the chunks each.
-  static __device__ __forceinline__ void compute_vs_f8(const LDS_AS char* __restrict__ st, int wm, int wn, int lane,
-                                                       f32x16 (&acc)[TM][TN], Stg& g, LDS_AS char* __restrict__ wst,
-                                                       __amdgpu_buffer_rsrc_t ra, __amdgpu_buffer_rsrc_t rb,
-                                                       const GemmArgs& p, const Offs& d, int k1) {
-    constexpr int NC = OA::PER_WAVE + OB::PER_WAVE;
-    const uint32_t kba = OA::slab_bytes(p.lda, k1), kbb = OB::slab_bytes(p.ldb, k1);
+
+  // The operand fragments of one MFMA k step (16 deep for bf16, 64 for fp8,
+  // whose fragments are two 16-byte chunks).
+  static constexpr int NF = F8 ? 2 : 1;
+  struct Frags {
+    u32x4 a[TM][NF], b[TN][NF];
+  };
+  static __device__ __forceinline__ void read_step(const LDS_AS char* __restrict__ st, int wm, int wn, int lane, int kk,
+                                                   Frags& f) {
     const LDS_AS char* sa = st;
     const LDS_AS char* sb = st + OA::BYTES;
-    u32x4 fa[2][TM][2], fb[2][TN][2];
+    if constexpr (F8 != 0) {
 #pragma unroll
-    for (int i = 0; i < TM; ++i) OA::frag8(sa, wm * TM + i, 0, lane, fa[0][i][0], fa[0][i][1]);
+      for (int i = 0; i < TM; ++i) OA::frag8(sa, wm * TM + i, kk, lane, f.a[i][0], f.a[i][1]);
 #pragma unroll
-    for (int j = 0; j < TN; ++j) OB::frag8(sb, wn * TN + j, 0, lane, fb[0][j][0], fb[0][j][1]);
+      for (int j = 0; j < TN; ++j) OB::frag8(sb, wn * TN + j, kk, lane, f.b[j][0], f.b[j][1]);
+    } else {
 #pragma unroll
-    for (int kk = 0; kk < KSTEPS; ++kk) {
-      const int cur = kk & 1, nxt = cur ^ 1;
-      if (kk + 1 < KSTEPS) {
+      for (int i = 0; i < TM; ++i) f.a[i][0] = OA::frag(sa, wm * TM + i, kk, lane);
 #pragma unroll
-        for (int i = 0; i < TM; ++i) OA::frag8(sa, wm * TM + i, kk + 1, lane, fa[nxt][i][0], fa[nxt][i][1]);
-#pragma unroll
-        for (int j = 0; j < TN; ++j) OB::frag8(sb, wn * TN + j, kk + 1, lane, fb[nxt][j][0], fb[nxt][j][1]);
-      }
-#pragma unroll
-      for (int i = 0; i < TM; ++i)
-#pragma unroll
-        for (int j = 0; j < TN; ++j)
-          acc[i][j] = mfma32_f8<FB, FA>(fb[cur][j][0], fb[cur][j][1], fa[cur][i][0], fa[cur][i][1], acc[i][j]);
-#pragma unroll
-      for (int c = kk * NC / KSTEPS; c < (kk + 1) * NC / KSTEPS; ++c) stage_chunk(c, g, wst, ra, rb, d, kba, kbb);
+      for (int j = 0; j < TN; ++j) f.b[j][0] = OB::frag(sb, wn * TN + j, kk, lane);
     }
-    constexpr int NR = 2 * (TM + TN);
-    constexpr int NM = TM * TN;
-    constexpr int NW = NC / KSTEPS;
-    constexpr int STEP = NM / (2 * NW) > 0 ? NM / (2 * NW) : 1;
-    __builtin_amdgcn_sched_group_barrier(0x100, NR, 0);
+  }
+  // The operands go in swapped (B fragment first) so that a lane owns 4
+  // consecutive output columns.
+  static __device__ __forceinline__ void mfma_step(const Frags& f, f32x16 (&acc)[TM][TN]) {
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+        if constexpr (F8 != 0)
+          acc[i][j] = mfma32_f8<FB, FA>(f.b[j][0], f.b[j][1], f.a[i][0], f.a[i][1], acc[i][j]);
+        else
+          acc[i][j] = mfma32(f.b[j][0], f.a[i][0], acc[i][j]);
+      }
+  }
+
+  // One slab, with the MFMA stream running one k step behind the fragment
+  // reads: step kk's fragments are read from st while step kk-1's MFMAs issue.
+  // On entry f[1] holds the previous slab's last step (read before the barrier
+  // that separates the slabs), so its MFMAs keep the matrix cores busy while
+  // this slab's first fragments arrive; FIRST (no previous slab) skips them.
+  // On exit f[1] holds this slab's last step, for the next slab or for finish().
+  // With STAGE, the staged slab is written into wst chunk by chunk and each
+  // staging register is reloaded with its chunk of slab k1 right behind.
+  template <bool FIRST, bool STAGE>
+  static __device__ __forceinline__ void slab(const LDS_AS char* __restrict__ st, int wm, int wn, int lane,
+                                              f32x16 (&acc)[TM][TN], Frags (&f)[2], Stg& g,
+                                              LDS_AS char* __restrict__ wst, __amdgpu_buffer_rsrc_t ra,
+                                              __amdgpu_buffer_rsrc_t rb, const GemmArgs& p, const Offs& d, int k1) {
+    constexpr int NC = OA::PER_WAVE + OB::PER_WAVE;
+    uint32_t kba = 0, kbb = 0;
+    if constexpr (STAGE) {
+      kba = OA::slab_bytes(p.lda, k1);
+      kbb = OB::slab_bytes(p.ldb, k1);
+    }
 #pragma unroll
     for (int kk = 0; kk < KSTEPS; ++kk) {
+      read_step(st, wm, wn, lane, kk, f[kk & 1]);
+      if (!(FIRST && kk == 0)) mfma_step(f[(kk & 1) ^ 1], acc);
+      if constexpr (STAGE) {
+#pragma unroll
+        for (int c = kk * NC / KSTEPS; c < (kk + 1) * NC / KSTEPS; ++c) stage_chunk(c, g, wst, ra, rb, d, kba, kbb);
+      }
+    }
+    // Schedule: each step's MFMAs with its fragment reads interleaved one for
+    // one, and its share of the chunk writes and reloads spread evenly over them
+    // (each reload right after its chunk's write).
+    constexpr int NR = (TM * OA::READS + TN * OB::READS) * NF;  // LDS reads per step
+    constexpr int NM = TM * TN;                                 // MFMAs per step
+    constexpr int NW = STAGE ? NC / KSTEPS : 0;                 // chunk writes (and loads) per step
+    constexpr int STEP = NW == 0 ? NM + 1 : (NM / (2 * NW) > 0 ? NM / (2 * NW) : 1);
+#pragma unroll
+    for (int kk = 0; kk < KSTEPS; ++kk) {
+      if (FIRST && kk == 0) {
+        __builtin_amdgcn_sched_group_barrier(0x100, NR, 0);
+#pragma unroll
+        for (int w = 0; w < NW; ++w) {
+          __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+        }
+        continue;
+      }
 #pragma unroll
       for (int x = 0; x < NM; ++x) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        if (kk + 1 < KSTEPS && x < NR) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-        if (x % STEP == STEP - 1) {  // writes and reloads spread over the MFMAs
+        if (x < NR) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        if (x % STEP == STEP - 1 && x / STEP < 2 * NW) {
           if ((x / STEP) & 1) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
           else __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
         }
       }
     }
   }
-
-  // compute(st) while writing the staged slab into wst and loading slab k1 into
-  // the staging registers, chunk by chunk behind each write.
-  static __device__ __forceinline__ void compute_vs(const LDS_AS char* __restrict__ st, int wm, int wn, int lane,
-                                                    f32x16 (&acc)[TM][TN], Stg& g, LDS_AS char* __restrict__ wst,
-                                                    __amdgpu_buffer_rsrc_t ra, __amdgpu_buffer_rsrc_t rb,
-                                                    const GemmArgs& p, const Offs& d, int k1) {
-    if constexpr (F8 != 0) {
-      compute_vs_f8(st, wm, wn, lane, acc, g, wst, ra, rb, p, d, k1);
-      return;
-    }
-    constexpr int NC = OA::PER_WAVE + OB::PER_WAVE;
-    const uint32_t kba = OA::slab_bytes(p.lda, k1), kbb = OB::slab_bytes(p.ldb, k1);
-    const LDS_AS char* sa = st;
-    const LDS_AS char* sb = st + OA::BYTES;
-    u32x4 fa[2][TM], fb[2][TN];
-#pragma unroll
-    for (int i = 0; i < TM; ++i) fa[0][i] = OA::frag(sa, wm * TM + i, 0, lane);
-#pragma unroll
-    for (int j = 0; j < TN; ++j) fb[0][j] = OB::frag(sb, wn * TN + j, 0, lane);
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      const int cur = kk & 1, nxt = cur ^ 1;
-      if (kk < 3) {
-#pragma unroll
-        for (int i = 0; i < TM; ++i) fa[nxt][i] = OA::frag(sa, wm * TM + i, kk + 1, lane);
-#pragma unroll
-        for (int j = 0; j < TN; ++j) fb[nxt][j] = OB::frag(sb, wn * TN + j, kk + 1, lane);
-      }
-#pragma unroll
-      for (int i = 0; i < TM; ++i)
-#pragma unroll
-        for (int j = 0; j < TN; ++j) acc[i][j] = mfma32(fb[cur][j], fa[cur][i], acc[i][j]);
-      // this step's share of the staged chunks: write, then reload for slab k1
-#pragma unroll
-      for (int c = kk * NC / 4; c < (kk + 1) * NC / 4; ++c) stage_chunk(c, g, wst, ra, rb, d, kba, kbb);
-    }
-    constexpr int NR = TM * (OA::READS) + TN * (OB::READS);  // LDS reads per step
-    constexpr int NM = TM * TN;                               // MFMAs per step
-    constexpr int NW = NC / 4;                                // LDS writes (and loads) per step
-    constexpr int STEP = NM / (2 * NW) > 0 ? NM / (2 * NW) : 1;
-    __builtin_amdgcn_sched_group_barrier(0x100, NR, 0);
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-#pragma unroll
-      for (int x = 0; x < NM; ++x) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        if (kk < 3 && x < NR) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-        // the step's chunk writes and reloads spread evenly over its MFMAs,
-        // each reload right after its chunk's write
-        if (x % STEP == STEP - 1) {
-          if ((x / STEP) & 1) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
-          else __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
-        }
-      }
-    }
-  }
-
-  static __device__ __forceinline__ void compute(const LDS_AS char* st, int wm, int wn, int lane,
-                                                 f32x16 (&acc)[TM][TN]) {
-    if constexpr (F8 != 0) {
-      compute_f8(st, wm, wn, lane, acc);
-      return;
-    }
-    const LDS_AS char* sa = st;
-    const LDS_AS char* sb = st + OA::BYTES;
-    u32x4 fa[2][TM], fb[2][TN];
-#pragma unroll
-    for (int i = 0; i < TM; ++i) fa[0][i] = OA::frag(sa, wm * TM + i, 0, lane);
-#pragma unroll
-    for (int j = 0; j < TN; ++j) fb[0][j] = OB::frag(sb, wn * TN + j, 0, lane);
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      const int cur = kk & 1, nxt = cur ^ 1;
-      if (kk < 3) {
-#pragma unroll
-        for (int i = 0; i < TM; ++i) fa[nxt][i] = OA::frag(sa, wm * TM + i, kk + 1, lane);
-#pragma unroll
-        for (int j = 0; j < TN; ++j) fb[nxt][j] = OB::frag(sb, wn * TN + j, kk + 1, lane);
-      }
-#pragma unroll
-      for (int i = 0; i < TM; ++i)
-#pragma unroll
-        for (int j = 0; j < TN; ++j) acc[i][j] = mfma32(fb[cur][j], fa[cur][i], acc[i][j]);
-    }
-    // Schedule: the first step's fragment reads, then for every step its MFMAs
-    // with the next step's fragment reads interleaved one for one, so LDS
-    // latency hides behind MFMA issue.
-    constexpr int NR = TM * (OA::READS) + TN * (OB::READS);  // LDS reads per step
-    constexpr int NM = TM * TN;                               // MFMAs per step
-    __builtin_amdgcn_sched_group_barrier(0x100, NR, 0);
-#pragma unroll
-    for (int kk = 0; kk < 3; ++kk) {
-#pragma unroll
-      for (int x = 0; x < NM; ++x) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        if (x < NR) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      }
-    }
-    __builtin_amdgcn_sched_group_barrier(0x008, NM, 0);
-  }
-  // fp8: two 64-deep k steps per slab, the same read/MFMA interleave.
-  static __device__ __forceinline__ void compute_f8(const LDS_AS char* st, int wm, int wn, int lane,
-                                                    f32x16 (&acc)[TM][TN]) {
-    const LDS_AS char* sa = st;
-    const LDS_AS char* sb = st + OA::BYTES;
-    u32x4 fa[2][TM][2], fb[2][TN][2];
-#pragma unroll
-    for (int i = 0; i < TM; ++i) OA::frag8(sa, wm * TM + i, 0, lane, fa[0][i][0], fa[0][i][1]);
-#pragma unroll
-    for (int j = 0; j < TN; ++j) OB::frag8(sb, wn * TN + j, 0, lane, fb[0][j][0], fb[0][j][1]);
-#pragma unroll
-    for (int kk = 0; kk < KSTEPS; ++kk) {
-      const int cur = kk & 1, nxt = cur ^ 1;
-      if (kk + 1 < KSTEPS) {
-#pragma unroll
-        for (int i = 0; i < TM; ++i) OA::frag8(sa, wm * TM + i, kk + 1, lane, fa[nxt][i][0], fa[nxt][i][1]);
-#pragma unroll
-        for (int j = 0; j < TN; ++j) OB::frag8(sb, wn * TN + j, kk + 1, lane, fb[nxt][j][0], fb[nxt][j][1]);
-      }
-      // operands swapped as in the bf16 path: the B fragment goes first
-#pragma unroll
-      for (int i = 0; i < TM; ++i)
-#pragma unroll
-        for (int j = 0; j < TN; ++j)
-          acc[i][j] = mfma32_f8<FB, FA>(fb[cur][j][0], fb[cur][j][1], fa[cur][i][0], fa[cur][i][1], acc[i][j]);
-    }
-    constexpr int NR = 2 * (TM + TN);
-    constexpr int NM = TM * TN;
-    __builtin_amdgcn_sched_group_barrier(0x100, NR, 0);
-#pragma unroll
-    for (int kk = 0; kk < KSTEPS - 1; ++kk) {
-#pragma unroll
-      for (int x = 0; x < NM; ++x) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        if (x < NR) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      }
-    }
-    __builtin_amdgcn_sched_group_barrier(0x008, NM, 0);
-  }
+  // The last slab's last step.
+  static __device__ __forceinline__ void finish(const Frags (&f)[2], f32x16 (&acc)[TM][TN]) { mfma_step(f[1], acc); }
 };
 
 // One output tile (workgroup index bid of the GEMM p) with the two LDS stages
@@ -491,19 +400,32 @@ __device__ __forceinline__ void gemm_tile(GemmArgs p, const int bid, LDS_AS char
     ML::OB::zero_tail(st0 + ML::OA::BYTES, p.K);
   }
   __syncthreads();
-  for (int kt = 0; kt + 1 < nk; ++kt) {
-    const bool odd = kt & 1;
-    const LDS_AS char* st = odd ? st1 : st0;
-    LDS_AS char* wst = odd ? st0 : st1;
-    ML::compute_vs(st, wm, wn, lane, acc, stg, wst, va, vb, p, off, (kt + 2) * KSLAB);
-    const int kv = p.K - (kt + 1) * KSLAB;
-    if (kv < KSLAB) {
-      ML::OA::zero_tail(wst, kv);
-      ML::OB::zero_tail(wst + ML::OA::BYTES, kv);
+  typename ML::Frags fr[2];
+  if (nk == 1) {
+    ML::template slab<true, false>(st0, wm, wn, lane, acc, fr, stg, st1, va, vb, p, off, 0);
+  } else if (nk > 1) {
+    // slab 0 (no previous step to finish), staging slab 1
+    ML::template slab<true, true>(st0, wm, wn, lane, acc, fr, stg, st1, va, vb, p, off, 2 * KSLAB);
+    if (p.K - KSLAB < KSLAB) {
+      ML::OA::zero_tail(st1, p.K - KSLAB);
+      ML::OB::zero_tail(st1 + ML::OA::BYTES, p.K - KSLAB);
     }
     __syncthreads();
+    for (int kt = 1; kt + 1 < nk; ++kt) {
+      const bool odd = kt & 1;
+      const LDS_AS char* st = odd ? st1 : st0;
+      LDS_AS char* wst = odd ? st0 : st1;
+      ML::template slab<false, true>(st, wm, wn, lane, acc, fr, stg, wst, va, vb, p, off, (kt + 2) * KSLAB);
+      const int kv = p.K - (kt + 1) * KSLAB;
+      if (kv < KSLAB) {
+        ML::OA::zero_tail(wst, kv);
+        ML::OB::zero_tail(wst + ML::OA::BYTES, kv);
+      }
+      __syncthreads();
+    }
+    ML::template slab<false, false>((nk - 1) & 1 ? st1 : st0, wm, wn, lane, acc, fr, stg, st1, va, vb, p, off, 0);
   }
-  if (nk > 0) ML::compute((nk - 1) & 1 ? st1 : st0, wm, wn, lane, acc);  // K = 0 (an empty expert): acc = 0
+  if (nk > 0) ML::finish(fr, acc);  // K = 0 (an empty expert): acc = 0
   const int lrow = lane & 31, lgrp = lane >> 5;
 
   // ---- epilogue ----------------------------------------------------------
