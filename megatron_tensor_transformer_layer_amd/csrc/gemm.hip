@@ -62,14 +62,15 @@ __device__ __forceinline__ int mn_swz(int k) {
   else return ((k >> 1) & 1) << 2;
 }
 
-template <int ROWS, bool KC, int EB = 2>
+template <int ROWS, bool KC, int EB = 2, int NWAVES = 4>
 struct Operand {
   static_assert(EB == 2 || KC, "fp8 operands are k-contiguous");
   static constexpr int BYTES = ROWS * 128;     // one slab: 128 bytes of k per row
   static constexpr int KSLAB = 128 / EB;       // k per slab: 64 bf16 or 128 fp8
   static constexpr int CHUNK = 16 / EB;        // k per 16-byte chunk
   static constexpr int INSTR = BYTES / 1024;   // wave instructions per slab
-  static constexpr int PER_WAVE = INSTR / 4;
+  static constexpr int PER_WAVE = INSTR / NWAVES;
+  static_assert(INSTR % NWAVES == 0, "slab chunks must split evenly over the waves");
   static constexpr int ROWB = ROWS * 2;        // row bytes of the mn-contiguous layout
   static constexpr int READS = (KC && EB == 2) ? 1 : 2;  // LDS read instructions per fragment
 
@@ -166,14 +167,15 @@ struct Operand {
 
 // F8 = 0: bf16 operands.  F8 = 1 + FA + 2*FB: fp8 operands, A in format FA and
 // B in format FB (0 = E4M3, 1 = E5M2), both k-contiguous.
-template <int BM, int BN, bool A_K, bool B_K, int F8 = 0>
+template <int BM, int BN, bool A_K, bool B_K, int F8 = 0, int NWN = 2>
 struct Mainloop {
-  static constexpr int WM = BM / 2, WN = BN / 2;
+  static constexpr int NWAVES = 2 * NWN;  // 2 x NWN waves over the tile
+  static constexpr int WM = BM / 2, WN = BN / NWN;
   static constexpr int TM = WM / 32, TN = WN / 32;
   static constexpr int EB = F8 ? 1 : 2;
   static constexpr int FA = F8 ? (F8 - 1) & 1 : 0, FB = F8 ? (F8 - 1) >> 1 : 0;
-  using OA = Operand<BM, A_K, EB>;
-  using OB = Operand<BN, B_K, EB>;
+  using OA = Operand<BM, A_K, EB, NWAVES>;
+  using OB = Operand<BN, B_K, EB, NWAVES>;
   static constexpr int KSLAB = OA::KSLAB;
   static constexpr int KSTEPS = F8 ? 2 : 4;  // MFMA k steps per slab
   static constexpr int STAGE = OA::BYTES + OB::BYTES;
@@ -312,9 +314,9 @@ struct Mainloop {
 
 // One output tile (workgroup index bid of the GEMM p) with the two LDS stages
 // st0, st1 of the launching kernel.
-template <int BM, int BN, bool A_K, bool B_K, int EPI, int F8>
+template <int BM, int BN, bool A_K, bool B_K, int EPI, int F8, int NWN = 2>
 __device__ __forceinline__ void gemm_tile(GemmArgs p, const int bid, LDS_AS char* st0, LDS_AS char* st1) {
-  using ML = Mainloop<BM, BN, A_K, B_K, F8>;
+  using ML = Mainloop<BM, BN, A_K, B_K, F8, NWN>;
   constexpr int EB = ML::EB, KSLAB = ML::KSLAB;
   constexpr int WM = ML::WM, WN = ML::WN, TM = ML::TM, TN = ML::TN;
   constexpr int OUT_BYTES = (EPI == EPI_F32 || EPI == EPI_F32_ACC) ? 4 : 2;
@@ -369,7 +371,7 @@ __device__ __forceinline__ void gemm_tile(GemmArgs p, const int bid, LDS_AS char
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / NWN, wn = wave % NWN;
 
   f32x16 acc[TM][TN];
 #pragma unroll
@@ -425,8 +427,27 @@ __device__ __forceinline__ void gemm_tile(GemmArgs p, const int bid, LDS_AS char
     }
     ML::template slab<false, false>((nk - 1) & 1 ? st1 : st0, wm, wn, lane, acc, fr, stg, st1, va, vb, p, off, 0);
   }
-  if (nk > 0) ML::finish(fr, acc);  // K = 0 (an empty expert): acc = 0
   const int lrow = lane & 31, lgrp = lane >> 5;
+  const int mw = m0 + wm * WM, nw = n0 + wn * WN;
+  // GeLU': z for the whole wave sub-tile, in the accumulator layout (4 columns
+  // per load), requested before the last MFMAs so that the loads land under
+  // them instead of one row block at a time in the epilogue.
+  u32x2 zr[EPI == EPI_DGELU ? TM : 1][TN][4];
+  if constexpr (EPI == EPI_DGELU) {
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+      const int m = mw + i * 32 + lrow;
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int n = nw + j * 32 + 8 * g + 4 * lgrp;
+          zr[i][j][g] = (m < p.M && n < p.N) ? *reinterpret_cast<const u32x2*>(p.aux + (int64_t)m * p.ld_aux + n)
+                                             : u32x2{0, 0};
+        }
+    }
+  }
+  if (nk > 0) ML::finish(fr, acc);  // K = 0 (an empty expert): acc = 0
 
   // ---- epilogue ----------------------------------------------------------
   // Lane (lrow, lgrp) holds, for every (i, j, g), row i*32 + lrow and columns
@@ -436,8 +457,9 @@ __device__ __forceinline__ void gemm_tile(GemmArgs p, const int bid, LDS_AS char
   // is 16 bytes per lane over whole rows.  fp32 results go in passes of IPP
   // row blocks.
   __syncthreads();  // all waves are done with the last slab
-  LDS_AS char* region = (wave < 2 ? st0 : st1) + (wave & 1) * (ML::STAGE / 2);
-  constexpr int REGION = ML::STAGE / 2;
+  constexpr int HALF = ML::NWAVES / 2;  // waves whose staging slices lie in each stage
+  constexpr int REGION = ML::STAGE / HALF;
+  LDS_AS char* region = (wave < HALF ? st0 : st1) + (wave % HALF) * REGION;
   constexpr bool HAS_BIAS = (EPI == EPI_BF16_BIAS || EPI == EPI_BIAS_GELU);
   constexpr bool F32OUT = (EPI == EPI_F32 || EPI == EPI_F32_ACC);
   constexpr bool F32STAGE = F32OUT;
@@ -446,7 +468,6 @@ __device__ __forceinline__ void gemm_tile(GemmArgs p, const int bid, LDS_AS char
   constexpr int CPR = RB / 16;               // 16-byte chunks per row
   constexpr int IPP = (REGION / (32 * RB)) < TM ? (REGION / (32 * RB)) : TM;
   static_assert(IPP >= 1, "epilogue staging does not fit");
-  const int mw = m0 + wm * WM, nw = n0 + wn * WN;
 
   // fp8: the product of the two operands' dequantisation factors
   float dq = 1.f;
@@ -473,19 +494,6 @@ __device__ __forceinline__ void gemm_tile(GemmArgs p, const int bid, LDS_AS char
       for (int ii = 0; ii < IPP; ++ii) {
         const int i = i0 + ii;
         const int rl = ii * 32 + lrow;
-        // GeLU': this row block's z, in the accumulator layout (4 columns per load)
-        u32x2 zr[TN][4];
-        if constexpr (EPI == EPI_DGELU) {
-          const int m = mw + i * 32 + lrow;
-#pragma unroll
-          for (int j = 0; j < TN; ++j)
-#pragma unroll
-            for (int g = 0; g < 4; ++g) {
-              const int n = nw + j * 32 + 8 * g + 4 * lgrp;
-              zr[j][g] = (m < p.M && n < p.N) ? *reinterpret_cast<const u32x2*>(p.aux + (int64_t)m * p.ld_aux + n)
-                                              : u32x2{0, 0};
-            }
-        }
 #pragma unroll
         for (int j = 0; j < TN; ++j)
 #pragma unroll
@@ -506,10 +514,10 @@ __device__ __forceinline__ void gemm_tile(GemmArgs p, const int bid, LDS_AS char
               for (int e = 0; e < 4; ++e) v[e] = gelu_f(v[e]);
             }
             if constexpr (EPI == EPI_DGELU) {
-              v[0] *= gelu_grad_f(bf16_lo(zr[j][g][0]));
-              v[1] *= gelu_grad_f(bf16_hi(zr[j][g][0]));
-              v[2] *= gelu_grad_f(bf16_lo(zr[j][g][1]));
-              v[3] *= gelu_grad_f(bf16_hi(zr[j][g][1]));
+              v[0] *= gelu_grad_f(bf16_lo(zr[i][j][g][0]));
+              v[1] *= gelu_grad_f(bf16_hi(zr[i][j][g][0]));
+              v[2] *= gelu_grad_f(bf16_lo(zr[i][j][g][1]));
+              v[3] *= gelu_grad_f(bf16_hi(zr[i][j][g][1]));
             }
             const int col = j * 32 + 8 * g + 4 * lgrp;
             if constexpr (F32STAGE) {
@@ -554,12 +562,12 @@ __device__ __forceinline__ void gemm_tile(GemmArgs p, const int bid, LDS_AS char
   }
 }
 
-template <int BM, int BN, bool A_K, bool B_K, int EPI, int F8 = 0>
-__global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmArgs p) {
-  constexpr int STAGE = Mainloop<BM, BN, A_K, B_K, F8>::STAGE;
+template <int BM, int BN, bool A_K, bool B_K, int EPI, int F8 = 0, int NWN = 2>
+__global__ __launch_bounds__(128 * NWN, 1) void gemm_bf16_kernel(GemmArgs p) {
+  constexpr int STAGE = Mainloop<BM, BN, A_K, B_K, F8, NWN>::STAGE;
   __shared__ __attribute__((aligned(1024))) char st0_[STAGE];
   __shared__ __attribute__((aligned(1024))) char st1_[STAGE];
-  gemm_tile<BM, BN, A_K, B_K, EPI, F8>(p, blockIdx.x, (LDS_AS char*)st0_, (LDS_AS char*)st1_);
+  gemm_tile<BM, BN, A_K, B_K, EPI, F8, NWN>(p, blockIdx.x, (LDS_AS char*)st0_, (LDS_AS char*)st1_);
 }
 
 // A tile configuration of gemm_tile.
@@ -588,7 +596,7 @@ __global__ __launch_bounds__(256, 1) void gemm_pair_kernel(GemmArgs p1, GemmArgs
                                                             (LDS_AS char*)st1_);
 }
 
-template <int BM, int BN, bool A_K, bool B_K, int EPI, int F8 = 0>
+template <int BM, int BN, bool A_K, bool B_K, int EPI, int F8 = 0, int NWN = 2>
 static hipError_t launch_cfg(const GemmArgs& p, hipStream_t s) {
   int64_t tiles;
   if (p.offsets == nullptr) {
@@ -600,16 +608,21 @@ static hipError_t launch_cfg(const GemmArgs& p, hipStream_t s) {
     tiles = (int64_t)p.groups * ((p.M + BM - 1) / BM) * ((p.N + BN - 1) / BN);
   }
   if (tiles <= 0) return hipSuccess;
-  hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, A_K, B_K, EPI, F8>), dim3((unsigned)tiles), dim3(256), 0, s, p);
+  hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, A_K, B_K, EPI, F8, NWN>), dim3((unsigned)tiles), dim3(128 * NWN), 0, s, p);
   return hipGetLastError();
 }
 
+// 256 x 256 tiles run with 8 waves (two per SIMD, 128 x 64 each) when the
+// epilogue evaluates GeLU or GeLU' for every element: the second wave on each
+// SIMD hides the transcendental work and the z loads of the first (-7 to -10 us
+// on 4096^3).  With light epilogues the 4-wave tile is as fast or faster.
 template <bool A_K, bool B_K, int EPI>
 static hipError_t launch_layout(const GemmArgs& p, hipStream_t s) {
-  if (p.offsets) return launch_cfg<256, 256, A_K, B_K, EPI>(p, s);  // expert GEMMs are large
+  constexpr int NWN = (EPI == EPI_BIAS_GELU || EPI == EPI_DGELU) ? 4 : 2;
+  if (p.offsets) return launch_cfg<256, 256, A_K, B_K, EPI, 0, NWN>(p, s);  // expert GEMMs are large
   const long t256 = (long)((p.M + 255) / 256) * ((p.N + 255) / 256);
   const long t192 = (long)((p.M + 255) / 256) * ((p.N + 191) / 192);
-  if (t256 >= 240) return launch_cfg<256, 256, A_K, B_K, EPI>(p, s);
+  if (t256 >= 240) return launch_cfg<256, 256, A_K, B_K, EPI, 0, NWN>(p, s);
   if (t192 >= 240 && p.N % 192 == 0) return launch_cfg<256, 192, A_K, B_K, EPI>(p, s);
   return launch_cfg<128, 128, A_K, B_K, EPI>(p, s);
 }
