@@ -129,24 +129,25 @@ mtl_status mtl_reduce(int32_t t, const void* const* partials, const void* bias, 
                       int64_t rows, int64_t cols, int64_t row_begin, int64_t row_end, mtl_stream_t stream);
 
 /* MLP half of the rank's forward (column-parallel fc1 with fused GeLU,
- * row-parallel fc2):
- *   z       = h . w1 + b1     [S, f/t] bf16 (saved)
- *   a       = GeLU(z)         [S, f/t] bf16 (saved; GeLU of the fp32 z)
+ * row-parallel fc2), with z = h . w1 + b1 in fp32:
+ *   gz      = GeLU'(z)        [S, f/t] bf16 (saved: the backward needs z only
+ *                             through the GeLU derivative)
+ *   a       = GeLU(z)         [S, f/t] bf16 (saved)
  *   partial = a . w2          [S, h]   bf16, this rank's partial sum
  * h [S, h] bf16 is the reduced attention output.  scratch as for mtl_attn_fwd;
  * in fp8, a is quantised from its bf16 values. */
 mtl_status mtl_mlp_fwd(const mtl_layer_cfg* cfg, const void* h, const void* w1, const void* b1, const void* w2,
-                       void* z, void* a, void* partial, void* scratch, size_t scratch_bytes, mtl_stream_t stream);
+                       void* gz, void* a, void* partial, void* scratch, size_t scratch_bytes, mtl_stream_t stream);
 
 /* MLP backward given dy = dL/dY [S, h] bf16 (every rank holds all of it):
- *   dz         = (dy . w2^T) * GeLU'(z)      (scratch, bf16)
+ *   dz         = (dy . w2^T) * gz            (scratch, bf16; gz = GeLU'(z) from mtl_mlp_fwd)
  *   dw2        = a^T . dy                    [f/t, h] fp32
  *   dw1        = h^T . dz                    [h, f/t] fp32
  *   db1        = colsum(dz)                  [f/t] fp32
  *   db2        = colsum(dy)                  [h] fp32, skipped when NULL
  *   dh_partial = dz . w1^T                   [S, h] bf16, this rank's partial
  * With MTL_F_WGRAD_ACCUM the fp32 gradients are added to what the buffers hold. */
-mtl_status mtl_mlp_bwd(const mtl_layer_cfg* cfg, const void* dy, const void* h, const void* z, const void* a,
+mtl_status mtl_mlp_bwd(const mtl_layer_cfg* cfg, const void* dy, const void* h, const void* gz, const void* a,
                        const void* w1, const void* w2, void* dh_partial, float* dw1, float* db1, float* dw2,
                        float* db2, void* scratch, size_t scratch_bytes, mtl_stream_t stream);
 
@@ -233,7 +234,7 @@ typedef struct mtl_moe_cfg {
  * (max(N_max, w) + 256) * w * 2 < 2^32 bytes with w = max(h, f) (MTL_E_SHAPE). */
 mtl_status mtl_moe_validate(const mtl_moe_cfg* cfg);
 
-/* N_max = tokens * min(topk, experts/ep): rows of xp, z, a, ye and of the
+/* N_max = tokens * min(topk, experts/ep): rows of xp, gz, a, ye and of the
  * backward scratch; and the backward's scratch bytes.  Either output may be NULL. */
 mtl_status mtl_moe_sizes(const mtl_moe_cfg* cfg, int64_t* max_rows, size_t* scratch_bytes);
 
@@ -254,20 +255,21 @@ mtl_status mtl_moe_permute(const mtl_moe_cfg* cfg, const int32_t* topk_idx, int3
 
 /* Expert forward (grouped GEMMs over the E_l local experts):
  *   xp = x[perm_token]                     [N_max, h] bf16 (saved)
- *   z  = xp_e . w1_e per expert            [N_max, f] bf16 (saved)
- *   a  = GeLU(z)                           [N_max, f] bf16 (saved, GeLU of fp32 z)
+ *   with z = xp_e . w1_e per expert in fp32:
+ *   gz = GeLU'(z)                          [N_max, f] bf16 (saved)
+ *   a  = GeLU(z)                           [N_max, f] bf16 (saved)
  *   ye = a_e . w2_e per expert             [N_max, h] bf16 (saved, not gate-scaled)
  *   y_partial[t] = sum over local slots s of t, ascending, of gates[t,s] * ye[row]
  *                                          [T, h] bf16 (zero rows for tokens with no local expert)
  * x [T, h] bf16; the routing arrays are those of mtl_moe_route/permute. */
 mtl_status mtl_moe_fwd(const mtl_moe_cfg* cfg, const void* x, const int32_t* offsets, const int32_t* perm_token,
-                       const int32_t* slot_row, const float* gates, const void* w1, const void* w2, void* xp, void* z,
+                       const int32_t* slot_row, const float* gates, const void* w1, const void* w2, void* xp, void* gz,
                        void* a, void* ye, void* y_partial, mtl_stream_t stream);
 
 /* Expert backward given dy = dL/dY [T, h] bf16:
  *   dye       = gates[t,s] * dy[t] per row       (scratch)
  *   dgates    = <ye[row], dy[t]>                 [T, k] fp32, 0 on non-local slots
- *   dz        = (dye_e . w2_e^T) * GeLU'(z)      (scratch)
+ *   dz        = (dye_e . w2_e^T) * gz            (scratch; gz = GeLU'(z) from mtl_moe_fwd)
  *   dw2[e]    = a_e^T . dye_e                    [E_l, f, h] fp32
  *   dw1[e]    = xp_e^T . dz_e                    [E_l, h, f] fp32 (zero for an expert with no rows)
  *   dx_partial[t] = sum over local slots of t, ascending, of (dz_e . w1_e^T)[row]
@@ -276,7 +278,7 @@ mtl_status mtl_moe_fwd(const mtl_moe_cfg* cfg, const void* x, const int32_t* off
  * With MTL_F_WGRAD_ACCUM, dw1/dw2 are added to. */
 mtl_status mtl_moe_bwd(const mtl_moe_cfg* cfg, const void* dy, const int32_t* offsets, const int32_t* perm_token,
                        const int32_t* perm_slot, const int32_t* slot_row, const float* gates, const void* xp,
-                       const void* z, const void* a, const void* ye, const void* w1, const void* w2, void* dx_partial,
+                       const void* gz, const void* a, const void* ye, const void* w1, const void* w2, void* dx_partial,
                        float* dw1, float* dw2, float* dgates, void* scratch, size_t scratch_bytes,
                        mtl_stream_t stream);
 

@@ -143,15 +143,15 @@ def mtl_reduce(partials, bias, residual, out, rows, cols, row_begin=0, row_end=N
                             rows if row_end is None else row_end, _stream(stream)), "mtl_reduce")
 
 
-def mtl_mlp_fwd(cfg, h, w1, b1, w2, z, a, partial, scratch=None, scratch_bytes=None, stream=None):
-    _check(lib().mtl_mlp_fwd(ctypes.byref(cfg), _ptr(h), _ptr(w1), _ptr(b1), _ptr(w2), _ptr(z), _ptr(a),
+def mtl_mlp_fwd(cfg, h, w1, b1, w2, gz, a, partial, scratch=None, scratch_bytes=None, stream=None):
+    _check(lib().mtl_mlp_fwd(ctypes.byref(cfg), _ptr(h), _ptr(w1), _ptr(b1), _ptr(w2), _ptr(gz), _ptr(a),
                              _ptr(partial), _ptr(scratch), _nbytes(scratch, scratch_bytes), _stream(stream)),
            "mtl_mlp_fwd")
 
 
-def mtl_mlp_bwd(cfg, dy, h, z, a, w1, w2, dh_partial, dw1, db1, dw2, db2, scratch, scratch_bytes=None, stream=None):
+def mtl_mlp_bwd(cfg, dy, h, gz, a, w1, w2, dh_partial, dw1, db1, dw2, db2, scratch, scratch_bytes=None, stream=None):
     nbytes = scratch.numel() * scratch.element_size() if scratch_bytes is None else scratch_bytes
-    _check(lib().mtl_mlp_bwd(ctypes.byref(cfg), _ptr(dy), _ptr(h), _ptr(z), _ptr(a), _ptr(w1), _ptr(w2),
+    _check(lib().mtl_mlp_bwd(ctypes.byref(cfg), _ptr(dy), _ptr(h), _ptr(gz), _ptr(a), _ptr(w1), _ptr(w2),
                              _ptr(dh_partial), _ptr(dw1), _ptr(db1), _ptr(dw2), _ptr(db2), _ptr(scratch), nbytes,
                              _stream(stream)), "mtl_mlp_bwd")
 
@@ -190,17 +190,17 @@ def mtl_moe_permute(cfg, topk_idx, counts, offsets, perm_token, perm_slot, slot_
                                  _ptr(perm_slot), _ptr(slot_row), _stream(stream)), "mtl_moe_permute")
 
 
-def mtl_moe_fwd(cfg, x, offsets, perm_token, slot_row, gates, w1, w2, xp, z, a, ye, y_partial, stream=None):
+def mtl_moe_fwd(cfg, x, offsets, perm_token, slot_row, gates, w1, w2, xp, gz, a, ye, y_partial, stream=None):
     _check(lib().mtl_moe_fwd(ctypes.byref(cfg), _ptr(x), _ptr(offsets), _ptr(perm_token), _ptr(slot_row),
-                             _ptr(gates), _ptr(w1), _ptr(w2), _ptr(xp), _ptr(z), _ptr(a), _ptr(ye), _ptr(y_partial),
+                             _ptr(gates), _ptr(w1), _ptr(w2), _ptr(xp), _ptr(gz), _ptr(a), _ptr(ye), _ptr(y_partial),
                              _stream(stream)), "mtl_moe_fwd")
 
 
-def mtl_moe_bwd(cfg, dy, offsets, perm_token, perm_slot, slot_row, gates, xp, z, a, ye, w1, w2, dx_partial, dw1,
+def mtl_moe_bwd(cfg, dy, offsets, perm_token, perm_slot, slot_row, gates, xp, gz, a, ye, w1, w2, dx_partial, dw1,
                 dw2, dgates, scratch, scratch_bytes=None, stream=None):
     nbytes = scratch.numel() * scratch.element_size() if scratch_bytes is None else scratch_bytes
     _check(lib().mtl_moe_bwd(ctypes.byref(cfg), _ptr(dy), _ptr(offsets), _ptr(perm_token), _ptr(perm_slot),
-                             _ptr(slot_row), _ptr(gates), _ptr(xp), _ptr(z), _ptr(a), _ptr(ye), _ptr(w1), _ptr(w2),
+                             _ptr(slot_row), _ptr(gates), _ptr(xp), _ptr(gz), _ptr(a), _ptr(ye), _ptr(w1), _ptr(w2),
                              _ptr(dx_partial), _ptr(dw1), _ptr(dw2), _ptr(dgates), _ptr(scratch), nbytes,
                              _stream(stream)), "mtl_moe_bwd")
 

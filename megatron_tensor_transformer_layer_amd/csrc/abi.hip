@@ -352,11 +352,11 @@ mtl_status mtl_reduce(int32_t t, const void* const* partials, const void* bias, 
                                     reinterpret_cast<hipStream_t>(stream)));
 }
 
-mtl_status mtl_mlp_fwd(const mtl_layer_cfg* c, const void* h, const void* w1, const void* b1, const void* w2, void* z,
+mtl_status mtl_mlp_fwd(const mtl_layer_cfg* c, const void* h, const void* w1, const void* b1, const void* w2, void* gz,
                        void* a, void* partial, void* scratch, size_t scratch_bytes, mtl_stream_t stream) {
   mtl_status st = mtl_validate(c);
   if (st != MTL_OK) return st;
-  if ((st = check_ptrs(h, w1, b1, w2, z, a, partial)) != MTL_OK) return st;
+  if ((st = check_ptrs(h, w1, b1, w2, gz, a, partial)) != MTL_OK) return st;
   const Dims d = dims_of(c);
   MlpFwdScratch ws{};
   if (is_fp8(c)) {
@@ -366,14 +366,14 @@ mtl_status mtl_mlp_fwd(const mtl_layer_cfg* c, const void* h, const void* w1, co
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
 
   if (is_fp8(c)) {
-    // z = h . w1 + b1, a = GeLU(z); partial = a . w2 (a re-quantised from bf16)
+    // z = h . w1 + b1: gz = GeLU'(z), a = GeLU(z); partial = a . w2 (a re-quantised from bf16)
     MTL_TRY(quantize({{h, &ws.h}, {w1, &ws.w1_t}, {w2, &ws.w2_t}}, ws.amax_ws, s));
-    MTL_TRY(gemm8(ws.h, ws.h.q, ws.w1_t, ws.w1_t.qt, d.S, d.f_l, d.h, z, d.f_l, EPI_BIAS_GELU, s, b1, a));
+    MTL_TRY(gemm8(ws.h, ws.h.q, ws.w1_t, ws.w1_t.qt, d.S, d.f_l, d.h, gz, d.f_l, EPI_BIAS_GELU, s, b1, a));
     MTL_TRY(quantize({{a, &ws.a}}, ws.amax_ws, s));
     MTL_TRY(gemm8(ws.a, ws.a.q, ws.w2_t, ws.w2_t.qt, d.S, d.h, d.f_l, partial, d.h, EPI_BF16, s));
     return MTL_OK;
   }
-  GemmArgs g = gemm(h, d.h, w1, d.f_l, d.S, d.f_l, d.h, z, d.f_l);
+  GemmArgs g = gemm(h, d.h, w1, d.f_l, d.S, d.f_l, d.h, gz, d.f_l);
   g.bias = static_cast<const uint16_t*>(b1);
   g.c2 = a;
   g.ldc2 = d.f_l;
@@ -398,12 +398,12 @@ static hipError_t attn_bias_grads(const Dims& d, const AttnScratch& ws, const vo
   return colsum_bf16(jobs, db_o ? 2 : 1, d.S, accum, ws.ws, s);
 }
 
-mtl_status mtl_mlp_bwd(const mtl_layer_cfg* c, const void* dy, const void* h, const void* z, const void* a,
+mtl_status mtl_mlp_bwd(const mtl_layer_cfg* c, const void* dy, const void* h, const void* gz, const void* a,
                        const void* w1, const void* w2, void* dh_partial, float* dw1, float* db1, float* dw2,
                        float* db2, void* scratch, size_t scratch_bytes, mtl_stream_t stream) {
   mtl_status st = mtl_validate(c);
   if (st != MTL_OK) return st;
-  if ((st = check_ptrs(dy, h, z, a, w1, w2, dh_partial, dw1, db1, dw2, scratch)) != MTL_OK) return st;
+  if ((st = check_ptrs(dy, h, gz, a, w1, w2, dh_partial, dw1, db1, dw2, scratch)) != MTL_OK) return st;
   if (db2 && !aligned16(db2)) return MTL_E_ALIGN;
   const Dims d = dims_of(c);
   MlpScratch ws;
@@ -415,7 +415,7 @@ mtl_status mtl_mlp_bwd(const mtl_layer_cfg* c, const void* dy, const void* h, co
   if (is_fp8(c)) {
     // E5M2 gradients, E4M3 activations and weights; wgrad operands transposed
     MTL_TRY(quantize({{dy, &ws.dy}, {w2, &ws.w2}, {a, &ws.a_t}}, ws.amax_ws, s));
-    MTL_TRY(gemm8(ws.dy, ws.dy.q, ws.w2, ws.w2.q, d.S, d.f_l, d.h, ws.dz, d.f_l, EPI_DGELU, s, nullptr, nullptr, z));
+    MTL_TRY(gemm8(ws.dy, ws.dy.q, ws.w2, ws.w2.q, d.S, d.f_l, d.h, ws.dz, d.f_l, EPI_DGELU, s, nullptr, nullptr, gz));
     MTL_TRY(gemm8(ws.a_t, ws.a_t.qt, ws.dy, ws.dy.qt, d.f_l, d.h, d.S, dw2, d.h, wepi, s));
     MTL_TRY(quantize({{ws.dz, &ws.dz8}, {h, &ws.h_t}, {w1, &ws.w1}}, ws.amax_ws, s));
     MTL_TRY(gemm8(ws.h_t, ws.h_t.qt, ws.dz8, ws.dz8.qt, d.h, d.f_l, d.S, dw1, d.f_l, wepi, s));
@@ -423,11 +423,11 @@ mtl_status mtl_mlp_bwd(const mtl_layer_cfg* c, const void* dy, const void* h, co
     MTL_TRY(gemm8(ws.dz8, ws.dz8.q, ws.w1, ws.w1.q, d.S, d.h, d.f_l, dh_partial, d.h, EPI_BF16, s));
     return MTL_OK;
   }
-  // dz = (dy . w2^T) * GeLU'(z), with the independent dw2 = a^T . dy in the same
+  // dz = (dy . w2^T) * gz, gz = GeLU'(z), with the independent dw2 = a^T . dy in the same
   // launch; the wgrad tiles go first, so their fp32 output drains under the
   // dgrad tiles' main loops
   GemmArgs g = gemm(dy, d.h, w2, d.h, d.S, d.f_l, d.h, ws.dz, d.f_l);
-  g.aux = static_cast<const uint16_t*>(z);
+  g.aux = static_cast<const uint16_t*>(gz);
   g.ld_aux = d.f_l;
   GemmArgs g2 = gemm(a, d.f_l, dy, d.h, d.f_l, d.h, d.S, dw2, d.h);
   MTL_TRY(gemm_bf16_pair(g2, GEMM_WGRAD, wepi, g, GEMM_DGRAD, EPI_DGELU, s));
@@ -640,17 +640,17 @@ mtl_status mtl_moe_permute(const mtl_moe_cfg* c, const int32_t* topk_idx, int32_
 }
 
 mtl_status mtl_moe_fwd(const mtl_moe_cfg* c, const void* x, const int32_t* offsets, const int32_t* perm_token,
-                       const int32_t* slot_row, const float* gates, const void* w1, const void* w2, void* xp, void* z,
+                       const int32_t* slot_row, const float* gates, const void* w1, const void* w2, void* xp, void* gz,
                        void* a, void* ye, void* y_partial, mtl_stream_t stream) {
   mtl_status st = mtl_moe_validate(c);
   if (st != MTL_OK) return st;
-  if ((st = check_ptrs(x, offsets, perm_token, slot_row, gates, w1, w2, xp, z, a, ye, y_partial)) != MTL_OK) return st;
+  if ((st = check_ptrs(x, offsets, perm_token, slot_row, gates, w1, w2, xp, gz, a, ye, y_partial)) != MTL_OK) return st;
   const MoeDims d = moe_dims(c);
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
 
   MTL_TRY(moe_gather(static_cast<const uint16_t*>(x), perm_token, offsets, (int)d.El, d.nmax, d.h,
                      static_cast<uint16_t*>(xp), s));
-  // z = xp_e . w1_e, a = GeLU(z)   (the grid covers N_max rows; M carries N_max)
+  // z = xp_e . w1_e: gz = GeLU'(z), a = GeLU(z)   (the grid covers N_max rows; M carries N_max)
   GemmArgs g = grouped(d, GROUP_M, offsets, d.h * d.f, 0);
   g.a = static_cast<const uint16_t*>(xp);
   g.lda = d.h;
@@ -659,7 +659,7 @@ mtl_status mtl_moe_fwd(const mtl_moe_cfg* c, const void* x, const int32_t* offse
   g.M = (int)d.nmax;
   g.N = (int)d.f;
   g.K = (int)d.h;
-  g.c = z;
+  g.c = gz;
   g.ldc = d.f;
   g.c2 = a;
   g.ldc2 = d.f;
@@ -683,12 +683,12 @@ mtl_status mtl_moe_fwd(const mtl_moe_cfg* c, const void* x, const int32_t* offse
 
 mtl_status mtl_moe_bwd(const mtl_moe_cfg* c, const void* dy, const int32_t* offsets, const int32_t* perm_token,
                        const int32_t* perm_slot, const int32_t* slot_row, const float* gates, const void* xp,
-                       const void* z, const void* a, const void* ye, const void* w1, const void* w2, void* dx_partial,
+                       const void* gz, const void* a, const void* ye, const void* w1, const void* w2, void* dx_partial,
                        float* dw1, float* dw2, float* dgates, void* scratch, size_t scratch_bytes,
                        mtl_stream_t stream) {
   mtl_status st = mtl_moe_validate(c);
   if (st != MTL_OK) return st;
-  if ((st = check_ptrs(dy, offsets, perm_token, perm_slot, slot_row, gates, xp, z, a, ye, w1, w2, dx_partial, dw1,
+  if ((st = check_ptrs(dy, offsets, perm_token, perm_slot, slot_row, gates, xp, gz, a, ye, w1, w2, dx_partial, dw1,
                        dw2, dgates, scratch)) != MTL_OK)
     return st;
   const MoeDims d = moe_dims(c);
@@ -699,7 +699,7 @@ mtl_status mtl_moe_bwd(const mtl_moe_cfg* c, const void* dy, const int32_t* offs
 
   MTL_TRY(moe_combine_bwd(static_cast<const uint16_t*>(dy), static_cast<const uint16_t*>(ye), perm_token, perm_slot,
                           slot_row, offsets, (int)d.El, d.nmax, gates, (int)d.T, (int)d.k, d.h, ws.dye, dgates, s));
-  // dz = (dye_e . w2_e^T) * GeLU'(z)
+  // dz = (dye_e . w2_e^T) * gz, gz = GeLU'(z)
   GemmArgs g = grouped(d, GROUP_M, offsets, d.f * d.h, 0);
   g.a = ws.dye;
   g.lda = d.h;
@@ -710,7 +710,7 @@ mtl_status mtl_moe_bwd(const mtl_moe_cfg* c, const void* dy, const int32_t* offs
   g.K = (int)d.h;
   g.c = ws.dz;
   g.ldc = d.f;
-  g.aux = static_cast<const uint16_t*>(z);
+  g.aux = static_cast<const uint16_t*>(gz);
   g.ld_aux = d.f;
   MTL_TRY(gemm_bf16(g, GEMM_DGRAD, EPI_DGELU, s));
   // dw2[e] = a_e^T . dye_e   (K = the expert's rows; K carries N_max for the range check)

@@ -429,7 +429,7 @@ __device__ __forceinline__ void gemm_tile(GemmArgs p, const int bid, LDS_AS char
   }
   const int lrow = lane & 31, lgrp = lane >> 5;
   const int mw = m0 + wm * WM, nw = n0 + wn * WN;
-  // GeLU': z for the whole wave sub-tile, in the accumulator layout (4 columns
+  // GeLU'(z) for the whole wave sub-tile, in the accumulator layout (4 columns
   // per load), requested before the last MFMAs so that the loads land under
   // them instead of one row block at a time in the epilogue.
   u32x2 zr[EPI == EPI_DGELU ? TM : 1][TN][4];
@@ -454,8 +454,8 @@ __device__ __forceinline__ void gemm_tile(GemmArgs p, const int bid, LDS_AS char
   // j*32 + 8g + 4*lgrp .. +3 of the wave's WM x WN sub-tile.  Values are first
   // finished in registers (bias, GeLU, GeLU'), then written to the wave's own slice of
   // the (now idle) LDS stages and read back row by row, so every global store
-  // is 16 bytes per lane over whole rows.  fp32 results go in passes of IPP
-  // row blocks.
+  // is 16 bytes per lane over whole rows.  fp32 results, and the two outputs
+  // of bias + GeLU, go in passes of IPP row blocks.
   __syncthreads();  // all waves are done with the last slab
   constexpr int HALF = ML::NWAVES / 2;  // waves whose staging slices lie in each stage
   constexpr int REGION = ML::STAGE / HALF;
@@ -466,7 +466,12 @@ __device__ __forceinline__ void gemm_tile(GemmArgs p, const int bid, LDS_AS char
   constexpr int E = F32STAGE ? 4 : 2;
   constexpr int RB = WN * E;                 // bytes per staged row
   constexpr int CPR = RB / 16;               // 16-byte chunks per row
-  constexpr int IPP = (REGION / (32 * RB)) < TM ? (REGION / (32 * RB)) : TM;
+  // Outputs staged per pass: with bias + GeLU, C receives GeLU'(z) and C2
+  // GeLU(z) of the biased sum z, both from one evaluation of the normal CDF and
+  // density, staged side by side (each pass then covers half as many rows).
+  constexpr int NOUT = EPI == EPI_BIAS_GELU ? 2 : 1;
+  constexpr int IPP = (REGION / (NOUT * 32 * RB)) < TM ? (REGION / (NOUT * 32 * RB)) : TM;
+  constexpr int OUTB = IPP * 32 * RB;        // staged bytes of one output per pass
   static_assert(IPP >= 1, "epilogue staging does not fit");
 
   // fp8: the product of the two operands' dequantisation factors
@@ -484,64 +489,72 @@ __device__ __forceinline__ void gemm_tile(GemmArgs p, const int bid, LDS_AS char
       }
   }
 
-  // out selects the output: 0 -> C, 1 -> C2 (GeLU of the biased sum).
 #pragma unroll
-  for (int out = 0; out < (EPI == EPI_BIAS_GELU ? 2 : 1); ++out) {
+  for (int i0 = 0; i0 < TM; i0 += IPP) {
+    // register phase
 #pragma unroll
-    for (int i0 = 0; i0 < TM; i0 += IPP) {
-      // register phase
+    for (int ii = 0; ii < IPP; ++ii) {
+      const int i = i0 + ii;
+      const int rl = ii * 32 + lrow;
 #pragma unroll
-      for (int ii = 0; ii < IPP; ++ii) {
-        const int i = i0 + ii;
-        const int rl = ii * 32 + lrow;
+      for (int j = 0; j < TN; ++j)
 #pragma unroll
-        for (int j = 0; j < TN; ++j)
+        for (int g = 0; g < 4; ++g) {
+          float v[4] = {acc[i][j][4 * g + 0], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]};
+          if constexpr (F8 != 0) {
 #pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            float v[4] = {acc[i][j][4 * g + 0], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]};
-            if constexpr (F8 != 0) {
+            for (int e = 0; e < 4; ++e) v[e] *= dq;
+          }
+          if constexpr (HAS_BIAS) {
+            v[0] += bf16_lo(braw[j][g][0]);
+            v[1] += bf16_hi(braw[j][g][0]);
+            v[2] += bf16_lo(braw[j][g][1]);
+            v[3] += bf16_hi(braw[j][g][1]);
+          }
+          float ge[4];  // GeLU(z), the second output
+          if constexpr (EPI == EPI_BIAS_GELU) {
 #pragma unroll
-              for (int e = 0; e < 4; ++e) v[e] *= dq;
-            }
-            if constexpr (HAS_BIAS) {
-              v[0] += bf16_lo(braw[j][g][0]);
-              v[1] += bf16_hi(braw[j][g][0]);
-              v[2] += bf16_lo(braw[j][g][1]);
-              v[3] += bf16_hi(braw[j][g][1]);
-            }
-            if (out == 1) {
-#pragma unroll
-              for (int e = 0; e < 4; ++e) v[e] = gelu_f(v[e]);
-            }
-            if constexpr (EPI == EPI_DGELU) {
-              v[0] *= gelu_grad_f(bf16_lo(zr[i][j][g][0]));
-              v[1] *= gelu_grad_f(bf16_hi(zr[i][j][g][0]));
-              v[2] *= gelu_grad_f(bf16_lo(zr[i][j][g][1]));
-              v[3] *= gelu_grad_f(bf16_hi(zr[i][j][g][1]));
-            }
-            const int col = j * 32 + 8 * g + 4 * lgrp;
-            if constexpr (F32STAGE) {
-              const int ch = col / 4;
-              const int pc = (ch + rl) % CPR;
-              *reinterpret_cast<LDS_AS f32x4*>(region + rl * RB + pc * 16) = f32x4{v[0], v[1], v[2], v[3]};
-            } else {
-              const int ch = col / 8;
-              const int pc = (ch + rl) % CPR;
-              *reinterpret_cast<LDS_AS u32x2*>(region + rl * RB + pc * 16 + (col & 7) * 2) =
-                  u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+            for (int e = 0; e < 4; ++e) {
+              float cdf, pdf;
+              normal_cdf_pdf(v[e], cdf, pdf);
+              ge[e] = v[e] * cdf;
+              v[e] = cdf + v[e] * pdf;  // GeLU'(z)
             }
           }
-      }
-      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-      // row phase: chunk idx of the IPP*32 staged rows
-      constexpr int TOTAL = IPP * 32 * CPR;
+          if constexpr (EPI == EPI_DGELU) {  // aux holds GeLU'(z)
+            v[0] *= bf16_lo(zr[i][j][g][0]);
+            v[1] *= bf16_hi(zr[i][j][g][0]);
+            v[2] *= bf16_lo(zr[i][j][g][1]);
+            v[3] *= bf16_hi(zr[i][j][g][1]);
+          }
+          const int col = j * 32 + 8 * g + 4 * lgrp;
+          if constexpr (F32STAGE) {
+            const int ch = col / 4;
+            const int pc = (ch + rl) % CPR;
+            *reinterpret_cast<LDS_AS f32x4*>(region + rl * RB + pc * 16) = f32x4{v[0], v[1], v[2], v[3]};
+          } else {
+            const int ch = col / 8;
+            const int pc = (ch + rl) % CPR;
+            const int o = rl * RB + pc * 16 + (col & 7) * 2;
+            *reinterpret_cast<LDS_AS u32x2*>(region + o) = u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+            if constexpr (NOUT == 2)
+              *reinterpret_cast<LDS_AS u32x2*>(region + OUTB + o) =
+                  u32x2{pack_bf16x2(ge[0], ge[1]), pack_bf16x2(ge[2], ge[3])};
+          }
+        }
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    // row phase: chunk idx of the IPP*32 staged rows of each output
+    constexpr int TOTAL = IPP * 32 * CPR;
+#pragma unroll
+    for (int out = 0; out < NOUT; ++out) {
 #pragma unroll
       for (int it = 0; it < (TOTAL + 63) / 64; ++it) {
         const int idx = it * 64 + lane;
         if (TOTAL % 64 == 0 || idx < TOTAL) {
           const int rl = idx / CPR, ch = idx % CPR;
           const int pc = (ch + rl) % CPR;
-          const u32x4 val = *reinterpret_cast<const LDS_AS u32x4*>(region + rl * RB + pc * 16);
+          const u32x4 val = *reinterpret_cast<const LDS_AS u32x4*>(region + out * OUTB + rl * RB + pc * 16);
           const int m = mw + i0 * 32 + rl;
           const int n = nw + ch * (16 / E);
           if (m < p.M && n < p.N) {
@@ -551,14 +564,15 @@ __device__ __forceinline__ void gemm_tile(GemmArgs p, const int bid, LDS_AS char
               if constexpr (EPI == EPI_F32_ACC) o += *reinterpret_cast<const f32x4*>(c);
               *reinterpret_cast<f32x4*>(c) = o;
             } else {
-              uint16_t* c = reinterpret_cast<uint16_t*>(out == 0 ? p.c : p.c2) + (int64_t)m * (out == 0 ? p.ldc : p.ldc2) + n;
+              uint16_t* c = reinterpret_cast<uint16_t*>(out == 0 ? p.c : p.c2) +
+                            (int64_t)m * (out == 0 ? p.ldc : p.ldc2) + n;
               *reinterpret_cast<u32x4*>(c) = val;
             }
           }
         }
       }
-      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
   }
 }
 

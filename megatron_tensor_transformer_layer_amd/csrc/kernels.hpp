@@ -10,8 +10,8 @@ namespace mtl {
 enum GemmEpi : int {
   EPI_BF16 = 0,       // C = acc                      (bf16)
   EPI_BF16_BIAS = 1,  // C = acc + bias[n]            (bf16)
-  EPI_BIAS_GELU = 2,  // C = acc + bias[n]; C2 = GeLU(C) (both bf16); bias may be null
-  EPI_DGELU = 3,      // C = acc * GeLU'(aux[m][n])   (bf16, aux bf16)
+  EPI_BIAS_GELU = 2,  // z = acc + bias[n]; C = GeLU'(z), C2 = GeLU(z) (both bf16); bias may be null
+  EPI_DGELU = 3,      // C = acc * aux[m][n], aux = GeLU'(z) as EPI_BIAS_GELU wrote it (bf16)
   EPI_F32 = 4,        // C = acc                      (fp32)
   EPI_F32_ACC = 5,    // C += acc                     (fp32)
 };
@@ -32,7 +32,7 @@ struct GemmArgs {
   const uint16_t* bias;  // [N] bf16 (EPI_BF16_BIAS, EPI_BIAS_GELU)
   void* c2;              // second output (EPI_BIAS_GELU)
   int64_t ldc2;
-  const uint16_t* aux;   // GeLU input Z (EPI_DGELU)
+  const uint16_t* aux;   // GeLU'(z) (EPI_DGELU)
   int64_t ld_aux;
   // Grouped (MoE experts): group e owns rows [offsets[e], offsets[e+1]).
   //  GROUP_M: those rows of A, C (and C2, aux) form expert e's M; B advances by

@@ -70,7 +70,7 @@ class RankState:
         self.qkv = empty_bf16(D.S, D.qkv_l, device=device)
         self.o = empty_bf16(D.S, D.o_l, device=device)
         self.lse = torch.empty(D.heads_l, D.S, dtype=torch.float32, device=device)
-        self.z = empty_bf16(D.S, D.f_l, device=device)
+        self.gz = empty_bf16(D.S, D.f_l, device=device)  # GeLU'(z)
         self.a = empty_bf16(D.S, D.f_l, device=device)
         self.p_attn = empty_bf16(D.S, D.h, device=device)
         self.p_mlp = empty_bf16(D.S, D.h, device=device)
@@ -92,11 +92,11 @@ class RankState:
                      self.p_attn, self.scratch)
 
     def mlp_fwd(self, h):
-        mtl_mlp_fwd(self.cfg, h, self.w["w1"], self.w["b1"], self.w["w2"], self.z, self.a, self.p_mlp,
+        mtl_mlp_fwd(self.cfg, h, self.w["w1"], self.w["b1"], self.w["w2"], self.gz, self.a, self.p_mlp,
                     self.scratch)
 
     def mlp_bwd(self, dy, h, want_db2=True):
-        mtl_mlp_bwd(self.cfg, dy, h, self.z, self.a, self.w["w1"], self.w["w2"], self.p_dh, self.dw1, self.db1,
+        mtl_mlp_bwd(self.cfg, dy, h, self.gz, self.a, self.w["w1"], self.w["w2"], self.p_dh, self.dw1, self.db1,
                     self.dw2, self.db2 if want_db2 else None, self.scratch)
 
     def attn_bwd(self, dh, x, want_db_o=True):
@@ -134,7 +134,7 @@ def run_sharded_layer(shape, tp: int, shards: list, x_bits, b_o_bits, b2_bits, d
     cat = lambda key, axis: np.concatenate([host_f64(getattr(r, key)) for r in ranks], axis=axis)
     return dict(
         y=host_f64(y), h=host_f64(h), dh=host_f64(dh), dx=host_f64(dx),
-        qkv=cat("qkv", 1), o=cat("o", 1), lse=cat("lse", 0), z=cat("z", 1), a=cat("a", 1),
+        qkv=cat("qkv", 1), o=cat("o", 1), lse=cat("lse", 0), gz=cat("gz", 1), a=cat("a", 1),
         dw_qkv=cat("dw_qkv", 1), db_qkv=cat("db_qkv", 0), dw_o=cat("dw_o", 0), dw1=cat("dw1", 1),
         db1=cat("db1", 0), dw2=cat("dw2", 0),
         db_o=host_f64(ranks[0].db_o), db2=host_f64(ranks[0].db2),

@@ -34,7 +34,7 @@ class MoeRank:
         self.perm_slot = torch.empty(N, **i32)
         self.slot_row = torch.empty(T, k, **i32)
         self.xp = torch.empty(N, h, **bf)
-        self.z = torch.empty(N, f, **bf)
+        self.gz = torch.empty(N, f, **bf)  # GeLU'(z)
         self.a = torch.empty(N, f, **bf)
         self.ye = torch.empty(N, h, **bf)
         self.y = torch.empty(T, h, **bf)
@@ -53,11 +53,11 @@ class MoeRank:
 
     def forward(self, x):
         mtl_moe_fwd(self.cfg, x, self.offsets, self.perm_token, self.slot_row, self.gates, self.w1, self.w2,
-                    self.xp, self.z, self.a, self.ye, self.y)
+                    self.xp, self.gz, self.a, self.ye, self.y)
 
     def backward(self, dy):
         mtl_moe_bwd(self.cfg, dy, self.offsets, self.perm_token, self.perm_slot, self.slot_row, self.gates,
-                    self.xp, self.z, self.a, self.ye, self.w1, self.w2, self.dx, self.dw1, self.dw2, self.dgates,
+                    self.xp, self.gz, self.a, self.ye, self.w1, self.w2, self.dx, self.dw1, self.dw2, self.dgates,
                     self.scratch)
 
     def step(self, logits, x, dy):

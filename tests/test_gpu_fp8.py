@@ -142,11 +142,11 @@ def test_fp8_layer_error_is_the_recipe_error(mtl, case):
     x, g = f64(full["x"]), f64(full["dy"])
     fwd = L.layer_forward(p, x, shape.heads, shape.micro_batch, residual)
     bwd = L.layer_backward(p, x, fwd, g, shape.heads, shape.micro_batch, residual)
-    ref_i = {**{k: fwd[k] for k in ("qkv", "h", "z", "a", "y")}, "dh": bwd["dh"],
+    ref_i = {**{k: fwd[k] for k in ("qkv", "h", "a", "y")}, "gz": L.gelu_grad(fwd["z"]), "dh": bwd["dh"],
              **{k: bwd[k] for k in ("dx", "dw_qkv", "db_qkv", "dw_o", "db_o", "dw1", "db1", "dw2", "db2")}}
     q = F8.sharded_layer(p, x, g, shape.heads, shape.tp, shape.micro_batch, residual, fq=_q4, gq=_q5)
     cat = lambda part, key, axis: np.concatenate([d[key] for d in q[part]], axis=axis)
-    ref_q = dict(y=q["y"], h=q["h"], dh=q["dh"], dx=q["dx"], qkv=cat("att", "qkv", 1), z=cat("mlp", "z", 1),
+    ref_q = dict(y=q["y"], h=q["h"], dh=q["dh"], dx=q["dx"], qkv=cat("att", "qkv", 1), gz=L.gelu_grad(cat("mlp", "z", 1)),
                  a=cat("mlp", "a", 1), dw_qkv=cat("attn_bwd", "dw_qkv", 1), db_qkv=cat("attn_bwd", "db_qkv", 0),
                  dw_o=cat("attn_bwd", "dw_o", 0), dw1=cat("mlp_bwd", "dw1", 1), db1=cat("mlp_bwd", "db1", 0),
                  dw2=cat("mlp_bwd", "dw2", 0), db_o=q["attn_bwd"][0]["db_o"], db2=q["mlp_bwd"][0]["db2"])
@@ -168,7 +168,7 @@ def test_fp8_gemms_on_identical_codes(mtl):
     """Every fp8 GEMM kind whose operands are call inputs -- so the device and
     the reference quantise the same bf16 values to the same codes (the cast is
     bit-exact) -- within the bf16 bound of the quantised-operand reference:
-    fwd E4M3 x E4M3 with bias (qkv) and with bias + GeLU (z, a); dgrad E5M2 x
+    fwd E4M3 x E4M3 with bias (qkv) and with bias + GeLU (GeLU'(z), a); dgrad E5M2 x
     E4M3 with GeLU' (through db1 = colsum(dz)); wgrad E4M3^T x E5M2 (dw2,
     dw_o).  Each call gets independent inputs, as in a real step."""
     import torch
@@ -187,8 +187,8 @@ def test_fp8_gemms_on_identical_codes(mtl):
     st.attn_fwd(x)
     st.mlp_fwd(h)
     torch.cuda.synchronize()
-    got = dict(qkv=host_f64(st.qkv), z=host_f64(st.z), a=host_f64(st.a))
-    st.z.copy_(bf16_dev(zb))
+    got = dict(qkv=host_f64(st.qkv), gz=host_f64(st.gz), a=host_f64(st.a))
+    st.gz.copy_(bf16_dev(synth.bf16_round_bits(L.gelu_grad(f64(zb)))))  # the saved GeLU'(z) of an independent z
     st.a.copy_(bf16_dev(ab))
     st.o.copy_(bf16_dev(ob))
     st.mlp_bwd(dy, h)
@@ -201,7 +201,7 @@ def test_fp8_gemms_on_identical_codes(mtl):
     fa = F8.rank_attn_forward(pr, X, shape.heads // t)
     fm = F8.rank_mlp_forward(pr, H)
     mb = F8.rank_mlp_backward(pr, DY, H, Z, A)
-    ref = dict(qkv=fa["qkv"], z=fm["z"], a=fm["a"], db1=mb["db1"], dw2=mb["dw2"],
+    ref = dict(qkv=fa["qkv"], gz=L.gelu_grad(fm["z"]), a=fm["a"], db1=mb["db1"], dw2=mb["dw2"],
                dw_o=F8.q4(O).T @ F8.q5(DH), db_o=DH.sum(axis=0))
     for k in ref:
         assert_bf16(k, got[k], ref[k])

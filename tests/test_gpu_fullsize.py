@@ -45,7 +45,7 @@ def test_rank_shard_full_size(mtl, workload):
     st.mlp_bwd(dy, h)
     st.attn_bwd(dh, x)
     torch.cuda.synchronize()
-    g = {k: host_f64(getattr(st, k)) for k in ("qkv", "o", "lse", "z", "a", "p_attn", "p_mlp", "p_dh", "p_dx",
+    g = {k: host_f64(getattr(st, k)) for k in ("qkv", "o", "lse", "gz", "a", "p_attn", "p_mlp", "p_dh", "p_dx",
                                                "dw_qkv", "db_qkv", "dw_o", "db_o", "dw1", "db1", "dw2", "db2")}
     del st
     torch.cuda.empty_cache()
@@ -66,7 +66,7 @@ def test_rank_shard_full_size(mtl, workload):
     # MLP forward on sampled rows
     z_r = H[rows] @ p["w1"] + p["b1"]
     a_r = L.gelu(z_r)
-    assert_bf16("z[rows]", g["z"][rows], z_r)
+    assert_bf16("gz[rows]", g["gz"][rows], L.gelu_grad(z_r))
     assert_bf16("a[rows]", g["a"][rows], a_r)
     assert_bf16("mlp partial[rows]", g["p_mlp"][rows], a_r @ p["w2"])
 
@@ -103,7 +103,7 @@ def test_fp8_rank_shard_full_size(mtl):
     configuration bench.py --precision fp8 times.  Every fp8 GEMM kind is
     checked where its operands are call inputs (so both sides quantise the same
     bf16 values to the same codes) against the fp64 product of the dequantised
-    codes: qkv in full, z and a on sampled rows, dw2 and dw_o on sampled
+    codes: qkv in full, GeLU'(z) and a on sampled rows, dw2 and dw_o on sampled
     columns, db1 (a column sum of the dgrad output dz) on sampled columns."""
     import torch
     from oracle import fp8_layer as F8
@@ -123,8 +123,8 @@ def test_fp8_rank_shard_full_size(mtl):
     st.attn_fwd(x)
     st.mlp_fwd(h)
     torch.cuda.synchronize()
-    g = dict(qkv=host_f64(st.qkv), z=host_f64(st.z[ROWS]), a=host_f64(st.a[ROWS]))
-    st.z.copy_(bf16_dev(zb))
+    g = dict(qkv=host_f64(st.qkv), gz=host_f64(st.gz[ROWS]), a=host_f64(st.a[ROWS]))
+    st.gz.copy_(bf16_dev(synth.bf16_round_bits(L.gelu_grad(f64(zb)))))  # the saved GeLU'(z) of an independent z
     st.a.copy_(bf16_dev(ab))
     st.o.copy_(bf16_dev(ob))
     st.mlp_bwd(dy, h)
@@ -141,7 +141,7 @@ def test_fp8_rank_shard_full_size(mtl):
     assert_bf16("qkv", g["qkv"], Xq @ q4(p["w_qkv"]) + p["b_qkv"])
     del Xq
     z_r = q4(f64(hb))[ROWS] @ q4(p["w1"]) + p["b1"]
-    assert_bf16("z[rows]", g["z"], z_r)
+    assert_bf16("gz[rows]", g["gz"], L.gelu_grad(z_r))
     assert_bf16("a[rows]", g["a"], L.gelu(z_r))
     DYq = q5(f64(inp["dy"]))
     ch = _cols(shape.hidden)

@@ -4,14 +4,16 @@ The small layer cases run every GEMM on 128 x 128 tiles; the full-size cases
 reach the 256-wide tiles only with sizes that are multiples of 256.  Here one
 MLP shard has 4000 tokens (15 full row tiles and 160 rows) and a local ffn of
 3896 (15 full column tiles and 56 columns), so that the fc1 forward (bias +
-GeLU, two outputs) and the fc2 dgrad with GeLU' run on 16 x 16 = 256 tiles of
-256 x 256 whose last tile row and column are partial.  Every output is
-compared in full with the fp64 oracle of the rank's MLP share.
+GeLU, writing GeLU'(z) and GeLU(z)) and the fc2 dgrad with GeLU' run on
+16 x 16 = 256 tiles of 256 x 256 whose last tile row and column are partial.
+Every output is compared in full with the fp64 oracle of the rank's MLP
+share.
 """
 import numpy as np
 import pytest
 
 import synth
+from oracle import layer as L
 from oracle import shard as S
 from tests.parity_util import assert_bf16, f64
 
@@ -31,14 +33,14 @@ def test_mlp_ragged_256_tiles(mtl):
     st.mlp_fwd(h)
     st.mlp_bwd(dy, h)
     torch.cuda.synchronize()
-    g = {k: host_f64(getattr(st, k)) for k in ("z", "a", "p_mlp", "p_dh", "dw1", "db1", "dw2", "db2")}
+    g = {k: host_f64(getattr(st, k)) for k in ("gz", "a", "p_mlp", "p_dh", "dw1", "db1", "dw2", "db2")}
     del st
     torch.cuda.empty_cache()
 
     pr = {k: f64(inp[k]) for k in ("w1", "b1", "w2")}
     H, DY = f64(hb), f64(inp["dy"])
     fw = S.rank_mlp_forward(pr, H)
-    assert_bf16("z", g["z"], fw["z"])
+    assert_bf16("gz", g["gz"], L.gelu_grad(fw["z"]))
     assert_bf16("a", g["a"], fw["a"])
     assert_bf16("mlp partial", g["p_mlp"], fw["partial"])
     bw = S.rank_mlp_backward(pr, DY, H, fw["z"], fw["a"])

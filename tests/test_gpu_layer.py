@@ -1,7 +1,7 @@
 """Parity of the whole tensor-parallel layer step on the GPU against the fp64
 oracle of the unsharded layer: all t rank shards run on one device through the
 C ABI, the four reductions add their partials, and every output (Y, dX, H, dH,
-the concatenated QKV/O/Z/A, every weight and bias gradient) must match the
+the concatenated QKV/O/A and GeLU'(Z), every weight and bias gradient) must match the
 oracle to the bf16 tolerance."""
 import numpy as np
 import pytest
@@ -42,8 +42,9 @@ def test_layer_matches_oracle(mtl, case):
     x, g = f64(full["x"]), f64(full["dy"])
     fwd = L.layer_forward(p, x, shape.heads, shape.micro_batch, residual)
     bwd = L.layer_backward(p, x, fwd, g, shape.heads, shape.micro_batch, residual)
-    for k in ("qkv", "o", "lse", "h", "z", "a", "y"):
+    for k in ("qkv", "o", "lse", "h", "a", "y"):
         assert_bf16(k, got[k], fwd[k])
+    assert_bf16("gz", got["gz"], L.gelu_grad(fwd["z"]))
     assert_bf16("dh", got["dh"], bwd["dh"])
     for k in ("dx", "dw_qkv", "db_qkv", "dw_o", "db_o", "dw1", "db1", "dw2", "db2"):
         assert_bf16(k, got[k], bwd[k])

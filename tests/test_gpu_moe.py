@@ -7,6 +7,7 @@ import numpy as np
 import pytest
 
 import synth
+from oracle import layer as L
 from oracle import moe as M
 from tests.parity_util import assert_bf16, f64
 
@@ -97,7 +98,8 @@ def test_moe_rank_matches_oracle(mtl, case):
     # the gather moves bf16 rows unchanged
     assert np.array_equal(f64(_host(r.xp)[:n]), fwd["xp"])
 
-    for key in ("z", "a", "ye"):
+    assert_bf16("gz", f64(_host(r.gz)[:n]), L.gelu_grad(fwd["z"]))
+    for key in ("a", "ye"):
         assert_bf16(key, f64(_host(getattr(r, key))[:n]), fwd[key])
     assert_bf16("y", f64(_host(r.y)), fwd["y"])
     assert_bf16("dx", f64(_host(r.dx)), bwd["dx"])
@@ -121,7 +123,7 @@ def test_moe_is_deterministic(mtl):
     n = int(_host(a.offsets)[-1])
     for key in ("idx", "gates", "offsets", "slot_row", "y", "dx", "dw1", "dw2", "dgates"):
         assert np.array_equal(_host(getattr(a, key)), _host(getattr(b, key))), key
-    for key in ("perm_token", "perm_slot", "xp", "z", "a", "ye"):  # rows past N are never written
+    for key in ("perm_token", "perm_slot", "xp", "gz", "a", "ye"):  # rows past N are never written
         assert np.array_equal(_host(getattr(a, key))[:n], _host(getattr(b, key))[:n]), key
 
 

@@ -9,7 +9,7 @@ local one).  Their weights come from the host generator; the other 14 local
 experts get device-drawn weights that no check reads.
 
 * Every token whose local slots all fall in experts {0, 15} (and the token
-  with no local slot) is checked in full: its z, a, ye rows, its combined
+  with no local slot) is checked in full: its GeLU'(z), a, ye rows, its combined
   output y, its input gradient dx and its gate gradients.  Those tokens' rows
   form an exact sub-problem for the oracle.
 * dW1[e][:, c] and dW2[e][c, :] for sampled ffn columns c of both experts:
@@ -20,6 +20,7 @@ import numpy as np
 import pytest
 
 import synth
+from oracle import layer as L
 from oracle import moe as M
 from tests.parity_util import assert_bf16, f64
 
@@ -104,8 +105,9 @@ def test_moe_rank0_full_size(mtl):
     sub = dict(perm_token=sptok, perm_slot=spslot, offsets=sub_off, gates=gates, **ef)
     bwd = M.moe_backward(x, W1, W2, sub, dy)
     del W1, W2
-    for key in ("z", "a", "ye"):
-        assert_bf16(key, f64(_host(getattr(r, key)[torch.from_numpy(rows).cuda()])), ef[key])
+    exp = dict(gz=L.gelu_grad(ef["z"]), a=ef["a"], ye=ef["ye"])
+    for key in exp:
+        assert_bf16(key, f64(_host(getattr(r, key)[torch.from_numpy(rows).cuda()])), exp[key])
     assert_bf16("y", f64(_host(r.y))[toks], y[toks])
     assert_bf16("dx", f64(_host(r.dx))[toks], bwd["dx"][toks])
     assert_bf16("dgates", _host(r.dgates)[toks], bwd["dgates"][toks])
