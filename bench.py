@@ -37,6 +37,9 @@ def parse():
     ap.add_argument("--rank", type=int, default=0)
     ap.add_argument("--precision", choices=("bf16", "fp8"), default="bf16",
                     help="fp8: the linears' GEMMs on per-tensor scaled E4M3/E5M2 codes (--fp8-format hybrid)")
+    ap.add_argument("--sp", action="store_true",
+                    help="sequence parallel: X, H, dY, dH arrive as row shares and are gathered in place "
+                         "(mtl_allgather_rows) before each column-parallel linear")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-seq", type=int, default=4096)
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -253,7 +256,7 @@ def main():
         return
     import torch
     import synth
-    from megatron_tensor_transformer_layer_amd import mtl_reduce
+    from megatron_tensor_transformer_layer_amd import mtl_allgather_rows, mtl_reduce
     from megatron_tensor_transformer_layer_amd.layer import RankState, bf16_dev, empty_bf16
 
     if not torch.cuda.is_available():
@@ -282,6 +285,15 @@ def main():
     dh = empty_bf16(D.S, D.h)
     dx = empty_bf16(D.S, D.h)
     r0, r1 = r * D.S // t, (r + 1) * D.S // t
+    # sequence parallel: the peers' full-size buffers of X, H, dY, dH, whose own
+    # shares this rank's in-place all-gathers copy (resident copies on one GPU)
+    sp_peers = {k: [torch.randn(D.S, D.h, device="cuda", generator=g).to(torch.bfloat16) for _ in range(t - 1)]
+                for k in ("x", "h", "dy", "dh")} if args.sp else None
+
+    def gather(key, buf):
+        if args.sp:
+            bufs = sp_peers[key][:r] + [buf] + sp_peers[key][r:]
+            mtl_allgather_rows(bufs, buf, D.S, D.h, r)
 
     # rows of H / dH outside this rank's share come from the all-gather; fill them once
     st.attn_fwd(x)
@@ -295,8 +307,10 @@ def main():
     mlp_ev = []
 
     def step(record=False):
+        gather("x", x)
         st.attn_fwd(x)
         mtl_reduce([st.p_attn] + peers["attn"], b_o, None, h, D.S, D.h, r0, r1)
+        gather("h", h)
         if record:
             e0, e1 = ev(), ev()
             e0.record()
@@ -305,8 +319,10 @@ def main():
             e1.record()
             mlp_ev.append((e0, e1))
         mtl_reduce([st.p_mlp] + peers["mlp"], b2, None, y, D.S, D.h, r0, r1)
+        gather("dy", dy)
         st.mlp_bwd(dy, h)
         mtl_reduce([st.p_dh] + peers["dh"], None, None, dh, D.S, D.h, r0, r1)
+        gather("dh", dh)
         st.attn_bwd(dh, x)
         mtl_reduce([st.p_dx] + peers["dx"], None, None, dx, D.S, D.h, r0, r1)
 
@@ -358,8 +374,11 @@ def main():
                                f"({shape.heads // t} local), ffn {shape.ffn} ({shape.ffn // t} local), "
                                f"seq {shape.seq}, micro-batch {shape.micro_batch}"
                                + (", fp8 hybrid (E4M3 activations/weights, E5M2 gradients, per-tensor current "
-                                  "scaling; attention bf16)" if fp8 else ""),
-                   "global_batch": shape.micro_batch, "seq_len": shape.seq, "parallelism": f"tp{t}-rank{r}-of-1gpu"},
+                                  "scaling; attention bf16)" if fp8 else "")
+                               + (", sequence parallel (reduce-scatter shares, in-place all-gathers of X, H, dY, dH)"
+                                  if args.sp else ""),
+                   "global_batch": shape.micro_batch, "seq_len": shape.seq,
+                   "parallelism": f"tp{t}{'-sp' if args.sp else ''}-rank{r}-of-1gpu"},
         "pct_of_peak": round(100 * fl["total"] / (ms / 1e3) / 1e12 / peak, 2),
         "pct_of_bf16_peak": round(100 * fl["total"] / (ms / 1e3) / 1e12 / PEAK_BF16_TFLOPS, 2),
         "step_ms_p50": round(float(np.percentile(per_step, 50)), 4),

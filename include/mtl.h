@@ -128,6 +128,23 @@ mtl_status mtl_attn_fwd(const mtl_layer_cfg* cfg, const void* x, const void* w_q
 mtl_status mtl_reduce(int32_t t, const void* const* partials, const void* bias, const void* residual, void* out,
                       int64_t rows, int64_t cols, int64_t row_begin, int64_t row_end, mtl_stream_t stream);
 
+/* The sequence-parallel all-gather stand-in.  With sequence parallelism
+ * (ai.lansai.wang/82226, the table of parallelism strategies: its EP row asks
+ * for it whenever TP and EP are combined; the pages give no algorithm) the
+ * all-reduce after a row-parallel linear becomes a reduce-scatter -- each rank
+ * keeps the rows [rank*rows/t, (rank+1)*rows/t) of the sum, which is
+ * mtl_reduce with that row range -- and the full tensor is gathered again
+ * before the next column-parallel linear.  Each rank holds a full-size
+ * [rows, cols] bf16 buffer with its own share in place; this call copies the
+ * t-1 peer shares, rows [i*rows/t, (i+1)*rows/t) of bufs[i] for every i !=
+ * rank, into the same rows of `out` (normally bufs[rank]: an in-place gather).
+ * `bufs` is a HOST array of t device pointers; bufs[rank] is not read and may
+ * be NULL.  rows % t == 0, cols % 8 == 0, 1 <= t <= 16; the rows of `out` in
+ * the caller's own share are not touched.  Errors: MTL_E_RANK for rank outside
+ * [0, t), MTL_E_UNSUPPORTED when a peer buffer is `out`. */
+mtl_status mtl_allgather_rows(int32_t t, int32_t rank, const void* const* bufs, void* out, int64_t rows, int64_t cols,
+                              mtl_stream_t stream);
+
 /* MLP half of the rank's forward (column-parallel fc1 with fused GeLU,
  * row-parallel fc2), with z = h . w1 + b1 in fp32:
  *   gz      = GeLU'(z)        [S, f/t] bf16 (saved: the backward needs z only

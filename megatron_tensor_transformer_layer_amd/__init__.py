@@ -50,6 +50,7 @@ _SIGS = {
     "mtl_workspace_bytes": (ctypes.c_int, [_CFG, ctypes.POINTER(_SZ)]),
     "mtl_attn_fwd": (ctypes.c_int, [_CFG, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "mtl_reduce": (ctypes.c_int, [_I32, ctypes.POINTER(_P), _P, _P, _P, _I64, _I64, _I64, _I64, _P]),
+    "mtl_allgather_rows": (ctypes.c_int, [_I32, _I32, ctypes.POINTER(_P), _P, _I64, _I64, _P]),
     "mtl_mlp_fwd": (ctypes.c_int, [_CFG, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "mtl_mlp_bwd": (ctypes.c_int, [_CFG, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "mtl_attn_bwd": (ctypes.c_int, [_CFG, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
@@ -141,6 +142,12 @@ def mtl_reduce(partials, bias, residual, out, rows, cols, row_begin=0, row_end=N
     arr = (_P * t)(*[_ptr(p) for p in partials])
     _check(lib().mtl_reduce(t, arr, _ptr(bias), _ptr(residual), _ptr(out), rows, cols, row_begin,
                             rows if row_end is None else row_end, _stream(stream)), "mtl_reduce")
+
+
+def mtl_allgather_rows(bufs, out, rows, cols, rank, stream=None):
+    t = len(bufs)
+    arr = (_P * t)(*[_ptr(b) for b in bufs])
+    _check(lib().mtl_allgather_rows(t, rank, arr, _ptr(out), rows, cols, _stream(stream)), "mtl_allgather_rows")
 
 
 def mtl_mlp_fwd(cfg, h, w1, b1, w2, gz, a, partial, scratch=None, scratch_bytes=None, stream=None):

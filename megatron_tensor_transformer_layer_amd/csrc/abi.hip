@@ -352,6 +352,24 @@ mtl_status mtl_reduce(int32_t t, const void* const* partials, const void* bias, 
                                     reinterpret_cast<hipStream_t>(stream)));
 }
 
+mtl_status mtl_allgather_rows(int32_t t, int32_t rank, const void* const* bufs, void* out, int64_t rows, int64_t cols,
+                              mtl_stream_t stream) {
+  if (!bufs || !out) return MTL_E_NULL;
+  if (t < 1 || t > 16 || rows <= 0 || cols <= 0 || cols % 8 != 0 || rows % t != 0) return MTL_E_SHAPE;
+  if (rank < 0 || rank >= t) return MTL_E_RANK;
+  if (!aligned16(out)) return MTL_E_ALIGN;
+  const uint16_t* p[16] = {};
+  for (int i = 0; i < t; ++i) {
+    if (i == rank) continue;  // the caller's own share is already in place and is not read
+    if (!bufs[i]) return MTL_E_NULL;
+    if (!aligned16(bufs[i])) return MTL_E_ALIGN;
+    if (bufs[i] == out) return MTL_E_UNSUPPORTED;
+    p[i] = static_cast<const uint16_t*>(bufs[i]);
+  }
+  return hip_status(allgather_rows(t, rank, p, static_cast<uint16_t*>(out), rows, cols,
+                                   reinterpret_cast<hipStream_t>(stream)));
+}
+
 mtl_status mtl_mlp_fwd(const mtl_layer_cfg* c, const void* h, const void* w1, const void* b1, const void* w2, void* gz,
                        void* a, void* partial, void* scratch, size_t scratch_bytes, mtl_stream_t stream) {
   mtl_status st = mtl_validate(c);

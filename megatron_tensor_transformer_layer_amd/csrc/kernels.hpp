@@ -96,6 +96,10 @@ hipError_t attention_bwd(const AttnArgs& a, hipStream_t s);
 // out[r, :] = sum_i partials[i][r, :] (+ bias) (+ residual) for r in [row_begin, row_end).
 hipError_t reduce_partials(int t, const uint16_t* const* partials, const uint16_t* bias, const uint16_t* residual,
                            uint16_t* out, int64_t cols, int64_t row_begin, int64_t row_end, hipStream_t s);
+// Sequence-parallel all-gather stand-in: copies rows [i*rows/t, (i+1)*rows/t)
+// of bufs[i] into out for every i != rank (rows % t == 0, cols % 8 == 0).
+hipError_t allgather_rows(int t, int rank, const uint16_t* const* bufs, uint16_t* out, int64_t rows, int64_t cols,
+                          hipStream_t s);
 // For one or two jobs j: out_j[c] (=|+=) sum_r x_j[r][c] over [rows, cols_j]
 // row-major bf16, fp32, deterministic, two launches for all jobs together;
 // ws holds colsum_ws_floats(rows, cols_0 + cols_1) floats.

@@ -5,6 +5,12 @@
 // summed in fp32 in rank order, written bf16.  Every lane moves 16 bytes per
 // load; the grid is a multiple of the 256 CUs and strides over the row range.
 //
+// allgather_rows: the on-device stand-in for the sequence-parallel all-gather
+// that precedes a column-parallel linear: rank i's share of a [rows, cols]
+// tensor is rows [i*rows/t, (i+1)*rows/t) of its own full-size buffer; the
+// t-1 peer shares are copied into the calling rank's buffer in place.  One
+// launch moves all of them, 16 bytes per lane.
+//
 // colsum_bf16: the bias gradients of the four linears are column sums of a
 // [rows, cols] bf16 gradient.  Deterministic two-stage sum: stage 1 gives each
 // 256-thread block 512 columns x 64 rows (16-byte loads, all 16 of a lane in
@@ -103,6 +109,43 @@ hipError_t reduce_partials(int t, const uint16_t* const* partials, const uint16_
     case 8: hipLaunchKernelGGL(reduce_partials_kernel<8>, dim3((unsigned)blocks), dim3(256), 0, s, a); break;
     default: hipLaunchKernelGGL(reduce_partials_kernel<0>, dim3((unsigned)blocks), dim3(256), 0, s, a); break;
   }
+  return hipGetLastError();
+}
+
+struct GatherArgs {
+  const uint16_t* src[MAX_PARTIALS];  // the t-1 peer buffers, in rank order
+  int64_t first[MAX_PARTIALS];        // element offset of each peer's share
+  uint16_t* out;
+  int64_t share;                      // elements per share (multiple of 8)
+  int peers;
+};
+
+__global__ __launch_bounds__(256) void allgather_rows_kernel(GatherArgs a) {
+  const int64_t vper = a.share / 8;
+  const int64_t nvec = vper * a.peers;
+  for (int64_t v = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; v < nvec; v += (int64_t)gridDim.x * blockDim.x) {
+    const int i = (int)(v / vper);
+    const int64_t e = a.first[i] + (v - (int64_t)i * vper) * 8;
+    *reinterpret_cast<u32x4*>(a.out + e) = *reinterpret_cast<const u32x4*>(a.src[i] + e);
+  }
+}
+
+hipError_t allgather_rows(int t, int rank, const uint16_t* const* bufs, uint16_t* out, int64_t rows, int64_t cols,
+                          hipStream_t s) {
+  if (t < 1 || t > MAX_PARTIALS || rank < 0 || rank >= t || rows % t) return hipErrorInvalidValue;
+  GatherArgs a{};
+  a.out = out;
+  a.share = rows / t * cols;
+  for (int i = 0; i < t; ++i) {
+    if (i == rank) continue;
+    a.src[a.peers] = bufs[i];
+    a.first[a.peers] = (int64_t)i * a.share;
+    ++a.peers;
+  }
+  if (a.peers == 0 || a.share == 0) return hipSuccess;
+  int64_t blocks = (a.share / 8 * a.peers + 255) / 256;
+  if (blocks > 2048) blocks = 2048;
+  hipLaunchKernelGGL(allgather_rows_kernel, dim3((unsigned)blocks), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

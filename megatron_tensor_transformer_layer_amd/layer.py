@@ -12,8 +12,8 @@ from dataclasses import dataclass
 import numpy as np
 import torch
 
-from . import (MTL_PREC_BF16, make_cfg, mtl_attn_bwd, mtl_attn_fwd, mtl_mlp_bwd, mtl_mlp_fwd, mtl_reduce,
-               mtl_workspace_bytes)
+from . import (MTL_PREC_BF16, make_cfg, mtl_allgather_rows, mtl_attn_bwd, mtl_attn_fwd, mtl_mlp_bwd, mtl_mlp_fwd,
+               mtl_reduce, mtl_workspace_bytes)
 
 DEV = "cuda"
 
@@ -105,11 +105,17 @@ class RankState:
 
 
 def run_sharded_layer(shape, tp: int, shards: list, x_bits, b_o_bits, b2_bits, dy_bits, residual: bool = False,
-                      precision: int = MTL_PREC_BF16, device=DEV) -> dict:
+                      precision: int = MTL_PREC_BF16, device=DEV, sp: bool = False) -> dict:
     """Run the whole layer as tp rank shards plus the four full reductions on
-    one device; returns host fp64 copies of every output."""
+    one device; returns host fp64 copies of every output.  With sp, the
+    sequence-parallel form: every rank holds full-size buffers of X, H, dY, dH
+    with only its own row share filled, reduces only its share of each sum and
+    gathers the peers' shares in place (mtl_allgather_rows) before the next
+    column-parallel linear; Y and dX stay row-sharded."""
     ranks = [RankState(shape, tp, r, shards[r], device=device, precision=precision) for r in range(tp)]
     D = ranks[0].D
+    if sp:
+        return _run_sp(ranks, tp, D, x_bits, b_o_bits, b2_bits, dy_bits, residual, device)
     x = bf16_dev(x_bits, device)
     b_o = bf16_dev(b_o_bits, device)
     b2 = bf16_dev(b2_bits, device)
@@ -131,12 +137,66 @@ def run_sharded_layer(shape, tp: int, shards: list, x_bits, b_o_bits, b2_bits, d
         r.attn_bwd(dh, x)
     mtl_reduce([r.p_dx for r in ranks], None, dh if residual else None, dx, D.S, D.h)
     torch.cuda.synchronize()
+    return _outputs(ranks, host_f64(y), host_f64(h), host_f64(dh), host_f64(dx))
+
+
+def _outputs(ranks, y, h, dh, dx) -> dict:
     cat = lambda key, axis: np.concatenate([host_f64(getattr(r, key)) for r in ranks], axis=axis)
     return dict(
-        y=host_f64(y), h=host_f64(h), dh=host_f64(dh), dx=host_f64(dx),
+        y=y, h=h, dh=dh, dx=dx,
         qkv=cat("qkv", 1), o=cat("o", 1), lse=cat("lse", 0), gz=cat("gz", 1), a=cat("a", 1),
         dw_qkv=cat("dw_qkv", 1), db_qkv=cat("db_qkv", 0), dw_o=cat("dw_o", 0), dw1=cat("dw1", 1),
         db1=cat("db1", 0), dw2=cat("dw2", 0),
         db_o=host_f64(ranks[0].db_o), db2=host_f64(ranks[0].db2),
         db_o_all=[host_f64(r.db_o) for r in ranks], db2_all=[host_f64(r.db2) for r in ranks],
     )
+
+
+def _run_sp(ranks, tp, D, x_bits, b_o_bits, b2_bits, dy_bits, residual, device) -> dict:
+    S, H = D.S, D.h
+    share = [(i * S // tp, (i + 1) * S // tp) for i in range(tp)]
+    full = lambda: [torch.zeros(S, H, dtype=torch.bfloat16, device=device) for _ in range(tp)]
+
+    def gather(bufs):
+        for i in range(tp):
+            mtl_allgather_rows(bufs, bufs[i], S, H, i)
+
+    def scattered(bits):  # each rank starts with only its own rows of the tensor
+        src = bf16_dev(bits, device)
+        bufs = full()
+        for i, (r0, r1) in enumerate(share):
+            bufs[i][r0:r1] = src[r0:r1]
+        return bufs
+
+    def reduce_scatter(partials, bias, residuals, out):
+        for i, (r0, r1) in enumerate(share):
+            mtl_reduce(partials, bias, residuals[i] if residual else None, out[i], S, H, r0, r1)
+
+    b_o, b2 = bf16_dev(b_o_bits, device), bf16_dev(b2_bits, device)
+    xs = scattered(x_bits)
+    gather(xs)
+    for i, r in enumerate(ranks):
+        r.attn_fwd(xs[i])
+    hs = full()
+    reduce_scatter([r.p_attn for r in ranks], b_o, xs, hs)
+    gather(hs)
+    for i, r in enumerate(ranks):
+        r.mlp_fwd(hs[i])
+    ys = full()
+    reduce_scatter([r.p_mlp for r in ranks], b2, hs, ys)
+    dys = scattered(dy_bits)
+    gather(dys)
+    for i, r in enumerate(ranks):
+        r.mlp_bwd(dys[i], hs[i])
+    dhs = full()
+    reduce_scatter([r.p_dh for r in ranks], None, dys, dhs)
+    gather(dhs)
+    for i, r in enumerate(ranks):
+        r.attn_bwd(dhs[i], xs[i])
+    dxs = full()
+    reduce_scatter([r.p_dx for r in ranks], None, dhs, dxs)
+    torch.cuda.synchronize()
+    rows = lambda bufs: np.concatenate([host_f64(bufs[i][r0:r1]) for i, (r0, r1) in enumerate(share)], axis=0)
+    out = _outputs(ranks, rows(ys), host_f64(hs[0]), host_f64(dhs[0]), rows(dxs))
+    out["gathered"] = {k: [host_f64(b) for b in v] for k, v in (("x", xs), ("h", hs), ("dy", dys), ("dh", dhs))}
+    return out

@@ -95,6 +95,16 @@ def test_errors_before_launch(mtl):
     assert lib.mtl_reduce(0, arr, None, None, P, 64, 16, 0, 64, None) == mtl.MTL_E_SHAPE
     assert lib.mtl_reduce(2, arr, None, None, P, 64, 16, 0, 64, None) == mtl.MTL_E_UNSUPPORTED  # out aliases
     assert lib.mtl_reduce(2, None, None, None, P, 64, 16, 0, 64, None) == mtl.MTL_E_NULL
+    Q = P + (1 << 16)
+    bufs = (ctypes.c_void_p * 2)(P, Q)
+    assert lib.mtl_allgather_rows(2, 0, bufs, P, 63, 16, None) == mtl.MTL_E_SHAPE  # rows % t
+    assert lib.mtl_allgather_rows(2, 0, bufs, P, 64, 12, None) == mtl.MTL_E_SHAPE  # cols % 8
+    assert lib.mtl_allgather_rows(2, 2, bufs, P, 64, 16, None) == mtl.MTL_E_RANK
+    assert lib.mtl_allgather_rows(2, -1, bufs, P, 64, 16, None) == mtl.MTL_E_RANK
+    assert lib.mtl_allgather_rows(2, 1, bufs, P, 64, 16, None) == mtl.MTL_E_UNSUPPORTED  # a peer buffer is out
+    assert lib.mtl_allgather_rows(2, 0, None, P, 64, 16, None) == mtl.MTL_E_NULL
+    assert lib.mtl_allgather_rows(2, 0, (ctypes.c_void_p * 2)(P, None), Q, 64, 16, None) == mtl.MTL_E_NULL
+    assert lib.mtl_allgather_rows(2, 0, (ctypes.c_void_p * 2)(P, Q + 8), P, 64, 16, None) == mtl.MTL_E_ALIGN
 
 
 def test_status_strings(mtl):
