@@ -40,6 +40,9 @@ def parse():
     ap.add_argument("--sp", action="store_true",
                     help="sequence parallel: X, H, dY, dH arrive as row shares and are gathered in place "
                          "(mtl_allgather_rows) before each column-parallel linear")
+    ap.add_argument("--router", action="store_true",
+                    help="with an MoE workload: time the router alone (linear, top-k routing, gate and "
+                         "load-balancing backward, dW_r and dX) over all tokens")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-seq", type=int, default=4096)
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -159,9 +162,78 @@ def moe_cpu_baseline(shape, rank, sample_tokens, sample_ffn):
                       f"(fp64 numpy), {dt:.2f} s"}
 
 
+def router_cpu_baseline(shape, sample_tokens, alpha):
+    """The router oracle (fp64 numpy) on the first sample_tokens tokens."""
+    import synth
+    from oracle import moe as M
+    from oracle import router as R
+    x = synth.bf16_bits_to_f64(synth.moe_tokens(shape, 0, "moe_x"))[:sample_tokens]
+    w = synth.bf16_bits_to_f64(synth.router_weight(shape))
+    dg = synth.gate_grads(shape)[:sample_tokens].astype(np.float64)
+    t0 = time.perf_counter()
+    logits = R.router_forward(x, w)
+    idx, gates = M.route_topk(logits, shape.topk)
+    R.router_backward(x, w, logits, idx, gates, dg, alpha)
+    dt = time.perf_counter() - t0
+    fl = 6.0 * sample_tokens * shape.hidden * shape.experts
+    return {"value": fl / dt / 1e12, "unit": "TFLOP/s", "cores": len(os.sched_getaffinity(0)), "kind": "oracle",
+            "sample": f"router forward+backward on the first {sample_tokens} of {shape.tokens} tokens "
+                      f"(fp64 numpy), {dt:.2f} s"}
+
+
+def router_main(args):
+    """The MoE router over all tokens: logits = x W_r, top-k routing, the gate
+    and load-balancing backward into the logits, dW_r and the router's dX."""
+    import torch
+    import synth
+    from megatron_tensor_transformer_layer_amd import mtl_moe_route
+    from megatron_tensor_transformer_layer_amd.layer import bf16_dev
+    from megatron_tensor_transformer_layer_amd.moe import Router
+
+    shape = synth.MOE_WORKLOADS[args.workload]
+    T, E, k, alpha = shape.tokens, shape.experts, shape.topk, 0.001
+    x = bf16_dev(synth.moe_tokens(shape, 0, "moe_x"))
+    ro = Router(T, shape.hidden, E, k, bf16_dev(synth.router_weight(shape)), aux_coeff=alpha)
+    idx = torch.empty(T, k, dtype=torch.int32, device="cuda")
+    gates = torch.empty(T, k, dtype=torch.float32, device="cuda")
+    dgates = torch.from_numpy(synth.gate_grads(shape)).cuda()
+
+    def step():
+        mtl_moe_route(ro.cfg, ro.forward(x), idx, gates)
+        ro.backward(x, idx, gates, dgates)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) / args.steps * 1e3
+    fl = 6.0 * T * shape.hidden * E  # the three router products, 2*T*h*E FLOP each
+    out = {
+        "metric": "TFLOP/s of the MoE router fwd+bwd (bf16 GEMMs) and % of MI355X MFMA peak",
+        "value": round(fl / (ms / 1e3) / 1e12, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (N(0,1) tokens, N(0,0.02) router weight, N(0,1) gate gradients)",
+        "config": {"workload": f"{args.workload} router: {T} tokens, hidden {shape.hidden}, {E} experts, "
+                               f"top-{k}, load-balancing coefficient {alpha}",
+                   "global_batch": 1, "seq_len": T, "parallelism": "router-replicated-1gpu"},
+        "pct_of_peak": round(100 * fl / (ms / 1e3) / 1e12 / PEAK_BF16_TFLOPS, 2),
+        "flop_per_step": fl,
+        "roofline": None,
+        "cpu_baseline": None if args.no_cpu_baseline else router_cpu_baseline(shape, 1024, alpha),
+    }
+    print(json.dumps(out), flush=True)
+
+
 def moe_main(args):
     """One EP rank's MoE expert block: route, permute, grouped fc1+GeLU, fc2,
     combine, and the backward (combine', grouped dgrad and wgrad, dX scatter)."""
+    if args.router:
+        router_main(args)
+        return
     import torch
     import synth
     from megatron_tensor_transformer_layer_amd.layer import bf16_dev

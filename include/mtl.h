@@ -260,6 +260,40 @@ mtl_status mtl_moe_sizes(const mtl_moe_cfg* cfg, int64_t* max_rows, size_t* scra
 mtl_status mtl_moe_route(const mtl_moe_cfg* cfg, const float* logits, int32_t* topk_idx, float* gates,
                          mtl_stream_t stream);
 
+/* The MoE router's linear (replicated on every expert-parallel rank; the site
+ * summary's MoE deploy step routes each token to --moe-router-topk experts of
+ * --num-experts):
+ *   logits = x . w_r    [T, E] fp32 (bf16 operands, fp32 accumulate)
+ * x [T, h] bf16, w_r [h, E] bf16.  E % 8 == 0.  The routing itself is
+ * mtl_moe_route. */
+mtl_status mtl_moe_router_fwd(const mtl_moe_cfg* cfg, const void* x, const void* w_r, float* logits,
+                              mtl_stream_t stream);
+
+/* Scratch bytes of mtl_moe_router_bwd. */
+mtl_status mtl_moe_router_sizes(const mtl_moe_cfg* cfg, size_t* scratch_bytes);
+
+/* Router backward with the load-balancing loss.  The deploy step sets
+ * --moe-aux-loss-coeff (alpha) without a formula; the Switch Transformer form
+ * is taken:
+ *   L_aux = alpha * E * sum_e f_e P_e,   f_e = c_e / (T k),
+ *   P_e = mean over tokens of softmax(logits_t)_e (over all E experts),
+ * c_e = assignments routed to expert e in topk_idx (a constant of the
+ * backward).  Computed:
+ *   aux_loss  [1] fp32 (device; NULL to skip the value, the gradient is kept)
+ *   dlogits   [T, E] fp32 = backward of the gate softmax over the k selected
+ *             logits given dgates, plus dL_aux/dlogits
+ *   dw_r      [h, E] fp32 = x^T . dlogits   (+= with MTL_F_WGRAD_ACCUM)
+ *   dx        [T, h] bf16 = dlogits . w_r^T (the router's share of dL/dx)
+ * The two products take dlogits rounded to bf16.  logits, topk_idx [T, k]
+ * int32 (ids in [0, E)) and gates [T, k] fp32 are those of mtl_moe_router_fwd
+ * and mtl_moe_route; dgates [T, k] fp32 is dL/dgates summed over the ranks
+ * that hold the experts (on one rank, what mtl_moe_bwd returns).  0 <=
+ * aux_coeff < inf.  scratch: mtl_moe_router_sizes bytes. */
+mtl_status mtl_moe_router_bwd(const mtl_moe_cfg* cfg, const void* x, const void* w_r, const float* logits,
+                              const int32_t* topk_idx, const float* gates, const float* dgates, float aux_coeff,
+                              float* aux_loss, float* dlogits, float* dw_r, void* dx, void* scratch,
+                              size_t scratch_bytes, mtl_stream_t stream);
+
 /* Stable grouping of this rank's assignments by local expert:
  *   counts   [E_l]     assignments per local expert
  *   offsets  [E_l + 1] exclusive prefix sum; offsets[E_l] = N

@@ -58,6 +58,10 @@ _SIGS = {
     "mtl_fp8_cast": (ctypes.c_int, [_P, _I64, _I64, _I32, _P, _P, _P, _P]),
     "mtl_fp8_quantize": (ctypes.c_int, [_P, _I64, _I64, _I32, _P, _P, _P, _P, _SZ, _P]),
     "mtl_moe_validate": (ctypes.c_int, [_MCFG]),
+    "mtl_moe_router_fwd": (ctypes.c_int, [_MCFG, _P, _P, _P, _P]),
+    "mtl_moe_router_sizes": (ctypes.c_int, [_MCFG, ctypes.POINTER(_SZ)]),
+    "mtl_moe_router_bwd": (ctypes.c_int, [_MCFG, _P, _P, _P, _P, _P, _P, ctypes.c_float, _P, _P, _P, _P, _P, _SZ,
+                                          _P]),
     "mtl_moe_sizes": (ctypes.c_int, [_MCFG, ctypes.POINTER(_I64), ctypes.POINTER(_SZ)]),
     "mtl_moe_route": (ctypes.c_int, [_MCFG, _P, _P, _P, _P]),
     "mtl_moe_permute": (ctypes.c_int, [_MCFG, _P, _P, _P, _P, _P, _P, _P]),
@@ -185,6 +189,25 @@ def mtl_moe_sizes(cfg: MoeCfg):
     rows, n = _I64(0), _SZ(0)
     _check(lib().mtl_moe_sizes(ctypes.byref(cfg), ctypes.byref(rows), ctypes.byref(n)), "mtl_moe_sizes")
     return rows.value, n.value
+
+
+def mtl_moe_router_fwd(cfg, x, w_r, logits, stream=None):
+    _check(lib().mtl_moe_router_fwd(ctypes.byref(cfg), _ptr(x), _ptr(w_r), _ptr(logits), _stream(stream)),
+           "mtl_moe_router_fwd")
+
+
+def mtl_moe_router_sizes(cfg) -> int:
+    n = _SZ(0)
+    _check(lib().mtl_moe_router_sizes(ctypes.byref(cfg), ctypes.byref(n)), "mtl_moe_router_sizes")
+    return int(n.value)
+
+
+def mtl_moe_router_bwd(cfg, x, w_r, logits, topk_idx, gates, dgates, aux_coeff, aux_loss, dlogits, dw_r, dx,
+                       scratch, scratch_bytes=None, stream=None):
+    _check(lib().mtl_moe_router_bwd(ctypes.byref(cfg), _ptr(x), _ptr(w_r), _ptr(logits), _ptr(topk_idx), _ptr(gates),
+                                    _ptr(dgates), float(aux_coeff), _ptr(aux_loss), _ptr(dlogits), _ptr(dw_r),
+                                    _ptr(dx), _ptr(scratch), _nbytes(scratch, scratch_bytes), _stream(stream)),
+           "mtl_moe_router_bwd")
 
 
 def mtl_moe_route(cfg, logits, topk_idx, gates, stream=None):

@@ -638,6 +638,70 @@ mtl_status mtl_moe_sizes(const mtl_moe_cfg* c, int64_t* max_rows, size_t* scratc
   return MTL_OK;
 }
 
+// The router GEMMs address x [T, h] and w_r [h, E] with 32-bit byte offsets.
+static mtl_status router_check(const mtl_moe_cfg* c) {
+  mtl_status st = mtl_moe_validate(c);
+  if (st != MTL_OK) return st;
+  if (c->experts % 8 != 0) return MTL_E_SHAPE;
+  const int64_t T = c->tokens, h = c->hidden, E = c->experts;
+  if ((T + 256) * h * 2 >= ((int64_t)1 << 32) || (h + 256) * E * 2 >= ((int64_t)1 << 32) ||
+      (T + 256) * E * 2 >= ((int64_t)1 << 32))
+    return MTL_E_SHAPE;
+  return MTL_OK;
+}
+
+mtl_status mtl_moe_router_fwd(const mtl_moe_cfg* c, const void* x, const void* w_r, float* logits,
+                              mtl_stream_t stream) {
+  mtl_status st = router_check(c);
+  if (st != MTL_OK) return st;
+  if ((st = check_ptrs(x, w_r, logits)) != MTL_OK) return st;
+  const int64_t T = c->tokens, h = c->hidden, E = c->experts;
+  return hip_status(gemm_bf16(gemm(x, h, w_r, E, T, E, h, logits, E), GEMM_FWD, EPI_F32,
+                              reinterpret_cast<hipStream_t>(stream)));
+}
+
+// Router backward scratch: dlogits in bf16 [T, E], counts [E] int32, q [T] fp32.
+static size_t router_scratch(const mtl_moe_cfg* c, uint16_t** dl16, int32_t** counts, float** q, char* base) {
+  Bump b{base};
+  uint16_t* a = b.take<uint16_t>((int64_t)c->tokens * c->experts * 2);
+  int32_t* n = b.take<int32_t>((int64_t)c->experts * 4);
+  float* r = b.take<float>((int64_t)c->tokens * 4);
+  if (dl16) *dl16 = a;
+  if (counts) *counts = n;
+  if (q) *q = r;
+  return b.off;
+}
+
+mtl_status mtl_moe_router_sizes(const mtl_moe_cfg* c, size_t* scratch_bytes) {
+  mtl_status st = router_check(c);
+  if (st != MTL_OK) return st;
+  if (scratch_bytes) *scratch_bytes = router_scratch(c, nullptr, nullptr, nullptr, nullptr);
+  return MTL_OK;
+}
+
+mtl_status mtl_moe_router_bwd(const mtl_moe_cfg* c, const void* x, const void* w_r, const float* logits,
+                              const int32_t* topk_idx, const float* gates, const float* dgates, float aux_coeff,
+                              float* aux_loss, float* dlogits, float* dw_r, void* dx, void* scratch,
+                              size_t scratch_bytes, mtl_stream_t stream) {
+  mtl_status st = router_check(c);
+  if (st != MTL_OK) return st;
+  if ((st = check_ptrs(x, w_r, logits, topk_idx, gates, dgates, dlogits, dw_r, dx, scratch)) != MTL_OK) return st;
+  if (!(aux_coeff >= 0.f) || aux_coeff == INFINITY) return MTL_E_SHAPE;
+  uint16_t* dl16;
+  int32_t* counts;
+  float* q;
+  if (scratch_bytes < router_scratch(c, &dl16, &counts, &q, static_cast<char*>(scratch))) return MTL_E_WORKSPACE;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const int64_t T = c->tokens, h = c->hidden, E = c->experts;
+  MTL_TRY(moe_router_bwd(logits, topk_idx, gates, dgates, (int)T, (int)E, c->topk, aux_coeff, counts, q, aux_loss,
+                         dlogits, dl16, s));
+  // dw_r = x^T . dlogits and dx = dlogits . w_r^T, on the bf16 rounding of dlogits
+  const int wepi = (c->flags & MTL_F_WGRAD_ACCUM) ? EPI_F32_ACC : EPI_F32;
+  MTL_TRY(gemm_bf16_pair(gemm(x, h, dl16, E, h, E, T, dw_r, E), GEMM_WGRAD, wepi,
+                         gemm(dl16, E, w_r, E, T, h, E, dx, h), GEMM_DGRAD, EPI_BF16, s));
+  return MTL_OK;
+}
+
 mtl_status mtl_moe_route(const mtl_moe_cfg* c, const float* logits, int32_t* topk_idx, float* gates,
                          mtl_stream_t stream) {
   mtl_status st = mtl_moe_validate(c);

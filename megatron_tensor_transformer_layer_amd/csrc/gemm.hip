@@ -725,6 +725,7 @@ hipError_t gemm_bf16(const GemmArgs& p, GemmLayout layout, int epi, hipStream_t 
       if (epi == EPI_BF16) return launch_layout<true, false, EPI_BF16>(p, s);
       if (epi == EPI_BF16_BIAS) return launch_layout<true, false, EPI_BF16_BIAS>(p, s);
       if (epi == EPI_BIAS_GELU) return launch_layout<true, false, EPI_BIAS_GELU>(p, s);
+      if (epi == EPI_F32) return launch_layout<true, false, EPI_F32>(p, s);  // fp32 logits of the MoE router
       break;
     case GEMM_DGRAD:  // A k-contig, B k-contig
       if (epi == EPI_BF16) return launch_layout<true, true, EPI_BF16>(p, s);

@@ -140,6 +140,12 @@ hipError_t fp8_quantize_n(const QuantJob* jobs, int n, void* ws, hipStream_t s);
 // Top-k expert ids per token (descending logit, ties to the lower id) and the
 // softmax of the selected logits.  E <= 1024, k <= min(E, 64).
 hipError_t moe_route(const float* logits, int T, int E, int k, int32_t* idx, float* gates, hipStream_t s);
+// Router backward: counts [E] (assignments per expert), q [T] scratch,
+// aux_loss (1 float, NULL: not computed), dlogits [T, E] fp32 and its bf16
+// rounding dlogits_bf16 (the operand of the router's dgrad and wgrad GEMMs).
+hipError_t moe_router_bwd(const float* logits, const int32_t* idx, const float* gates, const float* dgates, int T,
+                          int E, int k, float alpha, int32_t* counts, float* q, float* aux_loss, float* dlogits,
+                          uint16_t* dlogits_bf16, hipStream_t s);
 // Stable grouping of the (token, slot) entries whose expert lies in
 // [e_lo, e_lo + E_l): counts[E_l], offsets[E_l + 1], ptok/pslot[N] and the
 // inverse slot_row[T*k] (row of the entry, or -1 when its expert is not local).

@@ -80,6 +80,134 @@ hipError_t moe_route(const float* logits, int T, int E, int k, int32_t* idx, flo
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------- router backward
+// Load-balancing loss (the site's --moe-aux-loss-coeff; the pages give no
+// formula, the Switch Transformer form is taken): L = alpha * E * sum_e f_e P_e
+// with f_e = c_e / (T k) the share of the T*k assignments routed to e and P_e
+// the token mean of the full softmax over all E logits; c_e is a constant of
+// the backward.  With coef = alpha E / (T^2 k):
+//   L = coef * sum_t q_t,  q_t = sum_e p_te c_e,
+//   dL/dl_te = coef * p_te (c_e - q_t).
+// The gates are the softmax over the k selected logits, whose backward is
+//   dl_j += g_j (dg_j - sum_s g_s dg_s)  for the selected j.
+
+// c_e over all T*k assignments: one workgroup, an LDS histogram (integer, so
+// the result does not depend on the order of the atomic adds).
+__global__ __launch_bounds__(1024) void moe_router_counts_kernel(const int32_t* __restrict__ idx, int64_t n, int E,
+                                                                 int32_t* __restrict__ counts) {
+  __shared__ int hist[1024];
+  for (int e = threadIdx.x; e < 1024; e += blockDim.x) hist[e] = 0;
+  __syncthreads();
+  for (int64_t i = threadIdx.x; i < n; i += blockDim.x) {
+    const int e = idx[i];
+    if ((unsigned)e < (unsigned)E) atomicAdd(&hist[e], 1);
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < E; e += blockDim.x) counts[e] = hist[e];
+}
+
+// One wave per token; lane l holds experts l, l+64, ... (PER of them, E <= 64 PER).
+template <int PER>
+__global__ __launch_bounds__(256) void moe_router_bwd_kernel(const float* __restrict__ logits,
+                                                             const int32_t* __restrict__ idx,
+                                                             const float* __restrict__ gates,
+                                                             const float* __restrict__ dgates,
+                                                             const int32_t* __restrict__ counts, int T, int E, int k,
+                                                             float coef, float* __restrict__ dlogits,
+                                                             uint16_t* __restrict__ dlogits_bf16,
+                                                             float* __restrict__ q_out) {
+  const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (t >= T) return;
+  const float* row = logits + t * E;
+  float l[PER], c[PER];
+  float m = -INFINITY;
+#pragma unroll
+  for (int j = 0; j < PER; ++j) {
+    const int e = lane + 64 * j;
+    l[j] = e < E ? row[e] : -INFINITY;
+    c[j] = e < E ? (float)counts[e] : 0.f;
+    m = fmaxf(m, l[j]);
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+  float z = 0.f;
+#pragma unroll
+  for (int j = 0; j < PER; ++j) {
+    l[j] = lane + 64 * j < E ? expf(l[j] - m) : 0.f;  // l now holds the unnormalised p
+    z += l[j];
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) z += __shfl_xor(z, off);
+  const float inv = 1.f / z;
+  float q = 0.f;
+#pragma unroll
+  for (int j = 0; j < PER; ++j) {
+    l[j] *= inv;
+    q += l[j] * c[j];
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) q += __shfl_xor(q, off);
+  // the gate softmax backward: lanes s < k hold slot s
+  const float gs = lane < k ? gates[t * k + lane] : 0.f;
+  const float dgs = lane < k ? dgates[t * k + lane] : 0.f;
+  const int is = lane < k ? idx[t * k + lane] : -1;
+  float inner = gs * dgs;
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) inner += __shfl_xor(inner, off);
+  float dl[PER];
+#pragma unroll
+  for (int j = 0; j < PER; ++j) dl[j] = coef * l[j] * (c[j] - q);
+  for (int s = 0; s < k; ++s) {
+    const int js = __shfl(is, s);
+    const float add = __shfl(gs, s) * (__shfl(dgs, s) - inner);
+#pragma unroll
+    for (int j = 0; j < PER; ++j)
+      if (lane + 64 * j == js) dl[j] += add;
+  }
+#pragma unroll
+  for (int j = 0; j < PER; ++j) {
+    const int e = lane + 64 * j;
+    if (e < E) {
+      dlogits[t * E + e] = dl[j];
+      dlogits_bf16[t * E + e] = (uint16_t)f32_to_bf16_bits(dl[j]);
+    }
+  }
+  if (lane == 0) q_out[t] = q;
+}
+
+// L = coef * sum_t q_t, one workgroup in a fixed order (deterministic).
+__global__ __launch_bounds__(1024) void moe_router_aux_kernel(const float* __restrict__ q, int T, float coef,
+                                                              float* __restrict__ out) {
+  __shared__ float part[1024];
+  float s = 0.f;
+  for (int t = threadIdx.x; t < T; t += blockDim.x) s += q[t];
+  part[threadIdx.x] = s;
+  __syncthreads();
+  for (int w = 512; w >= 1; w >>= 1) {
+    if ((int)threadIdx.x < w) part[threadIdx.x] += part[threadIdx.x + w];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) out[0] = coef * part[0];
+}
+
+hipError_t moe_router_bwd(const float* logits, const int32_t* idx, const float* gates, const float* dgates, int T,
+                          int E, int k, float alpha, int32_t* counts, float* q, float* aux_loss, float* dlogits,
+                          uint16_t* dlogits_bf16, hipStream_t s) {
+  if (T <= 0 || E <= 0 || E > 1024 || k <= 0 || k > 64) return hipErrorInvalidValue;
+  const float coef = (float)((double)alpha * E / ((double)T * T * k));
+  hipLaunchKernelGGL(moe_router_counts_kernel, dim3(1), dim3(1024), 0, s, idx, (int64_t)T * k, E, counts);
+  const dim3 grid((unsigned)((T + 3) / 4));
+  if (E <= 256)
+    hipLaunchKernelGGL(moe_router_bwd_kernel<4>, grid, dim3(256), 0, s, logits, idx, gates, dgates, counts, T, E, k,
+                       coef, dlogits, dlogits_bf16, q);
+  else
+    hipLaunchKernelGGL(moe_router_bwd_kernel<16>, grid, dim3(256), 0, s, logits, idx, gates, dgates, counts, T, E,
+                       k, coef, dlogits, dlogits_bf16, q);
+  if (aux_loss) hipLaunchKernelGGL(moe_router_aux_kernel, dim3(1), dim3(1024), 0, s, q, T, coef, aux_loss);
+  return hipGetLastError();
+}
+
 // ---------------------------------------------------------------- permute
 // One workgroup of 1024 threads; thread t owns a contiguous chunk of the
 // (token, slot) entries.  For each local expert in turn: count the chunk's

@@ -9,7 +9,7 @@ from __future__ import annotations
 import torch
 
 from . import (MTL_PREC_BF16, make_moe_cfg, mtl_moe_bwd, mtl_moe_fwd, mtl_moe_permute, mtl_moe_route,
-               mtl_moe_sizes)
+               mtl_moe_router_bwd, mtl_moe_router_fwd, mtl_moe_router_sizes, mtl_moe_sizes)
 
 DEV = "cuda"
 
@@ -65,3 +65,29 @@ class MoeRank:
         self.permute()
         self.forward(x)
         self.backward(dy)
+
+
+class Router:
+    """The MoE router's linear and its backward (replicated on every EP rank):
+    logits, the gate/logit gradients, the load-balancing loss, dW_r and the
+    router's share of dX.  ``w_r`` [h, E] is a bf16 device tensor."""
+
+    def __init__(self, tokens, hidden, experts, topk, w_r, aux_coeff=0.001, ep=1, rank=0, flags=0, device=DEV):
+        self.cfg = make_moe_cfg(tokens, hidden, 8, experts, topk, ep, rank, MTL_PREC_BF16, flags)
+        self.scratch_bytes = mtl_moe_router_sizes(self.cfg)
+        f32 = dict(dtype=torch.float32, device=device)
+        self.w_r, self.aux_coeff = w_r, aux_coeff
+        self.logits = torch.empty(tokens, experts, **f32)
+        self.dlogits = torch.empty(tokens, experts, **f32)
+        self.dw_r = torch.zeros(hidden, experts, **f32)
+        self.dx = torch.empty(tokens, hidden, dtype=torch.bfloat16, device=device)
+        self.aux_loss = torch.zeros(1, **f32)
+        self.scratch = torch.empty(self.scratch_bytes, dtype=torch.uint8, device=device)
+
+    def forward(self, x):
+        mtl_moe_router_fwd(self.cfg, x, self.w_r, self.logits)
+        return self.logits
+
+    def backward(self, x, idx, gates, dgates):
+        mtl_moe_router_bwd(self.cfg, x, self.w_r, self.logits, idx, gates, dgates, self.aux_coeff, self.aux_loss,
+                           self.dlogits, self.dw_r, self.dx, self.scratch)

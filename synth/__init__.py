@@ -33,7 +33,7 @@ import numpy as np
 _TID = {
     "x": 1, "w_qkv": 2, "b_qkv": 3, "w_o": 4, "b_o": 5, "w1": 6, "b1": 7,
     "w2": 8, "b2": 9, "dy": 10, "h": 11, "dh": 12,
-    "moe_x": 20, "moe_w1": 21, "moe_w2": 22, "moe_dy": 23, "moe_gumbel": 24,
+    "moe_x": 20, "moe_w1": 21, "moe_w2": 22, "moe_dy": 23, "moe_gumbel": 24, "moe_wr": 25, "moe_dgates": 26,
 }
 
 WEIGHT_STD = 0.02
@@ -213,6 +213,16 @@ def moe_expert_weight(shape: MoeShape, name: str, expert: int, seed: int = 0) ->
     else:
         raise KeyError(name)
     return bf16_round_bits(_normal(seed, name, expert, shp, WEIGHT_STD))
+
+
+def router_weight(shape: MoeShape, seed: int = 0) -> np.ndarray:
+    """bf16 bits of the router's weight [hidden, experts], N(0, WEIGHT_STD)."""
+    return bf16_round_bits(_normal(seed, "moe_wr", 0, (shape.hidden, shape.experts), WEIGHT_STD))
+
+
+def gate_grads(shape: MoeShape, seed: int = 0) -> np.ndarray:
+    """fp32 upstream gradients of the gates [tokens, topk], N(0, 1)."""
+    return _normal(seed, "moe_dgates", 0, (shape.tokens, shape.topk), 1.0).astype(np.float32)
 
 
 def moe_expert_weight_device(shape: MoeShape, name: str, expert: int, seed: int = 0, device="cuda"):
