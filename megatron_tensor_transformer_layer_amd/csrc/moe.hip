@@ -209,10 +209,13 @@ hipError_t moe_router_bwd(const float* logits, const int32_t* idx, const float* 
 }
 
 // ---------------------------------------------------------------- permute
-// One workgroup of 1024 threads; thread t owns a contiguous chunk of the
-// (token, slot) entries.  For each local expert in turn: count the chunk's
-// matches, exclusive-scan the counts over threads, write the matches in entry
-// order.  Entry order is (token, slot), so tokens ascend within an expert.
+// One workgroup of 1024 threads per local expert, in two launches.  Thread t
+// owns a contiguous chunk of the (token, slot) entries.  The first launch
+// counts each expert's matches and clears the inverse map; the second takes
+// the expert's base offset from the counts of the experts before it, counts
+// its chunk's matches again, exclusive-scans them over the threads and writes
+// the matches in entry order.  Entry order is (token, slot), so tokens ascend
+// within an expert.
 __device__ __forceinline__ int block_exclusive_scan(int v, int* sh, int& total) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   int x = v;
@@ -239,44 +242,67 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int* sh, int& total) 
   return excl;
 }
 
-__global__ __launch_bounds__(1024) void moe_permute_kernel(const int32_t* __restrict__ idx, int T, int k, int e_lo,
-                                                            int E_l, int32_t* __restrict__ counts,
-                                                            int32_t* __restrict__ offsets, int32_t* __restrict__ ptok,
-                                                            int32_t* __restrict__ pslot, int32_t* __restrict__ slot_row) {
+__device__ __forceinline__ int chunk_matches(const int32_t* __restrict__ idx, int64_t b0, int64_t b1, int ex) {
+  int c = 0;
+  for (int64_t j = b0; j < b1; ++j) c += (idx[j] == ex);
+  return c;
+}
+
+__global__ __launch_bounds__(1024) void moe_permute_count_kernel(const int32_t* __restrict__ idx, int T, int k,
+                                                                 int e_lo, int32_t* __restrict__ counts,
+                                                                 int32_t* __restrict__ slot_row) {
   __shared__ int sh[17];
+  const int e = blockIdx.x;
+  const int64_t n = (int64_t)T * k;
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t j = (int64_t)e * blockDim.x + threadIdx.x; j < n; j += stride) slot_row[j] = -1;
+  const int64_t chunk = (n + 1023) / 1024;
+  const int64_t b0 = min(n, threadIdx.x * chunk), b1 = min(n, b0 + chunk);
+  int total;
+  block_exclusive_scan(chunk_matches(idx, b0, b1, e_lo + e), sh, total);
+  if (threadIdx.x == 0) counts[e] = total;
+}
+
+__global__ __launch_bounds__(1024) void moe_permute_scatter_kernel(const int32_t* __restrict__ idx, int T, int k,
+                                                                   int e_lo, int E_l,
+                                                                   const int32_t* __restrict__ counts,
+                                                                   int32_t* __restrict__ offsets,
+                                                                   int32_t* __restrict__ ptok,
+                                                                   int32_t* __restrict__ pslot,
+                                                                   int32_t* __restrict__ slot_row) {
+  __shared__ int sh[17];
+  __shared__ int base_sh;
+  const int e = blockIdx.x, ex = e_lo + e;
+  if (threadIdx.x == 0) {
+    int base = 0;
+    for (int i = 0; i < e; ++i) base += counts[i];
+    base_sh = base;
+    offsets[e] = base;
+    if (e == E_l - 1) offsets[E_l] = base + counts[e];
+  }
   const int64_t n = (int64_t)T * k;
   const int64_t chunk = (n + 1023) / 1024;
-  const int64_t b0 = threadIdx.x * chunk, b1 = min(n, b0 + chunk);
-  for (int64_t j = b0; j < b1; ++j) slot_row[j] = -1;
-  int base = 0;
-  for (int e = 0; e < E_l; ++e) {
-    const int ex = e_lo + e;
-    int c = 0;
-    for (int64_t j = b0; j < b1; ++j) c += (idx[j] == ex);
-    int total;
-    const int excl = block_exclusive_scan(c, sh, total);
-    int pos = base + excl;
-    for (int64_t j = b0; j < b1; ++j) {
-      if (idx[j] == ex) {
-        ptok[pos] = (int32_t)(j / k);
-        pslot[pos] = (int32_t)(j % k);
-        slot_row[j] = pos;
-        ++pos;
-      }
+  const int64_t b0 = min(n, threadIdx.x * chunk), b1 = min(n, b0 + chunk);
+  int total;
+  const int excl = block_exclusive_scan(chunk_matches(idx, b0, b1, ex), sh, total);  // its barriers publish base_sh
+  int pos = base_sh + excl;
+  for (int64_t j = b0; j < b1; ++j) {
+    if (idx[j] == ex) {
+      ptok[pos] = (int32_t)(j / k);
+      pslot[pos] = (int32_t)(j % k);
+      slot_row[j] = pos;
+      ++pos;
     }
-    if (threadIdx.x == 0) {
-      counts[e] = total;
-      offsets[e] = base;
-    }
-    base += total;
   }
-  if (threadIdx.x == 0) offsets[E_l] = base;
 }
 
 hipError_t moe_permute(const int32_t* idx, int T, int k, int e_lo, int E_l, int32_t* counts, int32_t* offsets,
                        int32_t* ptok, int32_t* pslot, int32_t* slot_row, hipStream_t s) {
-  hipLaunchKernelGGL(moe_permute_kernel, dim3(1), dim3(1024), 0, s, idx, T, k, e_lo, E_l, counts, offsets, ptok, pslot,
+  if (E_l <= 0) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(moe_permute_count_kernel, dim3((unsigned)E_l), dim3(1024), 0, s, idx, T, k, e_lo, counts,
                      slot_row);
+  hipLaunchKernelGGL(moe_permute_scatter_kernel, dim3((unsigned)E_l), dim3(1024), 0, s, idx, T, k, e_lo, E_l, counts,
+                     offsets, ptok, pslot, slot_row);
   return hipGetLastError();
 }
 
