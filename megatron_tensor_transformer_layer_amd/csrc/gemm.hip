@@ -312,6 +312,14 @@ struct Mainloop {
   static __device__ __forceinline__ void finish(const Frags (&f)[2], f32x16 (&acc)[TM][TN]) { mfma_step(f[1], acc); }
 };
 
+// Row blocks the epilogue stages per pass: the largest divisor of tm that fits
+// (a pass never reaches past the wave's last row block).
+constexpr int rows_per_pass(int tm, int fit) {
+  int r = fit < tm ? fit : tm;
+  while (r > 1 && tm % r != 0) --r;
+  return r;
+}
+
 // One output tile (workgroup index bid of the GEMM p) with the two LDS stages
 // st0, st1 of the launching kernel.
 template <int BM, int BN, bool A_K, bool B_K, int EPI, int F8, int NWN = 2>
@@ -470,7 +478,7 @@ __device__ __forceinline__ void gemm_tile(GemmArgs p, const int bid, LDS_AS char
   // GeLU(z) of the biased sum z, both from one evaluation of the normal CDF and
   // density, staged side by side (each pass then covers half as many rows).
   constexpr int NOUT = EPI == EPI_BIAS_GELU ? 2 : 1;
-  constexpr int IPP = (REGION / (NOUT * 32 * RB)) < TM ? (REGION / (NOUT * 32 * RB)) : TM;
+  constexpr int IPP = rows_per_pass(TM, REGION / (NOUT * 32 * RB));
   constexpr int OUTB = IPP * 32 * RB;        // staged bytes of one output per pass
   static_assert(IPP >= 1, "epilogue staging does not fit");
 
