@@ -18,19 +18,31 @@ namespace {
 
 constexpr int AMAX_BLOCKS = 1024;
 
+// Max of the bf16 magnitudes of the 8-element vectors v0, v0 + stride, ...
+// below nv: AU loads in flight per lane at a time.
+constexpr int AU = 4;
+__device__ __forceinline__ uint32_t vec_amax(const uint16_t* __restrict__ x, int64_t v0, int64_t nv, int64_t stride) {
+  uint32_t m = 0;
+  for (int64_t v = v0; v < nv; v += stride * AU) {
+    u32x4 q[AU];
+#pragma unroll
+    for (int u = 0; u < AU; ++u)
+      q[u] = v + u * stride < nv ? *reinterpret_cast<const u32x4*>(x + (v + u * stride) * 8) : u32x4{0, 0, 0, 0};
+#pragma unroll
+    for (int u = 0; u < AU; ++u)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        m = max(m, q[u][j] & 0x7fffu);
+        m = max(m, (q[u][j] >> 16) & 0x7fffu);
+      }
+  }
+  return m;
+}
+
 __global__ __launch_bounds__(256) void amax_stage1(const uint16_t* __restrict__ x, int64_t n,
                                                    uint32_t* __restrict__ part) {
-  uint32_t m = 0;
   const int64_t nv = n / 8;
-  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-  for (int64_t v = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; v < nv; v += stride) {
-    const u32x4 q = *reinterpret_cast<const u32x4*>(x + v * 8);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      m = max(m, q[j] & 0x7fffu);
-      m = max(m, (q[j] >> 16) & 0x7fffu);
-    }
-  }
+  uint32_t m = vec_amax(x, (int64_t)blockIdx.x * blockDim.x + threadIdx.x, nv, (int64_t)gridDim.x * blockDim.x);
   // tail of n % 8 elements, block 0 only
   if (blockIdx.x == 0)
     for (int64_t i = nv * 8 + threadIdx.x; i < n; i += blockDim.x) m = max(m, (uint32_t)(x[i] & 0x7fffu));
@@ -72,17 +84,8 @@ __global__ __launch_bounds__(256) void amax_stage1_multi(QuantArgs a) {
   const int lb = (int)blockIdx.x - a.first1[j], nb = a.first1[j + 1] - a.first1[j];
   const uint16_t* x = a.x[j];
   const int64_t n = a.rows[j] * a.cols[j];
-  uint32_t m = 0;
   const int64_t nv = n / 8;
-  const int64_t stride = (int64_t)nb * blockDim.x;
-  for (int64_t v = (int64_t)lb * blockDim.x + threadIdx.x; v < nv; v += stride) {
-    const u32x4 q = *reinterpret_cast<const u32x4*>(x + v * 8);
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      m = max(m, q[k] & 0x7fffu);
-      m = max(m, (q[k] >> 16) & 0x7fffu);
-    }
-  }
+  uint32_t m = vec_amax(x, (int64_t)lb * blockDim.x + threadIdx.x, nv, (int64_t)nb * blockDim.x);
   if (lb == 0)
     for (int64_t i = nv * 8 + threadIdx.x; i < n; i += blockDim.x) m = max(m, (uint32_t)(x[i] & 0x7fffu));
 #pragma unroll
@@ -159,23 +162,44 @@ __device__ __forceinline__ uint32_t encode(float y) {
   else return to_fp8<2, 15, 0x7bu>(y);
 }
 
-// Tile of 64 rows x 64 columns per workgroup: each thread converts 16 elements
-// (two 8-element vectors), writes the row-major codes directly and stages them
-// in LDS for the transposed copy, which is written as 16 consecutive rows of one
-// column per thread.  The scale comes from rec[1], or -- with part non-null --
+// Two scaled values to two codes (y0 in bits 0-7, y1 in bits 8-15) with
+// gfx950's OCP conversion (round to nearest even): the operands are first
+// clamped to +-fmt_max, which is the saturation of encode(); NaN, which the
+// clamp would turn into a bound, gets the format's NaN code 0x7F afterwards.
+// The result equals encode() on every fp32 input.
+template <int FMT>
+__device__ __forceinline__ uint32_t encode2(float y0, float y1) {
+  constexpr float MX = FMT == 0 ? 448.f : 57344.f;
+  const float c0 = fminf(fmaxf(y0, -MX), MX), c1 = fminf(fmaxf(y1, -MX), MX);
+  uint32_t r;
+  if constexpr (FMT == 0) r = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(c0, c1, 0, false) & 0xffffu;
+  else r = (uint32_t)__builtin_amdgcn_cvt_pk_bf8_f32(c0, c1, 0, false) & 0xffffu;
+  if (y0 != y0) r = (r & 0xff00u) | 0x7fu;
+  if (y1 != y1) r = (r & 0x00ffu) | 0x7f00u;
+  return r;
+}
+
+// Tile of CT_ROWS = 128 rows x 64 columns per workgroup: each thread converts
+// 32 elements (four 8-element vectors, all loaded before the first is used),
+// writes the row-major codes directly and stages them in LDS for the
+// transposed copy, which is written as 32 consecutive rows of one column per
+// thread (two 16-byte stores; four lanes cover a column's 128 rows).  The scale comes from rec[1], or -- with part non-null --
 // from the amax stage-1 partials, reduced by every block (its tile loads are
 // issued first), and block (0, 0) writes the record: one launch fewer.
+constexpr int CT_PASSES = 4;               // 32-row passes per cast tile
+constexpr int CT_ROWS = 32 * CT_PASSES;    // rows per cast tile
+
 template <int FMT>
 __device__ __forceinline__ void cast_tile(const uint16_t* __restrict__ x, int64_t rows, int64_t cols,
                                           const float* __restrict__ rec_in, const uint32_t* __restrict__ part,
                                           int nparts, float* __restrict__ rec_out, uint8_t* __restrict__ out,
                                           uint8_t* __restrict__ out_t, int bx, int by) {
-  __shared__ uint8_t tile[64][64 + 4];
-  const int64_t r0 = (int64_t)by * 64, c0 = (int64_t)bx * 64;
+  __shared__ uint8_t tile[CT_ROWS][64 + 4];
+  const int64_t r0 = (int64_t)by * CT_ROWS, c0 = (int64_t)bx * 64;
   const int tr = threadIdx.x >> 3, tc = (threadIdx.x & 7) * 8;
-  u32x4 qv[2];
+  u32x4 qv[CT_PASSES];
 #pragma unroll
-  for (int pass = 0; pass < 2; ++pass) {
+  for (int pass = 0; pass < CT_PASSES; ++pass) {
     const int64_t r = r0 + tr + pass * 32, c = c0 + tc;
     qv[pass] = (r < rows && c < cols) ? *reinterpret_cast<const u32x4*>(x + r * cols + c) : u32x4{0, 0, 0, 0};
   }
@@ -192,7 +216,7 @@ __device__ __forceinline__ void cast_tile(const uint16_t* __restrict__ x, int64_
     s = rec_in[1];
   }
 #pragma unroll
-  for (int pass = 0; pass < 2; ++pass) {
+  for (int pass = 0; pass < CT_PASSES; ++pass) {
     const int lr = tr + pass * 32;
     const int64_t r = r0 + lr, c = c0 + tc;
     if (r < rows && c < cols) {
@@ -200,10 +224,8 @@ __device__ __forceinline__ void cast_tile(const uint16_t* __restrict__ x, int64_
       uint32_t w0 = 0, w1 = 0;
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
-        w0 |= encode<FMT>(__fmul_rn(bf16_lo(q[j]), s)) << (16 * j);
-        w0 |= encode<FMT>(__fmul_rn(bf16_hi(q[j]), s)) << (16 * j + 8);
-        w1 |= encode<FMT>(__fmul_rn(bf16_lo(q[j + 2]), s)) << (16 * j);
-        w1 |= encode<FMT>(__fmul_rn(bf16_hi(q[j + 2]), s)) << (16 * j + 8);
+        w0 |= encode2<FMT>(__fmul_rn(bf16_lo(q[j]), s), __fmul_rn(bf16_hi(q[j]), s)) << (16 * j);
+        w1 |= encode2<FMT>(__fmul_rn(bf16_lo(q[j + 2]), s), __fmul_rn(bf16_hi(q[j + 2]), s)) << (16 * j);
       }
       if (out) *reinterpret_cast<u32x2*>(out + r * cols + c) = u32x2{w0, w1};
       *reinterpret_cast<uint32_t*>(&tile[lr][tc]) = w0;
@@ -212,19 +234,25 @@ __device__ __forceinline__ void cast_tile(const uint16_t* __restrict__ x, int64_
   }
   if (!out_t) return;
   __syncthreads();
-  // thread -> column lc, rows seg*16 .. seg*16+15
-  const int lc = threadIdx.x & 63, seg = threadIdx.x >> 6;
-  const int64_t c = c0 + lc, rbase = r0 + seg * 16;
-  if (c < cols && rbase < rows) {
-    u32x4 o;
+  // thread -> column lc = t/4, rows (t%4)*32 .. +31 as two 16-row stores: the
+  // four lanes of a column write its 128-row line of the transposed copy
+  const int lc = threadIdx.x >> 2, seg = threadIdx.x & 3;
+  const int64_t c = c0 + lc;
 #pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      uint32_t v = 0;
+  for (int hlf = 0; hlf < CT_ROWS / 64; ++hlf) {
+    const int lr0 = seg * (CT_ROWS / 4) + hlf * 16;
+    const int64_t rbase = r0 + lr0;
+    if (c < cols && rbase < rows) {
+      u32x4 o;
 #pragma unroll
-      for (int b = 0; b < 4; ++b) v |= (uint32_t)tile[seg * 16 + 4 * w + b][lc] << (8 * b);
-      o[w] = v;
+      for (int w = 0; w < 4; ++w) {
+        uint32_t v = 0;
+#pragma unroll
+        for (int b = 0; b < 4; ++b) v |= (uint32_t)tile[lr0 + 4 * w + b][lc] << (8 * b);
+        o[w] = v;
+      }
+      *reinterpret_cast<u32x4*>(out_t + c * rows + rbase) = o;
     }
-    *reinterpret_cast<u32x4*>(out_t + c * rows + rbase) = o;
   }
 }
 
@@ -266,7 +294,7 @@ hipError_t fp8_amax(const uint16_t* x, int64_t n, int fmt, float* rec, void* ws,
 hipError_t fp8_cast(const uint16_t* x, int64_t rows, int64_t cols, int fmt, const float* rec, uint8_t* out,
                     uint8_t* out_t, hipStream_t s) {
   if (rows <= 0 || cols <= 0 || (!out && !out_t)) return hipSuccess;
-  const dim3 grid((unsigned)((cols + 63) / 64), (unsigned)((rows + 63) / 64));
+  const dim3 grid((unsigned)((cols + 63) / 64), (unsigned)((rows + CT_ROWS - 1) / CT_ROWS));
   if (fmt == 0) hipLaunchKernelGGL(cast_kernel<0>, grid, dim3(256), 0, s, x, rows, cols, rec, out, out_t);
   else hipLaunchKernelGGL(cast_kernel<1>, grid, dim3(256), 0, s, x, rows, cols, rec, out, out_t);
   return hipGetLastError();
@@ -295,7 +323,7 @@ hipError_t fp8_quantize_n(const QuantJob* jobs, int n, void* ws, hipStream_t s) 
     b1 += nb;
     a.tiles_x[j] = (int)((q.cols + 63) / 64);
     a.first2[j] = b2;
-    b2 += a.tiles_x[j] * (int)((q.rows + 63) / 64);
+    b2 += a.tiles_x[j] * (int)((q.rows + CT_ROWS - 1) / CT_ROWS);
   }
   a.first1[n] = b1;
   a.first2[n] = b2;

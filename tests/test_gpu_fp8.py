@@ -46,11 +46,24 @@ def _cast_case(name):
         b = synth.bf16_round_bits(rng.standard_normal(4096))
         b[17], b[1000], b[2001] = 0x7F80, 0xFF80, 0x7FC1  # +inf, -inf, NaN
         return b, 1
+    if name in ("saturate-e4m3", "saturate-e5m2"):
+        # an infinity makes amax unusable, so s = 1 and finite values beyond the
+        # format's maximum reach the saturation: just above it, at the rounding
+        # midpoint to the next (absent) step, far beyond, both signs; NaN and -0
+        fmt = int(name.endswith("e5m2"))
+        mx = 448.0 if fmt == 0 else 57344.0
+        over = np.array([mx, mx * 1.0078125, mx * 1.03125, mx * 1.0625, mx * 1.07, 2 * mx, 1e30])
+        b = synth.bf16_round_bits(rng.standard_normal(4096) * mx / 4)
+        b[:7] = synth.bf16_round_bits(over)
+        b[7:14] = synth.bf16_round_bits(-over)
+        b[14], b[15], b[16], b[17] = 0x7F80, 0xFF80, 0x7FC1, 0x8000  # +inf, -inf, NaN, -0
+        return b, fmt
     raise KeyError(name)
 
 
 @pytest.mark.gpu
-@pytest.mark.parametrize("case", ["grid-e4m3", "grid-e5m2", "gauss-e4m3", "gauss-e5m2", "zeros", "inf-nan"])
+@pytest.mark.parametrize("case", ["grid-e4m3", "grid-e5m2", "gauss-e4m3", "gauss-e5m2", "zeros", "inf-nan",
+                                  "saturate-e4m3", "saturate-e5m2"])
 def test_amax_and_cast_bit_exact(mtl, case):
     import torch
     from megatron_tensor_transformer_layer_amd.layer import bf16_dev
