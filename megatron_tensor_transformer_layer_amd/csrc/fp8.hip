@@ -166,7 +166,9 @@ __device__ __forceinline__ uint32_t encode(float y) {
 // gfx950's OCP conversion (round to nearest even): the operands are first
 // clamped to +-fmt_max, which is the saturation of encode(); NaN, which the
 // clamp would turn into a bound, gets the format's NaN code 0x7F afterwards.
-// The result equals encode() on every fp32 input.
+// encode() above states the rounding in plain arithmetic; the two agree bit
+// for bit on every bf16 value in range at scale 1, on scaled Gaussian data and
+// on saturating and non-finite inputs (the GPU cast tests).
 template <int FMT>
 __device__ __forceinline__ uint32_t encode2(float y0, float y1) {
   constexpr float MX = FMT == 0 ? 448.f : 57344.f;
