@@ -117,9 +117,9 @@ hipError_t quantize(std::initializer_list<QIn> in, void* amax_ws, hipStream_t s)
 }
 
 // fp8 GEMM C[M, N] = A . B^T over K, both operands k-contiguous codes.
-hipError_t gemm8(const Q8& a, const uint8_t* a_codes, const Q8& b, const uint8_t* b_codes, int64_t M, int64_t N,
-                 int64_t K, void* c, int64_t ldc, int epi, hipStream_t s, const void* bias = nullptr,
-                 void* c2 = nullptr, const void* aux = nullptr) {
+GemmArgs gemm8_args(const Q8& a, const uint8_t* a_codes, const Q8& b, const uint8_t* b_codes, int64_t M, int64_t N,
+                    int64_t K, void* c, int64_t ldc, const void* bias = nullptr, void* c2 = nullptr,
+                    const void* aux = nullptr) {
   GemmArgs g{};
   g.a = reinterpret_cast<const uint16_t*>(a_codes);
   g.b = reinterpret_cast<const uint16_t*>(b_codes);
@@ -137,7 +137,12 @@ hipError_t gemm8(const Q8& a, const uint8_t* a_codes, const Q8& b, const uint8_t
   g.ld_aux = ldc;
   g.scale_a = a.rec + 2;
   g.scale_b = b.rec + 2;
-  return gemm_fp8(g, a.fmt, b.fmt, epi, s);
+  return g;
+}
+hipError_t gemm8(const Q8& a, const uint8_t* a_codes, const Q8& b, const uint8_t* b_codes, int64_t M, int64_t N,
+                 int64_t K, void* c, int64_t ldc, int epi, hipStream_t s, const void* bias = nullptr,
+                 void* c2 = nullptr, const void* aux = nullptr) {
+  return gemm_fp8(gemm8_args(a, a_codes, b, b_codes, M, N, K, c, ldc, bias, c2, aux), a.fmt, b.fmt, epi, s);
 }
 
 struct MlpScratch {
@@ -433,12 +438,16 @@ mtl_status mtl_mlp_bwd(const mtl_layer_cfg* c, const void* dy, const void* h, co
   if (is_fp8(c)) {
     // E5M2 gradients, E4M3 activations and weights; wgrad operands transposed
     MTL_TRY(quantize({{dy, &ws.dy}, {w2, &ws.w2}, {a, &ws.a_t}}, ws.amax_ws, s));
-    MTL_TRY(gemm8(ws.dy, ws.dy.q, ws.w2, ws.w2.q, d.S, d.f_l, d.h, ws.dz, d.f_l, EPI_DGELU, s, nullptr, nullptr, gz));
-    MTL_TRY(gemm8(ws.a_t, ws.a_t.qt, ws.dy, ws.dy.qt, d.f_l, d.h, d.S, dw2, d.h, wepi, s));
+    // dw2 = a^T . dy with dz = (dy . w2^T) * gz in one launch, then dw1 = h^T . dz with dh_partial = dz . w1^T
+    MTL_TRY(gemm_fp8_pair(gemm8_args(ws.a_t, ws.a_t.qt, ws.dy, ws.dy.qt, d.f_l, d.h, d.S, dw2, d.h), wepi,
+                          gemm8_args(ws.dy, ws.dy.q, ws.w2, ws.w2.q, d.S, d.f_l, d.h, ws.dz, d.f_l, nullptr, nullptr,
+                                     gz),
+                          EPI_DGELU, s));
     MTL_TRY(quantize({{ws.dz, &ws.dz8}, {h, &ws.h_t}, {w1, &ws.w1}}, ws.amax_ws, s));
-    MTL_TRY(gemm8(ws.h_t, ws.h_t.qt, ws.dz8, ws.dz8.qt, d.h, d.f_l, d.S, dw1, d.f_l, wepi, s));
+    MTL_TRY(gemm_fp8_pair(gemm8_args(ws.h_t, ws.h_t.qt, ws.dz8, ws.dz8.qt, d.h, d.f_l, d.S, dw1, d.f_l), wepi,
+                          gemm8_args(ws.dz8, ws.dz8.q, ws.w1, ws.w1.q, d.S, d.h, d.f_l, dh_partial, d.h), EPI_BF16,
+                          s));
     MTL_TRY(mlp_bias_grads(d, ws, dy, db1, db2, accum, s));
-    MTL_TRY(gemm8(ws.dz8, ws.dz8.q, ws.w1, ws.w1.q, d.S, d.h, d.f_l, dh_partial, d.h, EPI_BF16, s));
     return MTL_OK;
   }
   // dz = (dy . w2^T) * gz, gz = GeLU'(z), with the independent dw2 = a^T . dy in the same
@@ -477,8 +486,8 @@ mtl_status mtl_attn_bwd(const mtl_layer_cfg* c, const void* dh, const void* x, c
   if (f8) {
     // do = dh . w_o^T ; dw_o = o^T . dh
     MTL_TRY(quantize({{dh, &ws.dh}, {w_o, &ws.wo}, {o, &ws.o_t}}, ws.amax_ws, s));
-    MTL_TRY(gemm8(ws.dh, ws.dh.q, ws.wo, ws.wo.q, d.S, d.o_l, d.h, ws.dout, d.o_l, EPI_BF16, s));
-    MTL_TRY(gemm8(ws.o_t, ws.o_t.qt, ws.dh, ws.dh.qt, d.o_l, d.h, d.S, dw_o, d.h, wepi, s));
+    MTL_TRY(gemm_fp8_pair(gemm8_args(ws.o_t, ws.o_t.qt, ws.dh, ws.dh.qt, d.o_l, d.h, d.S, dw_o, d.h), wepi,
+                          gemm8_args(ws.dh, ws.dh.q, ws.wo, ws.wo.q, d.S, d.o_l, d.h, ws.dout, d.o_l), EPI_BF16, s));
   } else {
     // dw_o = o^T . dh and do = dh . w_o^T, one launch (wgrad tiles first)
     GemmArgs g = gemm(dh, d.h, w_o, d.h, d.S, d.o_l, d.h, ws.dout, d.o_l);
@@ -505,9 +514,11 @@ mtl_status mtl_attn_bwd(const mtl_layer_cfg* c, const void* dh, const void* x, c
   if (f8) {
     // dw_qkv = x^T . dqkv ; dx_partial = dqkv . w_qkv^T
     MTL_TRY(quantize({{ws.dqkv, &ws.dqkv8}, {x, &ws.x_t}, {w_qkv, &ws.wqkv}}, ws.amax_ws, s));
-    MTL_TRY(gemm8(ws.x_t, ws.x_t.qt, ws.dqkv8, ws.dqkv8.qt, d.h, d.qkv_l, d.S, dw_qkv, d.qkv_l, wepi, s));
+    MTL_TRY(gemm_fp8_pair(gemm8_args(ws.x_t, ws.x_t.qt, ws.dqkv8, ws.dqkv8.qt, d.h, d.qkv_l, d.S, dw_qkv, d.qkv_l),
+                          wepi,
+                          gemm8_args(ws.dqkv8, ws.dqkv8.q, ws.wqkv, ws.wqkv.q, d.S, d.h, d.qkv_l, dx_partial, d.h),
+                          EPI_BF16, s));
     MTL_TRY(attn_bias_grads(d, ws, dh, db_qkv, db_o, accum, s));
-    MTL_TRY(gemm8(ws.dqkv8, ws.dqkv8.q, ws.wqkv, ws.wqkv.q, d.S, d.h, d.qkv_l, dx_partial, d.h, EPI_BF16, s));
     return MTL_OK;
   }
   // dw_qkv = x^T . dqkv and dx_partial = dqkv . w_qkv^T, one launch; then

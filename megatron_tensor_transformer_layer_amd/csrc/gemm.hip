@@ -592,12 +592,12 @@ __global__ __launch_bounds__(128 * NWN, 1) void gemm_bf16_kernel(GemmArgs p) {
   gemm_tile<BM, BN, A_K, B_K, EPI, F8, NWN>(p, blockIdx.x, (LDS_AS char*)st0_, (LDS_AS char*)st1_);
 }
 
-// A tile configuration of gemm_tile.
-template <int BM_, int BN_, bool A_K_, bool B_K_, int EPI_>
+// A tile configuration of gemm_tile (F8 as in Mainloop: 0 = bf16 operands).
+template <int BM_, int BN_, bool A_K_, bool B_K_, int EPI_, int F8_ = 0>
 struct TileCfg {
-  static constexpr int BM = BM_, BN = BN_, EPI = EPI_;
+  static constexpr int BM = BM_, BN = BN_, EPI = EPI_, F8 = F8_;
   static constexpr bool A_K = A_K_, B_K = B_K_;
-  static constexpr int STAGE = Mainloop<BM, BN, A_K, B_K, 0>::STAGE;
+  static constexpr int STAGE = Mainloop<BM, BN, A_K, B_K, F8_>::STAGE;
 };
 
 // Two independent GEMMs in one launch: workgroups [0, tiles1) take p1, the rest
@@ -612,10 +612,10 @@ __global__ __launch_bounds__(256, 1) void gemm_pair_kernel(GemmArgs p1, GemmArgs
   __shared__ __attribute__((aligned(1024))) char st1_[STAGE];
   const int bid = blockIdx.x;
   if (bid < tiles1)
-    gemm_tile<C1::BM, C1::BN, C1::A_K, C1::B_K, C1::EPI, 0>(p1, bid, (LDS_AS char*)st0_, (LDS_AS char*)st1_);
+    gemm_tile<C1::BM, C1::BN, C1::A_K, C1::B_K, C1::EPI, C1::F8>(p1, bid, (LDS_AS char*)st0_, (LDS_AS char*)st1_);
   else
-    gemm_tile<C2::BM, C2::BN, C2::A_K, C2::B_K, C2::EPI, 0>(p2, bid - tiles1, (LDS_AS char*)st0_,
-                                                            (LDS_AS char*)st1_);
+    gemm_tile<C2::BM, C2::BN, C2::A_K, C2::B_K, C2::EPI, C2::F8>(p2, bid - tiles1, (LDS_AS char*)st0_,
+                                                                 (LDS_AS char*)st1_);
 }
 
 template <int BM, int BN, bool A_K, bool B_K, int EPI, int F8 = 0, int NWN = 2>
@@ -754,12 +754,44 @@ static hipError_t launch_f8(const GemmArgs& p, hipStream_t s) {
   return launch_cfg<128, 128, true, true, EPI, F8>(p, s);
 }
 
+static bool fp8_args_ok(const GemmArgs& p) {
+  if (p.offsets || p.K <= 0 || p.K % 16 || p.lda % 16 || p.ldb % 16 || !p.scale_a || !p.scale_b) return false;
+  return ((int64_t)p.M + 256) * p.lda < ((int64_t)1 << 32) && ((int64_t)p.N + 256) * p.ldb < ((int64_t)1 << 32);
+}
+
+// The backward's independent fp8 pairs in one launch, wgrad tiles (E4M3 x E5M2,
+// fp32 output) first, dgrad tiles (E5M2 x E4M3, bf16 output) second, where both
+// take 128 x 128 tiles (the output projection's pair at the 7B-class shape:
+// 51 -> 40 us).  Pairs with a 256 x 256 half ran slower as one launch than as
+// two (4096^3 pairs +8-10%; a 128 x 128 wgrad beside a 256 x 256 dgrad +19%,
+// its tiles then holding the larger LDS footprint, one workgroup per CU instead
+// of two), so they stay two launches.
+template <int EPI_W>
+static hipError_t fp8_pair_dispatch(const GemmArgs& pw, const GemmArgs& pd, int epi_d, hipStream_t s, bool* done) {
+  *done = false;
+  const bool w256 = (long)((pw.M + 255) / 256) * ((pw.N + 255) / 256) >= 240;
+  const bool d256 = (long)((pd.M + 255) / 256) * ((pd.N + 255) / 256) >= 240;
+  if (w256 || d256 || epi_d != EPI_BF16) return hipSuccess;
+  *done = true;
+  return launch_pair<TileCfg<128, 128, true, true, EPI_W, 3>, TileCfg<128, 128, true, true, EPI_BF16, 2>>(pw, pd, s);
+}
+
+hipError_t gemm_fp8_pair(const GemmArgs& pw, int epi_w, const GemmArgs& pd, int epi_d, hipStream_t s) {
+  const bool plain = pw.M > 0 && pw.N > 0 && pd.M > 0 && pd.N > 0 && fp8_args_ok(pw) && fp8_args_ok(pd);
+  if (plain && (epi_w == EPI_F32 || epi_w == EPI_F32_ACC)) {
+    bool done = false;
+    hipError_t e = epi_w == EPI_F32 ? fp8_pair_dispatch<EPI_F32>(pw, pd, epi_d, s, &done)
+                                    : fp8_pair_dispatch<EPI_F32_ACC>(pw, pd, epi_d, s, &done);
+    if (done) return e;
+  }
+  hipError_t e = gemm_fp8(pw, 0, 1, epi_w, s);
+  if (e != hipSuccess) return e;
+  return gemm_fp8(pd, 1, 0, epi_d, s);
+}
+
 hipError_t gemm_fp8(const GemmArgs& p, int fmt_a, int fmt_b, int epi, hipStream_t s) {
   if (p.M <= 0 || p.N <= 0) return hipSuccess;
-  if (p.offsets || p.K <= 0 || p.K % 16 || p.lda % 16 || p.ldb % 16 || !p.scale_a || !p.scale_b)
-    return hipErrorInvalidValue;
-  if (((int64_t)p.M + 256) * p.lda >= ((int64_t)1 << 32) || ((int64_t)p.N + 256) * p.ldb >= ((int64_t)1 << 32))
-    return hipErrorInvalidValue;
+  if (!fp8_args_ok(p)) return hipErrorInvalidValue;
   const int f8 = 1 + fmt_a + 2 * fmt_b;
   if (f8 == 1) {  // forward: E4M3 x E4M3
     if (epi == EPI_BF16) return launch_f8<EPI_BF16, 1>(p, s);

@@ -70,6 +70,10 @@ hipError_t gemm_bf16_pair(const GemmArgs& p1, GemmLayout l1, int e1, const GemmA
 // (E4M3, E4M3) with BF16 / BF16_BIAS / BIAS_GELU, (E5M2, E4M3) with BF16 / DGELU,
 // (E4M3, E5M2) with F32 / F32_ACC.  K % 16 == 0, lda and ldb % 16 == 0, not grouped.
 hipError_t gemm_fp8(const GemmArgs& p, int fmt_a, int fmt_b, int epi, hipStream_t s);
+// A backward pair in one launch where a fused configuration exists: pw an
+// E4M3 x E5M2 wgrad (EPI_F32 / EPI_F32_ACC), pd an E5M2 x E4M3 dgrad (EPI_BF16 /
+// EPI_DGELU); else two launches.  Same requirements as gemm_fp8 for each.
+hipError_t gemm_fp8_pair(const GemmArgs& pw, int epi_w, const GemmArgs& pd, int epi_d, hipStream_t s);
 
 // ---------------------------------------------------------------- attention
 // Causal attention over `heads` heads of a head-interleaved QKV tensor
