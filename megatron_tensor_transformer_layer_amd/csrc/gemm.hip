@@ -750,7 +750,12 @@ hipError_t gemm_bf16(const GemmArgs& p, GemmLayout layout, int epi, hipStream_t 
 template <int EPI, int F8>
 static hipError_t launch_f8(const GemmArgs& p, hipStream_t s) {
   const long t256 = (long)((p.M + 255) / 256) * ((p.N + 255) / 256);
+  const long t192 = (long)((p.M + 255) / 256) * ((p.N + 191) / 192);
   if (t256 >= 240) return launch_cfg<256, 256, true, true, EPI, F8>(p, s);
+  // forward products 192 columns wide fill the chip with 256 x 192 tiles (the
+  // fused QKV projection: 256 tiles instead of 768 of 128 x 128)
+  if constexpr (F8 == 1)
+    if (t192 >= 240 && p.N % 192 == 0) return launch_cfg<256, 192, true, true, EPI, F8>(p, s);
   return launch_cfg<128, 128, true, true, EPI, F8>(p, s);
 }
 
