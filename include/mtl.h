@@ -265,7 +265,9 @@ mtl_status mtl_moe_route(const mtl_moe_cfg* cfg, const float* logits, int32_t* t
  * --num-experts):
  *   logits = x . w_r    [T, E] fp32 (bf16 operands, fp32 accumulate)
  * x [T, h] bf16, w_r [h, E] bf16.  E % 8 == 0.  The routing itself is
- * mtl_moe_route. */
+ * mtl_moe_route.  The router calls read tokens, hidden, experts, topk and
+ * flags of cfg; ffn only has to pass mtl_moe_validate (the experts' sizes do
+ * not enter). */
 mtl_status mtl_moe_router_fwd(const mtl_moe_cfg* cfg, const void* x, const void* w_r, float* logits,
                               mtl_stream_t stream);
 

@@ -73,6 +73,7 @@ class Router:
     router's share of dX.  ``w_r`` [h, E] is a bf16 device tensor."""
 
     def __init__(self, tokens, hidden, experts, topk, w_r, aux_coeff=0.001, ep=1, rank=0, flags=0, device=DEV):
+        # the router calls do not read ffn; 8 passes the configuration check
         self.cfg = make_moe_cfg(tokens, hidden, 8, experts, topk, ep, rank, MTL_PREC_BF16, flags)
         self.scratch_bytes = mtl_moe_router_sizes(self.cfg)
         f32 = dict(dtype=torch.float32, device=device)
