@@ -194,3 +194,23 @@ def test_fp8_validate_and_errors_before_launch(mtl):
     assert lib.mtl_fp8_quantize(P, 64, 16, 0, P, None, None, P, S, None) == mtl.MTL_E_NULL
     assert lib.mtl_fp8_quantize(P, 64, 16, 0, P, P, None, None, S, None) == mtl.MTL_E_NULL
     assert lib.mtl_fp8_quantize(P, 64, 16, 3, P, P, None, P, S, None) == mtl.MTL_E_UNSUPPORTED
+
+
+def test_router_validation_before_any_launch(mtl):
+    """The router calls check their configuration, pointers, coefficient and
+    workspace on the host (fake, never dereferenced addresses)."""
+    P = 1 << 20
+    lib = mtl.lib()
+    cfg = mtl.make_moe_cfg(64, 128, 8, 32, 4)
+    n = mtl.mtl_moe_router_sizes(cfg)
+    assert n > 0
+    assert lib.mtl_moe_router_fwd(ctypes.byref(cfg), P, P, None, None) == mtl.MTL_E_NULL
+    assert lib.mtl_moe_router_fwd(ctypes.byref(cfg), P, P + 4, P, None) == mtl.MTL_E_ALIGN
+    bad = mtl.make_moe_cfg(64, 128, 8, 12, 4)  # experts % 8
+    assert lib.mtl_moe_router_fwd(ctypes.byref(bad), P, P, P, None) == mtl.MTL_E_SHAPE
+    args = [P, P, P, P, P, P]
+    for coeff in (-1.0, float("nan"), float("inf")):
+        assert lib.mtl_moe_router_bwd(ctypes.byref(cfg), *args, coeff, None, P, P, P, P, n, None) == mtl.MTL_E_SHAPE
+    assert lib.mtl_moe_router_bwd(ctypes.byref(cfg), *args, 0.001, None, P, P, P, P, n - 1, None) == \
+        mtl.MTL_E_WORKSPACE
+    assert lib.mtl_moe_router_bwd(ctypes.byref(cfg), *args, 0.001, None, P, P, None, P, n, None) == mtl.MTL_E_NULL
