@@ -95,6 +95,26 @@ def calibrate_copy():
     assert torch.equal(src, dst)
     print(json.dumps({"copy_kernel": "reduce_partials_kernel (t=1)", "bytes_read": rows * cols * 2,
                       "bytes_written": rows * cols * 2, "launches": 3}), flush=True)
+    # the rate the same copy reaches, read + written bytes over the launch time,
+    # as the practical HBM ceiling of the streaming kernels
+    del src, dst
+    for mib in (64, 256, 1024):
+        rows = (mib << 20) // 2 // cols
+        src = torch.randn(rows, cols, device="cuda").to(torch.bfloat16)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            mtl_reduce([src], None, None, dst, rows, cols)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        reps = 20
+        e0.record()
+        for _ in range(reps):
+            mtl_reduce([src], None, None, dst, rows, cols)
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / reps
+        print(json.dumps({"copy_mib": mib, "us_per_launch": round(us, 2),
+                          "gb_per_s": round(2 * rows * cols * 2 / us / 1e3, 1)}), flush=True)
+        del src, dst
 
 
 def cpu_baseline(shape, rank, sample_seq, fp8=False):
