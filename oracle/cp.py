@@ -1,0 +1,68 @@
+"""fp64 oracle of one context-parallel rank's share of causal attention (forward).
+
+Test infrastructure only (see the package docstring).
+
+The guide ([guide] ai.lansai.wang/82226, the parallel-dimension table and the
+tolerance section) says that context parallelism cuts the inputs and
+activations along the sequence, that attention still needs the keys and values
+held by the other ranks, and that masks must be re-checked at several sequence
+lengths; the site summary ([site] navi2ai.com/sites/1106, its parallelism list
+and deploy examples) sets `--context-parallel-size`.  Neither fixes how the
+sequence is assigned to ranks.  Reading taken here: the S tokens are cut into
+cp contiguous chunks of C = S/cp, rank r holds the queries of chunk r, and its
+result is rows [rC, (r+1)C) of the causal attention over the whole sequence
+(O and the row log-sum-exp), i.e. the plain definition.  How a device splits
+that work over key chunks is not restated here.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+from . import layer as L
+
+
+def chunk_rows(seq: int, cp: int, rank: int) -> slice:
+    """Token rows held by CP rank `rank`: [rank*seq/cp, (rank+1)*seq/cp)."""
+    if cp < 1 or seq % cp != 0:
+        raise ValueError("seq must split into cp equal chunks")
+    if not 0 <= rank < cp:
+        raise ValueError("rank outside [0, cp)")
+    c = seq // cp
+    return slice(rank * c, (rank + 1) * c)
+
+
+def rank_attention(qkv_full, heads: int, cp: int, rank: int):
+    """O [C, heads*d] and lse [heads, C] of rank `rank`'s queries.
+
+    Causal attention of a row depends only on the tokens up to it, so the full
+    attention is evaluated over the prefix that ends with the rank's chunk and
+    the rank's rows are taken from it."""
+    qkv_full = np.asarray(qkv_full, dtype=np.float64)
+    rows = chunk_rows(qkv_full.shape[0], cp, rank)
+    o, lse = L.attention_forward(qkv_full[: rows.stop], heads)
+    return o[rows], lse[:, rows]
+
+
+def attention_rows(qkv_full, heads: int, rows) -> tuple:
+    """Causal attention for selected query rows only (global token indices):
+    query i of head n sees keys 0..i.  Returns O [len(rows), heads*d] and
+    lse [heads, len(rows)].  One query at a time, for sampled checks at sizes
+    where the full attention is too slow."""
+    qkv_full = np.asarray(qkv_full, dtype=np.float64)
+    d = qkv_full.shape[1] // (3 * heads)
+    scale = 1.0 / math.sqrt(d)
+    rows = list(rows)
+    o = np.zeros((len(rows), heads * d))
+    lse = np.zeros((heads, len(rows)))
+    for n in range(heads):
+        sq, sk, sv = L.head_slices(heads, d, n)
+        for j, i in enumerate(rows):
+            s = (qkv_full[i, sq] @ qkv_full[: i + 1, sk].T) * scale
+            m = s.max()
+            e = np.exp(s - m)
+            z = e.sum()
+            o[j, n * d:(n + 1) * d] = (e / z) @ qkv_full[: i + 1, sv]
+            lse[n, j] = m + math.log(z)
+    return o, lse

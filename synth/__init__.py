@@ -34,6 +34,7 @@ _TID = {
     "x": 1, "w_qkv": 2, "b_qkv": 3, "w_o": 4, "b_o": 5, "w1": 6, "b1": 7,
     "w2": 8, "b2": 9, "dy": 10, "h": 11, "dh": 12,
     "moe_x": 20, "moe_w1": 21, "moe_w2": 22, "moe_dy": 23, "moe_gumbel": 24, "moe_wr": 25, "moe_dgates": 26,
+    "cp_qkv": 27,
 }
 
 WEIGHT_STD = 0.02
@@ -103,6 +104,23 @@ WORKLOADS = {
     "gpt2-small-tp2": LayerShape(hidden=768, heads=12, ffn=3072, seq=512, micro_batch=1, tp=2),
     "7b-tp4": LayerShape(hidden=4096, heads=32, ffn=16384, seq=4096, micro_batch=1, tp=4),
     "gpt96l-tp8": LayerShape(hidden=8192, heads=64, ffn=32768, seq=4096, micro_batch=1, tp=8),
+}
+# One context-parallel rank's attention share: the local heads of the 7B-class
+# rank (8 heads of 128) over a 32768-token sequence cut into 4 chunks.
+@dataclass(frozen=True)
+class CpShape:
+    seq: int
+    heads: int
+    head_dim: int
+    cp: int
+
+    @property
+    def chunk(self) -> int:
+        return self.seq // self.cp
+
+
+CP_WORKLOADS = {
+    "cp4-seq32k-7b-tp4": CpShape(seq=32768, heads=8, head_dim=128, cp=4),
 }
 MOE_WORKLOADS = {
     "moe-256e-top8-ep16": MoeShape(tokens=4096, hidden=7168, ffn=18432, experts=256, topk=8, ep=16),
@@ -187,6 +205,28 @@ LAYER_NAMES = ("x", "w_qkv", "b_qkv", "w_o", "b_o", "w1", "b1", "w2", "b2", "dy"
 def layer_inputs(shape: LayerShape, seed: int = 0, tp: int = 1, rank: int = 0, names=LAYER_NAMES) -> dict:
     """bf16 bits of every layer input (the rank's shard where split)."""
     return {n: layer_tensor(shape, n, seed, tp, rank) for n in names}
+
+
+# ---------------------------------------------------------------- CP inputs
+CP_QKV_STD = WEIGHT_STD * 64.0  # x ~ N(0,1) through a N(0, 0.02) projection over 4096 inputs
+
+
+def cp_qkv(shape: CpShape, seed: int = 0) -> np.ndarray:
+    """bf16 bits of the whole sequence's head-interleaved QKV [seq, 3*heads*d],
+    N(0, CP_QKV_STD) (the spread of a QKV projection of N(0,1) activations);
+    chunk j is rows [j*C, (j+1)*C).  Drawn per 4096-row granule."""
+    from concurrent.futures import ThreadPoolExecutor
+    width = 3 * shape.heads * shape.head_dim
+    g = 4096
+    out = np.empty((shape.seq, width), dtype=np.uint16)
+
+    def fill(i):
+        rows = min(g, shape.seq - i * g)
+        out[i * g:i * g + rows] = bf16_round_bits(_normal(seed, "cp_qkv", i, (rows, width), CP_QKV_STD))
+
+    with ThreadPoolExecutor(max_workers=8) as ex:
+        list(ex.map(fill, range((shape.seq + g - 1) // g)))
+    return out
 
 
 # ---------------------------------------------------------------- MoE inputs

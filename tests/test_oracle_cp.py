@@ -1,0 +1,105 @@
+"""Pins of the context-parallel attention oracle (oracle/cp.py) against closed
+forms, invariants of the causal mask across chunks, and the log-sum-exp merge
+identity, independent of the oracle's own code path."""
+import math
+
+import numpy as np
+import pytest
+
+from oracle import cp as CP
+from oracle import layer as L
+
+
+def _qkv(seed, seq, heads, d, std=1.0):
+    return np.random.default_rng(seed).standard_normal((seq, 3 * heads * d)) * std
+
+
+def test_chunk_rows_cover_the_sequence_once():
+    seq, cp = 96, 4
+    got = np.concatenate([np.arange(seq)[CP.chunk_rows(seq, cp, r)] for r in range(cp)])
+    assert np.array_equal(got, np.arange(seq))
+    with pytest.raises(ValueError):
+        CP.chunk_rows(97, 4, 0)
+    with pytest.raises(ValueError):
+        CP.chunk_rows(96, 4, 4)
+
+
+def test_cp1_is_plain_attention():
+    qkv = _qkv(1, 40, 2, 8)
+    o, lse = CP.rank_attention(qkv, 2, 1, 0)
+    o_ref, lse_ref = L.attention_forward(qkv, 2)
+    assert np.array_equal(o, o_ref) and np.array_equal(lse, lse_ref)
+
+
+def test_constant_keys_give_prefix_mean_at_global_positions():
+    """Equal keys make every visible score equal: query i (global index) gets
+    the mean of V over tokens 0..i and lse = q.k/sqrt(d) + log(i+1).  A chunk
+    masked by local instead of global positions fails this."""
+    seq, cp, heads, d = 48, 4, 2, 4
+    qkv = _qkv(2, seq, heads, d)
+    for n in range(heads):
+        _, sk, _ = L.head_slices(heads, d, n)
+        qkv[:, sk] = qkv[0, sk]
+    for r in range(cp):
+        o, lse = CP.rank_attention(qkv, heads, cp, r)
+        rows = CP.chunk_rows(seq, cp, r)
+        for j, i in enumerate(range(rows.start, rows.stop)):
+            for n in range(heads):
+                sq, sk, sv = L.head_slices(heads, d, n)
+                assert np.allclose(o[j, n * d:(n + 1) * d], qkv[: i + 1, sv].mean(axis=0), rtol=0, atol=1e-12)
+                want = qkv[i, sq] @ qkv[0, sk] / math.sqrt(d) + math.log(i + 1)
+                assert abs(lse[n, j] - want) < 1e-12
+
+
+def test_later_chunks_do_not_matter_and_earlier_ones_do():
+    seq, cp, heads, d = 64, 4, 2, 8
+    qkv = _qkv(3, seq, heads, d)
+    r = 2
+    o, lse = CP.rank_attention(qkv, heads, cp, r)
+    later = qkv.copy()
+    later[CP.chunk_rows(seq, cp, 3)] = _qkv(4, seq // cp, heads, d)
+    o2, lse2 = CP.rank_attention(later, heads, cp, r)
+    assert np.array_equal(o, o2) and np.array_equal(lse, lse2)
+    earlier = qkv.copy()
+    earlier[CP.chunk_rows(seq, cp, 0)] = _qkv(5, seq // cp, heads, d)
+    o3, _ = CP.rank_attention(earlier, heads, cp, r)
+    assert np.max(np.abs(o3 - o)) > 1e-3
+
+
+def test_sampled_rows_match_full_attention():
+    seq, heads, d = 70, 3, 8
+    qkv = _qkv(6, seq, heads, d, std=1.5)
+    rows = [0, 1, 17, 63, 64, 69]
+    o, lse = CP.attention_rows(qkv, heads, rows)
+    o_ref, lse_ref = L.attention_forward(qkv, heads)
+    assert np.allclose(o, o_ref[rows], rtol=0, atol=1e-12)
+    assert np.allclose(lse, lse_ref[:, rows], rtol=0, atol=1e-12)
+
+
+def test_merge_of_chunk_partials_equals_the_rank_rows():
+    """Rank r's rows equal the log-sum-exp merge of its queries' attention over
+    each key chunk j <= r on its own (full for j < r, causal for j = r):
+    L = log sum_j exp(L_j), O = sum_j exp(L_j - L) O_j."""
+    seq, cp, heads, d = 64, 4, 2, 8
+    qkv = _qkv(7, seq, heads, d, std=1.3)
+    c = seq // cp
+    scale = 1.0 / math.sqrt(d)
+    for r in range(cp):
+        o_ref, lse_ref = CP.rank_attention(qkv, heads, cp, r)
+        q_rows = CP.chunk_rows(seq, cp, r)
+        for n in range(heads):
+            sq, sk, sv = L.head_slices(heads, d, n)
+            parts = []
+            for j in range(r + 1):
+                kr = CP.chunk_rows(seq, cp, j)
+                s = qkv[q_rows, sq] @ qkv[kr, sk].T * scale
+                if j == r:
+                    s = np.where(np.tril(np.ones((c, c), dtype=bool)), s, -np.inf)
+                m = s.max(axis=1, keepdims=True)
+                e = np.exp(s - m)
+                z = e.sum(axis=1, keepdims=True)
+                parts.append(((e / z) @ qkv[kr, sv], (m + np.log(z))[:, 0]))
+            lse = np.logaddexp.reduce(np.stack([p[1] for p in parts]), axis=0)
+            o = sum(np.exp(p[1] - lse)[:, None] * p[0] for p in parts)
+            assert np.allclose(o, o_ref[:, n * d:(n + 1) * d], rtol=0, atol=1e-12)
+            assert np.allclose(lse, lse_ref[n], rtol=0, atol=1e-12)
