@@ -11,7 +11,10 @@ two reduce shares.  The reduce shares are the rank's reduce-scatter rows
 Prints one JSON line.  Default workload: rank 0 of a 7B-class layer at TP=4
 (hidden 4096, 32 heads, ffn 16384, seq 4096, micro-batch 1, bf16).  With
 --workload moe-256e-top8-ep16 the step is one expert-parallel rank's MoE
-expert block instead (route, permute, grouped expert GEMMs, combine, backward).
+expert block instead (route, permute, grouped expert GEMMs, combine, backward);
+with --workload cp4-seq32k-7b-tp4 it is one context-parallel rank's causal
+attention forward share (by default the last of 4 ranks of a 32768-token
+sequence: its own chunk causally and the three earlier chunks in full).
 """
 from __future__ import annotations
 
@@ -34,7 +37,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=30)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="7b-tp4")
-    ap.add_argument("--rank", type=int, default=0)
+    ap.add_argument("--rank", type=int, default=None,
+                    help="the rank whose share runs (default 0; for a CP workload the last, busiest rank)")
     ap.add_argument("--precision", choices=("bf16", "fp8"), default="bf16",
                     help="fp8: the linears' GEMMs on per-tensor scaled E4M3/E5M2 codes (--fp8-format hybrid)")
     ap.add_argument("--sp", action="store_true",
@@ -248,6 +252,89 @@ def router_main(args):
     print(json.dumps(out), flush=True)
 
 
+def cp_flops(chunk, heads, d, rank):
+    """Algorithmic FLOP of CP rank `rank`'s causal attention forward: QK^T and
+    PV over the causal triangle of its own chunk (C(C+1)/2 scores) and over
+    every score of the `rank` earlier chunks, 2 products x 2 FLOP per score and
+    dimension."""
+    return float(heads) * (2.0 * chunk * (chunk + 1) * d + rank * 4.0 * chunk * chunk * d)
+
+
+def cp_cpu_baseline(shape, rank, bits, every):
+    """The CP oracle (fp64 numpy) on every `every`-th query row of the rank's chunk."""
+    import synth
+    from oracle import cp as CP
+    C = shape.chunk
+    full = synth.bf16_bits_to_f64(bits[: (rank + 1) * C])
+    rows = [rank * C + i for i in range(0, C, every)]
+    t0 = time.perf_counter()
+    CP.attention_rows(full, shape.heads, rows)
+    dt = time.perf_counter() - t0
+    fl = sum(4.0 * (i + 1) * shape.head_dim for i in rows) * shape.heads
+    return {"value": fl / dt / 1e12, "unit": "TFLOP/s", "cores": len(os.sched_getaffinity(0)), "kind": "oracle",
+            "sample": f"rank {rank}'s attention for every {every}th of its {C} query rows ({len(rows)} rows, "
+                      f"{shape.heads} heads, fp64 numpy), {dt:.2f} s"}
+
+
+def cp_main(args):
+    """One context-parallel rank's causal attention forward (mtl_cp_attn_fwd):
+    its chunk's queries against its own chunk (causal) and every earlier chunk,
+    merged by log-sum-exp."""
+    import torch
+    import synth
+    from megatron_tensor_transformer_layer_amd import mtl_cp_attn_fwd, mtl_cp_attn_scratch_bytes
+    from megatron_tensor_transformer_layer_amd.layer import bf16_dev
+
+    shape = synth.CP_WORKLOADS[args.workload]
+    C, H, d, cp = shape.chunk, shape.heads, shape.head_dim, shape.cp
+    r = cp - 1 if args.rank is None else args.rank
+    bits = synth.cp_qkv(shape)
+    qkv = bf16_dev(bits)
+    ld = 3 * H * d
+    chunks = [qkv.data_ptr() + j * C * ld * 2 for j in range(cp)]
+    o = torch.empty(C, H * d, dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty(H, C, dtype=torch.float32, device="cuda")
+    nb = mtl_cp_attn_scratch_bytes(cp, r, C, H, d)
+    scratch = torch.empty(max(nb, 1), dtype=torch.uint8, device="cuda")
+
+    def step():
+        mtl_cp_attn_fwd(cp, r, C, H, d, chunks, o, lse, scratch, nb)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for e0, e1 in ev:
+        e0.record()
+        step()
+        e1.record()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) / args.steps * 1e3
+    ev_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    fl = cp_flops(C, H, d, r)
+    achieved = fl / (ev_ms / 1e3) / 1e12
+    out = {
+        "metric": "TFLOP/s of one CP rank's causal attention forward share (bf16) and % of MI355X MFMA peak",
+        "value": round(fl / (ms / 1e3) / 1e12, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16",
+        "data": f"synthetic (QKV N(0,{synth.CP_QKV_STD:.2f}), the spread of a projection of N(0,1) activations)",
+        "config": {"workload": f"{args.workload}: CP rank {r} of {cp}, sequence {shape.seq} in chunks of {C}, "
+                               f"{H} heads of {d}; its chunk causal + {r} earlier chunks, log-sum-exp merge",
+                   "global_batch": 1, "seq_len": shape.seq, "parallelism": f"cp{cp}-rank{r}-of-1gpu"},
+        "pct_of_peak": round(100 * fl / (ms / 1e3) / 1e12 / PEAK_BF16_TFLOPS, 2),
+        "flop_per_step": fl,
+        "roofline": {"bound": "mfma",
+                     "kernel": "attn_fwd_kernel<128> (causal and unmasked variants) + cp_merge_kernel: the whole "
+                               "mtl_cp_attn_fwd call, timed with HIP events on its stream",
+                     "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None, "call_us": round(ev_ms * 1e3, 1)},
+        "cpu_baseline": None if args.no_cpu_baseline else cp_cpu_baseline(shape, r, bits, 16),
+    }
+    print(json.dumps(out), flush=True)
+
+
 def moe_main(args):
     """One EP rank's MoE expert block: route, permute, grouped fc1+GeLU, fc2,
     combine, and the backward (combine', grouped dgrad and wgrad, dX scatter)."""
@@ -261,7 +348,7 @@ def moe_main(args):
     from oracle.moe import moe_flops  # FLOP count only (closed form)
 
     shape = synth.MOE_WORKLOADS[args.workload]
-    r, El = args.rank, shape.experts // shape.ep
+    r, El = args.rank or 0, shape.experts // shape.ep
     lo = r * El
     w1 = torch.stack([synth.moe_expert_weight_device(shape, "moe_w1", lo + e) for e in range(El)])
     w2 = torch.stack([synth.moe_expert_weight_device(shape, "moe_w2", lo + e) for e in range(El)])
@@ -357,8 +444,11 @@ def main():
     if args.workload in synth.MOE_WORKLOADS:
         moe_main(args)
         return
+    if args.workload in synth.CP_WORKLOADS:
+        cp_main(args)
+        return
     shape = synth.WORKLOADS[args.workload]
-    t, r = shape.tp, args.rank
+    t, r = shape.tp, args.rank or 0
     inp = synth.layer_inputs(shape, tp=t, rank=r)
     fp8 = args.precision == "fp8"
     from megatron_tensor_transformer_layer_amd import MTL_PREC_BF16, MTL_PREC_FP8_HYBRID

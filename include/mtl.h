@@ -145,6 +145,33 @@ mtl_status mtl_reduce(int32_t t, const void* const* partials, const void* bias, 
 mtl_status mtl_allgather_rows(int32_t t, int32_t rank, const void* const* bufs, void* out, int64_t rows, int64_t cols,
                               mtl_stream_t stream);
 
+/* Context-parallel causal attention, forward: one CP rank's share.  Context
+ * parallelism (ai.lansai.wang/82226, the table of parallelism strategies and the
+ * tolerance section; navi2ai.com/sites/1106, --context-parallel-size) cuts the
+ * sequence across ranks while attention still needs every earlier rank's keys
+ * and values; the pages give no algorithm.  Here the sequence is cp contiguous
+ * chunks of `chunk` tokens and rank `rank` holds the queries of chunk `rank`.
+ * Its result is those rows of causal attention over the whole sequence: the
+ * rank's own chunk is attended causally, chunks rank-1, ..., 0 (the ring order
+ * in which a peer would pass them on) with every key visible, and the partial
+ * results are merged by their row log-sum-exp; later chunks are fully masked
+ * and not read.
+ * qkv_chunks: HOST array of cp device pointers, chunk j's head-interleaved QKV
+ * [chunk, 3*heads*head_dim] bf16 (head n: q, k, v at columns n*3d + [0, d),
+ * [d, 2d), [2d, 3d)); only entries 0..rank are read.  o: [chunk, heads*head_dim]
+ * bf16; lse: [heads, chunk] fp32 natural-log row log-sum-exp of the scaled
+ * scores (scale 1/sqrt(head_dim)).  scratch: device memory of at least
+ * mtl_cp_attn_scratch_bytes() bytes (none for rank 0), caller-owned, contents
+ * undefined afterwards.  Micro-batch 1.  chunk % 64 == 0, head_dim 64 or 128,
+ * 1 <= cp <= MTL_CP_MAX.  Errors: MTL_E_RANK, MTL_E_SHAPE, MTL_E_NULL,
+ * MTL_E_ALIGN (pointers 16-byte aligned), MTL_E_WORKSPACE. */
+#define MTL_CP_MAX 64
+mtl_status mtl_cp_attn_scratch_bytes(int32_t cp, int32_t rank, int64_t chunk, int32_t heads, int32_t head_dim,
+                                     size_t* scratch_bytes);
+mtl_status mtl_cp_attn_fwd(int32_t cp, int32_t rank, int64_t chunk, int32_t heads, int32_t head_dim,
+                           const void* const* qkv_chunks, void* o, float* lse, void* scratch, size_t scratch_bytes,
+                           mtl_stream_t stream);
+
 /* MLP half of the rank's forward (column-parallel fc1 with fused GeLU,
  * row-parallel fc2), with z = h . w1 + b1 in fp32:
  *   gz      = GeLU'(z)        [S, f/t] bf16 (saved: the backward needs z only

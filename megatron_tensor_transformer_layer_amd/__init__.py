@@ -21,6 +21,7 @@ MTL_E_ALIGN, MTL_E_WORKSPACE, MTL_E_UNSUPPORTED, MTL_E_HIP = 5, 6, 7, 8
 MTL_PREC_BF16, MTL_PREC_FP8_HYBRID = 0, 1
 MTL_FP8_E4M3, MTL_FP8_E5M2 = 0, 1
 MTL_FP8_AMAX_SCRATCH = 4096
+MTL_CP_MAX = 64
 MTL_F_RESIDUAL, MTL_F_WGRAD_ACCUM = 1, 2
 
 
@@ -51,6 +52,8 @@ _SIGS = {
     "mtl_attn_fwd": (ctypes.c_int, [_CFG, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "mtl_reduce": (ctypes.c_int, [_I32, ctypes.POINTER(_P), _P, _P, _P, _I64, _I64, _I64, _I64, _P]),
     "mtl_allgather_rows": (ctypes.c_int, [_I32, _I32, ctypes.POINTER(_P), _P, _I64, _I64, _P]),
+    "mtl_cp_attn_scratch_bytes": (ctypes.c_int, [_I32, _I32, _I64, _I32, _I32, ctypes.POINTER(_SZ)]),
+    "mtl_cp_attn_fwd": (ctypes.c_int, [_I32, _I32, _I64, _I32, _I32, ctypes.POINTER(_P), _P, _P, _P, _SZ, _P]),
     "mtl_mlp_fwd": (ctypes.c_int, [_CFG, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "mtl_mlp_bwd": (ctypes.c_int, [_CFG, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "mtl_attn_bwd": (ctypes.c_int, [_CFG, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
@@ -152,6 +155,20 @@ def mtl_allgather_rows(bufs, out, rows, cols, rank, stream=None):
     t = len(bufs)
     arr = (_P * t)(*[_ptr(b) for b in bufs])
     _check(lib().mtl_allgather_rows(t, rank, arr, _ptr(out), rows, cols, _stream(stream)), "mtl_allgather_rows")
+
+
+def mtl_cp_attn_scratch_bytes(cp, rank, chunk, heads, head_dim) -> int:
+    n = _SZ(0)
+    _check(lib().mtl_cp_attn_scratch_bytes(cp, rank, chunk, heads, head_dim, ctypes.byref(n)),
+           "mtl_cp_attn_scratch_bytes")
+    return int(n.value)
+
+
+def mtl_cp_attn_fwd(cp, rank, chunk, heads, head_dim, qkv_chunks, o, lse, scratch=None, scratch_bytes=None,
+                    stream=None):
+    arr = (_P * len(qkv_chunks))(*[_ptr(c) for c in qkv_chunks])
+    _check(lib().mtl_cp_attn_fwd(cp, rank, chunk, heads, head_dim, arr, _ptr(o), _ptr(lse), _ptr(scratch),
+                                 _nbytes(scratch, scratch_bytes), _stream(stream)), "mtl_cp_attn_fwd")
 
 
 def mtl_mlp_fwd(cfg, h, w1, b1, w2, gz, a, partial, scratch=None, scratch_bytes=None, stream=None):

@@ -375,6 +375,90 @@ mtl_status mtl_allgather_rows(int32_t t, int32_t rank, const void* const* bufs, 
                                    reinterpret_cast<hipStream_t>(stream)));
 }
 
+static mtl_status cp_check(int32_t cp, int32_t rank, int64_t chunk, int32_t heads, int32_t head_dim) {
+  if (cp < 1 || cp > MTL_CP_MAX) return MTL_E_SHAPE;
+  if (rank < 0 || rank >= cp) return MTL_E_RANK;
+  if (chunk <= 0 || chunk % 64 != 0 || heads <= 0 || (head_dim != 64 && head_dim != 128)) return MTL_E_SHAPE;
+  // the kernels address a chunk's QKV through 32-bit buffer offsets
+  if ((chunk + 64) * 3 * heads * head_dim * 2 > (int64_t)UINT32_MAX) return MTL_E_SHAPE;
+  return MTL_OK;
+}
+
+// One partial (O_j, L_j) per key chunk the rank's queries see; none for rank 0.
+static size_t cp_slot_o(int64_t chunk, int32_t heads, int32_t head_dim) { return up(chunk * heads * head_dim * 2); }
+static size_t cp_slot_l(int64_t chunk, int32_t heads) { return up(chunk * heads * 4); }
+
+mtl_status mtl_cp_attn_scratch_bytes(int32_t cp, int32_t rank, int64_t chunk, int32_t heads, int32_t head_dim,
+                                     size_t* scratch_bytes) {
+  mtl_status st = cp_check(cp, rank, chunk, heads, head_dim);
+  if (st != MTL_OK) return st;
+  if (!scratch_bytes) return MTL_E_NULL;
+  *scratch_bytes = rank == 0 ? 0 : (size_t)(rank + 1) * (cp_slot_o(chunk, heads, head_dim) + cp_slot_l(chunk, heads));
+  return MTL_OK;
+}
+
+mtl_status mtl_cp_attn_fwd(int32_t cp, int32_t rank, int64_t chunk, int32_t heads, int32_t head_dim,
+                           const void* const* qkv_chunks, void* o, float* lse, void* scratch, size_t scratch_bytes,
+                           mtl_stream_t stream) {
+  mtl_status st = cp_check(cp, rank, chunk, heads, head_dim);
+  if (st != MTL_OK) return st;
+  if (!qkv_chunks) return MTL_E_NULL;
+  for (int j = 0; j <= rank; ++j)
+    if ((st = check_ptrs(qkv_chunks[j])) != MTL_OK) return st;
+  if ((st = check_ptrs(o, lse)) != MTL_OK) return st;
+  size_t need = 0;
+  mtl_cp_attn_scratch_bytes(cp, rank, chunk, heads, head_dim, &need);
+  if (need) {
+    if ((st = check_ptrs(scratch)) != MTL_OK) return st;
+    if (scratch_bytes < need) return MTL_E_WORKSPACE;
+  }
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  AttnArgs a{};
+  a.ld_qkv = 3 * (int64_t)heads * head_dim;
+  a.ld_o = (int64_t)heads * head_dim;
+  a.seq = (int)chunk;
+  a.batch = 1;
+  a.heads = heads;
+  a.d = head_dim;
+  a.scale = 1.0f / sqrtf((float)head_dim);
+  a.qkv = static_cast<const uint16_t*>(qkv_chunks[rank]);
+  if (rank == 0) {  // the first chunk sees only itself
+    a.o = static_cast<uint16_t*>(o);
+    a.lse = lse;
+    return hip_status(attention_fwd(a, s));
+  }
+  // ring order: the rank's own chunk (causal), then chunks rank-1, ..., 0 as
+  // they would arrive from the previous rank (every key visible); chunks
+  // after the rank are masked out entirely and take no work
+  const size_t so = cp_slot_o(chunk, heads, head_dim), sl = cp_slot_l(chunk, heads);
+  char* base = static_cast<char*>(scratch);
+  uint16_t* o_parts = reinterpret_cast<uint16_t*>(base);
+  float* l_parts = reinterpret_cast<float*>(base + (size_t)(rank + 1) * so);
+  for (int k = 0; k <= rank; ++k) {
+    a.o = reinterpret_cast<uint16_t*>(base + (size_t)k * so);
+    a.lse = reinterpret_cast<float*>(base + (size_t)(rank + 1) * so + (size_t)k * sl);
+    if (k == 0) {
+      MTL_TRY(attention_fwd(a, s));
+    } else {
+      a.kv = static_cast<const uint16_t*>(qkv_chunks[rank - k]);
+      a.kv_seq = (int)chunk;
+      MTL_TRY(attention_fwd_full(a, s));
+    }
+  }
+  CpMergeArgs m{};
+  m.o_parts = o_parts;
+  m.lse_parts = l_parts;
+  m.o_stride = (int64_t)(so / 2);
+  m.lse_stride = (int64_t)(sl / 4);
+  m.nparts = rank + 1;
+  m.tokens = chunk;
+  m.heads = heads;
+  m.d = head_dim;
+  m.o = static_cast<uint16_t*>(o);
+  m.lse = lse;
+  return hip_status(cp_merge(m, s));
+}
+
 mtl_status mtl_mlp_fwd(const mtl_layer_cfg* c, const void* h, const void* w1, const void* b1, const void* w2, void* gz,
                        void* a, void* partial, void* scratch, size_t scratch_bytes, mtl_stream_t stream) {
   mtl_status st = mtl_validate(c);

@@ -93,7 +93,10 @@ struct FwdTiles {
   }
 };
 
-template <int D>
+// FULL: queries of a.qkv against every key of a separate chunk a.kv (a.kv_seq
+// keys, a multiple of 64, same head-interleaved layout): no mask, every item
+// takes all key blocks.  Otherwise causal self-attention of a.qkv.
+template <int D, bool FULL>
 __global__ __launch_bounds__(256, 1) void attn_fwd_kernel(AttnArgs a) {
   using T = FwdTiles<D>;
   constexpr int KS = D / 16;
@@ -116,8 +119,11 @@ __global__ __launch_bounds__(256, 1) void attn_fwd_kernel(AttnArgs a) {
   const int colq = n * 3 * D;
   const uint16_t* qbase = a.qkv + tok0 * a.ld_qkv + colq;
   const float c = a.scale * LOG2E;
-  const i32x4 rs = make_rsrc(a.qkv, (uint32_t)(tokens * a.ld_qkv * 2));
-  const int nkb_all = nitems;
+  // K and V tiles come from the buffer resource rs, starting at token kvtok0
+  const i32x4 rs = FULL ? make_rsrc(a.kv, (uint32_t)((int64_t)a.kv_seq * a.batch * a.ld_qkv * 2))
+                        : make_rsrc(a.qkv, (uint32_t)(tokens * a.ld_qkv * 2));
+  const int64_t kvtok0 = FULL ? (int64_t)b * a.kv_seq : tok0;
+  const int nkb_all = FULL ? a.kv_seq / 64 : nitems;
 
   for (int side = 0; side < 2; ++side) {
     const int item = side == 0 ? pair : nitems - 1 - pair;
@@ -126,7 +132,7 @@ __global__ __launch_bounds__(256, 1) void attn_fwd_kernel(AttnArgs a) {
     const int qw = q0 + qsub * 32;
     const int q = qw + (lane & 31);
     const bool qok = q < a.seq;
-    const int nkb = min(item + 1, nkb_all);
+    const int nkb = FULL ? nkb_all : min(item + 1, nkb_all);
     const int niter = (nkb + 1) / 2;
 
     u32x4 qf[KS];
@@ -150,8 +156,8 @@ __global__ __launch_bounds__(256, 1) void attn_fwd_kernel(AttnArgs a) {
       for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
         for (int sb = 0; sb < 2; ++sb) s[sb] = mfma32(T::kfrag(kt, sb * 32, ks, lane), qf[ks], s[sb]);
-      const bool diag = (k0 + 63 > qw);
-      // every processed block holds key k0 <= q, so bmax is finite
+      const bool diag = !FULL && (k0 + 63 > qw);
+      // every processed block holds key k0 <= q (or, FULL, 64 unmasked keys), so bmax is finite
       if (diag) {  // wave-uniform: only the diagonal block is masked
         asm volatile("" ::: "memory");
 #pragma unroll
@@ -200,23 +206,23 @@ __global__ __launch_bounds__(256, 1) void attn_fwd_kernel(AttnArgs a) {
       }
     };
 
-    T::load(rs, a.ld_qkv, tok0, colq, 0, st0);
+    T::load(rs, a.ld_qkv, kvtok0, colq, 0, st0);
     wait_dma();
     __syncthreads();
     for (int it = 0; it < niter; it += 2) {
       const bool more1 = it + 1 < niter;
-      if (more1) T::load(rs, a.ld_qkv, tok0, colq, 2 * (it + 1), st1);
+      if (more1) T::load(rs, a.ld_qkv, kvtok0, colq, 2 * (it + 1), st1);
       {
         const int kb = 2 * it + kpar;
-        if (kb < nkb && kb * 64 <= qw + 31) block(st0, kb);
+        if (kb < nkb && (FULL || kb * 64 <= qw + 31)) block(st0, kb);
       }
       if (more1) wait_dma();
       __syncthreads();
       if (more1) {
         const bool more2 = it + 2 < niter;
-        if (more2) T::load(rs, a.ld_qkv, tok0, colq, 2 * (it + 2), st0);
+        if (more2) T::load(rs, a.ld_qkv, kvtok0, colq, 2 * (it + 2), st0);
         const int kb = 2 * (it + 1) + kpar;
-        if (kb < nkb && kb * 64 <= qw + 31) block(st1, kb);
+        if (kb < nkb && (FULL || kb * 64 <= qw + 31)) block(st1, kb);
         if (more2) wait_dma();
         __syncthreads();
       }
@@ -563,12 +569,12 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_kernel(AttnArgs a) {
 }
 
 // ============================================================== launchers
-template <int D>
+template <int D, bool FULL>
 static hipError_t fwd_d(const AttnArgs& a, hipStream_t s) {
   const int64_t npairs = ((a.seq + 63) / 64 + 1) / 2;
   const int64_t units = npairs * a.heads * a.batch;
   if (units > INT32_MAX) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(attn_fwd_kernel<D>, dim3((unsigned)units), dim3(256), 0, s, a);
+  hipLaunchKernelGGL((attn_fwd_kernel<D, FULL>), dim3((unsigned)units), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
@@ -586,8 +592,16 @@ static hipError_t bwd_d(const AttnArgs& a, hipStream_t s) {
 
 hipError_t attention_fwd(const AttnArgs& a, hipStream_t s) {
   if (a.seq <= 0) return hipSuccess;
-  if (a.d == 64) return fwd_d<64>(a, s);
-  if (a.d == 128) return fwd_d<128>(a, s);
+  if (a.d == 64) return fwd_d<64, false>(a, s);
+  if (a.d == 128) return fwd_d<128, false>(a, s);
+  return hipErrorInvalidValue;
+}
+
+hipError_t attention_fwd_full(const AttnArgs& a, hipStream_t s) {
+  if (a.seq <= 0) return hipSuccess;
+  if (!a.kv || a.kv_seq <= 0 || a.kv_seq % 64 != 0) return hipErrorInvalidValue;
+  if (a.d == 64) return fwd_d<64, true>(a, s);
+  if (a.d == 128) return fwd_d<128, true>(a, s);
   return hipErrorInvalidValue;
 }
 
@@ -596,6 +610,52 @@ hipError_t attention_bwd(const AttnArgs& a, hipStream_t s) {
   if (a.d == 64) return bwd_d<64>(a, s);
   if (a.d == 128) return bwd_d<128>(a, s);
   return hipErrorInvalidValue;
+}
+
+// ============================================================== context-parallel merge
+// The partial results of one set of queries against separate key chunks,
+// (O_j, L_j) for j = 0 .. nparts-1, combine into the attention over all of
+// them: L = log sum_j exp(L_j), O = sum_j exp(L_j - L) O_j, in ascending j,
+// fp32.  d/8 lanes per (token, head) row, 16 bytes of each O_j per lane; rows
+// are numbered token-major so a wave reads whole O rows.
+__global__ __launch_bounds__(256) void cp_merge_kernel(CpMergeArgs a) {
+  const int lanes = a.d / 8;
+  const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t row = gid / lanes;
+  if (row >= a.tokens * a.heads) return;
+  const int sub = (int)(gid % lanes);
+  const int64_t tok = row / a.heads;
+  const int n = (int)(row % a.heads);
+  const int64_t li = (int64_t)n * a.tokens + tok;
+  float m = -INFINITY;
+  for (int j = 0; j < a.nparts; ++j) m = fmaxf(m, a.lse_parts[j * a.lse_stride + li]);
+  float z = 0.f;
+  for (int j = 0; j < a.nparts; ++j) z += expf(a.lse_parts[j * a.lse_stride + li] - m);
+  const float L = m + logf(z);
+  const int64_t oi = tok * a.heads * a.d + (int64_t)n * a.d + sub * 8;
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  for (int j = 0; j < a.nparts; ++j) {
+    const float w = expf(a.lse_parts[j * a.lse_stride + li] - L);
+    const u32x4 v = *reinterpret_cast<const u32x4*>(a.o_parts + j * a.o_stride + oi);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      acc[2 * e] += w * bf16_lo(v[e]);
+      acc[2 * e + 1] += w * bf16_hi(v[e]);
+    }
+  }
+  *reinterpret_cast<u32x4*>(a.o + oi) = u32x4{pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]),
+                                              pack_bf16x2(acc[4], acc[5]), pack_bf16x2(acc[6], acc[7])};
+  if (sub == 0) a.lse[li] = L;
+}
+
+hipError_t cp_merge(const CpMergeArgs& a, hipStream_t s) {
+  if (a.tokens <= 0 || a.nparts <= 0) return hipSuccess;
+  if (a.d % 8 != 0 || a.d > 2048) return hipErrorInvalidValue;
+  const int64_t threads = a.tokens * a.heads * (a.d / 8);
+  const int64_t blocks = (threads + 255) / 256;
+  if (blocks > INT32_MAX) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(cp_merge_kernel, dim3((unsigned)blocks), dim3(256), 0, s, a);
+  return hipGetLastError();
 }
 
 }  // namespace mtl

@@ -92,8 +92,27 @@ struct AttnArgs {
   const float* lse_in;
   float* delta;          // D = rowsum(dO * O), [heads, tokens]
   uint16_t* dqkv;        // [tokens, 3*heads*d], stride ld_qkv
+  // attention_fwd_full: keys and values of a separate chunk [kv_seq, ...], stride ld_qkv
+  const uint16_t* kv;
+  int kv_seq;
 };
 hipError_t attention_fwd(const AttnArgs& a, hipStream_t s);
+// Queries of a.qkv against all a.kv_seq keys of a.kv (no mask; kv_seq % 64 == 0).
+hipError_t attention_fwd_full(const AttnArgs& a, hipStream_t s);
+// Log-sum-exp merge of nparts partial attention results (O_j [tokens, heads*d]
+// bf16 at o_parts + j*o_stride, L_j [heads, tokens] fp32 at lse_parts +
+// j*lse_stride) into o and lse, summed in ascending j.
+struct CpMergeArgs {
+  const uint16_t* o_parts;
+  const float* lse_parts;
+  int64_t o_stride, lse_stride;
+  int nparts;
+  int64_t tokens;
+  int heads, d;
+  uint16_t* o;
+  float* lse;
+};
+hipError_t cp_merge(const CpMergeArgs& a, hipStream_t s);
 hipError_t attention_bwd(const AttnArgs& a, hipStream_t s);
 
 // ---------------------------------------------------------------- reductions

@@ -214,3 +214,37 @@ def test_router_validation_before_any_launch(mtl):
     assert lib.mtl_moe_router_bwd(ctypes.byref(cfg), *args, 0.001, None, P, P, P, P, n - 1, None) == \
         mtl.MTL_E_WORKSPACE
     assert lib.mtl_moe_router_bwd(ctypes.byref(cfg), *args, 0.001, None, P, P, None, P, n, None) == mtl.MTL_E_NULL
+
+
+def test_cp_attention_validation_before_any_launch(mtl):
+    """mtl_cp_attn_fwd / _scratch_bytes refuse bad shapes, ranks, pointers and
+    scratch on the host; the fake addresses are never dereferenced."""
+    lib = mtl.lib()
+    P = 1 << 20
+    n = ctypes.c_size_t(0)
+    sb = lambda *a: lib.mtl_cp_attn_scratch_bytes(*a, ctypes.byref(n))
+    assert sb(4, 0, 256, 2, 128) == mtl.MTL_OK and n.value == 0  # rank 0 merges nothing
+    assert sb(4, 3, 256, 2, 128) == mtl.MTL_OK
+    # four partials: O_j [256, 2*128] bf16 and L_j [2, 256] fp32 each, 256-byte aligned
+    assert n.value == 4 * (256 * 256 * 2 + 2 * 256 * 4)
+    assert sb(4, 4, 256, 2, 128) == mtl.MTL_E_RANK
+    assert sb(4, -1, 256, 2, 128) == mtl.MTL_E_RANK
+    assert sb(0, 0, 256, 2, 128) == mtl.MTL_E_SHAPE
+    assert sb(mtl.MTL_CP_MAX + 1, 0, 256, 2, 128) == mtl.MTL_E_SHAPE
+    assert sb(4, 1, 200, 2, 128) == mtl.MTL_E_SHAPE  # chunk % 64
+    assert sb(4, 1, 256, 2, 96) == mtl.MTL_E_SHAPE  # head_dim 64 or 128
+    assert sb(4, 1, 256, 0, 128) == mtl.MTL_E_SHAPE
+    assert sb(4, 1, 1 << 22, 64, 128) == mtl.MTL_E_SHAPE  # past 32-bit buffer offsets
+    assert lib.mtl_cp_attn_scratch_bytes(4, 1, 256, 2, 128, None) == mtl.MTL_E_NULL
+
+    chunks = (ctypes.c_void_p * 4)(P, P + 4096, None, None)  # only entries 0..rank are read
+    need = 2 * (256 * 256 * 2 + 2 * 256 * 4)
+    fwd = lambda rank, ch, o, lse, scr, nb: lib.mtl_cp_attn_fwd(4, rank, 256, 2, 128, ch, o, lse, scr, nb, None)
+    assert fwd(1, chunks, P, P, P, need - 1) == mtl.MTL_E_WORKSPACE
+    assert fwd(1, chunks, P, P, None, need) == mtl.MTL_E_NULL
+    assert fwd(2, chunks, P, P, P, 10 * need) == mtl.MTL_E_NULL  # chunk 2 missing
+    assert fwd(1, None, P, P, P, need) == mtl.MTL_E_NULL
+    assert fwd(1, chunks, None, P, P, need) == mtl.MTL_E_NULL
+    assert fwd(1, chunks, P + 8, P, P, need) == mtl.MTL_E_ALIGN
+    assert fwd(1, (ctypes.c_void_p * 2)(P, P + 2), P, P, P, need) == mtl.MTL_E_ALIGN
+    assert fwd(4, chunks, P, P, P, need) == mtl.MTL_E_RANK
