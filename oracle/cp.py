@@ -1,4 +1,5 @@
-"""fp64 oracle of one context-parallel rank's share of causal attention (forward).
+"""fp64 oracle of one context-parallel rank's share of causal attention, forward
+and backward.
 
 Test infrastructure only (see the package docstring).
 
@@ -11,8 +12,10 @@ and deploy examples) sets `--context-parallel-size`.  Neither fixes how the
 sequence is assigned to ranks.  Reading taken here: the S tokens are cut into
 cp contiguous chunks of C = S/cp, rank r holds the queries of chunk r, and its
 result is rows [rC, (r+1)C) of the causal attention over the whole sequence
-(O and the row log-sum-exp), i.e. the plain definition.  How a device splits
-that work over key chunks is not restated here.
+(O and the row log-sum-exp), i.e. the plain definition.  Its backward is the
+gradient that its rows' dO sends into the QKV of the sequence: the complete dQ
+of its queries and a dK/dV share for every chunk up to its own.  How a device
+splits that work over key chunks is not restated here.
 """
 from __future__ import annotations
 
@@ -66,3 +69,34 @@ def attention_rows(qkv_full, heads: int, rows) -> tuple:
             o[j, n * d:(n + 1) * d] = (e / z) @ qkv_full[: i + 1, sv]
             lse[n, j] = m + math.log(z)
     return o, lse
+
+
+def rank_attention_backward(qkv_full, do_rank, heads: int, cp: int, rank: int) -> dict:
+    """Gradients that flow from CP rank `rank`'s output gradient dO [C, heads*d]
+    (its own rows only) back into the QKV of the sequence, split the way the
+    ranks own them:
+
+    * ``dq``: dQ of the rank's queries [C, heads*d] (heads in order), complete;
+    * ``dkv[j]`` for j <= rank: the [C, 2*heads*d] dK and dV (per head
+      [dK_n | dV_n]) of chunk j's keys from the rank's queries, the share the
+      rank hands back to chunk j's owner (for j = rank, its own diagonal share).
+
+    Definition: the causal attention backward over the whole sequence with dO
+    zero outside the rank's rows; chunks after the rank receive nothing."""
+    qkv_full = np.asarray(qkv_full, dtype=np.float64)
+    rows = chunk_rows(qkv_full.shape[0], cp, rank)
+    prefix = qkv_full[: rows.stop]
+    d = prefix.shape[1] // (3 * heads)
+    do_full = np.zeros((prefix.shape[0], heads * d))
+    do_full[rows] = np.asarray(do_rank, dtype=np.float64)
+    g = L.attention_backward(prefix, do_full, heads)
+    dq = np.concatenate([g[rows, L.head_slices(heads, d, n)[0]] for n in range(heads)], axis=1)
+    dkv = []
+    for j in range(rank + 1):
+        rj = chunk_rows(qkv_full.shape[0], cp, j)
+        parts = []
+        for n in range(heads):
+            _, sk, sv = L.head_slices(heads, d, n)
+            parts += [g[rj, sk], g[rj, sv]]
+        dkv.append(np.concatenate(parts, axis=1))
+    return dict(dq=dq, dkv=dkv)

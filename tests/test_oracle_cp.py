@@ -1,6 +1,7 @@
 """Pins of the context-parallel attention oracle (oracle/cp.py) against closed
-forms, invariants of the causal mask across chunks, and the log-sum-exp merge
-identity, independent of the oracle's own code path."""
+forms, invariants of the causal mask across chunks, the log-sum-exp merge
+identity, and (backward) linearity over the ranks and finite differences,
+independent of the oracle's own code path."""
 import math
 
 import numpy as np
@@ -103,3 +104,59 @@ def test_merge_of_chunk_partials_equals_the_rank_rows():
             o = sum(np.exp(p[1] - lse)[:, None] * p[0] for p in parts)
             assert np.allclose(o, o_ref[:, n * d:(n + 1) * d], rtol=0, atol=1e-12)
             assert np.allclose(lse, lse_ref[n], rtol=0, atol=1e-12)
+
+
+def test_backward_cp1_is_plain_attention_backward():
+    seq, heads, d = 24, 2, 4
+    qkv = _qkv(8, seq, heads, d)
+    do = _qkv(9, seq, heads, d)[:, : heads * d]
+    g = CP.rank_attention_backward(qkv, do, heads, 1, 0)
+    ref = L.attention_backward(qkv, do, heads)
+    for n in range(heads):
+        sq, sk, sv = L.head_slices(heads, d, n)
+        assert np.array_equal(g["dq"][:, n * d:(n + 1) * d], ref[:, sq])
+        assert np.array_equal(g["dkv"][0][:, 2 * n * d:(2 * n + 1) * d], ref[:, sk])
+        assert np.array_equal(g["dkv"][0][:, (2 * n + 1) * d:(2 * n + 2) * d], ref[:, sv])
+
+
+def test_backward_shares_of_all_ranks_add_up_to_the_full_gradient():
+    """Linearity in dO: every rank's dQ rows, and the dK/dV shares every rank
+    hands each chunk summed over the ranks, give the backward of the whole
+    sequence's dO."""
+    seq, cp, heads, d = 64, 4, 2, 8
+    c = seq // cp
+    qkv = _qkv(10, seq, heads, d, std=1.2)
+    do = _qkv(11, seq, heads, d)[:, : heads * d]
+    ref = L.attention_backward(qkv, do, heads)
+    dq = np.zeros((seq, heads * d))
+    dkv = np.zeros((seq, 2 * heads * d))
+    for r in range(cp):
+        g = CP.rank_attention_backward(qkv, do[r * c:(r + 1) * c], heads, cp, r)
+        dq[r * c:(r + 1) * c] = g["dq"]
+        for j, part in enumerate(g["dkv"]):
+            dkv[j * c:(j + 1) * c] += part
+    for n in range(heads):
+        sq, sk, sv = L.head_slices(heads, d, n)
+        assert np.allclose(dq[:, n * d:(n + 1) * d], ref[:, sq], rtol=0, atol=1e-12)
+        assert np.allclose(dkv[:, 2 * n * d:(2 * n + 1) * d], ref[:, sk], rtol=0, atol=1e-12)
+        assert np.allclose(dkv[:, (2 * n + 1) * d:(2 * n + 2) * d], ref[:, sv], rtol=0, atol=1e-12)
+
+
+def test_backward_by_finite_differences_through_the_rank_loss():
+    """dq and the dkv shares are the gradient of <dO, O_rank> with respect to
+    the rank's queries and each earlier chunk's keys and values."""
+    seq, cp, heads, d, r = 32, 4, 1, 4, 2
+    c = seq // cp
+    qkv = _qkv(12, seq, heads, d)
+    do = _qkv(13, c, heads, d)[:, : heads * d]
+    g = CP.rank_attention_backward(qkv, do, heads, cp, r)
+    loss = lambda t: float(np.sum(CP.rank_attention(t, heads, cp, r)[0] * do))
+    sq, sk, sv = L.head_slices(heads, d, 0)
+    eps = 1e-6
+    for tok, col, want in [(r * c + 3, sq.start + 1, g["dq"][3, 1]), (5, sk.start + 2, g["dkv"][0][5, 2]),
+                           (c + 7, sv.start, g["dkv"][1][7, d]), (r * c + 1, sk.start, g["dkv"][r][1, 0])]:
+        p, m = qkv.copy(), qkv.copy()
+        p[tok, col] += eps
+        m[tok, col] -= eps
+        fd = (loss(p) - loss(m)) / (2 * eps)
+        assert abs(fd - want) < 1e-7 * max(1.0, abs(want)), (tok, col, fd, want)
