@@ -13,8 +13,9 @@ Prints one JSON line.  Default workload: rank 0 of a 7B-class layer at TP=4
 --workload moe-256e-top8-ep16 the step is one expert-parallel rank's MoE
 expert block instead (route, permute, grouped expert GEMMs, combine, backward);
 with --workload cp4-seq32k-7b-tp4 it is one context-parallel rank's causal
-attention forward share (by default the last of 4 ranks of a 32768-token
-sequence: its own chunk causally and the three earlier chunks in full).
+attention share, forward and backward (by default the last of 4 ranks of a
+32768-token sequence: its own chunk causally and the three earlier chunks in
+full).
 """
 from __future__ import annotations
 
@@ -260,29 +261,34 @@ def cp_flops(chunk, heads, d, rank):
     return float(heads) * (2.0 * chunk * (chunk + 1) * d + rank * 4.0 * chunk * chunk * d)
 
 
-def cp_cpu_baseline(shape, rank, bits, every):
-    """The CP oracle (fp64 numpy) on every `every`-th query row of the rank's chunk."""
+def cp_cpu_baseline(shape, rank, sample_seq, sample_heads):
+    """The CP oracle (fp64 numpy, as it stands) on a bounded sample of the
+    workload: the same rank of the same CP degree over a sequence of sample_seq
+    tokens with sample_heads heads, forward and backward."""
     import synth
     from oracle import cp as CP
-    C = shape.chunk
-    full = synth.bf16_bits_to_f64(bits[: (rank + 1) * C])
-    rows = [rank * C + i for i in range(0, C, every)]
+    sub = synth.CpShape(seq=sample_seq, heads=sample_heads, head_dim=shape.head_dim, cp=shape.cp)
+    full = synth.bf16_bits_to_f64(synth.cp_qkv(sub))
+    do = synth.bf16_bits_to_f64(synth.cp_dout(sub))
     t0 = time.perf_counter()
-    CP.attention_rows(full, shape.heads, rows)
+    CP.rank_attention(full, sub.heads, sub.cp, rank)
+    CP.rank_attention_backward(full, do, sub.heads, sub.cp, rank)
     dt = time.perf_counter() - t0
-    fl = sum(4.0 * (i + 1) * shape.head_dim for i in rows) * shape.heads
+    fl = 3.0 * cp_flops(sub.chunk, sub.heads, sub.head_dim, rank)
     return {"value": fl / dt / 1e12, "unit": "TFLOP/s", "cores": len(os.sched_getaffinity(0)), "kind": "oracle",
-            "sample": f"rank {rank}'s attention for every {every}th of its {C} query rows ({len(rows)} rows, "
-                      f"{shape.heads} heads, fp64 numpy), {dt:.2f} s"}
+            "sample": f"rank {rank} of CP {sub.cp} over a {sample_seq}-token sequence (chunks of {sub.chunk}), "
+                      f"{sample_heads} of {shape.heads} heads, forward+backward (fp64 numpy), {dt:.2f} s"}
 
 
 def cp_main(args):
-    """One context-parallel rank's causal attention forward (mtl_cp_attn_fwd):
-    its chunk's queries against its own chunk (causal) and every earlier chunk,
-    merged by log-sum-exp."""
+    """One context-parallel rank's causal attention share, forward and backward
+    (mtl_cp_attn_fwd, mtl_cp_attn_bwd): its chunk's queries against its own
+    chunk (causal) and every earlier chunk, merged by log-sum-exp; then dQ of
+    its queries and the dK/dV shares of every chunk up to its own."""
     import torch
     import synth
-    from megatron_tensor_transformer_layer_amd import mtl_cp_attn_fwd, mtl_cp_attn_scratch_bytes
+    from megatron_tensor_transformer_layer_amd import (mtl_cp_attn_bwd, mtl_cp_attn_bwd_scratch_bytes,
+                                                       mtl_cp_attn_fwd, mtl_cp_attn_scratch_bytes)
     from megatron_tensor_transformer_layer_amd.layer import bf16_dev
 
     shape = synth.CP_WORKLOADS[args.workload]
@@ -290,47 +296,66 @@ def cp_main(args):
     r = cp - 1 if args.rank is None else args.rank
     bits = synth.cp_qkv(shape)
     qkv = bf16_dev(bits)
+    dout = bf16_dev(synth.cp_dout(shape))
     ld = 3 * H * d
     chunks = [qkv.data_ptr() + j * C * ld * 2 for j in range(cp)]
     o = torch.empty(C, H * d, dtype=torch.bfloat16, device="cuda")
     lse = torch.empty(H, C, dtype=torch.float32, device="cuda")
-    nb = mtl_cp_attn_scratch_bytes(cp, r, C, H, d)
-    scratch = torch.empty(max(nb, 1), dtype=torch.uint8, device="cuda")
+    dqkv = torch.empty(C, ld, dtype=torch.bfloat16, device="cuda")
+    dkv = [torch.empty(C, ld, dtype=torch.bfloat16, device="cuda") for _ in range(r)]
+    nf = mtl_cp_attn_scratch_bytes(cp, r, C, H, d)
+    nbw = mtl_cp_attn_bwd_scratch_bytes(cp, r, C, H, d)
+    scratch = torch.empty(max(nf, nbw, 1), dtype=torch.uint8, device="cuda")
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+    marks = []
 
-    def step():
-        mtl_cp_attn_fwd(cp, r, C, H, d, chunks, o, lse, scratch, nb)
+    def step(record=False):
+        e = [ev(), ev(), ev()] if record else None
+        if record:
+            e[0].record()
+        mtl_cp_attn_fwd(cp, r, C, H, d, chunks, o, lse, scratch, nf)
+        if record:
+            e[1].record()
+        mtl_cp_attn_bwd(cp, r, C, H, d, chunks, o, lse, dout, dqkv, dkv, scratch, nbw)
+        if record:
+            e[2].record()
+            marks.append(e)
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
     t0 = time.perf_counter()
-    for e0, e1 in ev:
-        e0.record()
-        step()
-        e1.record()
+    for _ in range(args.steps):
+        step(record=True)
     torch.cuda.synchronize()
     ms = (time.perf_counter() - t0) / args.steps * 1e3
-    ev_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
-    fl = cp_flops(C, H, d, r)
-    achieved = fl / (ev_ms / 1e3) / 1e12
+    fwd_ms = float(np.mean([m[0].elapsed_time(m[1]) for m in marks]))
+    bwd_ms = float(np.mean([m[1].elapsed_time(m[2]) for m in marks]))
+    ffl = cp_flops(C, H, d, r)
+    fl = 3.0 * ffl  # the backward counts twice the forward
+    achieved = 2.0 * ffl / (bwd_ms / 1e3) / 1e12
     out = {
-        "metric": "TFLOP/s of one CP rank's causal attention forward share (bf16) and % of MI355X MFMA peak",
+        "metric": "TFLOP/s of one CP rank's causal attention share fwd+bwd (bf16) and % of MI355X MFMA peak",
         "value": round(fl / (ms / 1e3) / 1e12, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "bf16",
-        "data": f"synthetic (QKV N(0,{synth.CP_QKV_STD:.2f}), the spread of a projection of N(0,1) activations)",
+        "data": f"synthetic (QKV N(0,{synth.CP_QKV_STD:.2f}), the spread of a projection of N(0,1) activations; "
+                f"dO N(0,1))",
         "config": {"workload": f"{args.workload}: CP rank {r} of {cp}, sequence {shape.seq} in chunks of {C}, "
-                               f"{H} heads of {d}; its chunk causal + {r} earlier chunks, log-sum-exp merge",
+                               f"{H} heads of {d}; its chunk causal + {r} earlier chunks, log-sum-exp merge; "
+                               f"backward to dQ and the dK/dV shares of chunks 0..{r}",
                    "global_batch": 1, "seq_len": shape.seq, "parallelism": f"cp{cp}-rank{r}-of-1gpu"},
         "pct_of_peak": round(100 * fl / (ms / 1e3) / 1e12 / PEAK_BF16_TFLOPS, 2),
         "flop_per_step": fl,
         "roofline": {"bound": "mfma",
-                     "kernel": "attn_fwd_kernel<128> (causal and unmasked variants) + cp_merge_kernel: the whole "
-                               "mtl_cp_attn_fwd call, timed with HIP events on its stream",
+                     "kernel": "attn_bwd_kernel<128> (causal and unmasked variants) with the D and dQ-sum "
+                               "launches: the whole mtl_cp_attn_bwd call (2x the forward FLOP), timed with HIP "
+                               "events on its stream",
                      "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None, "call_us": round(ev_ms * 1e3, 1)},
-        "cpu_baseline": None if args.no_cpu_baseline else cp_cpu_baseline(shape, r, bits, 16),
+                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "bwd_call_us": round(bwd_ms * 1e3, 1), "fwd_call_us": round(fwd_ms * 1e3, 1),
+                     "fwd_tflops": round(ffl / (fwd_ms / 1e3) / 1e12, 1)},
+        "cpu_baseline": None if args.no_cpu_baseline else cp_cpu_baseline(shape, r, 8192, 8),
     }
     print(json.dumps(out), flush=True)
 

@@ -172,6 +172,30 @@ mtl_status mtl_cp_attn_fwd(int32_t cp, int32_t rank, int64_t chunk, int32_t head
                            const void* const* qkv_chunks, void* o, float* lse, void* scratch, size_t scratch_bytes,
                            mtl_stream_t stream);
 
+/* Context-parallel causal attention, backward: the gradients that CP rank
+ * `rank`'s output gradient sends into the QKV of the sequence (same chunks and
+ * reading as mtl_cp_attn_fwd).  o and lse: the rank's merged forward results;
+ * dout: dO of its rows, [chunk, heads*head_dim] bf16.  Writes
+ *   dqkv [chunk, 3*heads*head_dim] bf16, head-interleaved like the QKV: the
+ *     query columns get the complete dQ of the rank's queries (over all chunks
+ *     0..rank); the key and value columns get the dK, dV of the rank's own chunk
+ *     from its own queries only (the later ranks' queries add their shares);
+ *   dkv_chunks[j] for j < rank (HOST array of device pointers, entries 0..rank-1
+ *     read): the key and value columns of a [chunk, 3*heads*head_dim] bf16
+ *     tensor of chunk j's layout get the dK, dV share of chunk j's keys from the
+ *     rank's queries -- what it hands back to chunk j's owner; query columns
+ *     are not touched.
+ * scratch: at least mtl_cp_attn_bwd_scratch_bytes() bytes (D = rowsum(dO*O)
+ * and one dQ partial per earlier chunk), caller-owned.  dQ sums the rank's own
+ * chunk first, then chunks rank-1, ..., 0, in fp32 over bf16 partials.
+ * Errors as mtl_cp_attn_fwd; MTL_E_UNSUPPORTED when a dkv_chunks entry is dqkv. */
+mtl_status mtl_cp_attn_bwd_scratch_bytes(int32_t cp, int32_t rank, int64_t chunk, int32_t heads, int32_t head_dim,
+                                         size_t* scratch_bytes);
+mtl_status mtl_cp_attn_bwd(int32_t cp, int32_t rank, int64_t chunk, int32_t heads, int32_t head_dim,
+                           const void* const* qkv_chunks, const void* o, const float* lse, const void* dout,
+                           void* dqkv, void* const* dkv_chunks, void* scratch, size_t scratch_bytes,
+                           mtl_stream_t stream);
+
 /* MLP half of the rank's forward (column-parallel fc1 with fused GeLU,
  * row-parallel fc2), with z = h . w1 + b1 in fp32:
  *   gz      = GeLU'(z)        [S, f/t] bf16 (saved: the backward needs z only

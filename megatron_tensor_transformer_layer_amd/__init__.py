@@ -54,6 +54,9 @@ _SIGS = {
     "mtl_allgather_rows": (ctypes.c_int, [_I32, _I32, ctypes.POINTER(_P), _P, _I64, _I64, _P]),
     "mtl_cp_attn_scratch_bytes": (ctypes.c_int, [_I32, _I32, _I64, _I32, _I32, ctypes.POINTER(_SZ)]),
     "mtl_cp_attn_fwd": (ctypes.c_int, [_I32, _I32, _I64, _I32, _I32, ctypes.POINTER(_P), _P, _P, _P, _SZ, _P]),
+    "mtl_cp_attn_bwd_scratch_bytes": (ctypes.c_int, [_I32, _I32, _I64, _I32, _I32, ctypes.POINTER(_SZ)]),
+    "mtl_cp_attn_bwd": (ctypes.c_int, [_I32, _I32, _I64, _I32, _I32, ctypes.POINTER(_P), _P, _P, _P, _P,
+                                       ctypes.POINTER(_P), _P, _SZ, _P]),
     "mtl_mlp_fwd": (ctypes.c_int, [_CFG, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "mtl_mlp_bwd": (ctypes.c_int, [_CFG, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "mtl_attn_bwd": (ctypes.c_int, [_CFG, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
@@ -169,6 +172,22 @@ def mtl_cp_attn_fwd(cp, rank, chunk, heads, head_dim, qkv_chunks, o, lse, scratc
     arr = (_P * len(qkv_chunks))(*[_ptr(c) for c in qkv_chunks])
     _check(lib().mtl_cp_attn_fwd(cp, rank, chunk, heads, head_dim, arr, _ptr(o), _ptr(lse), _ptr(scratch),
                                  _nbytes(scratch, scratch_bytes), _stream(stream)), "mtl_cp_attn_fwd")
+
+
+def mtl_cp_attn_bwd_scratch_bytes(cp, rank, chunk, heads, head_dim) -> int:
+    n = _SZ(0)
+    _check(lib().mtl_cp_attn_bwd_scratch_bytes(cp, rank, chunk, heads, head_dim, ctypes.byref(n)),
+           "mtl_cp_attn_bwd_scratch_bytes")
+    return int(n.value)
+
+
+def mtl_cp_attn_bwd(cp, rank, chunk, heads, head_dim, qkv_chunks, o, lse, dout, dqkv, dkv_chunks, scratch,
+                    scratch_bytes=None, stream=None):
+    arr = (_P * len(qkv_chunks))(*[_ptr(c) for c in qkv_chunks])
+    dkv = (_P * max(len(dkv_chunks), 1))(*[_ptr(c) for c in dkv_chunks])
+    _check(lib().mtl_cp_attn_bwd(cp, rank, chunk, heads, head_dim, arr, _ptr(o), _ptr(lse), _ptr(dout), _ptr(dqkv),
+                                 dkv, _ptr(scratch), _nbytes(scratch, scratch_bytes), _stream(stream)),
+           "mtl_cp_attn_bwd")
 
 
 def mtl_mlp_fwd(cfg, h, w1, b1, w2, gz, a, partial, scratch=None, scratch_bytes=None, stream=None):

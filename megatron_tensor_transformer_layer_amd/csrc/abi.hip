@@ -459,6 +459,73 @@ mtl_status mtl_cp_attn_fwd(int32_t cp, int32_t rank, int64_t chunk, int32_t head
   return hip_status(cp_merge(m, s));
 }
 
+// D = rowsum(dO * O) of the rank's queries, then one dQ partial per earlier chunk.
+mtl_status mtl_cp_attn_bwd_scratch_bytes(int32_t cp, int32_t rank, int64_t chunk, int32_t heads, int32_t head_dim,
+                                         size_t* scratch_bytes) {
+  mtl_status st = cp_check(cp, rank, chunk, heads, head_dim);
+  if (st != MTL_OK) return st;
+  if (!scratch_bytes) return MTL_E_NULL;
+  *scratch_bytes = cp_slot_l(chunk, heads) + (size_t)rank * cp_slot_o(chunk, heads, head_dim);
+  return MTL_OK;
+}
+
+mtl_status mtl_cp_attn_bwd(int32_t cp, int32_t rank, int64_t chunk, int32_t heads, int32_t head_dim,
+                           const void* const* qkv_chunks, const void* o, const float* lse, const void* dout,
+                           void* dqkv, void* const* dkv_chunks, void* scratch, size_t scratch_bytes,
+                           mtl_stream_t stream) {
+  mtl_status st = cp_check(cp, rank, chunk, heads, head_dim);
+  if (st != MTL_OK) return st;
+  if (!qkv_chunks || (rank > 0 && !dkv_chunks)) return MTL_E_NULL;
+  for (int j = 0; j <= rank; ++j)
+    if ((st = check_ptrs(qkv_chunks[j])) != MTL_OK) return st;
+  for (int j = 0; j < rank; ++j) {
+    if ((st = check_ptrs(dkv_chunks[j])) != MTL_OK) return st;
+    if (dkv_chunks[j] == dqkv) return MTL_E_UNSUPPORTED;
+  }
+  if ((st = check_ptrs(o, lse, dout, dqkv, scratch)) != MTL_OK) return st;
+  size_t need = 0;
+  mtl_cp_attn_bwd_scratch_bytes(cp, rank, chunk, heads, head_dim, &need);
+  if (scratch_bytes < need) return MTL_E_WORKSPACE;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  char* base = static_cast<char*>(scratch);
+  const size_t so = cp_slot_o(chunk, heads, head_dim);
+  uint16_t* dq_parts = reinterpret_cast<uint16_t*>(base + cp_slot_l(chunk, heads));
+  AttnArgs a{};
+  a.qkv = static_cast<const uint16_t*>(qkv_chunks[rank]);
+  a.ld_qkv = 3 * (int64_t)heads * head_dim;
+  a.ld_o = (int64_t)heads * head_dim;
+  a.seq = (int)chunk;
+  a.batch = 1;
+  a.heads = heads;
+  a.d = head_dim;
+  a.scale = 1.0f / sqrtf((float)head_dim);
+  a.dout = static_cast<const uint16_t*>(dout);
+  a.out = static_cast<const uint16_t*>(o);
+  a.lse_in = lse;
+  a.delta = reinterpret_cast<float*>(base);
+  a.dqkv = static_cast<uint16_t*>(dqkv);
+  // the rank's own chunk (causal; also computes D), then chunks rank-1, ..., 0
+  // in ring order: dK, dV of chunk j to dkv_chunks[j], dQ to a partial
+  MTL_TRY(attention_bwd(a, s));
+  for (int k = 1; k <= rank; ++k) {
+    a.kv = static_cast<const uint16_t*>(qkv_chunks[rank - k]);
+    a.kv_seq = (int)chunk;
+    a.dkv = static_cast<uint16_t*>(dkv_chunks[rank - k]);
+    a.dq = reinterpret_cast<uint16_t*>(base + cp_slot_l(chunk, heads) + (size_t)(k - 1) * so);
+    MTL_TRY(attention_bwd_full(a, s));
+  }
+  if (rank == 0) return MTL_OK;
+  CpDqSumArgs q{};
+  q.dqkv = static_cast<uint16_t*>(dqkv);
+  q.parts = dq_parts;
+  q.part_stride = (int64_t)(so / 2);
+  q.nparts = rank;
+  q.tokens = chunk;
+  q.heads = heads;
+  q.d = head_dim;
+  return hip_status(cp_dq_sum(q, s));
+}
+
 mtl_status mtl_mlp_fwd(const mtl_layer_cfg* c, const void* h, const void* w1, const void* b1, const void* w2, void* gz,
                        void* a, void* partial, void* scratch, size_t scratch_bytes, mtl_stream_t stream) {
   mtl_status st = mtl_validate(c);

@@ -355,7 +355,11 @@ struct BwdTiles {
   }
 };
 
-template <int D>
+// FULL: the queries of a.qkv (with their dO, LSE and D) against every key of a
+// separate chunk a.kv of the same length, no mask; dK and dV go to the key
+// columns of a.dkv (the chunk's layout), dQ to a.dq ([tokens, heads*d], stride
+// ld_o).  Otherwise causal self-attention of a.qkv into a.dqkv.
+template <int D, bool FULL>
 __global__ __launch_bounds__(256, 2) void attn_bwd_kernel(AttnArgs a) {
   using T = BwdTiles<D>;
   constexpr int KS = D / 16;
@@ -381,6 +385,9 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_kernel(AttnArgs a) {
   const float c = a.scale * LOG2E;
   const i32x4 rq = make_rsrc(a.qkv, (uint32_t)(tokens * a.ld_qkv * 2));
   const i32x4 ro = make_rsrc(a.dout, (uint32_t)(tokens * a.ld_o * 2));
+  // K and V tiles: the resource rk from token ktok0 (FULL: kv_seq == seq)
+  const i32x4 rk = FULL ? make_rsrc(a.kv, (uint32_t)(tokens * a.ld_qkv * 2)) : rq;
+  const int64_t ktok0 = tok0;
   const float* lse = a.lse_in + (int64_t)n * tokens + tok0;
   const float* dlt = a.delta + (int64_t)n * tokens + tok0;
 
@@ -391,10 +398,10 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_kernel(AttnArgs a) {
     const int kw = k0 + kh * 32;
     const int key = kw + (lane & 31);
     {
-      const i32x4 rs[2] = {rq, rq};
+      const i32x4 rs[2] = {rk, rk};
       const int64_t ld[2] = {a.ld_qkv, a.ld_qkv};
       const int64_t col[2] = {colq + D, colq + 2 * D};
-      T::load(2, rs, ld, col, tok0 + k0, tK);
+      T::load(2, rs, ld, col, ktok0 + k0, tK);
     }
     f32x16 dk[DB], dv[DB];
 #pragma unroll
@@ -402,7 +409,7 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_kernel(AttnArgs a) {
       dk[i] = f32x16{};
       dv[i] = f32x16{};
     }
-    for (int qb = w; qb < nblk; ++qb) {
+    for (int qb = FULL ? 0 : w; qb < nblk; ++qb) {
       const int q0 = qb * 64;
       {
         const i32x4 rs[2] = {rq, ro};
@@ -417,7 +424,7 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_kernel(AttnArgs a) {
       wait_dma();
       __syncthreads();
       const int qw = q0 + qh * 32;
-      if (qw + 31 >= kw) {
+      if (FULL || qw + 31 >= kw) {
         // S[q][key], dP[q][key]: rows = this wave's 32 queries, column = key
         f32x16 sc = f32x16{}, dp = f32x16{};
 #pragma unroll
@@ -435,7 +442,7 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_kernel(AttnArgs a) {
             const int r = 4 * r4 + e;
             const int qg = q0 + ql + e;
             float pv = __builtin_amdgcn_exp2f(sc[r] * c - L[e]);
-            if (key > qg || qg >= a.seq) pv = 0.f;
+            if ((!FULL && key > qg) || qg >= a.seq) pv = 0.f;
             sc[r] = pv;
             dp[r] = pv * (dp[r] - Dl[e]);
           }
@@ -467,7 +474,7 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_kernel(AttnArgs a) {
     }
     __syncthreads();
     if (qh == 0 && key < a.seq) {
-      uint16_t* kout = a.dqkv + (tok0 + key) * a.ld_qkv + colq + D;
+      uint16_t* kout = (FULL ? a.dkv : a.dqkv) + (ktok0 + key) * a.ld_qkv + colq + D;
       uint16_t* vout = kout + D;
 #pragma unroll
       for (int i = 0; i < DB; ++i)
@@ -508,18 +515,18 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_kernel(AttnArgs a) {
     f32x16 dq[DB];
 #pragma unroll
     for (int i = 0; i < DB; ++i) dq[i] = f32x16{};
-    for (int kb = 0; kb <= w; ++kb) {
+    for (int kb = 0; kb < (FULL ? nblk : w + 1); ++kb) {
       const int k0 = kb * 64;
       {
-        const i32x4 rs[2] = {rq, rq};
+        const i32x4 rs[2] = {rk, rk};
         const int64_t ld[2] = {a.ld_qkv, a.ld_qkv};
         const int64_t col[2] = {colq + D, colq + 2 * D};
-        T::load(2, rs, ld, col, tok0 + k0, tK);
+        T::load(2, rs, ld, col, ktok0 + k0, tK);
       }
       wait_dma();
       __syncthreads();
       const int kw = k0 + kh * 32;
-      if (kw <= qw + 31) {
+      if (FULL || kw <= qw + 31) {
         // S^T[key][q], dP^T[key][q]: rows = this wave's 32 keys, column = query
         f32x16 sc = f32x16{}, dp = f32x16{};
 #pragma unroll
@@ -531,7 +538,7 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_kernel(AttnArgs a) {
         for (int r = 0; r < 16; ++r) {
           const int kk = kw + 8 * (r >> 2) + 4 * g + (r & 3);
           float pv = __builtin_amdgcn_exp2f(sc[r] * c - L2);
-          if (kk > q || !qok) pv = 0.f;
+          if ((!FULL && kk > q) || !qok) pv = 0.f;
           dp[r] = pv * (dp[r] - Dq);
         }
         // dQ^T[dim][q] += K^T dS^T (k = this wave's 32 keys)
@@ -553,7 +560,7 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_kernel(AttnArgs a) {
     }
     __syncthreads();
     if (kh == 0 && qok) {
-      uint16_t* qout = a.dqkv + (tok0 + q) * a.ld_qkv + colq;
+      uint16_t* qout = FULL ? a.dq + (tok0 + q) * a.ld_o + colo : a.dqkv + (tok0 + q) * a.ld_qkv + colq;
 #pragma unroll
       for (int i = 0; i < DB; ++i)
 #pragma unroll
@@ -578,15 +585,19 @@ static hipError_t fwd_d(const AttnArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <int D>
-static hipError_t bwd_d(const AttnArgs& a, hipStream_t s) {
-  const int64_t rows = (int64_t)a.seq * a.batch * a.heads;
-  hipLaunchKernelGGL(attn_delta_kernel<D>, dim3((unsigned)((rows + 31) / 32)), dim3(256), 0, s, a);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+// with_delta: compute D = rowsum(dO * O) first (the FULL calls of one set of
+// queries reuse the D of their first call)
+template <int D, bool FULL>
+static hipError_t bwd_d(const AttnArgs& a, bool with_delta, hipStream_t s) {
+  if (with_delta) {
+    const int64_t rows = (int64_t)a.seq * a.batch * a.heads;
+    hipLaunchKernelGGL(attn_delta_kernel<D>, dim3((unsigned)((rows + 31) / 32)), dim3(256), 0, s, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   const int64_t units = (int64_t)((a.seq + 63) / 64) * a.heads * a.batch;
   if (units > INT32_MAX) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(attn_bwd_kernel<D>, dim3((unsigned)units), dim3(256), 0, s, a);
+  hipLaunchKernelGGL((attn_bwd_kernel<D, FULL>), dim3((unsigned)units), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
@@ -607,8 +618,16 @@ hipError_t attention_fwd_full(const AttnArgs& a, hipStream_t s) {
 
 hipError_t attention_bwd(const AttnArgs& a, hipStream_t s) {
   if (a.seq <= 0) return hipSuccess;
-  if (a.d == 64) return bwd_d<64>(a, s);
-  if (a.d == 128) return bwd_d<128>(a, s);
+  if (a.d == 64) return bwd_d<64, false>(a, true, s);
+  if (a.d == 128) return bwd_d<128, false>(a, true, s);
+  return hipErrorInvalidValue;
+}
+
+hipError_t attention_bwd_full(const AttnArgs& a, hipStream_t s) {
+  if (a.seq <= 0) return hipSuccess;
+  if (!a.kv || !a.dkv || !a.dq || a.kv_seq != a.seq || a.seq % 64 != 0) return hipErrorInvalidValue;
+  if (a.d == 64) return bwd_d<64, true>(a, false, s);
+  if (a.d == 128) return bwd_d<128, true>(a, false, s);
   return hipErrorInvalidValue;
 }
 
@@ -646,6 +665,47 @@ __global__ __launch_bounds__(256) void cp_merge_kernel(CpMergeArgs a) {
   *reinterpret_cast<u32x4*>(a.o + oi) = u32x4{pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]),
                                               pack_bf16x2(acc[4], acc[5]), pack_bf16x2(acc[6], acc[7])};
   if (sub == 0) a.lse[li] = L;
+}
+
+// dQ of a CP rank's queries: dqkv's query columns (the rank's own chunk) plus
+// the partials from the earlier chunks, parts[j] [tokens, heads*d], summed in
+// fp32 in ascending j.  d/8 lanes per (token, head) row.
+__global__ __launch_bounds__(256) void cp_dq_sum_kernel(CpDqSumArgs a) {
+  const int lanes = a.d / 8;
+  const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t row = gid / lanes;
+  if (row >= a.tokens * a.heads) return;
+  const int sub = (int)(gid % lanes);
+  const int64_t tok = row / a.heads;
+  const int n = (int)(row % a.heads);
+  uint16_t* dst = a.dqkv + tok * 3 * a.heads * a.d + (int64_t)n * 3 * a.d + sub * 8;
+  const u32x4 v0 = *reinterpret_cast<const u32x4*>(dst);
+  float acc[8];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    acc[2 * e] = bf16_lo(v0[e]);
+    acc[2 * e + 1] = bf16_hi(v0[e]);
+  }
+  const int64_t pi = tok * a.heads * a.d + (int64_t)n * a.d + sub * 8;
+  for (int j = 0; j < a.nparts; ++j) {
+    const u32x4 v = *reinterpret_cast<const u32x4*>(a.parts + j * a.part_stride + pi);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      acc[2 * e] += bf16_lo(v[e]);
+      acc[2 * e + 1] += bf16_hi(v[e]);
+    }
+  }
+  *reinterpret_cast<u32x4*>(dst) = u32x4{pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]),
+                                         pack_bf16x2(acc[4], acc[5]), pack_bf16x2(acc[6], acc[7])};
+}
+
+hipError_t cp_dq_sum(const CpDqSumArgs& a, hipStream_t s) {
+  if (a.tokens <= 0 || a.nparts <= 0) return hipSuccess;
+  if (a.d % 8 != 0 || a.d > 2048) return hipErrorInvalidValue;
+  const int64_t blocks = (a.tokens * a.heads * (a.d / 8) + 255) / 256;
+  if (blocks > INT32_MAX) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(cp_dq_sum_kernel, dim3((unsigned)blocks), dim3(256), 0, s, a);
+  return hipGetLastError();
 }
 
 hipError_t cp_merge(const CpMergeArgs& a, hipStream_t s) {

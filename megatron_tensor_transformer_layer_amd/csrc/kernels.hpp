@@ -95,6 +95,9 @@ struct AttnArgs {
   // attention_fwd_full: keys and values of a separate chunk [kv_seq, ...], stride ld_qkv
   const uint16_t* kv;
   int kv_seq;
+  // attention_bwd_full: dK, dV into the key columns of dkv (kv's layout), dQ into dq (stride ld_o)
+  uint16_t* dkv;
+  uint16_t* dq;
 };
 hipError_t attention_fwd(const AttnArgs& a, hipStream_t s);
 // Queries of a.qkv against all a.kv_seq keys of a.kv (no mask; kv_seq % 64 == 0).
@@ -113,7 +116,21 @@ struct CpMergeArgs {
   float* lse;
 };
 hipError_t cp_merge(const CpMergeArgs& a, hipStream_t s);
+// dqkv[tok, n*3d + i] += sum_j parts[j][tok, n*d + i] (the query columns of a
+// head-interleaved [tokens, 3*heads*d] tensor), fp32 in ascending j, bf16 out.
+struct CpDqSumArgs {
+  uint16_t* dqkv;
+  const uint16_t* parts;
+  int64_t part_stride;
+  int nparts;
+  int64_t tokens;
+  int heads, d;
+};
+hipError_t cp_dq_sum(const CpDqSumArgs& a, hipStream_t s);
 hipError_t attention_bwd(const AttnArgs& a, hipStream_t s);
+// The backward of attention_fwd_full for queries whose D = rowsum(dO * O) is
+// already in a.delta (kv_seq == seq, seq % 64 == 0): no D launch.
+hipError_t attention_bwd_full(const AttnArgs& a, hipStream_t s);
 
 // ---------------------------------------------------------------- reductions
 // out[r, :] = sum_i partials[i][r, :] (+ bias) (+ residual) for r in [row_begin, row_end).

@@ -100,3 +100,27 @@ def rank_attention_backward(qkv_full, do_rank, heads: int, cp: int, rank: int) -
             parts += [g[rj, sk], g[rj, sv]]
         dkv.append(np.concatenate(parts, axis=1))
     return dict(dq=dq, dkv=dkv)
+
+
+def dq_rows(qkv_full, do_rows, heads: int, rows) -> np.ndarray:
+    """dQ [len(rows), heads*d] of selected query rows (global indices) of causal
+    attention, given their dO rows [len(rows), heads*d]: per head and query i
+    over keys 0..i, P = softmax(q K^T * scale), D = dO_i . (P V),
+    dS = P * (dO_i V^T - D), dq = dS K * scale.  A query's dQ depends only on
+    its own dO row, so this is the rank backward's dq on those rows."""
+    qkv_full = np.asarray(qkv_full, dtype=np.float64)
+    do_rows = np.asarray(do_rows, dtype=np.float64)
+    d = qkv_full.shape[1] // (3 * heads)
+    scale = 1.0 / math.sqrt(d)
+    out = np.zeros((len(rows), heads * d))
+    for n in range(heads):
+        sq, sk, sv = L.head_slices(heads, d, n)
+        for j, i in enumerate(rows):
+            k, v = qkv_full[: i + 1, sk], qkv_full[: i + 1, sv]
+            s = (qkv_full[i, sq] @ k.T) * scale
+            p = np.exp(s - s.max())
+            p /= p.sum()
+            g = do_rows[j, n * d:(n + 1) * d]
+            ds = p * (v @ g - g @ (p @ v))
+            out[j, n * d:(n + 1) * d] = (ds @ k) * scale
+    return out

@@ -34,7 +34,7 @@ _TID = {
     "x": 1, "w_qkv": 2, "b_qkv": 3, "w_o": 4, "b_o": 5, "w1": 6, "b1": 7,
     "w2": 8, "b2": 9, "dy": 10, "h": 11, "dh": 12,
     "moe_x": 20, "moe_w1": 21, "moe_w2": 22, "moe_dy": 23, "moe_gumbel": 24, "moe_wr": 25, "moe_dgates": 26,
-    "cp_qkv": 27,
+    "cp_qkv": 27, "cp_dout": 28,
 }
 
 WEIGHT_STD = 0.02
@@ -227,6 +227,11 @@ def cp_qkv(shape: CpShape, seed: int = 0) -> np.ndarray:
     with ThreadPoolExecutor(max_workers=8) as ex:
         list(ex.map(fill, range((shape.seq + g - 1) // g)))
     return out
+
+
+def cp_dout(shape: CpShape, seed: int = 0) -> np.ndarray:
+    """bf16 bits of one rank's output gradient dO [chunk, heads*d], N(0,1)."""
+    return bf16_round_bits(_normal(seed, "cp_dout", 0, (shape.chunk, shape.heads * shape.head_dim), 1.0))
 
 
 # ---------------------------------------------------------------- MoE inputs

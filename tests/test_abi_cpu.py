@@ -248,3 +248,28 @@ def test_cp_attention_validation_before_any_launch(mtl):
     assert fwd(1, chunks, P + 8, P, P, need) == mtl.MTL_E_ALIGN
     assert fwd(1, (ctypes.c_void_p * 2)(P, P + 2), P, P, P, need) == mtl.MTL_E_ALIGN
     assert fwd(4, chunks, P, P, P, need) == mtl.MTL_E_RANK
+
+
+def test_cp_attention_backward_validation_before_any_launch(mtl):
+    lib = mtl.lib()
+    P = 1 << 20
+    n = ctypes.c_size_t(0)
+    assert lib.mtl_cp_attn_bwd_scratch_bytes(4, 0, 256, 2, 128, ctypes.byref(n)) == mtl.MTL_OK
+    assert n.value == 2 * 256 * 4  # D only
+    assert lib.mtl_cp_attn_bwd_scratch_bytes(4, 2, 256, 2, 128, ctypes.byref(n)) == mtl.MTL_OK
+    assert n.value == 2 * 256 * 4 + 2 * 256 * 256 * 2  # D and two dQ partials
+    assert lib.mtl_cp_attn_bwd_scratch_bytes(4, 4, 256, 2, 128, ctypes.byref(n)) == mtl.MTL_E_RANK
+    assert lib.mtl_cp_attn_bwd_scratch_bytes(4, 1, 100, 2, 128, ctypes.byref(n)) == mtl.MTL_E_SHAPE
+    need = 2 * 256 * 4 + 256 * 256 * 2
+    qkv = (ctypes.c_void_p * 2)(P, P + 4096)
+    dkv = (ctypes.c_void_p * 1)(P + 8192)
+    bwd = lambda rank, q, o, lse, do, dqkv, dk, scr, nb: lib.mtl_cp_attn_bwd(4, rank, 256, 2, 128, q, o, lse, do,
+                                                                             dqkv, dk, scr, nb, None)
+    assert bwd(1, qkv, P, P, P, P, dkv, P, need - 1) == mtl.MTL_E_WORKSPACE
+    assert bwd(1, qkv, P, P, P, P, None, P, need) == mtl.MTL_E_NULL
+    assert bwd(1, qkv, P, P, None, P, dkv, P, need) == mtl.MTL_E_NULL
+    assert bwd(1, qkv, P, P, P, P, (ctypes.c_void_p * 1)(None), P, need) == mtl.MTL_E_NULL
+    assert bwd(1, qkv, P, P, P, P + 8192, dkv, P, need) == mtl.MTL_E_UNSUPPORTED  # a peer share is dqkv
+    assert bwd(1, qkv, P, P, P, P + 2, dkv, P, need) == mtl.MTL_E_ALIGN
+    assert bwd(1, qkv, P, P, P, P, dkv, None, need) == mtl.MTL_E_NULL
+    assert bwd(5, qkv, P, P, P, P, dkv, P, need) == mtl.MTL_E_RANK

@@ -160,3 +160,14 @@ def test_backward_by_finite_differences_through_the_rank_loss():
         m[tok, col] -= eps
         fd = (loss(p) - loss(m)) / (2 * eps)
         assert abs(fd - want) < 1e-7 * max(1.0, abs(want)), (tok, col, fd, want)
+
+
+def test_dq_rows_match_the_rank_backward():
+    seq, cp, heads, d, r = 64, 4, 2, 8, 3
+    c = seq // cp
+    qkv = _qkv(14, seq, heads, d, std=1.3)
+    do = _qkv(15, c, heads, d)[:, : heads * d]
+    g = CP.rank_attention_backward(qkv, do, heads, cp, r)
+    local = [0, 5, 15]
+    got = CP.dq_rows(qkv, do[local], heads, [r * c + i for i in local])
+    assert np.allclose(got, g["dq"][local], rtol=0, atol=1e-12)
