@@ -1,7 +1,8 @@
 """The oracle: a plain, slow fp64 CPU implementation of one transformer layer's
 training step, of its tensor-parallel sharded view, of one context-parallel
 rank's share of causal attention, of the MoE expert block and its router
-(linear, gate backward, load-balancing loss), and of fp8 quantisation.
+(linear, gate backward, load-balancing loss), of fp8 quantisation, and of
+MXFP4 quantisation with a GEMM on MXFP4 operands.
 
 TEST INFRASTRUCTURE ONLY.  Nothing in the library path imports, calls or links
 this package; only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline
@@ -25,4 +26,4 @@ the oracle takes the plain textbook definition (scaled dot-product causal
 attention, exact erf GeLU, softmax gates over the selected experts, OCP fp8
 encodings) -- each reading is listed in the module that uses it.
 """
-from . import layer, shard, moe, fp8, router, cp  # noqa: F401
+from . import layer, shard, moe, fp8, router, cp, mxfp4  # noqa: F401

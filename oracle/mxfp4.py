@@ -1,0 +1,108 @@
+"""fp64 oracle of MXFP4 quantisation and of a GEMM on MXFP4 operands.
+
+Test infrastructure only (see the package docstring).
+
+The site summary ([site] navi2ai.com/sites/1106, its precision list and deploy
+step 7, `--fp4-format nvfp4` on Blackwell) names 4-bit floating-point
+training and gives no format details.  The reading taken here is AMD's
+native counterpart, the OCP Microscaling (MX) format MXFP4, as the OCP MX
+specification v1.0 defines it:
+
+* element type FP4 E2M1: sign, 2 exponent bits (bias 1), 1 mantissa bit, no
+  infinities or NaN; magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6;
+* blocks of 32 consecutive elements along the reduction (K) dimension share
+  one scale X = 2^e stored as E8M0 (biased exponent e + 127);
+* e = floor(log2(max |v|)) - 2 (2 is the largest exponent of E2M1), clamped to
+  E8M0's lowest exponent -127 (an all-zero block gets -127);
+* each element is v / X rounded to the nearest E2M1 value, ties to the even
+  code (mantissa bit 0), magnitudes past 6 saturating to 6; the sign bit
+  follows the sign of v, zero included.
+
+Finite inputs only.  Codes pack two per byte, the even element in the low
+nibble.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+BLOCK = 32
+EMAX_ELEM = 2
+E8M0_BIAS = 127
+SCALE_EXP_MIN = -127
+
+
+def e2m1_value(code: int) -> float:
+    """Value of a 4-bit E2M1 code from its fields."""
+    s, e, m = (code >> 3) & 1, (code >> 1) & 3, code & 1
+    mag = m * 0.5 if e == 0 else 2.0 ** (e - 1) * (1.0 + m / 2.0)
+    return -mag if s else mag
+
+
+E2M1_MAGNITUDES = np.array([e2m1_value(c) for c in range(8)])
+
+
+def round_e2m1(y: float) -> int:
+    """Code of the E2M1 value nearest to y (ties to the even code, saturating)."""
+    if not math.isfinite(y):
+        raise ValueError("finite inputs only")
+    a = abs(y)
+    dist = np.abs(E2M1_MAGNITUDES - a)
+    best = np.flatnonzero(dist == dist.min())
+    code = int(best[0]) if len(best) == 1 else int([c for c in best if c % 2 == 0][0])
+    return code | (8 if math.copysign(1.0, y) < 0 else 0)
+
+
+def block_scale_exp(block) -> int:
+    amax = float(np.max(np.abs(block)))
+    if amax == 0.0:
+        return SCALE_EXP_MIN
+    return max(math.floor(math.log2(amax)) - EMAX_ELEM, SCALE_EXP_MIN)
+
+
+def quantize(x):
+    """x [rows, cols] (cols % 32 == 0) -> (codes uint8 [rows, cols] one code per
+    element, scales uint8 [rows, cols/32] E8M0)."""
+    x = np.asarray(x, dtype=np.float64)
+    rows, cols = x.shape
+    if cols % BLOCK:
+        raise ValueError("cols must be a multiple of 32")
+    codes = np.zeros((rows, cols), dtype=np.uint8)
+    scales = np.zeros((rows, cols // BLOCK), dtype=np.uint8)
+    for r in range(rows):
+        for b in range(cols // BLOCK):
+            blk = x[r, b * BLOCK:(b + 1) * BLOCK]
+            e = block_scale_exp(blk)
+            scales[r, b] = e + E8M0_BIAS
+            for i, v in enumerate(blk):
+                codes[r, b * BLOCK + i] = round_e2m1(math.ldexp(v, -e))
+    return codes, scales
+
+
+def pack(codes):
+    """One code per element -> two per byte (element 2i in the low nibble)."""
+    c = np.asarray(codes, dtype=np.uint8)
+    return (c[:, 0::2] | (c[:, 1::2] << 4)).astype(np.uint8)
+
+
+def unpack(packed):
+    p = np.asarray(packed, dtype=np.uint8)
+    out = np.zeros((p.shape[0], p.shape[1] * 2), dtype=np.uint8)
+    out[:, 0::2] = p & 15
+    out[:, 1::2] = p >> 4
+    return out
+
+
+def dequantize(codes, scales):
+    """Values X * E2M1(code) [rows, cols] in fp64 (codes one per element)."""
+    c = np.asarray(codes, dtype=np.int64)
+    vals = np.array([e2m1_value(k) for k in range(16)])[c]
+    e = np.asarray(scales, dtype=np.int64) - E8M0_BIAS
+    return vals * np.repeat(np.ldexp(1.0, e), BLOCK, axis=1)
+
+
+def gemm(a_codes, a_scales, b_codes, b_scales):
+    """C [M, N] = A B^T of two MXFP4 operands, both K-contiguous ([M, K] and
+    [N, K], one code per element), in fp64."""
+    return dequantize(a_codes, a_scales) @ dequantize(b_codes, b_scales).T

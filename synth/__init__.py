@@ -34,7 +34,7 @@ _TID = {
     "x": 1, "w_qkv": 2, "b_qkv": 3, "w_o": 4, "b_o": 5, "w1": 6, "b1": 7,
     "w2": 8, "b2": 9, "dy": 10, "h": 11, "dh": 12,
     "moe_x": 20, "moe_w1": 21, "moe_w2": 22, "moe_dy": 23, "moe_gumbel": 24, "moe_wr": 25, "moe_dgates": 26,
-    "cp_qkv": 27, "cp_dout": 28,
+    "cp_qkv": 27, "cp_dout": 28, "mx_a": 29, "mx_b": 30,
 }
 
 WEIGHT_STD = 0.02
@@ -232,6 +232,19 @@ def cp_qkv(shape: CpShape, seed: int = 0) -> np.ndarray:
 def cp_dout(shape: CpShape, seed: int = 0) -> np.ndarray:
     """bf16 bits of one rank's output gradient dO [chunk, heads*d], N(0,1)."""
     return bf16_round_bits(_normal(seed, "cp_dout", 0, (shape.chunk, shape.heads * shape.head_dim), 1.0))
+
+
+# ---------------------------------------------------------------- MXFP4 GEMM inputs
+def mx_operand(rows: int, cols: int, name: str, std: float, seed: int = 0) -> np.ndarray:
+    """bf16 bits of a K-contiguous GEMM operand [rows, cols] (name mx_a: the
+    activations, N(0,1); mx_b: a weight stored [out, in], N(0, WEIGHT_STD)),
+    drawn per 1024-row granule."""
+    g = 1024
+    out = np.empty((rows, cols), dtype=np.uint16)
+    for i in range((rows + g - 1) // g):
+        r = min(g, rows - i * g)
+        out[i * g:i * g + r] = bf16_round_bits(_normal(seed, name, i, (r, cols), std))
+    return out
 
 
 # ---------------------------------------------------------------- MoE inputs
