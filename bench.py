@@ -15,7 +15,8 @@ expert block instead (route, permute, grouped expert GEMMs, combine, backward);
 with --workload cp4-seq32k-7b-tp4 it is one context-parallel rank's causal
 attention share, forward and backward (by default the last of 4 ranks of a
 32768-token sequence: its own chunk causally and the three earlier chunks in
-full).
+full); with --workload mxfp4-gemm-7b-tp4 it is the rank's fc1 GEMM in MXFP4
+(both operands quantised, then the block-scaled MFMA GEMM).
 """
 from __future__ import annotations
 
@@ -29,6 +30,7 @@ import numpy as np
 
 PEAK_BF16_TFLOPS = 2516.6  # MI355X dense bf16 MFMA
 PEAK_FP8_TFLOPS = 5033.2   # MI355X dense fp8 MFMA
+PEAK_FP4_TFLOPS = 10066.3  # MI355X dense fp4 / fp6 MFMA
 PEAK_HBM_GBS = 8000.0
 
 
@@ -360,6 +362,87 @@ def cp_main(args):
     print(json.dumps(out), flush=True)
 
 
+def mx_cpu_baseline(shape, sample_rows):
+    """The MXFP4 oracle (fp64, as it stands) on a bounded sample: quantise
+    sample_rows rows of A and of B and multiply them (sample_rows^2 outputs)."""
+    import synth
+    from oracle import mxfp4 as MX
+    a = synth.bf16_bits_to_f64(synth.mx_operand(shape.M, shape.K, "mx_a", 1.0)[:sample_rows])
+    b = synth.bf16_bits_to_f64(synth.mx_operand(shape.N, shape.K, "mx_b", synth.WEIGHT_STD)[:sample_rows])
+    t0 = time.perf_counter()
+    ca, sa = MX.quantize(a)
+    cb, sb = MX.quantize(b)
+    MX.gemm(ca, sa, cb, sb)
+    dt = time.perf_counter() - t0
+    fl = 2.0 * sample_rows * sample_rows * shape.K
+    return {"value": fl / dt / 1e12, "unit": "TFLOP/s", "cores": len(os.sched_getaffinity(0)), "kind": "oracle",
+            "sample": f"quantise {sample_rows} rows of A and of B and multiply them ({sample_rows}x{sample_rows}x"
+                      f"{shape.K}, fp64), {dt:.2f} s"}
+
+
+def mx_main(args):
+    """One GEMM of the 7B-class rank in MXFP4: quantise the activations and the
+    weight (mtl_mxfp4_quantize) and multiply them on the block-scaled MFMA
+    (mtl_mxfp4_gemm)."""
+    import torch
+    import synth
+    from megatron_tensor_transformer_layer_amd import mtl_mxfp4_gemm, mtl_mxfp4_quantize
+    from megatron_tensor_transformer_layer_amd.layer import bf16_dev
+
+    shape = synth.MX_WORKLOADS[args.workload]
+    M, N, K = shape.M, shape.N, shape.K
+    a = bf16_dev(synth.mx_operand(M, K, "mx_a", 1.0))
+    b = bf16_dev(synth.mx_operand(N, K, "mx_b", synth.WEIGHT_STD))
+    ca = torch.empty(M, K // 2, dtype=torch.uint8, device="cuda")
+    sa = torch.empty(M, K // 32, dtype=torch.uint8, device="cuda")
+    cb = torch.empty(N, K // 2, dtype=torch.uint8, device="cuda")
+    sb = torch.empty(N, K // 32, dtype=torch.uint8, device="cuda")
+    c = torch.empty(M, N, dtype=torch.bfloat16, device="cuda")
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+    marks = []
+
+    def step(record=False):
+        mtl_mxfp4_quantize(a, M, K, ca, sa)
+        mtl_mxfp4_quantize(b, N, K, cb, sb)
+        if record:
+            e0, e1 = ev(), ev()
+            e0.record()
+        mtl_mxfp4_gemm(M, N, K, ca, sa, cb, sb, c)
+        if record:
+            e1.record()
+            marks.append((e0, e1))
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step(record=True)
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) / args.steps * 1e3
+    gemm_ms = float(np.mean([x.elapsed_time(y) for x, y in marks]))
+    fl = 2.0 * M * N * K
+    achieved = fl / (gemm_ms / 1e3) / 1e12
+    out = {
+        "metric": "TFLOP/s of one MXFP4 GEMM of the TP-rank layer (quantisation included) and % of MI355X MFMA peak",
+        "value": round(fl / (ms / 1e3) / 1e12, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "mxfp4",
+        "data": "synthetic (N(0,1) activations, N(0,0.02) weight, bf16 before quantisation)",
+        "config": {"workload": f"{args.workload}: fc1 forward of the 7B-class TP=4 rank, {M}x{N}x{K}, both "
+                               f"operands quantised to MXFP4 each step, bf16 output",
+                   "global_batch": 1, "seq_len": M, "parallelism": "tp4-rank0-of-1gpu"},
+        "pct_of_peak": round(100 * fl / (ms / 1e3) / 1e12 / PEAK_FP4_TFLOPS, 2),
+        "flop_per_step": fl,
+        "roofline": {"bound": "mfma", "kernel": "mxfp4_gemm_kernel, 128x128 tiles, HIP events on its stream",
+                     "achieved": round(achieved, 1), "peak": PEAK_FP4_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / PEAK_FP4_TFLOPS, 4), "traffic": None,
+                     "gemm_launch_us": round(gemm_ms * 1e3, 1)},
+        "cpu_baseline": None if args.no_cpu_baseline else mx_cpu_baseline(shape, 64),
+    }
+    print(json.dumps(out), flush=True)
+
+
 def moe_main(args):
     """One EP rank's MoE expert block: route, permute, grouped fc1+GeLU, fc2,
     combine, and the backward (combine', grouped dgrad and wgrad, dX scatter)."""
@@ -471,6 +554,9 @@ def main():
         return
     if args.workload in synth.CP_WORKLOADS:
         cp_main(args)
+        return
+    if args.workload in synth.MX_WORKLOADS:
+        mx_main(args)
         return
     shape = synth.WORKLOADS[args.workload]
     t, r = shape.tp, args.rank or 0

@@ -196,6 +196,29 @@ mtl_status mtl_cp_attn_bwd(int32_t cp, int32_t rank, int64_t chunk, int32_t head
                            void* dqkv, void* const* dkv_chunks, void* scratch, size_t scratch_bytes,
                            mtl_stream_t stream);
 
+/* MXFP4 quantisation.  The site summary (navi2ai.com/sites/1106, its precision
+ * list and deploy step 7) names 4-bit floating-point training (NVFP4 on
+ * Blackwell) without a format; the CDNA4 counterpart taken here is OCP MXFP4:
+ * FP4 E2M1 elements in blocks of 32 consecutive elements along a row sharing
+ * an E8M0 scale 2^e, e = floor(log2(max |v|)) - 2 clamped at -127 (byte e+127);
+ * elements v / 2^e rounded to the nearest E2M1 value (0, 0.5, 1, 1.5, 2, 3, 4,
+ * 6), ties to the even code, saturating at 6, with the sign of v.
+ * x: [rows, cols] bf16 row-major (the GEMM's K along the row), finite values;
+ * codes: [rows, cols/2] bytes, element 2i in the low nibble of byte i; scales:
+ * [rows, cols/32] bytes.  cols % 32 == 0; pointers 16-byte aligned.  Errors:
+ * MTL_E_NULL, MTL_E_ALIGN, MTL_E_SHAPE. */
+mtl_status mtl_mxfp4_quantize(const void* x, int64_t rows, int64_t cols, void* codes, void* scales,
+                              mtl_stream_t stream);
+
+/* GEMM on MXFP4 operands with CDNA4's block-scaled MFMA: c [M, N] bf16 (row
+ * stride ldc elements) = A . B^T over K, with A [M, K] and B [N, K] given as
+ * the codes and scales mtl_mxfp4_quantize writes (a weight W [K, N] enters as
+ * its transpose [N, K]).  Products of the scaled elements are exact in fp32 and
+ * summed in fp32.  M % 128 == 0, N % 128 == 0, K % 256 == 0, ldc >= N, ldc % 8
+ * == 0.  Errors: MTL_E_NULL, MTL_E_ALIGN, MTL_E_SHAPE. */
+mtl_status mtl_mxfp4_gemm(int64_t M, int64_t N, int64_t K, const void* a_codes, const void* a_scales,
+                          const void* b_codes, const void* b_scales, void* c, int64_t ldc, mtl_stream_t stream);
+
 /* MLP half of the rank's forward (column-parallel fc1 with fused GeLU,
  * row-parallel fc2), with z = h . w1 + b1 in fp32:
  *   gz      = GeLU'(z)        [S, f/t] bf16 (saved: the backward needs z only

@@ -54,6 +54,8 @@ _SIGS = {
     "mtl_allgather_rows": (ctypes.c_int, [_I32, _I32, ctypes.POINTER(_P), _P, _I64, _I64, _P]),
     "mtl_cp_attn_scratch_bytes": (ctypes.c_int, [_I32, _I32, _I64, _I32, _I32, ctypes.POINTER(_SZ)]),
     "mtl_cp_attn_fwd": (ctypes.c_int, [_I32, _I32, _I64, _I32, _I32, ctypes.POINTER(_P), _P, _P, _P, _SZ, _P]),
+    "mtl_mxfp4_quantize": (ctypes.c_int, [_P, _I64, _I64, _P, _P, _P]),
+    "mtl_mxfp4_gemm": (ctypes.c_int, [_I64, _I64, _I64, _P, _P, _P, _P, _P, _I64, _P]),
     "mtl_cp_attn_bwd_scratch_bytes": (ctypes.c_int, [_I32, _I32, _I64, _I32, _I32, ctypes.POINTER(_SZ)]),
     "mtl_cp_attn_bwd": (ctypes.c_int, [_I32, _I32, _I64, _I32, _I32, ctypes.POINTER(_P), _P, _P, _P, _P,
                                        ctypes.POINTER(_P), _P, _SZ, _P]),
@@ -188,6 +190,16 @@ def mtl_cp_attn_bwd(cp, rank, chunk, heads, head_dim, qkv_chunks, o, lse, dout, 
     _check(lib().mtl_cp_attn_bwd(cp, rank, chunk, heads, head_dim, arr, _ptr(o), _ptr(lse), _ptr(dout), _ptr(dqkv),
                                  dkv, _ptr(scratch), _nbytes(scratch, scratch_bytes), _stream(stream)),
            "mtl_cp_attn_bwd")
+
+
+def mtl_mxfp4_quantize(x, rows, cols, codes, scales, stream=None):
+    _check(lib().mtl_mxfp4_quantize(_ptr(x), rows, cols, _ptr(codes), _ptr(scales), _stream(stream)),
+           "mtl_mxfp4_quantize")
+
+
+def mtl_mxfp4_gemm(M, N, K, a_codes, a_scales, b_codes, b_scales, c, ldc=None, stream=None):
+    _check(lib().mtl_mxfp4_gemm(M, N, K, _ptr(a_codes), _ptr(a_scales), _ptr(b_codes), _ptr(b_scales), _ptr(c),
+                                N if ldc is None else ldc, _stream(stream)), "mtl_mxfp4_gemm")
 
 
 def mtl_mlp_fwd(cfg, h, w1, b1, w2, gz, a, partial, scratch=None, scratch_bytes=None, stream=None):

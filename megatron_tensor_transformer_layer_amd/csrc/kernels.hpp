@@ -127,6 +127,25 @@ struct CpDqSumArgs {
   int heads, d;
 };
 hipError_t cp_dq_sum(const CpDqSumArgs& a, hipStream_t s);
+
+// ---------------------------------------------------------------- MXFP4
+// x [rows, cols] bf16 (cols % 32 == 0) -> codes [rows, cols/2] (two E2M1 per
+// byte, even element low) and E8M0 scales [rows, cols/32].
+hipError_t mxfp4_quantize(const uint16_t* x, int64_t rows, int64_t cols, uint8_t* codes, uint8_t* scales,
+                          hipStream_t s);
+// c [M, N] bf16 (row stride ldc) = A B^T over K, A [M, K] and B [N, K] in
+// MXFP4 (codes and scales as mxfp4_quantize writes them); M, N % 128 == 0,
+// K % 256 == 0.
+struct Mxfp4GemmArgs {
+  const uint8_t* a;
+  const uint8_t* sa;
+  const uint8_t* b;
+  const uint8_t* sb;
+  uint16_t* c;
+  int64_t ldc;
+  int M, N, K;
+};
+hipError_t mxfp4_gemm(const Mxfp4GemmArgs& g, hipStream_t s);
 hipError_t attention_bwd(const AttnArgs& a, hipStream_t s);
 // The backward of attention_fwd_full for queries whose D = rowsum(dO * O) is
 // already in a.delta (kv_seq == seq, seq % 64 == 0): no D launch.

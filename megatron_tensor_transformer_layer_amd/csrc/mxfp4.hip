@@ -1,0 +1,210 @@
+// MXFP4 (OCP Microscaling, FP4 E2M1 elements in blocks of 32 along K sharing
+// an E8M0 scale) quantisation and GEMM for gfx950.
+//
+// Format: the scale of a block is 2^e with e = floor(log2(max |v|)) - 2
+// (clamped at -127), stored as e + 127; each element is v / 2^e rounded to the
+// nearest of 0, 0.5, 1, 1.5, 2, 3, 4, 6 (ties to the even code, saturating at
+// 6) with the sign of v; two codes per byte, the even element in the low
+// nibble.  Finite inputs only.
+//
+// The GEMM multiplies on v_mfma_scale_f32_32x32x64_f8f6f4 with both operands
+// in FP4 and the block scales fed per lane: in a 32 x 64 operand fragment lane
+// l holds row l % 32 and the 32 elements k = (l / 32) * 32 .. +31 (16 bytes),
+// i.e. exactly one scale block, whose E8M0 byte it passes as its scale.
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace mtl {
+
+// ---------------------------------------------------------------- quantise
+// One thread per block of 32 elements: 64 bytes in, 16 bytes of codes and one
+// scale byte out.
+__device__ __forceinline__ uint32_t e2m1_code(float y, uint32_t sign) {
+  const float a = fabsf(y);
+  uint32_t c;
+  if (a <= 0.25f) c = 0;        // ties: 0.25 -> 0
+  else if (a < 0.75f) c = 1;    // 0.5
+  else if (a <= 1.25f) c = 2;   // 1 (0.75 and 1.25 -> 1)
+  else if (a < 1.75f) c = 3;    // 1.5
+  else if (a <= 2.5f) c = 4;    // 2 (1.75 and 2.5 -> 2)
+  else if (a < 3.5f) c = 5;     // 3
+  else if (a <= 5.0f) c = 6;    // 4 (3.5 and 5 -> 4)
+  else c = 7;                   // 6, and everything above
+  return c | (sign << 3);
+}
+
+__global__ __launch_bounds__(256) void mxfp4_quant_kernel(const uint16_t* __restrict__ x, int64_t nblocks,
+                                                          uint8_t* __restrict__ codes, uint8_t* __restrict__ scales) {
+  const int64_t blk = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (blk >= nblocks) return;
+  const u32x4* src = reinterpret_cast<const u32x4*>(x + blk * 32);
+  u32x4 v[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) v[i] = src[i];
+  uint32_t mx = 0;  // largest magnitude bits: integer order is value order for finite bf16
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) mx = max(mx, max(v[i][j] & 0x7fffu, (v[i][j] >> 16) & 0x7fffu));
+  // amax = 2^(E-127) * 1.m for exponent field E >= 1; e = max(E - 129, -127),
+  // so the E8M0 byte is max(E - 2, 0) (also for zero or subnormal amax)
+  const int E = (int)(mx >> 7);
+  const uint32_t sc = (uint32_t)max(E - 2, 0);
+  const float mul = __uint_as_float((254u - sc) << 23);  // 2^-e, exact
+  u32x4 out;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    uint32_t w = 0;
+#pragma unroll
+    for (int h = 0; h < 8; ++h) {  // element 8*i + h
+      const uint32_t word = v[i][h >> 1];
+      const uint32_t bits = (h & 1) ? (word >> 16) : (word & 0xffffu);
+      const float y = __uint_as_float(bits << 16) * mul;
+      w |= e2m1_code(y, bits >> 15) << (4 * h);
+    }
+    out[i] = w;
+  }
+  *reinterpret_cast<u32x4*>(codes + blk * 16) = out;
+  scales[blk] = (uint8_t)sc;
+}
+
+hipError_t mxfp4_quantize(const uint16_t* x, int64_t rows, int64_t cols, uint8_t* codes, uint8_t* scales,
+                          hipStream_t s) {
+  const int64_t nblocks = rows * (cols / 32);
+  if (nblocks <= 0) return hipSuccess;
+  const int64_t grid = (nblocks + 255) / 256;
+  if (grid > INT32_MAX) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(mxfp4_quant_kernel, dim3((unsigned)grid), dim3(256), 0, s, x, nblocks, codes, scales);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------- GEMM
+// C [M, N] (bf16, row stride ldc) = A B^T, A [M, K] and B [N, K] MXFP4 (codes
+// K/2 bytes per row, scales K/32 bytes per row).  128 x 128 tiles, 4 waves of
+// 64 x 64 (2 x 2 MFMA blocks of 32 x 32); K slabs of 256 elements (128 code
+// bytes and 8 scale bytes per row) through two LDS buffers, the next slab
+// loaded into registers while the current one is multiplied.  M, N % 128 == 0,
+// K % 256 == 0.
+namespace {
+constexpr int MT = 128, KSLAB = 256, ROWB = KSLAB / 2;  // 128 code bytes per row and slab
+constexpr int TILEB = MT * ROWB;                         // 16 KB of codes per operand and slab
+constexpr int SCB = MT * (KSLAB / 32);                   // 1 KB of scales per operand and slab
+constexpr int BUF = 2 * TILEB + 2 * SCB;
+
+// 16-byte chunk c of row r sits at chunk c ^ ((r >> 1) & 7): the 16 rows a
+// quarter-wave reads (or writes) at one logical chunk hit 16 distinct groups of
+// four banks on the 64-bank LDS.
+__device__ __forceinline__ int chunk_off(int r, int c) { return r * ROWB + ((c ^ ((r >> 1) & 7)) << 4); }
+}  // namespace
+
+__global__ __launch_bounds__(256, 2) void mxfp4_gemm_kernel(Mxfp4GemmArgs g) {
+  __shared__ __attribute__((aligned(1024))) char lds_[2 * BUF];
+  const int ntn = g.N / MT;
+  const int ntiles = (g.M / MT) * ntn;
+  const int u = xcd_index(blockIdx.x, ntiles);
+  const int tm = u / ntn, tn = u % ntn;
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int64_t kb = g.K / 2, ks = g.K / 32;  // code and scale bytes per row
+  const uint8_t* a0 = g.a + (int64_t)tm * MT * kb;
+  const uint8_t* b0 = g.b + (int64_t)tn * MT * kb;
+  const uint8_t* sa0 = g.sa + (int64_t)tm * MT * ks;
+  const uint8_t* sb0 = g.sb + (int64_t)tn * MT * ks;
+  const int nslab = g.K / KSLAB;
+
+  // staging registers: 4 code chunks of A and of B per thread, 8 scale bytes
+  // of one row of A (threads 0..127) or of B (threads 128..255)
+  u32x4 ra[4], rb[4];
+  u32x2 rsc;
+  auto load = [&](int s) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int idx = t + 256 * i, r = idx >> 3, c = idx & 7;
+      ra[i] = *reinterpret_cast<const u32x4*>(a0 + r * kb + s * ROWB + c * 16);
+      rb[i] = *reinterpret_cast<const u32x4*>(b0 + r * kb + s * ROWB + c * 16);
+    }
+    const int r = t & 127;
+    const uint8_t* sp = (t < 128 ? sa0 : sb0) + r * ks + s * 8;
+    rsc = *reinterpret_cast<const u32x2*>(sp);
+  };
+  auto store = [&](char* buf) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int idx = t + 256 * i, r = idx >> 3, c = idx & 7;
+      *reinterpret_cast<u32x4*>(buf + chunk_off(r, c)) = ra[i];
+      *reinterpret_cast<u32x4*>(buf + TILEB + chunk_off(r, c)) = rb[i];
+    }
+    *reinterpret_cast<u32x2*>(buf + 2 * TILEB + (t < 128 ? 0 : SCB) + (t & 127) * 8) = rsc;
+  };
+
+  f32x16 acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) acc[i][j] = f32x16{};
+
+  typedef int i32x8 __attribute__((ext_vector_type(8)));
+  load(0);
+  store(lds_);
+  __syncthreads();
+  for (int s = 0; s < nslab; ++s) {
+    const bool more = s + 1 < nslab;
+    if (more) load(s + 1);
+    const char* buf = lds_ + (s & 1) * BUF;
+#pragma unroll
+    for (int kk = 0; kk < KSLAB / 64; ++kk) {
+      const int c = kk * 2 + (lane >> 5);  // this lane's 16-byte chunk (32 elements) of the k step
+      i32x8 fa[2], fb[2];
+      int sca[2], scb[2];
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int r = wm * 64 + i * 32 + (lane & 31);
+        const u32x4 v = *reinterpret_cast<const u32x4*>(buf + chunk_off(r, c));
+        fa[i] = i32x8{(int)v[0], (int)v[1], (int)v[2], (int)v[3], 0, 0, 0, 0};
+        sca[i] = (int)(uint8_t)buf[2 * TILEB + r * 8 + c];
+      }
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int r = wn * 64 + j * 32 + (lane & 31);
+        const u32x4 v = *reinterpret_cast<const u32x4*>(buf + TILEB + chunk_off(r, c));
+        fb[j] = i32x8{(int)v[0], (int)v[1], (int)v[2], (int)v[3], 0, 0, 0, 0};
+        scb[j] = (int)(uint8_t)buf[2 * TILEB + SCB + r * 8 + c];
+      }
+      // B first: a lane then owns one output row and 4 consecutive columns per register group
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fb[j], fa[i], acc[i][j], 4, 4, 0, scb[j], 0,
+                                                                      sca[i]);
+    }
+    if (more) store(lds_ + ((s + 1) & 1) * BUF);
+    __syncthreads();
+  }
+
+  // lane: row m = lane % 32 of block i, columns 8*(r/4) + 4*(lane/32) + r%4 of block j
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int64_t m = (int64_t)tm * MT + wm * 64 + i * 32 + (lane & 31);
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int n = tn * MT + wn * 64 + j * 32 + 8 * q + 4 * (lane >> 5);
+        *reinterpret_cast<u32x2*>(g.c + m * g.ldc + n) =
+            u32x2{pack_bf16x2(acc[i][j][4 * q], acc[i][j][4 * q + 1]),
+                  pack_bf16x2(acc[i][j][4 * q + 2], acc[i][j][4 * q + 3])};
+      }
+  }
+}
+
+hipError_t mxfp4_gemm(const Mxfp4GemmArgs& g, hipStream_t s) {
+  if (g.M <= 0 || g.N <= 0 || g.K <= 0) return hipSuccess;
+  if (g.M % MT || g.N % MT || g.K % KSLAB) return hipErrorInvalidValue;
+  const int64_t tiles = (int64_t)(g.M / MT) * (g.N / MT);
+  if (tiles > INT32_MAX) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(mxfp4_gemm_kernel, dim3((unsigned)tiles), dim3(256), 0, s, g);
+  return hipGetLastError();
+}
+
+}  // namespace mtl

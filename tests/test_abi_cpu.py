@@ -273,3 +273,19 @@ def test_cp_attention_backward_validation_before_any_launch(mtl):
     assert bwd(1, qkv, P, P, P, P + 2, dkv, P, need) == mtl.MTL_E_ALIGN
     assert bwd(1, qkv, P, P, P, P, dkv, None, need) == mtl.MTL_E_NULL
     assert bwd(5, qkv, P, P, P, P, dkv, P, need) == mtl.MTL_E_RANK
+
+
+def test_mxfp4_validation_before_any_launch(mtl):
+    lib = mtl.lib()
+    P = 1 << 20
+    assert lib.mtl_mxfp4_quantize(None, 4, 64, P, P, None) == mtl.MTL_E_NULL
+    assert lib.mtl_mxfp4_quantize(P, 4, 48, P, P, None) == mtl.MTL_E_SHAPE  # cols % 32
+    assert lib.mtl_mxfp4_quantize(P, 0, 64, P, P, None) == mtl.MTL_E_SHAPE
+    assert lib.mtl_mxfp4_quantize(P, 4, 64, P + 4, P, None) == mtl.MTL_E_ALIGN
+    g = lambda M, N, K, c, ldc: lib.mtl_mxfp4_gemm(M, N, K, P, P, P, P, c, ldc, None)
+    assert g(128, 128, 256, None, 128) == mtl.MTL_E_NULL
+    assert g(100, 128, 256, P, 128) == mtl.MTL_E_SHAPE  # M % 128
+    assert g(128, 192, 256, P, 192) == mtl.MTL_E_SHAPE  # N % 128
+    assert g(128, 128, 320, P, 128) == mtl.MTL_E_SHAPE  # K % 256
+    assert g(128, 128, 256, P, 64) == mtl.MTL_E_SHAPE  # ldc < N
+    assert g(128, 128, 256, P + 8, 128) == mtl.MTL_E_ALIGN
