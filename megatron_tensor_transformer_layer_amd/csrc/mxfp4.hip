@@ -17,8 +17,8 @@
 namespace mtl {
 
 // ---------------------------------------------------------------- quantise
-// One thread per block of 32 elements: 64 bytes in, 16 bytes of codes and one
-// scale byte out.
+// Four lanes per block of 32 elements: 16 bytes in and 4 bytes of codes out per
+// lane, the block's amax exchanged among its four lanes, one scale byte.
 __device__ __forceinline__ uint32_t e2m1_code(float y, uint32_t sign) {
   const float a = fabsf(y);
   uint32_t c;
@@ -33,48 +33,42 @@ __device__ __forceinline__ uint32_t e2m1_code(float y, uint32_t sign) {
   return c | (sign << 3);
 }
 
-__global__ __launch_bounds__(256) void mxfp4_quant_kernel(const uint16_t* __restrict__ x, int64_t nblocks,
+__global__ __launch_bounds__(256) void mxfp4_quant_kernel(const uint16_t* __restrict__ x, int64_t nchunks,
                                                           uint8_t* __restrict__ codes, uint8_t* __restrict__ scales) {
-  const int64_t blk = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (blk >= nblocks) return;
-  const u32x4* src = reinterpret_cast<const u32x4*>(x + blk * 32);
-  u32x4 v[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) v[i] = src[i];
+  // chunk i = elements 8i .. 8i+7: consecutive lanes read consecutive 16 bytes,
+  // and the four lanes 4b .. 4b+3 of a group hold block b's 32 elements
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const bool ok = i < nchunks;  // nchunks % 4 == 0, so a group is all in or all out
+  const u32x4 v = ok ? *reinterpret_cast<const u32x4*>(x + i * 8) : u32x4{0, 0, 0, 0};
   uint32_t mx = 0;  // largest magnitude bits: integer order is value order for finite bf16
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) mx = max(mx, max(v[i][j] & 0x7fffu, (v[i][j] >> 16) & 0x7fffu));
+  for (int j = 0; j < 4; ++j) mx = max(mx, max(v[j] & 0x7fffu, (v[j] >> 16) & 0x7fffu));
+  mx = max(mx, (uint32_t)__shfl_xor((int)mx, 1));
+  mx = max(mx, (uint32_t)__shfl_xor((int)mx, 2));
   // amax = 2^(E-127) * 1.m for exponent field E >= 1; e = max(E - 129, -127),
   // so the E8M0 byte is max(E - 2, 0) (also for zero or subnormal amax)
   const int E = (int)(mx >> 7);
   const uint32_t sc = (uint32_t)max(E - 2, 0);
   const float mul = __uint_as_float((254u - sc) << 23);  // 2^-e, exact
-  u32x4 out;
+  uint32_t w = 0;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    uint32_t w = 0;
-#pragma unroll
-    for (int h = 0; h < 8; ++h) {  // element 8*i + h
-      const uint32_t word = v[i][h >> 1];
-      const uint32_t bits = (h & 1) ? (word >> 16) : (word & 0xffffu);
-      const float y = __uint_as_float(bits << 16) * mul;
-      w |= e2m1_code(y, bits >> 15) << (4 * h);
-    }
-    out[i] = w;
+  for (int h = 0; h < 8; ++h) {
+    const uint32_t bits = (h & 1) ? (v[h >> 1] >> 16) : (v[h >> 1] & 0xffffu);
+    const float y = __uint_as_float(bits << 16) * mul;
+    w |= e2m1_code(y, bits >> 15) << (4 * h);
   }
-  *reinterpret_cast<u32x4*>(codes + blk * 16) = out;
-  scales[blk] = (uint8_t)sc;
+  if (!ok) return;
+  *reinterpret_cast<uint32_t*>(codes + i * 4) = w;
+  if ((i & 3) == 0) scales[i >> 2] = (uint8_t)sc;
 }
 
 hipError_t mxfp4_quantize(const uint16_t* x, int64_t rows, int64_t cols, uint8_t* codes, uint8_t* scales,
                           hipStream_t s) {
-  const int64_t nblocks = rows * (cols / 32);
-  if (nblocks <= 0) return hipSuccess;
-  const int64_t grid = (nblocks + 255) / 256;
+  const int64_t nchunks = rows * (cols / 32) * 4;
+  if (nchunks <= 0) return hipSuccess;
+  const int64_t grid = (nchunks + 255) / 256;
   if (grid > INT32_MAX) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(mxfp4_quant_kernel, dim3((unsigned)grid), dim3(256), 0, s, x, nblocks, codes, scales);
+  hipLaunchKernelGGL(mxfp4_quant_kernel, dim3((unsigned)grid), dim3(256), 0, s, x, nchunks, codes, scales);
   return hipGetLastError();
 }
 
