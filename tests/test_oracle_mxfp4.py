@@ -98,3 +98,45 @@ def test_gemm_of_lossless_operands_is_the_plain_product():
     ca, sa = MX.quantize(a)
     cb, sb = MX.quantize(b)
     assert np.array_equal(MX.gemm(ca, sa, cb, sb), a @ b.T)
+
+
+# ---------------------------------------------------------------- MXFP6 (E2M3)
+# The OCP MX specification's E2M3 magnitudes: subnormals k/8, then 1..1.875,
+# 2..3.75, 4..7.5 in steps of 1/8, 1/4, 1/2.
+SPEC_E2M3 = [k / 8 for k in range(8)] + [1 + k / 8 for k in range(8)] + [2 + k / 4 for k in range(8)] + \
+    [4 + k / 2 for k in range(8)]
+
+
+def test_e2m3_table_matches_the_spec():
+    assert [MX.e2m3_value(c) for c in range(32)] == SPEC_E2M3
+    assert MX.e2m3_value(32 + 31) == -7.5
+
+
+def test_e2m3_rounding_ties_and_saturation():
+    x = np.zeros((1, 32))
+    x[0, 0] = 7.5  # floor(log2 7.5) = 2: scale 2^0
+    probes = {1: (0.0625, 0), 2: (0.1875, 2), 3: (0.9375, 8), 4: (1.0625, 8), 5: (1.9375, 16), 6: (3.875, 24),
+              7: (7.75, 31), 8: (7.7, 31), 9: (5.25, 26), 10: (5.26, 27)}
+    for col, (v, _) in probes.items():
+        x[0, col] = v
+    codes, scales = MX.quantize(x, "e2m3")
+    assert scales[0, 0] == 127
+    for col, (v, want) in probes.items():
+        assert codes[0, col] == want, (v, codes[0, col], want)
+    x[0, 1:] = -x[0, 1:]
+    codes, _ = MX.quantize(x, "e2m3")
+    assert codes[0, 3] == 8 | 32
+
+
+def test_e2m3_round_trip_and_pack6():
+    rng = np.random.default_rng(4)
+    vals = rng.choice(SPEC_E2M3, (3, 64)) * rng.choice([-1, 1], (3, 64))
+    vals[:, 0] = vals[:, 32] = 7.5
+    x = vals * 2.0 ** np.array([[-5], [0], [9]])
+    codes, scales = MX.quantize(x, "e2m3")
+    assert np.array_equal(MX.dequantize(codes, scales, "e2m3"), x)
+    p = MX.pack6(codes)
+    assert p.shape == (3, 48)
+    # element j of a block at bits 6j..6j+5 of its 24 little-endian bytes
+    v = int.from_bytes(bytes(p[1, 24:48]), "little")
+    assert [(v >> (6 * j)) & 63 for j in range(32)] == codes[1, 32:64].tolist()
