@@ -15,8 +15,9 @@ expert block instead (route, permute, grouped expert GEMMs, combine, backward);
 with --workload cp4-seq32k-7b-tp4 it is one context-parallel rank's causal
 attention share, forward and backward (by default the last of 4 ranks of a
 32768-token sequence: its own chunk causally and the three earlier chunks in
-full); with --workload mxfp4-gemm-7b-tp4 it is the rank's fc1 GEMM in MXFP4
-(both operands quantised, then the block-scaled MFMA GEMM).
+full); with --workload mxfp4-gemm-7b-tp4 (or mxfp6-gemm-7b-tp4) it is the
+rank's fc1 GEMM in MXFP4 (MXFP6): both operands quantised, then the
+block-scaled MFMA GEMM.
 """
 from __future__ import annotations
 
@@ -363,16 +364,16 @@ def cp_main(args):
 
 
 def mx_cpu_baseline(shape, sample_rows):
-    """The MXFP4 oracle (fp64, as it stands) on a bounded sample: quantise
+    """The MX oracle (fp64, as it stands) on a bounded sample: quantise
     sample_rows rows of A and of B and multiply them (sample_rows^2 outputs)."""
     import synth
     from oracle import mxfp4 as MX
     a = synth.bf16_bits_to_f64(synth.mx_operand(shape.M, shape.K, "mx_a", 1.0)[:sample_rows])
     b = synth.bf16_bits_to_f64(synth.mx_operand(shape.N, shape.K, "mx_b", synth.WEIGHT_STD)[:sample_rows])
     t0 = time.perf_counter()
-    ca, sa = MX.quantize(a)
-    cb, sb = MX.quantize(b)
-    MX.gemm(ca, sa, cb, sb)
+    ca, sa = MX.quantize(a, shape.elem)
+    cb, sb = MX.quantize(b, shape.elem)
+    MX.gemm(ca, sa, cb, sb, shape.elem)
     dt = time.perf_counter() - t0
     fl = 2.0 * sample_rows * sample_rows * shape.K
     return {"value": fl / dt / 1e12, "unit": "TFLOP/s", "cores": len(os.sched_getaffinity(0)), "kind": "oracle",
@@ -381,33 +382,38 @@ def mx_cpu_baseline(shape, sample_rows):
 
 
 def mx_main(args):
-    """One GEMM of the 7B-class rank in MXFP4: quantise the activations and the
-    weight (mtl_mxfp4_quantize) and multiply them on the block-scaled MFMA
-    (mtl_mxfp4_gemm)."""
+    """One GEMM of the 7B-class rank in MXFP4 or MXFP6: quantise the activations
+    and the weight (mtl_mxfp4_quantize / mtl_mxfp6_quantize) and multiply them
+    on the block-scaled MFMA (mtl_mxfp4_gemm / mtl_mxfp6_gemm)."""
     import torch
     import synth
-    from megatron_tensor_transformer_layer_amd import mtl_mxfp4_gemm, mtl_mxfp4_quantize
+    import megatron_tensor_transformer_layer_amd as mtl
     from megatron_tensor_transformer_layer_amd.layer import bf16_dev
 
     shape = synth.MX_WORKLOADS[args.workload]
+    fp6 = shape.elem == "e2m3"
+    name = "MXFP6" if fp6 else "MXFP4"
+    quant = mtl.mtl_mxfp6_quantize if fp6 else mtl.mtl_mxfp4_quantize
+    gemm = mtl.mtl_mxfp6_gemm if fp6 else mtl.mtl_mxfp4_gemm
     M, N, K = shape.M, shape.N, shape.K
+    cb_cols = K * 3 // 4 if fp6 else K // 2
     a = bf16_dev(synth.mx_operand(M, K, "mx_a", 1.0))
     b = bf16_dev(synth.mx_operand(N, K, "mx_b", synth.WEIGHT_STD))
-    ca = torch.empty(M, K // 2, dtype=torch.uint8, device="cuda")
+    ca = torch.empty(M, cb_cols, dtype=torch.uint8, device="cuda")
     sa = torch.empty(M, K // 32, dtype=torch.uint8, device="cuda")
-    cb = torch.empty(N, K // 2, dtype=torch.uint8, device="cuda")
+    cb = torch.empty(N, cb_cols, dtype=torch.uint8, device="cuda")
     sb = torch.empty(N, K // 32, dtype=torch.uint8, device="cuda")
     c = torch.empty(M, N, dtype=torch.bfloat16, device="cuda")
     ev = lambda: torch.cuda.Event(enable_timing=True)
     marks = []
 
     def step(record=False):
-        mtl_mxfp4_quantize(a, M, K, ca, sa)
-        mtl_mxfp4_quantize(b, N, K, cb, sb)
+        quant(a, M, K, ca, sa)
+        quant(b, N, K, cb, sb)
         if record:
             e0, e1 = ev(), ev()
             e0.record()
-        mtl_mxfp4_gemm(M, N, K, ca, sa, cb, sb, c)
+        gemm(M, N, K, ca, sa, cb, sb, c)
         if record:
             e1.record()
             marks.append((e0, e1))
@@ -424,17 +430,17 @@ def mx_main(args):
     fl = 2.0 * M * N * K
     achieved = fl / (gemm_ms / 1e3) / 1e12
     out = {
-        "metric": "TFLOP/s of one MXFP4 GEMM of the TP-rank layer (quantisation included) and % of MI355X MFMA peak",
+        "metric": f"TFLOP/s of one {name} GEMM of the TP-rank layer (quantisation included) and % of MI355X MFMA peak",
         "value": round(fl / (ms / 1e3) / 1e12, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": "mxfp4",
+        "vs_baseline": None, "dtype": name.lower(),
         "data": "synthetic (N(0,1) activations, N(0,0.02) weight, bf16 before quantisation)",
         "config": {"workload": f"{args.workload}: fc1 forward of the 7B-class TP=4 rank, {M}x{N}x{K}, both "
-                               f"operands quantised to MXFP4 each step, bf16 output",
+                               f"operands quantised to {name} each step, bf16 output",
                    "global_batch": 1, "seq_len": M, "parallelism": "tp4-rank0-of-1gpu"},
         "pct_of_peak": round(100 * fl / (ms / 1e3) / 1e12 / PEAK_FP4_TFLOPS, 2),
         "flop_per_step": fl,
-        "roofline": {"bound": "mfma", "kernel": "mxfp4_gemm_kernel, 128x128 tiles, HIP events on its stream",
+        "roofline": {"bound": "mfma", "kernel": f"{name.lower()}_gemm_kernel, 128x128 tiles, HIP events on its stream",
                      "achieved": round(achieved, 1), "peak": PEAK_FP4_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved / PEAK_FP4_TFLOPS, 4), "traffic": None,
                      "gemm_launch_us": round(gemm_ms * 1e3, 1)},

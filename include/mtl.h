@@ -219,6 +219,18 @@ mtl_status mtl_mxfp4_quantize(const void* x, int64_t rows, int64_t cols, void* c
 mtl_status mtl_mxfp4_gemm(int64_t M, int64_t N, int64_t K, const void* a_codes, const void* a_scales,
                           const void* b_codes, const void* b_scales, void* c, int64_t ldc, mtl_stream_t stream);
 
+/* MXFP6: the same as mtl_mxfp4_quantize / mtl_mxfp4_gemm with FP6 E2M3 elements
+ * (sign, 2 exponent bits of bias 1, 3 mantissa bits; magnitudes k/8 below 1,
+ * then steps of 1/8, 1/4, 1/2 up to 7.5; the largest exponent is again 2, so
+ * the block scale rule is the same).  codes: [rows, cols*3/4] bytes, each
+ * block of 32 elements in 24 bytes with element j at bits 6j .. 6j+5 of the
+ * block read as a little-endian number.  The GEMM takes M % 128 == 0,
+ * N % 128 == 0, K % 128 == 0. */
+mtl_status mtl_mxfp6_quantize(const void* x, int64_t rows, int64_t cols, void* codes, void* scales,
+                              mtl_stream_t stream);
+mtl_status mtl_mxfp6_gemm(int64_t M, int64_t N, int64_t K, const void* a_codes, const void* a_scales,
+                          const void* b_codes, const void* b_scales, void* c, int64_t ldc, mtl_stream_t stream);
+
 /* MLP half of the rank's forward (column-parallel fc1 with fused GeLU,
  * row-parallel fc2), with z = h . w1 + b1 in fp32:
  *   gz      = GeLU'(z)        [S, f/t] bf16 (saved: the backward needs z only

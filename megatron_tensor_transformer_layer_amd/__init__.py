@@ -56,6 +56,8 @@ _SIGS = {
     "mtl_cp_attn_fwd": (ctypes.c_int, [_I32, _I32, _I64, _I32, _I32, ctypes.POINTER(_P), _P, _P, _P, _SZ, _P]),
     "mtl_mxfp4_quantize": (ctypes.c_int, [_P, _I64, _I64, _P, _P, _P]),
     "mtl_mxfp4_gemm": (ctypes.c_int, [_I64, _I64, _I64, _P, _P, _P, _P, _P, _I64, _P]),
+    "mtl_mxfp6_quantize": (ctypes.c_int, [_P, _I64, _I64, _P, _P, _P]),
+    "mtl_mxfp6_gemm": (ctypes.c_int, [_I64, _I64, _I64, _P, _P, _P, _P, _P, _I64, _P]),
     "mtl_cp_attn_bwd_scratch_bytes": (ctypes.c_int, [_I32, _I32, _I64, _I32, _I32, ctypes.POINTER(_SZ)]),
     "mtl_cp_attn_bwd": (ctypes.c_int, [_I32, _I32, _I64, _I32, _I32, ctypes.POINTER(_P), _P, _P, _P, _P,
                                        ctypes.POINTER(_P), _P, _SZ, _P]),
@@ -200,6 +202,16 @@ def mtl_mxfp4_quantize(x, rows, cols, codes, scales, stream=None):
 def mtl_mxfp4_gemm(M, N, K, a_codes, a_scales, b_codes, b_scales, c, ldc=None, stream=None):
     _check(lib().mtl_mxfp4_gemm(M, N, K, _ptr(a_codes), _ptr(a_scales), _ptr(b_codes), _ptr(b_scales), _ptr(c),
                                 N if ldc is None else ldc, _stream(stream)), "mtl_mxfp4_gemm")
+
+
+def mtl_mxfp6_quantize(x, rows, cols, codes, scales, stream=None):
+    _check(lib().mtl_mxfp6_quantize(_ptr(x), rows, cols, _ptr(codes), _ptr(scales), _stream(stream)),
+           "mtl_mxfp6_quantize")
+
+
+def mtl_mxfp6_gemm(M, N, K, a_codes, a_scales, b_codes, b_scales, c, ldc=None, stream=None):
+    _check(lib().mtl_mxfp6_gemm(M, N, K, _ptr(a_codes), _ptr(a_scales), _ptr(b_codes), _ptr(b_scales), _ptr(c),
+                                N if ldc is None else ldc, _stream(stream)), "mtl_mxfp6_gemm")
 
 
 def mtl_mlp_fwd(cfg, h, w1, b1, w2, gz, a, partial, scratch=None, scratch_bytes=None, stream=None):

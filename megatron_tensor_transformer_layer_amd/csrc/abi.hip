@@ -554,6 +554,34 @@ mtl_status mtl_mxfp4_gemm(int64_t M, int64_t N, int64_t K, const void* a_codes, 
   return hip_status(mxfp4_gemm(g, reinterpret_cast<hipStream_t>(stream)));
 }
 
+mtl_status mtl_mxfp6_quantize(const void* x, int64_t rows, int64_t cols, void* codes, void* scales,
+                              mtl_stream_t stream) {
+  mtl_status st = check_ptrs(x, codes, scales);
+  if (st != MTL_OK) return st;
+  if (rows <= 0 || cols <= 0 || cols % 32 != 0) return MTL_E_SHAPE;
+  return hip_status(mxfp6_quantize(static_cast<const uint16_t*>(x), rows, cols, static_cast<uint8_t*>(codes),
+                                   static_cast<uint8_t*>(scales), reinterpret_cast<hipStream_t>(stream)));
+}
+
+mtl_status mtl_mxfp6_gemm(int64_t M, int64_t N, int64_t K, const void* a_codes, const void* a_scales,
+                          const void* b_codes, const void* b_scales, void* c, int64_t ldc, mtl_stream_t stream) {
+  mtl_status st = check_ptrs(a_codes, a_scales, b_codes, b_scales, c);
+  if (st != MTL_OK) return st;
+  if (M <= 0 || N <= 0 || K <= 0 || M % 128 || N % 128 || K % 128 || ldc < N || ldc % 8) return MTL_E_SHAPE;
+  if (M > INT32_MAX || N > INT32_MAX || K > INT32_MAX) return MTL_E_SHAPE;
+  Mxfp4GemmArgs g{};
+  g.a = static_cast<const uint8_t*>(a_codes);
+  g.sa = static_cast<const uint8_t*>(a_scales);
+  g.b = static_cast<const uint8_t*>(b_codes);
+  g.sb = static_cast<const uint8_t*>(b_scales);
+  g.c = static_cast<uint16_t*>(c);
+  g.ldc = ldc;
+  g.M = (int)M;
+  g.N = (int)N;
+  g.K = (int)K;
+  return hip_status(mxfp6_gemm(g, reinterpret_cast<hipStream_t>(stream)));
+}
+
 mtl_status mtl_mlp_fwd(const mtl_layer_cfg* c, const void* h, const void* w1, const void* b1, const void* w2, void* gz,
                        void* a, void* partial, void* scratch, size_t scratch_bytes, mtl_stream_t stream) {
   mtl_status st = mtl_validate(c);

@@ -146,6 +146,12 @@ struct Mxfp4GemmArgs {
   int M, N, K;
 };
 hipError_t mxfp4_gemm(const Mxfp4GemmArgs& g, hipStream_t s);
+// The same for MXFP6 (FP6 E2M3 elements): codes [rows, cols*3/4], 32 elements
+// of 6 bits per 24 bytes, element j at bits 6j.. of the little-endian block;
+// the GEMM takes K % 128 == 0.
+hipError_t mxfp6_quantize(const uint16_t* x, int64_t rows, int64_t cols, uint8_t* codes, uint8_t* scales,
+                          hipStream_t s);
+hipError_t mxfp6_gemm(const Mxfp4GemmArgs& g, hipStream_t s);
 hipError_t attention_bwd(const AttnArgs& a, hipStream_t s);
 // The backward of attention_fwd_full for queries whose D = rowsum(dO * O) is
 // already in a.delta (kv_seq == seq, seq % 64 == 0): no D launch.

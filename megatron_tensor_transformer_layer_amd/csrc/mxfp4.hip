@@ -1,5 +1,5 @@
-// MXFP4 (OCP Microscaling, FP4 E2M1 elements in blocks of 32 along K sharing
-// an E8M0 scale) quantisation and GEMM for gfx950.
+// MXFP4 and MXFP6 (OCP Microscaling: FP4 E2M1 or FP6 E2M3 elements in blocks
+// of 32 along K sharing an E8M0 scale) quantisation and GEMMs for gfx950.
 //
 // Format: the scale of a block is 2^e with e = floor(log2(max |v|)) - 2
 // (clamped at -127), stored as e + 127; each element is v / 2^e rounded to the
@@ -60,6 +60,67 @@ __global__ __launch_bounds__(256) void mxfp4_quant_kernel(const uint16_t* __rest
   if (!ok) return;
   *reinterpret_cast<uint32_t*>(codes + i * 4) = w;
   if ((i & 3) == 0) scales[i >> 2] = (uint8_t)sc;
+}
+
+// FP6 E2M3 code of y (|y| < 8 by the block scale): below 1 the spacing is 1/8
+// (subnormals, code = rint(8|y|)); in [2^E, 2^(E+1)) it is 2^(E-3); ties to
+// even through rint, a rounding up to 2^(E+1) moves to the next exponent, and
+// past 7.5 saturates.
+__device__ __forceinline__ uint32_t e2m3_code(float y, uint32_t sign) {
+  const float a = fabsf(y);
+  uint32_t c;
+  if (a < 1.0f) {
+    c = (uint32_t)__builtin_rintf(a * 8.0f);  // 8 is the code of 1.0
+  } else {
+    int E = (int)((__float_as_uint(a) >> 23) & 0xffu) - 127;           // 0, 1 or 2
+    uint32_t q = (uint32_t)__builtin_rintf(a * __uint_as_float((uint32_t)(130 - E) << 23));  // 8 .. 16
+    if (q == 16) {
+      ++E;
+      q = 8;
+    }
+    c = E > 2 ? 31u : (((uint32_t)(E + 1) << 3) | (q - 8));
+  }
+  return c | (sign << 5);
+}
+
+// MXFP6: four lanes per block as for MXFP4; each lane's 8 codes are 48
+// consecutive bits of the block's 24 bytes, written as three 16-bit words.
+__global__ __launch_bounds__(256) void mxfp6_quant_kernel(const uint16_t* __restrict__ x, int64_t nchunks,
+                                                          uint8_t* __restrict__ codes, uint8_t* __restrict__ scales) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const bool ok = i < nchunks;
+  const u32x4 v = ok ? *reinterpret_cast<const u32x4*>(x + i * 8) : u32x4{0, 0, 0, 0};
+  uint32_t mx = 0;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) mx = max(mx, max(v[j] & 0x7fffu, (v[j] >> 16) & 0x7fffu));
+  mx = max(mx, (uint32_t)__shfl_xor((int)mx, 1));
+  mx = max(mx, (uint32_t)__shfl_xor((int)mx, 2));
+  const int E = (int)(mx >> 7);
+  const uint32_t sc = (uint32_t)max(E - 2, 0);  // E2M3's largest exponent is 2 as well
+  const float mul = __uint_as_float((254u - sc) << 23);
+  uint64_t w = 0;
+#pragma unroll
+  for (int h = 0; h < 8; ++h) {
+    const uint32_t bits = (h & 1) ? (v[h >> 1] >> 16) : (v[h >> 1] & 0xffffu);
+    const float y = __uint_as_float(bits << 16) * mul;
+    w |= (uint64_t)e2m3_code(y, bits >> 15) << (6 * h);
+  }
+  if (!ok) return;
+  uint16_t* dst = reinterpret_cast<uint16_t*>(codes + i * 6);
+  dst[0] = (uint16_t)w;
+  dst[1] = (uint16_t)(w >> 16);
+  dst[2] = (uint16_t)(w >> 32);
+  if ((i & 3) == 0) scales[i >> 2] = (uint8_t)sc;
+}
+
+hipError_t mxfp6_quantize(const uint16_t* x, int64_t rows, int64_t cols, uint8_t* codes, uint8_t* scales,
+                          hipStream_t s) {
+  const int64_t nchunks = rows * (cols / 32) * 4;
+  if (nchunks <= 0) return hipSuccess;
+  const int64_t grid = (nchunks + 255) / 256;
+  if (grid > INT32_MAX) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(mxfp6_quant_kernel, dim3((unsigned)grid), dim3(256), 0, s, x, nchunks, codes, scales);
+  return hipGetLastError();
 }
 
 hipError_t mxfp4_quantize(const uint16_t* x, int64_t rows, int64_t cols, uint8_t* codes, uint8_t* scales,
@@ -190,6 +251,127 @@ __global__ __launch_bounds__(256, 2) void mxfp4_gemm_kernel(Mxfp4GemmArgs g) {
                   pack_bf16x2(acc[i][j][4 * q + 2], acc[i][j][4 * q + 3])};
       }
   }
+}
+
+// MXFP6 GEMM: the same tiling with 128-deep K slabs (96 code bytes and 4
+// scale bytes per row, 58 KB of LDS for both buffers, two workgroups per CU);
+// a lane's fragment is 24 bytes (32 elements of 6 bits), read as three 8-byte
+// words.  LDS rows are padded to 112 bytes: the 16 rows a half-wave reads
+// then start 28 banks apart (mod 64), on 16 distinct pairs of banks.
+namespace {
+constexpr int KS6 = 128, ROWB6 = KS6 * 6 / 8;  // 96 code bytes per row and slab
+constexpr int LROW6 = ROWB6 + 16;               // LDS row stride
+constexpr int TILEB6 = MT * LROW6;              // 14 KB per operand and slab
+constexpr int SCB6 = MT * (KS6 / 32);           // 512 B of scales per operand and slab
+constexpr int BUF6 = 2 * TILEB6 + 2 * SCB6;
+}  // namespace
+
+__global__ __launch_bounds__(256, 2) void mxfp6_gemm_kernel(Mxfp4GemmArgs g) {
+  __shared__ __attribute__((aligned(1024))) char lds_[2 * BUF6];
+  const int ntn = g.N / MT;
+  const int ntiles = (g.M / MT) * ntn;
+  const int u = xcd_index(blockIdx.x, ntiles);
+  const int tm = u / ntn, tn = u % ntn;
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int64_t kb = (int64_t)g.K * 6 / 8, ks = g.K / 32;
+  const uint8_t* a0 = g.a + (int64_t)tm * MT * kb;
+  const uint8_t* b0 = g.b + (int64_t)tn * MT * kb;
+  const uint8_t* sa0 = g.sa + (int64_t)tm * MT * ks;
+  const uint8_t* sb0 = g.sb + (int64_t)tn * MT * ks;
+  const int nslab = g.K / KS6;
+
+  // 128 rows x 6 chunks of 16 bytes per operand: 3 per thread; 4 scale bytes of
+  // one row of A (threads 0..127) or B (128..255)
+  u32x4 ra[3], rb[3];
+  uint32_t rsc;
+  auto load = [&](int s) {
+#pragma unroll
+    for (int i = 0; i < 3; ++i) {
+      const int idx = t + 256 * i, r = idx / 6, c = idx % 6;
+      ra[i] = *reinterpret_cast<const u32x4*>(a0 + r * kb + s * ROWB6 + c * 16);
+      rb[i] = *reinterpret_cast<const u32x4*>(b0 + r * kb + s * ROWB6 + c * 16);
+    }
+    rsc = *reinterpret_cast<const uint32_t*>((t < 128 ? sa0 : sb0) + (t & 127) * ks + s * 4);
+  };
+  auto store = [&](char* buf) {
+#pragma unroll
+    for (int i = 0; i < 3; ++i) {
+      const int idx = t + 256 * i, off = (idx / 6) * LROW6 + (idx % 6) * 16;
+      *reinterpret_cast<u32x4*>(buf + off) = ra[i];
+      *reinterpret_cast<u32x4*>(buf + TILEB6 + off) = rb[i];
+    }
+    *reinterpret_cast<uint32_t*>(buf + 2 * TILEB6 + (t < 128 ? 0 : SCB6) + (t & 127) * 4) = rsc;
+  };
+
+  f32x16 acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) acc[i][j] = f32x16{};
+
+  typedef int i32x8 __attribute__((ext_vector_type(8)));
+  load(0);
+  store(lds_);
+  __syncthreads();
+  for (int s = 0; s < nslab; ++s) {
+    const bool more = s + 1 < nslab;
+    if (more) load(s + 1);
+    const char* buf = lds_ + (s & 1) * BUF6;
+#pragma unroll
+    for (int kk = 0; kk < KS6 / 64; ++kk) {
+      const int blk = kk * 2 + (lane >> 5);  // this lane's 32-element block of the slab
+      i32x8 fa[2], fb[2];
+      int sca[2], scb[2];
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int r = wm * 64 + i * 32 + (lane & 31);
+        const u32x2* p = reinterpret_cast<const u32x2*>(buf + r * LROW6 + blk * 24);
+        const u32x2 x0 = p[0], x1 = p[1], x2 = p[2];
+        fa[i] = i32x8{(int)x0[0], (int)x0[1], (int)x1[0], (int)x1[1], (int)x2[0], (int)x2[1], 0, 0};
+        sca[i] = (int)(uint8_t)buf[2 * TILEB6 + r * 4 + blk];
+      }
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int r = wn * 64 + j * 32 + (lane & 31);
+        const u32x2* p = reinterpret_cast<const u32x2*>(buf + TILEB6 + r * LROW6 + blk * 24);
+        const u32x2 x0 = p[0], x1 = p[1], x2 = p[2];
+        fb[j] = i32x8{(int)x0[0], (int)x0[1], (int)x1[0], (int)x1[1], (int)x2[0], (int)x2[1], 0, 0};
+        scb[j] = (int)(uint8_t)buf[2 * TILEB6 + SCB6 + r * 4 + blk];
+      }
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)  // format 2: FP6 E2M3
+          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fb[j], fa[i], acc[i][j], 2, 2, 0, scb[j], 0,
+                                                                      sca[i]);
+    }
+    if (more) store(lds_ + ((s + 1) & 1) * BUF6);
+    __syncthreads();
+  }
+
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int64_t m = (int64_t)tm * MT + wm * 64 + i * 32 + (lane & 31);
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int n = tn * MT + wn * 64 + j * 32 + 8 * q + 4 * (lane >> 5);
+        *reinterpret_cast<u32x2*>(g.c + m * g.ldc + n) =
+            u32x2{pack_bf16x2(acc[i][j][4 * q], acc[i][j][4 * q + 1]),
+                  pack_bf16x2(acc[i][j][4 * q + 2], acc[i][j][4 * q + 3])};
+      }
+  }
+}
+
+hipError_t mxfp6_gemm(const Mxfp4GemmArgs& g, hipStream_t s) {
+  if (g.M <= 0 || g.N <= 0 || g.K <= 0) return hipSuccess;
+  if (g.M % MT || g.N % MT || g.K % KS6) return hipErrorInvalidValue;
+  const int64_t tiles = (int64_t)(g.M / MT) * (g.N / MT);
+  if (tiles > INT32_MAX) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(mxfp6_gemm_kernel, dim3((unsigned)tiles), dim3(256), 0, s, g);
+  return hipGetLastError();
 }
 
 hipError_t mxfp4_gemm(const Mxfp4GemmArgs& g, hipStream_t s) {

@@ -122,17 +122,19 @@ class CpShape:
 CP_WORKLOADS = {
     "cp4-seq32k-7b-tp4": CpShape(seq=32768, heads=8, head_dim=128, cp=4),
 }
-# A GEMM of the 7B-class TP=4 rank in MXFP4: the fc1 forward, tokens x hidden
-# times hidden x local ffn (4096 x 4096 x 4096).
+# A GEMM of the 7B-class TP=4 rank in MXFP4 or MXFP6: the fc1 forward, tokens x
+# hidden times hidden x local ffn (4096 x 4096 x 4096).
 @dataclass(frozen=True)
 class MxShape:
     M: int
     N: int
     K: int
+    elem: str = "e2m1"  # MXFP4; "e2m3" for MXFP6
 
 
 MX_WORKLOADS = {
     "mxfp4-gemm-7b-tp4": MxShape(M=4096, N=4096, K=4096),
+    "mxfp6-gemm-7b-tp4": MxShape(M=4096, N=4096, K=4096, elem="e2m3"),
 }
 MOE_WORKLOADS = {
     "moe-256e-top8-ep16": MoeShape(tokens=4096, hidden=7168, ffn=18432, experts=256, topk=8, ep=16),

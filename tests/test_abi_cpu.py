@@ -289,3 +289,14 @@ def test_mxfp4_validation_before_any_launch(mtl):
     assert g(128, 128, 320, P, 128) == mtl.MTL_E_SHAPE  # K % 256
     assert g(128, 128, 256, P, 64) == mtl.MTL_E_SHAPE  # ldc < N
     assert g(128, 128, 256, P + 8, 128) == mtl.MTL_E_ALIGN
+
+
+def test_mxfp6_validation_before_any_launch(mtl):
+    lib = mtl.lib()
+    P = 1 << 20
+    assert lib.mtl_mxfp6_quantize(P, 4, 48, P, P, None) == mtl.MTL_E_SHAPE  # cols % 32
+    assert lib.mtl_mxfp6_quantize(P, 4, 64, None, P, None) == mtl.MTL_E_NULL
+    g = lambda M, N, K: lib.mtl_mxfp6_gemm(M, N, K, P, P, P, P, P, N, None)
+    assert g(128, 128, 192) == mtl.MTL_E_SHAPE  # K % 128
+    assert g(64, 128, 128) == mtl.MTL_E_SHAPE
+    assert lib.mtl_mxfp6_gemm(128, 128, 128, P, P, P + 4, P, P, 128, None) == mtl.MTL_E_ALIGN
