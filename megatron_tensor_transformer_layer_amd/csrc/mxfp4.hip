@@ -146,10 +146,14 @@ constexpr int TILEB = MT * ROWB;                         // 16 KB of codes per o
 constexpr int SCB = MT * (KSLAB / 32);                   // 1 KB of scales per operand and slab
 constexpr int BUF = 2 * TILEB + 2 * SCB;
 
-// 16-byte chunk c of row r sits at chunk c ^ ((r >> 1) & 7): the 16 rows a
-// quarter-wave reads (or writes) at one logical chunk hit 16 distinct groups of
-// four banks on the 64-bank LDS.
-__device__ __forceinline__ int chunk_off(int r, int c) { return r * ROWB + ((c ^ ((r >> 1) & 7)) << 4); }
+// 16-byte chunk c of row r sits at chunk c ^ s(r), s(r) = 2*((r >> 1) & 3) +
+// ((r >> 3) & 1).  Rows are 128 bytes (half the 64 banks, by row parity), so
+// the 16 rows of a quarter-wave at one chunk, and the 8 rows of the lower and
+// upper half-waves at chunks c and c ^ 1 (the two K halves of a fragment), each
+// fall on distinct groups of four banks.
+__device__ __forceinline__ int chunk_off(int r, int c) {
+  return r * ROWB + ((c ^ ((((r >> 1) & 3) << 1) | ((r >> 3) & 1))) << 4);
+}
 }  // namespace
 
 __global__ __launch_bounds__(256, 2) void mxfp4_gemm_kernel(Mxfp4GemmArgs g) {
@@ -206,6 +210,19 @@ __global__ __launch_bounds__(256, 2) void mxfp4_gemm_kernel(Mxfp4GemmArgs g) {
     const bool more = s + 1 < nslab;
     if (more) load(s + 1);
     const char* buf = lds_ + (s & 1) * BUF;
+    // the 8 scale bytes of each of the lane's four rows, read once per slab and
+    // shifted by the lane's K half: k step kk takes byte 2*(kk & 1) of word kk >> 1
+    u32x2 sva[2], svb[2];
+    {
+      const int sh = 8 * (lane >> 5);
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const u32x2 w = *reinterpret_cast<const u32x2*>(buf + 2 * TILEB + (wm * 64 + i * 32 + (lane & 31)) * 8);
+        sva[i] = u32x2{w[0] >> sh, w[1] >> sh};
+        const u32x2 x = *reinterpret_cast<const u32x2*>(buf + 2 * TILEB + SCB + (wn * 64 + i * 32 + (lane & 31)) * 8);
+        svb[i] = u32x2{x[0] >> sh, x[1] >> sh};
+      }
+    }
 #pragma unroll
     for (int kk = 0; kk < KSLAB / 64; ++kk) {
       const int c = kk * 2 + (lane >> 5);  // this lane's 16-byte chunk (32 elements) of the k step
@@ -216,14 +233,14 @@ __global__ __launch_bounds__(256, 2) void mxfp4_gemm_kernel(Mxfp4GemmArgs g) {
         const int r = wm * 64 + i * 32 + (lane & 31);
         const u32x4 v = *reinterpret_cast<const u32x4*>(buf + chunk_off(r, c));
         fa[i] = i32x8{(int)v[0], (int)v[1], (int)v[2], (int)v[3], 0, 0, 0, 0};
-        sca[i] = (int)(uint8_t)buf[2 * TILEB + r * 8 + c];
+        sca[i] = (int)((sva[i][kk >> 1] >> (16 * (kk & 1))) & 0xffu);
       }
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
         const int r = wn * 64 + j * 32 + (lane & 31);
         const u32x4 v = *reinterpret_cast<const u32x4*>(buf + TILEB + chunk_off(r, c));
         fb[j] = i32x8{(int)v[0], (int)v[1], (int)v[2], (int)v[3], 0, 0, 0, 0};
-        scb[j] = (int)(uint8_t)buf[2 * TILEB + SCB + r * 8 + c];
+        scb[j] = (int)((svb[j][kk >> 1] >> (16 * (kk & 1))) & 0xffu);
       }
       // B first: a lane then owns one output row and 4 consecutive columns per register group
 #pragma unroll
