@@ -55,6 +55,8 @@ def parse():
     ap.add_argument("--cpu-sample-seq", type=int, default=4096)
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run only a plain device copy of known size (for scaling HBM byte counters)")
+    ap.add_argument("--copy-rate", action="store_true",
+                    help="time the plain copy at 64 MiB, 256 MiB and 1 GiB (the practical HBM ceiling) and exit")
     return ap.parse_args()
 
 
@@ -103,9 +105,15 @@ def calibrate_copy():
     assert torch.equal(src, dst)
     print(json.dumps({"copy_kernel": "reduce_partials_kernel (t=1)", "bytes_read": rows * cols * 2,
                       "bytes_written": rows * cols * 2, "launches": 3}), flush=True)
-    # the rate the same copy reaches, read + written bytes over the launch time,
-    # as the practical HBM ceiling of the streaming kernels
-    del src, dst
+
+
+def copy_rate():
+    """The rate the plain copy of calibrate_copy reaches, read + written bytes
+    over the launch time (HIP events, 20 launches), at 64 MiB, 256 MiB and
+    1 GiB: the practical HBM ceiling of the streaming kernels."""
+    import torch
+    from megatron_tensor_transformer_layer_amd import mtl_reduce
+    cols = 4096
     for mib in (64, 256, 1024):
         rows = (mib << 20) // 2 // cols
         src = torch.randn(rows, cols, device="cuda").to(torch.bfloat16)
@@ -546,6 +554,9 @@ def main():
 
     if args.calibrate_copy:
         calibrate_copy()
+        return
+    if args.copy_rate:
+        copy_rate()
         return
     import torch
     import synth
