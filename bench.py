@@ -548,7 +548,7 @@ def moe_main(args):
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path (collectives are replaced by an "
+        print("bench.py measures one GPU: the library has no multi-GPU path (collectives are replaced by an "
               "on-device reduce); run with --gpus 1", file=sys.stderr)
         sys.exit(2)
 
