@@ -378,7 +378,8 @@ mtl_status mtl_allgather_rows(int32_t t, int32_t rank, const void* const* bufs, 
 static mtl_status cp_check(int32_t cp, int32_t rank, int64_t chunk, int32_t heads, int32_t head_dim) {
   if (cp < 1 || cp > MTL_CP_MAX) return MTL_E_SHAPE;
   if (rank < 0 || rank >= cp) return MTL_E_RANK;
-  if (chunk <= 0 || chunk % 64 != 0 || heads <= 0 || (head_dim != 64 && head_dim != 128)) return MTL_E_SHAPE;
+  if (chunk <= 0 || chunk > INT32_MAX || chunk % 64 != 0 || heads <= 0 || (head_dim != 64 && head_dim != 128))
+    return MTL_E_SHAPE;
   // the kernels address a chunk's QKV through 32-bit buffer offsets
   if ((chunk + 64) * 3 * heads * head_dim * 2 > (int64_t)UINT32_MAX) return MTL_E_SHAPE;
   return MTL_OK;
