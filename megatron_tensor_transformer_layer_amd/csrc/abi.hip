@@ -531,7 +531,7 @@ mtl_status mtl_mxfp4_quantize(const void* x, int64_t rows, int64_t cols, void* c
                               mtl_stream_t stream) {
   mtl_status st = check_ptrs(x, codes, scales);
   if (st != MTL_OK) return st;
-  if (rows <= 0 || cols <= 0 || cols % 32 != 0) return MTL_E_SHAPE;
+  if (rows <= 0 || cols <= 0 || cols % 32 != 0 || rows > INT32_MAX || cols > INT32_MAX) return MTL_E_SHAPE;
   return hip_status(mxfp4_quantize(static_cast<const uint16_t*>(x), rows, cols, static_cast<uint8_t*>(codes),
                                    static_cast<uint8_t*>(scales), reinterpret_cast<hipStream_t>(stream)));
 }
@@ -559,7 +559,7 @@ mtl_status mtl_mxfp6_quantize(const void* x, int64_t rows, int64_t cols, void* c
                               mtl_stream_t stream) {
   mtl_status st = check_ptrs(x, codes, scales);
   if (st != MTL_OK) return st;
-  if (rows <= 0 || cols <= 0 || cols % 32 != 0) return MTL_E_SHAPE;
+  if (rows <= 0 || cols <= 0 || cols % 32 != 0 || rows > INT32_MAX || cols > INT32_MAX) return MTL_E_SHAPE;
   return hip_status(mxfp6_quantize(static_cast<const uint16_t*>(x), rows, cols, static_cast<uint8_t*>(codes),
                                    static_cast<uint8_t*>(scales), reinterpret_cast<hipStream_t>(stream)));
 }
