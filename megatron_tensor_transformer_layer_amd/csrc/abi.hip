@@ -380,8 +380,11 @@ static mtl_status cp_check(int32_t cp, int32_t rank, int64_t chunk, int32_t head
   if (rank < 0 || rank >= cp) return MTL_E_RANK;
   if (chunk <= 0 || chunk > INT32_MAX || chunk % 64 != 0 || heads <= 0 || (head_dim != 64 && head_dim != 128))
     return MTL_E_SHAPE;
-  // the kernels address a chunk's QKV through 32-bit buffer offsets
-  if ((chunk + 64) * 3 * heads * head_dim * 2 > (int64_t)UINT32_MAX) return MTL_E_SHAPE;
+  // the kernels address a chunk's QKV through 32-bit buffer offsets; the row
+  // width is bounded first so that the byte-range product cannot wrap
+  const int64_t row_bytes = (int64_t)3 * heads * head_dim * 2;
+  if (row_bytes > (int64_t)INT32_MAX) return MTL_E_SHAPE;
+  if (chunk + 64 > (int64_t)UINT32_MAX / row_bytes) return MTL_E_SHAPE;
   return MTL_OK;
 }
 

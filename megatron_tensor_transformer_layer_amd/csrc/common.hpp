@@ -1,6 +1,6 @@
 // Device-side building blocks shared by the gfx950 kernels: vector types,
-// bf16 packing, the MFMA wrappers, LDS tile swizzle and the 8x8 register
-// transpose used to turn mn-contiguous global tiles into k-contiguous LDS tiles.
+// bf16 packing, the MFMA wrappers, the attention tiles' LDS swizzle, the normal
+// CDF/density behind GeLU, transpose reads from LDS and the LDS DMA load.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -17,7 +17,6 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 // ---------------------------------------------------------------- bf16 <-> fp32
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
-__device__ __forceinline__ float bf16_to_f32(uint16_t h) { return __uint_as_float(((uint32_t)h) << 16); }
 
 // fp32 -> bf16, round to nearest even: gfx950's v_cvt_pk_bf16_f32 converts two
 // values per instruction (NaN stays NaN).
@@ -60,20 +59,6 @@ __device__ __forceinline__ uint32_t swz(uint32_t row, uint32_t chunk) {
   return row * 128u + ((chunk ^ (row & 7u)) << 4);
 }
 
-// ---------------------------------------------------------------- 8x8 transpose
-// in[r] holds 8 bf16 of row r (element e in dword e/2, low half for even e).
-// out[i] receives column i: element r of out[i] = in[r] element i.
-__device__ __forceinline__ void transpose8x8(const u32x4 (&in)[8], u32x4 (&out)[8]) {
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const uint32_t sel = (i & 1) ? 0x07060302u : 0x05040100u;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      out[i][j] = __builtin_amdgcn_perm(in[2 * j + 1][i >> 1], in[2 * j][i >> 1], sel);
-    }
-  }
-}
-
 // ---------------------------------------------------------------- GeLU
 // Exact-form GeLU z * Phi(z) and its derivative Phi(z) + z * phi(z).  The normal
 // CDF uses the rational approximation of erfc in Abramowitz & Stegun (1964),
@@ -89,16 +74,6 @@ __device__ __forceinline__ void normal_cdf_pdf(float z, float& cdf, float& pdf) 
   const float half_erfc = 0.5f * poly * e;
   cdf = z >= 0.f ? 1.0f - half_erfc : half_erfc;
   pdf = 0.39894228040143268f * e;
-}
-__device__ __forceinline__ float gelu_f(float z) {
-  float c, p;
-  normal_cdf_pdf(z, c, p);
-  return z * c;
-}
-__device__ __forceinline__ float gelu_grad_f(float z) {
-  float c, p;
-  normal_cdf_pdf(z, c, p);
-  return c + z * p;
 }
 
 // ---------------------------------------------------------------- LDS DMA

@@ -16,8 +16,23 @@
 namespace mtl {
 
 // ---------------------------------------------------------------- route
+// Selection order: larger logit first, ties to the lower expert id; -0 and +0
+// are equal, and NaN ranks below every number (-inf included), so a row with
+// NaN logits still yields k distinct valid ids.  The order is taken on an
+// integer key: NaN -> INT_MIN, otherwise the float's bits mapped monotonically
+// onto signed integers (zero of either sign -> 0).
+__device__ __forceinline__ int route_key(float f) {
+  if (f != f) return INT_MIN;
+  const int b = f == 0.f ? 0 : __float_as_int(f);
+  return b >= 0 ? b : b ^ 0x7fffffff;
+}
+__device__ __forceinline__ float route_value(int key) {
+  if (key == INT_MIN) return __int_as_float(0x7fc00000);
+  return __int_as_float(key >= 0 ? key : key ^ 0x7fffffff);
+}
+
 // One wave per token; lane l holds logits l, l+64, ... (E <= 1024).  Round r
-// of k picks the largest untaken logit (lowest id among equals) by a wave
+// of k picks the largest untaken key (lowest id among equals) by a wave
 // butterfly; lane r keeps it, so slot r's id and gate are written by lane r.
 __global__ __launch_bounds__(256) void moe_route_kernel(const float* __restrict__ logits, int T, int E, int k,
                                                         int32_t* __restrict__ idx, float* __restrict__ gates) {
@@ -26,18 +41,20 @@ __global__ __launch_bounds__(256) void moe_route_kernel(const float* __restrict_
   if (t >= T) return;
   const float* row = logits + t * E;
   constexpr int PER = 16;
-  float v[PER];
+  int v[PER];
   uint32_t taken = 0;
 #pragma unroll
   for (int j = 0; j < PER; ++j) {
     const int e = lane + 64 * j;
-    v[j] = e < E ? row[e] : -INFINITY;
+    v[j] = e < E ? route_key(row[e]) : INT_MIN;
     if (e >= E) taken |= 1u << j;
   }
   float mine_v = -INFINITY;
   int mine_i = 0;
   for (int r = 0; r < k; ++r) {
-    float bv = -INFINITY;
+    // (INT_MIN, past every id) loses to every untaken candidate, a NaN included;
+    // k <= E leaves at least one candidate per round
+    int bv = INT_MIN;
     int bi = 0x7fffffff;
 #pragma unroll
     for (int j = 0; j < PER; ++j) {
@@ -49,7 +66,7 @@ __global__ __launch_bounds__(256) void moe_route_kernel(const float* __restrict_
     }
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) {
-      const float ov = __shfl_xor(bv, off);
+      const int ov = __shfl_xor(bv, off);
       const int oi = __shfl_xor(bi, off);
       if (ov > bv || (ov == bv && oi < bi)) {
         bv = ov;
@@ -58,11 +75,12 @@ __global__ __launch_bounds__(256) void moe_route_kernel(const float* __restrict_
     }
     if ((bi & 63) == lane) taken |= 1u << (bi >> 6);
     if (lane == r) {
-      mine_v = bv;
+      mine_v = route_value(bv);
       mine_i = bi;
     }
   }
-  // softmax over the k selected logits; slot 0 holds the largest
+  // softmax over the k selected logits; slot 0 holds the largest (a NaN among
+  // them, or an all -inf selection, makes the gates NaN)
   const float top = __shfl(mine_v, 0);
   const float ex = lane < k ? expf(mine_v - top) : 0.f;
   float z = ex;

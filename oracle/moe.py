@@ -31,7 +31,13 @@ from . import layer as L
 def route_topk(logits, k: int):
     """Top-k expert ids per token (descending logit, ties -> lower id) and the
     softmax gates over the selected logits.  logits: [T, E] fp32.
-    Returns (idx int32 [T, k], gates fp64 [T, k])."""
+    Returns (idx int32 [T, k], gates fp64 [T, k]).
+
+    Non-finite logits follow the order of numpy's stable sort of the negated
+    row: +inf first, -inf below every finite value, NaN below -inf (ties among
+    NaNs and between -0 and +0 to the lower id).  A NaN among the selected
+    logits, or a selection of only infinities of one sign, makes that row's
+    gates NaN."""
     logits = np.asarray(logits)
     order = np.argsort(-logits, axis=1, kind="stable")[:, :k]
     sel = np.take_along_axis(logits, order, axis=1).astype(np.float64)

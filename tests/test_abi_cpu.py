@@ -235,6 +235,9 @@ def test_cp_attention_validation_before_any_launch(mtl):
     assert sb(4, 1, 256, 2, 96) == mtl.MTL_E_SHAPE  # head_dim 64 or 128
     assert sb(4, 1, 256, 0, 128) == mtl.MTL_E_SHAPE
     assert sb(4, 1, 1 << 22, 64, 128) == mtl.MTL_E_SHAPE  # past 32-bit buffer offsets
+    # (chunk + 64) * 3 * heads * head_dim * 2 = 3 * 2^69 wraps to 0 in 64 bits: still refused
+    assert sb(4, 1, (1 << 31) - 64, 1 << 30, 128) == mtl.MTL_E_SHAPE
+    assert sb(4, 1, 64, (1 << 31) - 1, 128) == mtl.MTL_E_SHAPE
     assert lib.mtl_cp_attn_scratch_bytes(4, 1, 256, 2, 128, None) == mtl.MTL_E_NULL
 
     chunks = (ctypes.c_void_p * 4)(P, P + 4096, None, None)  # only entries 0..rank are read

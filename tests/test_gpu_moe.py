@@ -136,3 +136,34 @@ def test_moe_wgrad_accumulates(mtl):
     # the same products added to themselves: exactly twice the single result
     assert np.array_equal(_host(twice.dw1), 2 * _host(once.dw1))
     assert np.array_equal(_host(twice.dw2), 2 * _host(once.dw2))
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("seed", [0, 1])
+def test_route_nonfinite_logits_bit_exact(mtl, seed):
+    """Rows holding NaN, +-inf and +-0 logits: the device picks the oracle's ids
+    bit for bit (NaN below -inf, ties to the lower id) and its gates are NaN
+    exactly where the oracle's are, equal to fp32 rounding elsewhere."""
+    import torch
+    from megatron_tensor_transformer_layer_amd import make_moe_cfg, mtl_moe_route
+    rng = np.random.default_rng(seed)
+    T, E, k = 300, 70, 8
+    pool = np.array([np.nan, -np.inf, np.inf, 0.0, -0.0, -1.0, 1.0, 2.5], dtype=np.float32)
+    logits = rng.standard_normal((T, E)).astype(np.float32)
+    mask = rng.random((T, E)) < 0.3
+    logits[mask] = pool[rng.integers(0, len(pool), size=int(mask.sum()))]
+    logits[0, :] = np.nan  # every logit NaN: ids 0..k-1
+    logits[1, :] = -np.inf
+    print(f"route nonfinite seed={seed} T={T} E={E} k={k}", flush=True)
+    cfg = make_moe_cfg(T, 64, 64, E, k)
+    idx = torch.empty(T, k, dtype=torch.int32, device="cuda")
+    gates = torch.empty(T, k, dtype=torch.float32, device="cuda")
+    mtl_moe_route(cfg, torch.from_numpy(logits).cuda(), idx, gates)
+    torch.cuda.synchronize()
+    ref_idx, ref_g = M.route_topk(logits, k)
+    got_idx, got_g = idx.cpu().numpy(), gates.cpu().numpy()
+    assert np.array_equal(got_idx, ref_idx)
+    assert got_idx[0].tolist() == list(range(k)) and got_idx[1].tolist() == list(range(k))
+    assert np.array_equal(np.isnan(got_g), np.isnan(ref_g))
+    fin = ~np.isnan(ref_g)
+    assert np.max(np.abs(got_g[fin] - ref_g[fin])) <= 1e-6

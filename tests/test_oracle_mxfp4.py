@@ -140,3 +140,17 @@ def test_e2m3_round_trip_and_pack6():
     # element j of a block at bits 6j..6j+5 of its 24 little-endian bytes
     v = int.from_bytes(bytes(p[1, 24:48]), "little")
     assert [(v >> (6 * j)) & 63 for j in range(32)] == codes[1, 32:64].tolist()
+
+
+def test_pack6_hand_worked_bytes():
+    """pack6 against bytes worked out by hand from the FP6 operand layout of the
+    block-scaled MFMA (code j in bits 6j..6j+5 of a lane's 6 dwords)."""
+    import json
+    import os
+    g = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "pack6.json")))
+    for case in g["cases"]:
+        codes = np.array([case["codes"]], dtype=np.uint8)
+        assert MX.pack6(codes)[0].tolist() == case["bytes"], case["note"]
+    # two blocks in one row: each packs on its own
+    both = np.array([g["cases"][0]["codes"] + g["cases"][1]["codes"]], dtype=np.uint8)
+    assert MX.pack6(both)[0].tolist() == g["cases"][0]["bytes"] + g["cases"][1]["bytes"]
