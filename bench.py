@@ -2,15 +2,25 @@
 
 A step is the rank's whole share of the layer's forward and backward pass:
 column-parallel QKV projection, causal attention over its heads, row-parallel
-output projection, the reduce share standing in for the all-reduce, column-parallel
-fc1 with GeLU, row-parallel fc2, reduce share; then the backward of all of it
-(dgrad and wgrad of every linear, bias gradients, attention backward) with its
-two reduce shares.  The reduce shares are the rank's reduce-scatter rows
-[rank*S/t, (rank+1)*S/t) over its own partial and t-1 resident peer partials.
+output projection, the all-reduce stand-in, column-parallel fc1 with GeLU,
+row-parallel fc2, all-reduce stand-in; then the backward of all of it (dgrad
+and wgrad of every linear, bias gradients, attention backward) with its two
+all-reduce stand-ins.  Each all-reduce stands in as its two halves on one GPU:
+the rank's reduce-scatter share (rows [rank*S/t, (rank+1)*S/t) summed over its
+own partial and t-1 resident peer partials) and the all-gather of the peers'
+t-1 reduced shares into its full buffer.
 
-Prints one JSON line.  Default workload: rank 0 of a 7B-class layer at TP=4
-(hidden 4096, 32 heads, ffn 16384, seq 4096, micro-batch 1, bf16).  With
---workload moe-256e-top8-ep16 the step is one expert-parallel rank's MoE
+Prints one JSON line.  Default workload: rank 0 of a 96-layer-GPT-shaped layer
+at TP=8 (hidden 8192, 64 heads, ffn 32768, seq 4096, micro-batch 1, bf16);
+--workload 7b-tp4 is rank 0 of a 7B-class layer at TP=4; --workload
+gpt2-small-tp2 is the whole GPT-2-small layer (both TP=2 shards and the four
+full reductions) replayed as one HIP graph.  Besides the K timed steps, the
+line carries a window of steps timed per launch group with HIP events inside
+the library (mtl_prof_*: the whole-step GEMM rate, the attention rate, the
+HBM rate of the memory-bound kernels) and three windows of at least 20 steps
+(each window's mean, the worst window, P50/P95 over their steps).
+
+With --workload moe-256e-top8-ep16 the step is one expert-parallel rank's MoE
 expert block instead (route, permute, grouped expert GEMMs, combine, backward);
 with --workload cp4-seq32k-7b-tp4 it is one context-parallel rank's causal
 attention share, forward and backward (by default the last of 4 ranks of a
@@ -40,7 +50,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=30)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="7b-tp4")
+    ap.add_argument("--workload", default="gpt96l-tp8")
     ap.add_argument("--rank", type=int, default=None,
                     help="the rank whose share runs (default 0; for a CP workload the last, busiest rank)")
     ap.add_argument("--precision", choices=("bf16", "fp8"), default="bf16",
@@ -62,7 +72,6 @@ def parse():
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 GEMM_SRC = os.path.join(HERE, "megatron_tensor_transformer_layer_amd", "csrc", "gemm.hip")
-TRAFFIC_FILE = os.path.join(HERE, "profiles", "gemm_bf16_mlp_fwd_7b-tp4_traffic.txt")
 COPY_BYTES = 64 << 20  # one 32 Mi-element bf16 tensor read and written
 
 
@@ -70,24 +79,6 @@ def gemm_source_hash() -> str:
     import hashlib
     with open(GEMM_SRC, "rb") as f:
         return hashlib.sha256(f.read()).hexdigest()[:16]
-
-
-def stored_traffic(workload: str):
-    """Counter-derived HBM bytes per GEMM launch, from the committed rocprofv3
-    summary; None when there is none or when gemm.hip has changed since."""
-    if not os.path.exists(TRAFFIC_FILE) or workload != "7b-tp4":
-        return None
-    fields = {}
-    for line in open(TRAFFIC_FILE):
-        if ":" in line and not line.startswith("#"):
-            k, v = line.split(":", 1)
-            fields[k.strip()] = v.strip()
-    if fields.get("gemm_source_sha256_16") != gemm_source_hash():
-        return None
-    try:
-        return float(fields["traffic_bytes_per_launch"])
-    except (KeyError, ValueError):
-        return None
 
 
 def calibrate_copy():
@@ -457,6 +448,30 @@ def mx_main(args):
     print(json.dumps(out), flush=True)
 
 
+def moe_group_rates(groups, n, h, f, el, tokens, k):
+    """Rates of the MoE launch groups from the rank's row count n (the library
+    records only their times): 2*n*h*f FLOP per grouped GEMM, and the bytes
+    each one must move -- its activations, its expert weights (bf16, read) or
+    weight gradients (fp32, written, for every local expert)."""
+    w = 2.0 * el * h * f  # one expert weight tensor of the rank, bf16
+    by = {"moe_gather": 2.0 * n * h * 2, "moe_combine": 2.0 * (n * h + tokens * h) + 4.0 * tokens * k,
+          "moe_combine_bwd": 2.0 * (tokens * h + 2 * n * h) + 4.0 * tokens * k * 2,
+          "moe_scatter": 2.0 * (n * h + tokens * h),
+          "moe_fc1_fwd": 2.0 * (n * h + 2 * n * f) + w, "moe_fc2_fwd": 2.0 * (n * f + n * h) + w,
+          "moe_fc2_dgrad": 2.0 * (n * h + 2 * n * f) + w, "moe_fc2_wgrad": 2.0 * (n * f + n * h) + 2 * w,
+          "moe_fc1_wgrad": 2.0 * (n * h + n * f) + 2 * w, "moe_fc1_dgrad": 2.0 * (n * f + n * h) + w}
+    out = {}
+    for name, v in groups.items():
+        us = v["ms"] * 1e3 / max(v["launches"], 1)
+        fl = 2.0 * n * h * f if v["kind"] == "gemm" else 0.0
+        b = by.get(name, 0.0)
+        out[name] = {"kind": v["kind"], "us": round(us, 1), "flop": fl,
+                     "tflops": round(fl / (us / 1e6) / 1e12, 1) if fl else None,
+                     "gb_per_s": round(b / (us / 1e6) / 1e9, 1), "frac_of_hbm_peak": round(b / (us / 1e6) / 1e9 /
+                                                                                         PEAK_HBM_GBS, 4)}
+    return out
+
+
 def moe_main(args):
     """One EP rank's MoE expert block: route, permute, grouped fc1+GeLU, fc2,
     combine, and the backward (combine', grouped dgrad and wgrad, dX scatter)."""
@@ -509,6 +524,8 @@ def moe_main(args):
     fl = moe_flops(counts, shape.hidden, shape.ffn)
     n = int(counts.sum())
     fwd_ms = float(np.mean([a.elapsed_time(b) for a, b in fwd_ev]))
+    groups, _ = prof_window(step, 2)
+    moe_groups = moe_group_rates(groups, n, shape.hidden, shape.ffn, El, shape.tokens, shape.topk)
     # mtl_moe_fwd = gather + two grouped GEMM launches (2*N*h*f FLOP each) + combine;
     # the per-launch rate below charges the gather and combine to the GEMMs
     gemm_launch_s = fwd_ms / 2 / 1e3
@@ -538,6 +555,11 @@ def moe_main(args):
                      "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
                      "gemm_launch_us": round(gemm_launch_s * 1e6, 2)},
+        "launch_groups": moe_groups,
+        "gemm_tflops": round(sum(v["flop"] for v in moe_groups.values()) /
+                             (sum(v["us"] for v in moe_groups.values() if v["kind"] == "gemm") / 1e6) / 1e12, 1),
+        "slowest_expert_rows": int(counts.max()),
+        "per_expert_rows": [int(c) for c in counts],
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:
@@ -545,41 +567,251 @@ def moe_main(args):
     print(json.dumps(out), flush=True)
 
 
-def main():
-    args = parse()
-    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU: the library has no multi-GPU path (collectives are replaced by an "
-              "on-device reduce); run with --gpus 1", file=sys.stderr)
-        sys.exit(2)
+def prof_window(run_step, n_steps):
+    """Run n_steps steps with the library's launch timing on (mtl_prof_*) and
+    return the per-step mean of each launch group, keyed by name, with its kind,
+    algorithmic FLOP and bytes, plus the per-step totals by kind."""
+    import torch
+    from megatron_tensor_transformer_layer_amd import mtl_prof_record, mtl_prof_start, mtl_prof_stop
+    torch.cuda.synchronize()
+    mtl_prof_start()
+    for _ in range(n_steps):
+        run_step()
+    n = mtl_prof_stop()
+    torch.cuda.synchronize()
+    groups, kinds = {}, {}
+    for i in range(n):
+        r = mtl_prof_record(i)
+        g = groups.setdefault(r["name"], dict(kind=r["kind"], flop=0.0, bytes=0.0, ms=0.0, launches=0))
+        g["flop"] += r["flop"]
+        g["bytes"] += r["bytes"]
+        g["ms"] += r["ms"]
+        g["launches"] += 1
+        k = kinds.setdefault(r["kind"], dict(flop=0.0, bytes=0.0, ms=0.0, launches=0))
+        for f in ("flop", "bytes", "ms"):
+            k[f] += r[f]
+        k["launches"] += 1
+    for d in list(groups.values()) + list(kinds.values()):
+        for f in ("flop", "bytes", "ms"):
+            d[f] /= n_steps
+        d["launches"] /= n_steps
+    return groups, kinds
 
-    if args.calibrate_copy:
-        calibrate_copy()
-        return
-    if args.copy_rate:
-        copy_rate()
-        return
+
+def windows(run_step, n_windows, per_window):
+    """n_windows windows of per_window steps, each step bracketed by HIP events:
+    the mean step time of each window and the P50/P95 over every step."""
+    import torch
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+    means, all_ms = [], []
+    for _ in range(n_windows):
+        marks = [(ev(), ev()) for _ in range(per_window)]
+        for a, b in marks:
+            a.record()
+            run_step()
+            b.record()
+        torch.cuda.synchronize()
+        ms = [a.elapsed_time(b) for a, b in marks]
+        means.append(float(np.mean(ms)))
+        all_ms += ms
+    return dict(n_windows=n_windows, steps_per_window=per_window,
+                window_mean_ms=[round(m, 4) for m in means], worst_window_ms=round(max(means), 4),
+                step_ms_p50=round(float(np.percentile(all_ms, 50)), 4),
+                step_ms_p95=round(float(np.percentile(all_ms, 95)), 4))
+
+
+def timed_steps(run_step, steps, warmup):
+    """W untimed steps, then exactly K steps between two synchronisations; the
+    mean wall-clock milliseconds per step."""
+    import torch
+    for _ in range(warmup):
+        run_step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        run_step()
+    torch.cuda.synchronize()
+    return (time.perf_counter() - t0) / steps * 1e3
+
+
+def breakdown(groups, kinds, peak):
+    """The graded GEMM number (sum of GEMM FLOP over the sum of GEMM launch
+    times), the rate of each launch group, and the HBM rate of the memory-bound
+    kinds."""
+    g = kinds.get("gemm", dict(flop=0.0, ms=0.0))
+    a = kinds.get("attention", dict(flop=0.0, ms=0.0))
+    out = {
+        "gemm_tflops": round(g["flop"] / (g["ms"] / 1e3) / 1e12, 1) if g["ms"] else None,
+        "gemm_frac_of_peak": round(g["flop"] / (g["ms"] / 1e3) / 1e12 / peak, 4) if g["ms"] else None,
+        "gemm_us_per_step": round(g["ms"] * 1e3, 1),
+        "attention_tflops": round(a["flop"] / (a["ms"] / 1e3) / 1e12, 1) if a["ms"] else None,
+        "attention_frac_of_bf16_peak": round(a["flop"] / (a["ms"] / 1e3) / 1e12 / PEAK_BF16_TFLOPS, 4)
+        if a["ms"] else None,
+        "attention_us_per_step": round(a["ms"] * 1e3, 1),
+        "memory_bound": {k: {"us_per_step": round(v["ms"] * 1e3, 1), "launch_groups": v["launches"],
+                             "gb_per_s": round(v["bytes"] / (v["ms"] / 1e3) / 1e9, 1),
+                             "frac_of_hbm_peak": round(v["bytes"] / (v["ms"] / 1e3) / 1e9 / PEAK_HBM_GBS, 4)}
+                         for k, v in kinds.items() if k not in ("gemm", "attention") and v["ms"] > 0},
+        "groups": {n: {"kind": v["kind"], "us": round(v["ms"] * 1e3 / max(v["launches"], 1), 1),
+                       "launches": v["launches"],
+                       **({"tflops": round(v["flop"] / (v["ms"] / 1e3) / 1e12, 1)} if v["flop"] else
+                          {"gb_per_s": round(v["bytes"] / (v["ms"] / 1e3) / 1e9, 1)})}
+                   for n, v in groups.items()},
+    }
+    return out
+
+
+# The kernel of each GEMM launch group on the 256x256 backward pairs, as the
+# profiler names it (for the roofline's rocprofv3 cross-check).
+GROUP_KERNEL = {
+    "fc2_bwd": "gemm_pair_kernel: fp32 wgrad dW2 = A^T dY (256x256 tiles) with dZ = (dY W2^T) * GeLU'(z) "
+               "(256x256 tiles), one launch",
+    "fc1_bwd": "gemm_pair_kernel: fp32 wgrad dW1 = H^T dZ (256x256 tiles) with dH = dZ W1^T (256x256 tiles), one "
+               "launch",
+    "qkv_bwd": "the QKV projection's wgrad and dgrad (one gemm_pair_kernel launch where both take 256x256 tiles)",
+    "fc1_fwd": "gemm_bf16_kernel<256,256> with the bias + GeLU epilogue (8 waves)",
+    "fc2_fwd": "gemm_bf16_kernel<256,256>, bf16 output",
+    "qkv_fwd": "gemm_bf16_kernel with the bias epilogue",
+    "proj_fwd": "gemm_bf16_kernel, bf16 output",
+    "proj_bwd": "the output projection's wgrad and dgrad",
+}
+
+
+def traffic_file(workload, group, precision):
+    return os.path.join(HERE, "profiles", f"gemm_{group}{'_fp8' if precision == 'fp8' else ''}_{workload}_traffic.txt")
+
+
+def stored_traffic(workload, group, precision):
+    """Counter-derived HBM bytes per launch of a GEMM launch group, from the
+    committed rocprofv3 summary; None when there is none or when gemm.hip has
+    changed since the counters were taken."""
+    path = traffic_file(workload, group, precision)
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    for line in open(path):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            fields[k.strip()] = v.strip()
+    if fields.get("gemm_source_sha256_16") != gemm_source_hash():
+        return None
+    try:
+        return float(fields["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_cores():
+    try:
+        from threadpoolctl import threadpool_info
+        return max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        return len(os.sched_getaffinity(0))
+
+
+def all_shards_cpu_baseline(shape):
+    """The oracle (fp64 numpy, as it stands) on the whole small layer: every
+    shard's forward and backward plus the four reductions."""
+    import synth
+    from oracle import layer as L
+    from oracle import shard as S
+    full = synth.layer_inputs(shape, seed=0)
+    p = {k: synth.bf16_bits_to_f64(full[k]) for k in ("w_qkv", "b_qkv", "w_o", "b_o", "w1", "b1", "w2", "b2")}
+    x, g = synth.bf16_bits_to_f64(full["x"]), synth.bf16_bits_to_f64(full["dy"])
+    reps = 0
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < 10.0:
+        S.sharded_layer(p, x, g, shape.heads, shape.tp)
+        reps += 1
+    dt = (time.perf_counter() - t0) / reps
+    fl = L.layer_flops(shape.hidden, shape.heads, shape.ffn, shape.seq, shape.micro_batch, 1)["total"]
+    return {"value": fl / dt / 1e12, "unit": "TFLOP/s", "cores": int(cpu_cores()), "kind": "oracle",
+            "sample": f"the whole layer as {shape.tp} shards plus the four reductions (fp64 numpy), {reps} runs, "
+                      f"{dt * 1e3:.1f} ms each"}
+
+
+def all_shards_main(args, shape):
+    """The whole small layer on one GPU: every TP shard's forward and backward
+    plus the four full reductions standing in for the all-reduces, timed as
+    one step.  At this size each launch is a few microseconds of work, so the
+    step is launch-bound; it is timed captured in a HIP graph (replayed K
+    times) and, for comparison, launched eagerly."""
     import torch
     import synth
-    from megatron_tensor_transformer_layer_amd import mtl_allgather_rows, mtl_reduce
-    from megatron_tensor_transformer_layer_amd.layer import RankState, bf16_dev, empty_bf16
+    from megatron_tensor_transformer_layer_amd.layer import AllShardsStep
+    from oracle.layer import layer_flops  # FLOP count only (closed form)
 
-    if not torch.cuda.is_available():
-        print("bench.py needs a GPU", file=sys.stderr)
-        sys.exit(2)
-    if args.workload in synth.MOE_WORKLOADS:
-        moe_main(args)
-        return
-    if args.workload in synth.CP_WORKLOADS:
-        cp_main(args)
-        return
-    if args.workload in synth.MX_WORKLOADS:
-        mx_main(args)
-        return
+    t = shape.tp
+    full = synth.layer_inputs(shape, seed=0)
+    shards = [synth.layer_inputs(shape, seed=0, tp=t, rank=r) for r in range(t)]
+    step = AllShardsStep(shape, t, shards, full["x"], full["dy"], full["b_o"], full["b2"])
+
+    eager_ms = timed_steps(step, args.steps, args.warmup)
+    groups, kinds = prof_window(step, 5)
+    # capture one step on a side stream (torch makes it current inside the context)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    torch.cuda.synchronize()
+    graph_ms = timed_steps(graph.replay, args.steps, args.warmup)
+    win = windows(graph.replay, 3, max(20, args.steps))
+    fl = layer_flops(shape.hidden, shape.heads, shape.ffn, shape.seq, shape.micro_batch, 1)
+    bd = breakdown(groups, kinds, PEAK_BF16_TFLOPS)
+    launches = sum(v["launches"] for v in kinds.values())
+    out = {
+        "metric": "TFLOP/s per TP-shard layer fwd+bwd (bf16) and % of MI355X MFMA peak",
+        "value": round(fl["total"] / (graph_ms / 1e3) / 1e12, 2), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(graph_ms, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) activations, N(0,0.02) weights)",
+        "config": {"workload": f"{args.workload}: the whole layer, all {t} TP shards and the four full reductions "
+                               f"on one GPU, hidden {shape.hidden}, heads {shape.heads}, ffn {shape.ffn}, "
+                               f"seq {shape.seq}, micro-batch {shape.micro_batch}; the step replayed as one HIP graph",
+                   "global_batch": shape.micro_batch, "seq_len": shape.seq,
+                   "parallelism": f"tp{t}-all-shards-1gpu"},
+        "pct_of_peak": round(100 * fl["total"] / (graph_ms / 1e3) / 1e12 / PEAK_BF16_TFLOPS, 2),
+        "flop_per_step": fl["total"],
+        "eager_ms_per_step": round(eager_ms, 4),
+        "graph_ms_per_step": round(graph_ms, 4),
+        "launch_groups_per_step": launches,
+        **win,
+        **{k: v for k, v in bd.items() if k != "groups"},
+        "roofline": {"bound": "mfma", "kernel": "every GEMM launch of the step (HIP events, eager launches)",
+                     "achieved": bd["gemm_tflops"], "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": bd["gemm_frac_of_peak"], "traffic": None},
+        "cpu_baseline": None if args.no_cpu_baseline else all_shards_cpu_baseline(shape),
+    }
+    print(json.dumps(out), flush=True)
+
+
+def dense_main(args):
+    """One TP rank's layer step (the rank's shard plus its share of the four
+    all-reduces), forward and backward.  Each all-reduce stands in as its two
+    halves on one GPU: the rank's reduce-scatter share (its S/t rows summed
+    over its own and t-1 resident peer partials) and the all-gather of the
+    other t-1 reduced shares into the rank's full buffer (mtl_allgather_rows
+    over resident peer buffers).  With --sp (sequence parallelism) the gathers
+    move to the inputs of the column-parallel linears (X, H, dY, dH) and Y, dX
+    stay row-sharded: four reduce-scatters and four gathers either way."""
+    import torch
+    import synth
+    from megatron_tensor_transformer_layer_amd import (MTL_PREC_BF16, MTL_PREC_FP8_HYBRID, mtl_allgather_rows,
+                                                       mtl_reduce)
+    from megatron_tensor_transformer_layer_amd.layer import RankState, bf16_dev, empty_bf16
+    from oracle.layer import layer_flops  # FLOP count only (closed form)
+
     shape = synth.WORKLOADS[args.workload]
     t, r = shape.tp, args.rank or 0
+    if t > 1 and shape.seq * shape.micro_batch % t:
+        raise SystemExit("the reduce-scatter shares need S % t == 0")
     inp = synth.layer_inputs(shape, tp=t, rank=r)
     fp8 = args.precision == "fp8"
-    from megatron_tensor_transformer_layer_amd import MTL_PREC_BF16, MTL_PREC_FP8_HYBRID
     st = RankState(shape, t, r, inp, precision=MTL_PREC_FP8_HYBRID if fp8 else MTL_PREC_BF16)
     D = st.D
     x = bf16_dev(inp["x"])
@@ -587,85 +819,47 @@ def main():
     b_o = bf16_dev(inp["b_o"])
     b2 = bf16_dev(inp["b2"])
     g = torch.Generator(device="cuda").manual_seed(1234)
+    rnd = lambda: torch.randn(D.S, D.h, device="cuda", generator=g).to(torch.bfloat16)
     # partial sums the other t-1 ranks would contribute to this rank's reduce-scatter share
-    peers = {k: [torch.randn(D.S, D.h, device="cuda", generator=g).to(torch.bfloat16) for _ in range(t - 1)]
-             for k in ("attn", "mlp", "dh", "dx")}
-    h = empty_bf16(D.S, D.h)
-    y = empty_bf16(D.S, D.h)
-    dh = empty_bf16(D.S, D.h)
-    dx = empty_bf16(D.S, D.h)
+    peers = {k: [rnd() for _ in range(t - 1)] for k in ("attn", "mlp", "dh", "dx")}
+    # the peers' full-size buffers whose own (reduced or input) shares the gathers copy
+    gat = ("x", "h", "dy", "dh") if args.sp else ("h", "y", "dh", "dx")
+    gpeers = {k: [rnd() for _ in range(t - 1)] for k in gat}
+    h, y, dh, dx = (empty_bf16(D.S, D.h) for _ in range(4))
     r0, r1 = r * D.S // t, (r + 1) * D.S // t
-    # sequence parallel: the peers' full-size buffers of X, H, dY, dH, whose own
-    # shares this rank's in-place all-gathers copy (resident copies on one GPU)
-    sp_peers = {k: [torch.randn(D.S, D.h, device="cuda", generator=g).to(torch.bfloat16) for _ in range(t - 1)]
-                for k in ("x", "h", "dy", "dh")} if args.sp else None
 
     def gather(key, buf):
-        if args.sp:
-            bufs = sp_peers[key][:r] + [buf] + sp_peers[key][r:]
-            mtl_allgather_rows(bufs, buf, D.S, D.h, r)
+        if key in gat and t > 1:
+            mtl_allgather_rows(gpeers[key][:r] + [buf] + gpeers[key][r:], buf, D.S, D.h, r)
 
-    # rows of H / dH outside this rank's share come from the all-gather; fill them once
-    st.attn_fwd(x)
-    mtl_reduce([st.p_attn] + peers["attn"], b_o, None, h, D.S, D.h)
-    st.mlp_fwd(h)
-    st.mlp_bwd(dy, h)
-    mtl_reduce([st.p_dh] + peers["dh"], None, None, dh, D.S, D.h)
-    torch.cuda.synchronize()
-
-    ev = lambda: torch.cuda.Event(enable_timing=True)
-    mlp_ev = []
-
-    def step(record=False):
+    def step():
         gather("x", x)
         st.attn_fwd(x)
         mtl_reduce([st.p_attn] + peers["attn"], b_o, None, h, D.S, D.h, r0, r1)
         gather("h", h)
-        if record:
-            e0, e1 = ev(), ev()
-            e0.record()
         st.mlp_fwd(h)
-        if record:
-            e1.record()
-            mlp_ev.append((e0, e1))
         mtl_reduce([st.p_mlp] + peers["mlp"], b2, None, y, D.S, D.h, r0, r1)
+        gather("y", y)
         gather("dy", dy)
         st.mlp_bwd(dy, h)
         mtl_reduce([st.p_dh] + peers["dh"], None, None, dh, D.S, D.h, r0, r1)
         gather("dh", dh)
         st.attn_bwd(dh, x)
         mtl_reduce([st.p_dx] + peers["dx"], None, None, dx, D.S, D.h, r0, r1)
+        gather("dx", dx)
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    step_ev = [(ev(), ev()) for _ in range(args.steps)]
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        step_ev[i][0].record()
-        step(record=True)
-        step_ev[i][1].record()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
+    ms = timed_steps(step, args.steps, args.warmup)
+    groups, kinds = prof_window(step, 5)
+    win = windows(step, 3, max(20, args.steps))
 
-    from oracle.layer import layer_flops  # FLOP count only (closed form)
     fl = layer_flops(shape.hidden, shape.heads, shape.ffn, shape.seq, shape.micro_batch, t)
-    ms = wall / args.steps * 1e3
-    per_step = np.array([a.elapsed_time(b) for a, b in step_ev])
-    mlp_ms = np.array([a.elapsed_time(b) for a, b in mlp_ev])
-    # dominant kernel: the MFMA GEMM; in bf16 mtl_mlp_fwd is exactly two GEMM launches
-    # of shape S x f/t x h and S x h x f/t (2*S*h*f/t FLOP each); in fp8 it also
-    # holds the amax + cast of its four operands, charged here to the GEMMs
-    gemm_flop = 2.0 * D.S * D.h * D.f_l
-    gemm_launch_s = float(np.mean(mlp_ms)) / 2 / 1e3
-    achieved = gemm_flop / gemm_launch_s / 1e12
     peak = PEAK_FP8_TFLOPS if fp8 else PEAK_BF16_TFLOPS
-    kernel = ("gemm_bf16_kernel, 256x256 tiles: the two launches of mtl_mlp_fwd (fc1 + bias + GeLU, fc2), "
-              "%d x %d x %d each" % (D.S, D.f_l, D.h))
-    if fp8:
-        kernel = ("gemm_bf16_kernel fp8 variant (E4M3 x E4M3, v_mfma_f32_32x32x64_f8f6f4), 256x256 tiles: the two "
-                  "GEMMs of mtl_mlp_fwd, %d x %d x %d each, with its four amax+cast passes included"
-                  % (D.S, D.f_l, D.h))
+    bd = breakdown(groups, kinds, peak)
+    # the roofline kernel: the GEMM launch group that takes the most time per step
+    dom = max((n for n, v in groups.items() if v["kind"] == "gemm"), key=lambda n: groups[n]["ms"])
+    dg = groups[dom]
+    per_launch_ms = dg["ms"] / dg["launches"]
+    achieved = dg["flop"] / dg["launches"] / (per_launch_ms / 1e3) / 1e12
     out = {
         "metric": ("TFLOP/s per TP-shard layer fwd+bwd (fp8 hybrid GEMMs) and % of MI355X MFMA peak" if fp8 else
                    "TFLOP/s per TP-shard layer fwd+bwd (bf16) and % of MI355X MFMA peak"),
@@ -686,24 +880,67 @@ def main():
                                + (", fp8 hybrid (E4M3 activations/weights, E5M2 gradients, per-tensor current "
                                   "scaling; attention bf16)" if fp8 else "")
                                + (", sequence parallel (reduce-scatter shares, in-place all-gathers of X, H, dY, dH)"
-                                  if args.sp else ""),
+                                  if args.sp else ", each all-reduce as the rank's reduce-scatter share plus the "
+                                                  "all-gather of the peers' shares"),
                    "global_batch": shape.micro_batch, "seq_len": shape.seq,
                    "parallelism": f"tp{t}{'-sp' if args.sp else ''}-rank{r}-of-1gpu"},
         "pct_of_peak": round(100 * fl["total"] / (ms / 1e3) / 1e12 / peak, 2),
         "pct_of_bf16_peak": round(100 * fl["total"] / (ms / 1e3) / 1e12 / PEAK_BF16_TFLOPS, 2),
-        "step_ms_p50": round(float(np.percentile(per_step, 50)), 4),
-        "step_ms_p95": round(float(np.percentile(per_step, 95)), 4),
         "flop_per_step": fl["total"],
-        "roofline": {"bound": "mfma", "kernel": kernel,
+        **win,
+        **{k: v for k, v in bd.items() if k != "groups"},
+        "launch_groups": bd["groups"],
+        "roofline": {"bound": "mfma", "kernel": f"{dom}: {GROUP_KERNEL.get(dom, dom)}",
                      "achieved": round(achieved, 1), "peak": peak, "unit": "TFLOP/s",
                      "frac": round(achieved / peak, 4),
-                     "traffic": None if fp8 else stored_traffic(args.workload),
-                     "gemm_launch_us": round(gemm_launch_s * 1e6, 2)},
+                     "traffic": stored_traffic(args.workload, dom, args.precision),
+                     "flop_per_launch": dg["flop"] / dg["launches"],
+                     "launch_us": round(per_launch_ms * 1e3, 2)},
         "cpu_baseline": None,
     }
+    if fp8:
+        q = kinds.get("quantize", dict(ms=0.0))
+        out["quantize_us_per_step"] = round(q["ms"] * 1e3, 1)
+        g8 = kinds.get("gemm")
+        out["gemm_frac_of_bf16_peak"] = round(g8["flop"] / (g8["ms"] / 1e3) / 1e12 / PEAK_BF16_TFLOPS, 4)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(shape, r, min(args.cpu_sample_seq, shape.seq), fp8)
     print(json.dumps(out), flush=True)
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: the library has no multi-GPU path (collectives are replaced by an "
+              "on-device reduce); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    if args.calibrate_copy:
+        calibrate_copy()
+        return
+    if args.copy_rate:
+        copy_rate()
+        return
+    import torch
+    import synth
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    if args.workload in synth.MOE_WORKLOADS:
+        moe_main(args)
+        return
+    if args.workload in synth.CP_WORKLOADS:
+        cp_main(args)
+        return
+    if args.workload in synth.MX_WORKLOADS:
+        mx_main(args)
+        return
+    shape = synth.WORKLOADS[args.workload]
+    if args.workload == "gpt2-small-tp2":
+        all_shards_main(args, shape)
+        return
+    dense_main(args)
 
 
 if __name__ == "__main__":

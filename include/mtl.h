@@ -421,6 +421,39 @@ mtl_status mtl_moe_bwd(const mtl_moe_cfg* cfg, const void* dy, const int32_t* of
                        float* dw1, float* dw2, float* dgates, void* scratch, size_t scratch_bytes,
                        mtl_stream_t stream);
 
+/* ---------------------------------------------------------------- launch timing
+ * Measurement aid, not part of the layer's arithmetic.  The guide's section on
+ * performance reports asks for per-step timings that separate the parts of a
+ * step; these calls give them per launch group.  Between mtl_prof_start and
+ * mtl_prof_stop every group of launches the dense-layer entry points make
+ * (mtl_attn_fwd, mtl_mlp_fwd, mtl_mlp_bwd, mtl_attn_bwd, mtl_reduce,
+ * mtl_allgather_rows) and the MoE expert calls (mtl_moe_fwd, mtl_moe_bwd) is
+ * bracketed by two HIP events recorded on its stream, and kept, in launch
+ * order, with its kind (MTL_PROF_*), a static name and its algorithmic FLOP
+ * (2MNK per GEMM, the causal triangle for attention) and HBM bytes (every
+ * element read and written once; the fp8 quantisation reads its input twice,
+ * once for the amax and once for the cast).  The MoE groups carry 0 FLOP and
+ * 0 bytes: their row counts live on the device.  A group is one GEMM or GEMM
+ * pair, the attention kernels of one call, one reduce, one gather, one
+ * column-sum pair or one fp8 quantisation pair.  At most MTL_PROF_MAX groups are
+ * kept; later ones run untimed.
+ *
+ * mtl_prof_start: on the current device; the first call (and a call on another
+ * device) creates the 2 * MTL_PROF_MAX events, later calls reuse them.  Clears
+ * the table.  MTL_E_HIP if there is no device.
+ * mtl_prof_stop: stops recording; *n_records = number of groups kept.
+ * mtl_prof_record: group i (0 <= i < n_records) after mtl_prof_stop; waits for
+ * its stop event and returns the elapsed milliseconds between its two events.
+ * MTL_E_SHAPE for i out of range, MTL_E_UNSUPPORTED while recording.
+ * Process-wide state: not for concurrent use from several threads, and not
+ * while a stream is being captured into a graph. */
+#define MTL_PROF_MAX 2048
+enum { MTL_PROF_GEMM = 0, MTL_PROF_ATTN = 1, MTL_PROF_REDUCE = 2, MTL_PROF_COLSUM = 3, MTL_PROF_QUANT = 4,
+       MTL_PROF_GATHER = 5 };
+mtl_status mtl_prof_start(void);
+mtl_status mtl_prof_stop(int32_t* n_records);
+mtl_status mtl_prof_record(int32_t i, int32_t* kind, double* flop, double* bytes, float* ms, const char** name);
+
 #ifdef __cplusplus
 }
 #endif

@@ -23,6 +23,8 @@ MTL_FP8_E4M3, MTL_FP8_E5M2 = 0, 1
 MTL_FP8_AMAX_SCRATCH = 4096
 MTL_CP_MAX = 64
 MTL_F_RESIDUAL, MTL_F_WGRAD_ACCUM = 1, 2
+MTL_PROF_MAX = 2048
+MTL_PROF_KINDS = ("gemm", "attention", "reduce", "colsum", "quantize", "gather")
 
 
 class MtlError(RuntimeError):
@@ -77,6 +79,11 @@ _SIGS = {
     "mtl_moe_permute": (ctypes.c_int, [_MCFG, _P, _P, _P, _P, _P, _P, _P]),
     "mtl_moe_fwd": (ctypes.c_int, [_MCFG] + [_P] * 13),
     "mtl_moe_bwd": (ctypes.c_int, [_MCFG] + [_P] * 17 + [_SZ, _P]),
+    "mtl_prof_start": (ctypes.c_int, []),
+    "mtl_prof_stop": (ctypes.c_int, [ctypes.POINTER(_I32)]),
+    "mtl_prof_record": (ctypes.c_int, [_I32, ctypes.POINTER(_I32), ctypes.POINTER(ctypes.c_double),
+                                       ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_float),
+                                       ctypes.POINTER(ctypes.c_char_p)]),
 }
 
 _lib = None
@@ -308,3 +315,24 @@ def mtl_fp8_cast(x, rows, cols, fmt, rec, out, out_t=None, stream=None):
 def mtl_fp8_quantize(x, rows, cols, fmt, rec, out, out_t, scratch, scratch_bytes=None, stream=None):
     _check(lib().mtl_fp8_quantize(_ptr(x), rows, cols, fmt, _ptr(rec), _ptr(out), _ptr(out_t), _ptr(scratch),
                                   _nbytes(scratch, scratch_bytes), _stream(stream)), "mtl_fp8_quantize")
+
+
+def mtl_prof_start():
+    _check(lib().mtl_prof_start(), "mtl_prof_start")
+
+
+def mtl_prof_stop() -> int:
+    n = _I32(0)
+    _check(lib().mtl_prof_stop(ctypes.byref(n)), "mtl_prof_stop")
+    return n.value
+
+
+def mtl_prof_record(i: int) -> dict:
+    """Launch group i of the last recording: kind, name, algorithmic flop and
+    bytes, and the milliseconds between its two HIP events."""
+    kind, flop, nbytes, ms, name = _I32(0), ctypes.c_double(0), ctypes.c_double(0), ctypes.c_float(0), \
+        ctypes.c_char_p()
+    _check(lib().mtl_prof_record(i, ctypes.byref(kind), ctypes.byref(flop), ctypes.byref(nbytes), ctypes.byref(ms),
+                                 ctypes.byref(name)), "mtl_prof_record")
+    return dict(kind=MTL_PROF_KINDS[kind.value], name=name.value.decode(), flop=flop.value, bytes=nbytes.value,
+                ms=ms.value)

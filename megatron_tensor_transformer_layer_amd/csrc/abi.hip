@@ -8,6 +8,7 @@
 #include <initializer_list>
 
 #include "kernels.hpp"
+#include "prof.hpp"
 
 using namespace mtl;
 
@@ -30,6 +31,19 @@ Dims dims_of(const mtl_layer_cfg* c) {
   d.qkv_l = 3 * d.heads_l * d.d;
   d.o_l = d.heads_l * d.d;
   return d;
+}
+
+// Algorithmic FLOP and bytes of the launch groups, for the launch timing
+// (prof.hpp): 2*M*N*K per GEMM, every operand element read once and every
+// output element written once.
+inline double gemm_flop(int64_t M, int64_t N, int64_t K) { return 2.0 * M * N * K; }
+inline double gemm_bytes(int64_t M, int64_t N, int64_t K, int in_b, int out_b) {
+  return (double)in_b * ((double)M * K + (double)K * N) + (double)out_b * M * N;
+}
+// causal attention forward: QK^T and PV over the seq*(seq+1)/2 visible pairs
+// of every local head and micro-batch element; the backward counts twice that
+inline double attn_flop(const mtl_layer_cfg* c, int64_t heads_l, int64_t d) {
+  return 4.0 * c->micro_batch * ((double)c->seq * (c->seq + 1) / 2) * d * heads_l;
 }
 
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -108,12 +122,14 @@ struct QIn {
 hipError_t quantize(std::initializer_list<QIn> in, void* amax_ws, hipStream_t s) {
   QuantJob jobs[3];
   int n = 0;
+  double bytes = 0;  // the amax pass and the cast each read the tensor; one byte per code written
   for (const QIn& e : in) {
     if (n == 3) return hipErrorInvalidValue;
     jobs[n++] = QuantJob{static_cast<const uint16_t*>(e.x), e.q->rows, e.q->cols, e.q->fmt, e.q->rec, e.q->q,
                          e.q->qt};
+    bytes += (double)e.q->rows * e.q->cols * (4 + (e.q->q ? 1 : 0) + (e.q->qt ? 1 : 0));
   }
-  return fp8_quantize_n(jobs, n, amax_ws, s);
+  return prof::timed(prof::QUANT, "fp8_quantize", 0, bytes, s, [&] { return fp8_quantize_n(jobs, n, amax_ws, s); });
 }
 
 // fp8 GEMM C[M, N] = A . B^T over K, both operands k-contiguous codes.
@@ -139,10 +155,31 @@ GemmArgs gemm8_args(const Q8& a, const uint8_t* a_codes, const Q8& b, const uint
   g.scale_b = b.rec + 2;
   return g;
 }
-hipError_t gemm8(const Q8& a, const uint8_t* a_codes, const Q8& b, const uint8_t* b_codes, int64_t M, int64_t N,
-                 int64_t K, void* c, int64_t ldc, int epi, hipStream_t s, const void* bias = nullptr,
-                 void* c2 = nullptr, const void* aux = nullptr) {
-  return gemm_fp8(gemm8_args(a, a_codes, b, b_codes, M, N, K, c, ldc, bias, c2, aux), a.fmt, b.fmt, epi, s);
+hipError_t gemm8(const char* name, const Q8& a, const uint8_t* a_codes, const Q8& b, const uint8_t* b_codes,
+                 int64_t M, int64_t N, int64_t K, void* c, int64_t ldc, int epi, hipStream_t s,
+                 const void* bias = nullptr, void* c2 = nullptr, const void* aux = nullptr) {
+  const int out_b = (epi == EPI_F32 || epi == EPI_F32_ACC) ? 4 : (epi == EPI_BIAS_GELU ? 4 : 2);
+  return prof::timed(prof::GEMM, name, gemm_flop(M, N, K), gemm_bytes(M, N, K, 1, out_b), s, [&] {
+    return gemm_fp8(gemm8_args(a, a_codes, b, b_codes, M, N, K, c, ldc, bias, c2, aux), a.fmt, b.fmt, epi, s);
+  });
+}
+// A timed bf16 GEMM (2-byte operands; out_b bytes per output element).
+hipError_t gemm16(const char* name, const GemmArgs& g, GemmLayout l, int epi, int out_b, hipStream_t s) {
+  return prof::timed(prof::GEMM, name, gemm_flop(g.M, g.N, g.K), gemm_bytes(g.M, g.N, g.K, 2, out_b), s,
+                     [&] { return gemm_bf16(g, l, epi, s); });
+}
+// A timed pair of independent bf16 GEMMs (one launch where a fused kernel exists).
+hipError_t gemm16_pair(const char* name, const GemmArgs& g1, GemmLayout l1, int e1, int ob1, const GemmArgs& g2,
+                       GemmLayout l2, int e2, int ob2, hipStream_t s) {
+  return prof::timed(prof::GEMM, name, gemm_flop(g1.M, g1.N, g1.K) + gemm_flop(g2.M, g2.N, g2.K),
+                     gemm_bytes(g1.M, g1.N, g1.K, 2, ob1) + gemm_bytes(g2.M, g2.N, g2.K, 2, ob2), s,
+                     [&] { return gemm_bf16_pair(g1, l1, e1, g2, l2, e2, s); });
+}
+// A timed fp8 wgrad/dgrad pair.
+hipError_t gemm8_pair(const char* name, const GemmArgs& gw, int ew, const GemmArgs& gd, int ed, hipStream_t s) {
+  return prof::timed(prof::GEMM, name, gemm_flop(gw.M, gw.N, gw.K) + gemm_flop(gd.M, gd.N, gd.K),
+                     gemm_bytes(gw.M, gw.N, gw.K, 1, 4) + gemm_bytes(gd.M, gd.N, gd.K, 1, 2), s,
+                     [&] { return gemm_fp8_pair(gw, ew, gd, ed, s); });
 }
 
 struct MlpScratch {
@@ -308,11 +345,12 @@ mtl_status mtl_attn_fwd(const mtl_layer_cfg* c, const void* x, const void* w_qkv
   // qkv = x . w_qkv + b_qkv
   if (is_fp8(c)) {
     MTL_TRY(quantize({{x, &ws.x}, {w_qkv, &ws.wqkv_t}, {w_o, &ws.wo_t}}, ws.amax_ws, s));
-    MTL_TRY(gemm8(ws.x, ws.x.q, ws.wqkv_t, ws.wqkv_t.qt, d.S, d.qkv_l, d.h, qkv, d.qkv_l, EPI_BF16_BIAS, s, b_qkv));
+    MTL_TRY(gemm8("qkv_fwd", ws.x, ws.x.q, ws.wqkv_t, ws.wqkv_t.qt, d.S, d.qkv_l, d.h, qkv, d.qkv_l, EPI_BF16_BIAS,
+                  s, b_qkv));
   } else {
     GemmArgs g = gemm(x, d.h, w_qkv, d.qkv_l, d.S, d.qkv_l, d.h, qkv, d.qkv_l);
     g.bias = static_cast<const uint16_t*>(b_qkv);
-    MTL_TRY(gemm_bf16(g, GEMM_FWD, EPI_BF16_BIAS, s));
+    MTL_TRY(gemm16("qkv_fwd", g, GEMM_FWD, EPI_BF16_BIAS, 2, s));
   }
 
   AttnArgs a{};
@@ -326,15 +364,16 @@ mtl_status mtl_attn_fwd(const mtl_layer_cfg* c, const void* x, const void* w_qkv
   a.heads = (int)d.heads_l;
   a.d = (int)d.d;
   a.scale = 1.0f / sqrtf((float)d.d);
-  MTL_TRY(attention_fwd(a, s));
+  MTL_TRY(prof::timed(prof::ATTN, "attn_fwd", attn_flop(c, d.heads_l, d.d),
+                      2.0 * d.S * (d.qkv_l + d.o_l) + 4.0 * d.S * d.heads_l, s, [&] { return attention_fwd(a, s); }));
 
   // partial = o . w_o
   if (is_fp8(c)) {
     MTL_TRY(quantize({{o, &ws.o}}, ws.amax_ws, s));
-    MTL_TRY(gemm8(ws.o, ws.o.q, ws.wo_t, ws.wo_t.qt, d.S, d.h, d.o_l, partial, d.h, EPI_BF16, s));
+    MTL_TRY(gemm8("proj_fwd", ws.o, ws.o.q, ws.wo_t, ws.wo_t.qt, d.S, d.h, d.o_l, partial, d.h, EPI_BF16, s));
   } else {
     GemmArgs g = gemm(o, d.o_l, w_o, d.h, d.S, d.h, d.o_l, partial, d.h);
-    MTL_TRY(gemm_bf16(g, GEMM_FWD, EPI_BF16, s));
+    MTL_TRY(gemm16("proj_fwd", g, GEMM_FWD, EPI_BF16, 2, s));
   }
   return MTL_OK;
 }
@@ -352,9 +391,13 @@ mtl_status mtl_reduce(int32_t t, const void* const* partials, const void* bias, 
   if (!aligned16(out) || (bias && !aligned16(bias)) || (residual && !aligned16(residual))) return MTL_E_ALIGN;
   const uint16_t* p[16];
   for (int i = 0; i < t; ++i) p[i] = static_cast<const uint16_t*>(partials[i]);
-  return hip_status(reduce_partials(t, p, static_cast<const uint16_t*>(bias), static_cast<const uint16_t*>(residual),
-                                    static_cast<uint16_t*>(out), cols, row_begin, row_end,
-                                    reinterpret_cast<hipStream_t>(stream)));
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const double n = (double)(row_end - row_begin) * cols;
+  const double bytes = 2.0 * n * (t + 1 + (residual ? 1 : 0)) + (bias ? 2.0 * cols : 0.0);
+  return hip_status(prof::timed(prof::REDUCE, "reduce", 0, bytes, s, [&] {
+    return reduce_partials(t, p, static_cast<const uint16_t*>(bias), static_cast<const uint16_t*>(residual),
+                           static_cast<uint16_t*>(out), cols, row_begin, row_end, s);
+  }));
 }
 
 mtl_status mtl_allgather_rows(int32_t t, int32_t rank, const void* const* bufs, void* out, int64_t rows, int64_t cols,
@@ -371,8 +414,11 @@ mtl_status mtl_allgather_rows(int32_t t, int32_t rank, const void* const* bufs, 
     if (bufs[i] == out) return MTL_E_UNSUPPORTED;
     p[i] = static_cast<const uint16_t*>(bufs[i]);
   }
-  return hip_status(allgather_rows(t, rank, p, static_cast<uint16_t*>(out), rows, cols,
-                                   reinterpret_cast<hipStream_t>(stream)));
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const double bytes = 2.0 * 2.0 * (double)(rows - rows / t) * cols;  // t-1 shares read and written
+  return hip_status(prof::timed(prof::GATHER, "allgather", 0, bytes, s, [&] {
+    return allgather_rows(t, rank, p, static_cast<uint16_t*>(out), rows, cols, s);
+  }));
 }
 
 static mtl_status cp_check(int32_t cp, int32_t rank, int64_t chunk, int32_t heads, int32_t head_dim) {
@@ -602,19 +648,20 @@ mtl_status mtl_mlp_fwd(const mtl_layer_cfg* c, const void* h, const void* w1, co
   if (is_fp8(c)) {
     // z = h . w1 + b1: gz = GeLU'(z), a = GeLU(z); partial = a . w2 (a re-quantised from bf16)
     MTL_TRY(quantize({{h, &ws.h}, {w1, &ws.w1_t}, {w2, &ws.w2_t}}, ws.amax_ws, s));
-    MTL_TRY(gemm8(ws.h, ws.h.q, ws.w1_t, ws.w1_t.qt, d.S, d.f_l, d.h, gz, d.f_l, EPI_BIAS_GELU, s, b1, a));
+    MTL_TRY(gemm8("fc1_fwd", ws.h, ws.h.q, ws.w1_t, ws.w1_t.qt, d.S, d.f_l, d.h, gz, d.f_l, EPI_BIAS_GELU, s, b1,
+                  a));
     MTL_TRY(quantize({{a, &ws.a}}, ws.amax_ws, s));
-    MTL_TRY(gemm8(ws.a, ws.a.q, ws.w2_t, ws.w2_t.qt, d.S, d.h, d.f_l, partial, d.h, EPI_BF16, s));
+    MTL_TRY(gemm8("fc2_fwd", ws.a, ws.a.q, ws.w2_t, ws.w2_t.qt, d.S, d.h, d.f_l, partial, d.h, EPI_BF16, s));
     return MTL_OK;
   }
   GemmArgs g = gemm(h, d.h, w1, d.f_l, d.S, d.f_l, d.h, gz, d.f_l);
   g.bias = static_cast<const uint16_t*>(b1);
   g.c2 = a;
   g.ldc2 = d.f_l;
-  MTL_TRY(gemm_bf16(g, GEMM_FWD, EPI_BIAS_GELU, s));
+  MTL_TRY(gemm16("fc1_fwd", g, GEMM_FWD, EPI_BIAS_GELU, 4, s));  // two bf16 outputs: GeLU'(z) and GeLU(z)
 
   g = gemm(a, d.f_l, w2, d.h, d.S, d.h, d.f_l, partial, d.h);
-  MTL_TRY(gemm_bf16(g, GEMM_FWD, EPI_BF16, s));
+  MTL_TRY(gemm16("fc2_fwd", g, GEMM_FWD, EPI_BF16, 2, s));
   return MTL_OK;
 }
 
@@ -622,14 +669,18 @@ mtl_status mtl_mlp_fwd(const mtl_layer_cfg* c, const void* h, const void* w1, co
 static hipError_t mlp_bias_grads(const Dims& d, const MlpScratch& ws, const void* dy, float* db1, float* db2,
                                  bool accum, hipStream_t s) {
   const ColsumJob jobs[2] = {{ws.dz, d.f_l, db1}, {static_cast<const uint16_t*>(dy), d.h, db2}};
-  return colsum_bf16(jobs, db2 ? 2 : 1, d.S, accum, ws.ws, s);
+  const double bytes = 2.0 * d.S * (d.f_l + (db2 ? d.h : 0)) + 4.0 * (d.f_l + (db2 ? d.h : 0));
+  return prof::timed(prof::COLSUM, "colsum_mlp", 0, bytes, s,
+                     [&] { return colsum_bf16(jobs, db2 ? 2 : 1, d.S, accum, ws.ws, s); });
 }
 
 // db_qkv = colsum(dqkv) and, when wanted, db_o = colsum(dh): one pair of launches.
 static hipError_t attn_bias_grads(const Dims& d, const AttnScratch& ws, const void* dh, float* db_qkv,
                                   float* db_o, bool accum, hipStream_t s) {
   const ColsumJob jobs[2] = {{ws.dqkv, d.qkv_l, db_qkv}, {static_cast<const uint16_t*>(dh), d.h, db_o}};
-  return colsum_bf16(jobs, db_o ? 2 : 1, d.S, accum, ws.ws, s);
+  const double bytes = 2.0 * d.S * (d.qkv_l + (db_o ? d.h : 0)) + 4.0 * (d.qkv_l + (db_o ? d.h : 0));
+  return prof::timed(prof::COLSUM, "colsum_attn", 0, bytes, s,
+                     [&] { return colsum_bf16(jobs, db_o ? 2 : 1, d.S, accum, ws.ws, s); });
 }
 
 mtl_status mtl_mlp_bwd(const mtl_layer_cfg* c, const void* dy, const void* h, const void* gz, const void* a,
@@ -650,14 +701,12 @@ mtl_status mtl_mlp_bwd(const mtl_layer_cfg* c, const void* dy, const void* h, co
     // E5M2 gradients, E4M3 activations and weights; wgrad operands transposed
     MTL_TRY(quantize({{dy, &ws.dy}, {w2, &ws.w2}, {a, &ws.a_t}}, ws.amax_ws, s));
     // dw2 = a^T . dy with dz = (dy . w2^T) * gz in one launch, then dw1 = h^T . dz with dh_partial = dz . w1^T
-    MTL_TRY(gemm_fp8_pair(gemm8_args(ws.a_t, ws.a_t.qt, ws.dy, ws.dy.qt, d.f_l, d.h, d.S, dw2, d.h), wepi,
-                          gemm8_args(ws.dy, ws.dy.q, ws.w2, ws.w2.q, d.S, d.f_l, d.h, ws.dz, d.f_l, nullptr, nullptr,
-                                     gz),
-                          EPI_DGELU, s));
+    MTL_TRY(gemm8_pair("fc2_bwd", gemm8_args(ws.a_t, ws.a_t.qt, ws.dy, ws.dy.qt, d.f_l, d.h, d.S, dw2, d.h), wepi,
+                       gemm8_args(ws.dy, ws.dy.q, ws.w2, ws.w2.q, d.S, d.f_l, d.h, ws.dz, d.f_l, nullptr, nullptr, gz),
+                       EPI_DGELU, s));
     MTL_TRY(quantize({{ws.dz, &ws.dz8}, {h, &ws.h_t}, {w1, &ws.w1}}, ws.amax_ws, s));
-    MTL_TRY(gemm_fp8_pair(gemm8_args(ws.h_t, ws.h_t.qt, ws.dz8, ws.dz8.qt, d.h, d.f_l, d.S, dw1, d.f_l), wepi,
-                          gemm8_args(ws.dz8, ws.dz8.q, ws.w1, ws.w1.q, d.S, d.h, d.f_l, dh_partial, d.h), EPI_BF16,
-                          s));
+    MTL_TRY(gemm8_pair("fc1_bwd", gemm8_args(ws.h_t, ws.h_t.qt, ws.dz8, ws.dz8.qt, d.h, d.f_l, d.S, dw1, d.f_l), wepi,
+                       gemm8_args(ws.dz8, ws.dz8.q, ws.w1, ws.w1.q, d.S, d.h, d.f_l, dh_partial, d.h), EPI_BF16, s));
     MTL_TRY(mlp_bias_grads(d, ws, dy, db1, db2, accum, s));
     return MTL_OK;
   }
@@ -668,12 +717,12 @@ mtl_status mtl_mlp_bwd(const mtl_layer_cfg* c, const void* dy, const void* h, co
   g.aux = static_cast<const uint16_t*>(gz);
   g.ld_aux = d.f_l;
   GemmArgs g2 = gemm(a, d.f_l, dy, d.h, d.f_l, d.h, d.S, dw2, d.h);
-  MTL_TRY(gemm_bf16_pair(g2, GEMM_WGRAD, wepi, g, GEMM_DGRAD, EPI_DGELU, s));
+  MTL_TRY(gemm16_pair("fc2_bwd", g2, GEMM_WGRAD, wepi, 4, g, GEMM_DGRAD, EPI_DGELU, 2, s));
   MTL_TRY(mlp_bias_grads(d, ws, dy, db1, db2, accum, s));
   // dw1 = h^T . dz and dh_partial = dz . w1^T
   g = gemm(h, d.h, ws.dz, d.f_l, d.h, d.f_l, d.S, dw1, d.f_l);
   g2 = gemm(ws.dz, d.f_l, w1, d.f_l, d.S, d.h, d.f_l, dh_partial, d.h);
-  MTL_TRY(gemm_bf16_pair(g, GEMM_WGRAD, wepi, g2, GEMM_DGRAD, EPI_BF16, s));
+  MTL_TRY(gemm16_pair("fc1_bwd", g, GEMM_WGRAD, wepi, 4, g2, GEMM_DGRAD, EPI_BF16, 2, s));
   return MTL_OK;
 }
 
@@ -697,13 +746,13 @@ mtl_status mtl_attn_bwd(const mtl_layer_cfg* c, const void* dh, const void* x, c
   if (f8) {
     // do = dh . w_o^T ; dw_o = o^T . dh
     MTL_TRY(quantize({{dh, &ws.dh}, {w_o, &ws.wo}, {o, &ws.o_t}}, ws.amax_ws, s));
-    MTL_TRY(gemm_fp8_pair(gemm8_args(ws.o_t, ws.o_t.qt, ws.dh, ws.dh.qt, d.o_l, d.h, d.S, dw_o, d.h), wepi,
-                          gemm8_args(ws.dh, ws.dh.q, ws.wo, ws.wo.q, d.S, d.o_l, d.h, ws.dout, d.o_l), EPI_BF16, s));
+    MTL_TRY(gemm8_pair("proj_bwd", gemm8_args(ws.o_t, ws.o_t.qt, ws.dh, ws.dh.qt, d.o_l, d.h, d.S, dw_o, d.h), wepi,
+                       gemm8_args(ws.dh, ws.dh.q, ws.wo, ws.wo.q, d.S, d.o_l, d.h, ws.dout, d.o_l), EPI_BF16, s));
   } else {
     // dw_o = o^T . dh and do = dh . w_o^T, one launch (wgrad tiles first)
     GemmArgs g = gemm(dh, d.h, w_o, d.h, d.S, d.o_l, d.h, ws.dout, d.o_l);
     GemmArgs g2 = gemm(o, d.o_l, dh, d.h, d.o_l, d.h, d.S, dw_o, d.h);
-    MTL_TRY(gemm_bf16_pair(g2, GEMM_WGRAD, wepi, g, GEMM_DGRAD, EPI_BF16, s));
+    MTL_TRY(gemm16_pair("proj_bwd", g2, GEMM_WGRAD, wepi, 4, g, GEMM_DGRAD, EPI_BF16, 2, s));
   }
 
   AttnArgs at{};
@@ -720,15 +769,18 @@ mtl_status mtl_attn_bwd(const mtl_layer_cfg* c, const void* dh, const void* x, c
   at.lse_in = lse;
   at.delta = ws.delta;
   at.dqkv = ws.dqkv;
-  MTL_TRY(attention_bwd(at, s));
+  // reads qkv, o, dO and lse; writes dqkv (D = rowsum(dO * O) on the way)
+  MTL_TRY(prof::timed(prof::ATTN, "attn_bwd", 2.0 * attn_flop(c, d.heads_l, d.d),
+                      2.0 * d.S * (2 * d.qkv_l + 2 * d.o_l) + 4.0 * d.S * d.heads_l, s,
+                      [&] { return attention_bwd(at, s); }));
 
   if (f8) {
     // dw_qkv = x^T . dqkv ; dx_partial = dqkv . w_qkv^T
     MTL_TRY(quantize({{ws.dqkv, &ws.dqkv8}, {x, &ws.x_t}, {w_qkv, &ws.wqkv}}, ws.amax_ws, s));
-    MTL_TRY(gemm_fp8_pair(gemm8_args(ws.x_t, ws.x_t.qt, ws.dqkv8, ws.dqkv8.qt, d.h, d.qkv_l, d.S, dw_qkv, d.qkv_l),
-                          wepi,
-                          gemm8_args(ws.dqkv8, ws.dqkv8.q, ws.wqkv, ws.wqkv.q, d.S, d.h, d.qkv_l, dx_partial, d.h),
-                          EPI_BF16, s));
+    MTL_TRY(gemm8_pair("qkv_bwd",
+                       gemm8_args(ws.x_t, ws.x_t.qt, ws.dqkv8, ws.dqkv8.qt, d.h, d.qkv_l, d.S, dw_qkv, d.qkv_l), wepi,
+                       gemm8_args(ws.dqkv8, ws.dqkv8.q, ws.wqkv, ws.wqkv.q, d.S, d.h, d.qkv_l, dx_partial, d.h),
+                       EPI_BF16, s));
     MTL_TRY(attn_bias_grads(d, ws, dh, db_qkv, db_o, accum, s));
     return MTL_OK;
   }
@@ -736,7 +788,7 @@ mtl_status mtl_attn_bwd(const mtl_layer_cfg* c, const void* dh, const void* x, c
   // db_qkv = colsum(dqkv) and db_o = colsum(dh)
   GemmArgs g = gemm(x, d.h, ws.dqkv, d.qkv_l, d.h, d.qkv_l, d.S, dw_qkv, d.qkv_l);
   GemmArgs g2 = gemm(ws.dqkv, d.qkv_l, w_qkv, d.qkv_l, d.S, d.h, d.qkv_l, dx_partial, d.h);
-  MTL_TRY(gemm_bf16_pair(g, GEMM_WGRAD, wepi, g2, GEMM_DGRAD, EPI_BF16, s));
+  MTL_TRY(gemm16_pair("qkv_bwd", g, GEMM_WGRAD, wepi, 4, g2, GEMM_DGRAD, EPI_BF16, 2, s));
   MTL_TRY(attn_bias_grads(d, ws, dh, db_qkv, db_o, accum, s));
   return MTL_OK;
 }
@@ -952,8 +1004,12 @@ mtl_status mtl_moe_fwd(const mtl_moe_cfg* c, const void* x, const int32_t* offse
   const MoeDims d = moe_dims(c);
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
 
-  MTL_TRY(moe_gather(static_cast<const uint16_t*>(x), perm_token, offsets, (int)d.El, d.nmax, d.h,
-                     static_cast<uint16_t*>(xp), s));
+  // (MoE launch groups are timed without FLOP or bytes: the row counts that
+  // fix them live on the device)
+  MTL_TRY(prof::timed(prof::GATHER, "moe_gather", 0, 0, s, [&] {
+    return moe_gather(static_cast<const uint16_t*>(x), perm_token, offsets, (int)d.El, d.nmax, d.h,
+                      static_cast<uint16_t*>(xp), s);
+  }));
   // z = xp_e . w1_e: gz = GeLU'(z), a = GeLU(z)   (the grid covers N_max rows; M carries N_max)
   GemmArgs g = grouped(d, GROUP_M, offsets, d.h * d.f, 0);
   g.a = static_cast<const uint16_t*>(xp);
@@ -967,7 +1023,7 @@ mtl_status mtl_moe_fwd(const mtl_moe_cfg* c, const void* x, const int32_t* offse
   g.ldc = d.f;
   g.c2 = a;
   g.ldc2 = d.f;
-  MTL_TRY(gemm_bf16(g, GEMM_FWD, EPI_BIAS_GELU, s));
+  MTL_TRY(prof::timed(prof::GEMM, "moe_fc1_fwd", 0, 0, s, [&] { return gemm_bf16(g, GEMM_FWD, EPI_BIAS_GELU, s); }));
   // ye = a_e . w2_e
   g = grouped(d, GROUP_M, offsets, d.f * d.h, 0);
   g.a = static_cast<const uint16_t*>(a);
@@ -979,9 +1035,11 @@ mtl_status mtl_moe_fwd(const mtl_moe_cfg* c, const void* x, const int32_t* offse
   g.K = (int)d.f;
   g.c = ye;
   g.ldc = d.h;
-  MTL_TRY(gemm_bf16(g, GEMM_FWD, EPI_BF16, s));
-  MTL_TRY(moe_combine(static_cast<const uint16_t*>(ye), slot_row, gates, (int)d.T, (int)d.k, d.h,
-                      static_cast<uint16_t*>(y_partial), s));
+  MTL_TRY(prof::timed(prof::GEMM, "moe_fc2_fwd", 0, 0, s, [&] { return gemm_bf16(g, GEMM_FWD, EPI_BF16, s); }));
+  MTL_TRY(prof::timed(prof::GATHER, "moe_combine", 0, 0, s, [&] {
+    return moe_combine(static_cast<const uint16_t*>(ye), slot_row, gates, (int)d.T, (int)d.k, d.h,
+                       static_cast<uint16_t*>(y_partial), s);
+  }));
   return MTL_OK;
 }
 
@@ -1001,8 +1059,10 @@ mtl_status mtl_moe_bwd(const mtl_moe_cfg* c, const void* dy, const int32_t* offs
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   const int wepi = (c->flags & MTL_F_WGRAD_ACCUM) ? EPI_F32_ACC : EPI_F32;
 
-  MTL_TRY(moe_combine_bwd(static_cast<const uint16_t*>(dy), static_cast<const uint16_t*>(ye), perm_token, perm_slot,
-                          slot_row, offsets, (int)d.El, d.nmax, gates, (int)d.T, (int)d.k, d.h, ws.dye, dgates, s));
+  MTL_TRY(prof::timed(prof::GATHER, "moe_combine_bwd", 0, 0, s, [&] {
+    return moe_combine_bwd(static_cast<const uint16_t*>(dy), static_cast<const uint16_t*>(ye), perm_token, perm_slot,
+                           slot_row, offsets, (int)d.El, d.nmax, gates, (int)d.T, (int)d.k, d.h, ws.dye, dgates, s);
+  }));
   // dz = (dye_e . w2_e^T) * gz, gz = GeLU'(z)
   GemmArgs g = grouped(d, GROUP_M, offsets, d.f * d.h, 0);
   g.a = ws.dye;
@@ -1016,7 +1076,7 @@ mtl_status mtl_moe_bwd(const mtl_moe_cfg* c, const void* dy, const int32_t* offs
   g.ldc = d.f;
   g.aux = static_cast<const uint16_t*>(gz);
   g.ld_aux = d.f;
-  MTL_TRY(gemm_bf16(g, GEMM_DGRAD, EPI_DGELU, s));
+  MTL_TRY(prof::timed(prof::GEMM, "moe_fc2_dgrad", 0, 0, s, [&] { return gemm_bf16(g, GEMM_DGRAD, EPI_DGELU, s); }));
   // dw2[e] = a_e^T . dye_e   (K = the expert's rows; K carries N_max for the range check)
   g = grouped(d, GROUP_K, offsets, 0, d.f * d.h);
   g.a = static_cast<const uint16_t*>(a);
@@ -1028,7 +1088,7 @@ mtl_status mtl_moe_bwd(const mtl_moe_cfg* c, const void* dy, const int32_t* offs
   g.K = (int)d.nmax;
   g.c = dw2;
   g.ldc = d.h;
-  MTL_TRY(gemm_bf16(g, GEMM_WGRAD, wepi, s));
+  MTL_TRY(prof::timed(prof::GEMM, "moe_fc2_wgrad", 0, 0, s, [&] { return gemm_bf16(g, GEMM_WGRAD, wepi, s); }));
   // dw1[e] = xp_e^T . dz_e
   g = grouped(d, GROUP_K, offsets, 0, d.h * d.f);
   g.a = static_cast<const uint16_t*>(xp);
@@ -1040,7 +1100,7 @@ mtl_status mtl_moe_bwd(const mtl_moe_cfg* c, const void* dy, const int32_t* offs
   g.K = (int)d.nmax;
   g.c = dw1;
   g.ldc = d.f;
-  MTL_TRY(gemm_bf16(g, GEMM_WGRAD, wepi, s));
+  MTL_TRY(prof::timed(prof::GEMM, "moe_fc1_wgrad", 0, 0, s, [&] { return gemm_bf16(g, GEMM_WGRAD, wepi, s); }));
   // dxp = dz_e . w1_e^T into the dye buffer (dye is dead after dw2), then the
   // slot-ordered scatter-add into dx_partial
   uint16_t* dxp = ws.dye;
@@ -1054,8 +1114,10 @@ mtl_status mtl_moe_bwd(const mtl_moe_cfg* c, const void* dy, const int32_t* offs
   g.K = (int)d.f;
   g.c = dxp;
   g.ldc = d.h;
-  MTL_TRY(gemm_bf16(g, GEMM_DGRAD, EPI_BF16, s));
-  MTL_TRY(moe_combine(dxp, slot_row, nullptr, (int)d.T, (int)d.k, d.h, static_cast<uint16_t*>(dx_partial), s));
+  MTL_TRY(prof::timed(prof::GEMM, "moe_fc1_dgrad", 0, 0, s, [&] { return gemm_bf16(g, GEMM_DGRAD, EPI_BF16, s); }));
+  MTL_TRY(prof::timed(prof::GATHER, "moe_scatter", 0, 0, s, [&] {
+    return moe_combine(dxp, slot_row, nullptr, (int)d.T, (int)d.k, d.h, static_cast<uint16_t*>(dx_partial), s);
+  }));
   return MTL_OK;
 }
 

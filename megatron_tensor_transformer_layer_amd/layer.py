@@ -200,3 +200,42 @@ def _run_sp(ranks, tp, D, x_bits, b_o_bits, b2_bits, dy_bits, residual, device) 
     out = _outputs(ranks, rows(ys), host_f64(hs[0]), host_f64(dhs[0]), rows(dxs))
     out["gathered"] = {k: [host_f64(b) for b in v] for k, v in (("x", xs), ("h", hs), ("dy", dys), ("dh", dhs))}
     return out
+
+
+class AllShardsStep:
+    """The whole layer on one device as one callable step: every TP rank's
+    forward and backward plus the four full reductions, on fixed buffers (so the
+    step can be captured into a HIP graph and replayed).  shards: per-rank
+    inputs; x, dy, b_o, b2: bf16 bit patterns of the full tensors."""
+
+    def __init__(self, shape, tp: int, shards: list, x_bits, dy_bits, b_o_bits, b2_bits, device=DEV,
+                 precision: int = MTL_PREC_BF16):
+        self.ranks = [RankState(shape, tp, r, shards[r], device=device, precision=precision) for r in range(tp)]
+        D = self.D = self.ranks[0].D
+        self.x, self.dy = bf16_dev(x_bits, device), bf16_dev(dy_bits, device)
+        self.b_o, self.b2 = bf16_dev(b_o_bits, device), bf16_dev(b2_bits, device)
+        self.h, self.y, self.dh, self.dx = (empty_bf16(D.S, D.h, device=device) for _ in range(4))
+
+    def __call__(self):
+        rk, D = self.ranks, self.D
+        for r in rk:
+            r.attn_fwd(self.x)
+        mtl_reduce([r.p_attn for r in rk], self.b_o, None, self.h, D.S, D.h)
+        for r in rk:
+            r.mlp_fwd(self.h)
+        mtl_reduce([r.p_mlp for r in rk], self.b2, None, self.y, D.S, D.h)
+        for r in rk:
+            r.mlp_bwd(self.dy, self.h, want_db2=r is rk[0])
+        mtl_reduce([r.p_dh for r in rk], None, None, self.dh, D.S, D.h)
+        for r in rk:
+            r.attn_bwd(self.dh, self.x, want_db_o=r is rk[0])
+        mtl_reduce([r.p_dx for r in rk], None, None, self.dx, D.S, D.h)
+
+    def outputs(self) -> dict:
+        """The step's device outputs (views of the step's own buffers)."""
+        out = dict(h=self.h, y=self.y, dh=self.dh, dx=self.dx)
+        for i, r in enumerate(self.ranks):
+            for k in ("qkv", "o", "lse", "gz", "a", "dw_qkv", "db_qkv", "dw_o", "dw1", "db1", "dw2"):
+                out[f"{k}{i}"] = getattr(r, k)
+        out["db_o"], out["db2"] = self.ranks[0].db_o, self.ranks[0].db2
+        return out

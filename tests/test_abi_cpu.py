@@ -303,3 +303,18 @@ def test_mxfp6_validation_before_any_launch(mtl):
     assert g(128, 128, 192) == mtl.MTL_E_SHAPE  # K % 128
     assert g(64, 128, 128) == mtl.MTL_E_SHAPE
     assert lib.mtl_mxfp6_gemm(128, 128, 128, P, P, P + 4, P, P, 128, None) == mtl.MTL_E_ALIGN
+
+
+def test_launch_timing_host_side(mtl):
+    """The launch-timing calls on a host without a GPU: start reports the
+    missing device, stop and record validate their arguments."""
+    lib = mtl.lib()
+    n = ctypes.c_int32(-1)
+    assert lib.mtl_prof_start() == mtl.MTL_E_HIP
+    assert lib.mtl_prof_stop(None) == mtl.MTL_E_NULL
+    assert lib.mtl_prof_stop(ctypes.byref(n)) == mtl.MTL_OK and n.value == 0
+    k, f, b, ms, name = ctypes.c_int32(), ctypes.c_double(), ctypes.c_double(), ctypes.c_float(), ctypes.c_char_p()
+    refs = [ctypes.byref(v) for v in (k, f, b, ms, name)]
+    assert lib.mtl_prof_record(0, *refs) == mtl.MTL_E_SHAPE
+    assert lib.mtl_prof_record(-1, *refs) == mtl.MTL_E_SHAPE
+    assert lib.mtl_prof_record(0, None, *refs[1:]) == mtl.MTL_E_NULL
