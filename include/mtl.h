@@ -254,6 +254,25 @@ mtl_status mtl_mlp_bwd(const mtl_layer_cfg* cfg, const void* dy, const void* h, 
                        const void* w1, const void* w2, void* dh_partial, float* dw1, float* db1, float* dw2,
                        float* db2, void* scratch, size_t scratch_bytes, mtl_stream_t stream);
 
+/* mtl_mlp_bwd for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * same computation, arguments and outputs, with the scratch taken from a
+ * device array inside the library of MTL_NOALLOC_SCRATCH_BYTES bytes instead of
+ * a caller's buffer.  It allocates nothing and calls no allocating routine.
+ * Every GPU the library runs on holds one such array until the process ends;
+ * the first call on a device (with that device current) looks up its address.
+ * Status: mtl_validate's; MTL_E_WORKSPACE, before any HIP call, when the
+ * configuration needs more scratch than the array holds (in bf16 the MLP
+ * backward needs 2*S*(f/t) bytes for dz plus 4*ceil(S/64)*(f/t + h) for the
+ * column sums: S = 4096 with f/t = 4096 and h = 8192 takes 35 MiB; the fp8
+ * path's operand codes need far more at such sizes); otherwise as mtl_mlp_bwd.
+ * All calls on one GPU share its array: calls that overlap on one GPU (on
+ * different streams, or from several threads) race and give wrong results. */
+#define MTL_NOALLOC_SCRATCH_BYTES (48u << 20)
+mtl_status mtl_mlp_bwd_noalloc(const mtl_layer_cfg* cfg, const void* dy, const void* h, const void* gz,
+                               const void* a, const void* w1, const void* w2, void* dh_partial, float* dw1,
+                               float* db1, float* dw2, float* db2, mtl_stream_t stream);
+
 /* Attention backward given dh = dL/dH [S, h] bf16 (reduced) and the saved
  * qkv, o, lse of mtl_attn_fwd:
  *   do         = dh . w_o^T                  (scratch, bf16)

@@ -24,6 +24,7 @@ MTL_FP8_AMAX_SCRATCH = 4096
 MTL_CP_MAX = 64
 MTL_F_RESIDUAL, MTL_F_WGRAD_ACCUM = 1, 2
 MTL_PROF_MAX = 2048
+MTL_NOALLOC_SCRATCH_BYTES = 48 << 20
 MTL_PROF_KINDS = ("gemm", "attention", "reduce", "colsum", "quantize", "gather")
 
 
@@ -79,6 +80,7 @@ _SIGS = {
     "mtl_moe_permute": (ctypes.c_int, [_MCFG, _P, _P, _P, _P, _P, _P, _P]),
     "mtl_moe_fwd": (ctypes.c_int, [_MCFG] + [_P] * 13),
     "mtl_moe_bwd": (ctypes.c_int, [_MCFG] + [_P] * 17 + [_SZ, _P]),
+    "mtl_mlp_bwd_noalloc": (ctypes.c_int, [_CFG, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P]),
     "mtl_prof_start": (ctypes.c_int, []),
     "mtl_prof_stop": (ctypes.c_int, [ctypes.POINTER(_I32)]),
     "mtl_prof_record": (ctypes.c_int, [_I32, ctypes.POINTER(_I32), ctypes.POINTER(ctypes.c_double),
@@ -232,6 +234,12 @@ def mtl_mlp_bwd(cfg, dy, h, gz, a, w1, w2, dh_partial, dw1, db1, dw2, db2, scrat
     _check(lib().mtl_mlp_bwd(ctypes.byref(cfg), _ptr(dy), _ptr(h), _ptr(gz), _ptr(a), _ptr(w1), _ptr(w2),
                              _ptr(dh_partial), _ptr(dw1), _ptr(db1), _ptr(dw2), _ptr(db2), _ptr(scratch), nbytes,
                              _stream(stream)), "mtl_mlp_bwd")
+
+
+def mtl_mlp_bwd_noalloc(cfg, dy, h, gz, a, w1, w2, dh_partial, dw1, db1, dw2, db2, stream=None):
+    _check(lib().mtl_mlp_bwd_noalloc(ctypes.byref(cfg), _ptr(dy), _ptr(h), _ptr(gz), _ptr(a), _ptr(w1), _ptr(w2),
+                                     _ptr(dh_partial), _ptr(dw1), _ptr(db1), _ptr(dw2), _ptr(db2), _stream(stream)),
+           "mtl_mlp_bwd_noalloc")
 
 
 def mtl_attn_bwd(cfg, dh, x, qkv, o, lse, w_qkv, w_o, dx_partial, dw_qkv, db_qkv, dw_o, db_o, scratch,

@@ -274,6 +274,13 @@ size_t mlp_fwd_scratch(const mtl_layer_cfg* c, const Dims& d, MlpFwdScratch* s, 
 
 }  // namespace
 
+namespace mtl {
+size_t mlp_bwd_scratch_bytes(const mtl_layer_cfg* c) {
+  const Dims d = dims_of(c);
+  return mlp_scratch(c, d, nullptr, nullptr);
+}
+}  // namespace mtl
+
 extern "C" {
 
 const char* mtl_status_str(mtl_status s) {

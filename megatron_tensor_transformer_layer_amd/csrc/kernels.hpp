@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+struct mtl_layer_cfg;  // include/mtl.h
+
 namespace mtl {
 
 // ---------------------------------------------------------------- GEMM
@@ -226,5 +228,9 @@ hipError_t moe_combine(const uint16_t* rows, const int32_t* slot_row, const floa
 hipError_t moe_combine_bwd(const uint16_t* dy, const uint16_t* ye, const int32_t* ptok, const int32_t* pslot,
                            const int32_t* slot_row, const int32_t* offsets, int E_l, int64_t max_rows,
                            const float* gates, int T, int k, int64_t h, uint16_t* dye, float* dgates, hipStream_t s);
+
+// Scratch bytes mtl_mlp_bwd needs for a valid configuration (defined with the
+// entry points; used by the entry point that allocates nothing).
+size_t mlp_bwd_scratch_bytes(const ::mtl_layer_cfg* c);
 
 }  // namespace mtl

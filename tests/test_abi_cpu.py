@@ -318,3 +318,21 @@ def test_launch_timing_host_side(mtl):
     assert lib.mtl_prof_record(0, *refs) == mtl.MTL_E_SHAPE
     assert lib.mtl_prof_record(-1, *refs) == mtl.MTL_E_SHAPE
     assert lib.mtl_prof_record(0, None, *refs[1:]) == mtl.MTL_E_NULL
+
+
+def test_noalloc_mlp_backward_host_side(mtl):
+    """mtl_mlp_bwd_noalloc refuses, before any HIP call, a configuration whose
+    MLP backward needs more scratch than its array holds, and a bad
+    configuration; a configuration that fits reaches the device lookup, which
+    fails without a GPU.  The fake addresses are never dereferenced."""
+    lib = mtl.lib()
+    P = 1 << 20
+    args = [P] * 11 + [None]
+    call = lambda cfg: lib.mtl_mlp_bwd_noalloc(ctypes.byref(cfg), *args)
+    # dz alone: 2 * 4096 * 8192 bytes = 64 MiB > 48 MiB
+    assert call(mtl.make_cfg(4096, 32, 32768, 4096, 1, 4, 0)) == mtl.MTL_E_WORKSPACE
+    # fp8 codes at the 7B-class TP=4 shape do not fit either
+    assert call(mtl.make_cfg(4096, 32, 16384, 4096, 1, 4, 0, mtl.MTL_PREC_FP8_HYBRID)) == mtl.MTL_E_WORKSPACE
+    assert call(mtl.make_cfg(768, 12, 3072, 512, 1, 5, 0)) == mtl.MTL_E_DIVISIBILITY
+    # the 96-layer GPT TP=8 rank fits (35 MiB)
+    assert call(mtl.make_cfg(8192, 64, 32768, 4096, 1, 8, 0)) == mtl.MTL_E_HIP
