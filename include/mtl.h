@@ -291,6 +291,14 @@ mtl_status mtl_attn_bwd(const mtl_layer_cfg* cfg, const void* dh, const void* x,
                         float* db_qkv, float* dw_o, float* db_o, void* scratch, size_t scratch_bytes,
                         mtl_stream_t stream);
 
+/* Where mtl_attn_bwd leaves its two intermediate gradients in its scratch: dO
+ * [S, h/t] at byte offset *do_offset and dQKV [S, 3h/t] at *dqkv_offset, bf16
+ * row-major (dQKV in the head-interleaved layout of qkv).  They stay there until
+ * the scratch is reused; a caller may read them once the call's stream has
+ * drained (to check the attention backward on its own, or to reuse dQKV).
+ * Host-only; status as mtl_validate. */
+mtl_status mtl_attn_bwd_scratch_layout(const mtl_layer_cfg* cfg, size_t* do_offset, size_t* dqkv_offset);
+
 /* fp8 per-tensor scaling (the site summary's --fp8-format hybrid; the pages give
  * no encoding or scaling rule, read as OCP E4M3 (bias 7, max 448, no infinity)
  * and E5M2 (bias 15, max 57344) with current scaling).
@@ -316,6 +324,23 @@ mtl_status mtl_fp8_cast(const void* x, int64_t rows, int64_t cols, int32_t forma
  * quantise their GEMM operands. */
 mtl_status mtl_fp8_quantize(const void* x, int64_t rows, int64_t cols, int32_t format, float* rec, void* out,
                             void* out_t, void* scratch, size_t scratch_bytes, mtl_stream_t stream);
+
+/* One fp8 GEMM on codes the caller already holds (from mtl_fp8_quantize or
+ * mtl_fp8_cast): C[M, N] = (A . B^T) * a_rec[2] * b_rec[2] (+ bias[n]),
+ * accumulated in fp32, where A [M, K] and B [N, K] are k-contiguous codes
+ * (row stride K) in formats fmt_a, fmt_b and a_rec, b_rec their scale records
+ * {amax, s, 1/s} (device memory).  The format pairs of the hybrid recipe:
+ *   E4M3 x E4M3 (forward): C bf16, bias (bf16 [N]) optional;
+ *   E5M2 x E4M3 (dgrad: gradient x weight): C bf16, no bias;
+ *   E4M3 x E5M2 (wgrad: activation x gradient): C fp32, no bias.
+ * ldc >= N, ldc % 8 == 0.  K % 16 == 0 and every operand under 4 GiB
+ * ((M + 256) * K < 2^32, likewise N).  It runs the kernel and tile shape a
+ * layer call runs for a product of this shape and formats when that product
+ * is launched alone (every fp8 GEMM of the layer calls except the output
+ * projection's backward pair); for callers that keep quantised weights. */
+mtl_status mtl_fp8_gemm(int64_t M, int64_t N, int64_t K, const void* a, int32_t fmt_a, const float* a_rec,
+                        const void* b, int32_t fmt_b, const float* b_rec, const void* bias, void* c, int64_t ldc,
+                        mtl_stream_t stream);
 
 /* ------------------------------------------------------------------------
  * MoE expert block of one expert-parallel rank.

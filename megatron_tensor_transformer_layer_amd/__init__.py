@@ -70,6 +70,7 @@ _SIGS = {
     "mtl_fp8_amax": (ctypes.c_int, [_P, _I64, _I32, _P, _P, _SZ, _P]),
     "mtl_fp8_cast": (ctypes.c_int, [_P, _I64, _I64, _I32, _P, _P, _P, _P]),
     "mtl_fp8_quantize": (ctypes.c_int, [_P, _I64, _I64, _I32, _P, _P, _P, _P, _SZ, _P]),
+    "mtl_fp8_gemm": (ctypes.c_int, [_I64, _I64, _I64, _P, _I32, _P, _P, _I32, _P, _P, _P, _I64, _P]),
     "mtl_moe_validate": (ctypes.c_int, [_MCFG]),
     "mtl_moe_router_fwd": (ctypes.c_int, [_MCFG, _P, _P, _P, _P]),
     "mtl_moe_router_sizes": (ctypes.c_int, [_MCFG, ctypes.POINTER(_SZ)]),
@@ -80,6 +81,7 @@ _SIGS = {
     "mtl_moe_permute": (ctypes.c_int, [_MCFG, _P, _P, _P, _P, _P, _P, _P]),
     "mtl_moe_fwd": (ctypes.c_int, [_MCFG] + [_P] * 13),
     "mtl_moe_bwd": (ctypes.c_int, [_MCFG] + [_P] * 17 + [_SZ, _P]),
+    "mtl_attn_bwd_scratch_layout": (ctypes.c_int, [_CFG, ctypes.POINTER(_SZ), ctypes.POINTER(_SZ)]),
     "mtl_mlp_bwd_noalloc": (ctypes.c_int, [_CFG, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P]),
     "mtl_prof_start": (ctypes.c_int, []),
     "mtl_prof_stop": (ctypes.c_int, [ctypes.POINTER(_I32)]),
@@ -236,6 +238,14 @@ def mtl_mlp_bwd(cfg, dy, h, gz, a, w1, w2, dh_partial, dw1, db1, dw2, db2, scrat
                              _stream(stream)), "mtl_mlp_bwd")
 
 
+def mtl_attn_bwd_scratch_layout(cfg):
+    """(do_offset, dqkv_offset): byte offsets of dO and dQKV in mtl_attn_bwd's scratch."""
+    a, b = _SZ(0), _SZ(0)
+    _check(lib().mtl_attn_bwd_scratch_layout(ctypes.byref(cfg), ctypes.byref(a), ctypes.byref(b)),
+           "mtl_attn_bwd_scratch_layout")
+    return a.value, b.value
+
+
 def mtl_mlp_bwd_noalloc(cfg, dy, h, gz, a, w1, w2, dh_partial, dw1, db1, dw2, db2, stream=None):
     _check(lib().mtl_mlp_bwd_noalloc(ctypes.byref(cfg), _ptr(dy), _ptr(h), _ptr(gz), _ptr(a), _ptr(w1), _ptr(w2),
                                      _ptr(dh_partial), _ptr(dw1), _ptr(db1), _ptr(dw2), _ptr(db2), _stream(stream)),
@@ -344,3 +354,8 @@ def mtl_prof_record(i: int) -> dict:
                                  ctypes.byref(name)), "mtl_prof_record")
     return dict(kind=MTL_PROF_KINDS[kind.value], name=name.value.decode(), flop=flop.value, bytes=nbytes.value,
                 ms=ms.value)
+
+
+def mtl_fp8_gemm(M, N, K, a, fmt_a, a_rec, b, fmt_b, b_rec, bias, c, ldc=None, stream=None):
+    _check(lib().mtl_fp8_gemm(M, N, K, _ptr(a), fmt_a, _ptr(a_rec), _ptr(b), fmt_b, _ptr(b_rec), _ptr(bias), _ptr(c),
+                              N if ldc is None else ldc, _stream(stream)), "mtl_fp8_gemm")

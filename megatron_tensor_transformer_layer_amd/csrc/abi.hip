@@ -800,6 +800,18 @@ mtl_status mtl_attn_bwd(const mtl_layer_cfg* c, const void* dh, const void* x, c
   return MTL_OK;
 }
 
+mtl_status mtl_attn_bwd_scratch_layout(const mtl_layer_cfg* c, size_t* do_offset, size_t* dqkv_offset) {
+  mtl_status st = mtl_validate(c);
+  if (st != MTL_OK) return st;
+  if (!do_offset || !dqkv_offset) return MTL_E_NULL;
+  // the same carving as mtl_attn_bwd, over a base address of 0
+  AttnScratch ws;
+  attn_scratch(c, dims_of(c), &ws, reinterpret_cast<char*>(ALIGN));
+  *do_offset = (size_t)(reinterpret_cast<char*>(ws.dout) - reinterpret_cast<char*>(ALIGN));
+  *dqkv_offset = (size_t)(reinterpret_cast<char*>(ws.dqkv) - reinterpret_cast<char*>(ALIGN));
+  return MTL_OK;
+}
+
 // ---------------------------------------------------------------- fp8 scaling
 
 mtl_status mtl_fp8_amax(const void* x, int64_t n, int32_t format, float* rec, void* scratch, size_t scratch_bytes,
@@ -837,6 +849,36 @@ mtl_status mtl_fp8_quantize(const void* x, int64_t rows, int64_t cols, int32_t f
   const QuantJob job{static_cast<const uint16_t*>(x), rows, cols, format, rec, static_cast<uint8_t*>(out),
                      static_cast<uint8_t*>(out_t)};
   return hip_status(fp8_quantize_n(&job, 1, scratch, reinterpret_cast<hipStream_t>(stream)));
+}
+
+mtl_status mtl_fp8_gemm(int64_t M, int64_t N, int64_t K, const void* a, int32_t fmt_a, const float* a_rec,
+                        const void* b, int32_t fmt_b, const float* b_rec, const void* bias, void* c, int64_t ldc,
+                        mtl_stream_t stream) {
+  mtl_status st = check_ptrs(a, a_rec, b, b_rec, c);
+  if (st != MTL_OK) return st;
+  if (bias && !aligned16(bias)) return MTL_E_ALIGN;
+  if (M <= 0 || N <= 0 || K <= 0 || K % 16 || ldc < N || ldc % 8) return MTL_E_SHAPE;
+  if (M > INT32_MAX || N > INT32_MAX || K > INT32_MAX) return MTL_E_SHAPE;
+  if ((M + 256) * K >= ((int64_t)1 << 32) || (N + 256) * K >= ((int64_t)1 << 32)) return MTL_E_SHAPE;
+  int epi;
+  if (fmt_a == MTL_FP8_E4M3 && fmt_b == MTL_FP8_E4M3) epi = bias ? EPI_BF16_BIAS : EPI_BF16;
+  else if (fmt_a == MTL_FP8_E5M2 && fmt_b == MTL_FP8_E4M3 && !bias) epi = EPI_BF16;
+  else if (fmt_a == MTL_FP8_E4M3 && fmt_b == MTL_FP8_E5M2 && !bias) epi = EPI_F32;
+  else return MTL_E_UNSUPPORTED;
+  GemmArgs g{};
+  g.a = static_cast<const uint16_t*>(a);
+  g.b = static_cast<const uint16_t*>(b);
+  g.lda = K;
+  g.ldb = K;
+  g.M = (int)M;
+  g.N = (int)N;
+  g.K = (int)K;
+  g.c = c;
+  g.ldc = ldc;
+  g.bias = static_cast<const uint16_t*>(bias);
+  g.scale_a = a_rec + 2;
+  g.scale_b = b_rec + 2;
+  return hip_status(gemm_fp8(g, fmt_a, fmt_b, epi, reinterpret_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

@@ -124,3 +124,49 @@ def dq_rows(qkv_full, do_rows, heads: int, rows) -> np.ndarray:
             ds = p * (v @ g - g @ (p @ v))
             out[j, n * d:(n + 1) * d] = (ds @ k) * scale
     return out
+
+
+def dkv_rows(qkv_full, do_rank, heads: int, cp: int, rank: int, key_rows, head_ids=None,
+             block: int = 512) -> np.ndarray:
+    """dK and dV of selected key rows (global indices, before the end of the
+    rank's chunk) from CP rank `rank`'s queries, in the per-head [dK_n | dV_n]
+    layout of ``rank_attention_backward``'s shares, for the heads ``head_ids``
+    (default: all, in order): [len(key_rows), 2*len(head_ids)*d].
+
+    The textbook attention backward restricted to those key columns: per head
+    and block of the rank's queries i, P = softmax over keys j <= i of
+    q_i k_j * scale, O = P V, D_i = dO_i . O_i; for each selected key k,
+    dV_k = sum_i P_ik dO_i and dK_k = scale * sum_i P_ik (dO_i . v_k - D_i) q_i.
+    For sampled checks at sizes where the whole backward is too slow."""
+    qkv_full = np.asarray(qkv_full, dtype=np.float64)
+    do_rank = np.asarray(do_rank, dtype=np.float64)
+    rows = chunk_rows(qkv_full.shape[0], cp, rank)
+    d = qkv_full.shape[1] // (3 * heads)
+    scale = 1.0 / math.sqrt(d)
+    keys = np.asarray(list(key_rows), dtype=np.int64)
+    if keys.size and (keys.min() < 0 or keys.max() >= rows.stop):
+        raise ValueError("key rows outside the keys the rank's queries see")
+    head_ids = list(range(heads)) if head_ids is None else list(head_ids)
+    out = np.zeros((len(keys), 2 * len(head_ids) * d))
+    kv_end = rows.stop
+    for hi, n in enumerate(head_ids):
+        sq, sk, sv = L.head_slices(heads, d, n)
+        K, V = qkv_full[:kv_end, sk], qkv_full[:kv_end, sv]
+        for b0 in range(rows.start, rows.stop, block):
+            b1 = min(b0 + block, rows.stop)
+            q = qkv_full[b0:b1, sq]
+            g = do_rank[b0 - rows.start:b1 - rows.start, n * d:(n + 1) * d]
+            s = (q @ K.T) * scale
+            # keys of the rank's own chunk are visible up to the query itself;
+            # every earlier chunk's key is visible to all of its queries
+            own = s[:, rows.start:]
+            own[np.arange(b0, b1)[:, None] < np.arange(rows.start, kv_end)[None, :]] = -np.inf
+            m = s.max(axis=1, keepdims=True)
+            p = np.exp(s - m)
+            p /= p.sum(axis=1, keepdims=True)
+            D = np.sum(g * (p @ V), axis=1)
+            pk = p[:, keys]                       # [queries, selected keys]
+            ds = pk * (g @ V[keys].T - D[:, None])
+            out[:, 2 * hi * d:(2 * hi + 1) * d] += (ds.T @ q) * scale
+            out[:, (2 * hi + 1) * d:(2 * hi + 2) * d] += pk.T @ g
+    return out

@@ -336,3 +336,33 @@ def test_noalloc_mlp_backward_host_side(mtl):
     assert call(mtl.make_cfg(768, 12, 3072, 512, 1, 5, 0)) == mtl.MTL_E_DIVISIBILITY
     # the 96-layer GPT TP=8 rank fits (35 MiB)
     assert call(mtl.make_cfg(8192, 64, 32768, 4096, 1, 8, 0)) == mtl.MTL_E_HIP
+
+
+def test_attn_bwd_scratch_layout(mtl):
+    """dO sits at the start of mtl_attn_bwd's scratch and dQKV after it, at the
+    next 256-byte boundary; both fit in the size mtl_workspace_bytes reports."""
+    for hidden, heads, ffn, seq, tp in ((4096, 32, 16384, 4096, 4), (768, 12, 3072, 500, 2)):
+        cfg = mtl.make_cfg(hidden, heads, ffn, seq, 1, tp, 0)
+        off_do, off_dqkv = mtl.mtl_attn_bwd_scratch_layout(cfg)
+        o_l, qkv_l = hidden // tp, 3 * hidden // tp
+        assert off_do == 0
+        assert off_dqkv == (seq * o_l * 2 + 255) // 256 * 256
+        assert off_dqkv + seq * qkv_l * 2 <= mtl.mtl_workspace_bytes(cfg)
+    with pytest.raises(mtl.MtlError):
+        mtl.mtl_attn_bwd_scratch_layout(mtl.make_cfg(768, 12, 3072, 512, 1, 5, 0))
+
+
+def test_fp8_gemm_validation_before_any_launch(mtl):
+    lib = mtl.lib()
+    P = 1 << 20
+    g = lambda M, N, K, fa, fb, bias, c, ldc: lib.mtl_fp8_gemm(M, N, K, P, fa, P, P, fb, P, bias, c, ldc, None)
+    E4, E5 = mtl.MTL_FP8_E4M3, mtl.MTL_FP8_E5M2
+    assert g(256, 256, 100, E4, E4, None, P, 256) == mtl.MTL_E_SHAPE  # K % 16
+    assert g(256, 256, 128, E4, E4, None, P, 200) == mtl.MTL_E_SHAPE  # ldc < N
+    assert g(256, 256, 128, E4, E4, None, P, 260) == mtl.MTL_E_SHAPE  # ldc % 8
+    assert g(0, 256, 128, E4, E4, None, P, 256) == mtl.MTL_E_SHAPE
+    assert g(256, 256, 128, E5, E5, None, P, 256) == mtl.MTL_E_UNSUPPORTED  # not a pair of the recipe
+    assert g(256, 256, 128, E5, E4, P, P, 256) == mtl.MTL_E_UNSUPPORTED  # bias on a dgrad
+    assert g(256, 256, 128, E4, E4, P + 2, P, 256) == mtl.MTL_E_ALIGN
+    assert g(256, 256, 128, E4, E4, None, None, 256) == mtl.MTL_E_NULL
+    assert g(1 << 20, 256, 1 << 13, E4, E4, None, P, 256) == mtl.MTL_E_SHAPE  # A past 4 GiB

@@ -161,10 +161,12 @@ def test_cp_attention_backward_deterministic(mtl):
 @pytest.mark.gpu
 @pytest.mark.parametrize("rank", [3, 1])
 def test_cp_attention_backward_fullsize(mtl, rank):
-    """dQ on sampled query rows against the oracle; dK and dV of all chunks
-    through two identities of the exact gradient: summed over every key the
-    rank's queries see, dV gives the column sums of dO (each query's
-    probabilities sum to 1) and dK gives zero (each query's dS sums to 0)."""
+    """dQ on sampled query rows and dK/dV on sampled key rows of every chunk
+    the rank sees (its own diagonal chunk and each earlier chunk's share),
+    element-wise against the oracle; and, over every key, two identities of
+    the exact gradient: summed over the keys, dV gives the column sums of dO
+    (each query's probabilities sum to 1) and dK gives zero (each query's dS
+    sums to 0)."""
     from megatron_tensor_transformer_layer_amd.layer import bf16_dev, host_f64
     shape = synth.CP_WORKLOADS["cp4-seq32k-7b-tp4"]
     H, d, C = shape.heads, shape.head_dim, shape.chunk
@@ -183,6 +185,13 @@ def test_cp_attention_backward_fullsize(mtl, rank):
     ref = CP.dq_rows(f64(bits[: (rank + 1) * C]), f64(do_bits)[local], H, [rank * C + i for i in local])
     assert_bf16(f"rank {rank} dQ rows", dq[local], ref)
     allkv = np.concatenate(shares, axis=0)  # every key row of chunks 0..rank
+    keys = sorted(set([j * C + i for j in range(rank + 1) for i in (0, 1, 63, 64, C // 2, C - 1)]
+                      + rng.choice((rank + 1) * C, 10, replace=False).tolist()))
+    hs = [0, H - 1]  # two of the heads: the restricted backward still takes every query of the rank
+    ref_kv = CP.dkv_rows(f64(bits), f64(do_bits), H, shape.cp, rank, keys, head_ids=hs)
+    got_kv = np.concatenate([allkv[keys][:, 2 * n * d:(2 * n + 2) * d] for n in hs], axis=1)
+    print(f"  dK|dV on {len(keys)} key rows of heads {hs}", flush=True)
+    assert_bf16(f"rank {rank} dK|dV rows", got_kv, ref_kv)
     dsum = f64(do_bits).sum(axis=0)
     for n in range(H):
         dk = allkv[:, 2 * n * d:(2 * n + 1) * d]

@@ -7,12 +7,28 @@
   at scale 1), on Gaussian tensors (s not a power of two), on zeros, and on
   tensors holding inf and NaN; the transposed copy is the transpose.
 * The whole tensor-parallel layer in fp8 (all shards on one device) against
-  both references: the fp64 layer with quantised GEMM operands (the same
-  recipe in exact arithmetic) within the bf16 bound, and the plain fp64 layer
-  on the unquantised inputs within 8e-2 * max|ref| -- or, for outputs where the
-  recipe's own quantisation error already exceeds that (gradients that pass
-  through several E5M2 operands), within that error plus the bf16 bound.
+  the plain fp64 layer on the unquantised inputs, the reference the fp8
+  tolerance is stated against, in two parts per output:
+  - the stated bound, max|diff| <= 8e-2 * max|ref|, wherever the recipe itself
+    (the same layer with quantised GEMM operands, in exact arithmetic) meets
+    it; where the recipe does not, no implementation of it can, and the test
+    reports the miss instead;
+  - the device's error is the recipe's error: RMS(got - ref) <= 1.05 *
+    RMS(recipe - ref) + 2e-3 * RMS(ref).  Both are realisations of the same
+    quantisation noise (the device's intermediates differ from the exact ones
+    in their last bf16 bit, which moves a few codes by one step and so changes
+    the realisation, not its size), so their RMS agree to within sampling
+    noise; a wrong scale, format or operand multiplies it.
+  An element-wise comparison with the quantised-operand reference is not a
+  test of the kernels beyond the first quantised intermediate: a relative
+  perturbation of 2^-10 in the stored intermediates alone moves that reference
+  by 0.04-0.09 * max|ref| on Y, dH and dX of a 256-token layer of hidden 512
+  (test_oracle_fp8_layer.py), more than the bf16 bound.  The kernels are
+  instead checked on identical codes, GEMM by GEMM, below and in the full-size
+  tests.
 """
+import os
+
 import numpy as np
 import pytest
 
@@ -134,16 +150,29 @@ def _rms(t):
     return float(np.sqrt(np.mean(np.square(t))))
 
 
+def fp8_two_part_check(name, got, ref, recipe_err_max, recipe_rms, ref_max, ref_rms):
+    """The two-part fp8 check of one output (see the module docstring);
+    returns (bad, line): bad is a reason string or None, line the table row."""
+    err = float(np.max(np.abs(got - ref)))
+    rms = _rms(got - ref)
+    recipe_meets = recipe_err_max <= FP8_REL * ref_max
+    line = (f"  {name:8s} device max|diff|/max|ref| {err / ref_max:.4f}  recipe {recipe_err_max / ref_max:.4f}  "
+            f"(8e-2: {'met' if err <= FP8_REL * ref_max else 'MISSED'}; recipe {'meets' if recipe_meets else 'misses'})"
+            f"  rms/rms(ref) device {rms / ref_rms:.4f} recipe {recipe_rms / ref_rms:.4f}")
+    if not np.all(np.isfinite(got)):
+        return "non-finite", line
+    if recipe_meets and err > FP8_REL * ref_max:
+        return f"max|diff| {err / ref_max:.4f} > 8e-2 where the recipe meets it", line
+    if rms > 1.05 * recipe_rms + 2e-3 * ref_rms:
+        return f"rms {rms / ref_rms:.4f} above the recipe's {recipe_rms / ref_rms:.4f}", line
+    return None, line
+
+
 @pytest.mark.gpu
 @pytest.mark.parametrize("case", list(FP8_CASES))
 def test_fp8_layer_error_is_the_recipe_error(mtl, case):
     """The whole layer in fp8 against the plain fp64 layer on the unquantised
-    inputs.  Requirement per output: max|diff| <= 8e-2 * max|ref|, or -- where
-    the recipe's own quantisation error (the quantised-operand reference against
-    the plain one) is already larger -- no more than 1.5 times that error; and
-    in RMS no more than 1.25 times the recipe's RMS error plus 1% of the
-    output's RMS.  A device result whose fp8 error is larger than the recipe's
-    (a wrong scale, operand or format) fails the RMS bound by far."""
+    inputs, by the two-part check of the module docstring."""
     from megatron_tensor_transformer_layer_amd.layer import run_sharded_layer
     shape, residual = FP8_CASES[case]
     print(f"fp8 case {case} {shape} residual={residual}", flush=True)
@@ -165,14 +194,12 @@ def test_fp8_layer_error_is_the_recipe_error(mtl, case):
                  dw2=cat("mlp_bwd", "dw2", 0), db_o=q["attn_bwd"][0]["db_o"], db2=q["mlp_bwd"][0]["db2"])
     bad = []
     for k, ref in ref_i.items():
-        scale = float(np.max(np.abs(ref)))
-        err = float(np.max(np.abs(got[k] - ref)))
-        recipe = float(np.max(np.abs(ref_q[k] - ref)))
-        rms_err, rms_recipe = _rms(got[k] - ref), _rms(ref_q[k] - ref)
-        print(f"  {k:7s} max|got-ref|/max {err / scale:.4f} (recipe {recipe / scale:.4f})  "
-              f"rms {rms_err / _rms(ref):.4f} (recipe {rms_recipe / _rms(ref):.4f})")
-        if err > max(FP8_REL * scale, 1.5 * recipe) or rms_err > 1.25 * rms_recipe + 0.01 * _rms(ref):
-            bad.append(k)
+        d = ref_q[k] - ref
+        why, line = fp8_two_part_check(k, got[k], ref, float(np.max(np.abs(d))), _rms(d),
+                                       float(np.max(np.abs(ref))), _rms(ref))
+        print(line)
+        if why:
+            bad.append(f"{k}: {why}")
     assert not bad, bad
 
 
@@ -218,3 +245,46 @@ def test_fp8_gemms_on_identical_codes(mtl):
                dw_o=F8.q4(O).T @ F8.q5(DH), db_o=DH.sum(axis=0))
     for k in ref:
         assert_bf16(k, got[k], ref[k])
+
+
+GOLDEN_7B = os.path.join(os.path.dirname(__file__), "golden", "fp8_layer_7b_tp4.npz")
+
+
+@pytest.mark.gpu
+def test_fp8_layer_full_size_7b_tp4(mtl):
+    """The fp8 variant of the 7B-class TP=4 layer at full size (hidden 4096,
+    32 heads, ffn 16384, seq 4096; all four shards and the four reductions on
+    one GPU, the step bench.py --workload 7b-tp4 --precision fp8 times one
+    shard of) against the stored fp64 reference on the unquantised inputs
+    (tests/golden/make_fp8_layer_7b_tp4.py, which calls only the oracle): the
+    two-part check of the module docstring on sampled rows of every output and
+    the whole bias gradients, the 8e-2 bound taken against each output's
+    whole-tensor max|ref|, the RMS against the recipe's RMS on the same rows."""
+    import torch
+    from megatron_tensor_transformer_layer_amd.layer import AllShardsStep, host_f64
+    gold = np.load(GOLDEN_7B)
+    shape = synth.WORKLOADS[str(gold["workload"])]
+    print(f"fp8 full-size layer {shape}", flush=True)
+    full = synth.layer_inputs(shape, seed=int(gold["seed"]))
+    shards = [synth.layer_inputs(shape, seed=int(gold["seed"]), tp=shape.tp, rank=r) for r in range(shape.tp)]
+    print("inputs drawn", flush=True)
+    step = AllShardsStep(shape, shape.tp, shards, full["x"], full["dy"], full["b_o"], full["b2"],
+                         precision=mtl.MTL_PREC_FP8_HYBRID)
+    step()
+    torch.cuda.synchronize()
+    rk = step.ranks
+    cat = lambda key, dim: torch.cat([getattr(r, key) for r in rk], dim=dim)
+    dev = dict(y=step.y, h=step.h, dh=step.dh, dx=step.dx, dw_qkv=cat("dw_qkv", 1), dw_o=cat("dw_o", 0),
+               dw1=cat("dw1", 1), dw2=cat("dw2", 0), db_qkv=cat("db_qkv", 0), db1=cat("db1", 0),
+               db_o=rk[0].db_o, db2=rk[0].db2)
+    bad = []
+    for k, t in dev.items():
+        ref = gold[f"{k}/ref"].astype(np.float64)
+        got = host_f64(t[torch.from_numpy(gold[f"{k}/rows"]).cuda()] if f"{k}/rows" in gold else t)
+        st = gold[f"{k}/stats"]  # whole tensor: max|ref|, rms ref, max|q-ref|, rms(q-ref); then on the samples
+        ref_max, recipe_max = float(st[0]), float(st[2])
+        why, line = fp8_two_part_check(k, got, ref, recipe_max, float(st[7]), ref_max, float(st[5]))
+        print(line, flush=True)
+        if why:
+            bad.append(f"{k}: {why}")
+    assert not bad, bad

@@ -5,9 +5,10 @@ seq 4096, TP=4) and of a 96-layer-GPT-shaped layer (hidden 8192, 64 heads, ffn
 32768, seq 4096, TP=8), rank 0.  Each block call of the C ABI is fed seeded
 synthetic inputs (x and dY, plus independent H and dH for the MLP and
 attention halves) and compared with the fp64 oracle of the rank's share:
-QKV, attention output and log-sum-exp, the attention-input gradient and the
-bias gradients in full; the large GEMM outputs on sampled rows (activations)
-or sampled columns (weight gradients), which the oracle computes one by one.
+QKV, attention output and log-sum-exp, the attention backward's dO and dQKV
+(read from the call's scratch) and the bias gradients in full; the large GEMM
+outputs on sampled rows (activations) or sampled columns (weight gradients),
+which the oracle computes one by one.
 """
 import numpy as np
 import pytest
@@ -47,6 +48,11 @@ def test_rank_shard_full_size(mtl, workload):
     torch.cuda.synchronize()
     g = {k: host_f64(getattr(st, k)) for k in ("qkv", "o", "lse", "gz", "a", "p_attn", "p_mlp", "p_dh", "p_dx",
                                                "dw_qkv", "db_qkv", "dw_o", "db_o", "dw1", "db1", "dw2", "db2")}
+    # the attention backward's own outputs, left in the scratch: dO and dQKV
+    off_do, off_dqkv = mtl.mtl_attn_bwd_scratch_layout(st.cfg)
+    D = st.D
+    sview = lambda off, cols: host_f64(st.scratch[off:off + D.S * cols * 2].view(torch.bfloat16).view(D.S, cols))
+    g["do"], g["dqkv"] = sview(off_do, D.o_l), sview(off_dqkv, D.qkv_l)
     del st
     torch.cuda.empty_cache()
 
@@ -85,9 +91,11 @@ def test_rank_shard_full_size(mtl, workload):
     assert_bf16("db2", g["db2"], DY.sum(axis=0))
     del z_full, a_full, dz_full
 
-    # attention backward: dqkv in full (through dx partial rows and its weight gradient)
+    # attention backward: dO and dQKV in full, then the products that take them
     do = DH @ p["w_o"].T
+    assert_bf16("do", g["do"], do)
     dqkv = L.attention_backward(qkv, do, lh)
+    assert_bf16("dqkv", g["dqkv"], dqkv)
     co = _cols(shape.hidden)
     assert_bf16("dw_o[:, cols]", g["dw_o"][:, co], o.T @ DH[:, co])
     assert_bf16("db_o", g["db_o"], DH.sum(axis=0))
@@ -104,7 +112,8 @@ def test_fp8_rank_shard_full_size(mtl):
     checked where its operands are call inputs (so both sides quantise the same
     bf16 values to the same codes) against the fp64 product of the dequantised
     codes: qkv in full, GeLU'(z) and a on sampled rows, dw2 and dw_o on sampled
-    columns, db1 (a column sum of the dgrad output dz) on sampled columns."""
+    columns, db1 (a column sum of the dgrad output dz) on sampled columns, and
+    dO (read from the attention backward's scratch) in full."""
     import torch
     from oracle import fp8_layer as F8
     from megatron_tensor_transformer_layer_amd.layer import RankState, bf16_dev, host_f64
@@ -131,6 +140,8 @@ def test_fp8_rank_shard_full_size(mtl):
     st.attn_bwd(dh, x)
     torch.cuda.synchronize()
     g.update(dw2=host_f64(st.dw2), db1=host_f64(st.db1), dw_o=host_f64(st.dw_o), db_o=host_f64(st.db_o))
+    off_do, _ = mtl.mtl_attn_bwd_scratch_layout(st.cfg)
+    g["do"] = host_f64(st.scratch[off_do:off_do + shape.seq * o_l * 2].view(torch.bfloat16).view(shape.seq, o_l))
     del st
     torch.cuda.empty_cache()
     print("device calls done", flush=True)
@@ -151,5 +162,58 @@ def test_fp8_rank_shard_full_size(mtl):
     assert_bf16("db1[cols]", g["db1"][cf], dz_c.sum(axis=0))
     del DYq
     DH = f64(dhb)
+    # dO = dH . w_o^T: the dgrad half of the output projection's fp8 pair launch
+    assert_bf16("do", g["do"], q5(DH) @ q4(f64(inp["w_o"])).T)
     assert_bf16("dw_o[:, cols]", g["dw_o"][:, ch], q4(f64(ob)).T @ q5(DH)[:, ch])
     assert_bf16("db_o", g["db_o"], DH.sum(axis=0))
+
+
+# The fp8 GEMMs of the 7B-class TP=4 rank (M, N, K, fmt A, fmt B, what it is),
+# each launched alone as the layer calls launch them; operands k-contiguous.
+FP8_GEMMS = [
+    (4096, 3072, 4096, 0, 0, "qkv forward (with bias)"),
+    (4096, 4096, 1024, 0, 0, "output projection forward"),
+    (4096, 4096, 4096, 0, 0, "fc2 forward"),
+    (4096, 4096, 4096, 1, 0, "fc1 dgrad"),
+    (4096, 4096, 3072, 1, 0, "qkv dgrad"),
+    (4096, 4096, 4096, 0, 1, "fc1 wgrad"),
+    (4096, 3072, 4096, 0, 1, "qkv wgrad"),
+]
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("case", range(len(FP8_GEMMS)))
+def test_fp8_gemm_full_size_identical_codes(mtl, case):
+    """Every fp8 GEMM shape of the 7B-class TP=4 rank whose operand inside the
+    layer calls is an intermediate (and so differs from the oracle's in its last
+    bits): here both operands are quantised from the same bf16 values on both
+    sides (the cast is bit-exact), and the device product, through the same
+    dispatch and tile choice, is compared with the fp64 product of the
+    dequantised codes on sampled rows and columns, within the bf16 bound."""
+    import torch
+    from oracle import fp8_layer as F8
+    from megatron_tensor_transformer_layer_amd.layer import bf16_dev, host_f64
+    M, N, K, fa, fb, what = FP8_GEMMS[case]
+    print(f"fp8 gemm {what}: {M}x{N}x{K} formats {fa},{fb}", flush=True)
+    ab = synth.mx_operand(M, K, "mx_a", 1.0, seed=40 + case)
+    bb = synth.mx_operand(N, K, "mx_b", 1.0 if fb == 1 else synth.WEIGHT_STD, seed=60 + case)
+    bias = synth.bf16_round_bits(np.random.default_rng(case).standard_normal(N) * synth.WEIGHT_STD) \
+        if case == 0 else None
+    dev = lambda bits: bf16_dev(bits)
+    qa = torch.empty(M, K, dtype=torch.uint8, device="cuda")
+    qb = torch.empty(N, K, dtype=torch.uint8, device="cuda")
+    ra = torch.empty(4, dtype=torch.float32, device="cuda")
+    rb = torch.empty(4, dtype=torch.float32, device="cuda")
+    ws = torch.empty(mtl.MTL_FP8_AMAX_SCRATCH, dtype=torch.uint8, device="cuda")
+    mtl.mtl_fp8_quantize(dev(ab), M, K, fa, ra, qa, None, ws)
+    mtl.mtl_fp8_quantize(dev(bb), N, K, fb, rb, qb, None, ws)
+    out = torch.empty(M, N, dtype=torch.float32 if fb == 1 else torch.bfloat16, device="cuda")
+    mtl.mtl_fp8_gemm(M, N, K, qa, fa, ra, qb, fb, rb, None if bias is None else dev(bias), out)
+    torch.cuda.synchronize()
+    got = host_f64(out)
+    q = lambda bits, f: (F8.q5 if f == 1 else F8.q4)(f64(bits))
+    A, B = q(ab, fa), q(bb, fb)
+    rows, cols = ROWS, _cols(N)
+    add = 0.0 if bias is None else f64(bias)
+    assert_bf16(f"{what} rows", got[rows], A[rows] @ B.T + add)
+    assert_bf16(f"{what} cols", got[:, cols], A @ B[cols].T + (0.0 if bias is None else f64(bias)[cols]))

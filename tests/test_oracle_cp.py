@@ -171,3 +171,25 @@ def test_dq_rows_match_the_rank_backward():
     local = [0, 5, 15]
     got = CP.dq_rows(qkv, do[local], heads, [r * c + i for i in local])
     assert np.allclose(got, g["dq"][local], rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("cp,rank,heads,d", [(4, 2, 2, 64), (3, 2, 1, 128), (2, 0, 3, 64)])
+def test_dkv_rows_equal_the_rank_backward(cp, rank, heads, d):
+    """The key-restricted backward gives the rank backward's dK/dV shares on
+    every key row it sees (chunks 0..rank), including the diagonal chunk."""
+    seq = 192
+    rng = np.random.default_rng(31 + rank)
+    qkv = rng.standard_normal((seq, 3 * heads * d)) * 1.3
+    c = seq // cp
+    do = rng.standard_normal((c, heads * d))
+    ref = CP.rank_attention_backward(qkv, do, heads, cp, rank)
+    full = np.concatenate(ref["dkv"], axis=0)  # key rows 0 .. (rank+1)*c - 1
+    keys = list(range((rank + 1) * c))
+    got = CP.dkv_rows(qkv, do, heads, cp, rank, keys, block=40)
+    assert np.max(np.abs(got - full)) <= 1e-12 * max(1.0, np.max(np.abs(full)))
+    with pytest.raises(ValueError):
+        CP.dkv_rows(qkv, do, heads, cp, rank, [(rank + 1) * c])
+    # a subset of heads gives those heads' columns
+    last = heads - 1
+    sub = CP.dkv_rows(qkv, do, heads, cp, rank, keys[::7], head_ids=[last], block=64)
+    assert np.max(np.abs(sub - full[::7, 2 * last * d:(2 * last + 2) * d])) <= 1e-12 * max(1.0, np.max(np.abs(full)))
