@@ -284,10 +284,11 @@ struct Mainloop {
     // (each reload right after its chunk's write).
     constexpr int NR = (TM * OA::READS + TN * OB::READS) * NF;  // LDS reads per step
     constexpr int NM = TM * TN;                                 // MFMAs per step
-    constexpr int NW = STAGE ? NC / KSTEPS : 0;                 // chunk writes (and loads) per step
-    constexpr int STEP = NW == 0 ? NM + 1 : (NM / (2 * NW) > 0 ? NM / (2 * NW) : 1);
 #pragma unroll
     for (int kk = 0; kk < KSTEPS; ++kk) {
+      // this step's chunk writes (and loads): the chunks staged in it above
+      const int NW = STAGE ? (kk + 1) * NC / KSTEPS - kk * NC / KSTEPS : 0;
+      const int STEP = NW == 0 ? NM + 1 : (NM / (2 * NW) > 0 ? NM / (2 * NW) : 1);
       if (FIRST && kk == 0) {
         __builtin_amdgcn_sched_group_barrier(0x100, NR, 0);
 #pragma unroll
@@ -420,6 +421,12 @@ __device__ __forceinline__ void gemm_tile(GemmArgs p, const int bid, LDS_AS char
       ML::OA::zero_tail(st1, p.K - KSLAB);
       ML::OB::zero_tail(st1 + ML::OA::BYTES, p.K - KSLAB);
     }
+    // No load in flight on entry to the loop: the staging loads of the peeled
+    // slab above are issued in a different order than the loop's, and the
+    // compiler, merging both orders at the loop head, would otherwise wait in
+    // every iteration for the youngest of them (vmcnt(4) instead of vmcnt(15)
+    // before the fifth chunk write of a 256 x 256 tile).
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
     __syncthreads();
     for (int kt = 1; kt + 1 < nk; ++kt) {
       const bool odd = kt & 1;
