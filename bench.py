@@ -733,9 +733,11 @@ def all_shards_cpu_baseline(shape):
 def all_shards_main(args, shape):
     """The whole small layer on one GPU: every TP shard's forward and backward
     plus the four full reductions standing in for the all-reduces, timed as
-    one step.  At this size each launch is a few microseconds of work, so the
-    step is launch-bound; it is timed captured in a HIP graph (replayed K
-    times) and, for comparison, launched eagerly."""
+    one step.  At this size a launch is a few microseconds of work on a
+    fraction of the chip, so the shards run side by side, each on a stream of
+    its own, and the step is captured in a HIP graph (replayed K times); the
+    line also gives the step launched eagerly, with the shards concurrent and
+    one after the other."""
     import torch
     import synth
     from megatron_tensor_transformer_layer_amd.layer import AllShardsStep
@@ -744,10 +746,13 @@ def all_shards_main(args, shape):
     t = shape.tp
     full = synth.layer_inputs(shape, seed=0)
     shards = [synth.layer_inputs(shape, seed=0, tp=t, rank=r) for r in range(t)]
-    step = AllShardsStep(shape, t, shards, full["x"], full["dy"], full["b_o"], full["b2"])
-
+    serial = AllShardsStep(shape, t, shards, full["x"], full["dy"], full["b_o"], full["b2"])
+    eager_serial_ms = timed_steps(serial, args.steps, args.warmup)
+    groups, kinds = prof_window(serial, 5)  # per-group times with the shards one after the other
+    del serial
+    # the product form: each shard on its own stream, the step captured as one graph
+    step = AllShardsStep(shape, t, shards, full["x"], full["dy"], full["b_o"], full["b2"], concurrent=True)
     eager_ms = timed_steps(step, args.steps, args.warmup)
-    groups, kinds = prof_window(step, 5)
     # capture one step on a side stream (torch makes it current inside the context)
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
@@ -772,17 +777,20 @@ def all_shards_main(args, shape):
         "data": "synthetic (seeded N(0,1) activations, N(0,0.02) weights)",
         "config": {"workload": f"{args.workload}: the whole layer, all {t} TP shards and the four full reductions "
                                f"on one GPU, hidden {shape.hidden}, heads {shape.heads}, ffn {shape.ffn}, "
-                               f"seq {shape.seq}, micro-batch {shape.micro_batch}; the step replayed as one HIP graph",
+                               f"seq {shape.seq}, micro-batch {shape.micro_batch}; the shards on concurrent streams, "
+                               f"the step replayed as one HIP graph",
                    "global_batch": shape.micro_batch, "seq_len": shape.seq,
                    "parallelism": f"tp{t}-all-shards-1gpu"},
         "pct_of_peak": round(100 * fl["total"] / (graph_ms / 1e3) / 1e12 / PEAK_BF16_TFLOPS, 2),
         "flop_per_step": fl["total"],
-        "eager_ms_per_step": round(eager_ms, 4),
-        "graph_ms_per_step": round(graph_ms, 4),
+        "eager_serial_ms_per_step": round(eager_serial_ms, 4),
+        "eager_concurrent_ms_per_step": round(eager_ms, 4),
+        "graph_concurrent_ms_per_step": round(graph_ms, 4),
         "launch_groups_per_step": launches,
         **win,
         **{k: v for k, v in bd.items() if k != "groups"},
-        "roofline": {"bound": "mfma", "kernel": "every GEMM launch of the step (HIP events, eager launches)",
+        "roofline": {"bound": "mfma", "kernel": "every GEMM launch of the step (HIP events, eager launches, shards "
+                                                "one after the other)",
                      "achieved": bd["gemm_tflops"], "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": bd["gemm_frac_of_peak"], "traffic": None},
         "cpu_baseline": None if args.no_cpu_baseline else all_shards_cpu_baseline(shape),

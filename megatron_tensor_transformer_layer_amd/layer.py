@@ -206,29 +206,42 @@ class AllShardsStep:
     """The whole layer on one device as one callable step: every TP rank's
     forward and backward plus the four full reductions, on fixed buffers (so the
     step can be captured into a HIP graph and replayed).  shards: per-rank
-    inputs; x, dy, b_o, b2: bf16 bit patterns of the full tensors."""
+    inputs; x, dy, b_o, b2: bf16 bit patterns of the full tensors.  With
+    concurrent, each rank's calls go to a stream of its own (forked from and
+    joined back into the current stream around every phase), so the shards'
+    small launches run side by side instead of one after the other."""
 
     def __init__(self, shape, tp: int, shards: list, x_bits, dy_bits, b_o_bits, b2_bits, device=DEV,
-                 precision: int = MTL_PREC_BF16):
+                 precision: int = MTL_PREC_BF16, concurrent: bool = False):
         self.ranks = [RankState(shape, tp, r, shards[r], device=device, precision=precision) for r in range(tp)]
         D = self.D = self.ranks[0].D
         self.x, self.dy = bf16_dev(x_bits, device), bf16_dev(dy_bits, device)
         self.b_o, self.b2 = bf16_dev(b_o_bits, device), bf16_dev(b2_bits, device)
         self.h, self.y, self.dh, self.dx = (empty_bf16(D.S, D.h, device=device) for _ in range(4))
+        self.streams = [torch.cuda.Stream(device=device) for _ in range(tp)] if concurrent else None
+
+    def _per_rank(self, fn):
+        if self.streams is None:
+            for r in self.ranks:
+                fn(r)
+            return
+        main = torch.cuda.current_stream()
+        for r, s in zip(self.ranks, self.streams):
+            s.wait_stream(main)
+            with torch.cuda.stream(s):
+                fn(r)
+        for s in self.streams:
+            main.wait_stream(s)
 
     def __call__(self):
         rk, D = self.ranks, self.D
-        for r in rk:
-            r.attn_fwd(self.x)
+        self._per_rank(lambda r: r.attn_fwd(self.x))
         mtl_reduce([r.p_attn for r in rk], self.b_o, None, self.h, D.S, D.h)
-        for r in rk:
-            r.mlp_fwd(self.h)
+        self._per_rank(lambda r: r.mlp_fwd(self.h))
         mtl_reduce([r.p_mlp for r in rk], self.b2, None, self.y, D.S, D.h)
-        for r in rk:
-            r.mlp_bwd(self.dy, self.h, want_db2=r is rk[0])
+        self._per_rank(lambda r: r.mlp_bwd(self.dy, self.h, want_db2=r is rk[0]))
         mtl_reduce([r.p_dh for r in rk], None, None, self.dh, D.S, D.h)
-        for r in rk:
-            r.attn_bwd(self.dh, self.x, want_db_o=r is rk[0])
+        self._per_rank(lambda r: r.attn_bwd(self.dh, self.x, want_db_o=r is rk[0]))
         mtl_reduce([r.p_dx for r in rk], None, None, self.dx, D.S, D.h)
 
     def outputs(self) -> dict:

@@ -13,11 +13,11 @@ def _snapshot(outs):
 
 
 @pytest.mark.gpu
-@pytest.mark.parametrize("case", ["gpt2-small-tp2", "ragged-tp2-fp8"])
+@pytest.mark.parametrize("case", ["gpt2-small-tp2", "ragged-tp2-fp8", "gpt2-small-tp2-concurrent"])
 def test_graph_replays_match_eager_step(mtl, case):
     import torch
     from megatron_tensor_transformer_layer_amd.layer import AllShardsStep
-    if case == "gpt2-small-tp2":
+    if case.startswith("gpt2-small-tp2"):
         shape, prec = synth.WORKLOADS["gpt2-small-tp2"], mtl.MTL_PREC_BF16
     else:
         shape, prec = synth.LayerShape(hidden=256, heads=2, ffn=544, seq=208, micro_batch=1, tp=2), \
@@ -25,10 +25,18 @@ def test_graph_replays_match_eager_step(mtl, case):
     print(f"graph case {case} {shape}", flush=True)
     full = synth.layer_inputs(shape, seed=0)
     shards = [synth.layer_inputs(shape, seed=0, tp=shape.tp, rank=r) for r in range(shape.tp)]
-    step = AllShardsStep(shape, shape.tp, shards, full["x"], full["dy"], full["b_o"], full["b2"], precision=prec)
+    step = AllShardsStep(shape, shape.tp, shards, full["x"], full["dy"], full["b_o"], full["b2"], precision=prec,
+                         concurrent=case.endswith("concurrent"))
     step()
     torch.cuda.synchronize()
     eager = _snapshot(step.outputs())
+    if step.streams is not None:  # the concurrent step equals the shards run one after the other
+        serial = AllShardsStep(shape, shape.tp, shards, full["x"], full["dy"], full["b_o"], full["b2"],
+                               precision=prec)
+        serial()
+        torch.cuda.synchronize()
+        assert all(torch.equal(serial.outputs()[k], eager[k]) for k in eager)
+        del serial
 
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
