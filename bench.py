@@ -53,8 +53,9 @@ def parse():
     ap.add_argument("--workload", default="gpt96l-tp8")
     ap.add_argument("--rank", type=int, default=None,
                     help="the rank whose share runs (default 0; for a CP workload the last, busiest rank)")
-    ap.add_argument("--precision", choices=("bf16", "fp8"), default="bf16",
-                    help="fp8: the linears' GEMMs on per-tensor scaled E4M3/E5M2 codes (--fp8-format hybrid)")
+    ap.add_argument("--precision", choices=("bf16", "fp8", "mxfp4"), default="bf16",
+                    help="fp8: the linears' GEMMs on per-tensor scaled E4M3/E5M2 codes (--fp8-format hybrid); "
+                         "mxfp4: on MXFP4 codes blocked along each product's contraction")
     ap.add_argument("--sp", action="store_true",
                     help="sequence parallel: X, H, dY, dH arrive as row shares and are gathered in place "
                          "(mtl_allgather_rows) before each column-parallel linear")
@@ -124,15 +125,17 @@ def copy_rate():
         del src, dst
 
 
-def cpu_baseline(shape, rank, sample_seq, fp8=False):
+def cpu_baseline(shape, rank, sample_seq, precision="bf16"):
     """The oracle (fp64 numpy, as it stands) on a bounded sample: the same rank's
-    forward + backward over the first sample_seq tokens (for fp8, the reference
-    with quantised GEMM operands)."""
+    forward + backward over the first sample_seq tokens (for fp8 and mxfp4, the
+    reference with quantised GEMM operands)."""
     import synth
     from oracle import layer as L
     from oracle import shard as S
-    if fp8:
+    if precision == "fp8":
         from oracle import fp8_layer as S  # noqa: F811 -- same rank functions, quantised operands
+    elif precision == "mxfp4":
+        from oracle import mx_layer as S  # noqa: F811
 
     try:
         from threadpoolctl import threadpool_info
@@ -155,7 +158,8 @@ def cpu_baseline(shape, rank, sample_seq, fp8=False):
     flops = L.layer_flops(shape.hidden, shape.heads, shape.ffn, sample_seq, 1, shape.tp)["total"]
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
             "sample": f"rank {rank} shard forward+backward on the first {sample_seq} of {shape.seq} tokens "
-                      f"(fp64 numpy{', fp8 quant-dequant operands' if fp8 else ''}), {dt:.2f} s"}
+                      f"(fp64 numpy{'' if precision == 'bf16' else ', ' + precision + ' quant-dequant operands'}), "
+                      f"{dt:.2f} s"}
 
 
 def moe_cpu_baseline(shape, rank, sample_tokens, sample_ffn):
@@ -819,8 +823,10 @@ def dense_main(args):
     if t > 1 and shape.seq * shape.micro_batch % t:
         raise SystemExit("the reduce-scatter shares need S % t == 0")
     inp = synth.layer_inputs(shape, tp=t, rank=r)
-    fp8 = args.precision == "fp8"
-    st = RankState(shape, t, r, inp, precision=MTL_PREC_FP8_HYBRID if fp8 else MTL_PREC_BF16)
+    fp8, mx = args.precision == "fp8", args.precision == "mxfp4"
+    from megatron_tensor_transformer_layer_amd import MTL_PREC_MXFP4
+    st = RankState(shape, t, r, inp, precision={"bf16": MTL_PREC_BF16, "fp8": MTL_PREC_FP8_HYBRID,
+                                                 "mxfp4": MTL_PREC_MXFP4}[args.precision])
     D = st.D
     x = bf16_dev(inp["x"])
     dy = bf16_dev(inp["dy"])
@@ -861,7 +867,7 @@ def dense_main(args):
     win = windows(step, 3, max(20, args.steps))
 
     fl = layer_flops(shape.hidden, shape.heads, shape.ffn, shape.seq, shape.micro_batch, t)
-    peak = PEAK_FP8_TFLOPS if fp8 else PEAK_BF16_TFLOPS
+    peak = PEAK_FP8_TFLOPS if fp8 else (PEAK_FP4_TFLOPS if mx else PEAK_BF16_TFLOPS)
     bd = breakdown(groups, kinds, peak)
     # the roofline kernel: the GEMM launch group that takes the most time per step
     dom = max((n for n, v in groups.items() if v["kind"] == "gemm"), key=lambda n: groups[n]["ms"])
@@ -870,6 +876,7 @@ def dense_main(args):
     achieved = dg["flop"] / dg["launches"] / (per_launch_ms / 1e3) / 1e12
     out = {
         "metric": ("TFLOP/s per TP-shard layer fwd+bwd (fp8 hybrid GEMMs) and % of MI355X MFMA peak" if fp8 else
+                   "TFLOP/s per TP-shard layer fwd+bwd (MXFP4 GEMMs) and % of MI355X MFMA peak" if mx else
                    "TFLOP/s per TP-shard layer fwd+bwd (bf16) and % of MI355X MFMA peak"),
         "value": round(fl["total"] / (ms / 1e3) / 1e12, 2),
         "unit": "TFLOP/s",
@@ -880,13 +887,15 @@ def dense_main(args):
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "fp8" if fp8 else "bf16",
+        "dtype": args.precision,
         "data": "synthetic (seeded N(0,1) activations, N(0,0.02) weights)",
         "config": {"workload": f"{args.workload}: rank {r} of TP={t}, hidden {shape.hidden}, heads {shape.heads} "
                                f"({shape.heads // t} local), ffn {shape.ffn} ({shape.ffn // t} local), "
                                f"seq {shape.seq}, micro-batch {shape.micro_batch}"
                                + (", fp8 hybrid (E4M3 activations/weights, E5M2 gradients, per-tensor current "
                                   "scaling; attention bf16)" if fp8 else "")
+                               + (", MXFP4 GEMMs (E2M1 in blocks of 32 along each product's contraction, E8M0 "
+                                  "scales; attention bf16)" if mx else "")
                                + (", sequence parallel (reduce-scatter shares, in-place all-gathers of X, H, dY, dH)"
                                   if args.sp else ", each all-reduce as the rank's reduce-scatter share plus the "
                                                   "all-gather of the peers' shares"),
@@ -898,7 +907,8 @@ def dense_main(args):
         **win,
         **{k: v for k, v in bd.items() if k != "groups"},
         "launch_groups": bd["groups"],
-        "roofline": {"bound": "mfma", "kernel": f"{dom}: {GROUP_KERNEL.get(dom, dom)}",
+        "roofline": {"bound": "mfma", "kernel": (f"{dom}: {GROUP_KERNEL.get(dom, dom)}" if args.precision == "bf16"
+                                                 else f"{dom}: the {args.precision} GEMM launch group of that name"),
                      "achieved": round(achieved, 1), "peak": peak, "unit": "TFLOP/s",
                      "frac": round(achieved / peak, 4),
                      "traffic": stored_traffic(args.workload, dom, args.precision),
@@ -906,13 +916,13 @@ def dense_main(args):
                      "launch_us": round(per_launch_ms * 1e3, 2)},
         "cpu_baseline": None,
     }
-    if fp8:
+    if fp8 or mx:
         q = kinds.get("quantize", dict(ms=0.0))
         out["quantize_us_per_step"] = round(q["ms"] * 1e3, 1)
         g8 = kinds.get("gemm")
         out["gemm_frac_of_bf16_peak"] = round(g8["flop"] / (g8["ms"] / 1e3) / 1e12 / PEAK_BF16_TFLOPS, 4)
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(shape, r, min(args.cpu_sample_seq, shape.seq), fp8)
+        out["cpu_baseline"] = cpu_baseline(shape, r, min(args.cpu_sample_seq, shape.seq), args.precision)
     print(json.dumps(out), flush=True)
 
 

@@ -61,7 +61,7 @@ typedef enum mtl_status {
   MTL_E_HIP = 8           /* a HIP launch failed (no device, bad stream, ...) */
 } mtl_status;
 
-enum { MTL_PREC_BF16 = 0, MTL_PREC_FP8_HYBRID = 1 };
+enum { MTL_PREC_BF16 = 0, MTL_PREC_FP8_HYBRID = 1, MTL_PREC_MXFP4 = 2 };
 enum { MTL_FP8_E4M3 = 0, MTL_FP8_E5M2 = 1 };
 #define MTL_FP8_AMAX_SCRATCH 4096 /* bytes of scratch mtl_fp8_amax needs */
 
@@ -90,9 +90,11 @@ const char* mtl_status_str(mtl_status s);
  * (ffn/tp) % 8 == 0 (MTL_E_SHAPE otherwise: the attention kernels are built for
  * those head sizes and the GEMMs move 16-byte vectors); tp <= 16; every GEMM
  * operand under 4 GiB: (max(S, w) + 256) * w * 2 < 2^32 bytes with
- * w = max(h, 3h/t, f/t).  precision MTL_PREC_BF16 or MTL_PREC_FP8_HYBRID; the
- * latter also needs S % 16 == 0 and (ffn/tp) % 16 == 0 (fp8 GEMMs contract over
- * 16-byte chunks of codes). */
+ * w = max(h, 3h/t, f/t).  precision MTL_PREC_BF16, MTL_PREC_FP8_HYBRID or
+ * MTL_PREC_MXFP4; fp8 also needs S % 16 == 0 and (ffn/tp) % 16 == 0 (fp8 GEMMs
+ * contract over 16-byte chunks of codes); MXFP4 needs S, h, h/t, 3h/t and f/t
+ * all multiples of 256 (every GEMM dimension a multiple of the MX GEMM's
+ * 128-row tiles, every contraction a multiple of its 256-deep K slabs). */
 mtl_status mtl_validate(const mtl_layer_cfg* cfg);
 
 /* Bytes of device scratch (*scratch_bytes) that suffice for every call of this
@@ -112,7 +114,17 @@ mtl_status mtl_workspace_bytes(const mtl_layer_cfg* cfg, size_t* scratch_bytes);
  * operand is quantised per tensor (mtl_fp8_amax + mtl_fp8_cast) -- E4M3 for
  * activations and weights, E5M2 for gradients -- the product accumulates in
  * fp32 and is multiplied by both operands' 1/s in the epilogue; outputs, bias,
- * GeLU, attention and the reductions stay bf16/fp32 as in the bf16 path. */
+ * GeLU, attention and the reductions stay bf16/fp32 as in the bf16 path.
+ *
+ * MXFP4 (MTL_PREC_MXFP4, the site summary's 4-bit training read as OCP MXFP4,
+ * see mtl_mxfp4_quantize): every GEMM of the four linears, forward, dgrad and
+ * wgrad, takes both operands quantised to MXFP4 with the 32-element blocks
+ * along that GEMM's contraction (mtl_mxfp4_quantize for an operand whose K runs
+ * along its rows, mtl_mxfp4_quantize_t for one whose K runs down its columns:
+ * a weight in the forward, the activations and gradients in a weight
+ * gradient) and multiplies them on the block-scaled MFMA with fp32
+ * accumulation and the same epilogues (bias, GeLU, GeLU', fp32 wgrad) as the
+ * bf16 path; attention, the bias gradients and the reductions stay bf16/fp32. */
 mtl_status mtl_attn_fwd(const mtl_layer_cfg* cfg, const void* x, const void* w_qkv, const void* b_qkv,
                         const void* w_o, void* qkv, void* o, float* lse, void* partial, void* scratch,
                         size_t scratch_bytes, mtl_stream_t stream);
@@ -218,6 +230,17 @@ mtl_status mtl_mxfp4_quantize(const void* x, int64_t rows, int64_t cols, void* c
  * == 0.  Errors: MTL_E_NULL, MTL_E_ALIGN, MTL_E_SHAPE. */
 mtl_status mtl_mxfp4_gemm(int64_t M, int64_t N, int64_t K, const void* a_codes, const void* a_scales,
                           const void* b_codes, const void* b_scales, void* c, int64_t ldc, mtl_stream_t stream);
+
+/* MXFP4 quantisation along the rows of x [rows, cols] (blocks of 32 rows of
+ * one column, the scale rule and rounding of mtl_mxfp4_quantize): the codes and
+ * scales of x^T, codes [cols, rows/2] bytes and scales [cols, rows/32] bytes,
+ * as mtl_mxfp4_gemm takes an operand whose K runs down the columns of a
+ * row-major tensor (a weight W [K, N] in a forward product, an activation or
+ * gradient [tokens, features] in a weight-gradient product).  rows % 32 == 0,
+ * cols % 8 == 0, rows <= 2^23; pointers 16-byte aligned.  Errors: MTL_E_NULL,
+ * MTL_E_ALIGN, MTL_E_SHAPE. */
+mtl_status mtl_mxfp4_quantize_t(const void* x, int64_t rows, int64_t cols, void* codes, void* scales,
+                                mtl_stream_t stream);
 
 /* MXFP6: the same as mtl_mxfp4_quantize / mtl_mxfp4_gemm with FP6 E2M3 elements
  * (sign, 2 exponent bits of bias 1, 3 mantissa bits; magnitudes k/8 below 1,

@@ -18,7 +18,7 @@ HEADER = os.path.join(os.path.dirname(HERE), "include", "mtl.h")
 
 MTL_OK, MTL_E_NULL, MTL_E_DIVISIBILITY, MTL_E_RANK, MTL_E_SHAPE = 0, 1, 2, 3, 4
 MTL_E_ALIGN, MTL_E_WORKSPACE, MTL_E_UNSUPPORTED, MTL_E_HIP = 5, 6, 7, 8
-MTL_PREC_BF16, MTL_PREC_FP8_HYBRID = 0, 1
+MTL_PREC_BF16, MTL_PREC_FP8_HYBRID, MTL_PREC_MXFP4 = 0, 1, 2
 MTL_FP8_E4M3, MTL_FP8_E5M2 = 0, 1
 MTL_FP8_AMAX_SCRATCH = 4096
 MTL_CP_MAX = 64
@@ -59,6 +59,7 @@ _SIGS = {
     "mtl_cp_attn_fwd": (ctypes.c_int, [_I32, _I32, _I64, _I32, _I32, ctypes.POINTER(_P), _P, _P, _P, _SZ, _P]),
     "mtl_mxfp4_quantize": (ctypes.c_int, [_P, _I64, _I64, _P, _P, _P]),
     "mtl_mxfp4_gemm": (ctypes.c_int, [_I64, _I64, _I64, _P, _P, _P, _P, _P, _I64, _P]),
+    "mtl_mxfp4_quantize_t": (ctypes.c_int, [_P, _I64, _I64, _P, _P, _P]),
     "mtl_mxfp6_quantize": (ctypes.c_int, [_P, _I64, _I64, _P, _P, _P]),
     "mtl_mxfp6_gemm": (ctypes.c_int, [_I64, _I64, _I64, _P, _P, _P, _P, _P, _I64, _P]),
     "mtl_cp_attn_bwd_scratch_bytes": (ctypes.c_int, [_I32, _I32, _I64, _I32, _I32, ctypes.POINTER(_SZ)]),
@@ -208,6 +209,11 @@ def mtl_cp_attn_bwd(cp, rank, chunk, heads, head_dim, qkv_chunks, o, lse, dout, 
 def mtl_mxfp4_quantize(x, rows, cols, codes, scales, stream=None):
     _check(lib().mtl_mxfp4_quantize(_ptr(x), rows, cols, _ptr(codes), _ptr(scales), _stream(stream)),
            "mtl_mxfp4_quantize")
+
+
+def mtl_mxfp4_quantize_t(x, rows, cols, codes, scales, stream=None):
+    _check(lib().mtl_mxfp4_quantize_t(_ptr(x), rows, cols, _ptr(codes), _ptr(scales), _stream(stream)),
+           "mtl_mxfp4_quantize_t")
 
 
 def mtl_mxfp4_gemm(M, N, K, a_codes, a_scales, b_codes, b_scales, c, ldc=None, stream=None):

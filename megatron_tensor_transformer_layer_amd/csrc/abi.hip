@@ -182,12 +182,65 @@ hipError_t gemm8_pair(const char* name, const GemmArgs& gw, int ew, const GemmAr
                      [&] { return gemm_fp8_pair(gw, ew, gd, ed, s); });
 }
 
+// An MXFP4 copy of one GEMM operand, K-contiguous: codes [rows, k/2] bytes and
+// scales [rows, k/32] (k = the GEMM's contraction).
+struct MX4 {
+  uint8_t* q;
+  uint8_t* s;
+  int64_t rows, k;
+};
+MX4 mx4(Bump& b, int64_t rows, int64_t k) {
+  MX4 m{};
+  m.q = b.take<uint8_t>(rows * k / 2);
+  m.s = b.take<uint8_t>(rows * k / 32);
+  m.rows = rows;
+  m.k = k;
+  return m;
+}
+inline double mx4_bytes(const MX4& m) { return (double)m.rows * m.k * (2.0 + 0.5 + 1.0 / 32); }
+// x [rows, k] quantised along its rows into m ([rows, k])
+hipError_t mxq(const void* x, const MX4& m, hipStream_t s) {
+  return prof::timed(prof::QUANT, "mx_quantize_rows", 0, mx4_bytes(m), s,
+                     [&] { return mxfp4_quantize(static_cast<const uint16_t*>(x), m.rows, m.k, m.q, m.s, s); });
+}
+// x [k, rows] quantised down its columns into m ([rows, k] = x^T)
+hipError_t mxqt(const void* x, const MX4& m, hipStream_t s) {
+  return prof::timed(prof::QUANT, "mx_quantize_cols", 0, mx4_bytes(m), s,
+                     [&] { return mxfp4_quantize_t(static_cast<const uint16_t*>(x), m.k, m.rows, m.q, m.s, s); });
+}
+// C [a.rows, b.rows] = A . B^T on MXFP4 codes, epilogue epi (fp32 C for the wgrad epilogues)
+hipError_t mxgemm(const char* name, const MX4& a, const MX4& b, int epi, void* c, hipStream_t s,
+                  const void* bias = nullptr, void* c2 = nullptr, const void* aux = nullptr) {
+  Mxfp4GemmArgs g{};
+  g.a = a.q;
+  g.sa = a.s;
+  g.b = b.q;
+  g.sb = b.s;
+  g.M = (int)a.rows;
+  g.N = (int)b.rows;
+  g.K = (int)a.k;
+  g.ldc = b.rows;
+  g.epi = epi;
+  const bool f32 = epi == EPI_F32 || epi == EPI_F32_ACC;
+  if (f32) g.c32 = static_cast<float*>(c);
+  else g.c = static_cast<uint16_t*>(c);
+  g.bias = static_cast<const uint16_t*>(bias);
+  g.c2 = static_cast<uint16_t*>(c2);
+  g.aux = static_cast<const uint16_t*>(aux);
+  const int out_b = f32 ? 4 : (epi == EPI_BIAS_GELU ? 4 : 2);
+  return prof::timed(prof::GEMM, name, gemm_flop(a.rows, b.rows, a.k),
+                     (a.rows + b.rows) * (a.k / 2.0 + a.k / 32.0) + (double)out_b * a.rows * b.rows, s,
+                     [&] { return mxfp4_gemm(g, s); });
+}
+
 struct MlpScratch {
   uint16_t* dz;
   float* ws;
   // fp8 copies
   Q8 dy, w2, a_t, dz8, h_t, w1;
   void* amax_ws;
+  // MXFP4 copies
+  MX4 m_dy, m_dy_t, m_w2, m_a_t, m_dz, m_dz_t, m_h_t, m_w1;
 };
 struct AttnScratch {
   uint16_t* dout;
@@ -196,17 +249,21 @@ struct AttnScratch {
   float* ws;
   Q8 dh, wo, o_t, dqkv8, x_t, wqkv;
   void* amax_ws;
+  MX4 m_dh, m_dh_t, m_wo, m_o_t, m_dqkv, m_dqkv_t, m_x_t, m_wqkv;
 };
 struct AttnFwdScratch {
   Q8 x, wqkv_t, o, wo_t;
   void* amax_ws;
+  MX4 m_x, m_wqkv_t, m_o, m_wo_t;
 };
 struct MlpFwdScratch {
   Q8 h, w1_t, a, w2_t;
   void* amax_ws;
+  MX4 m_h, m_w1_t, m_a, m_w2_t;
 };
 
 inline bool is_fp8(const mtl_layer_cfg* c) { return c->precision == MTL_PREC_FP8_HYBRID; }
+inline bool is_mx4(const mtl_layer_cfg* c) { return c->precision == MTL_PREC_MXFP4; }
 
 size_t mlp_scratch(const mtl_layer_cfg* c, const Dims& d, MlpScratch* s, char* base) {
   Bump b{base};
@@ -221,6 +278,16 @@ size_t mlp_scratch(const mtl_layer_cfg* c, const Dims& d, MlpScratch* s, char* b
     t.h_t = q8(b, d.S, d.h, E4M3, false, true);
     t.w1 = q8(b, d.h, d.f_l, E4M3, true, false);
     t.amax_ws = b.take<char>(fp8_amax_ws_bytes());
+  }
+  if (is_mx4(c)) {
+    t.m_dy = mx4(b, d.S, d.h);
+    t.m_dy_t = mx4(b, d.h, d.S);
+    t.m_w2 = mx4(b, d.f_l, d.h);
+    t.m_a_t = mx4(b, d.f_l, d.S);
+    t.m_dz = mx4(b, d.S, d.f_l);
+    t.m_dz_t = mx4(b, d.f_l, d.S);
+    t.m_h_t = mx4(b, d.h, d.S);
+    t.m_w1 = mx4(b, d.h, d.f_l);
   }
   if (s) *s = t;
   return b.off;
@@ -242,32 +309,56 @@ size_t attn_scratch(const mtl_layer_cfg* c, const Dims& d, AttnScratch* s, char*
     t.wqkv = q8(b, d.h, d.qkv_l, E4M3, true, false);
     t.amax_ws = b.take<char>(fp8_amax_ws_bytes());
   }
+  if (is_mx4(c)) {
+    t.m_dh = mx4(b, d.S, d.h);
+    t.m_dh_t = mx4(b, d.h, d.S);
+    t.m_wo = mx4(b, d.o_l, d.h);
+    t.m_o_t = mx4(b, d.o_l, d.S);
+    t.m_dqkv = mx4(b, d.S, d.qkv_l);
+    t.m_dqkv_t = mx4(b, d.qkv_l, d.S);
+    t.m_x_t = mx4(b, d.h, d.S);
+    t.m_wqkv = mx4(b, d.h, d.qkv_l);
+  }
   if (s) *s = t;
   return b.off;
 }
 
 size_t attn_fwd_scratch(const mtl_layer_cfg* c, const Dims& d, AttnFwdScratch* s, char* base) {
-  if (!is_fp8(c)) return 0;
+  if (!is_fp8(c) && !is_mx4(c)) return 0;
   Bump b{base};
   AttnFwdScratch t{};
-  t.x = q8(b, d.S, d.h, E4M3, true, false);
-  t.wqkv_t = q8(b, d.h, d.qkv_l, E4M3, false, true);
-  t.o = q8(b, d.S, d.o_l, E4M3, true, false);
-  t.wo_t = q8(b, d.o_l, d.h, E4M3, false, true);
-  t.amax_ws = b.take<char>(fp8_amax_ws_bytes());
+  if (is_fp8(c)) {
+    t.x = q8(b, d.S, d.h, E4M3, true, false);
+    t.wqkv_t = q8(b, d.h, d.qkv_l, E4M3, false, true);
+    t.o = q8(b, d.S, d.o_l, E4M3, true, false);
+    t.wo_t = q8(b, d.o_l, d.h, E4M3, false, true);
+    t.amax_ws = b.take<char>(fp8_amax_ws_bytes());
+  } else {
+    t.m_x = mx4(b, d.S, d.h);
+    t.m_wqkv_t = mx4(b, d.qkv_l, d.h);
+    t.m_o = mx4(b, d.S, d.o_l);
+    t.m_wo_t = mx4(b, d.h, d.o_l);
+  }
   if (s) *s = t;
   return b.off;
 }
 
 size_t mlp_fwd_scratch(const mtl_layer_cfg* c, const Dims& d, MlpFwdScratch* s, char* base) {
-  if (!is_fp8(c)) return 0;
+  if (!is_fp8(c) && !is_mx4(c)) return 0;
   Bump b{base};
   MlpFwdScratch t{};
-  t.h = q8(b, d.S, d.h, E4M3, true, false);
-  t.w1_t = q8(b, d.h, d.f_l, E4M3, false, true);
-  t.a = q8(b, d.S, d.f_l, E4M3, true, false);
-  t.w2_t = q8(b, d.f_l, d.h, E4M3, false, true);
-  t.amax_ws = b.take<char>(fp8_amax_ws_bytes());
+  if (is_fp8(c)) {
+    t.h = q8(b, d.S, d.h, E4M3, true, false);
+    t.w1_t = q8(b, d.h, d.f_l, E4M3, false, true);
+    t.a = q8(b, d.S, d.f_l, E4M3, true, false);
+    t.w2_t = q8(b, d.f_l, d.h, E4M3, false, true);
+    t.amax_ws = b.take<char>(fp8_amax_ws_bytes());
+  } else {
+    t.m_h = mx4(b, d.S, d.h);
+    t.m_w1_t = mx4(b, d.f_l, d.h);
+    t.m_a = mx4(b, d.S, d.f_l);
+    t.m_w2_t = mx4(b, d.h, d.f_l);
+  }
   if (s) *s = t;
   return b.off;
 }
@@ -315,7 +406,16 @@ mtl_status mtl_validate(const mtl_layer_cfg* c) {
     const int64_t w = std::max({d.h, d.qkv_l, d.f_l});
     if ((std::max(d.S, w) + 256) * w * 2 >= ((int64_t)1 << 32)) return MTL_E_SHAPE;
   }
-  if (c->precision != MTL_PREC_BF16 && c->precision != MTL_PREC_FP8_HYBRID) return MTL_E_UNSUPPORTED;
+  if (c->precision != MTL_PREC_BF16 && c->precision != MTL_PREC_FP8_HYBRID && c->precision != MTL_PREC_MXFP4)
+    return MTL_E_UNSUPPORTED;
+  if (c->precision == MTL_PREC_MXFP4) {
+    // every M, N of the MX GEMMs a multiple of 128 and every K of 256
+    const Dims d = dims_of(c);
+    for (int64_t v : {d.S, d.h, d.o_l, d.qkv_l, d.f_l})
+      if (v % 256 != 0) return MTL_E_SHAPE;
+    // the column-direction quantiser's grid takes at most 2^23 rows (S, h, h/t or f/t)
+    if (std::max({d.S, d.h, d.o_l, d.f_l}) > ((int64_t)1 << 23)) return MTL_E_SHAPE;
+  }
   // fp8 GEMMs contract over 16-byte code chunks: every K (h, 3h/t, h/t, f/t, S)
   // must be a multiple of 16
   if (c->precision == MTL_PREC_FP8_HYBRID &&
@@ -343,14 +443,18 @@ mtl_status mtl_attn_fwd(const mtl_layer_cfg* c, const void* x, const void* w_qkv
   if ((st = check_ptrs(x, w_qkv, b_qkv, w_o, qkv, o, lse, partial)) != MTL_OK) return st;
   const Dims d = dims_of(c);
   AttnFwdScratch ws{};
-  if (is_fp8(c)) {
+  if (is_fp8(c) || is_mx4(c)) {
     if ((st = check_ptrs(scratch)) != MTL_OK) return st;
     if (scratch_bytes < attn_fwd_scratch(c, d, &ws, static_cast<char*>(scratch))) return MTL_E_WORKSPACE;
   }
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
 
   // qkv = x . w_qkv + b_qkv
-  if (is_fp8(c)) {
+  if (is_mx4(c)) {
+    MTL_TRY(mxq(x, ws.m_x, s));
+    MTL_TRY(mxqt(w_qkv, ws.m_wqkv_t, s));
+    MTL_TRY(mxgemm("qkv_fwd", ws.m_x, ws.m_wqkv_t, EPI_BF16_BIAS, qkv, s, b_qkv));
+  } else if (is_fp8(c)) {
     MTL_TRY(quantize({{x, &ws.x}, {w_qkv, &ws.wqkv_t}, {w_o, &ws.wo_t}}, ws.amax_ws, s));
     MTL_TRY(gemm8("qkv_fwd", ws.x, ws.x.q, ws.wqkv_t, ws.wqkv_t.qt, d.S, d.qkv_l, d.h, qkv, d.qkv_l, EPI_BF16_BIAS,
                   s, b_qkv));
@@ -375,7 +479,11 @@ mtl_status mtl_attn_fwd(const mtl_layer_cfg* c, const void* x, const void* w_qkv
                       2.0 * d.S * (d.qkv_l + d.o_l) + 4.0 * d.S * d.heads_l, s, [&] { return attention_fwd(a, s); }));
 
   // partial = o . w_o
-  if (is_fp8(c)) {
+  if (is_mx4(c)) {
+    MTL_TRY(mxq(o, ws.m_o, s));
+    MTL_TRY(mxqt(w_o, ws.m_wo_t, s));
+    MTL_TRY(mxgemm("proj_fwd", ws.m_o, ws.m_wo_t, EPI_BF16, partial, s));
+  } else if (is_fp8(c)) {
     MTL_TRY(quantize({{o, &ws.o}}, ws.amax_ws, s));
     MTL_TRY(gemm8("proj_fwd", ws.o, ws.o.q, ws.wo_t, ws.wo_t.qt, d.S, d.h, d.o_l, partial, d.h, EPI_BF16, s));
   } else {
@@ -611,6 +719,16 @@ mtl_status mtl_mxfp4_gemm(int64_t M, int64_t N, int64_t K, const void* a_codes, 
   return hip_status(mxfp4_gemm(g, reinterpret_cast<hipStream_t>(stream)));
 }
 
+mtl_status mtl_mxfp4_quantize_t(const void* x, int64_t rows, int64_t cols, void* codes, void* scales,
+                                mtl_stream_t stream) {
+  mtl_status st = check_ptrs(x, codes, scales);
+  if (st != MTL_OK) return st;
+  if (rows <= 0 || cols <= 0 || rows % 32 != 0 || cols % 8 != 0 || rows > ((int64_t)1 << 23) || cols > INT32_MAX)
+    return MTL_E_SHAPE;
+  return hip_status(mxfp4_quantize_t(static_cast<const uint16_t*>(x), rows, cols, static_cast<uint8_t*>(codes),
+                                     static_cast<uint8_t*>(scales), reinterpret_cast<hipStream_t>(stream)));
+}
+
 mtl_status mtl_mxfp6_quantize(const void* x, int64_t rows, int64_t cols, void* codes, void* scales,
                               mtl_stream_t stream) {
   mtl_status st = check_ptrs(x, codes, scales);
@@ -646,11 +764,22 @@ mtl_status mtl_mlp_fwd(const mtl_layer_cfg* c, const void* h, const void* w1, co
   if ((st = check_ptrs(h, w1, b1, w2, gz, a, partial)) != MTL_OK) return st;
   const Dims d = dims_of(c);
   MlpFwdScratch ws{};
-  if (is_fp8(c)) {
+  if (is_fp8(c) || is_mx4(c)) {
     if ((st = check_ptrs(scratch)) != MTL_OK) return st;
     if (scratch_bytes < mlp_fwd_scratch(c, d, &ws, static_cast<char*>(scratch))) return MTL_E_WORKSPACE;
   }
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+
+  if (is_mx4(c)) {
+    // z = h . w1 + b1: gz = GeLU'(z), a = GeLU(z); partial = a . w2
+    MTL_TRY(mxq(h, ws.m_h, s));
+    MTL_TRY(mxqt(w1, ws.m_w1_t, s));
+    MTL_TRY(mxgemm("fc1_fwd", ws.m_h, ws.m_w1_t, EPI_BIAS_GELU, gz, s, b1, a));
+    MTL_TRY(mxq(a, ws.m_a, s));
+    MTL_TRY(mxqt(w2, ws.m_w2_t, s));
+    MTL_TRY(mxgemm("fc2_fwd", ws.m_a, ws.m_w2_t, EPI_BF16, partial, s));
+    return MTL_OK;
+  }
 
   if (is_fp8(c)) {
     // z = h . w1 + b1: gz = GeLU'(z), a = GeLU(z); partial = a . w2 (a re-quantised from bf16)
@@ -704,6 +833,23 @@ mtl_status mtl_mlp_bwd(const mtl_layer_cfg* c, const void* dy, const void* h, co
   const bool accum = (c->flags & MTL_F_WGRAD_ACCUM) != 0;
   const int wepi = accum ? EPI_F32_ACC : EPI_F32;
 
+  if (is_mx4(c)) {
+    // every operand quantised along its product's contraction
+    MTL_TRY(mxq(dy, ws.m_dy, s));
+    MTL_TRY(mxq(w2, ws.m_w2, s));
+    MTL_TRY(mxgemm("fc2_dgrad", ws.m_dy, ws.m_w2, EPI_DGELU, ws.dz, s, nullptr, nullptr, gz));
+    MTL_TRY(mxqt(a, ws.m_a_t, s));
+    MTL_TRY(mxqt(dy, ws.m_dy_t, s));
+    MTL_TRY(mxgemm("fc2_wgrad", ws.m_a_t, ws.m_dy_t, wepi, dw2, s));
+    MTL_TRY(mxq(ws.dz, ws.m_dz, s));
+    MTL_TRY(mxq(w1, ws.m_w1, s));
+    MTL_TRY(mxgemm("fc1_dgrad", ws.m_dz, ws.m_w1, EPI_BF16, dh_partial, s));
+    MTL_TRY(mxqt(h, ws.m_h_t, s));
+    MTL_TRY(mxqt(ws.dz, ws.m_dz_t, s));
+    MTL_TRY(mxgemm("fc1_wgrad", ws.m_h_t, ws.m_dz_t, wepi, dw1, s));
+    MTL_TRY(mlp_bias_grads(d, ws, dy, db1, db2, accum, s));
+    return MTL_OK;
+  }
   if (is_fp8(c)) {
     // E5M2 gradients, E4M3 activations and weights; wgrad operands transposed
     MTL_TRY(quantize({{dy, &ws.dy}, {w2, &ws.w2}, {a, &ws.a_t}}, ws.amax_ws, s));
@@ -750,7 +896,14 @@ mtl_status mtl_attn_bwd(const mtl_layer_cfg* c, const void* dh, const void* x, c
   const int wepi = accum ? EPI_F32_ACC : EPI_F32;
   const bool f8 = is_fp8(c);
 
-  if (f8) {
+  if (is_mx4(c)) {
+    MTL_TRY(mxq(dh, ws.m_dh, s));
+    MTL_TRY(mxq(w_o, ws.m_wo, s));
+    MTL_TRY(mxgemm("proj_dgrad", ws.m_dh, ws.m_wo, EPI_BF16, ws.dout, s));
+    MTL_TRY(mxqt(o, ws.m_o_t, s));
+    MTL_TRY(mxqt(dh, ws.m_dh_t, s));
+    MTL_TRY(mxgemm("proj_wgrad", ws.m_o_t, ws.m_dh_t, wepi, dw_o, s));
+  } else if (f8) {
     // do = dh . w_o^T ; dw_o = o^T . dh
     MTL_TRY(quantize({{dh, &ws.dh}, {w_o, &ws.wo}, {o, &ws.o_t}}, ws.amax_ws, s));
     MTL_TRY(gemm8_pair("proj_bwd", gemm8_args(ws.o_t, ws.o_t.qt, ws.dh, ws.dh.qt, d.o_l, d.h, d.S, dw_o, d.h), wepi,
@@ -781,6 +934,16 @@ mtl_status mtl_attn_bwd(const mtl_layer_cfg* c, const void* dh, const void* x, c
                       2.0 * d.S * (2 * d.qkv_l + 2 * d.o_l) + 4.0 * d.S * d.heads_l, s,
                       [&] { return attention_bwd(at, s); }));
 
+  if (is_mx4(c)) {
+    MTL_TRY(mxq(ws.dqkv, ws.m_dqkv, s));
+    MTL_TRY(mxq(w_qkv, ws.m_wqkv, s));
+    MTL_TRY(mxgemm("qkv_dgrad", ws.m_dqkv, ws.m_wqkv, EPI_BF16, dx_partial, s));
+    MTL_TRY(mxqt(x, ws.m_x_t, s));
+    MTL_TRY(mxqt(ws.dqkv, ws.m_dqkv_t, s));
+    MTL_TRY(mxgemm("qkv_wgrad", ws.m_x_t, ws.m_dqkv_t, wepi, dw_qkv, s));
+    MTL_TRY(attn_bias_grads(d, ws, dh, db_qkv, db_o, accum, s));
+    return MTL_OK;
+  }
   if (f8) {
     // dw_qkv = x^T . dqkv ; dx_partial = dqkv . w_qkv^T
     MTL_TRY(quantize({{ws.dqkv, &ws.dqkv8}, {x, &ws.x_t}, {w_qkv, &ws.wqkv}}, ws.amax_ws, s));

@@ -146,8 +146,19 @@ struct Mxfp4GemmArgs {
   uint16_t* c;
   int64_t ldc;
   int M, N, K;
+  // MXFP4 epilogues (mxfp4_gemm; MXFP6 is EPI_BF16 only), as the bf16 GEMM's:
+  int epi;               // EPI_* (0: bf16 C)
+  const uint16_t* bias;  // [N] (EPI_BF16_BIAS, EPI_BIAS_GELU)
+  uint16_t* c2;          // GeLU(z) [M, N], row stride ldc (EPI_BIAS_GELU)
+  const uint16_t* aux;   // GeLU'(z) [M, N], row stride ldc (EPI_DGELU)
+  float* c32;            // fp32 C [M, N], row stride ldc (EPI_F32, EPI_F32_ACC)
 };
 hipError_t mxfp4_gemm(const Mxfp4GemmArgs& g, hipStream_t s);
+// MXFP4 quantisation of x [rows, cols] along its rows (blocks of 32 rows of
+// one column): codes of x^T, [cols, rows/2] bytes, and scales [cols, rows/32]
+// (rows % 32 == 0, cols % 8 == 0).
+hipError_t mxfp4_quantize_t(const uint16_t* x, int64_t rows, int64_t cols, uint8_t* codes, uint8_t* scales,
+                            hipStream_t s);
 // The same for MXFP6 (FP6 E2M3 elements): codes [rows, cols*3/4], 32 elements
 // of 6 bits per 24 bytes, element j at bits 6j.. of the little-endian block;
 // the GEMM takes K % 128 == 0.

@@ -62,6 +62,38 @@ __global__ __launch_bounds__(256) void mxfp4_quant_kernel(const uint16_t* __rest
   if ((i & 3) == 0) scales[i >> 2] = (uint8_t)sc;
 }
 
+// Along rows: lane l of a 64-lane group takes column c0 + l and one block of
+// 32 rows, so the 64 lanes read 128 consecutive bytes per row; the lane then
+// holds its block's 32 elements and writes their 16 code bytes and the scale
+// byte at row c of the transposed codes.
+__global__ __launch_bounds__(256) void mxfp4_quant_t_kernel(const uint16_t* __restrict__ x, int64_t rows,
+                                                            int64_t cols, uint8_t* __restrict__ codes,
+                                                            uint8_t* __restrict__ scales) {
+  const int64_t c = (int64_t)blockIdx.x * 64 + (threadIdx.x & 63);
+  const int64_t rb = (int64_t)blockIdx.y * 4 + (threadIdx.x >> 6);  // block of 32 rows
+  if (c >= cols || rb * 32 >= rows) return;
+  uint32_t bits[32];
+  uint32_t mx = 0;
+  const uint16_t* p = x + rb * 32 * cols + c;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) {
+    bits[i] = p[(int64_t)i * cols];
+    mx = max(mx, bits[i] & 0x7fffu);
+  }
+  // the scale rule of mxfp4_quant_kernel
+  const int E = (int)(mx >> 7);
+  const uint32_t sc = (uint32_t)max(E - 2, 0);
+  const float mul = __uint_as_float((254u - sc) << 23);
+  u32x4 w = {0, 0, 0, 0};
+#pragma unroll
+  for (int i = 0; i < 32; ++i) {
+    const float y = __uint_as_float(bits[i] << 16) * mul;
+    w[i >> 3] |= e2m1_code(y, bits[i] >> 15) << (4 * (i & 7));
+  }
+  *reinterpret_cast<u32x4*>(codes + c * (rows / 2) + rb * 16) = w;
+  scales[c * (rows / 32) + rb] = (uint8_t)sc;
+}
+
 // FP6 E2M3 code of y (|y| < 8 by the block scale): below 1 the spacing is 1/8
 // (subnormals, code = rint(8|y|)); in [2^E, 2^(E+1)) it is 2^(E-3); ties to
 // even through rint, a rounding up to 2^(E+1) moves to the next exponent, and
@@ -156,6 +188,7 @@ __device__ __forceinline__ int chunk_off(int r, int c) {
 }
 }  // namespace
 
+template <int EPI>
 __global__ __launch_bounds__(256, 2) void mxfp4_gemm_kernel(Mxfp4GemmArgs g) {
   __shared__ __attribute__((aligned(1024))) char lds_[2 * BUF];
   const int ntn = g.N / MT;
@@ -254,7 +287,8 @@ __global__ __launch_bounds__(256, 2) void mxfp4_gemm_kernel(Mxfp4GemmArgs g) {
     __syncthreads();
   }
 
-  // lane: row m = lane % 32 of block i, columns 8*(r/4) + 4*(lane/32) + r%4 of block j
+  // lane: row m = lane % 32 of block i, columns 8*(r/4) + 4*(lane/32) + r%4 of
+  // block j; the epilogue works on those 4 consecutive columns at a time
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
     const int64_t m = (int64_t)tm * MT + wm * 64 + i * 32 + (lane & 31);
@@ -263,9 +297,42 @@ __global__ __launch_bounds__(256, 2) void mxfp4_gemm_kernel(Mxfp4GemmArgs g) {
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int n = tn * MT + wn * 64 + j * 32 + 8 * q + 4 * (lane >> 5);
-        *reinterpret_cast<u32x2*>(g.c + m * g.ldc + n) =
-            u32x2{pack_bf16x2(acc[i][j][4 * q], acc[i][j][4 * q + 1]),
-                  pack_bf16x2(acc[i][j][4 * q + 2], acc[i][j][4 * q + 3])};
+        float v[4] = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
+        const int64_t o = m * g.ldc + n;
+        if constexpr (EPI == EPI_F32 || EPI == EPI_F32_ACC) {
+          f32x4 r = {v[0], v[1], v[2], v[3]};
+          if constexpr (EPI == EPI_F32_ACC) r += *reinterpret_cast<const f32x4*>(g.c32 + o);
+          *reinterpret_cast<f32x4*>(g.c32 + o) = r;
+          continue;
+        }
+        if constexpr (EPI == EPI_BF16_BIAS || EPI == EPI_BIAS_GELU) {
+          if (g.bias) {
+            const u32x2 b = *reinterpret_cast<const u32x2*>(g.bias + n);
+            v[0] += bf16_lo(b[0]);
+            v[1] += bf16_hi(b[0]);
+            v[2] += bf16_lo(b[1]);
+            v[3] += bf16_hi(b[1]);
+          }
+        }
+        if constexpr (EPI == EPI_BIAS_GELU) {  // C = GeLU'(z), C2 = GeLU(z)
+          float ge[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            float cdf, pdf;
+            normal_cdf_pdf(v[e], cdf, pdf);
+            ge[e] = v[e] * cdf;
+            v[e] = cdf + v[e] * pdf;
+          }
+          *reinterpret_cast<u32x2*>(g.c2 + o) = u32x2{pack_bf16x2(ge[0], ge[1]), pack_bf16x2(ge[2], ge[3])};
+        }
+        if constexpr (EPI == EPI_DGELU) {  // aux holds GeLU'(z)
+          const u32x2 z = *reinterpret_cast<const u32x2*>(g.aux + o);
+          v[0] *= bf16_lo(z[0]);
+          v[1] *= bf16_hi(z[0]);
+          v[2] *= bf16_lo(z[1]);
+          v[3] *= bf16_hi(z[1]);
+        }
+        *reinterpret_cast<u32x2*>(g.c + o) = u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
       }
   }
 }
@@ -396,7 +463,27 @@ hipError_t mxfp4_gemm(const Mxfp4GemmArgs& g, hipStream_t s) {
   if (g.M % MT || g.N % MT || g.K % KSLAB) return hipErrorInvalidValue;
   const int64_t tiles = (int64_t)(g.M / MT) * (g.N / MT);
   if (tiles > INT32_MAX) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(mxfp4_gemm_kernel, dim3((unsigned)tiles), dim3(256), 0, s, g);
+  const dim3 grid((unsigned)tiles), block(256);
+  switch (g.epi) {
+    case EPI_BF16: hipLaunchKernelGGL(mxfp4_gemm_kernel<EPI_BF16>, grid, block, 0, s, g); break;
+    case EPI_BF16_BIAS: hipLaunchKernelGGL(mxfp4_gemm_kernel<EPI_BF16_BIAS>, grid, block, 0, s, g); break;
+    case EPI_BIAS_GELU: hipLaunchKernelGGL(mxfp4_gemm_kernel<EPI_BIAS_GELU>, grid, block, 0, s, g); break;
+    case EPI_DGELU: hipLaunchKernelGGL(mxfp4_gemm_kernel<EPI_DGELU>, grid, block, 0, s, g); break;
+    case EPI_F32: hipLaunchKernelGGL(mxfp4_gemm_kernel<EPI_F32>, grid, block, 0, s, g); break;
+    case EPI_F32_ACC: hipLaunchKernelGGL(mxfp4_gemm_kernel<EPI_F32_ACC>, grid, block, 0, s, g); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t mxfp4_quantize_t(const uint16_t* x, int64_t rows, int64_t cols, uint8_t* codes, uint8_t* scales,
+                            hipStream_t s) {
+  if (rows <= 0 || cols <= 0) return hipSuccess;
+  if (rows % 32) return hipErrorInvalidValue;
+  const int64_t gx = (cols + 63) / 64, gy = (rows / 32 + 3) / 4;
+  if (gx > INT32_MAX || gy > 65535) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(mxfp4_quant_t_kernel, dim3((unsigned)gx, (unsigned)gy), dim3(256), 0, s, x, rows, cols, codes,
+                     scales);
   return hipGetLastError();
 }
 

@@ -1,8 +1,9 @@
 """The oracle: a plain, slow fp64 CPU implementation of one transformer layer's
 training step, of its tensor-parallel sharded view, of one context-parallel
 rank's share of causal attention, of the MoE expert block and its router
-(linear, gate backward, load-balancing loss), of fp8 quantisation, and of
-MXFP4 quantisation with a GEMM on MXFP4 operands.
+(linear, gate backward, load-balancing loss), of fp8 quantisation and the
+layer with fp8 GEMM operands, and of MXFP4 quantisation, GEMMs on MXFP4
+operands and the layer with MXFP4 GEMM operands.
 
 TEST INFRASTRUCTURE ONLY.  Nothing in the library path imports, calls or links
 this package; only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline
@@ -27,3 +28,4 @@ attention, exact erf GeLU, softmax gates over the selected experts, OCP fp8
 encodings) -- each reading is listed in the module that uses it.
 """
 from . import layer, shard, moe, fp8, router, cp, mxfp4  # noqa: F401
+from . import fp8_layer, mx_layer  # noqa: F401

@@ -141,6 +141,33 @@ def pack6(codes):
     return out
 
 
+def quantize_fast(x, elem: str = "e2m1"):
+    """The codes and scales of ``quantize`` computed on whole arrays, for the
+    sizes where its element loop is too slow (pinned to it element for element).
+    floor(log2 amax) is the exponent frexp returns minus one; the nearest
+    magnitude is chosen by distance with ties to the even code; the sign bit
+    follows the sign of the value, zero included."""
+    mags = {"e2m1": E2M1_MAGNITUDES, "e2m3": E2M3_MAGNITUDES}[elem]
+    x = np.asarray(x, dtype=np.float64)
+    rows, cols = x.shape
+    if cols % BLOCK:
+        raise ValueError("cols must be a multiple of 32")
+    if not np.all(np.isfinite(x)):
+        raise ValueError("finite inputs only")
+    blocks = x.reshape(rows, cols // BLOCK, BLOCK)
+    amax = np.max(np.abs(blocks), axis=2)
+    _, fe = np.frexp(amax)
+    e = np.where(amax > 0, fe - 1 - EMAX_ELEM, SCALE_EXP_MIN)
+    e = np.maximum(e, SCALE_EXP_MIN)
+    y = np.ldexp(blocks, -e[:, :, None])
+    dist = np.abs(mags[None, None, None, :] - np.abs(y)[..., None])
+    nearest = dist == dist.min(axis=-1, keepdims=True)
+    even = (np.arange(len(mags)) % 2 == 0)
+    code = np.argmax(nearest * np.where(even, 2, 1), axis=-1)  # an even code wins a tie
+    code = code | np.where(np.signbit(y), len(mags), 0)
+    return code.reshape(rows, cols).astype(np.uint8), (e + E8M0_BIAS).astype(np.uint8)
+
+
 def dequantize(codes, scales, elem: str = "e2m1"):
     """Values X * element(code) [rows, cols] in fp64 (codes one per element)."""
     c = np.asarray(codes, dtype=np.int64)
