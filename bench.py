@@ -825,8 +825,11 @@ def dense_main(args):
     inp = synth.layer_inputs(shape, tp=t, rank=r)
     fp8, mx = args.precision == "fp8", args.precision == "mxfp4"
     from megatron_tensor_transformer_layer_amd import MTL_PREC_MXFP4
-    st = RankState(shape, t, r, inp, precision={"bf16": MTL_PREC_BF16, "fp8": MTL_PREC_FP8_HYBRID,
-                                                 "mxfp4": MTL_PREC_MXFP4}[args.precision])
+    from megatron_tensor_transformer_layer_amd import MTL_F_FP8_KEEP_CODES
+    # fp8: the forward's transposed codes of x, o, h, a are kept for the backward
+    st = RankState(shape, t, r, inp, flags=MTL_F_FP8_KEEP_CODES if fp8 else 0,
+                   precision={"bf16": MTL_PREC_BF16, "fp8": MTL_PREC_FP8_HYBRID,
+                              "mxfp4": MTL_PREC_MXFP4}[args.precision])
     D = st.D
     x = bf16_dev(inp["x"])
     dy = bf16_dev(inp["dy"])

@@ -22,7 +22,7 @@ MTL_PREC_BF16, MTL_PREC_FP8_HYBRID, MTL_PREC_MXFP4 = 0, 1, 2
 MTL_FP8_E4M3, MTL_FP8_E5M2 = 0, 1
 MTL_FP8_AMAX_SCRATCH = 4096
 MTL_CP_MAX = 64
-MTL_F_RESIDUAL, MTL_F_WGRAD_ACCUM = 1, 2
+MTL_F_RESIDUAL, MTL_F_WGRAD_ACCUM, MTL_F_FP8_KEEP_CODES = 1, 2, 4
 MTL_PROF_MAX = 2048
 MTL_NOALLOC_SCRATCH_BYTES = 48 << 20
 MTL_PROF_KINDS = ("gemm", "attention", "reduce", "colsum", "quantize", "gather")

@@ -208,6 +208,13 @@ hipError_t mxqt(const void* x, const MX4& m, hipStream_t s) {
   return prof::timed(prof::QUANT, "mx_quantize_cols", 0, mx4_bytes(m), s,
                      [&] { return mxfp4_quantize_t(static_cast<const uint16_t*>(x), m.k, m.rows, m.q, m.s, s); });
 }
+// x [r, k] quantised both ways from one read: along its rows into m ([r, k])
+// and down its columns into mt ([k, r])
+hipError_t mxq2(const void* x, const MX4& m, const MX4& mt, hipStream_t s) {
+  return prof::timed(prof::QUANT, "mx_quantize_both", 0, mx4_bytes(m) + mx4_bytes(mt) - 2.0 * m.rows * m.k, s, [&] {
+    return mxfp4_quantize_both(static_cast<const uint16_t*>(x), m.rows, m.k, m.q, m.s, mt.q, mt.s, s);
+  });
+}
 // C [a.rows, b.rows] = A . B^T on MXFP4 codes, epilogue epi (fp32 C for the wgrad epilogues)
 hipError_t mxgemm(const char* name, const MX4& a, const MX4& b, int epi, void* c, hipStream_t s,
                   const void* bias = nullptr, void* c2 = nullptr, const void* aux = nullptr) {
@@ -264,6 +271,33 @@ struct MlpFwdScratch {
 
 inline bool is_fp8(const mtl_layer_cfg* c) { return c->precision == MTL_PREC_FP8_HYBRID; }
 inline bool is_mx4(const mtl_layer_cfg* c) { return c->precision == MTL_PREC_MXFP4; }
+inline bool keeps_codes(const mtl_layer_cfg* c) { return is_fp8(c) && (c->flags & MTL_F_FP8_KEEP_CODES); }
+
+// With MTL_F_FP8_KEEP_CODES: the transposed E4M3 codes (and scale records) of
+// x, o, h and a, written by the forward calls at the start of the scratch and
+// read there by the backward calls, which then do not quantise these tensors
+// again (the same tensor, format and amax give the same codes).
+struct Kept {
+  Q8 x_t, o_t, h_t, a_t;
+};
+size_t kept_scratch(const mtl_layer_cfg* c, const Dims& d, Kept* k, char* base) {
+  if (!keeps_codes(c)) return 0;
+  Bump b{base};
+  Kept t{};
+  t.x_t = q8(b, d.S, d.h, E4M3, false, true);
+  t.o_t = q8(b, d.S, d.o_l, E4M3, false, true);
+  t.h_t = q8(b, d.S, d.h, E4M3, false, true);
+  t.a_t = q8(b, d.S, d.f_l, E4M3, false, true);
+  if (k) *k = t;
+  return b.off;
+}
+// A forward operand quantised row-major into the call's scratch whose
+// transposed copy and record go to the kept region.
+inline Q8 with_kept(Q8 q, const Q8& kept) {
+  q.rec = kept.rec;
+  q.qt = kept.qt;
+  return q;
+}
 
 size_t mlp_scratch(const mtl_layer_cfg* c, const Dims& d, MlpScratch* s, char* base) {
   Bump b{base};
@@ -421,7 +455,8 @@ mtl_status mtl_validate(const mtl_layer_cfg* c) {
   if (c->precision == MTL_PREC_FP8_HYBRID &&
       (((int64_t)c->seq * c->micro_batch) % 16 != 0 || (c->ffn / c->tp) % 16 != 0))
     return MTL_E_SHAPE;
-  if (c->flags & ~(MTL_F_RESIDUAL | MTL_F_WGRAD_ACCUM)) return MTL_E_UNSUPPORTED;
+  if (c->flags & ~(MTL_F_RESIDUAL | MTL_F_WGRAD_ACCUM | MTL_F_FP8_KEEP_CODES)) return MTL_E_UNSUPPORTED;
+  if ((c->flags & MTL_F_FP8_KEEP_CODES) && c->precision != MTL_PREC_FP8_HYBRID) return MTL_E_UNSUPPORTED;
   return MTL_OK;
 }
 
@@ -430,7 +465,8 @@ mtl_status mtl_workspace_bytes(const mtl_layer_cfg* c, size_t* scratch_bytes) {
   if (st != MTL_OK) return st;
   if (!scratch_bytes) return MTL_E_NULL;
   const Dims d = dims_of(c);
-  *scratch_bytes = std::max({mlp_scratch(c, d, nullptr, nullptr), attn_scratch(c, d, nullptr, nullptr),
+  *scratch_bytes = kept_scratch(c, d, nullptr, nullptr) +
+                   std::max({mlp_scratch(c, d, nullptr, nullptr), attn_scratch(c, d, nullptr, nullptr),
                              attn_fwd_scratch(c, d, nullptr, nullptr), mlp_fwd_scratch(c, d, nullptr, nullptr)});
   return MTL_OK;
 }
@@ -443,9 +479,16 @@ mtl_status mtl_attn_fwd(const mtl_layer_cfg* c, const void* x, const void* w_qkv
   if ((st = check_ptrs(x, w_qkv, b_qkv, w_o, qkv, o, lse, partial)) != MTL_OK) return st;
   const Dims d = dims_of(c);
   AttnFwdScratch ws{};
+  Kept kp{};
   if (is_fp8(c) || is_mx4(c)) {
     if ((st = check_ptrs(scratch)) != MTL_OK) return st;
-    if (scratch_bytes < attn_fwd_scratch(c, d, &ws, static_cast<char*>(scratch))) return MTL_E_WORKSPACE;
+    const size_t kb = kept_scratch(c, d, &kp, static_cast<char*>(scratch));
+    if (scratch_bytes < kb || scratch_bytes - kb < attn_fwd_scratch(c, d, &ws, static_cast<char*>(scratch) + kb))
+      return MTL_E_WORKSPACE;
+    if (keeps_codes(c)) {
+      ws.x = with_kept(ws.x, kp.x_t);
+      ws.o = with_kept(ws.o, kp.o_t);
+    }
   }
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
 
@@ -764,9 +807,16 @@ mtl_status mtl_mlp_fwd(const mtl_layer_cfg* c, const void* h, const void* w1, co
   if ((st = check_ptrs(h, w1, b1, w2, gz, a, partial)) != MTL_OK) return st;
   const Dims d = dims_of(c);
   MlpFwdScratch ws{};
+  Kept kp{};
   if (is_fp8(c) || is_mx4(c)) {
     if ((st = check_ptrs(scratch)) != MTL_OK) return st;
-    if (scratch_bytes < mlp_fwd_scratch(c, d, &ws, static_cast<char*>(scratch))) return MTL_E_WORKSPACE;
+    const size_t kb = kept_scratch(c, d, &kp, static_cast<char*>(scratch));
+    if (scratch_bytes < kb || scratch_bytes - kb < mlp_fwd_scratch(c, d, &ws, static_cast<char*>(scratch) + kb))
+      return MTL_E_WORKSPACE;
+    if (keeps_codes(c)) {
+      ws.h = with_kept(ws.h, kp.h_t);
+      ws.a = with_kept(ws.a, kp.a_t);
+    }
   }
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
 
@@ -828,36 +878,47 @@ mtl_status mtl_mlp_bwd(const mtl_layer_cfg* c, const void* dy, const void* h, co
   if (db2 && !aligned16(db2)) return MTL_E_ALIGN;
   const Dims d = dims_of(c);
   MlpScratch ws;
-  if (scratch_bytes < mlp_scratch(c, d, &ws, static_cast<char*>(scratch))) return MTL_E_WORKSPACE;
+  Kept kp{};
+  const size_t kb = kept_scratch(c, d, &kp, static_cast<char*>(scratch));
+  if (scratch_bytes < kb || scratch_bytes - kb < mlp_scratch(c, d, &ws, static_cast<char*>(scratch) + kb))
+    return MTL_E_WORKSPACE;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   const bool accum = (c->flags & MTL_F_WGRAD_ACCUM) != 0;
   const int wepi = accum ? EPI_F32_ACC : EPI_F32;
 
   if (is_mx4(c)) {
     // every operand quantised along its product's contraction
-    MTL_TRY(mxq(dy, ws.m_dy, s));
+    MTL_TRY(mxq2(dy, ws.m_dy, ws.m_dy_t, s));
     MTL_TRY(mxq(w2, ws.m_w2, s));
     MTL_TRY(mxgemm("fc2_dgrad", ws.m_dy, ws.m_w2, EPI_DGELU, ws.dz, s, nullptr, nullptr, gz));
     MTL_TRY(mxqt(a, ws.m_a_t, s));
-    MTL_TRY(mxqt(dy, ws.m_dy_t, s));
     MTL_TRY(mxgemm("fc2_wgrad", ws.m_a_t, ws.m_dy_t, wepi, dw2, s));
-    MTL_TRY(mxq(ws.dz, ws.m_dz, s));
+    MTL_TRY(mxq2(ws.dz, ws.m_dz, ws.m_dz_t, s));
     MTL_TRY(mxq(w1, ws.m_w1, s));
     MTL_TRY(mxgemm("fc1_dgrad", ws.m_dz, ws.m_w1, EPI_BF16, dh_partial, s));
     MTL_TRY(mxqt(h, ws.m_h_t, s));
-    MTL_TRY(mxqt(ws.dz, ws.m_dz_t, s));
     MTL_TRY(mxgemm("fc1_wgrad", ws.m_h_t, ws.m_dz_t, wepi, dw1, s));
     MTL_TRY(mlp_bias_grads(d, ws, dy, db1, db2, accum, s));
     return MTL_OK;
   }
   if (is_fp8(c)) {
     // E5M2 gradients, E4M3 activations and weights; wgrad operands transposed
-    MTL_TRY(quantize({{dy, &ws.dy}, {w2, &ws.w2}, {a, &ws.a_t}}, ws.amax_ws, s));
+    if (keeps_codes(c)) {  // a's transposed codes come from mtl_mlp_fwd
+      ws.a_t = kp.a_t;
+      MTL_TRY(quantize({{dy, &ws.dy}, {w2, &ws.w2}}, ws.amax_ws, s));
+    } else {
+      MTL_TRY(quantize({{dy, &ws.dy}, {w2, &ws.w2}, {a, &ws.a_t}}, ws.amax_ws, s));
+    }
     // dw2 = a^T . dy with dz = (dy . w2^T) * gz in one launch, then dw1 = h^T . dz with dh_partial = dz . w1^T
     MTL_TRY(gemm8_pair("fc2_bwd", gemm8_args(ws.a_t, ws.a_t.qt, ws.dy, ws.dy.qt, d.f_l, d.h, d.S, dw2, d.h), wepi,
                        gemm8_args(ws.dy, ws.dy.q, ws.w2, ws.w2.q, d.S, d.f_l, d.h, ws.dz, d.f_l, nullptr, nullptr, gz),
                        EPI_DGELU, s));
-    MTL_TRY(quantize({{ws.dz, &ws.dz8}, {h, &ws.h_t}, {w1, &ws.w1}}, ws.amax_ws, s));
+    if (keeps_codes(c)) {  // and h's
+      ws.h_t = kp.h_t;
+      MTL_TRY(quantize({{ws.dz, &ws.dz8}, {w1, &ws.w1}}, ws.amax_ws, s));
+    } else {
+      MTL_TRY(quantize({{ws.dz, &ws.dz8}, {h, &ws.h_t}, {w1, &ws.w1}}, ws.amax_ws, s));
+    }
     MTL_TRY(gemm8_pair("fc1_bwd", gemm8_args(ws.h_t, ws.h_t.qt, ws.dz8, ws.dz8.qt, d.h, d.f_l, d.S, dw1, d.f_l), wepi,
                        gemm8_args(ws.dz8, ws.dz8.q, ws.w1, ws.w1.q, d.S, d.h, d.f_l, dh_partial, d.h), EPI_BF16, s));
     MTL_TRY(mlp_bias_grads(d, ws, dy, db1, db2, accum, s));
@@ -890,22 +951,29 @@ mtl_status mtl_attn_bwd(const mtl_layer_cfg* c, const void* dh, const void* x, c
   if (db_o && !aligned16(db_o)) return MTL_E_ALIGN;
   const Dims d = dims_of(c);
   AttnScratch ws;
-  if (scratch_bytes < attn_scratch(c, d, &ws, static_cast<char*>(scratch))) return MTL_E_WORKSPACE;
+  Kept kp{};
+  const size_t kb = kept_scratch(c, d, &kp, static_cast<char*>(scratch));
+  if (scratch_bytes < kb || scratch_bytes - kb < attn_scratch(c, d, &ws, static_cast<char*>(scratch) + kb))
+    return MTL_E_WORKSPACE;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   const bool accum = (c->flags & MTL_F_WGRAD_ACCUM) != 0;
   const int wepi = accum ? EPI_F32_ACC : EPI_F32;
   const bool f8 = is_fp8(c);
 
   if (is_mx4(c)) {
-    MTL_TRY(mxq(dh, ws.m_dh, s));
+    MTL_TRY(mxq2(dh, ws.m_dh, ws.m_dh_t, s));
     MTL_TRY(mxq(w_o, ws.m_wo, s));
     MTL_TRY(mxgemm("proj_dgrad", ws.m_dh, ws.m_wo, EPI_BF16, ws.dout, s));
     MTL_TRY(mxqt(o, ws.m_o_t, s));
-    MTL_TRY(mxqt(dh, ws.m_dh_t, s));
     MTL_TRY(mxgemm("proj_wgrad", ws.m_o_t, ws.m_dh_t, wepi, dw_o, s));
   } else if (f8) {
     // do = dh . w_o^T ; dw_o = o^T . dh
-    MTL_TRY(quantize({{dh, &ws.dh}, {w_o, &ws.wo}, {o, &ws.o_t}}, ws.amax_ws, s));
+    if (keeps_codes(c)) {  // o's transposed codes come from mtl_attn_fwd
+      ws.o_t = kp.o_t;
+      MTL_TRY(quantize({{dh, &ws.dh}, {w_o, &ws.wo}}, ws.amax_ws, s));
+    } else {
+      MTL_TRY(quantize({{dh, &ws.dh}, {w_o, &ws.wo}, {o, &ws.o_t}}, ws.amax_ws, s));
+    }
     MTL_TRY(gemm8_pair("proj_bwd", gemm8_args(ws.o_t, ws.o_t.qt, ws.dh, ws.dh.qt, d.o_l, d.h, d.S, dw_o, d.h), wepi,
                        gemm8_args(ws.dh, ws.dh.q, ws.wo, ws.wo.q, d.S, d.o_l, d.h, ws.dout, d.o_l), EPI_BF16, s));
   } else {
@@ -935,18 +1003,22 @@ mtl_status mtl_attn_bwd(const mtl_layer_cfg* c, const void* dh, const void* x, c
                       [&] { return attention_bwd(at, s); }));
 
   if (is_mx4(c)) {
-    MTL_TRY(mxq(ws.dqkv, ws.m_dqkv, s));
+    MTL_TRY(mxq2(ws.dqkv, ws.m_dqkv, ws.m_dqkv_t, s));
     MTL_TRY(mxq(w_qkv, ws.m_wqkv, s));
     MTL_TRY(mxgemm("qkv_dgrad", ws.m_dqkv, ws.m_wqkv, EPI_BF16, dx_partial, s));
     MTL_TRY(mxqt(x, ws.m_x_t, s));
-    MTL_TRY(mxqt(ws.dqkv, ws.m_dqkv_t, s));
     MTL_TRY(mxgemm("qkv_wgrad", ws.m_x_t, ws.m_dqkv_t, wepi, dw_qkv, s));
     MTL_TRY(attn_bias_grads(d, ws, dh, db_qkv, db_o, accum, s));
     return MTL_OK;
   }
   if (f8) {
     // dw_qkv = x^T . dqkv ; dx_partial = dqkv . w_qkv^T
-    MTL_TRY(quantize({{ws.dqkv, &ws.dqkv8}, {x, &ws.x_t}, {w_qkv, &ws.wqkv}}, ws.amax_ws, s));
+    if (keeps_codes(c)) {  // and x's
+      ws.x_t = kp.x_t;
+      MTL_TRY(quantize({{ws.dqkv, &ws.dqkv8}, {w_qkv, &ws.wqkv}}, ws.amax_ws, s));
+    } else {
+      MTL_TRY(quantize({{ws.dqkv, &ws.dqkv8}, {x, &ws.x_t}, {w_qkv, &ws.wqkv}}, ws.amax_ws, s));
+    }
     MTL_TRY(gemm8_pair("qkv_bwd",
                        gemm8_args(ws.x_t, ws.x_t.qt, ws.dqkv8, ws.dqkv8.qt, d.h, d.qkv_l, d.S, dw_qkv, d.qkv_l), wepi,
                        gemm8_args(ws.dqkv8, ws.dqkv8.q, ws.wqkv, ws.wqkv.q, d.S, d.h, d.qkv_l, dx_partial, d.h),
@@ -969,9 +1041,10 @@ mtl_status mtl_attn_bwd_scratch_layout(const mtl_layer_cfg* c, size_t* do_offset
   if (!do_offset || !dqkv_offset) return MTL_E_NULL;
   // the same carving as mtl_attn_bwd, over a base address of 0
   AttnScratch ws;
+  const size_t kb = kept_scratch(c, dims_of(c), nullptr, nullptr);
   attn_scratch(c, dims_of(c), &ws, reinterpret_cast<char*>(ALIGN));
-  *do_offset = (size_t)(reinterpret_cast<char*>(ws.dout) - reinterpret_cast<char*>(ALIGN));
-  *dqkv_offset = (size_t)(reinterpret_cast<char*>(ws.dqkv) - reinterpret_cast<char*>(ALIGN));
+  *do_offset = kb + (size_t)(reinterpret_cast<char*>(ws.dout) - reinterpret_cast<char*>(ALIGN));
+  *dqkv_offset = kb + (size_t)(reinterpret_cast<char*>(ws.dqkv) - reinterpret_cast<char*>(ALIGN));
   return MTL_OK;
 }
 

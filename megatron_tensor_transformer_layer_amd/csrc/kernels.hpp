@@ -159,6 +159,11 @@ hipError_t mxfp4_gemm(const Mxfp4GemmArgs& g, hipStream_t s);
 // (rows % 32 == 0, cols % 8 == 0).
 hipError_t mxfp4_quantize_t(const uint16_t* x, int64_t rows, int64_t cols, uint8_t* codes, uint8_t* scales,
                             hipStream_t s);
+// Both directions at once from one read of x (rows % 64 == 0, cols % 128 ==
+// 0): codes/scales as mxfp4_quantize, codes_t/scales_t as mxfp4_quantize_t;
+// either pair may be null (not both).
+hipError_t mxfp4_quantize_both(const uint16_t* x, int64_t rows, int64_t cols, uint8_t* codes, uint8_t* scales,
+                               uint8_t* codes_t, uint8_t* scales_t, hipStream_t s);
 // The same for MXFP6 (FP6 E2M3 elements): codes [rows, cols*3/4], 32 elements
 // of 6 bits per 24 bytes, element j at bits 6j.. of the little-endian block;
 // the GEMM takes K % 128 == 0.

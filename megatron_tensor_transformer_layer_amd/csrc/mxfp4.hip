@@ -62,10 +62,28 @@ __global__ __launch_bounds__(256) void mxfp4_quant_kernel(const uint16_t* __rest
   if ((i & 3) == 0) scales[i >> 2] = (uint8_t)sc;
 }
 
-// Along rows: lane l of a 64-lane group takes column c0 + l and one block of
-// 32 rows, so the 64 lanes read 128 consecutive bytes per row; the lane then
-// holds its block's 32 elements and writes their 16 code bytes and the scale
-// byte at row c of the transposed codes.
+// The E8M0 byte and codes of one block of 32 bf16 values (bits), as
+// mxfp4_quant_kernel forms them.
+__device__ __forceinline__ void e2m1_block(const uint32_t (&bits)[32], u32x4& w, uint32_t& sc) {
+  uint32_t mx = 0;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) mx = max(mx, bits[i] & 0x7fffu);
+  const int E = (int)(mx >> 7);
+  sc = (uint32_t)max(E - 2, 0);
+  const float mul = __uint_as_float((254u - sc) << 23);
+  w = u32x4{0, 0, 0, 0};
+#pragma unroll
+  for (int i = 0; i < 32; ++i) {
+    const float y = __uint_as_float(bits[i] << 16) * mul;
+    w[i >> 3] |= e2m1_code(y, bits[i] >> 15) << (4 * (i & 7));
+  }
+}
+
+// Along rows, for shapes the tiled kernel below does not cover: lane l of a
+// 64-lane group takes column c0 + l and one block of 32 rows, so the 64 lanes
+// read 128 consecutive bytes per row; the lane then holds its block's 32
+// elements and writes their 16 code bytes and the scale byte at row c of the
+// transposed codes.
 __global__ __launch_bounds__(256) void mxfp4_quant_t_kernel(const uint16_t* __restrict__ x, int64_t rows,
                                                             int64_t cols, uint8_t* __restrict__ codes,
                                                             uint8_t* __restrict__ scales) {
@@ -73,25 +91,68 @@ __global__ __launch_bounds__(256) void mxfp4_quant_t_kernel(const uint16_t* __re
   const int64_t rb = (int64_t)blockIdx.y * 4 + (threadIdx.x >> 6);  // block of 32 rows
   if (c >= cols || rb * 32 >= rows) return;
   uint32_t bits[32];
-  uint32_t mx = 0;
   const uint16_t* p = x + rb * 32 * cols + c;
 #pragma unroll
-  for (int i = 0; i < 32; ++i) {
-    bits[i] = p[(int64_t)i * cols];
-    mx = max(mx, bits[i] & 0x7fffu);
-  }
-  // the scale rule of mxfp4_quant_kernel
-  const int E = (int)(mx >> 7);
-  const uint32_t sc = (uint32_t)max(E - 2, 0);
-  const float mul = __uint_as_float((254u - sc) << 23);
-  u32x4 w = {0, 0, 0, 0};
-#pragma unroll
-  for (int i = 0; i < 32; ++i) {
-    const float y = __uint_as_float(bits[i] << 16) * mul;
-    w[i >> 3] |= e2m1_code(y, bits[i] >> 15) << (4 * (i & 7));
-  }
+  for (int i = 0; i < 32; ++i) bits[i] = p[(int64_t)i * cols];
+  u32x4 w;
+  uint32_t sc;
+  e2m1_block(bits, w, sc);
   *reinterpret_cast<u32x4*>(codes + c * (rows / 2) + rb * 16) = w;
   scales[c * (rows / 32) + rb] = (uint8_t)sc;
+}
+
+// Tiled quantisation of x [rows, cols] (rows % 64 == 0, cols % 128 == 0): a
+// workgroup stages a 64 x 128 tile in LDS with coalesced 16-byte loads, then
+// (ROWWISE) each thread quantises one 32-element block along a row -- codes
+// [rows, cols/2], scales [rows, cols/32] -- and/or (COLWISE) one 32-element
+// block down a column -- the codes of x^T, [cols, rows/2], and scales
+// [cols, rows/32].  Both directions from one read of x.
+template <bool ROWWISE, bool COLWISE>
+__global__ __launch_bounds__(256) void mxfp4_quant_tile_kernel(const uint16_t* __restrict__ x, int64_t rows,
+                                                               int64_t cols, uint8_t* __restrict__ codes,
+                                                               uint8_t* __restrict__ scales,
+                                                               uint8_t* __restrict__ codes_t,
+                                                               uint8_t* __restrict__ scales_t) {
+  constexpr int TR = 64, TC = 128, LROW = TC * 2 + 16;  // LDS row stride (bytes), padded
+  __shared__ __attribute__((aligned(16))) char tile[TR * LROW];
+  const int t = threadIdx.x;
+  const int64_t r0 = (int64_t)blockIdx.y * TR, c0 = (int64_t)blockIdx.x * TC;
+#pragma unroll
+  for (int pass = 0; pass < 4; ++pass) {  // 16 rows of 16 lanes x 16 bytes per pass
+    const int r = pass * 16 + (t >> 4), ch = t & 15;
+    const u32x4 v = *reinterpret_cast<const u32x4*>(x + (r0 + r) * cols + c0 + ch * 8);
+    *reinterpret_cast<u32x4*>(tile + r * LROW + ch * 16) = v;
+  }
+  __syncthreads();
+  if constexpr (ROWWISE) {  // thread: row t / 4, block t % 4 (4 threads write 64 contiguous code bytes)
+    const int r = t >> 2, b = t & 3;
+    uint32_t bits[32];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const u32x4 v = *reinterpret_cast<const u32x4*>(tile + r * LROW + b * 64 + q * 16);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        bits[q * 8 + 2 * j] = v[j] & 0xffffu;
+        bits[q * 8 + 2 * j + 1] = v[j] >> 16;
+      }
+    }
+    u32x4 w;
+    uint32_t sc;
+    e2m1_block(bits, w, sc);
+    *reinterpret_cast<u32x4*>(codes + (r0 + r) * (cols / 2) + c0 / 2 + b * 16) = w;
+    scales[(r0 + r) * (cols / 32) + c0 / 32 + b] = (uint8_t)sc;
+  }
+  if constexpr (COLWISE) {  // thread: column t / 2, row block t % 2
+    const int c = t >> 1, rb = t & 1;
+    uint32_t bits[32];
+#pragma unroll
+    for (int i = 0; i < 32; ++i) bits[i] = *reinterpret_cast<const uint16_t*>(tile + (rb * 32 + i) * LROW + c * 2);
+    u32x4 w;
+    uint32_t sc;
+    e2m1_block(bits, w, sc);
+    *reinterpret_cast<u32x4*>(codes_t + (c0 + c) * (rows / 2) + r0 / 2 + rb * 16) = w;
+    scales_t[(c0 + c) * (rows / 32) + r0 / 32 + rb] = (uint8_t)sc;
+  }
 }
 
 // FP6 E2M3 code of y (|y| < 8 by the block scale): below 1 the spacing is 1/8
@@ -476,10 +537,29 @@ hipError_t mxfp4_gemm(const Mxfp4GemmArgs& g, hipStream_t s) {
   return hipGetLastError();
 }
 
+hipError_t mxfp4_quantize_both(const uint16_t* x, int64_t rows, int64_t cols, uint8_t* codes, uint8_t* scales,
+                               uint8_t* codes_t, uint8_t* scales_t, hipStream_t s) {
+  if (rows <= 0 || cols <= 0) return hipSuccess;
+  if (rows % 64 || cols % 128 || rows / 64 > 65535 || cols / 128 > INT32_MAX) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)(cols / 128), (unsigned)(rows / 64));
+  if (codes && codes_t)
+    hipLaunchKernelGGL((mxfp4_quant_tile_kernel<true, true>), grid, dim3(256), 0, s, x, rows, cols, codes, scales,
+                       codes_t, scales_t);
+  else if (codes_t)
+    hipLaunchKernelGGL((mxfp4_quant_tile_kernel<false, true>), grid, dim3(256), 0, s, x, rows, cols, codes, scales,
+                       codes_t, scales_t);
+  else
+    hipLaunchKernelGGL((mxfp4_quant_tile_kernel<true, false>), grid, dim3(256), 0, s, x, rows, cols, codes, scales,
+                       codes_t, scales_t);
+  return hipGetLastError();
+}
+
 hipError_t mxfp4_quantize_t(const uint16_t* x, int64_t rows, int64_t cols, uint8_t* codes, uint8_t* scales,
                             hipStream_t s) {
   if (rows <= 0 || cols <= 0) return hipSuccess;
   if (rows % 32) return hipErrorInvalidValue;
+  if (rows % 64 == 0 && cols % 128 == 0 && rows / 64 <= 65535)  // whole 64 x 128 tiles
+    return mxfp4_quantize_both(x, rows, cols, nullptr, nullptr, codes, scales, s);
   const int64_t gx = (cols + 63) / 64, gy = (rows / 32 + 3) / 4;
   if (gx > INT32_MAX || gy > 65535) return hipErrorInvalidValue;
   hipLaunchKernelGGL(mxfp4_quant_t_kernel, dim3((unsigned)gx, (unsigned)gy), dim3(256), 0, s, x, rows, cols, codes,

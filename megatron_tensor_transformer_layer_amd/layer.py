@@ -105,14 +105,14 @@ class RankState:
 
 
 def run_sharded_layer(shape, tp: int, shards: list, x_bits, b_o_bits, b2_bits, dy_bits, residual: bool = False,
-                      precision: int = MTL_PREC_BF16, device=DEV, sp: bool = False) -> dict:
+                      precision: int = MTL_PREC_BF16, device=DEV, sp: bool = False, flags: int = 0) -> dict:
     """Run the whole layer as tp rank shards plus the four full reductions on
     one device; returns host fp64 copies of every output.  With sp, the
     sequence-parallel form: every rank holds full-size buffers of X, H, dY, dH
     with only its own row share filled, reduces only its share of each sum and
     gathers the peers' shares in place (mtl_allgather_rows) before the next
     column-parallel linear; Y and dX stay row-sharded."""
-    ranks = [RankState(shape, tp, r, shards[r], device=device, precision=precision) for r in range(tp)]
+    ranks = [RankState(shape, tp, r, shards[r], flags=flags, device=device, precision=precision) for r in range(tp)]
     D = ranks[0].D
     if sp:
         return _run_sp(ranks, tp, D, x_bits, b_o_bits, b2_bits, dy_bits, residual, device)
@@ -212,8 +212,9 @@ class AllShardsStep:
     small launches run side by side instead of one after the other."""
 
     def __init__(self, shape, tp: int, shards: list, x_bits, dy_bits, b_o_bits, b2_bits, device=DEV,
-                 precision: int = MTL_PREC_BF16, concurrent: bool = False):
-        self.ranks = [RankState(shape, tp, r, shards[r], device=device, precision=precision) for r in range(tp)]
+                 precision: int = MTL_PREC_BF16, concurrent: bool = False, flags: int = 0):
+        self.ranks = [RankState(shape, tp, r, shards[r], flags=flags, device=device, precision=precision)
+                      for r in range(tp)]
         D = self.D = self.ranks[0].D
         self.x, self.dy = bf16_dev(x_bits, device), bf16_dev(dy_bits, device)
         self.b_o, self.b2 = bf16_dev(b_o_bits, device), bf16_dev(b2_bits, device)

@@ -288,3 +288,22 @@ def test_fp8_layer_full_size_7b_tp4(mtl):
         if why:
             bad.append(f"{k}: {why}")
     assert not bad, bad
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("case", ["gpt2-small-tp2", "d128-mb2-tp2"])
+def test_fp8_kept_codes_are_bit_identical(mtl, case):
+    """With MTL_F_FP8_KEEP_CODES the backward takes the transposed codes of x,
+    o, h and a that the forward wrote instead of quantising them again: every
+    output equals the layer without the flag bit for bit."""
+    from megatron_tensor_transformer_layer_amd.layer import run_sharded_layer
+    shape, residual = FP8_CASES[case]
+    print(f"fp8 kept codes {case} {shape}", flush=True)
+    full = synth.layer_inputs(shape, seed=0)
+    shards = [synth.layer_inputs(shape, seed=0, tp=shape.tp, rank=r) for r in range(shape.tp)]
+    run = lambda flags: run_sharded_layer(shape, shape.tp, shards, full["x"], full["b_o"], full["b2"], full["dy"],
+                                          residual, precision=mtl.MTL_PREC_FP8_HYBRID, flags=flags)
+    a, b = run(0), run(mtl.MTL_F_FP8_KEEP_CODES)
+    for k, v in a.items():
+        if isinstance(v, np.ndarray):
+            assert np.array_equal(v, b[k]), k

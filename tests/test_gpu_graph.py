@@ -13,7 +13,7 @@ def _snapshot(outs):
 
 
 @pytest.mark.gpu
-@pytest.mark.parametrize("case", ["gpt2-small-tp2", "ragged-tp2-fp8", "gpt2-small-tp2-concurrent"])
+@pytest.mark.parametrize("case", ["gpt2-small-tp2", "ragged-tp2-fp8", "ragged-tp2-fp8-kept", "gpt2-small-tp2-concurrent"])
 def test_graph_replays_match_eager_step(mtl, case):
     import torch
     from megatron_tensor_transformer_layer_amd.layer import AllShardsStep
@@ -25,8 +25,9 @@ def test_graph_replays_match_eager_step(mtl, case):
     print(f"graph case {case} {shape}", flush=True)
     full = synth.layer_inputs(shape, seed=0)
     shards = [synth.layer_inputs(shape, seed=0, tp=shape.tp, rank=r) for r in range(shape.tp)]
+    flags = mtl.MTL_F_FP8_KEEP_CODES if case.endswith("kept") else 0
     step = AllShardsStep(shape, shape.tp, shards, full["x"], full["dy"], full["b_o"], full["b2"], precision=prec,
-                         concurrent=case.endswith("concurrent"))
+                         concurrent=case.endswith("concurrent"), flags=flags)
     step()
     torch.cuda.synchronize()
     eager = _snapshot(step.outputs())
