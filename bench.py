@@ -66,6 +66,9 @@ def parse():
     ap.add_argument("--cpu-sample-seq", type=int, default=4096)
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run only a plain device copy of known size (for scaling HBM byte counters)")
+    ap.add_argument("--mfma-ceiling", action="store_true",
+                    help="time the MFMA-only kernel (the 256x256-tile GEMM's MFMA stream of a 4096^3 product with "
+                         "every operand in registers) in bf16 and fp8 on N(0,1) operands, and exit")
     ap.add_argument("--copy-rate", action="store_true",
                     help="time the plain copy at 64 MiB, 256 MiB and 1 GiB (the practical HBM ceiling) and exit")
     return ap.parse_args()
@@ -123,6 +126,37 @@ def copy_rate():
         print(json.dumps({"copy_mib": mib, "us_per_launch": round(us, 2),
                           "gb_per_s": round(2 * rows * cols * 2 / us / 1e3, 1)}), flush=True)
         del src, dst
+
+
+def mfma_ceiling():
+    """The matrix cores' own rate: mtl_mfma_ceiling issuing the MFMAs of a
+    4096x4096x4096 product in 256x256 tiles (256 workgroups of 4 waves) with
+    every operand in registers, on N(0,1) bf16 values and on their E4M3 codes;
+    HIP events around 20 launches after 3 untimed ones."""
+    import torch
+    from megatron_tensor_transformer_layer_amd import MTL_CEILING_DATA_BYTES, mtl_mfma_ceiling
+    g = torch.Generator(device="cuda").manual_seed(0)
+    wgs = 256
+    out = torch.empty(wgs * 256, dtype=torch.float32, device="cuda")
+    for kind, name, iters, per_iter, peak in ((0, "bf16", 128, 1 << 20, PEAK_BF16_TFLOPS),
+                                               (1, "fp8", 64, 2 << 20, PEAK_FP8_TFLOPS)):
+        vals = torch.randn(MTL_CEILING_DATA_BYTES // (2 if kind == 0 else 1), device="cuda", generator=g)
+        data = vals.to(torch.bfloat16) if kind == 0 else vals.to(torch.float8_e4m3fn)
+        for _ in range(3):
+            mtl_mfma_ceiling(data, kind, wgs, iters, out)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        reps = 20
+        e0.record()
+        for _ in range(reps):
+            mtl_mfma_ceiling(data, kind, wgs, iters, out)
+        e1.record()
+        torch.cuda.synchronize()
+        assert torch.isfinite(out).all()
+        us = e0.elapsed_time(e1) * 1e3 / reps
+        flop = wgs * 4 * iters * per_iter
+        print(json.dumps({"mfma_ceiling": name, "flop_per_launch": flop, "workgroups": wgs, "iters": iters,
+                          "us_per_launch": round(us, 2), "tflops": round(flop / us / 1e6, 1),
+                          "frac_of_peak": round(flop / us / 1e6 / peak, 4), "peak": peak}), flush=True)
 
 
 def cpu_baseline(shape, rank, sample_seq, precision="bf16"):
@@ -941,6 +975,9 @@ def main():
         return
     if args.copy_rate:
         copy_rate()
+        return
+    if args.mfma_ceiling:
+        mfma_ceiling()
         return
     import torch
     import synth

@@ -25,6 +25,7 @@ MTL_CP_MAX = 64
 MTL_F_RESIDUAL, MTL_F_WGRAD_ACCUM, MTL_F_FP8_KEEP_CODES = 1, 2, 4
 MTL_PROF_MAX = 2048
 MTL_NOALLOC_SCRATCH_BYTES = 48 << 20
+MTL_CEILING_DATA_BYTES = 1 << 20
 MTL_PROF_KINDS = ("gemm", "attention", "reduce", "colsum", "quantize", "gather")
 
 
@@ -84,6 +85,7 @@ _SIGS = {
     "mtl_moe_bwd": (ctypes.c_int, [_MCFG] + [_P] * 17 + [_SZ, _P]),
     "mtl_attn_bwd_scratch_layout": (ctypes.c_int, [_CFG, ctypes.POINTER(_SZ), ctypes.POINTER(_SZ)]),
     "mtl_mlp_bwd_noalloc": (ctypes.c_int, [_CFG, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P]),
+    "mtl_mfma_ceiling": (ctypes.c_int, [_P, _SZ, _I32, _I64, _I64, _P, _P]),
     "mtl_prof_start": (ctypes.c_int, []),
     "mtl_prof_stop": (ctypes.c_int, [ctypes.POINTER(_I32)]),
     "mtl_prof_record": (ctypes.c_int, [_I32, ctypes.POINTER(_I32), ctypes.POINTER(ctypes.c_double),
@@ -360,6 +362,11 @@ def mtl_prof_record(i: int) -> dict:
                                  ctypes.byref(name)), "mtl_prof_record")
     return dict(kind=MTL_PROF_KINDS[kind.value], name=name.value.decode(), flop=flop.value, bytes=nbytes.value,
                 ms=ms.value)
+
+
+def mtl_mfma_ceiling(data, kind, workgroups, iters, out, data_bytes=None, stream=None):
+    _check(lib().mtl_mfma_ceiling(_ptr(data), _nbytes(data, data_bytes), kind, workgroups, iters, _ptr(out),
+                                  _stream(stream)), "mtl_mfma_ceiling")
 
 
 def mtl_fp8_gemm(M, N, K, a, fmt_a, a_rec, b, fmt_b, b_rec, bias, c, ldc=None, stream=None):

@@ -381,3 +381,16 @@ def test_fp8_keep_codes_flag(mtl):
     assert mtl.mtl_workspace_bytes(kept) == mtl.mtl_workspace_bytes(base) + extra
     bad = mtl.make_cfg(768, 12, 3072, 512, 1, 2, 0, mtl.MTL_PREC_BF16, mtl.MTL_F_FP8_KEEP_CODES)
     assert mtl.mtl_validate(bad) == mtl.MTL_E_UNSUPPORTED
+
+
+def test_mfma_ceiling_argument_checks(mtl):
+    """mtl_mfma_ceiling refuses bad arguments before any HIP call."""
+    import ctypes
+    f = mtl.lib().mtl_mfma_ceiling
+    fake = ctypes.c_void_p(1 << 20)
+    assert f(None, 1 << 20, 0, 256, 1, fake, None) == mtl.MTL_E_NULL
+    assert f(ctypes.c_void_p((1 << 20) + 8), 1 << 20, 0, 256, 1, fake, None) == mtl.MTL_E_ALIGN
+    assert f(fake, 1 << 20, 2, 256, 1, fake, None) == mtl.MTL_E_UNSUPPORTED
+    assert f(fake, (1 << 20) - 16, 0, 256, 1, fake, None) == mtl.MTL_E_SHAPE
+    assert f(fake, 1 << 20, 0, 0, 1, fake, None) == mtl.MTL_E_SHAPE
+    assert f(fake, 1 << 20, 1, 256, 0, fake, None) == mtl.MTL_E_SHAPE
