@@ -503,7 +503,7 @@ def moe_group_rates(groups, n, h, f, el, tokens, k):
         us = v["ms"] * 1e3 / max(v["launches"], 1)
         fl = 2.0 * n * h * f if v["kind"] == "gemm" else 0.0
         b = by.get(name, 0.0)
-        out[name] = {"kind": v["kind"], "us": round(us, 1), "flop": fl,
+        out[name] = {"kind": v["kind"], "us": round(us, 1), "flop": fl, "bytes": b,
                      "tflops": round(fl / (us / 1e6) / 1e12, 1) if fl else None,
                      "gb_per_s": round(b / (us / 1e6) / 1e9, 1), "frac_of_hbm_peak": round(b / (us / 1e6) / 1e9 /
                                                                                          PEAK_HBM_GBS, 4)}
@@ -564,10 +564,21 @@ def moe_main(args):
     fwd_ms = float(np.mean([a.elapsed_time(b) for a, b in fwd_ev]))
     groups, _ = prof_window(step, 2)
     moe_groups = moe_group_rates(groups, n, shape.hidden, shape.ffn, El, shape.tokens, shape.topk)
-    # mtl_moe_fwd = gather + two grouped GEMM launches (2*N*h*f FLOP each) + combine;
-    # the per-launch rate below charges the gather and combine to the GEMMs
-    gemm_launch_s = fwd_ms / 2 / 1e3
-    achieved = 2.0 * n * shape.hidden * shape.ffn / gemm_launch_s / 1e12
+    # the roofline kernel: the grouped GEMM launch that takes the most time; it is
+    # bound by HBM when its FLOP per byte moved lies below the ridge point
+    # (peak FLOP/s over peak bytes/s), else by the matrix cores
+    dom = max((k for k, v in moe_groups.items() if v["kind"] == "gemm"), key=lambda k: moe_groups[k]["us"])
+    dg = moe_groups[dom]
+    hbm = dg["flop"] / dg["bytes"] < PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)
+    if hbm:
+        roof = {"bound": "hbm", "achieved": dg["gb_per_s"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(dg["gb_per_s"] / PEAK_HBM_GBS, 4)}
+    else:
+        roof = {"bound": "mfma", "achieved": dg["tflops"], "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(dg["tflops"] / PEAK_BF16_TFLOPS, 4)}
+    roof.update(kernel=f"{dom}: gemm_bf16_kernel grouped over the rank's experts (256x256 tiles), HIP events around "
+                       "the launch", traffic=None, launch_us=dg["us"], flop_per_launch=dg["flop"],
+                bytes_per_launch=dg["bytes"], flop_per_byte=round(dg["flop"] / dg["bytes"], 1))
     out = {
         "metric": "TFLOP/s per EP-rank MoE expert block fwd+bwd (bf16) and % of MI355X MFMA peak",
         "value": round(fl / (ms / 1e3) / 1e12, 2),
@@ -587,12 +598,8 @@ def moe_main(args):
                    "global_batch": 1, "seq_len": shape.tokens, "parallelism": f"ep{shape.ep}-rank{r}-of-1gpu"},
         "pct_of_peak": round(100 * fl / (ms / 1e3) / 1e12 / PEAK_BF16_TFLOPS, 2),
         "flop_per_step": fl,
-        "roofline": {"bound": "mfma",
-                     "kernel": "gemm_bf16_kernel grouped over experts, 256x256 tiles: the two launches of "
-                               "mtl_moe_fwd (fc1 + GeLU, fc2), gather and combine included",
-                     "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
-                     "gemm_launch_us": round(gemm_launch_s * 1e6, 2)},
+        "roofline": roof,
+        "forward_ms": round(fwd_ms, 4),
         "launch_groups": moe_groups,
         "gemm_tflops": round(sum(v["flop"] for v in moe_groups.values()) /
                              (sum(v["us"] for v in moe_groups.values() if v["kind"] == "gemm") / 1e6) / 1e12, 1),
