@@ -24,11 +24,12 @@ CXXFLAGS = [
 ]
 
 
-# Per-source options.  attention.hip: keep MFMA accumulators in architectural
-# VGPRs (its kernels fit in 256), which spares the AGPR<->VGPR copies the
-# compiler otherwise inserts around the softmax of every key block.
+# Per-source options.  attention.hip, attn_fwd.hip: keep MFMA accumulators in
+# architectural VGPRs, which spares the AGPR<->VGPR copies the compiler
+# otherwise inserts around the softmax of every key block.
 SOURCE_FLAGS = {
     "attention.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
+    "attn_fwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
 }
 
 

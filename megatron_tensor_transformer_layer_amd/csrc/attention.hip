@@ -1,4 +1,5 @@
-// Causal multi-head attention, forward and backward, for gfx950.
+// Causal multi-head attention, backward, for gfx950 (the forward is in
+// attn_fwd.hip).
 //
 // Operation (per head n, per micro-batch element): S = Q K^T * scale with key
 // j > query i masked, P = row-softmax(S), O = P V; the row log-sum-exp L is
@@ -35,237 +36,6 @@ __device__ __forceinline__ u32x4 pack_half(const f32x16& p, int half) {
 }
 
 __device__ __forceinline__ float xor32(float v) { return __shfl_xor(v, 32); }
-
-// ============================================================== forward
-// Work item: 64 queries of one head.  A workgroup (4 waves) takes the mirrored
-// pair of items (p, n-1-p) one after the other, so every workgroup sees the same
-// number of causal key blocks (n+1 of 64 keys).  Within an item, wave w handles
-// queries (w & 1)*32 .. +31 and the key blocks of parity w >> 1; the two
-// parities' online-softmax states are merged through LDS at the end of the item.
-// K and V tiles of two key blocks per stage arrive by LDS DMA in their global
-// layout; V^T fragments for the P.V product are read with ds_read_b64_tr_b16.
-template <int D>
-struct FwdTiles {
-  static constexpr int RB = 2 * D;              // bytes per key row
-  static constexpr int TILE = 64 * RB;          // one 64-key K or V tile
-  static constexpr int STAGE = 4 * TILE;        // K(even) V(even) K(odd) V(odd)
-  static constexpr int PER_TILE = TILE / 1024;  // DMA wave instructions per tile
-  static constexpr int PER_WAVE = 4 * PER_TILE / 4;
-  // 64-bank swizzles: K rows are read 16 rows per cycle (ds_read_b128), V rows
-  // 4 at a time by the transpose read; both maps are bijections on a row.
-  static __device__ __forceinline__ int kswz(int row) { return D == 128 ? (row & 15) : ((row >> 1) & 7); }
-  static __device__ __forceinline__ int vswz(int row) { return D == 128 ? ((row & 3) << 2) : (((row >> 1) & 1) << 2); }
-
-  // DMA the K and V tiles of key blocks kb0 and kb0+1 (64 keys each).
-  static __device__ __forceinline__ void load(i32x4 rs, int64_t ld, int64_t tok0, int colq, int kb0, LDS_AS char* st) {
-    const int lane = threadIdx.x & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-#pragma unroll
-    for (int q = 0; q < PER_WAVE; ++q) {
-      const int I = wave * PER_WAVE + q;
-      const int tile = I / PER_TILE;            // 0 K even, 1 V even, 2 K odd, 3 V odd
-      const int o = (I % PER_TILE) * 1024 + lane * 16;
-      const int row = o / RB;
-      const int pc = (o % RB) >> 4;
-      const bool isv = tile & 1;
-      const int c = pc ^ (isv ? vswz(row) : kswz(row));
-      const int key = (kb0 + (tile >> 1)) * 64 + row;
-      const uint32_t voff = (uint32_t)(((tok0 + key) * ld + colq + (isv ? 2 * D : D) + c * 8) * 2);
-      dma16(rs, voff, 0u, lds_addr(st + I * 1024));
-    }
-  }
-  // a-operand fragment of K (rows = keys row0 + l%32, 8 dims of k step ks)
-  static __device__ __forceinline__ u32x4 kfrag(const LDS_AS char* k, int row0, int ks, int lane) {
-    const int row = row0 + (lane & 31);
-    const int c = ks * 2 + (lane >> 5);
-    return *reinterpret_cast<const LDS_AS u32x4*>(k + row * RB + ((c ^ kswz(row)) << 4));
-  }
-  // a-operand fragment of V^T (rows = dims i*32 + l%32); its k slots are keys
-  // ks*16 + 8*(j/4) + 4*(l/32) + j%4, the order of a 32x32 accumulator's rows.
-  static __device__ __forceinline__ u32x4 vfrag(const LDS_AS char* v, int i, int ks, int lane) {
-    const int G = lane >> 4, R = (lane >> 2) & 3, c4 = lane & 3;
-    const int key = ks * 16 + 4 * (G >> 1) + R;
-    const int dim = i * 32 + (G & 1) * 16 + 4 * c4;
-    const LDS_AS char* p = v + key * RB + (((dim >> 3) ^ vswz(key)) << 4) + ((dim & 7) >> 2) * 8;
-    const u32x2 lo = read_tr(p);
-    const u32x2 hi = read_tr(p + 8 * RB);
-    return u32x4{lo[0], lo[1], hi[0], hi[1]};
-  }
-};
-
-// FULL: queries of a.qkv against every key of a separate chunk a.kv (a.kv_seq
-// keys, a multiple of 64, same head-interleaved layout): no mask, every item
-// takes all key blocks.  Otherwise causal self-attention of a.qkv.
-template <int D, bool FULL>
-__global__ __launch_bounds__(256, 1) void attn_fwd_kernel(AttnArgs a) {
-  using T = FwdTiles<D>;
-  constexpr int KS = D / 16;
-  constexpr int DB = D / 32;
-  __shared__ __attribute__((aligned(1024))) char st0_[T::STAGE];
-  __shared__ __attribute__((aligned(1024))) char st1_[T::STAGE];
-  LDS_AS char* st0 = (LDS_AS char*)st0_;
-  LDS_AS char* st1 = (LDS_AS char*)st1_;
-
-  // one work unit = (mirrored item pair, head, batch element); the units of a
-  // head share its K and V, so a head's units are kept on one XCD
-  const int nitems = (a.seq + 63) / 64;
-  const int npairs = (nitems + 1) / 2;
-  const int u = xcd_index(blockIdx.x, npairs * a.heads * a.batch);
-  const int pair = u % npairs, n = (u / npairs) % a.heads, b = u / (npairs * a.heads);
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, g = lane >> 5;
-  const int qsub = wave & 1, kpar = wave >> 1;
-  const int64_t tokens = (int64_t)a.seq * a.batch;
-  const int64_t tok0 = (int64_t)b * a.seq;
-  const int colq = n * 3 * D;
-  const uint16_t* qbase = a.qkv + tok0 * a.ld_qkv + colq;
-  const float c = a.scale * LOG2E;
-  // K and V tiles come from the buffer resource rs, starting at token kvtok0
-  const i32x4 rs = FULL ? make_rsrc(a.kv, (uint32_t)((int64_t)a.kv_seq * a.batch * a.ld_qkv * 2))
-                        : make_rsrc(a.qkv, (uint32_t)(tokens * a.ld_qkv * 2));
-  const int64_t kvtok0 = FULL ? (int64_t)b * a.kv_seq : tok0;
-  const int nkb_all = FULL ? a.kv_seq / 64 : nitems;
-
-  for (int side = 0; side < 2; ++side) {
-    const int item = side == 0 ? pair : nitems - 1 - pair;
-    if (side == 1 && item == pair) break;
-    const int q0 = item * 64;
-    const int qw = q0 + qsub * 32;
-    const int q = qw + (lane & 31);
-    const bool qok = q < a.seq;
-    const int nkb = FULL ? nkb_all : min(item + 1, nkb_all);
-    const int niter = (nkb + 1) / 2;
-
-    u32x4 qf[KS];
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
-      qf[ks] = qok ? *reinterpret_cast<const u32x4*>(qbase + (int64_t)q * a.ld_qkv + ks * 16 + g * 8)
-                   : u32x4{0, 0, 0, 0};
-    wait_loads();
-    f32x16 o[DB];
-#pragma unroll
-    for (int i = 0; i < DB; ++i) o[i] = f32x16{};
-    float m = -INFINITY, l = 0.f;
-
-    // one key block from the K and V tiles of this wave's parity in stage st
-    auto block = [&](const LDS_AS char* st, int kb) {
-      const LDS_AS char* kt = st + kpar * 2 * T::TILE;
-      const LDS_AS char* vt = kt + T::TILE;
-      const int k0 = kb * 64;
-      f32x16 s[2] = {f32x16{}, f32x16{}};
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks)
-#pragma unroll
-        for (int sb = 0; sb < 2; ++sb) s[sb] = mfma32(T::kfrag(kt, sb * 32, ks, lane), qf[ks], s[sb]);
-      const bool diag = !FULL && (k0 + 63 > qw);
-      // every processed block holds key k0 <= q (or, FULL, 64 unmasked keys), so bmax is finite
-      if (diag) {  // wave-uniform: only the diagonal block is masked
-        asm volatile("" ::: "memory");
-#pragma unroll
-        for (int sb = 0; sb < 2; ++sb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int key = k0 + sb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
-            if (key > q) s[sb][r] = -INFINITY;
-          }
-      }
-      float bmax = -INFINITY;
-#pragma unroll
-      for (int sb = 0; sb < 2; ++sb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) bmax = fmaxf(bmax, s[sb][r]);
-      bmax = fmaxf(bmax, xor32(bmax));
-      // The reference max m moves (and l, o are rescaled) only when some row's
-      // block max exceeds it by more than 2^8 in the exponent; otherwise the
-      // probabilities are taken against the stale m (at most 2^8, exact in the
-      // final normalisation), which spares the accumulator rescale.
-      if (__any((bmax - m) * c > 8.f)) {
-        asm volatile("" ::: "memory");  // keep this a branch, not a select on alpha
-        const float mx = fmaxf(m, bmax);
-        const float alpha = __builtin_amdgcn_exp2f((m - mx) * c);
-        l *= alpha;
-#pragma unroll
-        for (int i = 0; i < DB; ++i) o[i] *= alpha;
-        m = mx;
-      }
-      const float mc = m * c;
-      float rsum = 0.f;
-#pragma unroll
-      for (int sb = 0; sb < 2; ++sb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float pv = __builtin_amdgcn_exp2f(s[sb][r] * c - mc);
-          s[sb][r] = pv;
-          rsum += pv;
-        }
-      l += rsum;
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        const u32x4 pb = pack_half(s[ks >> 1], ks & 1);
-#pragma unroll
-        for (int i = 0; i < DB; ++i) o[i] = mfma32(T::vfrag(vt, i, ks, lane), pb, o[i]);
-      }
-    };
-
-    T::load(rs, a.ld_qkv, kvtok0, colq, 0, st0);
-    wait_dma();
-    __syncthreads();
-    for (int it = 0; it < niter; it += 2) {
-      const bool more1 = it + 1 < niter;
-      if (more1) T::load(rs, a.ld_qkv, kvtok0, colq, 2 * (it + 1), st1);
-      {
-        const int kb = 2 * it + kpar;
-        if (kb < nkb && (FULL || kb * 64 <= qw + 31)) block(st0, kb);
-      }
-      if (more1) wait_dma();
-      __syncthreads();
-      if (more1) {
-        const bool more2 = it + 2 < niter;
-        if (more2) T::load(rs, a.ld_qkv, kvtok0, colq, 2 * (it + 2), st0);
-        const int kb = 2 * (it + 1) + kpar;
-        if (kb < nkb && (FULL || kb * 64 <= qw + 31)) block(st1, kb);
-        if (more2) wait_dma();
-        __syncthreads();
-      }
-    }
-
-    // merge the odd-parity waves' state into the even ones (stage 0 is free)
-    float* mg = reinterpret_cast<float*>((char*)st0_) + qsub * (2 + 16 * DB) * 64;
-    if (kpar == 1) {
-      mg[lane] = m;
-      mg[64 + lane] = l;
-#pragma unroll
-      for (int i = 0; i < DB; ++i)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mg[(2 + i * 16 + r) * 64 + lane] = o[i][r];
-    }
-    __syncthreads();
-    if (kpar == 0) {
-      const float m2 = mg[lane], l2 = mg[64 + lane];
-      const float mt = fmaxf(m, m2);
-      const float a1 = __builtin_amdgcn_exp2f((m - mt) * c), a2 = __builtin_amdgcn_exp2f((m2 - mt) * c);
-      const float lp = l * a1 + l2 * a2;
-      const float lt = lp + xor32(lp);
-      if (qok) {
-        const float inv = 1.f / lt;
-        uint16_t* orow = a.o + (tok0 + q) * a.ld_o + (int64_t)n * D;
-#pragma unroll
-        for (int i = 0; i < DB; ++i) {
-          float v[16];
-#pragma unroll
-          for (int r = 0; r < 16; ++r) v[r] = (o[i][r] * a1 + mg[(2 + i * 16 + r) * 64 + lane] * a2) * inv;
-#pragma unroll
-          for (int gg = 0; gg < 4; ++gg) {
-            const int dim = i * 32 + 8 * gg + 4 * g;
-            *reinterpret_cast<u32x2*>(orow + dim) =
-                u32x2{pack_bf16x2(v[4 * gg], v[4 * gg + 1]), pack_bf16x2(v[4 * gg + 2], v[4 * gg + 3])};
-          }
-        }
-        if (g == 0) a.lse[(int64_t)n * tokens + tok0 + q] = mt * a.scale + logf(lt);
-      }
-    }
-    __syncthreads();  // the next item's DMA reuses stage 0
-  }
-}
 
 // ============================================================== backward: D
 // delta[n][tok] = sum_i dO[tok][n*d+i] * O[tok][n*d+i]; eight lanes per
@@ -576,15 +346,6 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_kernel(AttnArgs a) {
 }
 
 // ============================================================== launchers
-template <int D, bool FULL>
-static hipError_t fwd_d(const AttnArgs& a, hipStream_t s) {
-  const int64_t npairs = ((a.seq + 63) / 64 + 1) / 2;
-  const int64_t units = npairs * a.heads * a.batch;
-  if (units > INT32_MAX) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((attn_fwd_kernel<D, FULL>), dim3((unsigned)units), dim3(256), 0, s, a);
-  return hipGetLastError();
-}
-
 // with_delta: compute D = rowsum(dO * O) first (the FULL calls of one set of
 // queries reuse the D of their first call)
 template <int D, bool FULL>
@@ -601,20 +362,6 @@ static hipError_t bwd_d(const AttnArgs& a, bool with_delta, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t attention_fwd(const AttnArgs& a, hipStream_t s) {
-  if (a.seq <= 0) return hipSuccess;
-  if (a.d == 64) return fwd_d<64, false>(a, s);
-  if (a.d == 128) return fwd_d<128, false>(a, s);
-  return hipErrorInvalidValue;
-}
-
-hipError_t attention_fwd_full(const AttnArgs& a, hipStream_t s) {
-  if (a.seq <= 0) return hipSuccess;
-  if (!a.kv || a.kv_seq <= 0 || a.kv_seq % 64 != 0) return hipErrorInvalidValue;
-  if (a.d == 64) return fwd_d<64, true>(a, s);
-  if (a.d == 128) return fwd_d<128, true>(a, s);
-  return hipErrorInvalidValue;
-}
 
 hipError_t attention_bwd(const AttnArgs& a, hipStream_t s) {
   if (a.seq <= 0) return hipSuccess;
