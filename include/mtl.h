@@ -69,14 +69,15 @@ enum {
   MTL_F_RESIDUAL = 1,   /* mtl_reduce callers add residuals; recorded for validation only */
   MTL_F_WGRAD_ACCUM = 2, /* weight/bias gradients are accumulated (+=) instead of written */
   /* fp8 only: the forward calls also write the transposed E4M3 codes and scale
-   * records of x, o (mtl_attn_fwd) and h, a (mtl_mlp_fwd) into a region at the
-   * start of the scratch (mtl_workspace_bytes counts it; each call's own
-   * scratch follows it), and the backward calls read them there
-   * instead of quantising those tensors again (bit-identical results: the
-   * same tensor, format and amax give the same codes).  The caller passes the
-   * same scratch buffer to the rank's four calls of a step, leaves that region
-   * alone between a forward call and its backward, and passes the backward the
-   * same x and h (and saved o, a) as the forward -- as a training step does. */
+   * records of x, o (mtl_attn_fwd) and h, a (mtl_mlp_fwd), and the E4M3 codes
+   * of their weights in both orientations (w_qkv, w_o; w1, w2), into a region
+   * at the start of the scratch (mtl_workspace_bytes counts it; each call's own
+   * scratch follows it), and the backward calls read them there instead of
+   * quantising those tensors again (bit-identical results: the same tensor,
+   * format and amax give the same codes).  The caller passes the same scratch
+   * buffer to the rank's four calls of a step, leaves that region alone between
+   * a forward call and its backward, and passes the backward the same x, h and
+   * weights (and saved o, a) as the forward -- as a training step does. */
   MTL_F_FP8_KEEP_CODES = 4
 };
 

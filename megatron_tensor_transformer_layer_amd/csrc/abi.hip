@@ -274,11 +274,13 @@ inline bool is_mx4(const mtl_layer_cfg* c) { return c->precision == MTL_PREC_MXF
 inline bool keeps_codes(const mtl_layer_cfg* c) { return is_fp8(c) && (c->flags & MTL_F_FP8_KEEP_CODES); }
 
 // With MTL_F_FP8_KEEP_CODES: the transposed E4M3 codes (and scale records) of
-// x, o, h and a, written by the forward calls at the start of the scratch and
-// read there by the backward calls, which then do not quantise these tensors
-// again (the same tensor, format and amax give the same codes).
+// x, o, h and a, and the four weights' E4M3 codes in both orientations, written
+// by the forward calls at the start of the scratch and read there by the
+// backward calls, which then do not quantise these tensors again (the same
+// tensor, format and amax give the same codes).
 struct Kept {
   Q8 x_t, o_t, h_t, a_t;
+  Q8 wqkv, wo, w1, w2;
 };
 size_t kept_scratch(const mtl_layer_cfg* c, const Dims& d, Kept* k, char* base) {
   if (!keeps_codes(c)) return 0;
@@ -288,6 +290,10 @@ size_t kept_scratch(const mtl_layer_cfg* c, const Dims& d, Kept* k, char* base) 
   t.o_t = q8(b, d.S, d.o_l, E4M3, false, true);
   t.h_t = q8(b, d.S, d.h, E4M3, false, true);
   t.a_t = q8(b, d.S, d.f_l, E4M3, false, true);
+  t.wqkv = q8(b, d.h, d.qkv_l, E4M3, true, true);
+  t.wo = q8(b, d.o_l, d.h, E4M3, true, true);
+  t.w1 = q8(b, d.h, d.f_l, E4M3, true, true);
+  t.w2 = q8(b, d.f_l, d.h, E4M3, true, true);
   if (k) *k = t;
   return b.off;
 }
@@ -488,6 +494,8 @@ mtl_status mtl_attn_fwd(const mtl_layer_cfg* c, const void* x, const void* w_qkv
     if (keeps_codes(c)) {
       ws.x = with_kept(ws.x, kp.x_t);
       ws.o = with_kept(ws.o, kp.o_t);
+      ws.wqkv_t = kp.wqkv;  // the forward's cast writes both orientations
+      ws.wo_t = kp.wo;
     }
   }
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
@@ -816,6 +824,8 @@ mtl_status mtl_mlp_fwd(const mtl_layer_cfg* c, const void* h, const void* w1, co
     if (keeps_codes(c)) {
       ws.h = with_kept(ws.h, kp.h_t);
       ws.a = with_kept(ws.a, kp.a_t);
+      ws.w1_t = kp.w1;  // the forward's cast writes both orientations
+      ws.w2_t = kp.w2;
     }
   }
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
@@ -903,9 +913,10 @@ mtl_status mtl_mlp_bwd(const mtl_layer_cfg* c, const void* dy, const void* h, co
   }
   if (is_fp8(c)) {
     // E5M2 gradients, E4M3 activations and weights; wgrad operands transposed
-    if (keeps_codes(c)) {  // a's transposed codes come from mtl_mlp_fwd
+    if (keeps_codes(c)) {  // a's transposed codes and w2's codes come from mtl_mlp_fwd
       ws.a_t = kp.a_t;
-      MTL_TRY(quantize({{dy, &ws.dy}, {w2, &ws.w2}}, ws.amax_ws, s));
+      ws.w2 = kp.w2;
+      MTL_TRY(quantize({{dy, &ws.dy}}, ws.amax_ws, s));
     } else {
       MTL_TRY(quantize({{dy, &ws.dy}, {w2, &ws.w2}, {a, &ws.a_t}}, ws.amax_ws, s));
     }
@@ -913,9 +924,10 @@ mtl_status mtl_mlp_bwd(const mtl_layer_cfg* c, const void* dy, const void* h, co
     MTL_TRY(gemm8_pair("fc2_bwd", gemm8_args(ws.a_t, ws.a_t.qt, ws.dy, ws.dy.qt, d.f_l, d.h, d.S, dw2, d.h), wepi,
                        gemm8_args(ws.dy, ws.dy.q, ws.w2, ws.w2.q, d.S, d.f_l, d.h, ws.dz, d.f_l, nullptr, nullptr, gz),
                        EPI_DGELU, s));
-    if (keeps_codes(c)) {  // and h's
+    if (keeps_codes(c)) {  // and h's and w1's
       ws.h_t = kp.h_t;
-      MTL_TRY(quantize({{ws.dz, &ws.dz8}, {w1, &ws.w1}}, ws.amax_ws, s));
+      ws.w1 = kp.w1;
+      MTL_TRY(quantize({{ws.dz, &ws.dz8}}, ws.amax_ws, s));
     } else {
       MTL_TRY(quantize({{ws.dz, &ws.dz8}, {h, &ws.h_t}, {w1, &ws.w1}}, ws.amax_ws, s));
     }
@@ -968,9 +980,10 @@ mtl_status mtl_attn_bwd(const mtl_layer_cfg* c, const void* dh, const void* x, c
     MTL_TRY(mxgemm("proj_wgrad", ws.m_o_t, ws.m_dh_t, wepi, dw_o, s));
   } else if (f8) {
     // do = dh . w_o^T ; dw_o = o^T . dh
-    if (keeps_codes(c)) {  // o's transposed codes come from mtl_attn_fwd
+    if (keeps_codes(c)) {  // o's transposed codes and w_o's codes come from mtl_attn_fwd
       ws.o_t = kp.o_t;
-      MTL_TRY(quantize({{dh, &ws.dh}, {w_o, &ws.wo}}, ws.amax_ws, s));
+      ws.wo = kp.wo;
+      MTL_TRY(quantize({{dh, &ws.dh}}, ws.amax_ws, s));
     } else {
       MTL_TRY(quantize({{dh, &ws.dh}, {w_o, &ws.wo}, {o, &ws.o_t}}, ws.amax_ws, s));
     }
@@ -1013,9 +1026,10 @@ mtl_status mtl_attn_bwd(const mtl_layer_cfg* c, const void* dh, const void* x, c
   }
   if (f8) {
     // dw_qkv = x^T . dqkv ; dx_partial = dqkv . w_qkv^T
-    if (keeps_codes(c)) {  // and x's
+    if (keeps_codes(c)) {  // and x's and w_qkv's
       ws.x_t = kp.x_t;
-      MTL_TRY(quantize({{ws.dqkv, &ws.dqkv8}, {w_qkv, &ws.wqkv}}, ws.amax_ws, s));
+      ws.wqkv = kp.wqkv;
+      MTL_TRY(quantize({{ws.dqkv, &ws.dqkv8}}, ws.amax_ws, s));
     } else {
       MTL_TRY(quantize({{ws.dqkv, &ws.dqkv8}, {x, &ws.x_t}, {w_qkv, &ws.wqkv}}, ws.amax_ws, s));
     }

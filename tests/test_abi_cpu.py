@@ -370,14 +370,15 @@ def test_fp8_gemm_validation_before_any_launch(mtl):
 
 def test_fp8_keep_codes_flag(mtl):
     """MTL_F_FP8_KEEP_CODES is fp8-only, and its kept region adds the
-    transposed codes (1 byte per element) and records of x, o, h and a to the
-    scratch size."""
+    transposed codes (1 byte per element) and records of x, o, h and a, and
+    both orientations of the four weights' codes, to the scratch size."""
     base = mtl.make_cfg(768, 12, 3072, 512, 1, 2, 0, mtl.MTL_PREC_FP8_HYBRID)
     kept = mtl.make_cfg(768, 12, 3072, 512, 1, 2, 0, mtl.MTL_PREC_FP8_HYBRID, mtl.MTL_F_FP8_KEEP_CODES)
     assert mtl.mtl_validate(kept) == mtl.MTL_OK
-    S, h, o_l, f_l = 512, 768, 384, 1536
+    S, h, o_l, f_l, qkv_l = 512, 768, 384, 1536, 1152
     up = lambda n: (n + 255) // 256 * 256
-    extra = 4 * 256 + up(S * h) * 2 + up(S * o_l) + up(S * f_l)
+    # x, o, h, a transposed; w_qkv, w_o, w1, w2 in both orientations; 8 records
+    extra = 8 * 256 + up(S * h) * 2 + up(S * o_l) + up(S * f_l) + 2 * (up(h * qkv_l) + up(o_l * h) + 2 * up(h * f_l))
     assert mtl.mtl_workspace_bytes(kept) == mtl.mtl_workspace_bytes(base) + extra
     bad = mtl.make_cfg(768, 12, 3072, 512, 1, 2, 0, mtl.MTL_PREC_BF16, mtl.MTL_F_FP8_KEEP_CODES)
     assert mtl.mtl_validate(bad) == mtl.MTL_E_UNSUPPORTED
