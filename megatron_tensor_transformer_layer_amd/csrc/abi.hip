@@ -113,11 +113,20 @@ Q8 q8(Bump& b, int64_t rows, int64_t cols, int fmt, bool normal, bool trans) {
   return q;
 }
 constexpr int E4M3 = 0, E5M2 = 1;
+// Capacity (entries) of a buffer of amax stage-1 partials written by a GEMM
+// epilogue or the attention kernels, and whether an M x N output fits it: a
+// GEMM writes one entry per wave of each tile, at most 4 per 128 x 128 tile.
+constexpr int AMAX_PART_CAP = 65536;
+inline bool amax_fits(int64_t M, int64_t N) { return ((M + 127) / 128) * ((N + 127) / 128) * 4 <= AMAX_PART_CAP; }
 
 // Quantise 1..3 bf16 tensors (x, its Q8) in one amax launch and one cast launch.
+// part / nparts: the tensor's amax stage-1 partials, written by the kernel that
+// produced it (nullptr: computed here).
 struct QIn {
   const void* x;
   const Q8* q;
+  const uint32_t* part = nullptr;
+  int nparts = 0;
 };
 hipError_t quantize(std::initializer_list<QIn> in, void* amax_ws, hipStream_t s) {
   QuantJob jobs[3];
@@ -126,8 +135,8 @@ hipError_t quantize(std::initializer_list<QIn> in, void* amax_ws, hipStream_t s)
   for (const QIn& e : in) {
     if (n == 3) return hipErrorInvalidValue;
     jobs[n++] = QuantJob{static_cast<const uint16_t*>(e.x), e.q->rows, e.q->cols, e.q->fmt, e.q->rec, e.q->q,
-                         e.q->qt};
-    bytes += (double)e.q->rows * e.q->cols * (4 + (e.q->q ? 1 : 0) + (e.q->qt ? 1 : 0));
+                         e.q->qt, e.part, e.nparts};
+    bytes += (double)e.q->rows * e.q->cols * ((e.part ? 2 : 4) + (e.q->q ? 1 : 0) + (e.q->qt ? 1 : 0));
   }
   return prof::timed(prof::QUANT, "fp8_quantize", 0, bytes, s, [&] { return fp8_quantize_n(jobs, n, amax_ws, s); });
 }
@@ -155,12 +164,28 @@ GemmArgs gemm8_args(const Q8& a, const uint8_t* a_codes, const Q8& b, const uint
   g.scale_b = b.rec + 2;
   return g;
 }
+// Where a GEMM's epilogue leaves the amax partials of its bf16 output `out`
+// (0: c, 1: c2), and the count it wrote.
+struct AmaxOut {
+  uint32_t* part = nullptr;
+  int out = 0;
+  int* nparts = nullptr;
+};
+inline void set_amax(GemmArgs& g, const AmaxOut& m) {
+  g.amax_part = m.part;
+  g.amax_out = m.out;
+  g.amax_cap = AMAX_PART_CAP;
+  g.amax_nparts = m.nparts;
+}
 hipError_t gemm8(const char* name, const Q8& a, const uint8_t* a_codes, const Q8& b, const uint8_t* b_codes,
                  int64_t M, int64_t N, int64_t K, void* c, int64_t ldc, int epi, hipStream_t s,
-                 const void* bias = nullptr, void* c2 = nullptr, const void* aux = nullptr) {
+                 const void* bias = nullptr, void* c2 = nullptr, const void* aux = nullptr,
+                 const AmaxOut& amx = AmaxOut{}) {
   const int out_b = (epi == EPI_F32 || epi == EPI_F32_ACC) ? 4 : (epi == EPI_BIAS_GELU ? 4 : 2);
   return prof::timed(prof::GEMM, name, gemm_flop(M, N, K), gemm_bytes(M, N, K, 1, out_b), s, [&] {
-    return gemm_fp8(gemm8_args(a, a_codes, b, b_codes, M, N, K, c, ldc, bias, c2, aux), a.fmt, b.fmt, epi, s);
+    GemmArgs g = gemm8_args(a, a_codes, b, b_codes, M, N, K, c, ldc, bias, c2, aux);
+    set_amax(g, amx);
+    return gemm_fp8(g, a.fmt, b.fmt, epi, s);
   });
 }
 // A timed bf16 GEMM (2-byte operands; out_b bytes per output element).
@@ -246,6 +271,7 @@ struct MlpScratch {
   // fp8 copies
   Q8 dy, w2, a_t, dz8, h_t, w1;
   void* amax_ws;
+  uint32_t* dz_part;  // dz's amax partials from the fc2 dgrad epilogue
   // MXFP4 copies
   MX4 m_dy, m_dy_t, m_w2, m_a_t, m_dz, m_dz_t, m_h_t, m_w1;
 };
@@ -256,16 +282,19 @@ struct AttnScratch {
   float* ws;
   Q8 dh, wo, o_t, dqkv8, x_t, wqkv;
   void* amax_ws;
+  uint32_t* dqkv_part;  // dqkv's amax partials from the attention backward
   MX4 m_dh, m_dh_t, m_wo, m_o_t, m_dqkv, m_dqkv_t, m_x_t, m_wqkv;
 };
 struct AttnFwdScratch {
   Q8 x, wqkv_t, o, wo_t;
   void* amax_ws;
+  uint32_t* o_part;  // o's amax partials from the attention forward
   MX4 m_x, m_wqkv_t, m_o, m_wo_t;
 };
 struct MlpFwdScratch {
   Q8 h, w1_t, a, w2_t;
   void* amax_ws;
+  uint32_t* a_part;  // a's amax partials from the fc1 forward epilogue
   MX4 m_h, m_w1_t, m_a, m_w2_t;
 };
 
@@ -318,6 +347,7 @@ size_t mlp_scratch(const mtl_layer_cfg* c, const Dims& d, MlpScratch* s, char* b
     t.h_t = q8(b, d.S, d.h, E4M3, false, true);
     t.w1 = q8(b, d.h, d.f_l, E4M3, true, false);
     t.amax_ws = b.take<char>(fp8_amax_ws_bytes());
+    t.dz_part = b.take<uint32_t>(AMAX_PART_CAP * 4);
   }
   if (is_mx4(c)) {
     t.m_dy = mx4(b, d.S, d.h);
@@ -348,6 +378,7 @@ size_t attn_scratch(const mtl_layer_cfg* c, const Dims& d, AttnScratch* s, char*
     t.x_t = q8(b, d.S, d.h, E4M3, false, true);
     t.wqkv = q8(b, d.h, d.qkv_l, E4M3, true, false);
     t.amax_ws = b.take<char>(fp8_amax_ws_bytes());
+    t.dqkv_part = b.take<uint32_t>(AMAX_PART_CAP * 4);
   }
   if (is_mx4(c)) {
     t.m_dh = mx4(b, d.S, d.h);
@@ -373,6 +404,7 @@ size_t attn_fwd_scratch(const mtl_layer_cfg* c, const Dims& d, AttnFwdScratch* s
     t.o = q8(b, d.S, d.o_l, E4M3, true, false);
     t.wo_t = q8(b, d.o_l, d.h, E4M3, false, true);
     t.amax_ws = b.take<char>(fp8_amax_ws_bytes());
+    t.o_part = b.take<uint32_t>(AMAX_PART_CAP * 4);
   } else {
     t.m_x = mx4(b, d.S, d.h);
     t.m_wqkv_t = mx4(b, d.qkv_l, d.h);
@@ -393,6 +425,7 @@ size_t mlp_fwd_scratch(const mtl_layer_cfg* c, const Dims& d, MlpFwdScratch* s, 
     t.a = q8(b, d.S, d.f_l, E4M3, true, false);
     t.w2_t = q8(b, d.f_l, d.h, E4M3, false, true);
     t.amax_ws = b.take<char>(fp8_amax_ws_bytes());
+    t.a_part = b.take<uint32_t>(AMAX_PART_CAP * 4);
   } else {
     t.m_h = mx4(b, d.S, d.h);
     t.m_w1_t = mx4(b, d.f_l, d.h);
@@ -526,6 +559,12 @@ mtl_status mtl_attn_fwd(const mtl_layer_cfg* c, const void* x, const void* w_qkv
   a.heads = (int)d.heads_l;
   a.d = (int)d.d;
   a.scale = 1.0f / sqrtf((float)d.d);
+  int no = 0;  // fp8: the attention kernel leaves o's amax partials
+  if (is_fp8(c)) {
+    a.amax_part = ws.o_part;
+    a.amax_cap = AMAX_PART_CAP;
+    a.amax_nparts = &no;
+  }
   MTL_TRY(prof::timed(prof::ATTN, "attn_fwd", attn_flop(c, d.heads_l, d.d),
                       2.0 * d.S * (d.qkv_l + d.o_l) + 4.0 * d.S * d.heads_l, s, [&] { return attention_fwd(a, s); }));
 
@@ -535,7 +574,7 @@ mtl_status mtl_attn_fwd(const mtl_layer_cfg* c, const void* x, const void* w_qkv
     MTL_TRY(mxqt(w_o, ws.m_wo_t, s));
     MTL_TRY(mxgemm("proj_fwd", ws.m_o, ws.m_wo_t, EPI_BF16, partial, s));
   } else if (is_fp8(c)) {
-    MTL_TRY(quantize({{o, &ws.o}}, ws.amax_ws, s));
+    MTL_TRY(quantize({{o, &ws.o, ws.o_part, no}}, ws.amax_ws, s));
     MTL_TRY(gemm8("proj_fwd", ws.o, ws.o.q, ws.wo_t, ws.wo_t.qt, d.S, d.h, d.o_l, partial, d.h, EPI_BF16, s));
   } else {
     GemmArgs g = gemm(o, d.o_l, w_o, d.h, d.S, d.h, d.o_l, partial, d.h);
@@ -844,9 +883,12 @@ mtl_status mtl_mlp_fwd(const mtl_layer_cfg* c, const void* h, const void* w1, co
   if (is_fp8(c)) {
     // z = h . w1 + b1: gz = GeLU'(z), a = GeLU(z); partial = a . w2 (a re-quantised from bf16)
     MTL_TRY(quantize({{h, &ws.h}, {w1, &ws.w1_t}, {w2, &ws.w2_t}}, ws.amax_ws, s));
+    // the fc1 epilogue leaves a's amax partials, so a's quantisation reads it once
+    int na = 0;
+    const AmaxOut am = amax_fits(d.S, d.f_l) ? AmaxOut{ws.a_part, 1, &na} : AmaxOut{};
     MTL_TRY(gemm8("fc1_fwd", ws.h, ws.h.q, ws.w1_t, ws.w1_t.qt, d.S, d.f_l, d.h, gz, d.f_l, EPI_BIAS_GELU, s, b1,
-                  a));
-    MTL_TRY(quantize({{a, &ws.a}}, ws.amax_ws, s));
+                  a, nullptr, am));
+    MTL_TRY(quantize({{a, &ws.a, am.part, na}}, ws.amax_ws, s));
     MTL_TRY(gemm8("fc2_fwd", ws.a, ws.a.q, ws.w2_t, ws.w2_t.qt, d.S, d.h, d.f_l, partial, d.h, EPI_BF16, s));
     return MTL_OK;
   }
@@ -920,16 +962,20 @@ mtl_status mtl_mlp_bwd(const mtl_layer_cfg* c, const void* dy, const void* h, co
     } else {
       MTL_TRY(quantize({{dy, &ws.dy}, {w2, &ws.w2}, {a, &ws.a_t}}, ws.amax_ws, s));
     }
-    // dw2 = a^T . dy with dz = (dy . w2^T) * gz in one launch, then dw1 = h^T . dz with dh_partial = dz . w1^T
+    // dw2 = a^T . dy with dz = (dy . w2^T) * gz in one launch, then dw1 = h^T . dz with dh_partial = dz . w1^T;
+    // the dgrad epilogue leaves dz's amax partials
+    int nz = 0;
+    const AmaxOut az = amax_fits(d.S, d.f_l) ? AmaxOut{ws.dz_part, 0, &nz} : AmaxOut{};
+    GemmArgs gdz = gemm8_args(ws.dy, ws.dy.q, ws.w2, ws.w2.q, d.S, d.f_l, d.h, ws.dz, d.f_l, nullptr, nullptr, gz);
+    set_amax(gdz, az);
     MTL_TRY(gemm8_pair("fc2_bwd", gemm8_args(ws.a_t, ws.a_t.qt, ws.dy, ws.dy.qt, d.f_l, d.h, d.S, dw2, d.h), wepi,
-                       gemm8_args(ws.dy, ws.dy.q, ws.w2, ws.w2.q, d.S, d.f_l, d.h, ws.dz, d.f_l, nullptr, nullptr, gz),
-                       EPI_DGELU, s));
+                       gdz, EPI_DGELU, s));
     if (keeps_codes(c)) {  // and h's and w1's
       ws.h_t = kp.h_t;
       ws.w1 = kp.w1;
-      MTL_TRY(quantize({{ws.dz, &ws.dz8}}, ws.amax_ws, s));
+      MTL_TRY(quantize({{ws.dz, &ws.dz8, az.part, nz}}, ws.amax_ws, s));
     } else {
-      MTL_TRY(quantize({{ws.dz, &ws.dz8}, {h, &ws.h_t}, {w1, &ws.w1}}, ws.amax_ws, s));
+      MTL_TRY(quantize({{ws.dz, &ws.dz8, az.part, nz}, {h, &ws.h_t}, {w1, &ws.w1}}, ws.amax_ws, s));
     }
     MTL_TRY(gemm8_pair("fc1_bwd", gemm8_args(ws.h_t, ws.h_t.qt, ws.dz8, ws.dz8.qt, d.h, d.f_l, d.S, dw1, d.f_l), wepi,
                        gemm8_args(ws.dz8, ws.dz8.q, ws.w1, ws.w1.q, d.S, d.h, d.f_l, dh_partial, d.h), EPI_BF16, s));
@@ -1010,6 +1056,12 @@ mtl_status mtl_attn_bwd(const mtl_layer_cfg* c, const void* dh, const void* x, c
   at.lse_in = lse;
   at.delta = ws.delta;
   at.dqkv = ws.dqkv;
+  int nq = 0;  // fp8: the attention backward leaves dqkv's amax partials
+  if (f8) {
+    at.amax_part = ws.dqkv_part;
+    at.amax_cap = AMAX_PART_CAP;
+    at.amax_nparts = &nq;
+  }
   // reads qkv, o, dO and lse; writes dqkv (D = rowsum(dO * O) on the way)
   MTL_TRY(prof::timed(prof::ATTN, "attn_bwd", 2.0 * attn_flop(c, d.heads_l, d.d),
                       2.0 * d.S * (2 * d.qkv_l + 2 * d.o_l) + 4.0 * d.S * d.heads_l, s,
@@ -1029,9 +1081,9 @@ mtl_status mtl_attn_bwd(const mtl_layer_cfg* c, const void* dh, const void* x, c
     if (keeps_codes(c)) {  // and x's and w_qkv's
       ws.x_t = kp.x_t;
       ws.wqkv = kp.wqkv;
-      MTL_TRY(quantize({{ws.dqkv, &ws.dqkv8}}, ws.amax_ws, s));
+      MTL_TRY(quantize({{ws.dqkv, &ws.dqkv8, ws.dqkv_part, nq}}, ws.amax_ws, s));
     } else {
-      MTL_TRY(quantize({{ws.dqkv, &ws.dqkv8}, {x, &ws.x_t}, {w_qkv, &ws.wqkv}}, ws.amax_ws, s));
+      MTL_TRY(quantize({{ws.dqkv, &ws.dqkv8, ws.dqkv_part, nq}, {x, &ws.x_t}, {w_qkv, &ws.wqkv}}, ws.amax_ws, s));
     }
     MTL_TRY(gemm8_pair("qkv_bwd",
                        gemm8_args(ws.x_t, ws.x_t.qt, ws.dqkv8, ws.dqkv8.qt, d.h, d.qkv_l, d.S, dw_qkv, d.qkv_l), wepi,

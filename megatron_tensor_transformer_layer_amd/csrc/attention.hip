@@ -153,6 +153,7 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_kernel(AttnArgs a) {
   const int64_t tok0 = (int64_t)b * a.seq;
   const int64_t colq = (int64_t)n * 3 * D, colo = (int64_t)n * D;
   const float c = a.scale * LOG2E;
+  uint32_t amx = 0;  // largest bf16 magnitude of dQKV this wave stores
   const i32x4 rq = make_rsrc(a.qkv, (uint32_t)(tokens * a.ld_qkv * 2));
   const i32x4 ro = make_rsrc(a.dout, (uint32_t)(tokens * a.ld_o * 2));
   // K and V tiles: the resource rk from token ktok0 (FULL: kv_seq == seq)
@@ -258,8 +259,14 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_kernel(AttnArgs a) {
             kv[e] = (dk[i][r] + mg[(i * 16 + r) * 64 + lane]) * a.scale;
             vv[e] = dv[i][r] + mg[((DB + i) * 16 + r) * 64 + lane];
           }
-          *reinterpret_cast<u32x2*>(kout + dim) = u32x2{pack_bf16x2(kv[0], kv[1]), pack_bf16x2(kv[2], kv[3])};
-          *reinterpret_cast<u32x2*>(vout + dim) = u32x2{pack_bf16x2(vv[0], vv[1]), pack_bf16x2(vv[2], vv[3])};
+          const u32x2 wk = {pack_bf16x2(kv[0], kv[1]), pack_bf16x2(kv[2], kv[3])};
+          const u32x2 wv = {pack_bf16x2(vv[0], vv[1]), pack_bf16x2(vv[2], vv[3])};
+          *reinterpret_cast<u32x2*>(kout + dim) = wk;
+          *reinterpret_cast<u32x2*>(vout + dim) = wv;
+#pragma unroll
+          for (int k = 0; k < 2; ++k)
+            amx = max(amx, max(max(wk[k] & 0x7fffu, (wk[k] >> 16) & 0x7fffu),
+                               max(wv[k] & 0x7fffu, (wv[k] >> 16) & 0x7fffu)));
         }
     }
     __syncthreads();
@@ -339,9 +346,17 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_kernel(AttnArgs a) {
           float v[4];
 #pragma unroll
           for (int e = 0; e < 4; ++e) v[e] = (dq[i][4 * gg + e] + mg[(i * 16 + 4 * gg + e) * 64 + lane]) * a.scale;
-          *reinterpret_cast<u32x2*>(qout + dim) = u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+          const u32x2 wq = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+          *reinterpret_cast<u32x2*>(qout + dim) = wq;
+#pragma unroll
+          for (int k = 0; k < 2; ++k) amx = max(amx, max(wq[k] & 0x7fffu, (wq[k] >> 16) & 0x7fffu));
         }
     }
+  }
+  if (a.amax_part) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) amx = max(amx, (uint32_t)__shfl_xor((int)amx, off));
+    if (lane == 0) a.amax_part[blockIdx.x * 4 + wave] = amx;
   }
 }
 
@@ -358,6 +373,10 @@ static hipError_t bwd_d(const AttnArgs& a, bool with_delta, hipStream_t s) {
   }
   const int64_t units = (int64_t)((a.seq + 63) / 64) * a.heads * a.batch;
   if (units > INT32_MAX) return hipErrorInvalidValue;
+  if (a.amax_part) {
+    if (units * 4 > a.amax_cap) return hipErrorInvalidValue;
+    if (a.amax_nparts) *a.amax_nparts = (int)(units * 4);
+  }
   hipLaunchKernelGGL((attn_bwd_kernel<D, FULL>), dim3((unsigned)units), dim3(256), 0, s, a);
   return hipGetLastError();
 }

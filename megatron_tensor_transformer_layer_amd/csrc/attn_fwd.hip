@@ -139,6 +139,7 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_kernel(AttnArgs a) {
   const int64_t kvtok0 = FULL ? (int64_t)b * a.kv_seq : tok0;
   const int nkb_all = FULL ? a.kv_seq / 64 : nitems;
 
+  uint32_t amx = 0;  // largest bf16 magnitude of O this wave stores
   for (int side = 0; side < 2; ++side) {
     const int item = side == 0 ? pair : nitems - 1 - pair;
     if (side == 1 && item == pair) break;
@@ -279,13 +280,20 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_kernel(AttnArgs a) {
 #pragma unroll
         for (int gg = 0; gg < 4; ++gg) {
           const int dim = i * 32 + 8 * gg + 4 * g;
-          *reinterpret_cast<u32x2*>(orow + dim) =
-              u32x2{pack_bf16x2(val[4 * gg], val[4 * gg + 1]), pack_bf16x2(val[4 * gg + 2], val[4 * gg + 3])};
+          const u32x2 w = {pack_bf16x2(val[4 * gg], val[4 * gg + 1]), pack_bf16x2(val[4 * gg + 2], val[4 * gg + 3])};
+          *reinterpret_cast<u32x2*>(orow + dim) = w;
+#pragma unroll
+          for (int k = 0; k < 2; ++k) amx = max(amx, max(w[k] & 0x7fffu, (w[k] >> 16) & 0x7fffu));
         }
         if (i == 0 && g == 0) a.lse[(int64_t)n * tokens + tok0 + q] = mt * a.scale + logf(lt);
       }
     }
     __syncthreads();  // the next item's DMA reuses the stages
+  }
+  if (a.amax_part) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) amx = max(amx, (uint32_t)__shfl_xor((int)amx, off));
+    if (lane == 0) a.amax_part[blockIdx.x * 8 + wave] = amx;
   }
 }
 
@@ -294,6 +302,10 @@ hipError_t fwd_d(const AttnArgs& a, hipStream_t s) {
   const int64_t npairs = ((a.seq + 63) / 64 + 1) / 2;
   const int64_t units = npairs * a.heads * a.batch;
   if (units > INT32_MAX) return hipErrorInvalidValue;
+  if (a.amax_part) {
+    if (units * 8 > a.amax_cap) return hipErrorInvalidValue;
+    if (a.amax_nparts) *a.amax_nparts = (int)(units * 8);
+  }
   hipLaunchKernelGGL((attn_fwd_kernel<D, FULL>), dim3((unsigned)units), dim3(512), 0, s, a);
   return hipGetLastError();
 }

@@ -56,6 +56,8 @@ __global__ __launch_bounds__(256) void amax_stage1(const uint16_t* __restrict__ 
 
 // Stage 1 of up to QMAX tensors in one launch: blocks [first[j], first[j+1])
 // take tensor j (grid-stride over its 8-element vectors) and write its partials.
+// A tensor whose producer wrote its partials takes no blocks (the cast reduces
+// those instead).
 constexpr int QMAX = 3;
 constexpr int QBLOCKS = 256;  // stage-1 blocks per tensor of a multi-tensor launch
 struct QuantArgs {
@@ -288,10 +290,12 @@ hipError_t fp8_quantize_n(const QuantJob* jobs, int n, void* ws, hipStream_t s) 
     a.rec[j] = q.rec;
     a.out[j] = q.out;
     a.out_t[j] = q.out_t;
-    a.part[j] = static_cast<uint32_t*>(ws) + j * QBLOCKS;
     const int64_t nv = q.rows * q.cols / 8;
-    const int nb = (int)std::max<int64_t>(1, std::min<int64_t>(QBLOCKS, (nv + 1023) / 1024));
-    a.nparts[j] = nb;
+    // with the producer's partials, no stage-1 blocks for this tensor
+    const int nb = q.part ? 0 : (int)std::max<int64_t>(1, std::min<int64_t>(QBLOCKS, (nv + 1023) / 1024));
+    if (q.part && q.nparts < 1) return hipErrorInvalidValue;
+    a.part[j] = q.part ? const_cast<uint32_t*>(q.part) : static_cast<uint32_t*>(ws) + j * QBLOCKS;
+    a.nparts[j] = q.part ? q.nparts : nb;
     a.first1[j] = b1;
     b1 += nb;
     a.tiles_x[j] = (int)((q.cols + 63) / 64);
@@ -300,9 +304,11 @@ hipError_t fp8_quantize_n(const QuantJob* jobs, int n, void* ws, hipStream_t s) 
   }
   a.first1[n] = b1;
   a.first2[n] = b2;
-  hipLaunchKernelGGL(amax_stage1_multi, dim3((unsigned)b1), dim3(256), 0, s, a);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  if (b1 > 0) {
+    hipLaunchKernelGGL(amax_stage1_multi, dim3((unsigned)b1), dim3(256), 0, s, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   hipLaunchKernelGGL(cast_multi_kernel, dim3((unsigned)b2), dim3(256), 0, s, a);
   return hipGetLastError();
 }

@@ -504,6 +504,7 @@ __device__ __forceinline__ void gemm_tile(GemmArgs p, const int bid, LDS_AS char
       }
   }
 
+  uint32_t amx = 0;  // largest bf16 magnitude stored of output p.amax_out
 #pragma unroll
   for (int i0 = 0; i0 < TM; i0 += IPP) {
     // register phase
@@ -582,6 +583,10 @@ __device__ __forceinline__ void gemm_tile(GemmArgs p, const int bid, LDS_AS char
               uint16_t* c = reinterpret_cast<uint16_t*>(out == 0 ? p.c : p.c2) +
                             (int64_t)m * (out == 0 ? p.ldc : p.ldc2) + n;
               *reinterpret_cast<u32x4*>(c) = val;
+              if (p.amax_part && out == p.amax_out) {
+#pragma unroll
+                for (int w = 0; w < 4; ++w) amx = max(amx, max(val[w] & 0x7fffu, (val[w] >> 16) & 0x7fffu));
+              }
             }
           }
         }
@@ -589,6 +594,22 @@ __device__ __forceinline__ void gemm_tile(GemmArgs p, const int bid, LDS_AS char
     }
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
   }
+  if constexpr (!F32OUT) {
+    if (p.amax_part) {
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) amx = max(amx, (uint32_t)__shfl_xor((int)amx, off));
+      if (lane == 0) p.amax_part[bid * ML::NWAVES + wave] = amx;
+    }
+  }
+}
+
+// Entries of GemmArgs::amax_part a launch of `tiles` tiles of `waves` waves
+// writes; false when they exceed the capacity (or the GEMM is grouped).
+static bool amax_fits(const GemmArgs& p, int64_t tiles, int waves) {
+  if (!p.amax_part) return true;
+  if (p.offsets || tiles * waves > p.amax_cap) return false;
+  if (p.amax_nparts) *p.amax_nparts = (int)(tiles * waves);
+  return true;
 }
 
 template <int BM, int BN, bool A_K, bool B_K, int EPI, int F8 = 0, int NWN = 2>
@@ -637,6 +658,7 @@ static hipError_t launch_cfg(const GemmArgs& p, hipStream_t s) {
     tiles = (int64_t)p.groups * ((p.M + BM - 1) / BM) * ((p.N + BN - 1) / BN);
   }
   if (tiles <= 0) return hipSuccess;
+  if (!amax_fits(p, tiles, 2 * NWN)) return hipErrorInvalidValue;
   hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, A_K, B_K, EPI, F8, NWN>), dim3((unsigned)tiles), dim3(128 * NWN), 0, s, p);
   return hipGetLastError();
 }
@@ -669,6 +691,7 @@ template <class C1, class C2>
 static hipError_t launch_pair(const GemmArgs& p1, const GemmArgs& p2, hipStream_t s) {
   const int64_t t1 = (int64_t)((p1.M + C1::BM - 1) / C1::BM) * ((p1.N + C1::BN - 1) / C1::BN);
   const int64_t t2 = (int64_t)((p2.M + C2::BM - 1) / C2::BM) * ((p2.N + C2::BN - 1) / C2::BN);
+  if (!amax_fits(p1, t1, 4) || !amax_fits(p2, t2, 4)) return hipErrorInvalidValue;
   hipLaunchKernelGGL((gemm_pair_kernel<C1, C2>), dim3((unsigned)(t1 + t2)), dim3(256), 0, s, p1, p2, (int)t1);
   return hipGetLastError();
 }

@@ -48,6 +48,16 @@ struct GemmArgs {
   // fp8 operands (gemm_fp8): each operand's dequantisation factor 1/s (device scalars)
   const float* scale_a;
   const float* scale_b;
+  // Optional, plain (ungrouped) GEMMs with a bf16 output: every wave writes the
+  // largest bf16 magnitude bit pattern (sign cleared) it stored of output
+  // amax_out (0: c, 1: c2) to amax_part[tile * waves + wave] -- the stage-1
+  // partials of that tensor's per-tensor amax.  The launcher sets *amax_nparts
+  // (a host int) to the number of entries written and refuses more than
+  // amax_cap.
+  uint32_t* amax_part;
+  int amax_out;
+  int amax_cap;
+  int* amax_nparts;
 };
 
 enum GemmGroupMode : int { GROUP_M = 0, GROUP_K = 1 };
@@ -100,6 +110,14 @@ struct AttnArgs {
   // attention_bwd_full: dK, dV into the key columns of dkv (kv's layout), dQ into dq (stride ld_o)
   uint16_t* dkv;
   uint16_t* dq;
+  // Optional (attention_fwd: O; attention_bwd: dQKV): every wave writes the
+  // largest bf16 magnitude bit pattern it stored to amax_part[workgroup *
+  // waves + wave], the stage-1 partials of that tensor's per-tensor amax; the
+  // launcher sets *amax_nparts (a host int) to the count and refuses more than
+  // amax_cap.
+  uint32_t* amax_part;
+  int amax_cap;
+  int* amax_nparts;
 };
 hipError_t attention_fwd(const AttnArgs& a, hipStream_t s);
 // Queries of a.qkv against all a.kv_seq keys of a.kv (no mask; kv_seq % 64 == 0).
@@ -216,6 +234,10 @@ struct QuantJob {
   float* rec;
   uint8_t* out;
   uint8_t* out_t;
+  // the amax stage-1 partials of x written by the kernel that produced it
+  // (nullptr: the quantisation computes them)
+  const uint32_t* part;
+  int nparts;
 };
 hipError_t fp8_quantize_n(const QuantJob* jobs, int n, void* ws, hipStream_t s);
 

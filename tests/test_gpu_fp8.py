@@ -307,3 +307,37 @@ def test_fp8_kept_codes_are_bit_identical(mtl, case):
     for k, v in a.items():
         if isinstance(v, np.ndarray):
             assert np.array_equal(v, b[k]), k
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("case", ["gpt2-small-tp2", "d128-mb2-tp2"])
+def test_fp8_producer_amax_equals_the_amax_pass(mtl, case):
+    """The amax of O (from the attention kernel) and of A (from the fc1
+    epilogue), which the fp8 forward takes from the kernels that produced them,
+    is the one mtl_fp8_amax finds over the stored tensor: the kept records
+    (MTL_F_FP8_KEEP_CODES) equal mtl_fp8_amax's records bit for bit."""
+    import torch
+    from megatron_tensor_transformer_layer_amd import mtl_fp8_amax, MTL_FP8_AMAX_SCRATCH
+    from megatron_tensor_transformer_layer_amd.layer import RankState, bf16_dev
+    shape, _ = FP8_CASES[case]
+    t, r = shape.tp, shape.tp - 1
+    print(f"fp8 producer amax {case} {shape}", flush=True)
+    inp = synth.layer_inputs(shape, tp=t, rank=r)
+    st = RankState(shape, t, r, inp, flags=mtl.MTL_F_FP8_KEEP_CODES, precision=mtl.MTL_PREC_FP8_HYBRID)
+    x, h = bf16_dev(inp["x"]), bf16_dev(synth.layer_tensor(shape, "h"))
+    st.attn_fwd(x)
+    st.mlp_fwd(h)
+    torch.cuda.synchronize()
+    S, hd, o_l, f_l = shape.seq * shape.micro_batch, shape.hidden, shape.hidden // t, shape.ffn // t
+    up = lambda n: (n + 255) // 256 * 256
+    # kept region: x_t, o_t, h_t, a_t, each a 256-byte record then its codes
+    off_o = 256 + up(S * hd)
+    off_a = off_o + 256 + up(S * o_l) + 256 + up(S * hd)
+    scratch = torch.empty(MTL_FP8_AMAX_SCRATCH, dtype=torch.uint8, device="cuda")
+    for name, off, ten in (("o", off_o, st.o), ("a", off_a, st.a)):
+        kept = st.scratch[off:off + 12].view(torch.float32).clone()
+        rec = torch.zeros(4, dtype=torch.float32, device="cuda")
+        mtl_fp8_amax(ten, ten.numel(), mtl.MTL_FP8_E4M3, rec, scratch)
+        torch.cuda.synchronize()
+        assert torch.equal(kept[:3], rec[:3]), (name, kept.tolist(), rec.tolist())
+        assert kept[0].item() == ten.float().abs().max().item(), name
