@@ -33,6 +33,39 @@ __device__ __forceinline__ uint32_t e2m1_code(float y, uint32_t sign) {
   return c | (sign << 3);
 }
 
+// Eight codes (one 32-bit word, element 2j in the low nibble of byte j) of four
+// packed bf16 pairs under the block's E8M0 byte sc: gfx950's
+// v_cvt_scalef32_pk_fp4_f32 divides each value by the fp32 scale 2^(sc-127),
+// rounds to the nearest E2M1 value with ties to the even code, saturates at
+// +-6 and keeps the sign (also of zero) -- the rule above (checked bit for bit
+// against the oracle on every finite bf16 value).  The scale must be a normal
+// fp32 number, so sc = 0 (a block whose largest magnitude is below 2^-125)
+// takes the comparisons of e2m1_code instead.
+__device__ __forceinline__ uint32_t e2m1_pack8(const u32x4& v, uint32_t sc) {
+  if (sc == 0) {
+    uint32_t w = 0;
+#pragma unroll
+    for (int h = 0; h < 8; ++h) {
+      const uint32_t bits = (h & 1) ? (v[h >> 1] >> 16) : (v[h >> 1] & 0xffffu);
+      const float y = __uint_as_float(bits << 16) * 0x1p127f;
+      w |= e2m1_code(y, bits >> 15) << (4 * h);
+    }
+    return w;
+  }
+  const float scale = __uint_as_float(sc << 23);
+  // fp32 operands (exact widenings of the bf16 pair); the packed-bf16 form of
+  // the instruction was folded into one conversion for all four pairs by this
+  // compiler, so it is not used
+  auto lo = [&](int j) { return __uint_as_float(v[j] << 16); };
+  auto hi = [&](int j) { return __uint_as_float(v[j] & 0xffff0000u); };
+  uint32_t w = 0;
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, lo(0), hi(0), scale, 0);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, lo(1), hi(1), scale, 1);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, lo(2), hi(2), scale, 2);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, lo(3), hi(3), scale, 3);
+  return w;
+}
+
 __global__ __launch_bounds__(256) void mxfp4_quant_kernel(const uint16_t* __restrict__ x, int64_t nchunks,
                                                           uint8_t* __restrict__ codes, uint8_t* __restrict__ scales) {
   // chunk i = elements 8i .. 8i+7: consecutive lanes read consecutive 16 bytes,
@@ -49,14 +82,7 @@ __global__ __launch_bounds__(256) void mxfp4_quant_kernel(const uint16_t* __rest
   // so the E8M0 byte is max(E - 2, 0) (also for zero or subnormal amax)
   const int E = (int)(mx >> 7);
   const uint32_t sc = (uint32_t)max(E - 2, 0);
-  const float mul = __uint_as_float((254u - sc) << 23);  // 2^-e, exact
-  uint32_t w = 0;
-#pragma unroll
-  for (int h = 0; h < 8; ++h) {
-    const uint32_t bits = (h & 1) ? (v[h >> 1] >> 16) : (v[h >> 1] & 0xffffu);
-    const float y = __uint_as_float(bits << 16) * mul;
-    w |= e2m1_code(y, bits >> 15) << (4 * h);
-  }
+  const uint32_t w = e2m1_pack8(v, sc);
   if (!ok) return;
   *reinterpret_cast<uint32_t*>(codes + i * 4) = w;
   if ((i & 3) == 0) scales[i >> 2] = (uint8_t)sc;
@@ -70,12 +96,11 @@ __device__ __forceinline__ void e2m1_block(const uint32_t (&bits)[32], u32x4& w,
   for (int i = 0; i < 32; ++i) mx = max(mx, bits[i] & 0x7fffu);
   const int E = (int)(mx >> 7);
   sc = (uint32_t)max(E - 2, 0);
-  const float mul = __uint_as_float((254u - sc) << 23);
-  w = u32x4{0, 0, 0, 0};
 #pragma unroll
-  for (int i = 0; i < 32; ++i) {
-    const float y = __uint_as_float(bits[i] << 16) * mul;
-    w[i >> 3] |= e2m1_code(y, bits[i] >> 15) << (4 * (i & 7));
+  for (int q = 0; q < 4; ++q) {
+    const u32x4 v = {bits[8 * q] | (bits[8 * q + 1] << 16), bits[8 * q + 2] | (bits[8 * q + 3] << 16),
+                     bits[8 * q + 4] | (bits[8 * q + 5] << 16), bits[8 * q + 6] | (bits[8 * q + 7] << 16)};
+    w[q] = e2m1_pack8(v, sc);
   }
 }
 
