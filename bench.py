@@ -131,17 +131,25 @@ def copy_rate():
 def mfma_ceiling():
     """The matrix cores' own rate: mtl_mfma_ceiling issuing the MFMAs of a
     4096x4096x4096 product in 256x256 tiles (256 workgroups of 4 waves) with
-    every operand in registers, on N(0,1) bf16 values and on their E4M3 codes;
-    HIP events around 20 launches after 3 untimed ones."""
+    every operand in registers, on N(0,1) bf16 values, on their E4M3 codes and
+    on their MXFP4 codes; HIP events around 20 launches after 3 untimed ones."""
     import torch
-    from megatron_tensor_transformer_layer_amd import MTL_CEILING_DATA_BYTES, mtl_mfma_ceiling
+    from megatron_tensor_transformer_layer_amd import (MTL_CEILING_DATA_BYTES, mtl_mfma_ceiling,
+                                                       mtl_mxfp4_quantize)
     g = torch.Generator(device="cuda").manual_seed(0)
     wgs = 256
     out = torch.empty(wgs * 256, dtype=torch.float32, device="cuda")
     for kind, name, iters, per_iter, peak in ((0, "bf16", 128, 1 << 20, PEAK_BF16_TFLOPS),
-                                               (1, "fp8", 64, 2 << 20, PEAK_FP8_TFLOPS)):
-        vals = torch.randn(MTL_CEILING_DATA_BYTES // (2 if kind == 0 else 1), device="cuda", generator=g)
-        data = vals.to(torch.bfloat16) if kind == 0 else vals.to(torch.float8_e4m3fn)
+                                               (1, "fp8", 64, 2 << 20, PEAK_FP8_TFLOPS),
+                                               (2, "mxfp4", 64, 2 << 20, PEAK_FP4_TFLOPS)):
+        n = MTL_CEILING_DATA_BYTES // 2 if kind == 0 else MTL_CEILING_DATA_BYTES * (2 if kind == 2 else 1)
+        vals = torch.randn(n, device="cuda", generator=g)
+        if kind == 2:
+            data = torch.empty(MTL_CEILING_DATA_BYTES, dtype=torch.uint8, device="cuda")
+            scales = torch.empty(n // 32, dtype=torch.uint8, device="cuda")
+            mtl_mxfp4_quantize(vals.to(torch.bfloat16), 1024, n // 1024, data, scales)
+        else:
+            data = vals.to(torch.bfloat16) if kind == 0 else vals.to(torch.float8_e4m3fn)
         for _ in range(3):
             mtl_mfma_ceiling(data, kind, wgs, iters, out)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)

@@ -538,15 +538,16 @@ mtl_status mtl_prof_record(int32_t i, int32_t* kind, double* flop, double* bytes
  * (the site's precision section puts the layer's linears on the matrix cores in
  * bf16, fp8 and fp4).  Each of `workgroups` workgroups of 4 waves issues, per
  * wave, `iters` times the MFMA stream of one 128x128 output tile over one
- * k-slab -- 32 v_mfma_f32_32x32x16_bf16 (kind 0) or 16
- * v_mfma_scale_f32_32x32x64_f8f6f4 on E4M3 operands (kind 1) into 16
- * independent 32x32 fp32 accumulators -- with every operand fragment loaded
- * from `data` once before the loop: no other memory traffic, no LDS, no
- * barrier.  FLOP per launch = workgroups * 4 * iters * 1048576 (kind 0) or
- * 2097152 (kind 1); 256 workgroups and 128 (bf16) or 64 (fp8) iterations issue
- * exactly the MFMAs of a 4096x4096x4096 GEMM in 256x256 tiles.
- * data: device, >= MTL_CEILING_DATA_BYTES bytes of operand values (bf16 or
- * E4M3 codes, the distribution is the caller's); wave w reads the 16 KiB at
+ * k-slab -- 32 v_mfma_f32_32x32x16_bf16 (kind 0), or 16
+ * v_mfma_scale_f32_32x32x64_f8f6f4 on E4M3 operands (kind 1) or on E2M1
+ * operands with unit E8M0 scales (kind 2), into 16 independent 32x32 fp32
+ * accumulators -- with every operand fragment loaded from `data` once before
+ * the loop: no other memory traffic, no LDS, no barrier.  FLOP per launch =
+ * workgroups * 4 * iters * 1048576 (kind 0) or 2097152 (kinds 1 and 2); 256
+ * workgroups and 128 (bf16) or 64 (fp8, fp4) iterations issue exactly the
+ * MFMAs of a 4096x4096x4096 GEMM in 256x256 tiles.
+ * data: device, >= MTL_CEILING_DATA_BYTES bytes of operand values (bf16, E4M3
+ * codes or packed E2M1 codes; the distribution is the caller's); wave w reads the 16 KiB at
  * (w % 64) * 16 KiB.  out: device fp32 [workgroups * 256], each lane's sum of
  * its accumulators (keeps the MFMAs live).  16-byte aligned pointers
  * (MTL_E_ALIGN).  MTL_E_UNSUPPORTED for another kind; MTL_E_SHAPE for a short

@@ -208,7 +208,8 @@ hipError_t gemm8_pair(const char* name, const GemmArgs& gw, int ew, const GemmAr
 }
 
 // An MXFP4 copy of one GEMM operand, K-contiguous: codes [rows, k/2] bytes and
-// scales [rows, k/32] (k = the GEMM's contraction).
+// scales (rows * k/32 bytes) in the GEMM's order (k = the GEMM's contraction;
+// rows and k are multiples of 256 in the layer).
 struct MX4 {
   uint8_t* q;
   uint8_t* s;
@@ -226,18 +227,18 @@ inline double mx4_bytes(const MX4& m) { return (double)m.rows * m.k * (2.0 + 0.5
 // x [rows, k] quantised along its rows into m ([rows, k])
 hipError_t mxq(const void* x, const MX4& m, hipStream_t s) {
   return prof::timed(prof::QUANT, "mx_quantize_rows", 0, mx4_bytes(m), s,
-                     [&] { return mxfp4_quantize(static_cast<const uint16_t*>(x), m.rows, m.k, m.q, m.s, s); });
+                     [&] { return mxfp4_quantize(static_cast<const uint16_t*>(x), m.rows, m.k, m.q, m.s, s, true); });
 }
 // x [k, rows] quantised down its columns into m ([rows, k] = x^T)
 hipError_t mxqt(const void* x, const MX4& m, hipStream_t s) {
   return prof::timed(prof::QUANT, "mx_quantize_cols", 0, mx4_bytes(m), s,
-                     [&] { return mxfp4_quantize_t(static_cast<const uint16_t*>(x), m.k, m.rows, m.q, m.s, s); });
+                     [&] { return mxfp4_quantize_t(static_cast<const uint16_t*>(x), m.k, m.rows, m.q, m.s, s, true); });
 }
 // x [r, k] quantised both ways from one read: along its rows into m ([r, k])
 // and down its columns into mt ([k, r])
 hipError_t mxq2(const void* x, const MX4& m, const MX4& mt, hipStream_t s) {
   return prof::timed(prof::QUANT, "mx_quantize_both", 0, mx4_bytes(m) + mx4_bytes(mt) - 2.0 * m.rows * m.k, s, [&] {
-    return mxfp4_quantize_both(static_cast<const uint16_t*>(x), m.rows, m.k, m.q, m.s, mt.q, mt.s, s);
+    return mxfp4_quantize_both(static_cast<const uint16_t*>(x), m.rows, m.k, m.q, m.s, mt.q, mt.s, s, true);
   });
 }
 // C [a.rows, b.rows] = A . B^T on MXFP4 codes, epilogue epi (fp32 C for the wgrad epilogues)
@@ -253,6 +254,7 @@ hipError_t mxgemm(const char* name, const MX4& a, const MX4& b, int epi, void* c
   g.K = (int)a.k;
   g.ldc = b.rows;
   g.epi = epi;
+  g.scale_order = 1;
   const bool f32 = epi == EPI_F32 || epi == EPI_F32_ACC;
   if (f32) g.c32 = static_cast<float*>(c);
   else g.c = static_cast<uint16_t*>(c);
@@ -262,7 +264,7 @@ hipError_t mxgemm(const char* name, const MX4& a, const MX4& b, int epi, void* c
   const int out_b = f32 ? 4 : (epi == EPI_BIAS_GELU ? 4 : 2);
   return prof::timed(prof::GEMM, name, gemm_flop(a.rows, b.rows, a.k),
                      (a.rows + b.rows) * (a.k / 2.0 + a.k / 32.0) + (double)out_b * a.rows * b.rows, s,
-                     [&] { return mxfp4_gemm(g, s); });
+                     [&] { return gemm_mxfp4_tiled(g, s); });
 }
 
 struct MlpScratch {
@@ -806,7 +808,7 @@ mtl_status mtl_mxfp4_gemm(int64_t M, int64_t N, int64_t K, const void* a_codes, 
   g.M = (int)M;
   g.N = (int)N;
   g.K = (int)K;
-  return hip_status(mxfp4_gemm(g, reinterpret_cast<hipStream_t>(stream)));
+  return hip_status(gemm_mxfp4_tiled(g, reinterpret_cast<hipStream_t>(stream)));
 }
 
 mtl_status mtl_mxfp4_quantize_t(const void* x, int64_t rows, int64_t cols, void* codes, void* scales,

@@ -45,11 +45,17 @@ __global__ __launch_bounds__(256, 1) void mfma_ceiling_kernel(const u32x4* __res
         for (int i = 0; i < 4; ++i)
 #pragma unroll
           for (int j = 0; j < 4; ++j) acc[i][j] = mfma32(fa[kk][i], fb[kk][j], acc[i][j]);
-    } else {  // fp8 E4M3: one 32x32x64 k-step per tile, 32 bytes per lane per operand
+    } else if (KIND == 1) {  // fp8 E4M3: one 32x32x64 k-step per tile, 32 bytes per lane per operand
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc[i][j] = mfma32_f8<0, 0>(fa[0][i], fa[1][i], fb[0][j], fb[1][j], acc[i][j]);
+    } else {  // MXFP4: one 32x32x64 k-step per tile, 16 bytes per lane per operand, unit scales
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          acc[i][j] = mfma32_mxfp4(fa[0][i], fb[0][j], acc[i][j], 0x7f7f7f7fu, 0x7f7f7f7fu, 0);
     }
   }
   float s = 0.f;
@@ -69,14 +75,16 @@ extern "C" mtl_status mtl_mfma_ceiling(const void* data, size_t data_bytes, int3
                                        int64_t iters, float* out, mtl_stream_t stream) {
   if (!data || !out) return MTL_E_NULL;
   if (((uintptr_t)data | (uintptr_t)out) & 15) return MTL_E_ALIGN;
-  if (kind != 0 && kind != 1) return MTL_E_UNSUPPORTED;
+  if (kind < 0 || kind > 2) return MTL_E_UNSUPPORTED;
   if (data_bytes < (size_t)MTL_CEILING_DATA_BYTES || workgroups <= 0 || workgroups > (1 << 20) || iters <= 0)
     return MTL_E_SHAPE;
   const dim3 grid((unsigned)workgroups), block(256);
   const hipStream_t s = (hipStream_t)stream;
   if (kind == 0)
     hipLaunchKernelGGL(mtl::mfma_ceiling_kernel<0>, grid, block, 0, s, (const mtl::u32x4*)data, iters, out);
-  else
+  else if (kind == 1)
     hipLaunchKernelGGL(mtl::mfma_ceiling_kernel<1>, grid, block, 0, s, (const mtl::u32x4*)data, iters, out);
+  else
+    hipLaunchKernelGGL(mtl::mfma_ceiling_kernel<2>, grid, block, 0, s, (const mtl::u32x4*)data, iters, out);
   return hipGetLastError() == hipSuccess ? MTL_OK : MTL_E_HIP;
 }

@@ -51,6 +51,24 @@ __device__ __forceinline__ f32x16 mfma32_f8(const u32x4& a0, const u32x4& a1, co
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, FA, FB, 0, 0, 0, 0);
 }
 
+// MXFP4 x MXFP4 32x32x64 MFMA: a and b hold 32 E2M1 codes per lane (one
+// 16-byte chunk; the instruction reads four registers for this format), sa and
+// sb four E8M0 scale bytes of which byte kk applies.
+__device__ __forceinline__ f32x16 mfma32_mxfp4(const u32x4& a, const u32x4& b, const f32x16& c, uint32_t sa,
+                                               uint32_t sb, int kk) {
+  typedef int i32x4_t __attribute__((ext_vector_type(4)));
+  typedef int i32x8_t __attribute__((ext_vector_type(8)));
+  const i32x4_t a4 = __builtin_bit_cast(i32x4_t, a), b4 = __builtin_bit_cast(i32x4_t, b);
+  const i32x8_t va = __builtin_shufflevector(a4, a4, 0, 1, 2, 3, -1, -1, -1, -1);
+  const i32x8_t vb = __builtin_shufflevector(b4, b4, 0, 1, 2, 3, -1, -1, -1, -1);
+  switch (kk & 3) {  // op_sel must be a constant: kk is one after unrolling
+    case 0: return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(va, vb, c, 4, 4, 0, (int)sa, 0, (int)sb);
+    case 1: return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(va, vb, c, 4, 4, 1, (int)sa, 1, (int)sb);
+    case 2: return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(va, vb, c, 4, 4, 2, (int)sa, 2, (int)sb);
+    default: return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(va, vb, c, 4, 4, 3, (int)sa, 3, (int)sb);
+  }
+}
+
 // ---------------------------------------------------------------- LDS tiles
 // A k-contiguous tile of R rows x 64 bf16 (128 B per row) is stored as eight
 // 16-byte chunks per row, chunk c of row r at physical chunk c ^ (r & 7): eight

@@ -166,18 +166,27 @@ struct Operand {
 };
 
 // F8 = 0: bf16 operands.  F8 = 1 + FA + 2*FB: fp8 operands, A in format FA and
-// B in format FB (0 = E4M3, 1 = E5M2), both k-contiguous.
+// B in format FB (0 = E4M3, 1 = E5M2), both k-contiguous.  F8 = F8_MXFP4 or
+// F8_MXFP4_GO: MXFP4 operands (E2M1 codes, two per byte, low nibble first, with
+// one E8M0 scale byte per 32 k; scale matrices in plain or GEMM order), both
+// k-contiguous; K, lda and ldb then count code bytes.
+constexpr int F8_MXFP4 = 5, F8_MXFP4_GO = 6;
 template <int BM, int BN, bool A_K, bool B_K, int F8 = 0, int NWN = 2>
 struct Mainloop {
   static constexpr int NWAVES = 2 * NWN;  // 2 x NWN waves over the tile
   static constexpr int WM = BM / 2, WN = BN / NWN;
   static constexpr int TM = WM / 32, TN = WN / 32;
+  static constexpr bool FP4 = F8 == F8_MXFP4 || F8 == F8_MXFP4_GO;
+  static constexpr bool GO = F8 == F8_MXFP4_GO;
+  static_assert(!FP4 || (A_K && B_K), "MXFP4 operands are k-contiguous");
   static constexpr int EB = F8 ? 1 : 2;
-  static constexpr int FA = F8 ? (F8 - 1) & 1 : 0, FB = F8 ? (F8 - 1) >> 1 : 0;
+  static constexpr int FA = (F8 && !FP4) ? (F8 - 1) & 1 : 0, FB = (F8 && !FP4) ? (F8 - 1) >> 1 : 0;
   using OA = Operand<BM, A_K, EB, NWAVES>;
   using OB = Operand<BN, B_K, EB, NWAVES>;
   static constexpr int KSLAB = OA::KSLAB;
-  static constexpr int KSTEPS = F8 ? 2 : 4;  // MFMA k steps per slab
+  // MFMA k steps per slab: 16 bf16, 64 fp8 (two 16-byte chunks per lane) or 64
+  // MXFP4 (one chunk per lane) deep
+  static constexpr int KSTEPS = (F8 && !FP4) ? 2 : 4;
   static constexpr int STAGE = OA::BYTES + OB::BYTES;
 
   // per-lane chunk offsets of slab 0 for both operands
@@ -215,17 +224,66 @@ struct Mainloop {
     }
   }
 
+  // MXFP4 scales.  A slab (256 k of a row) has 8 scale bytes, one per 32 k; at
+  // k step kk lane l takes the block 2*kk + l/32 of its row, as byte kk of one
+  // word that the MFMA picks by op_sel.  Loads run two slabs ahead.  Plain
+  // order: each lane loads the 8 bytes of each of its rows (one row per 32-row
+  // block) and at the slab's start selects its four bytes into the word.  GEMM
+  // order: the word of lane l is already at 4 l of the 32-row block's 256-byte
+  // group of the slab, one coalesced dword load per row block.
+  static constexpr int NS = FP4 ? TM + TN : 1;
+  using SW = std::conditional_t<GO, uint32_t, u32x2>;  // loaded per row block and slab
+  struct Scl {
+    uint32_t off[NS];  // byte offset of the lane's row (block) in its scale matrix
+    SW cur[NS];        // the slab being multiplied
+    SW nxt[NS];        // the next slab
+  };
+  static __device__ __forceinline__ void scl_offsets(const GemmArgs& p, int m0, int n0, int wm, int wn, int lane,
+                                                     Scl& sc) {
+    const int ks = p.K / 16;  // scale bytes per row (K counts code bytes, two k each)
+    if constexpr (GO) {
+      // group (row / 32) * slabs + slab, 256 bytes each, 16 per row block per K / 2 code bytes
+#pragma unroll
+      for (int i = 0; i < TM; ++i) sc.off[i] = (uint32_t)((m0 + wm * WM + i * 32) * ks + lane * 4);
+#pragma unroll
+      for (int j = 0; j < TN; ++j) sc.off[TM + j] = (uint32_t)((n0 + wn * WN + j * 32) * ks + lane * 4);
+    } else {
+#pragma unroll
+      for (int i = 0; i < TM; ++i) sc.off[i] = (uint32_t)((m0 + wm * WM + i * 32 + (lane & 31)) * ks);
+#pragma unroll
+      for (int j = 0; j < TN; ++j) sc.off[TM + j] = (uint32_t)((n0 + wn * WN + j * 32 + (lane & 31)) * ks);
+    }
+  }
+  // scale bytes of the slab starting at code byte k0 (8 per row and slab)
+  static __device__ __forceinline__ void scl_load(__amdgpu_buffer_rsrc_t rsa, __amdgpu_buffer_rsrc_t rsb,
+                                                  const Scl& sc, int k0, SW (&dst)[NS]) {
+    if constexpr (GO) {
+      const uint32_t kb = (uint32_t)k0 * 2;  // 256 bytes per 128 code bytes of k
+#pragma unroll
+      for (int i = 0; i < NS; ++i)
+        dst[i] = __builtin_amdgcn_raw_buffer_load_b32(i < TM ? rsa : rsb, (int)(sc.off[i] + kb), 0, 0);
+    } else {
+      const uint32_t kb = (uint32_t)k0 / 16;
+#pragma unroll
+      for (int i = 0; i < NS; ++i)
+        dst[i] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(i < TM ? rsa : rsb,
+                                                                                (int)(sc.off[i] + kb), 0, 0));
+    }
+  }
+
   // The operand fragments of one MFMA k step (16 deep for bf16, 64 for fp8,
-  // whose fragments are two 16-byte chunks).
-  static constexpr int NF = F8 ? 2 : 1;
+  // whose fragments are two 16-byte chunks, and for MXFP4, whose fragments are
+  // one chunk, with the slab's scale words).
+  static constexpr int NF = (F8 && !FP4) ? 2 : 1;
   struct Frags {
     u32x4 a[TM][NF], b[TN][NF];
+    uint32_t s[NS];
   };
   static __device__ __forceinline__ void read_step(const LDS_AS char* __restrict__ st, int wm, int wn, int lane, int kk,
                                                    Frags& f) {
     const LDS_AS char* sa = st;
     const LDS_AS char* sb = st + OA::BYTES;
-    if constexpr (F8 != 0) {
+    if constexpr (F8 != 0 && !FP4) {
 #pragma unroll
       for (int i = 0; i < TM; ++i) OA::frag8(sa, wm * TM + i, kk, lane, f.a[i][0], f.a[i][1]);
 #pragma unroll
@@ -238,13 +296,16 @@ struct Mainloop {
     }
   }
   // The operands go in swapped (B fragment first) so that a lane owns 4
-  // consecutive output columns.
-  static __device__ __forceinline__ void mfma_step(const Frags& f, f32x16 (&acc)[TM][TN]) {
+  // consecutive output columns.  kk: the k step the fragments belong to (the
+  // MXFP4 scale byte).
+  static __device__ __forceinline__ void mfma_step(const Frags& f, f32x16 (&acc)[TM][TN], int kk) {
 #pragma unroll
     for (int i = 0; i < TM; ++i)
 #pragma unroll
       for (int j = 0; j < TN; ++j) {
-        if constexpr (F8 != 0)
+        if constexpr (FP4)
+          acc[i][j] = mfma32_mxfp4(f.b[j][0], f.a[i][0], acc[i][j], f.s[TM + j], f.s[i], kk);
+        else if constexpr (F8 != 0)
           acc[i][j] = mfma32_f8<FB, FA>(f.b[j][0], f.b[j][1], f.a[i][0], f.a[i][1], acc[i][j]);
         else
           acc[i][j] = mfma32(f.b[j][0], f.a[i][0], acc[i][j]);
@@ -259,21 +320,39 @@ struct Mainloop {
   // On exit f[1] holds this slab's last step, for the next slab or for finish().
   // With STAGE, the staged slab is written into wst chunk by chunk and each
   // staging register is reloaded with its chunk of slab k1 right behind.
+  // MXFP4: sc.cur holds this slab's scale bytes and moves on to the next
+  // slab's, whose own loads (of slab k1) are issued here.
   template <bool FIRST, bool STAGE>
   static __device__ __forceinline__ void slab(const LDS_AS char* __restrict__ st, int wm, int wn, int lane,
                                               f32x16 (&acc)[TM][TN], Frags (&f)[2], Stg& g,
                                               LDS_AS char* __restrict__ wst, __amdgpu_buffer_rsrc_t ra,
-                                              __amdgpu_buffer_rsrc_t rb, const GemmArgs& p, const Offs& d, int k1) {
+                                              __amdgpu_buffer_rsrc_t rb, const GemmArgs& p, const Offs& d, int k1,
+                                              Scl& sc, __amdgpu_buffer_rsrc_t rsa, __amdgpu_buffer_rsrc_t rsb) {
     constexpr int NC = OA::PER_WAVE + OB::PER_WAVE;
     uint32_t kba = 0, kbb = 0;
     if constexpr (STAGE) {
       kba = OA::slab_bytes(p.lda, k1);
       kbb = OB::slab_bytes(p.ldb, k1);
     }
+    uint32_t wsc[NS];
+    if constexpr (FP4) {
+      const uint32_t sel = (lane >> 5) ? 0x07050301u : 0x06040200u;  // bytes 2*kk + lane/32
+#pragma unroll
+      for (int i = 0; i < NS; ++i) {
+        if constexpr (GO) wsc[i] = sc.cur[i];
+        else wsc[i] = __builtin_amdgcn_perm(sc.cur[i][1], sc.cur[i][0], sel);
+        sc.cur[i] = sc.nxt[i];
+      }
+      if constexpr (STAGE) scl_load(rsa, rsb, sc, k1, sc.nxt);
+    }
 #pragma unroll
     for (int kk = 0; kk < KSTEPS; ++kk) {
       read_step(st, wm, wn, lane, kk, f[kk & 1]);
-      if (!(FIRST && kk == 0)) mfma_step(f[(kk & 1) ^ 1], acc);
+      if constexpr (FP4) {
+#pragma unroll
+        for (int i = 0; i < NS; ++i) f[kk & 1].s[i] = wsc[i];
+      }
+      if (!(FIRST && kk == 0)) mfma_step(f[(kk & 1) ^ 1], acc, (kk + KSTEPS - 1) % KSTEPS);
       if constexpr (STAGE) {
 #pragma unroll
         for (int c = kk * NC / KSTEPS; c < (kk + 1) * NC / KSTEPS; ++c) stage_chunk(c, g, wst, ra, rb, d, kba, kbb);
@@ -310,7 +389,9 @@ struct Mainloop {
     }
   }
   // The last slab's last step.
-  static __device__ __forceinline__ void finish(const Frags (&f)[2], f32x16 (&acc)[TM][TN]) { mfma_step(f[1], acc); }
+  static __device__ __forceinline__ void finish(const Frags (&f)[2], f32x16 (&acc)[TM][TN]) {
+    mfma_step(f[1], acc, KSTEPS - 1);
+  }
 };
 
 // Row blocks the epilogue stages per pass: the largest divisor of tm that fits
@@ -398,6 +479,19 @@ __device__ __forceinline__ void gemm_tile(GemmArgs p, const int bid, LDS_AS char
   typename ML::Offs off;
   ML::OA::offsets(p.lda, m0, off.a);
   ML::OB::offsets(p.ldb, n0, off.b);
+  // MXFP4 scale matrices [M, K/32] and [N, K/32] (K/16 bytes per row, K in code
+  // bytes); rows past M or N read as 0
+  __amdgpu_buffer_rsrc_t vsa = va, vsb = vb;  // (unused by the other modes)
+  typename ML::Scl sc;
+  if constexpr (ML::FP4) {  // (the same byte count in either order)
+    vsa = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(p.mx_sa), 0, (int)((int64_t)p.M * (p.K / 16)),
+                                            0x00020000);
+    vsb = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(p.mx_sb), 0, (int)((int64_t)p.N * (p.K / 16)),
+                                            0x00020000);
+    ML::scl_offsets(p, m0, n0, wm, wn, lane, sc);
+    ML::scl_load(vsa, vsb, sc, 0, sc.cur);
+    if (nk > 1) ML::scl_load(vsa, vsb, sc, KSLAB, sc.nxt);
+  }
   // Slab 0 goes to LDS now and slab 1 into the staging registers.  While slab
   // kt is multiplied, slab kt+1 is written from the registers into the other
   // stage and slab kt+2 is loaded behind it (slabs past K load in-range rows or
@@ -413,10 +507,10 @@ __device__ __forceinline__ void gemm_tile(GemmArgs p, const int bid, LDS_AS char
   __syncthreads();
   typename ML::Frags fr[2];
   if (nk == 1) {
-    ML::template slab<true, false>(st0, wm, wn, lane, acc, fr, stg, st1, va, vb, p, off, 0);
+    ML::template slab<true, false>(st0, wm, wn, lane, acc, fr, stg, st1, va, vb, p, off, 0, sc, vsa, vsb);
   } else if (nk > 1) {
     // slab 0 (no previous step to finish), staging slab 1
-    ML::template slab<true, true>(st0, wm, wn, lane, acc, fr, stg, st1, va, vb, p, off, 2 * KSLAB);
+    ML::template slab<true, true>(st0, wm, wn, lane, acc, fr, stg, st1, va, vb, p, off, 2 * KSLAB, sc, vsa, vsb);
     if (p.K - KSLAB < KSLAB) {
       ML::OA::zero_tail(st1, p.K - KSLAB);
       ML::OB::zero_tail(st1 + ML::OA::BYTES, p.K - KSLAB);
@@ -432,7 +526,8 @@ __device__ __forceinline__ void gemm_tile(GemmArgs p, const int bid, LDS_AS char
       const bool odd = kt & 1;
       const LDS_AS char* st = odd ? st1 : st0;
       LDS_AS char* wst = odd ? st0 : st1;
-      ML::template slab<false, true>(st, wm, wn, lane, acc, fr, stg, wst, va, vb, p, off, (kt + 2) * KSLAB);
+      ML::template slab<false, true>(st, wm, wn, lane, acc, fr, stg, wst, va, vb, p, off, (kt + 2) * KSLAB, sc, vsa,
+                                     vsb);
       const int kv = p.K - (kt + 1) * KSLAB;
       if (kv < KSLAB) {
         ML::OA::zero_tail(wst, kv);
@@ -440,7 +535,8 @@ __device__ __forceinline__ void gemm_tile(GemmArgs p, const int bid, LDS_AS char
       }
       __syncthreads();
     }
-    ML::template slab<false, false>((nk - 1) & 1 ? st1 : st0, wm, wn, lane, acc, fr, stg, st1, va, vb, p, off, 0);
+    ML::template slab<false, false>((nk - 1) & 1 ? st1 : st0, wm, wn, lane, acc, fr, stg, st1, va, vb, p, off, 0, sc,
+                                    vsa, vsb);
   }
   const int lrow = lane & 31, lgrp = lane >> 5;
   const int mw = m0 + wm * WM, nw = n0 + wn * WN;
@@ -489,9 +585,11 @@ __device__ __forceinline__ void gemm_tile(GemmArgs p, const int bid, LDS_AS char
   constexpr int OUTB = IPP * 32 * RB;        // staged bytes of one output per pass
   static_assert(IPP >= 1, "epilogue staging does not fit");
 
-  // fp8: the product of the two operands' dequantisation factors
+  // fp8: the product of the two operands' dequantisation factors (MXFP4 scales
+  // are applied by the MFMA)
+  constexpr bool DQ = F8 != 0 && !ML::FP4;
   float dq = 1.f;
-  if constexpr (F8 != 0) dq = *p.scale_a * *p.scale_b;
+  if constexpr (DQ) dq = *p.scale_a * *p.scale_b;
   // bias kept as packed bf16 (half the registers), widened where it is added
   u32x2 braw[TN][4];
   if constexpr (HAS_BIAS) {
@@ -517,7 +615,7 @@ __device__ __forceinline__ void gemm_tile(GemmArgs p, const int bid, LDS_AS char
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
           float v[4] = {acc[i][j][4 * g + 0], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]};
-          if constexpr (F8 != 0) {
+          if constexpr (DQ) {
 #pragma unroll
             for (int e = 0; e < 4; ++e) v[e] *= dq;
           }
@@ -821,6 +919,50 @@ hipError_t gemm_fp8_pair(const GemmArgs& pw, int epi_w, const GemmArgs& pd, int 
   hipError_t e = gemm_fp8(pw, 0, 1, epi_w, s);
   if (e != hipSuccess) return e;
   return gemm_fp8(pd, 1, 0, epi_d, s);
+}
+
+// MXFP4 x MXFP4 on the same pipeline.  K, lda and ldb count code bytes (two k
+// per byte); a slab is 128 code bytes = 256 k = 8 scale blocks per row.
+template <int EPI, int F8>
+static hipError_t launch_mx(const GemmArgs& p, hipStream_t s) {
+  const long t256 = (long)((p.M + 255) / 256) * ((p.N + 255) / 256);
+  const long t192 = (long)((p.M + 255) / 256) * ((p.N + 191) / 192);
+  if (t256 >= 240) return launch_cfg<256, 256, true, true, EPI, F8>(p, s);
+  if (t192 >= 240 && p.N % 192 == 0) return launch_cfg<256, 192, true, true, EPI, F8>(p, s);
+  return launch_cfg<128, 128, true, true, EPI, F8>(p, s);
+}
+
+hipError_t gemm_mxfp4_tiled(const Mxfp4GemmArgs& g, hipStream_t s) {
+  if (g.M <= 0 || g.N <= 0 || g.K <= 0) return hipSuccess;
+  if (g.K % 256) return hipErrorInvalidValue;
+  const int64_t kb = g.K / 2;  // code bytes per row
+  if (((int64_t)g.M + 256) * kb >= ((int64_t)1 << 31) || ((int64_t)g.N + 256) * kb >= ((int64_t)1 << 31))
+    return hipErrorInvalidValue;
+  GemmArgs p{};
+  p.a = reinterpret_cast<const uint16_t*>(g.a);
+  p.b = reinterpret_cast<const uint16_t*>(g.b);
+  p.lda = p.ldb = kb;
+  p.M = g.M;
+  p.N = g.N;
+  p.K = (int)kb;
+  p.ldc = p.ldc2 = p.ld_aux = g.ldc;
+  p.c = (g.epi == EPI_F32 || g.epi == EPI_F32_ACC) ? static_cast<void*>(g.c32) : static_cast<void*>(g.c);
+  p.bias = g.bias;
+  p.c2 = g.c2;
+  p.aux = g.aux;
+  p.mx_sa = g.sa;
+  p.mx_sb = g.sb;
+  if (!g.scale_order) return g.epi == EPI_BF16 ? launch_mx<EPI_BF16, F8_MXFP4>(p, s) : hipErrorInvalidValue;
+  if (g.M % 32 || g.N % 32) return hipErrorInvalidValue;
+  switch (g.epi) {
+    case EPI_BF16: return launch_mx<EPI_BF16, F8_MXFP4_GO>(p, s);
+    case EPI_BF16_BIAS: return launch_mx<EPI_BF16_BIAS, F8_MXFP4_GO>(p, s);
+    case EPI_BIAS_GELU: return launch_mx<EPI_BIAS_GELU, F8_MXFP4_GO>(p, s);
+    case EPI_DGELU: return launch_mx<EPI_DGELU, F8_MXFP4_GO>(p, s);
+    case EPI_F32: return launch_mx<EPI_F32, F8_MXFP4_GO>(p, s);
+    case EPI_F32_ACC: return launch_mx<EPI_F32_ACC, F8_MXFP4_GO>(p, s);
+  }
+  return hipErrorInvalidValue;
 }
 
 hipError_t gemm_fp8(const GemmArgs& p, int fmt_a, int fmt_b, int epi, hipStream_t s) {

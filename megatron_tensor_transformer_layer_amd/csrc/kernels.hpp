@@ -58,6 +58,10 @@ struct GemmArgs {
   int amax_out;
   int amax_cap;
   int* amax_nparts;
+  // MXFP4 operands (gemm_mxfp4_tiled): E8M0 scales of A [M, K/16] and B [N, K/16]
+  // bytes, K counting code bytes
+  const uint8_t* mx_sa;
+  const uint8_t* mx_sb;
 };
 
 enum GemmGroupMode : int { GROUP_M = 0, GROUP_K = 1 };
@@ -149,13 +153,26 @@ struct CpDqSumArgs {
 hipError_t cp_dq_sum(const CpDqSumArgs& a, hipStream_t s);
 
 // ---------------------------------------------------------------- MXFP4
+// Scale matrices come in two orders.  Plain: [rows, K/32], block q of row r at
+// r * K/32 + q.  GEMM order (rows % 32 == 0, K % 256 == 0): the 8 scale bytes
+// of the rows of one 32-row block rb in one 256-k slab s fill the 256-byte
+// group rb * K/256 + s, block q (0..7 within the slab) of row r at byte
+// 4 * (r % 32 + 32 * (q % 2)) + q / 2 of it -- lane l of a 32x32x64 MFMA
+// fragment (row l % 32, k half l / 32) reads its four k steps' scales as the
+// one word at 4 * l.
+template <bool GEMM_ORDER>
+__host__ __device__ __forceinline__ int64_t mx_scale_index(int64_t r, int64_t q, int64_t nblocks) {
+  if constexpr (!GEMM_ORDER) return r * nblocks + q;
+  return ((r >> 5) * (nblocks >> 3) + (q >> 3)) * 256 + ((r & 31) + 32 * (q & 1)) * 4 + ((q & 7) >> 1);
+}
 // x [rows, cols] bf16 (cols % 32 == 0) -> codes [rows, cols/2] (two E2M1 per
-// byte, even element low) and E8M0 scales [rows, cols/32].
+// byte, even element low) and E8M0 scales, plain or (gemm_order: rows % 32 ==
+// 0, cols % 256 == 0) in GEMM order.
 hipError_t mxfp4_quantize(const uint16_t* x, int64_t rows, int64_t cols, uint8_t* codes, uint8_t* scales,
-                          hipStream_t s);
+                          hipStream_t s, bool gemm_order = false);
 // c [M, N] bf16 (row stride ldc) = A B^T over K, A [M, K] and B [N, K] in
-// MXFP4 (codes and scales as mxfp4_quantize writes them); M, N % 128 == 0,
-// K % 256 == 0.
+// MXFP4 (codes and scales as mxfp4_quantize writes them, plain order); M, N %
+// 128 == 0, K % 256 == 0.
 struct Mxfp4GemmArgs {
   const uint8_t* a;
   const uint8_t* sa;
@@ -170,18 +187,24 @@ struct Mxfp4GemmArgs {
   uint16_t* c2;          // GeLU(z) [M, N], row stride ldc (EPI_BIAS_GELU)
   const uint16_t* aux;   // GeLU'(z) [M, N], row stride ldc (EPI_DGELU)
   float* c32;            // fp32 C [M, N], row stride ldc (EPI_F32, EPI_F32_ACC)
+  int scale_order;       // gemm_mxfp4_tiled: 0 plain (EPI_BF16 only), 1 GEMM order (M, N % 32 == 0)
 };
 hipError_t mxfp4_gemm(const Mxfp4GemmArgs& g, hipStream_t s);
-// MXFP4 quantisation of x [rows, cols] along its rows (blocks of 32 rows of
-// one column): codes of x^T, [cols, rows/2] bytes, and scales [cols, rows/32]
+// The same product on the bf16 GEMM's pipeline (256 x 256, 256 x 192 or 128 x
+// 128 tiles, two slabs in flight), for K % 256 == 0.
+hipError_t gemm_mxfp4_tiled(const Mxfp4GemmArgs& g, hipStream_t s);
+// MXFP4 quantisation of x [rows, cols] down its columns (blocks of 32 rows of
+// one column): codes of x^T, [cols, rows/2] bytes, and the scales of x^T,
+// plain [cols, rows/32] or in GEMM order (rows % 256 == 0, cols % 32 == 0)
 // (rows % 32 == 0, cols % 8 == 0).
 hipError_t mxfp4_quantize_t(const uint16_t* x, int64_t rows, int64_t cols, uint8_t* codes, uint8_t* scales,
-                            hipStream_t s);
+                            hipStream_t s, bool gemm_order = false);
 // Both directions at once from one read of x (rows % 64 == 0, cols % 128 ==
 // 0): codes/scales as mxfp4_quantize, codes_t/scales_t as mxfp4_quantize_t;
-// either pair may be null (not both).
+// either pair may be null (not both).  gemm_order: both scale matrices in GEMM
+// order (rows and cols % 256 == 0).
 hipError_t mxfp4_quantize_both(const uint16_t* x, int64_t rows, int64_t cols, uint8_t* codes, uint8_t* scales,
-                               uint8_t* codes_t, uint8_t* scales_t, hipStream_t s);
+                               uint8_t* codes_t, uint8_t* scales_t, hipStream_t s, bool gemm_order = false);
 // The same for MXFP6 (FP6 E2M3 elements): codes [rows, cols*3/4], 32 elements
 // of 6 bits per 24 bytes, element j at bits 6j.. of the little-endian block;
 // the GEMM takes K % 128 == 0.

@@ -66,8 +66,10 @@ __device__ __forceinline__ uint32_t e2m1_pack8(const u32x4& v, uint32_t sc) {
   return w;
 }
 
+template <bool GO>  // scales in GEMM order (else plain)
 __global__ __launch_bounds__(256) void mxfp4_quant_kernel(const uint16_t* __restrict__ x, int64_t nchunks,
-                                                          uint8_t* __restrict__ codes, uint8_t* __restrict__ scales) {
+                                                          int64_t nblocks, uint8_t* __restrict__ codes,
+                                                          uint8_t* __restrict__ scales) {
   // chunk i = elements 8i .. 8i+7: consecutive lanes read consecutive 16 bytes,
   // and the four lanes 4b .. 4b+3 of a group hold block b's 32 elements
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
@@ -85,7 +87,10 @@ __global__ __launch_bounds__(256) void mxfp4_quant_kernel(const uint16_t* __rest
   const uint32_t w = e2m1_pack8(v, sc);
   if (!ok) return;
   *reinterpret_cast<uint32_t*>(codes + i * 4) = w;
-  if ((i & 3) == 0) scales[i >> 2] = (uint8_t)sc;
+  if ((i & 3) == 0) {
+    const int64_t blk = i >> 2;  // row blk / nblocks, block blk % nblocks
+    scales[GO ? mx_scale_index<true>(blk / nblocks, blk % nblocks, nblocks) : blk] = (uint8_t)sc;
+  }
 }
 
 // The E8M0 byte and codes of one block of 32 bf16 values (bits), as
@@ -109,6 +114,7 @@ __device__ __forceinline__ void e2m1_block(const uint32_t (&bits)[32], u32x4& w,
 // read 128 consecutive bytes per row; the lane then holds its block's 32
 // elements and writes their 16 code bytes and the scale byte at row c of the
 // transposed codes.
+template <bool GO>
 __global__ __launch_bounds__(256) void mxfp4_quant_t_kernel(const uint16_t* __restrict__ x, int64_t rows,
                                                             int64_t cols, uint8_t* __restrict__ codes,
                                                             uint8_t* __restrict__ scales) {
@@ -123,7 +129,7 @@ __global__ __launch_bounds__(256) void mxfp4_quant_t_kernel(const uint16_t* __re
   uint32_t sc;
   e2m1_block(bits, w, sc);
   *reinterpret_cast<u32x4*>(codes + c * (rows / 2) + rb * 16) = w;
-  scales[c * (rows / 32) + rb] = (uint8_t)sc;
+  scales[mx_scale_index<GO>(c, rb, rows / 32)] = (uint8_t)sc;
 }
 
 // Tiled quantisation of x [rows, cols] (rows % 64 == 0, cols % 128 == 0): a
@@ -132,7 +138,7 @@ __global__ __launch_bounds__(256) void mxfp4_quant_t_kernel(const uint16_t* __re
 // [rows, cols/2], scales [rows, cols/32] -- and/or (COLWISE) one 32-element
 // block down a column -- the codes of x^T, [cols, rows/2], and scales
 // [cols, rows/32].  Both directions from one read of x.
-template <bool ROWWISE, bool COLWISE>
+template <bool ROWWISE, bool COLWISE, bool GO>
 __global__ __launch_bounds__(256) void mxfp4_quant_tile_kernel(const uint16_t* __restrict__ x, int64_t rows,
                                                                int64_t cols, uint8_t* __restrict__ codes,
                                                                uint8_t* __restrict__ scales,
@@ -165,7 +171,7 @@ __global__ __launch_bounds__(256) void mxfp4_quant_tile_kernel(const uint16_t* _
     uint32_t sc;
     e2m1_block(bits, w, sc);
     *reinterpret_cast<u32x4*>(codes + (r0 + r) * (cols / 2) + c0 / 2 + b * 16) = w;
-    scales[(r0 + r) * (cols / 32) + c0 / 32 + b] = (uint8_t)sc;
+    scales[mx_scale_index<GO>(r0 + r, c0 / 32 + b, cols / 32)] = (uint8_t)sc;
   }
   if constexpr (COLWISE) {  // thread: column t / 2, row block t % 2
     const int c = t >> 1, rb = t & 1;
@@ -176,7 +182,7 @@ __global__ __launch_bounds__(256) void mxfp4_quant_tile_kernel(const uint16_t* _
     uint32_t sc;
     e2m1_block(bits, w, sc);
     *reinterpret_cast<u32x4*>(codes_t + (c0 + c) * (rows / 2) + r0 / 2 + rb * 16) = w;
-    scales_t[(c0 + c) * (rows / 32) + r0 / 32 + rb] = (uint8_t)sc;
+    scales_t[mx_scale_index<GO>(c0 + c, r0 / 32 + rb, rows / 32)] = (uint8_t)sc;
   }
 }
 
@@ -242,12 +248,18 @@ hipError_t mxfp6_quantize(const uint16_t* x, int64_t rows, int64_t cols, uint8_t
 }
 
 hipError_t mxfp4_quantize(const uint16_t* x, int64_t rows, int64_t cols, uint8_t* codes, uint8_t* scales,
-                          hipStream_t s) {
+                          hipStream_t s, bool gemm_order) {
   const int64_t nchunks = rows * (cols / 32) * 4;
   if (nchunks <= 0) return hipSuccess;
   const int64_t grid = (nchunks + 255) / 256;
   if (grid > INT32_MAX) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(mxfp4_quant_kernel, dim3((unsigned)grid), dim3(256), 0, s, x, nchunks, codes, scales);
+  if (gemm_order && (rows % 32 || cols % 256)) return hipErrorInvalidValue;
+  if (gemm_order)
+    hipLaunchKernelGGL(mxfp4_quant_kernel<true>, dim3((unsigned)grid), dim3(256), 0, s, x, nchunks, cols / 32, codes,
+                       scales);
+  else
+    hipLaunchKernelGGL(mxfp4_quant_kernel<false>, dim3((unsigned)grid), dim3(256), 0, s, x, nchunks, cols / 32, codes,
+                       scales);
   return hipGetLastError();
 }
 
@@ -562,33 +574,48 @@ hipError_t mxfp4_gemm(const Mxfp4GemmArgs& g, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t mxfp4_quantize_both(const uint16_t* x, int64_t rows, int64_t cols, uint8_t* codes, uint8_t* scales,
+template <bool GO>
+static void launch_quant_tiles(const uint16_t* x, int64_t rows, int64_t cols, uint8_t* codes, uint8_t* scales,
                                uint8_t* codes_t, uint8_t* scales_t, hipStream_t s) {
-  if (rows <= 0 || cols <= 0) return hipSuccess;
-  if (rows % 64 || cols % 128 || rows / 64 > 65535 || cols / 128 > INT32_MAX) return hipErrorInvalidValue;
   const dim3 grid((unsigned)(cols / 128), (unsigned)(rows / 64));
   if (codes && codes_t)
-    hipLaunchKernelGGL((mxfp4_quant_tile_kernel<true, true>), grid, dim3(256), 0, s, x, rows, cols, codes, scales,
+    hipLaunchKernelGGL((mxfp4_quant_tile_kernel<true, true, GO>), grid, dim3(256), 0, s, x, rows, cols, codes, scales,
                        codes_t, scales_t);
   else if (codes_t)
-    hipLaunchKernelGGL((mxfp4_quant_tile_kernel<false, true>), grid, dim3(256), 0, s, x, rows, cols, codes, scales,
-                       codes_t, scales_t);
+    hipLaunchKernelGGL((mxfp4_quant_tile_kernel<false, true, GO>), grid, dim3(256), 0, s, x, rows, cols, codes,
+                       scales, codes_t, scales_t);
   else
-    hipLaunchKernelGGL((mxfp4_quant_tile_kernel<true, false>), grid, dim3(256), 0, s, x, rows, cols, codes, scales,
-                       codes_t, scales_t);
+    hipLaunchKernelGGL((mxfp4_quant_tile_kernel<true, false, GO>), grid, dim3(256), 0, s, x, rows, cols, codes,
+                       scales, codes_t, scales_t);
+}
+
+hipError_t mxfp4_quantize_both(const uint16_t* x, int64_t rows, int64_t cols, uint8_t* codes, uint8_t* scales,
+                               uint8_t* codes_t, uint8_t* scales_t, hipStream_t s, bool gemm_order) {
+  if (rows <= 0 || cols <= 0) return hipSuccess;
+  if (rows % 64 || cols % 128 || rows / 64 > 65535 || cols / 128 > INT32_MAX) return hipErrorInvalidValue;
+  // GEMM order: K % 256 for each written direction (cols for the row-wise
+  // scales, rows for the column-wise ones)
+  if (gemm_order && ((codes && cols % 256) || (codes_t && rows % 256))) return hipErrorInvalidValue;
+  if (gemm_order) launch_quant_tiles<true>(x, rows, cols, codes, scales, codes_t, scales_t, s);
+  else launch_quant_tiles<false>(x, rows, cols, codes, scales, codes_t, scales_t, s);
   return hipGetLastError();
 }
 
 hipError_t mxfp4_quantize_t(const uint16_t* x, int64_t rows, int64_t cols, uint8_t* codes, uint8_t* scales,
-                            hipStream_t s) {
+                            hipStream_t s, bool gemm_order) {
   if (rows <= 0 || cols <= 0) return hipSuccess;
   if (rows % 32) return hipErrorInvalidValue;
+  if (gemm_order && (rows % 256 || cols % 32)) return hipErrorInvalidValue;
   if (rows % 64 == 0 && cols % 128 == 0 && rows / 64 <= 65535)  // whole 64 x 128 tiles
-    return mxfp4_quantize_both(x, rows, cols, nullptr, nullptr, codes, scales, s);
+    return mxfp4_quantize_both(x, rows, cols, nullptr, nullptr, codes, scales, s, gemm_order);
   const int64_t gx = (cols + 63) / 64, gy = (rows / 32 + 3) / 4;
   if (gx > INT32_MAX || gy > 65535) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(mxfp4_quant_t_kernel, dim3((unsigned)gx, (unsigned)gy), dim3(256), 0, s, x, rows, cols, codes,
-                     scales);
+  if (gemm_order)
+    hipLaunchKernelGGL(mxfp4_quant_t_kernel<true>, dim3((unsigned)gx, (unsigned)gy), dim3(256), 0, s, x, rows, cols,
+                       codes, scales);
+  else
+    hipLaunchKernelGGL(mxfp4_quant_t_kernel<false>, dim3((unsigned)gx, (unsigned)gy), dim3(256), 0, s, x, rows, cols,
+                       codes, scales);
   return hipGetLastError();
 }
 

@@ -391,7 +391,8 @@ def test_mfma_ceiling_argument_checks(mtl):
     fake = ctypes.c_void_p(1 << 20)
     assert f(None, 1 << 20, 0, 256, 1, fake, None) == mtl.MTL_E_NULL
     assert f(ctypes.c_void_p((1 << 20) + 8), 1 << 20, 0, 256, 1, fake, None) == mtl.MTL_E_ALIGN
-    assert f(fake, 1 << 20, 2, 256, 1, fake, None) == mtl.MTL_E_UNSUPPORTED
+    assert f(fake, 1 << 20, 3, 256, 1, fake, None) == mtl.MTL_E_UNSUPPORTED
+    assert f(fake, 1 << 20, -1, 256, 1, fake, None) == mtl.MTL_E_UNSUPPORTED
     assert f(fake, (1 << 20) - 16, 0, 256, 1, fake, None) == mtl.MTL_E_SHAPE
     assert f(fake, 1 << 20, 0, 0, 1, fake, None) == mtl.MTL_E_SHAPE
     assert f(fake, 1 << 20, 1, 256, 0, fake, None) == mtl.MTL_E_SHAPE

@@ -1,8 +1,9 @@
 """Parity of mtl_mxfp4_quantize / mtl_mxfp6_quantize (bit-exact codes and
 scales) and mtl_mxfp4_gemm / mtl_mxfp6_gemm with the fp64 MX oracle: every
 finite bf16 value, special blocks (ties, saturation, zeros, tiny and huge
-magnitudes), a GEMM spanning several tiles and K slabs, and the
-4096 x 4096 x 4096 GEMM on sampled rows."""
+magnitudes), a GEMM spanning several tiles and K slabs, and on sampled rows
+and columns (tile edges among them) the 4096 x 4096 x 4096 GEMM and products
+that take each of the GEMM's tile shapes."""
 import numpy as np
 import pytest
 
@@ -99,18 +100,30 @@ def test_mxfp4_gemm_tiles_and_slabs(mtl):
     _close("C", host_f64(c), MX.gemm(ca, sa, cb, sb))
 
 
+# (M, N, K): the full-size workload (256 x 256 tiles), a product taking
+# 256 x 192 tiles (fewer than 240 tiles of 256 x 256, N % 192 == 0) and one
+# filling exactly 240 tiles of 256 x 256
+GEMM_SHAPES = {
+    "full-4096": (synth.MX_WORKLOADS["mxfp4-gemm-7b-tp4"].M, synth.MX_WORKLOADS["mxfp4-gemm-7b-tp4"].N,
+                  synth.MX_WORKLOADS["mxfp4-gemm-7b-tp4"].K),
+    "tiles-256x192": (2048, 6144, 1024),
+    "tiles-256x256-240": (4096, 3840, 768),
+}
+
+
 @pytest.mark.gpu
-def test_mxfp4_gemm_fullsize_sampled(mtl):
+@pytest.mark.parametrize("case", list(GEMM_SHAPES))
+def test_mxfp4_gemm_fullsize_sampled(mtl, case):
     from megatron_tensor_transformer_layer_amd.layer import host_f64
-    shape = synth.MX_WORKLOADS["mxfp4-gemm-7b-tp4"]
-    M, N, K = shape.M, shape.N, shape.K
-    print(f"mxfp4 gemm full size {M}x{N}x{K}", flush=True)
+    M, N, K = GEMM_SHAPES[case]
+    print(f"mxfp4 gemm {case} {M}x{N}x{K}", flush=True)
     a = synth.mx_operand(M, K, "mx_a", 1.0)
     b = synth.mx_operand(N, K, "mx_b", synth.WEIGHT_STD)
     c, (ca_d, sa_d, cb_d, sb_d) = _gemm_dev(a, b)
     rng = np.random.default_rng(5)
-    rm = sorted(set([0, 127, 128, M - 1] + rng.choice(M, 8, replace=False).tolist()))
-    rn = sorted(set([0, 127, 128, N - 1] + rng.choice(N, 8, replace=False).tolist()))
+    edges = [0, 31, 32, 127, 128, 191, 192, 255, 256]  # fragment, 128-, 192- and 256-tile boundaries
+    rm = sorted(set([e for e in edges if e < M] + [M - 1] + rng.choice(M, 8, replace=False).tolist()))
+    rn = sorted(set([e for e in edges if e < N] + [N - 1] + rng.choice(N, 8, replace=False).tolist()))
     ca, sa = MX.quantize(f64(a[rm]))
     cb, sb = MX.quantize(f64(b[rn]))
     assert np.array_equal(ca_d.cpu().numpy()[rm], MX.pack(ca)) and np.array_equal(sa_d.cpu().numpy()[rm], sa)
