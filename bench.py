@@ -428,8 +428,8 @@ def mx_cpu_baseline(shape, sample_rows):
 
 def mx_main(args):
     """One GEMM of the 7B-class rank in MXFP4 or MXFP6: quantise the activations
-    and the weight (mtl_mxfp4_quantize / mtl_mxfp6_quantize) and multiply them
-    on the block-scaled MFMA (mtl_mxfp4_gemm / mtl_mxfp6_gemm)."""
+    and the weight in the GEMM's byte order (mtl_mx_quantize_ordered) and
+    multiply them on the block-scaled MFMA (mtl_mx_gemm_ordered)."""
     import torch
     import synth
     import megatron_tensor_transformer_layer_amd as mtl
@@ -438,8 +438,9 @@ def mx_main(args):
     shape = synth.MX_WORKLOADS[args.workload]
     fp6 = shape.elem == "e2m3"
     name = "MXFP6" if fp6 else "MXFP4"
-    quant = mtl.mtl_mxfp6_quantize if fp6 else mtl.mtl_mxfp4_quantize
-    gemm = mtl.mtl_mxfp6_gemm if fp6 else mtl.mtl_mxfp4_gemm
+    elem = mtl.MTL_MX_E2M3 if fp6 else mtl.MTL_MX_E2M1
+    quant = lambda x, r, k, q, s_: mtl.mtl_mx_quantize_ordered(elem, x, r, k, q, s_, mtl.MTL_MX_ORDER_GEMM)
+    gemm = lambda *g: mtl.mtl_mx_gemm_ordered(elem, *g, mtl.MTL_MX_ORDER_GEMM)
     M, N, K = shape.M, shape.N, shape.K
     cb_cols = K * 3 // 4 if fp6 else K // 2
     a = bf16_dev(synth.mx_operand(M, K, "mx_a", 1.0))
@@ -485,7 +486,8 @@ def mx_main(args):
                    "global_batch": 1, "seq_len": M, "parallelism": "tp4-rank0-of-1gpu"},
         "pct_of_peak": round(100 * fl / (ms / 1e3) / 1e12 / PEAK_FP4_TFLOPS, 2),
         "flop_per_step": fl,
-        "roofline": {"bound": "mfma", "kernel": f"{name.lower()}_gemm_kernel, 128x128 tiles, HIP events on its stream",
+        "roofline": {"bound": "mfma", "kernel": f"gemm_bf16_kernel in its {name} mode (operands in the GEMM's byte "
+                               "order, 256x256 tiles), HIP events on its stream",
                      "achieved": round(achieved, 1), "peak": PEAK_FP4_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved / PEAK_FP4_TFLOPS, 4), "traffic": None,
                      "gemm_launch_us": round(gemm_ms * 1e3, 1)},

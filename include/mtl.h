@@ -265,6 +265,35 @@ mtl_status mtl_mxfp6_quantize(const void* x, int64_t rows, int64_t cols, void* c
 mtl_status mtl_mxfp6_gemm(int64_t M, int64_t N, int64_t K, const void* a_codes, const void* a_scales,
                           const void* b_codes, const void* b_scales, void* c, int64_t ldc, mtl_stream_t stream);
 
+/* The MX quantisers and GEMMs with a choice of byte order (the same values
+ * either way).  elem: MTL_MX_E2M1 (MXFP4) or MTL_MX_E2M3 (MXFP6).
+ * MTL_MX_ORDER_PLAIN: codes and scales as mtl_mxfp4_quantize /
+ * mtl_mxfp6_quantize write them (the calls above).
+ * MTL_MX_ORDER_GEMM (rows % 32 == 0, cols % 256 == 0), the order the GEMM
+ * reads fastest, one load per lane:
+ *   scales: the rows' scale bytes in groups of 256 bytes, one group per 32-row
+ *     block rb and 256-element span s of the row, group rb * cols/256 + s;
+ *     block q (0..7 within the span) of row r at byte 4 * (r % 32 + 32 * (q %
+ *     2)) + q / 2 of the group.
+ *   MXFP4 codes: plain.
+ *   MXFP6 codes: per row, each 128-element span (4 blocks, 96 bytes) holds
+ *     the four blocks' first 16 bytes at 16 b, then their last 8 bytes: blocks
+ *     0 and 1 in bytes 64..79, blocks 2 and 3 in bytes 80..95, block 2j at the
+ *     first 8 of those bytes and 2j + 1 at the last 8 -- swapped in rows r with
+ *     (r / 16) odd.
+ * The GEMM: as mtl_mxfp4_gemm on operands of that order; MTL_MX_ORDER_GEMM
+ * takes M % 32 == 0, N % 32 == 0, K % 256 == 0.  Errors: MTL_E_NULL,
+ * MTL_E_ALIGN, MTL_E_SHAPE, MTL_E_UNSUPPORTED (elem or order). */
+#define MTL_MX_E2M1 0
+#define MTL_MX_E2M3 1
+#define MTL_MX_ORDER_PLAIN 0
+#define MTL_MX_ORDER_GEMM 1
+mtl_status mtl_mx_quantize_ordered(int32_t elem, const void* x, int64_t rows, int64_t cols, void* codes,
+                                   void* scales, int32_t order, mtl_stream_t stream);
+mtl_status mtl_mx_gemm_ordered(int32_t elem, int64_t M, int64_t N, int64_t K, const void* a_codes,
+                               const void* a_scales, const void* b_codes, const void* b_scales, void* c, int64_t ldc,
+                               int32_t order, mtl_stream_t stream);
+
 /* MLP half of the rank's forward (column-parallel fc1 with fused GeLU,
  * row-parallel fc2), with z = h . w1 + b1 in fp32:
  *   gz      = GeLU'(z)        [S, f/t] bf16 (saved: the backward needs z only

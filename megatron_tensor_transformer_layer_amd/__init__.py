@@ -19,6 +19,8 @@ HEADER = os.path.join(os.path.dirname(HERE), "include", "mtl.h")
 MTL_OK, MTL_E_NULL, MTL_E_DIVISIBILITY, MTL_E_RANK, MTL_E_SHAPE = 0, 1, 2, 3, 4
 MTL_E_ALIGN, MTL_E_WORKSPACE, MTL_E_UNSUPPORTED, MTL_E_HIP = 5, 6, 7, 8
 MTL_PREC_BF16, MTL_PREC_FP8_HYBRID, MTL_PREC_MXFP4 = 0, 1, 2
+MTL_MX_E2M1, MTL_MX_E2M3 = 0, 1
+MTL_MX_ORDER_PLAIN, MTL_MX_ORDER_GEMM = 0, 1
 MTL_FP8_E4M3, MTL_FP8_E5M2 = 0, 1
 MTL_FP8_AMAX_SCRATCH = 4096
 MTL_CP_MAX = 64
@@ -63,6 +65,8 @@ _SIGS = {
     "mtl_mxfp4_quantize_t": (ctypes.c_int, [_P, _I64, _I64, _P, _P, _P]),
     "mtl_mxfp6_quantize": (ctypes.c_int, [_P, _I64, _I64, _P, _P, _P]),
     "mtl_mxfp6_gemm": (ctypes.c_int, [_I64, _I64, _I64, _P, _P, _P, _P, _P, _I64, _P]),
+    "mtl_mx_quantize_ordered": (ctypes.c_int, [_I32, _P, _I64, _I64, _P, _P, _I32, _P]),
+    "mtl_mx_gemm_ordered": (ctypes.c_int, [_I32, _I64, _I64, _I64, _P, _P, _P, _P, _P, _I64, _I32, _P]),
     "mtl_cp_attn_bwd_scratch_bytes": (ctypes.c_int, [_I32, _I32, _I64, _I32, _I32, ctypes.POINTER(_SZ)]),
     "mtl_cp_attn_bwd": (ctypes.c_int, [_I32, _I32, _I64, _I32, _I32, ctypes.POINTER(_P), _P, _P, _P, _P,
                                        ctypes.POINTER(_P), _P, _SZ, _P]),
@@ -231,6 +235,17 @@ def mtl_mxfp6_quantize(x, rows, cols, codes, scales, stream=None):
 def mtl_mxfp6_gemm(M, N, K, a_codes, a_scales, b_codes, b_scales, c, ldc=None, stream=None):
     _check(lib().mtl_mxfp6_gemm(M, N, K, _ptr(a_codes), _ptr(a_scales), _ptr(b_codes), _ptr(b_scales), _ptr(c),
                                 N if ldc is None else ldc, _stream(stream)), "mtl_mxfp6_gemm")
+
+
+def mtl_mx_quantize_ordered(elem, x, rows, cols, codes, scales, order, stream=None):
+    _check(lib().mtl_mx_quantize_ordered(elem, _ptr(x), rows, cols, _ptr(codes), _ptr(scales), order,
+                                         _stream(stream)), "mtl_mx_quantize_ordered")
+
+
+def mtl_mx_gemm_ordered(elem, M, N, K, a_codes, a_scales, b_codes, b_scales, c, order, ldc=None, stream=None):
+    _check(lib().mtl_mx_gemm_ordered(elem, M, N, K, _ptr(a_codes), _ptr(a_scales), _ptr(b_codes), _ptr(b_scales),
+                                     _ptr(c), N if ldc is None else ldc, order, _stream(stream)),
+           "mtl_mx_gemm_ordered")
 
 
 def mtl_mlp_fwd(cfg, h, w1, b1, w2, gz, a, partial, scratch=None, scratch_bytes=None, stream=None):

@@ -849,6 +849,51 @@ mtl_status mtl_mxfp6_gemm(int64_t M, int64_t N, int64_t K, const void* a_codes, 
   return hip_status(mxfp6_gemm(g, reinterpret_cast<hipStream_t>(stream)));
 }
 
+mtl_status mtl_mx_quantize_ordered(int32_t elem, const void* x, int64_t rows, int64_t cols, void* codes, void* scales,
+                                   int32_t order, mtl_stream_t stream) {
+  mtl_status st = check_ptrs(x, codes, scales);
+  if (st != MTL_OK) return st;
+  if (elem != MTL_MX_E2M1 && elem != MTL_MX_E2M3) return MTL_E_UNSUPPORTED;
+  if (order != MTL_MX_ORDER_PLAIN && order != MTL_MX_ORDER_GEMM) return MTL_E_UNSUPPORTED;
+  if (rows <= 0 || cols <= 0 || cols % 32 != 0 || rows > INT32_MAX || cols > INT32_MAX) return MTL_E_SHAPE;
+  const bool go = order == MTL_MX_ORDER_GEMM;
+  if (go && (rows % 32 || cols % 256)) return MTL_E_SHAPE;
+  const auto* xs = static_cast<const uint16_t*>(x);
+  auto* q = static_cast<uint8_t*>(codes);
+  auto* sc = static_cast<uint8_t*>(scales);
+  const hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  return hip_status(elem == MTL_MX_E2M1 ? mxfp4_quantize(xs, rows, cols, q, sc, s, go)
+                                        : mxfp6_quantize(xs, rows, cols, q, sc, s, go));
+}
+
+mtl_status mtl_mx_gemm_ordered(int32_t elem, int64_t M, int64_t N, int64_t K, const void* a_codes,
+                               const void* a_scales, const void* b_codes, const void* b_scales, void* c, int64_t ldc,
+                               int32_t order, mtl_stream_t stream) {
+  mtl_status st = check_ptrs(a_codes, a_scales, b_codes, b_scales, c);
+  if (st != MTL_OK) return st;
+  if (elem != MTL_MX_E2M1 && elem != MTL_MX_E2M3) return MTL_E_UNSUPPORTED;
+  if (order != MTL_MX_ORDER_PLAIN && order != MTL_MX_ORDER_GEMM) return MTL_E_UNSUPPORTED;
+  if (M <= 0 || N <= 0 || K <= 0 || ldc < N || ldc % 8) return MTL_E_SHAPE;
+  if (M > INT32_MAX || N > INT32_MAX || K > INT32_MAX) return MTL_E_SHAPE;
+  if (order == MTL_MX_ORDER_GEMM ? (M % 32 || N % 32 || K % 256)
+                                 : (M % 128 || N % 128 || K % (elem == MTL_MX_E2M1 ? 256 : 128)))
+    return MTL_E_SHAPE;
+  Mxfp4GemmArgs g{};
+  g.a = static_cast<const uint8_t*>(a_codes);
+  g.sa = static_cast<const uint8_t*>(a_scales);
+  g.b = static_cast<const uint8_t*>(b_codes);
+  g.sb = static_cast<const uint8_t*>(b_scales);
+  g.c = static_cast<uint16_t*>(c);
+  g.ldc = ldc;
+  g.M = (int)M;
+  g.N = (int)N;
+  g.K = (int)K;
+  g.scale_order = order;
+  const hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (elem == MTL_MX_E2M1) return hip_status(gemm_mxfp4_tiled(g, s));
+  return hip_status(order == MTL_MX_ORDER_GEMM ? gemm_mxfp6_tiled(g, s) : mxfp6_gemm(g, s));
+}
+
 mtl_status mtl_mlp_fwd(const mtl_layer_cfg* c, const void* h, const void* w1, const void* b1, const void* w2, void* gz,
                        void* a, void* partial, void* scratch, size_t scratch_bytes, mtl_stream_t stream) {
   mtl_status st = mtl_validate(c);

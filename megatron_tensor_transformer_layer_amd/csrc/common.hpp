@@ -69,6 +69,29 @@ __device__ __forceinline__ f32x16 mfma32_mxfp4(const u32x4& a, const u32x4& b, c
   }
 }
 
+// MXFP6 (E2M3) operand of one lane: 24 bytes (32 codes of 6 bits) from a
+// 16-byte head and an 8-byte tail; the instruction reads six registers for
+// this format, the last two stay undefined.
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+__device__ __forceinline__ i32x8 mx6_operand(const u32x4& head, const u32x2& tail) {
+  typedef int i32x2_t __attribute__((ext_vector_type(2)));
+  typedef int i32x4_t __attribute__((ext_vector_type(4)));
+  const i32x4_t h = __builtin_bit_cast(i32x4_t, head);
+  const i32x2_t t2 = __builtin_bit_cast(i32x2_t, tail);
+  const i32x4_t t = __builtin_shufflevector(t2, t2, 0, 1, -1, -1);
+  return __builtin_shufflevector(h, t, 0, 1, 2, 3, 4, 5, -1, -1);
+}
+// MXFP6 x MXFP6 32x32x64 MFMA; scales as mfma32_mxfp4.
+__device__ __forceinline__ f32x16 mfma32_mxfp6(const i32x8& a, const i32x8& b, const f32x16& c, uint32_t sa,
+                                               uint32_t sb, int kk) {
+  switch (kk & 3) {  // op_sel must be a constant: kk is one after unrolling
+    case 0: return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 2, 2, 0, (int)sa, 0, (int)sb);
+    case 1: return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 2, 2, 1, (int)sa, 1, (int)sb);
+    case 2: return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 2, 2, 2, (int)sa, 2, (int)sb);
+    default: return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 2, 2, 3, (int)sa, 3, (int)sb);
+  }
+}
+
 // ---------------------------------------------------------------- LDS tiles
 // A k-contiguous tile of R rows x 64 bf16 (128 B per row) is stored as eight
 // 16-byte chunks per row, chunk c of row r at physical chunk c ^ (r & 7): eight

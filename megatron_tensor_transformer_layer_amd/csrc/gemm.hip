@@ -62,11 +62,15 @@ __device__ __forceinline__ int mn_swz(int k) {
   else return ((k >> 1) & 1) << 2;
 }
 
-template <int ROWS, bool KC, int EB = 2, int NWAVES = 4>
+// USED: 16-byte chunks of a row's 128 LDS bytes that carry data (8; 6 for
+// MXFP6, whose slab of 128 k is 96 code bytes per row; the lanes of the other
+// two chunks load zeros, their loads placed out of the buffer's range).
+template <int ROWS, bool KC, int EB = 2, int NWAVES = 4, int USED = 8>
 struct Operand {
   static_assert(EB == 2 || KC, "fp8 operands are k-contiguous");
+  static_assert(USED == 8 || KC, "partial rows are k-contiguous");
   static constexpr int BYTES = ROWS * 128;     // one slab: 128 bytes of k per row
-  static constexpr int KSLAB = 128 / EB;       // k per slab: 64 bf16 or 128 fp8
+  static constexpr int KSLAB = USED * 16 / EB; // k per slab: 64 bf16 or 128 fp8 (96 MXFP6 code bytes)
   static constexpr int CHUNK = 16 / EB;        // k per 16-byte chunk
   static constexpr int INSTR = BYTES / 1024;   // wave instructions per slab
   static constexpr int PER_WAVE = INSTR / NWAVES;
@@ -94,7 +98,7 @@ struct Operand {
       if constexpr (KC) {
         const int row = I * 8 + (lane >> 3);
         const int c = (lane & 7) ^ kc_swz(row);
-        voff[q] = (uint32_t)(((int64_t)(row0 + row) * ld + c * CHUNK) * EB);
+        voff[q] = c < USED ? (uint32_t)(((int64_t)(row0 + row) * ld + c * CHUNK) * EB) : 0x80000000u;
       } else {
         const int o = I * 1024 + lane * 16;
         const int k = o / ROWB;
@@ -144,6 +148,19 @@ struct Operand {
     hi = *reinterpret_cast<const LDS_AS u32x4*>(lds + row * 128 + (((c + 1) ^ kc_swz(row)) << 4));
   }
 
+  // MXFP6 fragment (GEMM code order) of 32-row block r32 at k step kk (64
+  // deep, the slab's blocks 2 kk and 2 kk + 1): lane l holds row l % 32 and
+  // block b = 2 kk + l / 32 -- its first 16 bytes in chunk b, its last 8 in
+  // half (b % 2) ^ (row / 16 % 2) of chunk 4 + kk.
+  static __device__ __forceinline__ void frag6(const LDS_AS char* lds, int r32, int kk, int lane, u32x4& main,
+                                               u32x2& tail) {
+    const int row = r32 * 32 + (lane & 31);
+    const int b = kk * 2 + (lane >> 5);
+    const int half = (b & 1) ^ ((row >> 4) & 1);
+    main = *reinterpret_cast<const LDS_AS u32x4*>(lds + row * 128 + ((b ^ kc_swz(row)) << 4));
+    tail = *reinterpret_cast<const LDS_AS u32x2*>(lds + row * 128 + (((4 + kk) ^ kc_swz(row)) << 4) + half * 8);
+  }
+
   // Operand fragment of 32-row block r32 at k step kk (16 deep): lane l holds
   // row (l % 32) and k = kk*16 + (l/32)*8 + j, j = 0..7.
   static __device__ __forceinline__ u32x4 frag(const LDS_AS char* lds, int r32, int kk, int lane) {
@@ -171,22 +188,27 @@ struct Operand {
 // one E8M0 scale byte per 32 k; scale matrices in plain or GEMM order), both
 // k-contiguous; K, lda and ldb then count code bytes.
 constexpr int F8_MXFP4 = 5, F8_MXFP4_GO = 6;
+// F8 = F8_MXFP6_GO: MXFP6 (E2M3) operands with codes and scales in GEMM order;
+// K, lda and ldb count code bytes (3/4 per k), a slab is 128 k (96 bytes).
+constexpr int F8_MXFP6_GO = 7;
 template <int BM, int BN, bool A_K, bool B_K, int F8 = 0, int NWN = 2>
 struct Mainloop {
   static constexpr int NWAVES = 2 * NWN;  // 2 x NWN waves over the tile
   static constexpr int WM = BM / 2, WN = BN / NWN;
   static constexpr int TM = WM / 32, TN = WN / 32;
   static constexpr bool FP4 = F8 == F8_MXFP4 || F8 == F8_MXFP4_GO;
-  static constexpr bool GO = F8 == F8_MXFP4_GO;
-  static_assert(!FP4 || (A_K && B_K), "MXFP4 operands are k-contiguous");
+  static constexpr bool FP6 = F8 == F8_MXFP6_GO;
+  static constexpr bool MX = FP4 || FP6;  // block-scaled operands
+  static constexpr bool GO = F8 == F8_MXFP4_GO || FP6;
+  static_assert(!MX || (A_K && B_K), "MX operands are k-contiguous");
   static constexpr int EB = F8 ? 1 : 2;
-  static constexpr int FA = (F8 && !FP4) ? (F8 - 1) & 1 : 0, FB = (F8 && !FP4) ? (F8 - 1) >> 1 : 0;
-  using OA = Operand<BM, A_K, EB, NWAVES>;
-  using OB = Operand<BN, B_K, EB, NWAVES>;
+  static constexpr int FA = (F8 && !MX) ? (F8 - 1) & 1 : 0, FB = (F8 && !MX) ? (F8 - 1) >> 1 : 0;
+  using OA = Operand<BM, A_K, EB, NWAVES, FP6 ? 6 : 8>;
+  using OB = Operand<BN, B_K, EB, NWAVES, FP6 ? 6 : 8>;
   static constexpr int KSLAB = OA::KSLAB;
-  // MFMA k steps per slab: 16 bf16, 64 fp8 (two 16-byte chunks per lane) or 64
-  // MXFP4 (one chunk per lane) deep
-  static constexpr int KSTEPS = (F8 && !FP4) ? 2 : 4;
+  // MFMA k steps per slab: 16 bf16, 64 fp8 (two 16-byte chunks per lane), 64
+  // MXFP4 (one chunk per lane) or 64 MXFP6 (a chunk and a half) deep
+  static constexpr int KSTEPS = FP4 ? 4 : (F8 ? 2 : 4);
   static constexpr int STAGE = OA::BYTES + OB::BYTES;
 
   // per-lane chunk offsets of slab 0 for both operands
@@ -231,16 +253,22 @@ struct Mainloop {
   // block) and at the slab's start selects its four bytes into the word.  GEMM
   // order: the word of lane l is already at 4 l of the 32-row block's 256-byte
   // group of the slab, one coalesced dword load per row block.
-  static constexpr int NS = FP4 ? TM + TN : 1;
+  // MXFP6 slabs are 128 k: a word (256 k) serves two slabs, the first taking
+  // its bytes 0 and 1, the second (shifted down by 16) bytes 2 and 3.
+  static constexpr int NS = MX ? TM + TN : 1;
   using SW = std::conditional_t<GO, uint32_t, u32x2>;  // loaded per row block and slab
   struct Scl {
     uint32_t off[NS];  // byte offset of the lane's row (block) in its scale matrix
     SW cur[NS];        // the slab being multiplied
     SW nxt[NS];        // the next slab
+    int par;           // MXFP6: parity of the slab being multiplied
   };
+  // scale bytes per row: K/32 of K code bytes of two (MXFP4) or 4/3 (MXFP6) k each
+  static __device__ __forceinline__ int scale_row_bytes(const GemmArgs& p) { return FP6 ? p.K / 24 : p.K / 16; }
   static __device__ __forceinline__ void scl_offsets(const GemmArgs& p, int m0, int n0, int wm, int wn, int lane,
                                                      Scl& sc) {
-    const int ks = p.K / 16;  // scale bytes per row (K counts code bytes, two k each)
+    const int ks = scale_row_bytes(p);
+    sc.par = 0;
     if constexpr (GO) {
       // group (row / 32) * slabs + slab, 256 bytes each, 16 per row block per K / 2 code bytes
 #pragma unroll
@@ -258,7 +286,9 @@ struct Mainloop {
   static __device__ __forceinline__ void scl_load(__amdgpu_buffer_rsrc_t rsa, __amdgpu_buffer_rsrc_t rsb,
                                                   const Scl& sc, int k0, SW (&dst)[NS]) {
     if constexpr (GO) {
-      const uint32_t kb = (uint32_t)k0 * 2;  // 256 bytes per 128 code bytes of k
+      // the 256-byte group of the slab's 256 k: 128 code bytes per MXFP4 slab;
+      // two 96-byte MXFP6 slabs per group
+      const uint32_t kb = FP6 ? ((uint32_t)k0 / 96 / 2) * 256 : (uint32_t)k0 * 2;
 #pragma unroll
       for (int i = 0; i < NS; ++i)
         dst[i] = __builtin_amdgcn_raw_buffer_load_b32(i < TM ? rsa : rsb, (int)(sc.off[i] + kb), 0, 0);
@@ -274,16 +304,32 @@ struct Mainloop {
   // The operand fragments of one MFMA k step (16 deep for bf16, 64 for fp8,
   // whose fragments are two 16-byte chunks, and for MXFP4, whose fragments are
   // one chunk, with the slab's scale words).
-  static constexpr int NF = (F8 && !FP4) ? 2 : 1;
+  static constexpr int NF = (F8 && !MX) ? 2 : 1;
   struct Frags {
     u32x4 a[TM][NF], b[TN][NF];
+    i32x8 a6[FP6 ? TM : 1], b6[FP6 ? TN : 1];  // MXFP6 fragments (in place of a, b)
     uint32_t s[NS];
   };
   static __device__ __forceinline__ void read_step(const LDS_AS char* __restrict__ st, int wm, int wn, int lane, int kk,
                                                    Frags& f) {
     const LDS_AS char* sa = st;
     const LDS_AS char* sb = st + OA::BYTES;
-    if constexpr (F8 != 0 && !FP4) {
+    if constexpr (FP6) {
+#pragma unroll
+      for (int i = 0; i < TM; ++i) {
+        u32x4 h;
+        u32x2 t;
+        OA::frag6(sa, wm * TM + i, kk, lane, h, t);
+        f.a6[i] = mx6_operand(h, t);
+      }
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+        u32x4 h;
+        u32x2 t;
+        OB::frag6(sb, wn * TN + j, kk, lane, h, t);
+        f.b6[j] = mx6_operand(h, t);
+      }
+    } else if constexpr (F8 != 0 && !FP4) {
 #pragma unroll
       for (int i = 0; i < TM; ++i) OA::frag8(sa, wm * TM + i, kk, lane, f.a[i][0], f.a[i][1]);
 #pragma unroll
@@ -303,7 +349,9 @@ struct Mainloop {
     for (int i = 0; i < TM; ++i)
 #pragma unroll
       for (int j = 0; j < TN; ++j) {
-        if constexpr (FP4)
+        if constexpr (FP6)
+          acc[i][j] = mfma32_mxfp6(f.b6[j], f.a6[i], acc[i][j], f.s[TM + j], f.s[i], kk);
+        else if constexpr (FP4)
           acc[i][j] = mfma32_mxfp4(f.b[j][0], f.a[i][0], acc[i][j], f.s[TM + j], f.s[i], kk);
         else if constexpr (F8 != 0)
           acc[i][j] = mfma32_f8<FB, FA>(f.b[j][0], f.b[j][1], f.a[i][0], f.a[i][1], acc[i][j]);
@@ -335,20 +383,22 @@ struct Mainloop {
       kbb = OB::slab_bytes(p.ldb, k1);
     }
     uint32_t wsc[NS];
-    if constexpr (FP4) {
+    if constexpr (MX) {
       const uint32_t sel = (lane >> 5) ? 0x07050301u : 0x06040200u;  // bytes 2*kk + lane/32
 #pragma unroll
       for (int i = 0; i < NS; ++i) {
-        if constexpr (GO) wsc[i] = sc.cur[i];
+        if constexpr (FP6) wsc[i] = sc.cur[i] >> (16 * sc.par);
+        else if constexpr (GO) wsc[i] = sc.cur[i];
         else wsc[i] = __builtin_amdgcn_perm(sc.cur[i][1], sc.cur[i][0], sel);
         sc.cur[i] = sc.nxt[i];
       }
+      sc.par ^= 1;
       if constexpr (STAGE) scl_load(rsa, rsb, sc, k1, sc.nxt);
     }
 #pragma unroll
     for (int kk = 0; kk < KSTEPS; ++kk) {
       read_step(st, wm, wn, lane, kk, f[kk & 1]);
-      if constexpr (FP4) {
+      if constexpr (MX) {
 #pragma unroll
         for (int i = 0; i < NS; ++i) f[kk & 1].s[i] = wsc[i];
       }
@@ -361,7 +411,8 @@ struct Mainloop {
     // Schedule: each step's MFMAs with its fragment reads interleaved one for
     // one, and its share of the chunk writes and reloads spread evenly over them
     // (each reload right after its chunk's write).
-    constexpr int NR = (TM * OA::READS + TN * OB::READS) * NF;  // LDS reads per step
+    // LDS reads per step (an MXFP4 fragment is one read, an MXFP6 one two)
+    constexpr int NR = FP6 ? 2 * (TM + TN) : (FP4 ? TM + TN : (TM * OA::READS + TN * OB::READS) * NF);
     constexpr int NM = TM * TN;                                 // MFMAs per step
 #pragma unroll
     for (int kk = 0; kk < KSTEPS; ++kk) {
@@ -483,11 +534,10 @@ __device__ __forceinline__ void gemm_tile(GemmArgs p, const int bid, LDS_AS char
   // bytes); rows past M or N read as 0
   __amdgpu_buffer_rsrc_t vsa = va, vsb = vb;  // (unused by the other modes)
   typename ML::Scl sc;
-  if constexpr (ML::FP4) {  // (the same byte count in either order)
-    vsa = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(p.mx_sa), 0, (int)((int64_t)p.M * (p.K / 16)),
-                                            0x00020000);
-    vsb = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(p.mx_sb), 0, (int)((int64_t)p.N * (p.K / 16)),
-                                            0x00020000);
+  if constexpr (ML::MX) {  // (the same byte count in either order)
+    const int64_t ks = ML::scale_row_bytes(p);
+    vsa = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(p.mx_sa), 0, (int)(p.M * ks), 0x00020000);
+    vsb = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(p.mx_sb), 0, (int)(p.N * ks), 0x00020000);
     ML::scl_offsets(p, m0, n0, wm, wn, lane, sc);
     ML::scl_load(vsa, vsb, sc, 0, sc.cur);
     if (nk > 1) ML::scl_load(vsa, vsb, sc, KSLAB, sc.nxt);
@@ -587,7 +637,7 @@ __device__ __forceinline__ void gemm_tile(GemmArgs p, const int bid, LDS_AS char
 
   // fp8: the product of the two operands' dequantisation factors (MXFP4 scales
   // are applied by the MFMA)
-  constexpr bool DQ = F8 != 0 && !ML::FP4;
+  constexpr bool DQ = F8 != 0 && !ML::MX;
   float dq = 1.f;
   if constexpr (DQ) dq = *p.scale_a * *p.scale_b;
   // bias kept as packed bf16 (half the registers), widened where it is added
@@ -963,6 +1013,26 @@ hipError_t gemm_mxfp4_tiled(const Mxfp4GemmArgs& g, hipStream_t s) {
     case EPI_F32_ACC: return launch_mx<EPI_F32_ACC, F8_MXFP4_GO>(p, s);
   }
   return hipErrorInvalidValue;
+}
+
+hipError_t gemm_mxfp6_tiled(const Mxfp4GemmArgs& g, hipStream_t s) {
+  if (g.M <= 0 || g.N <= 0 || g.K <= 0) return hipSuccess;
+  if (g.K % 256 || g.M % 32 || g.N % 32 || g.epi != EPI_BF16) return hipErrorInvalidValue;
+  const int64_t kb = (int64_t)g.K * 3 / 4;  // code bytes per row
+  if (((int64_t)g.M + 256) * kb >= ((int64_t)1 << 31) || ((int64_t)g.N + 256) * kb >= ((int64_t)1 << 31))
+    return hipErrorInvalidValue;
+  GemmArgs p{};
+  p.a = reinterpret_cast<const uint16_t*>(g.a);
+  p.b = reinterpret_cast<const uint16_t*>(g.b);
+  p.lda = p.ldb = kb;
+  p.M = g.M;
+  p.N = g.N;
+  p.K = (int)kb;
+  p.ldc = g.ldc;
+  p.c = g.c;
+  p.mx_sa = g.sa;
+  p.mx_sb = g.sb;
+  return launch_mx<EPI_BF16, F8_MXFP6_GO>(p, s);
 }
 
 hipError_t gemm_fp8(const GemmArgs& p, int fmt_a, int fmt_b, int epi, hipStream_t s) {

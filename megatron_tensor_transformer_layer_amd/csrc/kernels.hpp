@@ -171,8 +171,7 @@ __host__ __device__ __forceinline__ int64_t mx_scale_index(int64_t r, int64_t q,
 hipError_t mxfp4_quantize(const uint16_t* x, int64_t rows, int64_t cols, uint8_t* codes, uint8_t* scales,
                           hipStream_t s, bool gemm_order = false);
 // c [M, N] bf16 (row stride ldc) = A B^T over K, A [M, K] and B [N, K] in
-// MXFP4 (codes and scales as mxfp4_quantize writes them, plain order); M, N %
-// 128 == 0, K % 256 == 0.
+// MXFP4 or MXFP6 (codes and scales as the quantisers write them).
 struct Mxfp4GemmArgs {
   const uint8_t* a;
   const uint8_t* sa;
@@ -181,7 +180,7 @@ struct Mxfp4GemmArgs {
   uint16_t* c;
   int64_t ldc;
   int M, N, K;
-  // MXFP4 epilogues (mxfp4_gemm; MXFP6 is EPI_BF16 only), as the bf16 GEMM's:
+  // MXFP4 epilogues (MXFP6 is EPI_BF16 only), as the bf16 GEMM's:
   int epi;               // EPI_* (0: bf16 C)
   const uint16_t* bias;  // [N] (EPI_BF16_BIAS, EPI_BIAS_GELU)
   uint16_t* c2;          // GeLU(z) [M, N], row stride ldc (EPI_BIAS_GELU)
@@ -189,9 +188,8 @@ struct Mxfp4GemmArgs {
   float* c32;            // fp32 C [M, N], row stride ldc (EPI_F32, EPI_F32_ACC)
   int scale_order;       // gemm_mxfp4_tiled: 0 plain (EPI_BF16 only), 1 GEMM order (M, N % 32 == 0)
 };
-hipError_t mxfp4_gemm(const Mxfp4GemmArgs& g, hipStream_t s);
-// The same product on the bf16 GEMM's pipeline (256 x 256, 256 x 192 or 128 x
-// 128 tiles, two slabs in flight), for K % 256 == 0.
+// MXFP4 on the bf16 GEMM's pipeline (256 x 256, 256 x 192 or 128 x 128 tiles,
+// two slabs in flight), for K % 256 == 0.
 hipError_t gemm_mxfp4_tiled(const Mxfp4GemmArgs& g, hipStream_t s);
 // MXFP4 quantisation of x [rows, cols] down its columns (blocks of 32 rows of
 // one column): codes of x^T, [cols, rows/2] bytes, and the scales of x^T,
@@ -209,8 +207,22 @@ hipError_t mxfp4_quantize_both(const uint16_t* x, int64_t rows, int64_t cols, ui
 // of 6 bits per 24 bytes, element j at bits 6j.. of the little-endian block;
 // the GEMM takes K % 128 == 0.
 hipError_t mxfp6_quantize(const uint16_t* x, int64_t rows, int64_t cols, uint8_t* codes, uint8_t* scales,
-                          hipStream_t s);
+                          hipStream_t s, bool gemm_order = false);
+// Byte offset, within its row's codes, of byte o (0..23) of block q of row r
+// in MXFP6 GEMM code order.
+__host__ __device__ __forceinline__ int64_t mx6_code_offset(int64_t r, int64_t q, int o) {
+  const int64_t slab = (q >> 2) * 96;
+  const int b = (int)(q & 3);
+  if (o < 16) return slab + b * 16 + o;
+  return slab + 64 + (b >> 1) * 16 + (((b & 1) ^ ((r >> 4) & 1)) * 8) + (o - 16);
+}
 hipError_t mxfp6_gemm(const Mxfp4GemmArgs& g, hipStream_t s);
+// MXFP6 codes in GEMM order (mxfp6_quantize with gemm_order): per row, each
+// slab of 128 k (4 blocks, 96 bytes) holds the blocks' first 16 bytes in
+// chunks 0..3 and their last 8 bytes in chunk 4 (blocks 0, 1) and chunk 5
+// (blocks 2, 3), the two halves of each of those chunks swapped in rows with
+// (row / 16) odd.  Scales in GEMM order.
+hipError_t gemm_mxfp6_tiled(const Mxfp4GemmArgs& g, hipStream_t s);
 hipError_t attention_bwd(const AttnArgs& a, hipStream_t s);
 // The backward of attention_fwd_full for queries whose D = rowsum(dO * O) is
 // already in a.delta (kv_seq == seq, seq % 64 == 0): no D launch.

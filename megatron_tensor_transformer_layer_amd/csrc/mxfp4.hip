@@ -7,9 +7,9 @@
 // 6) with the sign of v; two codes per byte, the even element in the low
 // nibble.  Finite inputs only.
 //
-// The GEMM multiplies on v_mfma_scale_f32_32x32x64_f8f6f4 with both operands
-// in FP4 and the block scales fed per lane: in a 32 x 64 operand fragment lane
-// l holds row l % 32 and the 32 elements k = (l / 32) * 32 .. +31 (16 bytes),
+// The GEMMs multiply on v_mfma_scale_f32_32x32x64_f8f6f4 with the block
+// scales fed per lane: in a 32 x 64 operand fragment lane l holds row l % 32
+// and the 32 elements k = (l / 32) * 32 .. +31 (16 bytes in FP4, 24 in FP6),
 // i.e. exactly one scale block, whose E8M0 byte it passes as its scale.
 #include "common.hpp"
 #include "kernels.hpp"
@@ -209,8 +209,10 @@ __device__ __forceinline__ uint32_t e2m3_code(float y, uint32_t sign) {
 
 // MXFP6: four lanes per block as for MXFP4; each lane's 8 codes are 48
 // consecutive bits of the block's 24 bytes, written as three 16-bit words.
+template <bool GO>  // codes and scales in GEMM order (else plain)
 __global__ __launch_bounds__(256) void mxfp6_quant_kernel(const uint16_t* __restrict__ x, int64_t nchunks,
-                                                          uint8_t* __restrict__ codes, uint8_t* __restrict__ scales) {
+                                                          int64_t nblocks, uint8_t* __restrict__ codes,
+                                                          uint8_t* __restrict__ scales) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
   const bool ok = i < nchunks;
   const u32x4 v = ok ? *reinterpret_cast<const u32x4*>(x + i * 8) : u32x4{0, 0, 0, 0};
@@ -230,20 +232,38 @@ __global__ __launch_bounds__(256) void mxfp6_quant_kernel(const uint16_t* __rest
     w |= (uint64_t)e2m3_code(y, bits >> 15) << (6 * h);
   }
   if (!ok) return;
-  uint16_t* dst = reinterpret_cast<uint16_t*>(codes + i * 6);
-  dst[0] = (uint16_t)w;
-  dst[1] = (uint16_t)(w >> 16);
-  dst[2] = (uint16_t)(w >> 32);
-  if ((i & 3) == 0) scales[i >> 2] = (uint8_t)sc;
+  if constexpr (GO) {
+    // the lane's bytes 6j .. 6j+5 of block q of row r, word by word (no word
+    // straddles a head/tail or half boundary)
+    const int64_t blk = i >> 2, r = blk / nblocks, q = blk % nblocks;
+    uint8_t* row = codes + r * nblocks * 24;
+    const int o = 6 * (int)(i & 3);
+#pragma unroll
+    for (int t = 0; t < 3; ++t)
+      *reinterpret_cast<uint16_t*>(row + mx6_code_offset(r, q, o + 2 * t)) = (uint16_t)(w >> (16 * t));
+    if ((i & 3) == 0) scales[mx_scale_index<true>(r, q, nblocks)] = (uint8_t)sc;
+  } else {
+    uint16_t* dst = reinterpret_cast<uint16_t*>(codes + i * 6);
+    dst[0] = (uint16_t)w;
+    dst[1] = (uint16_t)(w >> 16);
+    dst[2] = (uint16_t)(w >> 32);
+    if ((i & 3) == 0) scales[i >> 2] = (uint8_t)sc;
+  }
 }
 
 hipError_t mxfp6_quantize(const uint16_t* x, int64_t rows, int64_t cols, uint8_t* codes, uint8_t* scales,
-                          hipStream_t s) {
+                          hipStream_t s, bool gemm_order) {
   const int64_t nchunks = rows * (cols / 32) * 4;
   if (nchunks <= 0) return hipSuccess;
   const int64_t grid = (nchunks + 255) / 256;
   if (grid > INT32_MAX) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(mxfp6_quant_kernel, dim3((unsigned)grid), dim3(256), 0, s, x, nchunks, codes, scales);
+  if (gemm_order && (rows % 32 || cols % 256)) return hipErrorInvalidValue;
+  if (gemm_order)
+    hipLaunchKernelGGL(mxfp6_quant_kernel<true>, dim3((unsigned)grid), dim3(256), 0, s, x, nchunks, cols / 32, codes,
+                       scales);
+  else
+    hipLaunchKernelGGL(mxfp6_quant_kernel<false>, dim3((unsigned)grid), dim3(256), 0, s, x, nchunks, cols / 32, codes,
+                       scales);
   return hipGetLastError();
 }
 
@@ -264,183 +284,19 @@ hipError_t mxfp4_quantize(const uint16_t* x, int64_t rows, int64_t cols, uint8_t
 }
 
 // ---------------------------------------------------------------- GEMM
-// C [M, N] (bf16, row stride ldc) = A B^T, A [M, K] and B [N, K] MXFP4 (codes
-// K/2 bytes per row, scales K/32 bytes per row).  128 x 128 tiles, 4 waves of
-// 64 x 64 (2 x 2 MFMA blocks of 32 x 32); K slabs of 256 elements (128 code
-// bytes and 8 scale bytes per row) through two LDS buffers, the next slab
-// loaded into registers while the current one is multiplied.  M, N % 128 == 0,
-// K % 256 == 0.
+// The MXFP4 products, and the MXFP6 ones on GEMM-order operands, run on the
+// bf16 GEMM's pipeline (gemm.hip).  Here: the MXFP6 GEMM on plain-order
+// operands, C [M, N] (bf16, row stride ldc) = A B^T, A [M, K] and B [N, K]
+// (codes K*3/4 bytes per row, scales K/32 bytes per row).  128 x 128 tiles, 4
+// waves of 64 x 64 (2 x 2 MFMA blocks of 32 x 32); K slabs of 128 elements (96
+// code bytes and 4 scale bytes per row, 58 KB of LDS for both buffers, two
+// workgroups per CU) through two LDS buffers, the next slab loaded into
+// registers while the current one is multiplied; a lane's fragment is 24 bytes
+// (32 elements of 6 bits), read as three 8-byte words.  LDS rows are padded to
+// 112 bytes: the 16 rows a half-wave reads then start 28 banks apart (mod 64),
+// on 16 distinct pairs of banks.  M, N % 128 == 0, K % 128 == 0.
 namespace {
-constexpr int MT = 128, KSLAB = 256, ROWB = KSLAB / 2;  // 128 code bytes per row and slab
-constexpr int TILEB = MT * ROWB;                         // 16 KB of codes per operand and slab
-constexpr int SCB = MT * (KSLAB / 32);                   // 1 KB of scales per operand and slab
-constexpr int BUF = 2 * TILEB + 2 * SCB;
-
-// 16-byte chunk c of row r sits at chunk c ^ s(r), s(r) = 2*((r >> 1) & 3) +
-// ((r >> 3) & 1).  Rows are 128 bytes (half the 64 banks, by row parity), so
-// the 16 rows of a quarter-wave at one chunk, and the 8 rows of the lower and
-// upper half-waves at chunks c and c ^ 1 (the two K halves of a fragment), each
-// fall on distinct groups of four banks.
-__device__ __forceinline__ int chunk_off(int r, int c) {
-  return r * ROWB + ((c ^ ((((r >> 1) & 3) << 1) | ((r >> 3) & 1))) << 4);
-}
-}  // namespace
-
-template <int EPI>
-__global__ __launch_bounds__(256, 2) void mxfp4_gemm_kernel(Mxfp4GemmArgs g) {
-  __shared__ __attribute__((aligned(1024))) char lds_[2 * BUF];
-  const int ntn = g.N / MT;
-  const int ntiles = (g.M / MT) * ntn;
-  const int u = xcd_index(blockIdx.x, ntiles);
-  const int tm = u / ntn, tn = u % ntn;
-  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
-  const int64_t kb = g.K / 2, ks = g.K / 32;  // code and scale bytes per row
-  const uint8_t* a0 = g.a + (int64_t)tm * MT * kb;
-  const uint8_t* b0 = g.b + (int64_t)tn * MT * kb;
-  const uint8_t* sa0 = g.sa + (int64_t)tm * MT * ks;
-  const uint8_t* sb0 = g.sb + (int64_t)tn * MT * ks;
-  const int nslab = g.K / KSLAB;
-
-  // staging registers: 4 code chunks of A and of B per thread, 8 scale bytes
-  // of one row of A (threads 0..127) or of B (threads 128..255)
-  u32x4 ra[4], rb[4];
-  u32x2 rsc;
-  auto load = [&](int s) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int idx = t + 256 * i, r = idx >> 3, c = idx & 7;
-      ra[i] = *reinterpret_cast<const u32x4*>(a0 + r * kb + s * ROWB + c * 16);
-      rb[i] = *reinterpret_cast<const u32x4*>(b0 + r * kb + s * ROWB + c * 16);
-    }
-    const int r = t & 127;
-    const uint8_t* sp = (t < 128 ? sa0 : sb0) + r * ks + s * 8;
-    rsc = *reinterpret_cast<const u32x2*>(sp);
-  };
-  auto store = [&](char* buf) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int idx = t + 256 * i, r = idx >> 3, c = idx & 7;
-      *reinterpret_cast<u32x4*>(buf + chunk_off(r, c)) = ra[i];
-      *reinterpret_cast<u32x4*>(buf + TILEB + chunk_off(r, c)) = rb[i];
-    }
-    *reinterpret_cast<u32x2*>(buf + 2 * TILEB + (t < 128 ? 0 : SCB) + (t & 127) * 8) = rsc;
-  };
-
-  f32x16 acc[2][2];
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j) acc[i][j] = f32x16{};
-
-  typedef int i32x8 __attribute__((ext_vector_type(8)));
-  load(0);
-  store(lds_);
-  __syncthreads();
-  for (int s = 0; s < nslab; ++s) {
-    const bool more = s + 1 < nslab;
-    if (more) load(s + 1);
-    const char* buf = lds_ + (s & 1) * BUF;
-    // the 8 scale bytes of each of the lane's four rows, read once per slab and
-    // shifted by the lane's K half: k step kk takes byte 2*(kk & 1) of word kk >> 1
-    u32x2 sva[2], svb[2];
-    {
-      const int sh = 8 * (lane >> 5);
-#pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        const u32x2 w = *reinterpret_cast<const u32x2*>(buf + 2 * TILEB + (wm * 64 + i * 32 + (lane & 31)) * 8);
-        sva[i] = u32x2{w[0] >> sh, w[1] >> sh};
-        const u32x2 x = *reinterpret_cast<const u32x2*>(buf + 2 * TILEB + SCB + (wn * 64 + i * 32 + (lane & 31)) * 8);
-        svb[i] = u32x2{x[0] >> sh, x[1] >> sh};
-      }
-    }
-#pragma unroll
-    for (int kk = 0; kk < KSLAB / 64; ++kk) {
-      const int c = kk * 2 + (lane >> 5);  // this lane's 16-byte chunk (32 elements) of the k step
-      i32x8 fa[2], fb[2];
-      int sca[2], scb[2];
-#pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        const int r = wm * 64 + i * 32 + (lane & 31);
-        const u32x4 v = *reinterpret_cast<const u32x4*>(buf + chunk_off(r, c));
-        fa[i] = i32x8{(int)v[0], (int)v[1], (int)v[2], (int)v[3], 0, 0, 0, 0};
-        sca[i] = (int)((sva[i][kk >> 1] >> (16 * (kk & 1))) & 0xffu);
-      }
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int r = wn * 64 + j * 32 + (lane & 31);
-        const u32x4 v = *reinterpret_cast<const u32x4*>(buf + TILEB + chunk_off(r, c));
-        fb[j] = i32x8{(int)v[0], (int)v[1], (int)v[2], (int)v[3], 0, 0, 0, 0};
-        scb[j] = (int)((svb[j][kk >> 1] >> (16 * (kk & 1))) & 0xffu);
-      }
-      // B first: a lane then owns one output row and 4 consecutive columns per register group
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fb[j], fa[i], acc[i][j], 4, 4, 0, scb[j], 0,
-                                                                      sca[i]);
-    }
-    if (more) store(lds_ + ((s + 1) & 1) * BUF);
-    __syncthreads();
-  }
-
-  // lane: row m = lane % 32 of block i, columns 8*(r/4) + 4*(lane/32) + r%4 of
-  // block j; the epilogue works on those 4 consecutive columns at a time
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int64_t m = (int64_t)tm * MT + wm * 64 + i * 32 + (lane & 31);
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int n = tn * MT + wn * 64 + j * 32 + 8 * q + 4 * (lane >> 5);
-        float v[4] = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
-        const int64_t o = m * g.ldc + n;
-        if constexpr (EPI == EPI_F32 || EPI == EPI_F32_ACC) {
-          f32x4 r = {v[0], v[1], v[2], v[3]};
-          if constexpr (EPI == EPI_F32_ACC) r += *reinterpret_cast<const f32x4*>(g.c32 + o);
-          *reinterpret_cast<f32x4*>(g.c32 + o) = r;
-          continue;
-        }
-        if constexpr (EPI == EPI_BF16_BIAS || EPI == EPI_BIAS_GELU) {
-          if (g.bias) {
-            const u32x2 b = *reinterpret_cast<const u32x2*>(g.bias + n);
-            v[0] += bf16_lo(b[0]);
-            v[1] += bf16_hi(b[0]);
-            v[2] += bf16_lo(b[1]);
-            v[3] += bf16_hi(b[1]);
-          }
-        }
-        if constexpr (EPI == EPI_BIAS_GELU) {  // C = GeLU'(z), C2 = GeLU(z)
-          float ge[4];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            float cdf, pdf;
-            normal_cdf_pdf(v[e], cdf, pdf);
-            ge[e] = v[e] * cdf;
-            v[e] = cdf + v[e] * pdf;
-          }
-          *reinterpret_cast<u32x2*>(g.c2 + o) = u32x2{pack_bf16x2(ge[0], ge[1]), pack_bf16x2(ge[2], ge[3])};
-        }
-        if constexpr (EPI == EPI_DGELU) {  // aux holds GeLU'(z)
-          const u32x2 z = *reinterpret_cast<const u32x2*>(g.aux + o);
-          v[0] *= bf16_lo(z[0]);
-          v[1] *= bf16_hi(z[0]);
-          v[2] *= bf16_lo(z[1]);
-          v[3] *= bf16_hi(z[1]);
-        }
-        *reinterpret_cast<u32x2*>(g.c + o) = u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
-      }
-  }
-}
-
-// MXFP6 GEMM: the same tiling with 128-deep K slabs (96 code bytes and 4
-// scale bytes per row, 58 KB of LDS for both buffers, two workgroups per CU);
-// a lane's fragment is 24 bytes (32 elements of 6 bits), read as three 8-byte
-// words.  LDS rows are padded to 112 bytes: the 16 rows a half-wave reads
-// then start 28 banks apart (mod 64), on 16 distinct pairs of banks.
-namespace {
+constexpr int MT = 128;
 constexpr int KS6 = 128, ROWB6 = KS6 * 6 / 8;  // 96 code bytes per row and slab
 constexpr int LROW6 = ROWB6 + 16;               // LDS row stride
 constexpr int TILEB6 = MT * LROW6;              // 14 KB per operand and slab
@@ -553,24 +409,6 @@ hipError_t mxfp6_gemm(const Mxfp4GemmArgs& g, hipStream_t s) {
   const int64_t tiles = (int64_t)(g.M / MT) * (g.N / MT);
   if (tiles > INT32_MAX) return hipErrorInvalidValue;
   hipLaunchKernelGGL(mxfp6_gemm_kernel, dim3((unsigned)tiles), dim3(256), 0, s, g);
-  return hipGetLastError();
-}
-
-hipError_t mxfp4_gemm(const Mxfp4GemmArgs& g, hipStream_t s) {
-  if (g.M <= 0 || g.N <= 0 || g.K <= 0) return hipSuccess;
-  if (g.M % MT || g.N % MT || g.K % KSLAB) return hipErrorInvalidValue;
-  const int64_t tiles = (int64_t)(g.M / MT) * (g.N / MT);
-  if (tiles > INT32_MAX) return hipErrorInvalidValue;
-  const dim3 grid((unsigned)tiles), block(256);
-  switch (g.epi) {
-    case EPI_BF16: hipLaunchKernelGGL(mxfp4_gemm_kernel<EPI_BF16>, grid, block, 0, s, g); break;
-    case EPI_BF16_BIAS: hipLaunchKernelGGL(mxfp4_gemm_kernel<EPI_BF16_BIAS>, grid, block, 0, s, g); break;
-    case EPI_BIAS_GELU: hipLaunchKernelGGL(mxfp4_gemm_kernel<EPI_BIAS_GELU>, grid, block, 0, s, g); break;
-    case EPI_DGELU: hipLaunchKernelGGL(mxfp4_gemm_kernel<EPI_DGELU>, grid, block, 0, s, g); break;
-    case EPI_F32: hipLaunchKernelGGL(mxfp4_gemm_kernel<EPI_F32>, grid, block, 0, s, g); break;
-    case EPI_F32_ACC: hipLaunchKernelGGL(mxfp4_gemm_kernel<EPI_F32_ACC>, grid, block, 0, s, g); break;
-    default: return hipErrorInvalidValue;
-  }
   return hipGetLastError();
 }
 

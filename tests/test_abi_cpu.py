@@ -305,6 +305,32 @@ def test_mxfp6_validation_before_any_launch(mtl):
     assert lib.mtl_mxfp6_gemm(128, 128, 128, P, P, P + 4, P, P, 128, None) == mtl.MTL_E_ALIGN
 
 
+def test_mx_ordered_validation_before_any_launch(mtl):
+    lib = mtl.lib()
+    P = 1 << 20
+    E4, E6, PL, GO = mtl.MTL_MX_E2M1, mtl.MTL_MX_E2M3, mtl.MTL_MX_ORDER_PLAIN, mtl.MTL_MX_ORDER_GEMM
+    q = lambda e, x, r, c, o: lib.mtl_mx_quantize_ordered(e, x, r, c, P, P, o, None)
+    assert q(E4, None, 32, 256, GO) == mtl.MTL_E_NULL
+    assert q(2, P, 32, 256, GO) == mtl.MTL_E_UNSUPPORTED  # element format
+    assert q(E6, P, 32, 256, 2) == mtl.MTL_E_UNSUPPORTED  # order
+    assert q(E4, P, 48, 256, GO) == mtl.MTL_E_SHAPE  # rows % 32 in GEMM order
+    assert q(E6, P, 32, 384, GO) == mtl.MTL_E_SHAPE  # cols % 256 in GEMM order
+    assert q(E4, P, 4, 48, PL) == mtl.MTL_E_SHAPE  # cols % 32
+    assert q(E4, P + 4, 32, 256, GO) == mtl.MTL_E_ALIGN
+    g = lambda e, M, N, K, o, c=P, ldc=None: lib.mtl_mx_gemm_ordered(e, M, N, K, P, P, P, P, c, N if ldc is None
+                                                                     else ldc, o, None)
+    assert g(E4, 64, 64, 256, GO, c=None) == mtl.MTL_E_NULL
+    assert g(3, 64, 64, 256, GO) == mtl.MTL_E_UNSUPPORTED
+    assert g(E4, 64, 64, 256, 5) == mtl.MTL_E_UNSUPPORTED
+    assert g(E4, 48, 64, 256, GO) == mtl.MTL_E_SHAPE  # M % 32
+    assert g(E6, 64, 80, 256, GO) == mtl.MTL_E_SHAPE  # N % 32
+    assert g(E6, 64, 64, 384, GO) == mtl.MTL_E_SHAPE  # K % 256
+    assert g(E4, 64, 128, 256, PL) == mtl.MTL_E_SHAPE  # plain: M % 128
+    assert g(E6, 128, 128, 192, PL) == mtl.MTL_E_SHAPE  # plain MXFP6: K % 128
+    assert g(E4, 64, 64, 256, GO, ldc=32) == mtl.MTL_E_SHAPE  # ldc < N
+    assert g(E4, 64, 64, 256, GO, c=P + 8) == mtl.MTL_E_ALIGN
+
+
 def test_launch_timing_host_side(mtl):
     """The launch-timing calls on a host without a GPU: start reports the
     missing device, stop and record validate their arguments."""
