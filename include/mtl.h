@@ -78,7 +78,15 @@ enum {
    * buffer to the rank's four calls of a step, leaves that region alone between
    * a forward call and its backward, and passes the backward the same x, h and
    * weights (and saved o, a) as the forward -- as a training step does. */
-  MTL_F_FP8_KEEP_CODES = 4
+  MTL_F_FP8_KEEP_CODES = 4,
+  /* fp8, with MTL_F_FP8_KEEP_CODES: the forward calls do not quantise the
+   * weights; every call takes the four weights' codes and scale records from
+   * the kept region, where an earlier forward call with the same scratch (and
+   * without this flag) wrote them.  For the micro-batches after the first of a
+   * step with gradient accumulation, whose weights have not changed since: the
+   * caller guarantees that (the bf16 weights passed are then not read by the
+   * forward calls, nor by the backward calls, which read the kept codes). */
+  MTL_F_FP8_REUSE_WEIGHTS = 8
 };
 
 /* Layer configuration: the pretraining flags --hidden-size, --num-attention-heads,

@@ -303,6 +303,7 @@ struct MlpFwdScratch {
 inline bool is_fp8(const mtl_layer_cfg* c) { return c->precision == MTL_PREC_FP8_HYBRID; }
 inline bool is_mx4(const mtl_layer_cfg* c) { return c->precision == MTL_PREC_MXFP4; }
 inline bool keeps_codes(const mtl_layer_cfg* c) { return is_fp8(c) && (c->flags & MTL_F_FP8_KEEP_CODES); }
+inline bool reuses_weights(const mtl_layer_cfg* c) { return keeps_codes(c) && (c->flags & MTL_F_FP8_REUSE_WEIGHTS); }
 
 // With MTL_F_FP8_KEEP_CODES: the transposed E4M3 codes (and scale records) of
 // x, o, h and a, and the four weights' E4M3 codes in both orientations, written
@@ -496,8 +497,10 @@ mtl_status mtl_validate(const mtl_layer_cfg* c) {
   if (c->precision == MTL_PREC_FP8_HYBRID &&
       (((int64_t)c->seq * c->micro_batch) % 16 != 0 || (c->ffn / c->tp) % 16 != 0))
     return MTL_E_SHAPE;
-  if (c->flags & ~(MTL_F_RESIDUAL | MTL_F_WGRAD_ACCUM | MTL_F_FP8_KEEP_CODES)) return MTL_E_UNSUPPORTED;
+  if (c->flags & ~(MTL_F_RESIDUAL | MTL_F_WGRAD_ACCUM | MTL_F_FP8_KEEP_CODES | MTL_F_FP8_REUSE_WEIGHTS))
+    return MTL_E_UNSUPPORTED;
   if ((c->flags & MTL_F_FP8_KEEP_CODES) && c->precision != MTL_PREC_FP8_HYBRID) return MTL_E_UNSUPPORTED;
+  if ((c->flags & MTL_F_FP8_REUSE_WEIGHTS) && !(c->flags & MTL_F_FP8_KEEP_CODES)) return MTL_E_UNSUPPORTED;
   return MTL_OK;
 }
 
@@ -541,7 +544,8 @@ mtl_status mtl_attn_fwd(const mtl_layer_cfg* c, const void* x, const void* w_qkv
     MTL_TRY(mxqt(w_qkv, ws.m_wqkv_t, s));
     MTL_TRY(mxgemm("qkv_fwd", ws.m_x, ws.m_wqkv_t, EPI_BF16_BIAS, qkv, s, b_qkv));
   } else if (is_fp8(c)) {
-    MTL_TRY(quantize({{x, &ws.x}, {w_qkv, &ws.wqkv_t}, {w_o, &ws.wo_t}}, ws.amax_ws, s));
+    if (reuses_weights(c)) MTL_TRY(quantize({{x, &ws.x}}, ws.amax_ws, s));
+    else MTL_TRY(quantize({{x, &ws.x}, {w_qkv, &ws.wqkv_t}, {w_o, &ws.wo_t}}, ws.amax_ws, s));
     MTL_TRY(gemm8("qkv_fwd", ws.x, ws.x.q, ws.wqkv_t, ws.wqkv_t.qt, d.S, d.qkv_l, d.h, qkv, d.qkv_l, EPI_BF16_BIAS,
                   s, b_qkv));
   } else {
@@ -929,7 +933,8 @@ mtl_status mtl_mlp_fwd(const mtl_layer_cfg* c, const void* h, const void* w1, co
 
   if (is_fp8(c)) {
     // z = h . w1 + b1: gz = GeLU'(z), a = GeLU(z); partial = a . w2 (a re-quantised from bf16)
-    MTL_TRY(quantize({{h, &ws.h}, {w1, &ws.w1_t}, {w2, &ws.w2_t}}, ws.amax_ws, s));
+    if (reuses_weights(c)) MTL_TRY(quantize({{h, &ws.h}}, ws.amax_ws, s));
+    else MTL_TRY(quantize({{h, &ws.h}, {w1, &ws.w1_t}, {w2, &ws.w2_t}}, ws.amax_ws, s));
     // the fc1 epilogue leaves a's amax partials, so a's quantisation reads it once
     int na = 0;
     const AmaxOut am = amax_fits(d.S, d.f_l) ? AmaxOut{ws.a_part, 1, &na} : AmaxOut{};

@@ -408,6 +408,14 @@ def test_fp8_keep_codes_flag(mtl):
     assert mtl.mtl_workspace_bytes(kept) == mtl.mtl_workspace_bytes(base) + extra
     bad = mtl.make_cfg(768, 12, 3072, 512, 1, 2, 0, mtl.MTL_PREC_BF16, mtl.MTL_F_FP8_KEEP_CODES)
     assert mtl.mtl_validate(bad) == mtl.MTL_E_UNSUPPORTED
+    # reusing the weights' kept codes needs the kept region, and adds no scratch
+    reuse = mtl.make_cfg(768, 12, 3072, 512, 1, 2, 0, mtl.MTL_PREC_FP8_HYBRID,
+                         mtl.MTL_F_FP8_KEEP_CODES | mtl.MTL_F_FP8_REUSE_WEIGHTS)
+    assert mtl.mtl_validate(reuse) == mtl.MTL_OK
+    assert mtl.mtl_workspace_bytes(reuse) == mtl.mtl_workspace_bytes(kept)
+    for prec, flags in ((mtl.MTL_PREC_FP8_HYBRID, mtl.MTL_F_FP8_REUSE_WEIGHTS),
+                        (mtl.MTL_PREC_BF16, mtl.MTL_F_FP8_KEEP_CODES | mtl.MTL_F_FP8_REUSE_WEIGHTS)):
+        assert mtl.mtl_validate(mtl.make_cfg(768, 12, 3072, 512, 1, 2, 0, prec, flags)) == mtl.MTL_E_UNSUPPORTED
 
 
 def test_mfma_ceiling_argument_checks(mtl):

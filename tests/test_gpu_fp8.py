@@ -311,6 +311,46 @@ def test_fp8_kept_codes_are_bit_identical(mtl, case):
 
 @pytest.mark.gpu
 @pytest.mark.parametrize("case", ["gpt2-small-tp2", "d128-mb2-tp2"])
+def test_fp8_reused_weight_codes(mtl, case):
+    """MTL_F_FP8_REUSE_WEIGHTS: a rank step after a step without the flag gives
+    the first step's outputs bit for bit, and it reads no bf16 weight: with the
+    weights overwritten (a second micro-batch may not do that, but the call
+    must not notice) the outputs are still those of the first step."""
+    import torch
+    from megatron_tensor_transformer_layer_amd.layer import RankState, bf16_dev
+    shape, _ = FP8_CASES[case]
+    t, r = shape.tp, shape.tp - 1
+    print(f"fp8 reused weight codes {case} {shape}", flush=True)
+    inp = synth.layer_inputs(shape, tp=t, rank=r)
+    keep = mtl.MTL_F_FP8_KEEP_CODES
+    st = RankState(shape, t, r, inp, flags=keep, precision=mtl.MTL_PREC_FP8_HYBRID)
+    x, dy = bf16_dev(inp["x"]), bf16_dev(inp["dy"])
+    h, dh = bf16_dev(synth.layer_tensor(shape, "h")), bf16_dev(synth.layer_tensor(shape, "dh"))
+    names = ("qkv", "o", "lse", "gz", "a", "p_attn", "p_mlp", "p_dh", "p_dx", "dw_qkv", "db_qkv", "dw_o", "db_o",
+             "dw1", "db1", "dw2", "db2")
+
+    def step():
+        st.attn_fwd(x)
+        st.mlp_fwd(h)
+        st.mlp_bwd(dy, h)
+        st.attn_bwd(dh, x)
+        torch.cuda.synchronize()
+        return {k: getattr(st, k).clone() for k in names}
+
+    first = step()
+    st.cfg.flags = keep | mtl.MTL_F_FP8_REUSE_WEIGHTS
+    again = step()
+    bad = [k for k in names if not torch.equal(first[k], again[k])]
+    assert not bad, f"reused codes differ: {bad}"
+    for k in ("w_qkv", "w_o", "w1", "w2"):
+        st.w[k].mul_(-3.0)
+    ignored = step()
+    bad = [k for k in names if not torch.equal(first[k], ignored[k])]
+    assert not bad, f"bf16 weights were read: {bad}"
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("case", ["gpt2-small-tp2", "d128-mb2-tp2"])
 def test_fp8_producer_amax_equals_the_amax_pass(mtl, case):
     """The amax of O (from the attention kernel) and of A (from the fc1
     epilogue), which the fp8 forward takes from the kernels that produced them,
