@@ -876,9 +876,9 @@ def dense_main(args):
     inp = synth.layer_inputs(shape, tp=t, rank=r)
     fp8, mx = args.precision == "fp8", args.precision == "mxfp4"
     from megatron_tensor_transformer_layer_amd import MTL_PREC_MXFP4
-    from megatron_tensor_transformer_layer_amd import MTL_F_FP8_KEEP_CODES
-    # fp8: the forward's transposed codes of x, o, h, a are kept for the backward
-    st = RankState(shape, t, r, inp, flags=MTL_F_FP8_KEEP_CODES if fp8 else 0,
+    from megatron_tensor_transformer_layer_amd import MTL_F_KEEP_CODES
+    # fp8 / MXFP4: the forward's codes of the operands the backward needs are kept for it
+    st = RankState(shape, t, r, inp, flags=MTL_F_KEEP_CODES if (fp8 or mx) else 0,
                    precision={"bf16": MTL_PREC_BF16, "fp8": MTL_PREC_FP8_HYBRID,
                               "mxfp4": MTL_PREC_MXFP4}[args.precision])
     D = st.D
@@ -975,21 +975,21 @@ def dense_main(args):
         out["quantize_us_per_step"] = round(q["ms"] * 1e3, 1)
         g8 = kinds.get("gemm")
         out["gemm_frac_of_bf16_peak"] = round(g8["flop"] / (g8["ms"] / 1e3) / 1e12 / PEAK_BF16_TFLOPS, 4)
-    if fp8:
+    if fp8 or mx:
         # The same step for the micro-batches after the first of a step with
         # gradient accumulation: the weights' codes stay those the first
-        # micro-batch's forward kept (MTL_F_FP8_REUSE_WEIGHTS).  value and
+        # micro-batch's forward kept (MTL_F_REUSE_WEIGHTS).  value and
         # ms_per_step above quantise the weights in every step.
-        from megatron_tensor_transformer_layer_amd import MTL_F_FP8_REUSE_WEIGHTS
-        st.cfg.flags = MTL_F_FP8_KEEP_CODES | MTL_F_FP8_REUSE_WEIGHTS
+        from megatron_tensor_transformer_layer_amd import MTL_F_REUSE_WEIGHTS
+        st.cfg.flags = MTL_F_KEEP_CODES | MTL_F_REUSE_WEIGHTS
         ms_r = timed_steps(step, args.steps, args.warmup)
         _, kinds_r = prof_window(step, 5)
-        st.cfg.flags = MTL_F_FP8_KEEP_CODES
+        st.cfg.flags = MTL_F_KEEP_CODES
         out["reused_weight_codes"] = {
             "ms_per_step": round(ms_r, 4), "value": round(fl["total"] / (ms_r / 1e3) / 1e12, 2),
             "quantize_us_per_step": round(kinds_r.get("quantize", dict(ms=0.0))["ms"] * 1e3, 1),
             "note": "micro-batches after the first of a gradient-accumulation step: the forward takes the "
-                    "weights' E4M3 codes kept by the first micro-batch's forward (MTL_F_FP8_REUSE_WEIGHTS)"}
+                    "weights' codes kept by the first micro-batch's forward (MTL_F_REUSE_WEIGHTS)"}
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(shape, r, min(args.cpu_sample_seq, shape.seq), args.precision)
     print(json.dumps(out), flush=True)

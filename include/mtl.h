@@ -68,25 +68,32 @@ enum { MTL_FP8_E4M3 = 0, MTL_FP8_E5M2 = 1 };
 enum {
   MTL_F_RESIDUAL = 1,   /* mtl_reduce callers add residuals; recorded for validation only */
   MTL_F_WGRAD_ACCUM = 2, /* weight/bias gradients are accumulated (+=) instead of written */
-  /* fp8 only: the forward calls also write the transposed E4M3 codes and scale
-   * records of x, o (mtl_attn_fwd) and h, a (mtl_mlp_fwd), and the E4M3 codes
-   * of their weights in both orientations (w_qkv, w_o; w1, w2), into a region
-   * at the start of the scratch (mtl_workspace_bytes counts it; each call's own
-   * scratch follows it), and the backward calls read them there instead of
-   * quantising those tensors again (bit-identical results: the same tensor,
-   * format and amax give the same codes).  The caller passes the same scratch
-   * buffer to the rank's four calls of a step, leaves that region alone between
-   * a forward call and its backward, and passes the backward the same x, h and
-   * weights (and saved o, a) as the forward -- as a training step does. */
-  MTL_F_FP8_KEEP_CODES = 4,
-  /* fp8, with MTL_F_FP8_KEEP_CODES: the forward calls do not quantise the
-   * weights; every call takes the four weights' codes and scale records from
-   * the kept region, where an earlier forward call with the same scratch (and
+  /* fp8 or MXFP4: the forward calls also write the codes the backward calls
+   * need of their operands into a region at the start of the scratch
+   * (mtl_workspace_bytes counts it; each call's own scratch follows it), and
+   * the backward calls read them there instead of quantising those tensors
+   * again (bit-identical results: the same tensor and recipe give the same
+   * codes).  fp8: the transposed E4M3 codes and scale records of x, o
+   * (mtl_attn_fwd) and h, a (mtl_mlp_fwd), and the E4M3 codes of their weights
+   * in both orientations (w_qkv, w_o; w1, w2).  MXFP4: the codes of x, o, h and
+   * a blocked down their token columns and the weights' codes blocked both ways,
+   * each tensor quantised both ways from one read.  The caller passes the same
+   * scratch buffer to the rank's four calls of a step, leaves that region alone
+   * between a forward call and its backward, and passes the backward the same
+   * x, h and weights (and saved o, a) as the forward -- as a training step
+   * does. */
+  MTL_F_KEEP_CODES = 4,
+  /* With MTL_F_KEEP_CODES: the forward calls do not quantise the weights; every
+   * call takes the four weights' codes (and, in fp8, scale records) from the
+   * kept region, where an earlier forward call with the same scratch (and
    * without this flag) wrote them.  For the micro-batches after the first of a
    * step with gradient accumulation, whose weights have not changed since: the
    * caller guarantees that (the bf16 weights passed are then not read by the
    * forward calls, nor by the backward calls, which read the kept codes). */
-  MTL_F_FP8_REUSE_WEIGHTS = 8
+  MTL_F_REUSE_WEIGHTS = 8,
+  /* the names of these two flags when only fp8 had them */
+  MTL_F_FP8_KEEP_CODES = MTL_F_KEEP_CODES,
+  MTL_F_FP8_REUSE_WEIGHTS = MTL_F_REUSE_WEIGHTS
 };
 
 /* Layer configuration: the pretraining flags --hidden-size, --num-attention-heads,
@@ -332,7 +339,8 @@ mtl_status mtl_mlp_bwd(const mtl_layer_cfg* cfg, const void* dy, const void* h, 
  * a caller's buffer.  It allocates nothing and calls no allocating routine.
  * Every GPU the library runs on holds one such array until the process ends;
  * the first call on a device (with that device current) looks up its address.
- * Status: mtl_validate's; MTL_E_WORKSPACE, before any HIP call, when the
+ * Status: mtl_validate's; MTL_E_UNSUPPORTED with MTL_F_KEEP_CODES (the kept
+ * codes are in the scratch the forward calls were given); MTL_E_WORKSPACE, before any HIP call, when the
  * configuration needs more scratch than the array holds (in bf16 the MLP
  * backward needs 2*S*(f/t) bytes for dz plus 4*ceil(S/64)*(f/t + h) for the
  * column sums: S = 4096 with f/t = 4096 and h = 8192 takes 35 MiB; the fp8

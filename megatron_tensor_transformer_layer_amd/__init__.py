@@ -24,7 +24,8 @@ MTL_MX_ORDER_PLAIN, MTL_MX_ORDER_GEMM = 0, 1
 MTL_FP8_E4M3, MTL_FP8_E5M2 = 0, 1
 MTL_FP8_AMAX_SCRATCH = 4096
 MTL_CP_MAX = 64
-MTL_F_RESIDUAL, MTL_F_WGRAD_ACCUM, MTL_F_FP8_KEEP_CODES, MTL_F_FP8_REUSE_WEIGHTS = 1, 2, 4, 8
+MTL_F_RESIDUAL, MTL_F_WGRAD_ACCUM, MTL_F_KEEP_CODES, MTL_F_REUSE_WEIGHTS = 1, 2, 4, 8
+MTL_F_FP8_KEEP_CODES, MTL_F_FP8_REUSE_WEIGHTS = MTL_F_KEEP_CODES, MTL_F_REUSE_WEIGHTS  # earlier names
 MTL_PROF_MAX = 2048
 MTL_NOALLOC_SCRATCH_BYTES = 48 << 20
 MTL_CEILING_DATA_BYTES = 1 << 20

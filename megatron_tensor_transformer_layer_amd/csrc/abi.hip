@@ -302,30 +302,54 @@ struct MlpFwdScratch {
 
 inline bool is_fp8(const mtl_layer_cfg* c) { return c->precision == MTL_PREC_FP8_HYBRID; }
 inline bool is_mx4(const mtl_layer_cfg* c) { return c->precision == MTL_PREC_MXFP4; }
-inline bool keeps_codes(const mtl_layer_cfg* c) { return is_fp8(c) && (c->flags & MTL_F_FP8_KEEP_CODES); }
-inline bool reuses_weights(const mtl_layer_cfg* c) { return keeps_codes(c) && (c->flags & MTL_F_FP8_REUSE_WEIGHTS); }
+inline bool keeps_codes(const mtl_layer_cfg* c) { return is_fp8(c) && (c->flags & MTL_F_KEEP_CODES); }
+inline bool keeps_mx(const mtl_layer_cfg* c) { return is_mx4(c) && (c->flags & MTL_F_KEEP_CODES); }
+inline bool reuses_weights(const mtl_layer_cfg* c) {
+  return (keeps_codes(c) || keeps_mx(c)) && (c->flags & MTL_F_REUSE_WEIGHTS);
+}
 
-// With MTL_F_FP8_KEEP_CODES: the transposed E4M3 codes (and scale records) of
-// x, o, h and a, and the four weights' E4M3 codes in both orientations, written
-// by the forward calls at the start of the scratch and read there by the
-// backward calls, which then do not quantise these tensors again (the same
-// tensor, format and amax give the same codes).
+// With MTL_F_KEEP_CODES, written by the forward calls at the start of the
+// scratch and read there by the backward calls, which then do not quantise
+// these tensors again (the same tensor and recipe give the same codes):
+//  fp8: the transposed E4M3 codes (and scale records) of x, o, h and a, and the
+//  four weights' E4M3 codes in both orientations;
+//  MXFP4: the column-blocked codes of x, o, h and a (the wgrad operands) and
+//  the four weights' codes blocked both ways (the forward's and the dgrad's
+//  operands), all from one read of each tensor.
 struct Kept {
   Q8 x_t, o_t, h_t, a_t;
   Q8 wqkv, wo, w1, w2;
+  MX4 m_x_t, m_o_t, m_h_t, m_a_t;
+  MX4 m_wqkv, m_wqkv_t, m_wo, m_wo_t, m_w1, m_w1_t, m_w2, m_w2_t;
 };
 size_t kept_scratch(const mtl_layer_cfg* c, const Dims& d, Kept* k, char* base) {
-  if (!keeps_codes(c)) return 0;
   Bump b{base};
   Kept t{};
-  t.x_t = q8(b, d.S, d.h, E4M3, false, true);
-  t.o_t = q8(b, d.S, d.o_l, E4M3, false, true);
-  t.h_t = q8(b, d.S, d.h, E4M3, false, true);
-  t.a_t = q8(b, d.S, d.f_l, E4M3, false, true);
-  t.wqkv = q8(b, d.h, d.qkv_l, E4M3, true, true);
-  t.wo = q8(b, d.o_l, d.h, E4M3, true, true);
-  t.w1 = q8(b, d.h, d.f_l, E4M3, true, true);
-  t.w2 = q8(b, d.f_l, d.h, E4M3, true, true);
+  if (keeps_codes(c)) {
+    t.x_t = q8(b, d.S, d.h, E4M3, false, true);
+    t.o_t = q8(b, d.S, d.o_l, E4M3, false, true);
+    t.h_t = q8(b, d.S, d.h, E4M3, false, true);
+    t.a_t = q8(b, d.S, d.f_l, E4M3, false, true);
+    t.wqkv = q8(b, d.h, d.qkv_l, E4M3, true, true);
+    t.wo = q8(b, d.o_l, d.h, E4M3, true, true);
+    t.w1 = q8(b, d.h, d.f_l, E4M3, true, true);
+    t.w2 = q8(b, d.f_l, d.h, E4M3, true, true);
+  } else if (keeps_mx(c)) {
+    t.m_x_t = mx4(b, d.h, d.S);
+    t.m_o_t = mx4(b, d.o_l, d.S);
+    t.m_h_t = mx4(b, d.h, d.S);
+    t.m_a_t = mx4(b, d.f_l, d.S);
+    t.m_wqkv = mx4(b, d.h, d.qkv_l);
+    t.m_wqkv_t = mx4(b, d.qkv_l, d.h);
+    t.m_wo = mx4(b, d.o_l, d.h);
+    t.m_wo_t = mx4(b, d.h, d.o_l);
+    t.m_w1 = mx4(b, d.h, d.f_l);
+    t.m_w1_t = mx4(b, d.f_l, d.h);
+    t.m_w2 = mx4(b, d.f_l, d.h);
+    t.m_w2_t = mx4(b, d.h, d.f_l);
+  } else {
+    return 0;
+  }
   if (k) *k = t;
   return b.off;
 }
@@ -497,10 +521,11 @@ mtl_status mtl_validate(const mtl_layer_cfg* c) {
   if (c->precision == MTL_PREC_FP8_HYBRID &&
       (((int64_t)c->seq * c->micro_batch) % 16 != 0 || (c->ffn / c->tp) % 16 != 0))
     return MTL_E_SHAPE;
-  if (c->flags & ~(MTL_F_RESIDUAL | MTL_F_WGRAD_ACCUM | MTL_F_FP8_KEEP_CODES | MTL_F_FP8_REUSE_WEIGHTS))
+  if (c->flags & ~(MTL_F_RESIDUAL | MTL_F_WGRAD_ACCUM | MTL_F_KEEP_CODES | MTL_F_REUSE_WEIGHTS))
     return MTL_E_UNSUPPORTED;
-  if ((c->flags & MTL_F_FP8_KEEP_CODES) && c->precision != MTL_PREC_FP8_HYBRID) return MTL_E_UNSUPPORTED;
-  if ((c->flags & MTL_F_FP8_REUSE_WEIGHTS) && !(c->flags & MTL_F_FP8_KEEP_CODES)) return MTL_E_UNSUPPORTED;
+  if ((c->flags & MTL_F_KEEP_CODES) && c->precision != MTL_PREC_FP8_HYBRID && c->precision != MTL_PREC_MXFP4)
+    return MTL_E_UNSUPPORTED;
+  if ((c->flags & MTL_F_REUSE_WEIGHTS) && !(c->flags & MTL_F_KEEP_CODES)) return MTL_E_UNSUPPORTED;
   return MTL_OK;
 }
 
@@ -539,7 +564,11 @@ mtl_status mtl_attn_fwd(const mtl_layer_cfg* c, const void* x, const void* w_qkv
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
 
   // qkv = x . w_qkv + b_qkv
-  if (is_mx4(c)) {
+  if (keeps_mx(c)) {  // x and w_qkv both ways; the backward takes the other blocking
+    MTL_TRY(mxq2(x, ws.m_x, kp.m_x_t, s));
+    if (!reuses_weights(c)) MTL_TRY(mxq2(w_qkv, kp.m_wqkv, kp.m_wqkv_t, s));
+    MTL_TRY(mxgemm("qkv_fwd", ws.m_x, kp.m_wqkv_t, EPI_BF16_BIAS, qkv, s, b_qkv));
+  } else if (is_mx4(c)) {
     MTL_TRY(mxq(x, ws.m_x, s));
     MTL_TRY(mxqt(w_qkv, ws.m_wqkv_t, s));
     MTL_TRY(mxgemm("qkv_fwd", ws.m_x, ws.m_wqkv_t, EPI_BF16_BIAS, qkv, s, b_qkv));
@@ -575,7 +604,11 @@ mtl_status mtl_attn_fwd(const mtl_layer_cfg* c, const void* x, const void* w_qkv
                       2.0 * d.S * (d.qkv_l + d.o_l) + 4.0 * d.S * d.heads_l, s, [&] { return attention_fwd(a, s); }));
 
   // partial = o . w_o
-  if (is_mx4(c)) {
+  if (keeps_mx(c)) {
+    MTL_TRY(mxq2(o, ws.m_o, kp.m_o_t, s));
+    if (!reuses_weights(c)) MTL_TRY(mxq2(w_o, kp.m_wo, kp.m_wo_t, s));
+    MTL_TRY(mxgemm("proj_fwd", ws.m_o, kp.m_wo_t, EPI_BF16, partial, s));
+  } else if (is_mx4(c)) {
     MTL_TRY(mxq(o, ws.m_o, s));
     MTL_TRY(mxqt(w_o, ws.m_wo_t, s));
     MTL_TRY(mxgemm("proj_fwd", ws.m_o, ws.m_wo_t, EPI_BF16, partial, s));
@@ -920,6 +953,15 @@ mtl_status mtl_mlp_fwd(const mtl_layer_cfg* c, const void* h, const void* w1, co
   }
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
 
+  if (keeps_mx(c)) {  // as below, keeping the other blocking of h, a and the weights for the backward
+    MTL_TRY(mxq2(h, ws.m_h, kp.m_h_t, s));
+    if (!reuses_weights(c)) MTL_TRY(mxq2(w1, kp.m_w1, kp.m_w1_t, s));
+    MTL_TRY(mxgemm("fc1_fwd", ws.m_h, kp.m_w1_t, EPI_BIAS_GELU, gz, s, b1, a));
+    MTL_TRY(mxq2(a, ws.m_a, kp.m_a_t, s));
+    if (!reuses_weights(c)) MTL_TRY(mxq2(w2, kp.m_w2, kp.m_w2_t, s));
+    MTL_TRY(mxgemm("fc2_fwd", ws.m_a, kp.m_w2_t, EPI_BF16, partial, s));
+    return MTL_OK;
+  }
   if (is_mx4(c)) {
     // z = h . w1 + b1: gz = GeLU'(z), a = GeLU(z); partial = a . w2
     MTL_TRY(mxq(h, ws.m_h, s));
@@ -991,16 +1033,22 @@ mtl_status mtl_mlp_bwd(const mtl_layer_cfg* c, const void* dy, const void* h, co
   const int wepi = accum ? EPI_F32_ACC : EPI_F32;
 
   if (is_mx4(c)) {
-    // every operand quantised along its product's contraction
+    // every operand quantised along its product's contraction (with
+    // MTL_F_KEEP_CODES the weights' and a's, h's codes come from mtl_mlp_fwd)
+    const bool kept = keeps_mx(c);
     MTL_TRY(mxq2(dy, ws.m_dy, ws.m_dy_t, s));
-    MTL_TRY(mxq(w2, ws.m_w2, s));
+    if (kept) ws.m_w2 = kp.m_w2;
+    else MTL_TRY(mxq(w2, ws.m_w2, s));
     MTL_TRY(mxgemm("fc2_dgrad", ws.m_dy, ws.m_w2, EPI_DGELU, ws.dz, s, nullptr, nullptr, gz));
-    MTL_TRY(mxqt(a, ws.m_a_t, s));
+    if (kept) ws.m_a_t = kp.m_a_t;
+    else MTL_TRY(mxqt(a, ws.m_a_t, s));
     MTL_TRY(mxgemm("fc2_wgrad", ws.m_a_t, ws.m_dy_t, wepi, dw2, s));
     MTL_TRY(mxq2(ws.dz, ws.m_dz, ws.m_dz_t, s));
-    MTL_TRY(mxq(w1, ws.m_w1, s));
+    if (kept) ws.m_w1 = kp.m_w1;
+    else MTL_TRY(mxq(w1, ws.m_w1, s));
     MTL_TRY(mxgemm("fc1_dgrad", ws.m_dz, ws.m_w1, EPI_BF16, dh_partial, s));
-    MTL_TRY(mxqt(h, ws.m_h_t, s));
+    if (kept) ws.m_h_t = kp.m_h_t;
+    else MTL_TRY(mxqt(h, ws.m_h_t, s));
     MTL_TRY(mxgemm("fc1_wgrad", ws.m_h_t, ws.m_dz_t, wepi, dw1, s));
     MTL_TRY(mlp_bias_grads(d, ws, dy, db1, db2, accum, s));
     return MTL_OK;
@@ -1072,9 +1120,11 @@ mtl_status mtl_attn_bwd(const mtl_layer_cfg* c, const void* dh, const void* x, c
 
   if (is_mx4(c)) {
     MTL_TRY(mxq2(dh, ws.m_dh, ws.m_dh_t, s));
-    MTL_TRY(mxq(w_o, ws.m_wo, s));
+    if (keeps_mx(c)) ws.m_wo = kp.m_wo;  // with o's column-blocked codes, from mtl_attn_fwd
+    else MTL_TRY(mxq(w_o, ws.m_wo, s));
     MTL_TRY(mxgemm("proj_dgrad", ws.m_dh, ws.m_wo, EPI_BF16, ws.dout, s));
-    MTL_TRY(mxqt(o, ws.m_o_t, s));
+    if (keeps_mx(c)) ws.m_o_t = kp.m_o_t;
+    else MTL_TRY(mxqt(o, ws.m_o_t, s));
     MTL_TRY(mxgemm("proj_wgrad", ws.m_o_t, ws.m_dh_t, wepi, dw_o, s));
   } else if (f8) {
     // do = dh . w_o^T ; dw_o = o^T . dh
@@ -1121,9 +1171,11 @@ mtl_status mtl_attn_bwd(const mtl_layer_cfg* c, const void* dh, const void* x, c
 
   if (is_mx4(c)) {
     MTL_TRY(mxq2(ws.dqkv, ws.m_dqkv, ws.m_dqkv_t, s));
-    MTL_TRY(mxq(w_qkv, ws.m_wqkv, s));
+    if (keeps_mx(c)) ws.m_wqkv = kp.m_wqkv;  // with x's column-blocked codes, from mtl_attn_fwd
+    else MTL_TRY(mxq(w_qkv, ws.m_wqkv, s));
     MTL_TRY(mxgemm("qkv_dgrad", ws.m_dqkv, ws.m_wqkv, EPI_BF16, dx_partial, s));
-    MTL_TRY(mxqt(x, ws.m_x_t, s));
+    if (keeps_mx(c)) ws.m_x_t = kp.m_x_t;
+    else MTL_TRY(mxqt(x, ws.m_x_t, s));
     MTL_TRY(mxgemm("qkv_wgrad", ws.m_x_t, ws.m_dqkv_t, wepi, dw_qkv, s));
     MTL_TRY(attn_bias_grads(d, ws, dh, db_qkv, db_o, accum, s));
     return MTL_OK;

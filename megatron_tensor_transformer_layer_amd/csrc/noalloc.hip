@@ -42,6 +42,9 @@ extern "C" mtl_status mtl_mlp_bwd_noalloc(const mtl_layer_cfg* c, const void* dy
                                           float* db1, float* dw2, float* db2, mtl_stream_t stream) {
   mtl_status st = mtl_validate(c);
   if (st != MTL_OK) return st;
+  // the kept codes live in the caller's scratch of the forward calls, which
+  // this entry point does not see
+  if (c->flags & MTL_F_KEEP_CODES) return MTL_E_UNSUPPORTED;
   // refused before any HIP call when the configuration needs more scratch
   if (mtl::mlp_bwd_scratch_bytes(c) > (size_t)MTL_NOALLOC_SCRATCH_BYTES) return MTL_E_WORKSPACE;
   void* ws = nullptr;

@@ -362,6 +362,9 @@ def test_noalloc_mlp_backward_host_side(mtl):
     assert call(mtl.make_cfg(768, 12, 3072, 512, 1, 5, 0)) == mtl.MTL_E_DIVISIBILITY
     # the 96-layer GPT TP=8 rank fits (35 MiB)
     assert call(mtl.make_cfg(8192, 64, 32768, 4096, 1, 8, 0)) == mtl.MTL_E_HIP
+    # kept codes would be read from a scratch the forward never wrote
+    for prec in (mtl.MTL_PREC_FP8_HYBRID, mtl.MTL_PREC_MXFP4):
+        assert call(mtl.make_cfg(1024, 8, 4096, 512, 1, 2, 0, prec, mtl.MTL_F_KEEP_CODES)) == mtl.MTL_E_UNSUPPORTED
 
 
 def test_attn_bwd_scratch_layout(mtl):
@@ -395,9 +398,11 @@ def test_fp8_gemm_validation_before_any_launch(mtl):
 
 
 def test_fp8_keep_codes_flag(mtl):
-    """MTL_F_FP8_KEEP_CODES is fp8-only, and its kept region adds the
-    transposed codes (1 byte per element) and records of x, o, h and a, and
-    both orientations of the four weights' codes, to the scratch size."""
+    """MTL_F_KEEP_CODES (earlier name MTL_F_FP8_KEEP_CODES) is for fp8 and
+    MXFP4; in fp8 its kept region adds the transposed codes (1 byte per
+    element) and records of x, o, h and a, and both orientations of the four
+    weights' codes, to the scratch size; in MXFP4 the column-blocked codes and
+    scales of x, o, h, a and both blockings of the weights."""
     base = mtl.make_cfg(768, 12, 3072, 512, 1, 2, 0, mtl.MTL_PREC_FP8_HYBRID)
     kept = mtl.make_cfg(768, 12, 3072, 512, 1, 2, 0, mtl.MTL_PREC_FP8_HYBRID, mtl.MTL_F_FP8_KEEP_CODES)
     assert mtl.mtl_validate(kept) == mtl.MTL_OK
@@ -408,6 +413,16 @@ def test_fp8_keep_codes_flag(mtl):
     assert mtl.mtl_workspace_bytes(kept) == mtl.mtl_workspace_bytes(base) + extra
     bad = mtl.make_cfg(768, 12, 3072, 512, 1, 2, 0, mtl.MTL_PREC_BF16, mtl.MTL_F_FP8_KEEP_CODES)
     assert mtl.mtl_validate(bad) == mtl.MTL_E_UNSUPPORTED
+    # MXFP4 keeps the column-blocked codes of x, o, h, a and both blockings of the weights (codes + scales in
+    # 17/32 byte per element)
+    mb = mtl.make_cfg(1024, 8, 4096, 512, 1, 2, 0, mtl.MTL_PREC_MXFP4)
+    mk = mtl.make_cfg(1024, 8, 4096, 512, 1, 2, 0, mtl.MTL_PREC_MXFP4, mtl.MTL_F_KEEP_CODES)
+    assert mtl.mtl_validate(mk) == mtl.MTL_OK
+    S, h, o_l, f_l, qkv_l = 512, 1024, 512, 2048, 1536
+    mx = lambda r, k: up(r * k // 2) + up(r * k // 32)
+    extra_mx = (mx(h, S) + mx(o_l, S) + mx(h, S) + mx(f_l, S) + 2 * (mx(h, qkv_l) + mx(o_l, h) + mx(h, f_l) +
+                                                                    mx(f_l, h)))
+    assert mtl.mtl_workspace_bytes(mk) == mtl.mtl_workspace_bytes(mb) + extra_mx
     # reusing the weights' kept codes needs the kept region, and adds no scratch
     reuse = mtl.make_cfg(768, 12, 3072, 512, 1, 2, 0, mtl.MTL_PREC_FP8_HYBRID,
                          mtl.MTL_F_FP8_KEEP_CODES | mtl.MTL_F_FP8_REUSE_WEIGHTS)

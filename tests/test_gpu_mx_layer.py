@@ -16,6 +16,7 @@
   tolerance for 4-bit training; the printed table gives max|diff|/max|ref|
   beside the recipe's.  (As for fp8, element-wise agreement with the
   quantised reference holds only up to the first requantised intermediate.)
+* MTL_F_KEEP_CODES and MTL_F_REUSE_WEIGHTS leave every output bit-identical.
 """
 import numpy as np
 import pytest
@@ -149,3 +150,60 @@ def test_mx_layer_error_is_the_recipe_error(mtl, case):
         if not np.all(np.isfinite(got[k])) or rms > 1.05 * rrms + 2e-3 * rr:
             bad.append(k)
     assert not bad, bad
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("case", list(SHAPES))
+def test_mx_kept_codes_are_bit_identical(mtl, case):
+    """With MTL_F_KEEP_CODES the MXFP4 backward takes the column-blocked codes of
+    x, o, h, a and the weights' codes that the forward wrote (each tensor
+    quantised both ways from one read) instead of quantising them again: every
+    output equals the layer without the flag bit for bit."""
+    from megatron_tensor_transformer_layer_amd.layer import run_sharded_layer
+    shape = SHAPES[case]
+    print(f"mxfp4 kept codes {case} {shape}", flush=True)
+    full = synth.layer_inputs(shape, seed=0)
+    shards = [synth.layer_inputs(shape, seed=0, tp=shape.tp, rank=r) for r in range(shape.tp)]
+    run = lambda flags: run_sharded_layer(shape, shape.tp, shards, full["x"], full["b_o"], full["b2"], full["dy"],
+                                          precision=mtl.MTL_PREC_MXFP4, flags=flags)
+    a, b = run(0), run(mtl.MTL_F_KEEP_CODES)
+    for k, v in a.items():
+        if isinstance(v, np.ndarray):
+            assert np.array_equal(v, b[k]), k
+
+
+@pytest.mark.gpu
+def test_mx_reused_weight_codes(mtl):
+    """MTL_F_REUSE_WEIGHTS in MXFP4: a rank step after a step without it gives
+    the first step's outputs bit for bit and reads no bf16 weight (overwritten
+    weights change nothing)."""
+    import torch
+    from megatron_tensor_transformer_layer_amd.layer import RankState, bf16_dev
+    shape = SHAPES["d64-tp4-mb2"]
+    t, r = shape.tp, shape.tp - 1
+    print(f"mxfp4 reused weight codes {shape}", flush=True)
+    inp = synth.layer_inputs(shape, tp=t, rank=r)
+    st = RankState(shape, t, r, inp, flags=mtl.MTL_F_KEEP_CODES, precision=mtl.MTL_PREC_MXFP4)
+    x, dy = bf16_dev(inp["x"]), bf16_dev(inp["dy"])
+    h, dh = bf16_dev(synth.layer_tensor(shape, "h")), bf16_dev(synth.layer_tensor(shape, "dh"))
+    names = ("qkv", "o", "lse", "gz", "a", "p_attn", "p_mlp", "p_dh", "p_dx", "dw_qkv", "db_qkv", "dw_o", "db_o",
+             "dw1", "db1", "dw2", "db2")
+
+    def step():
+        st.attn_fwd(x)
+        st.mlp_fwd(h)
+        st.mlp_bwd(dy, h)
+        st.attn_bwd(dh, x)
+        torch.cuda.synchronize()
+        return {k: getattr(st, k).clone() for k in names}
+
+    first = step()
+    st.cfg.flags = mtl.MTL_F_KEEP_CODES | mtl.MTL_F_REUSE_WEIGHTS
+    again = step()
+    bad = [k for k in names if not torch.equal(first[k], again[k])]
+    assert not bad, f"reused codes differ: {bad}"
+    for k in ("w_qkv", "w_o", "w1", "w2"):
+        st.w[k].mul_(-3.0)
+    ignored = step()
+    bad = [k for k in names if not torch.equal(first[k], ignored[k])]
+    assert not bad, f"bf16 weights were read: {bad}"
