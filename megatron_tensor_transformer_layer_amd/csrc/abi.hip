@@ -200,6 +200,12 @@ hipError_t gemm16_pair(const char* name, const GemmArgs& g1, GemmLayout l1, int 
                      gemm_bytes(g1.M, g1.N, g1.K, 2, ob1) + gemm_bytes(g2.M, g2.N, g2.K, 2, ob2), s,
                      [&] { return gemm_bf16_pair(g1, l1, e1, g2, l2, e2, s); });
 }
+// A timed wgrad beside a dgrad split along its contraction into fp32 parts.
+hipError_t gemm16_pair_ksplit(const char* name, const GemmArgs& gw, int ew, const GemmArgs& gd, hipStream_t s) {
+  return prof::timed(prof::GEMM, name, gemm_flop(gw.M, gw.N, gw.K) + gemm_flop(gd.M, gd.N, gd.K),
+                     gemm_bytes(gw.M, gw.N, gw.K, 2, 4) + gemm_bytes(gd.M, gd.N, gd.K, 2, 4 * gd.ksplit), s,
+                     [&] { return gemm_bf16_pair_ksplit(gw, ew, gd, s); });
+}
 // A timed fp8 wgrad/dgrad pair.
 hipError_t gemm8_pair(const char* name, const GemmArgs& gw, int ew, const GemmArgs& gd, int ed, hipStream_t s) {
   return prof::timed(prof::GEMM, name, gemm_flop(gw.M, gw.N, gw.K) + gemm_flop(gd.M, gd.N, gd.K),
@@ -279,6 +285,7 @@ struct MlpScratch {
 };
 struct AttnScratch {
   uint16_t* dout;
+  float* dout_parts;  // the two fp32 halves of dO (proj_bwd_ksplit)
   uint16_t* dqkv;
   float* delta;
   float* ws;
@@ -302,6 +309,18 @@ struct MlpFwdScratch {
 
 inline bool is_fp8(const mtl_layer_cfg* c) { return c->precision == MTL_PREC_FP8_HYBRID; }
 inline bool is_mx4(const mtl_layer_cfg* c) { return c->precision == MTL_PREC_MXFP4; }
+// The bf16 output projection's backward runs dO = dH . W_o^T in two fp32 halves
+// of its contraction (hidden) beside dW_o = O^T . dH, all on 256 x 256 tiles,
+// when the data gradient has few output tiles and twice the wgrad's contraction
+// or more (hidden >= 1.5 tokens) and the halves with the wgrad fill the chip
+// about once; the attention backward's D pass sums the halves.  Otherwise both
+// run on 128 x 128 tiles.
+inline bool proj_bwd_ksplit(const mtl_layer_cfg* c, const Dims& d) {
+  if (is_fp8(c) || is_mx4(c)) return false;
+  const int64_t td = ((d.S + 255) / 256) * ((d.o_l + 255) / 256), tw = ((d.o_l + 255) / 256) * ((d.h + 255) / 256);
+  return 2 * d.h >= 3 * d.S && td < 240 && tw + 2 * td >= 192 && tw + 2 * td <= 320;
+}
+inline int proj_bwd_kchunk(const Dims& d) { return (int)(((d.h + 1) / 2 + 63) / 64 * 64); }
 inline bool keeps_codes(const mtl_layer_cfg* c) { return is_fp8(c) && (c->flags & MTL_F_KEEP_CODES); }
 inline bool keeps_mx(const mtl_layer_cfg* c) { return is_mx4(c) && (c->flags & MTL_F_KEEP_CODES); }
 inline bool reuses_weights(const mtl_layer_cfg* c) {
@@ -394,6 +413,7 @@ size_t attn_scratch(const mtl_layer_cfg* c, const Dims& d, AttnScratch* s, char*
   Bump b{base};
   AttnScratch t{};
   t.dout = b.take<uint16_t>(d.S * d.o_l * 2);
+  t.dout_parts = proj_bwd_ksplit(c, d) ? b.take<float>(2 * d.S * d.o_l * 4) : nullptr;
   t.dqkv = b.take<uint16_t>(d.S * d.qkv_l * 2);
   t.delta = b.take<float>(d.heads_l * d.S * 4);
   t.ws = b.take<float>(colsum_ws_floats(d.S, d.qkv_l + d.h) * 4);
@@ -1137,6 +1157,14 @@ mtl_status mtl_attn_bwd(const mtl_layer_cfg* c, const void* dh, const void* x, c
     }
     MTL_TRY(gemm8_pair("proj_bwd", gemm8_args(ws.o_t, ws.o_t.qt, ws.dh, ws.dh.qt, d.o_l, d.h, d.S, dw_o, d.h), wepi,
                        gemm8_args(ws.dh, ws.dh.q, ws.wo, ws.wo.q, d.S, d.o_l, d.h, ws.dout, d.o_l), EPI_BF16, s));
+  } else if (proj_bwd_ksplit(c, d)) {
+    // dw_o = o^T . dh beside the two halves (over hidden) of do = dh . w_o^T in fp32
+    GemmArgs g = gemm(dh, d.h, w_o, d.h, d.S, d.o_l, d.h, ws.dout_parts, d.o_l);
+    g.ksplit = 2;
+    g.k_chunk = proj_bwd_kchunk(d);
+    g.split_stride_c = d.S * d.o_l;
+    GemmArgs g2 = gemm(o, d.o_l, dh, d.h, d.o_l, d.h, d.S, dw_o, d.h);
+    MTL_TRY(gemm16_pair_ksplit("proj_bwd", g2, wepi, g, s));
   } else {
     // dw_o = o^T . dh and do = dh . w_o^T, one launch (wgrad tiles first)
     GemmArgs g = gemm(dh, d.h, w_o, d.h, d.S, d.o_l, d.h, ws.dout, d.o_l);
@@ -1154,6 +1182,11 @@ mtl_status mtl_attn_bwd(const mtl_layer_cfg* c, const void* dh, const void* x, c
   at.d = (int)d.d;
   at.scale = 1.0f / sqrtf((float)d.d);
   at.dout = ws.dout;
+  if (!is_fp8(c) && !is_mx4(c) && proj_bwd_ksplit(c, d)) {  // D's pass forms dO from the halves
+    at.dout_parts = ws.dout_parts;
+    at.dout_part_stride = d.S * d.o_l;
+    at.dout_w = ws.dout;
+  }
   at.out = static_cast<const uint16_t*>(o);
   at.lse_in = lse;
   at.delta = ws.delta;

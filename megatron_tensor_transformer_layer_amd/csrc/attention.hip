@@ -39,7 +39,8 @@ __device__ __forceinline__ float xor32(float v) { return __shfl_xor(v, 32); }
 
 // ============================================================== backward: D
 // delta[n][tok] = sum_i dO[tok][n*d+i] * O[tok][n*d+i]; eight lanes per
-// (token, head) row, each taking d/8 elements in 16-byte loads.
+// (token, head) row, each taking d/8 elements in 16-byte loads.  With dO in two
+// fp32 parts, the pass first forms dO = bf16(part 0 + part 1) and stores it.
 template <int D>
 __global__ __launch_bounds__(256) void attn_delta_kernel(AttnArgs a) {
   constexpr int V = D / 64;  // 16-byte vectors per lane and tensor (1 or 2)
@@ -51,14 +52,32 @@ __global__ __launch_bounds__(256) void attn_delta_kernel(AttnArgs a) {
   const int n = ok ? (int)(row % a.heads) : 0;
   float acc = 0.f;
   if (ok) {
-    const u32x4* po = reinterpret_cast<const u32x4*>(a.out + tok * a.ld_o + (int64_t)n * D) + sub * V;
-    const u32x4* pd = reinterpret_cast<const u32x4*>(a.dout + tok * a.ld_o + (int64_t)n * D) + sub * V;
+    const int64_t e0 = tok * a.ld_o + (int64_t)n * D + sub * V * 8;  // this lane's first element
+    const u32x4* po = reinterpret_cast<const u32x4*>(a.out + e0);
     u32x4 vo[V], vd[V];
+    if (a.dout_parts) {
+      const f32x4* p0 = reinterpret_cast<const f32x4*>(a.dout_parts + e0);
+      const f32x4* p1 = reinterpret_cast<const f32x4*>(a.dout_parts + a.dout_part_stride + e0);
+      f32x4 x[2 * V], y[2 * V];
 #pragma unroll
-    for (int i = 0; i < V; ++i) {
-      vo[i] = po[i];
-      vd[i] = pd[i];
+      for (int i = 0; i < 2 * V; ++i) {
+        x[i] = p0[i];
+        y[i] = p1[i];
+      }
+#pragma unroll
+      for (int i = 0; i < V; ++i) {
+        const f32x4 s0 = x[2 * i] + y[2 * i], s1 = x[2 * i + 1] + y[2 * i + 1];
+        vd[i] = u32x4{pack_bf16x2(s0[0], s0[1]), pack_bf16x2(s0[2], s0[3]), pack_bf16x2(s1[0], s1[1]),
+                      pack_bf16x2(s1[2], s1[3])};
+        reinterpret_cast<u32x4*>(a.dout_w + e0)[i] = vd[i];
+      }
+    } else {
+      const u32x4* pd = reinterpret_cast<const u32x4*>(a.dout + e0);
+#pragma unroll
+      for (int i = 0; i < V; ++i) vd[i] = pd[i];
     }
+#pragma unroll
+    for (int i = 0; i < V; ++i) vo[i] = po[i];
 #pragma unroll
     for (int i = 0; i < V; ++i)
 #pragma unroll
@@ -384,6 +403,7 @@ static hipError_t bwd_d(const AttnArgs& a, bool with_delta, hipStream_t s) {
 
 hipError_t attention_bwd(const AttnArgs& a, hipStream_t s) {
   if (a.seq <= 0) return hipSuccess;
+  if (a.dout_parts && (!a.dout_w || a.dout != a.dout_w)) return hipErrorInvalidValue;
   if (a.d == 64) return bwd_d<64, false>(a, true, s);
   if (a.d == 128) return bwd_d<128, false>(a, true, s);
   return hipErrorInvalidValue;

@@ -463,10 +463,24 @@ __device__ __forceinline__ void gemm_tile(GemmArgs p, const int bid, LDS_AS char
   constexpr int OUT_BYTES = (EPI == EPI_F32 || EPI == EPI_F32_ACC) ? 4 : 2;
 
   int tm, tn;
+  int64_t a_skip = 0, b_skip = 0;  // elements a k-split moves a k-contiguous operand's base by
   if (p.offsets == nullptr) {
     const int tiles_m = (p.M + BM - 1) / BM, tiles_n = (p.N + BN - 1) / BN;
     const int ntiles = tiles_m * tiles_n;
-    const int t = xcd_index(bid, ntiles);
+    int t = xcd_index(bid, F8 == 0 && p.ksplit > 1 ? ntiles * p.ksplit : ntiles);
+    if constexpr (F8 == 0) {
+      if (p.ksplit > 1) {  // part t / ntiles of the contraction, into its own fp32 output
+        const int part = t / ntiles;
+        t %= ntiles;
+        const int k0 = part * p.k_chunk;
+        p.K = min(p.K - k0, p.k_chunk);
+        if (A_K) a_skip = k0;
+        p.a += A_K ? (int64_t)k0 : (int64_t)k0 * p.lda;
+        if (B_K) b_skip = k0;
+        p.b += B_K ? (int64_t)k0 : (int64_t)k0 * p.ldb;
+        p.c = reinterpret_cast<char*>(p.c) + (int64_t)part * p.split_stride_c * OUT_BYTES;
+      }
+    }
     constexpr int GM = 4;
     const int group = GM * tiles_n;
     const int first_m = (t / group) * GM;
@@ -523,9 +537,9 @@ __device__ __forceinline__ void gemm_tile(GemmArgs p, const int bid, LDS_AS char
   // Buffer resources: k-contiguous operands end after their last row (M or N),
   // mn-contiguous ones after row K, so everything past the matrix reads as 0.
   const __amdgpu_buffer_rsrc_t va = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint16_t*>(p.a), 0, (int)((A_K ? (int64_t)p.M : (int64_t)p.K) * p.lda * EB), 0x00020000);
+      const_cast<uint16_t*>(p.a), 0, (int)(((A_K ? (int64_t)p.M : (int64_t)p.K) * p.lda - a_skip) * EB), 0x00020000);
   const __amdgpu_buffer_rsrc_t vb = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint16_t*>(p.b), 0, (int)((B_K ? (int64_t)p.N : (int64_t)p.K) * p.ldb * EB), 0x00020000);
+      const_cast<uint16_t*>(p.b), 0, (int)(((B_K ? (int64_t)p.N : (int64_t)p.K) * p.ldb - b_skip) * EB), 0x00020000);
   const int nk = (p.K + KSLAB - 1) / KSLAB;
   typename ML::Offs off;
   ML::OA::offsets(p.lda, m0, off.a);
@@ -837,8 +851,10 @@ static int tile_kind(const GemmArgs& p) {
 
 template <class C1, class C2>
 static hipError_t launch_pair(const GemmArgs& p1, const GemmArgs& p2, hipStream_t s) {
-  const int64_t t1 = (int64_t)((p1.M + C1::BM - 1) / C1::BM) * ((p1.N + C1::BN - 1) / C1::BN);
-  const int64_t t2 = (int64_t)((p2.M + C2::BM - 1) / C2::BM) * ((p2.N + C2::BN - 1) / C2::BN);
+  const int64_t t1 = (int64_t)((p1.M + C1::BM - 1) / C1::BM) * ((p1.N + C1::BN - 1) / C1::BN) *
+                     (C1::F8 == 0 && p1.ksplit > 1 ? p1.ksplit : 1);
+  const int64_t t2 = (int64_t)((p2.M + C2::BM - 1) / C2::BM) * ((p2.N + C2::BN - 1) / C2::BN) *
+                     (C2::F8 == 0 && p2.ksplit > 1 ? p2.ksplit : 1);
   if (!amax_fits(p1, t1, 4) || !amax_fits(p2, t2, 4)) return hipErrorInvalidValue;
   hipLaunchKernelGGL((gemm_pair_kernel<C1, C2>), dim3((unsigned)(t1 + t2)), dim3(256), 0, s, p1, p2, (int)t1);
   return hipGetLastError();
@@ -891,6 +907,26 @@ hipError_t gemm_bf16_pair(const GemmArgs& p1, GemmLayout l1, int e1, const GemmA
   hipError_t e = gemm_bf16(p1, l1, e1, s);
   if (e != hipSuccess) return e;
   return gemm_bf16(p2, l2, e2, s);
+}
+
+// The weight gradient p1 (fp32 epilogue e1) beside the data gradient p2 cut in
+// p2.ksplit parts along its contraction, each part an fp32 output of its own
+// (the caller sums them): one launch of 256 x 256 tiles.  A data gradient with
+// few output tiles and a long contraction then fills the chip with equal tiles
+// instead of running on 128 x 128 tiles.
+hipError_t gemm_bf16_pair_ksplit(const GemmArgs& p1, int e1, const GemmArgs& p2, hipStream_t s) {
+  if (p1.offsets || p2.offsets || p1.ksplit > 1 || p2.ksplit < 2 || p2.k_chunk <= 0 || p2.k_chunk % 64 != 0 ||
+      (int64_t)p2.k_chunk * (p2.ksplit - 1) >= p2.K || (int64_t)p2.k_chunk * p2.ksplit < p2.K)
+    return hipErrorInvalidValue;
+  if (p1.M <= 0 || p1.N <= 0 || p1.K <= 0 || p2.M <= 0 || p2.N <= 0) return hipErrorInvalidValue;
+  // the 32-bit buffer offsets gemm_bf16 checks (wgrad: rows K of both operands; dgrad: M and N)
+  if (((int64_t)p1.K + 256) * p1.lda * 2 >= ((int64_t)1 << 32) || ((int64_t)p1.K + 256) * p1.ldb * 2 >= ((int64_t)1 << 32) ||
+      ((int64_t)p2.M + 256) * p2.lda * 2 >= ((int64_t)1 << 32) || ((int64_t)p2.N + 256) * p2.ldb * 2 >= ((int64_t)1 << 32))
+    return hipErrorInvalidValue;
+  using D = TileCfg<256, 256, true, true, EPI_F32>;
+  if (e1 == EPI_F32) return launch_pair<TileCfg<256, 256, false, false, EPI_F32>, D>(p1, p2, s);
+  if (e1 == EPI_F32_ACC) return launch_pair<TileCfg<256, 256, false, false, EPI_F32_ACC>, D>(p1, p2, s);
+  return hipErrorInvalidValue;
 }
 
 int64_t gemm_group_m_grid(int64_t max_rows, int groups, int N) {

@@ -62,6 +62,13 @@ struct GemmArgs {
   // bytes, K counting code bytes
   const uint8_t* mx_sa;
   const uint8_t* mx_sb;
+  // Split contraction (plain bf16 GEMMs with an fp32 epilogue, gemm_bf16_pair_ksplit):
+  // ksplit > 1 runs every tile as ksplit workgroups, part j taking k in
+  // [j*k_chunk, min(K, (j+1)*k_chunk)) and writing its own fp32 C at
+  // c + j*split_stride_c elements.  0 or 1: no split.
+  int ksplit;
+  int k_chunk;
+  int64_t split_stride_c;
 };
 
 enum GemmGroupMode : int { GROUP_M = 0, GROUP_K = 1 };
@@ -79,6 +86,8 @@ hipError_t gemm_bf16(const GemmArgs& p, GemmLayout layout, int epi, hipStream_t 
 // requirements as gemm_bf16 for each.
 hipError_t gemm_bf16_pair(const GemmArgs& p1, GemmLayout l1, int e1, const GemmArgs& p2, GemmLayout l2, int e2,
                           hipStream_t s);
+// p1 wgrad (EPI_F32 / EPI_F32_ACC) beside p2, a dgrad in p2.ksplit fp32 parts (see GemmArgs::ksplit).
+hipError_t gemm_bf16_pair_ksplit(const GemmArgs& p1, int e1, const GemmArgs& p2, hipStream_t s);
 
 // fp8 GEMM: C = (A . B^T) * (*scale_a) * (*scale_b), fp32 accumulate, with the
 // epilogues above.  A [M][K] and B [N][K] are fp8 codes (both k-contiguous; a, b
@@ -122,6 +131,13 @@ struct AttnArgs {
   uint32_t* amax_part;
   int amax_cap;
   int* amax_nparts;
+  // attention_bwd: when dout_parts is set, dO arrives as two fp32 parts (dO's
+  // layout, the second dout_part_stride floats after the first); the D pass
+  // sums them (part 0 + part 1), rounds the sum to bf16 into dout_w and forms D
+  // from that, and the backward reads dout (= dout_w).
+  const float* dout_parts;
+  int64_t dout_part_stride;
+  uint16_t* dout_w;
 };
 hipError_t attention_fwd(const AttnArgs& a, hipStream_t s);
 // Queries of a.qkv against all a.kv_seq keys of a.kv (no mask; kv_seq % 64 == 0).
