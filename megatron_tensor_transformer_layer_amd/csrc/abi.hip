@@ -180,11 +180,12 @@ inline void set_amax(GemmArgs& g, const AmaxOut& m) {
 hipError_t gemm8(const char* name, const Q8& a, const uint8_t* a_codes, const Q8& b, const uint8_t* b_codes,
                  int64_t M, int64_t N, int64_t K, void* c, int64_t ldc, int epi, hipStream_t s,
                  const void* bias = nullptr, void* c2 = nullptr, const void* aux = nullptr,
-                 const AmaxOut& amx = AmaxOut{}) {
+                 const AmaxOut& amx = AmaxOut{}, bool keep_cached = false) {
   const int out_b = (epi == EPI_F32 || epi == EPI_F32_ACC) ? 4 : (epi == EPI_BIAS_GELU ? 4 : 2);
   return prof::timed(prof::GEMM, name, gemm_flop(M, N, K), gemm_bytes(M, N, K, 1, out_b), s, [&] {
     GemmArgs g = gemm8_args(a, a_codes, b, b_codes, M, N, K, c, ldc, bias, c2, aux);
     set_amax(g, amx);
+    g.keep_cached = keep_cached;
     return gemm_fp8(g, a.fmt, b.fmt, epi, s);
   });
 }
@@ -249,8 +250,10 @@ hipError_t mxq2(const void* x, const MX4& m, const MX4& mt, hipStream_t s) {
 }
 // C [a.rows, b.rows] = A . B^T on MXFP4 codes, epilogue epi (fp32 C for the wgrad epilogues)
 hipError_t mxgemm(const char* name, const MX4& a, const MX4& b, int epi, void* c, hipStream_t s,
-                  const void* bias = nullptr, void* c2 = nullptr, const void* aux = nullptr) {
+                  const void* bias = nullptr, void* c2 = nullptr, const void* aux = nullptr,
+                  bool keep_cached = false) {
   Mxfp4GemmArgs g{};
+  g.keep_cached = keep_cached;
   g.a = a.q;
   g.sa = a.s;
   g.b = b.q;
@@ -587,19 +590,20 @@ mtl_status mtl_attn_fwd(const mtl_layer_cfg* c, const void* x, const void* w_qkv
   if (keeps_mx(c)) {  // x and w_qkv both ways; the backward takes the other blocking
     MTL_TRY(mxq2(x, ws.m_x, kp.m_x_t, s));
     if (!reuses_weights(c)) MTL_TRY(mxq2(w_qkv, kp.m_wqkv, kp.m_wqkv_t, s));
-    MTL_TRY(mxgemm("qkv_fwd", ws.m_x, kp.m_wqkv_t, EPI_BF16_BIAS, qkv, s, b_qkv));
+    MTL_TRY(mxgemm("qkv_fwd", ws.m_x, kp.m_wqkv_t, EPI_BF16_BIAS, qkv, s, b_qkv, nullptr, nullptr, true));
   } else if (is_mx4(c)) {
     MTL_TRY(mxq(x, ws.m_x, s));
     MTL_TRY(mxqt(w_qkv, ws.m_wqkv_t, s));
-    MTL_TRY(mxgemm("qkv_fwd", ws.m_x, ws.m_wqkv_t, EPI_BF16_BIAS, qkv, s, b_qkv));
+    MTL_TRY(mxgemm("qkv_fwd", ws.m_x, ws.m_wqkv_t, EPI_BF16_BIAS, qkv, s, b_qkv, nullptr, nullptr, true));
   } else if (is_fp8(c)) {
     if (reuses_weights(c)) MTL_TRY(quantize({{x, &ws.x}}, ws.amax_ws, s));
     else MTL_TRY(quantize({{x, &ws.x}, {w_qkv, &ws.wqkv_t}, {w_o, &ws.wo_t}}, ws.amax_ws, s));
     MTL_TRY(gemm8("qkv_fwd", ws.x, ws.x.q, ws.wqkv_t, ws.wqkv_t.qt, d.S, d.qkv_l, d.h, qkv, d.qkv_l, EPI_BF16_BIAS,
-                  s, b_qkv));
+                  s, b_qkv, nullptr, nullptr, AmaxOut{}, true));  // the attention reads qkv next
   } else {
     GemmArgs g = gemm(x, d.h, w_qkv, d.qkv_l, d.S, d.qkv_l, d.h, qkv, d.qkv_l);
     g.bias = static_cast<const uint16_t*>(b_qkv);
+    g.keep_cached = 1;  // the attention reads qkv next
     MTL_TRY(gemm16("qkv_fwd", g, GEMM_FWD, EPI_BF16_BIAS, 2, s));
   }
 

@@ -630,7 +630,10 @@ __device__ __forceinline__ void gemm_tile(GemmArgs p, const int bid, LDS_AS char
   // finished in registers (bias, GeLU, GeLU'), then written to the wave's own slice of
   // the (now idle) LDS stages and read back row by row, so every global store
   // is 16 bytes per lane over whole rows.  fp32 results, and the two outputs
-  // of bias + GeLU, go in passes of IPP row blocks.
+  // of bias + GeLU, go in passes of IPP row blocks.  Stores are nontemporal
+  // unless the caller keeps the output cached for the next kernel: a tile
+  // round's outputs then stream out instead of filling the L2s with dirty lines
+  // that the end of the kernel has to write back.
   __syncthreads();  // all waves are done with the last slab
   constexpr int HALF = ML::NWAVES / 2;  // waves whose staging slices lie in each stage
   constexpr int REGION = ML::STAGE / HALF;
@@ -740,11 +743,13 @@ __device__ __forceinline__ void gemm_tile(GemmArgs p, const int bid, LDS_AS char
               float* c = reinterpret_cast<float*>(p.c) + (int64_t)m * p.ldc + n;
               f32x4 o = __builtin_bit_cast(f32x4, val);
               if constexpr (EPI == EPI_F32_ACC) o += *reinterpret_cast<const f32x4*>(c);
-              *reinterpret_cast<f32x4*>(c) = o;
+              if (p.keep_cached) *reinterpret_cast<f32x4*>(c) = o;
+              else __builtin_nontemporal_store(o, reinterpret_cast<f32x4*>(c));
             } else {
               uint16_t* c = reinterpret_cast<uint16_t*>(out == 0 ? p.c : p.c2) +
                             (int64_t)m * (out == 0 ? p.ldc : p.ldc2) + n;
-              *reinterpret_cast<u32x4*>(c) = val;
+              if (p.keep_cached) *reinterpret_cast<u32x4*>(c) = val;
+              else __builtin_nontemporal_store(val, reinterpret_cast<u32x4*>(c));
               if (p.amax_part && out == p.amax_out) {
 #pragma unroll
                 for (int w = 0; w < 4; ++w) amx = max(amx, max(val[w] & 0x7fffu, (val[w] >> 16) & 0x7fffu));
@@ -1038,6 +1043,7 @@ hipError_t gemm_mxfp4_tiled(const Mxfp4GemmArgs& g, hipStream_t s) {
   p.aux = g.aux;
   p.mx_sa = g.sa;
   p.mx_sb = g.sb;
+  p.keep_cached = g.keep_cached;
   if (!g.scale_order) return g.epi == EPI_BF16 ? launch_mx<EPI_BF16, F8_MXFP4>(p, s) : hipErrorInvalidValue;
   if (g.M % 32 || g.N % 32) return hipErrorInvalidValue;
   switch (g.epi) {

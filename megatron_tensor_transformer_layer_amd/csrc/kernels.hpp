@@ -69,6 +69,9 @@ struct GemmArgs {
   int ksplit;
   int k_chunk;
   int64_t split_stride_c;
+  // 1: plain stores, the output stays in the caches for the kernel that reads
+  // it next; 0: nontemporal stores (the output streams to memory)
+  int keep_cached;
 };
 
 enum GemmGroupMode : int { GROUP_M = 0, GROUP_K = 1 };
@@ -203,6 +206,7 @@ struct Mxfp4GemmArgs {
   const uint16_t* aux;   // GeLU'(z) [M, N], row stride ldc (EPI_DGELU)
   float* c32;            // fp32 C [M, N], row stride ldc (EPI_F32, EPI_F32_ACC)
   int scale_order;       // gemm_mxfp4_tiled: 0 plain (EPI_BF16 only), 1 GEMM order (M, N % 32 == 0)
+  int keep_cached;       // as GemmArgs::keep_cached
 };
 // MXFP4 on the bf16 GEMM's pipeline (256 x 256, 256 x 192 or 128 x 128 tiles,
 // two slabs in flight), for K % 256 == 0.
