@@ -125,6 +125,31 @@ struct BwdTiles {
       dma16(rs[t], voff, 0u, lds_addr(dst + I * 1024));
     }
   }
+  // The same DMA of two tiles in a loop over block steps: PW instructions per
+  // wave; lane_off is the lane's part of the byte offset of instruction q (row
+  // and column chunk within tile t = I / PER_TILE, plus the tile's column
+  // block), the same at every step; the step adds the uniform row0 * ld[t] * 2.
+  static constexpr int PW = 2 * PER_TILE / 4;
+  static __device__ __forceinline__ uint32_t lane_off(const int64_t* ld, const int64_t* col, int q) {
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int I = wave * PW + q;
+    const int t = I / PER_TILE;
+    const int o = (I % PER_TILE) * 1024 + lane * 16;
+    const int row = o / RB;
+    const int c = ((o % RB) >> 4) ^ swz(row);
+    return (uint32_t)((row * ld[t] + col[t] + c * 8) * 2);
+  }
+  static __device__ __forceinline__ void load2(const i32x4* rs, const uint32_t (&lo)[PW], const uint32_t* step,
+                                               LDS_AS char* dst) {
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+#pragma unroll
+    for (int q = 0; q < PW; ++q) {
+      const int I = wave * PW + q;
+      const int t = I / PER_TILE;
+      dma16(rs[t], lo[q] + step[t], 0u, lds_addr(dst + I * 1024));
+    }
+  }
   // row fragment: rows row0 + l%32, 8 columns of k step ks
   static __device__ __forceinline__ u32x4 rfrag(const LDS_AS char* t, int row0, int ks, int lane) {
     const int row = row0 + (lane & 31);
@@ -199,13 +224,19 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_kernel(AttnArgs a) {
       dk[i] = f32x16{};
       dv[i] = f32x16{};
     }
+    const i32x4 rs_qo[2] = {rq, ro};
+    const int64_t ld_qo[2] = {a.ld_qkv, a.ld_o};
+    uint32_t lo_qo[T::PW];
+    {
+      const int64_t col[2] = {colq, colo};
+#pragma unroll
+      for (int q = 0; q < T::PW; ++q) lo_qo[q] = T::lane_off(ld_qo, col, q);
+    }
     for (int qb = FULL ? 0 : w; qb < nblk; ++qb) {
       const int q0 = qb * 64;
       {
-        const i32x4 rs[2] = {rq, ro};
-        const int64_t ld[2] = {a.ld_qkv, a.ld_o};
-        const int64_t col[2] = {colq, colo};
-        T::load(2, rs, ld, col, tok0 + q0, tQ);
+        const uint32_t step[2] = {(uint32_t)((tok0 + q0) * ld_qo[0] * 2), (uint32_t)((tok0 + q0) * ld_qo[1] * 2)};
+        T::load2(rs_qo, lo_qo, step, tQ);
       }
       if (tid < 128) {
         const int qq = q0 + (tid & 63);
@@ -311,13 +342,20 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_kernel(AttnArgs a) {
     f32x16 dq[DB];
 #pragma unroll
     for (int i = 0; i < DB; ++i) dq[i] = f32x16{};
+    const i32x4 rs_kv[2] = {rk, rk};
+    uint32_t lo_kv[T::PW];
+    {
+      const int64_t ld[2] = {a.ld_qkv, a.ld_qkv};
+      const int64_t col[2] = {colq + D, colq + 2 * D};
+#pragma unroll
+      for (int q = 0; q < T::PW; ++q) lo_kv[q] = T::lane_off(ld, col, q);
+    }
     for (int kb = 0; kb < (FULL ? nblk : w + 1); ++kb) {
       const int k0 = kb * 64;
       {
-        const i32x4 rs[2] = {rk, rk};
-        const int64_t ld[2] = {a.ld_qkv, a.ld_qkv};
-        const int64_t col[2] = {colq + D, colq + 2 * D};
-        T::load(2, rs, ld, col, ktok0 + k0, tK);
+        const uint32_t st = (uint32_t)((ktok0 + k0) * a.ld_qkv * 2);
+        const uint32_t step[2] = {st, st};
+        T::load2(rs_kv, lo_kv, step, tK);
       }
       wait_dma();
       __syncthreads();

@@ -65,21 +65,27 @@ struct Tiles {
   static __device__ __forceinline__ int kswz(int row) { return D == 128 ? (row & 15) : ((row >> 1) & 7); }
   static __device__ __forceinline__ int vswz(int row) { return D == 128 ? ((row & 3) << 2) : (((row >> 1) & 1) << 2); }
 
-  // DMA the K and V tiles of key blocks kb0 and kb0+1 (64 keys each) into stage st
-  static __device__ __forceinline__ void load(i32x4 rs, int64_t ld, int64_t tok0, int colq, int kb0, LDS_AS char* st,
-                                              int wave, int lane) {
+  // The lane's part of the byte offset of DMA instruction q of a wave: key row
+  // (tile >> 1) * 64 + row, column chunk c of K or V, relative to the stage's
+  // first key; it is the same for every stage.
+  static __device__ __forceinline__ uint32_t lane_off(int64_t ld, int wave, int lane, int q) {
+    const int I = wave * PER_WAVE + q;
+    const int tile = I / PER_TILE;  // 0 K even, 1 V even, 2 K odd, 3 V odd
+    const int o = (I % PER_TILE) * 1024 + lane * 16;
+    const int row = o / RB;
+    const int pc = (o % RB) >> 4;
+    const bool isv = tile & 1;
+    const int c = pc ^ (isv ? vswz(row) : kswz(row));
+    return (uint32_t)((((tile >> 1) * 64 + row) * ld + (isv ? 2 * D : D) + c * 8) * 2);
+  }
+  // DMA the K and V tiles of key blocks kb0 and kb0+1 (64 keys each) into stage
+  // st; stage_off is the byte offset of the head's column 0 in key row kb0 * 64
+  static __device__ __forceinline__ void load(i32x4 rs, const uint32_t (&lo)[PER_WAVE], uint32_t stage_off,
+                                              LDS_AS char* st, int wave) {
 #pragma unroll
     for (int q = 0; q < PER_WAVE; ++q) {
       const int I = wave * PER_WAVE + q;
-      const int tile = I / PER_TILE;  // 0 K even, 1 V even, 2 K odd, 3 V odd
-      const int o = (I % PER_TILE) * 1024 + lane * 16;
-      const int row = o / RB;
-      const int pc = (o % RB) >> 4;
-      const bool isv = tile & 1;
-      const int c = pc ^ (isv ? vswz(row) : kswz(row));
-      const int key = (kb0 + (tile >> 1)) * 64 + row;
-      const uint32_t voff = (uint32_t)(((tok0 + key) * ld + colq + (isv ? 2 * D : D) + c * 8) * 2);
-      dma16(rs, voff, 0u, lds_addr(st + I * 1024));
+      dma16(rs, lo[q] + stage_off, 0u, lds_addr(st + I * 1024));
     }
   }
   // a-operand fragment of K (rows = keys row0 + l%32, 8 dims of k step ks)
@@ -138,6 +144,11 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_kernel(AttnArgs a) {
                         : make_rsrc(a.qkv, (uint32_t)(tokens * a.ld_qkv * 2));
   const int64_t kvtok0 = FULL ? (int64_t)b * a.kv_seq : tok0;
   const int nkb_all = FULL ? a.kv_seq / 64 : nitems;
+  uint32_t lo[T::PER_WAVE];
+#pragma unroll
+  for (int q = 0; q < T::PER_WAVE; ++q) lo[q] = T::lane_off(a.ld_qkv, wave, lane, q);
+  // byte offset of the head's column 0 in key row kb * 64 (wave-uniform)
+  auto stage_off = [&](int kb) { return (uint32_t)(((kvtok0 + (int64_t)kb * 64) * a.ld_qkv + colq) * 2); };
 
   uint32_t amx = 0;  // largest bf16 magnitude of O this wave stores
   for (int side = 0; side < 2; ++side) {
@@ -219,18 +230,18 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_kernel(AttnArgs a) {
     // does this wave's key half of block kb hold a key <= its last query?
     auto active = [&](int kb) { return kb < nkb && (FULL || kb * 64 + kh * 32 <= qw + 31); };
 
-    T::load(rs, a.ld_qkv, kvtok0, colq, 0, st0, wave, lane);
+    T::load(rs, lo, stage_off(0), st0, wave);
     wait_dma();
     __syncthreads();
     for (int it = 0; it < niter; it += 2) {
       const bool more1 = it + 1 < niter;
-      if (more1) T::load(rs, a.ld_qkv, kvtok0, colq, 2 * (it + 1), st1, wave, lane);
+      if (more1) T::load(rs, lo, stage_off(2 * (it + 1)), st1, wave);
       if (active(2 * it + kpar)) block(st0, 2 * it + kpar);
       if (more1) wait_dma();
       __syncthreads();
       if (more1) {
         const bool more2 = it + 2 < niter;
-        if (more2) T::load(rs, a.ld_qkv, kvtok0, colq, 2 * (it + 2), st0, wave, lane);
+        if (more2) T::load(rs, lo, stage_off(2 * (it + 2)), st0, wave);
         if (active(2 * (it + 1) + kpar)) block(st1, 2 * (it + 1) + kpar);
         if (more2) wait_dma();
         __syncthreads();
