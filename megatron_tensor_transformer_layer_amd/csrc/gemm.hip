@@ -40,6 +40,11 @@
 //    rows/columns past M or N are never stored; chunks past K of a partial last
 //    slab (which hold the next row's values in the k-contiguous layout) are
 //    zero-filled in LDS before use.
+#include <algorithm>
+#include <queue>
+#include <utility>
+#include <vector>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -800,17 +805,124 @@ struct TileCfg {
 // finish, so the first GEMM's output stores drain under the second's main loop
 // instead of at a kernel boundary.  The weight-gradient GEMM (fp32 output,
 // twice the bytes) is always the first of the pair.
+//
+// The order in which the workgroups take the two GEMMs' tiles: nseg == 0, all of
+// GEMM 1's, then GEMM 2's; otherwise per XCD (workgroup bid runs on XCD bid % 8
+// as its slot bid / 8 of that XCD's sequence) segments of count[k] consecutive
+// slots that take the next tiles of GEMM 1 (kind 0) or GEMM 2 (kind 1).  Slot j
+// of a GEMM's tiles on XCD x is its tile 8j + x, the tile gemm_tile places on
+// that XCD, so each GEMM keeps its XCD-aware tile order.
+constexpr int PAIR_MAX_SEG = 12;
+struct PairOrder {
+  int nseg;
+  int kind[PAIR_MAX_SEG];
+  int count[PAIR_MAX_SEG];
+};
+
 template <class C1, class C2>
-__global__ __launch_bounds__(256, 1) void gemm_pair_kernel(GemmArgs p1, GemmArgs p2, int tiles1) {
+__global__ __launch_bounds__(256, 1) void gemm_pair_kernel(GemmArgs p1, GemmArgs p2, int tiles1, PairOrder ord) {
   constexpr int STAGE = C1::STAGE > C2::STAGE ? C1::STAGE : C2::STAGE;
   __shared__ __attribute__((aligned(1024))) char st0_[STAGE];
   __shared__ __attribute__((aligned(1024))) char st1_[STAGE];
-  const int bid = blockIdx.x;
-  if (bid < tiles1)
+  int bid = blockIdx.x;
+  bool first = bid < tiles1;
+  if (ord.nseg > 0) {
+    const int slot = bid >> 3;
+    int base = 0, done0 = 0, done1 = 0;
+    for (int k = 0; k < ord.nseg; ++k) {
+      if (slot < base + ord.count[k]) {
+        first = ord.kind[k] == 0;
+        bid = 8 * ((first ? done0 : done1) + slot - base) + (bid & 7);
+        break;
+      }
+      base += ord.count[k];
+      (ord.kind[k] == 0 ? done0 : done1) += ord.count[k];
+    }
+  } else if (!first) {
+    bid -= tiles1;
+  }
+  if (first)
     gemm_tile<C1::BM, C1::BN, C1::A_K, C1::B_K, C1::EPI, C1::F8>(p1, bid, (LDS_AS char*)st0_, (LDS_AS char*)st1_);
   else
-    gemm_tile<C2::BM, C2::BN, C2::A_K, C2::B_K, C2::EPI, C2::F8>(p2, bid - tiles1, (LDS_AS char*)st0_,
-                                                                 (LDS_AS char*)st1_);
+    gemm_tile<C2::BM, C2::BN, C2::A_K, C2::B_K, C2::EPI, C2::F8>(p2, bid, (LDS_AS char*)st0_, (LDS_AS char*)st1_);
+}
+
+// Makespan of one XCD's CUs taking jobs of duration w[kind] in the given order,
+// each next job going to the CU that frees first.
+static double pair_makespan(const std::vector<int>& order, const double* w, int cus) {
+  std::priority_queue<double, std::vector<double>, std::greater<double>> free_at;
+  for (int i = 0; i < cus; ++i) free_at.push(0.0);
+  double end = 0.0;
+  for (int k : order) {
+    const double t = free_at.top() + w[k];
+    free_at.pop();
+    free_at.push(t);
+    end = std::max(end, t);
+  }
+  return end;
+}
+
+// A dispatch order for n1 tiles of work w1 beside n2 tiles of work w2 (both
+// multiples of 8; the hardware hands the next workgroup to the CU that frees
+// first).  GEMM 1's tiles before GEMM 2's can leave the last round half empty
+// (e.g. 48 tiles of 4 units and 64 of 3 per XCD of 32 CUs: 13 units where 12
+// would do).  The plan dedicates c of an XCD's CUs to GEMM 1 and the others to
+// GEMM 2, with c giving the smallest makespan, and lists the starts in time
+// order; it is taken when it beats the plain order by 3% or more.
+static PairOrder plan_pair(int64_t n1, double w1, int64_t n2, double w2) {
+  PairOrder none{};
+  static int cus = [] {
+    int dev = 0, n = 0;
+    if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) !=
+                                                hipSuccess)
+      return 0;
+    return n / 8;
+  }();
+  if (cus < 2 || n1 % 8 || n2 % 8 || n1 <= 0 || n2 <= 0 || n1 + n2 > 8 * 4096) return none;
+  const int m1 = (int)(n1 / 8), m2 = (int)(n2 / 8);
+  const double w[2] = {w1, w2};
+  std::vector<int> plain(m1, 0);
+  plain.insert(plain.end(), m2, 1);
+  const double base = pair_makespan(plain, w, cus);
+  double best = base;
+  std::vector<int> best_order;
+  for (int c = 1; c < cus; ++c) {
+    // c CUs run GEMM 1's tiles, cus - c GEMM 2's; quotas as even as the counts allow
+    std::vector<int> quota(cus), kind(cus);
+    for (int i = 0; i < cus; ++i) {
+      kind[i] = i < c ? 0 : 1;
+      const int n = i < c ? m1 : m2, share = i < c ? c : cus - c, j = i < c ? i : i - c;
+      quota[i] = n / share + (j < n % share ? 1 : 0);
+    }
+    using Ev = std::pair<double, int>;
+    std::priority_queue<Ev, std::vector<Ev>, std::greater<Ev>> ev;
+    for (int i = 0; i < cus; ++i) ev.push({0.0, i});
+    std::vector<int> order;
+    while (!ev.empty()) {
+      const Ev e = ev.top();
+      ev.pop();
+      if (quota[e.second]-- <= 0) continue;
+      order.push_back(kind[e.second]);
+      ev.push({e.first + w[kind[e.second]], e.second});
+    }
+    const double t = pair_makespan(order, w, cus);
+    if (t < best) {
+      best = t;
+      best_order = order;
+    }
+  }
+  if (best_order.empty() || best > 0.97 * base) return none;
+  PairOrder o{};
+  for (size_t i = 0; i < best_order.size();) {
+    size_t j = i;
+    while (j < best_order.size() && best_order[j] == best_order[i]) ++j;
+    if (o.nseg == PAIR_MAX_SEG) return none;
+    o.kind[o.nseg] = best_order[i];
+    o.count[o.nseg] = (int)(j - i);
+    ++o.nseg;
+    i = j;
+  }
+  return o;
 }
 
 template <int BM, int BN, bool A_K, bool B_K, int EPI, int F8 = 0, int NWN = 2>
@@ -861,7 +973,13 @@ static hipError_t launch_pair(const GemmArgs& p1, const GemmArgs& p2, hipStream_
   const int64_t t2 = (int64_t)((p2.M + C2::BM - 1) / C2::BM) * ((p2.N + C2::BN - 1) / C2::BN) *
                      (C2::F8 == 0 && p2.ksplit > 1 ? p2.ksplit : 1);
   if (!amax_fits(p1, t1, 4) || !amax_fits(p2, t2, 4)) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((gemm_pair_kernel<C1, C2>), dim3((unsigned)(t1 + t2)), dim3(256), 0, s, p1, p2, (int)t1);
+  // relative work of one workgroup of each GEMM (its tile area times its contraction)
+  const auto work = [](const GemmArgs& p, int bm, int bn) {
+    const int k = p.ksplit > 1 ? p.k_chunk : p.K;
+    return (double)bm * bn * k;
+  };
+  const PairOrder ord = plan_pair(t1, work(p1, C1::BM, C1::BN), t2, work(p2, C2::BM, C2::BN));
+  hipLaunchKernelGGL((gemm_pair_kernel<C1, C2>), dim3((unsigned)(t1 + t2)), dim3(256), 0, s, p1, p2, (int)t1, ord);
   return hipGetLastError();
 }
 
