@@ -36,6 +36,7 @@ struct ReduceArgs {
 
 // T > 0: exactly T partials, whose loads are all issued before the first add;
 // T == 0: a.t partials, one at a time.  The sum is in rank order either way.
+// The partials are read once: nontemporal loads keep them out of the caches.
 template <int T>
 __global__ __launch_bounds__(256) void reduce_partials_kernel(ReduceArgs a) {
   const int64_t nvec = a.count / 8;
@@ -45,7 +46,7 @@ __global__ __launch_bounds__(256) void reduce_partials_kernel(ReduceArgs a) {
     if constexpr (T > 0) {
       u32x4 x[T];
 #pragma unroll
-      for (int i = 0; i < T; ++i) x[i] = *reinterpret_cast<const u32x4*>(a.p[i] + e);
+      for (int i = 0; i < T; ++i) x[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(a.p[i] + e));
 #pragma unroll
       for (int i = 0; i < T; ++i)
 #pragma unroll
@@ -55,7 +56,7 @@ __global__ __launch_bounds__(256) void reduce_partials_kernel(ReduceArgs a) {
         }
     } else {
       for (int i = 0; i < a.t; ++i) {
-        const u32x4 x = *reinterpret_cast<const u32x4*>(a.p[i] + e);
+        const u32x4 x = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(a.p[i] + e));
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           s[2 * j] += bf16_lo(x[j]);
@@ -126,7 +127,7 @@ __global__ __launch_bounds__(256) void allgather_rows_kernel(GatherArgs a) {
   for (int64_t v = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; v < nvec; v += (int64_t)gridDim.x * blockDim.x) {
     const int i = (int)(v / vper);
     const int64_t e = a.first[i] + (v - (int64_t)i * vper) * 8;
-    *reinterpret_cast<u32x4*>(a.out + e) = *reinterpret_cast<const u32x4*>(a.src[i] + e);
+    *reinterpret_cast<u32x4*>(a.out + e) = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(a.src[i] + e));
   }
 }
 
