@@ -60,9 +60,9 @@ __global__ __launch_bounds__(256) void attn_delta_kernel(AttnArgs a) {
       const f32x4* p1 = reinterpret_cast<const f32x4*>(a.dout_parts + a.dout_part_stride + e0);
       f32x4 x[2 * V], y[2 * V];
 #pragma unroll
-      for (int i = 0; i < 2 * V; ++i) {
-        x[i] = p0[i];
-        y[i] = p1[i];
+      for (int i = 0; i < 2 * V; ++i) {  // read once
+        x[i] = __builtin_nontemporal_load(p0 + i);
+        y[i] = __builtin_nontemporal_load(p1 + i);
       }
 #pragma unroll
       for (int i = 0; i < V; ++i) {
@@ -77,7 +77,7 @@ __global__ __launch_bounds__(256) void attn_delta_kernel(AttnArgs a) {
       for (int i = 0; i < V; ++i) vd[i] = pd[i];
     }
 #pragma unroll
-    for (int i = 0; i < V; ++i) vo[i] = po[i];
+    for (int i = 0; i < V; ++i) vo[i] = __builtin_nontemporal_load(po + i);
 #pragma unroll
     for (int i = 0; i < V; ++i)
 #pragma unroll

@@ -176,7 +176,9 @@ __device__ __forceinline__ void cast_tile(const uint16_t* __restrict__ x, int64_
 #pragma unroll
   for (int pass = 0; pass < CT_PASSES; ++pass) {
     const int64_t r = r0 + tr + pass * 32, c = c0 + tc;
-    qv[pass] = (r < rows && c < cols) ? *reinterpret_cast<const u32x4*>(x + r * cols + c) : u32x4{0, 0, 0, 0};
+    // the tensor's last read (its amax pass, if any, ran before): nontemporal
+    qv[pass] = (r < rows && c < cols) ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(x + r * cols + c))
+                                      : u32x4{0, 0, 0, 0};
   }
   float s;
   if (part) {

@@ -74,7 +74,7 @@ __global__ __launch_bounds__(256) void mxfp4_quant_kernel(const uint16_t* __rest
   // and the four lanes 4b .. 4b+3 of a group hold block b's 32 elements
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
   const bool ok = i < nchunks;  // nchunks % 4 == 0, so a group is all in or all out
-  const u32x4 v = ok ? *reinterpret_cast<const u32x4*>(x + i * 8) : u32x4{0, 0, 0, 0};
+  const u32x4 v = ok ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(x + i * 8)) : u32x4{0, 0, 0, 0};
   uint32_t mx = 0;  // largest magnitude bits: integer order is value order for finite bf16
 #pragma unroll
   for (int j = 0; j < 4; ++j) mx = max(mx, max(v[j] & 0x7fffu, (v[j] >> 16) & 0x7fffu));
@@ -151,7 +151,7 @@ __global__ __launch_bounds__(256) void mxfp4_quant_tile_kernel(const uint16_t* _
 #pragma unroll
   for (int pass = 0; pass < 4; ++pass) {  // 16 rows of 16 lanes x 16 bytes per pass
     const int r = pass * 16 + (t >> 4), ch = t & 15;
-    const u32x4 v = *reinterpret_cast<const u32x4*>(x + (r0 + r) * cols + c0 + ch * 8);
+    const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(x + (r0 + r) * cols + c0 + ch * 8));
     *reinterpret_cast<u32x4*>(tile + r * LROW + ch * 16) = v;
   }
   __syncthreads();
@@ -215,7 +215,7 @@ __global__ __launch_bounds__(256) void mxfp6_quant_kernel(const uint16_t* __rest
                                                           uint8_t* __restrict__ scales) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
   const bool ok = i < nchunks;
-  const u32x4 v = ok ? *reinterpret_cast<const u32x4*>(x + i * 8) : u32x4{0, 0, 0, 0};
+  const u32x4 v = ok ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(x + i * 8)) : u32x4{0, 0, 0, 0};
   uint32_t mx = 0;
 #pragma unroll
   for (int j = 0; j < 4; ++j) mx = max(mx, max(v[j] & 0x7fffu, (v[j] >> 16) & 0x7fffu));

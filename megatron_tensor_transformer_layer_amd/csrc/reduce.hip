@@ -188,7 +188,7 @@ __global__ __launch_bounds__(256) void colsum_stage1(ColsumArgs a) {
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
       const int64_t r = r0 + wave + 4 * i;
-      v[i] = r < r1 ? *reinterpret_cast<const u32x4*>(x + r * cols + c) : u32x4{0, 0, 0, 0};
+      v[i] = r < r1 ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(x + r * cols + c)) : u32x4{0, 0, 0, 0};
     }
 #pragma unroll
     for (int i = 0; i < PER; ++i)
