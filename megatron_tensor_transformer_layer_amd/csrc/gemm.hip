@@ -870,7 +870,24 @@ static double pair_makespan(const std::vector<int>& order, const double* w, int 
 // GEMM 2, with c giving the smallest makespan, and lists the starts in time
 // order; it is taken when it beats the plain order by 3% or more (or, for tiles
 // of unequal work, the half-and-half split when it is no slower).
+static PairOrder plan_pair_uncached(int64_t n1, double w1, int64_t n2, double w2);
+// The plan depends only on the tile counts and works: each host thread keeps
+// the last few it computed, so a step's launches do not repeat the simulation.
 static PairOrder plan_pair(int64_t n1, double w1, int64_t n2, double w2) {
+  struct Entry {
+    int64_t n1, n2;
+    double w1, w2;
+    PairOrder o;
+  };
+  thread_local std::vector<Entry> cache;
+  for (const Entry& e : cache)
+    if (e.n1 == n1 && e.n2 == n2 && e.w1 == w1 && e.w2 == w2) return e.o;
+  const PairOrder o = plan_pair_uncached(n1, w1, n2, w2);
+  if (cache.size() >= 32) cache.erase(cache.begin());
+  cache.push_back({n1, n2, w1, w2, o});
+  return o;
+}
+static PairOrder plan_pair_uncached(int64_t n1, double w1, int64_t n2, double w2) {
   PairOrder none{};
   static int cus = [] {
     int dev = 0, n = 0;
