@@ -249,9 +249,8 @@ hipError_t mxq2(const void* x, const MX4& m, const MX4& mt, hipStream_t s) {
   });
 }
 // C [a.rows, b.rows] = A . B^T on MXFP4 codes, epilogue epi (fp32 C for the wgrad epilogues)
-hipError_t mxgemm(const char* name, const MX4& a, const MX4& b, int epi, void* c, hipStream_t s,
-                  const void* bias = nullptr, void* c2 = nullptr, const void* aux = nullptr,
-                  bool keep_cached = false) {
+Mxfp4GemmArgs mx_args(const MX4& a, const MX4& b, int epi, void* c, const void* bias = nullptr, void* c2 = nullptr,
+                      const void* aux = nullptr, bool keep_cached = false) {
   Mxfp4GemmArgs g{};
   g.keep_cached = keep_cached;
   g.a = a.q;
@@ -270,10 +269,23 @@ hipError_t mxgemm(const char* name, const MX4& a, const MX4& b, int epi, void* c
   g.bias = static_cast<const uint16_t*>(bias);
   g.c2 = static_cast<uint16_t*>(c2);
   g.aux = static_cast<const uint16_t*>(aux);
-  const int out_b = f32 ? 4 : (epi == EPI_BIAS_GELU ? 4 : 2);
-  return prof::timed(prof::GEMM, name, gemm_flop(a.rows, b.rows, a.k),
-                     (a.rows + b.rows) * (a.k / 2.0 + a.k / 32.0) + (double)out_b * a.rows * b.rows, s,
+  return g;
+}
+inline double mx_gemm_bytes(const Mxfp4GemmArgs& g) {
+  const int out_b = (g.epi == EPI_F32 || g.epi == EPI_F32_ACC) ? 4 : (g.epi == EPI_BIAS_GELU ? 4 : 2);
+  return ((double)g.M + g.N) * (g.K / 2.0 + g.K / 32.0) + (double)out_b * g.M * g.N;
+}
+hipError_t mxgemm(const char* name, const MX4& a, const MX4& b, int epi, void* c, hipStream_t s,
+                  const void* bias = nullptr, void* c2 = nullptr, const void* aux = nullptr,
+                  bool keep_cached = false) {
+  const Mxfp4GemmArgs g = mx_args(a, b, epi, c, bias, c2, aux, keep_cached);
+  return prof::timed(prof::GEMM, name, gemm_flop(a.rows, b.rows, a.k), mx_gemm_bytes(g), s,
                      [&] { return gemm_mxfp4_tiled(g, s); });
+}
+// A timed MXFP4 weight-gradient / data-gradient pair (one launch where both fill the chip).
+hipError_t mxgemm_pair(const char* name, const Mxfp4GemmArgs& gw, const Mxfp4GemmArgs& gd, hipStream_t s) {
+  return prof::timed(prof::GEMM, name, gemm_flop(gw.M, gw.N, gw.K) + gemm_flop(gd.M, gd.N, gd.K),
+                     mx_gemm_bytes(gw) + mx_gemm_bytes(gd), s, [&] { return gemm_mxfp4_pair(gw, gd, s); });
 }
 
 struct MlpScratch {
@@ -1063,17 +1075,18 @@ mtl_status mtl_mlp_bwd(const mtl_layer_cfg* c, const void* dy, const void* h, co
     MTL_TRY(mxq2(dy, ws.m_dy, ws.m_dy_t, s));
     if (kept) ws.m_w2 = kp.m_w2;
     else MTL_TRY(mxq(w2, ws.m_w2, s));
-    MTL_TRY(mxgemm("fc2_dgrad", ws.m_dy, ws.m_w2, EPI_DGELU, ws.dz, s, nullptr, nullptr, gz));
+    // each wgrad with its dgrad in one launch
     if (kept) ws.m_a_t = kp.m_a_t;
     else MTL_TRY(mxqt(a, ws.m_a_t, s));
-    MTL_TRY(mxgemm("fc2_wgrad", ws.m_a_t, ws.m_dy_t, wepi, dw2, s));
+    MTL_TRY(mxgemm_pair("fc2_bwd", mx_args(ws.m_a_t, ws.m_dy_t, wepi, dw2),
+                        mx_args(ws.m_dy, ws.m_w2, EPI_DGELU, ws.dz, nullptr, nullptr, gz), s));
     MTL_TRY(mxq2(ws.dz, ws.m_dz, ws.m_dz_t, s));
     if (kept) ws.m_w1 = kp.m_w1;
     else MTL_TRY(mxq(w1, ws.m_w1, s));
-    MTL_TRY(mxgemm("fc1_dgrad", ws.m_dz, ws.m_w1, EPI_BF16, dh_partial, s));
     if (kept) ws.m_h_t = kp.m_h_t;
     else MTL_TRY(mxqt(h, ws.m_h_t, s));
-    MTL_TRY(mxgemm("fc1_wgrad", ws.m_h_t, ws.m_dz_t, wepi, dw1, s));
+    MTL_TRY(mxgemm_pair("fc1_bwd", mx_args(ws.m_h_t, ws.m_dz_t, wepi, dw1),
+                        mx_args(ws.m_dz, ws.m_w1, EPI_BF16, dh_partial), s));
     MTL_TRY(mlp_bias_grads(d, ws, dy, db1, db2, accum, s));
     return MTL_OK;
   }
@@ -1146,10 +1159,10 @@ mtl_status mtl_attn_bwd(const mtl_layer_cfg* c, const void* dh, const void* x, c
     MTL_TRY(mxq2(dh, ws.m_dh, ws.m_dh_t, s));
     if (keeps_mx(c)) ws.m_wo = kp.m_wo;  // with o's column-blocked codes, from mtl_attn_fwd
     else MTL_TRY(mxq(w_o, ws.m_wo, s));
-    MTL_TRY(mxgemm("proj_dgrad", ws.m_dh, ws.m_wo, EPI_BF16, ws.dout, s));
     if (keeps_mx(c)) ws.m_o_t = kp.m_o_t;
     else MTL_TRY(mxqt(o, ws.m_o_t, s));
-    MTL_TRY(mxgemm("proj_wgrad", ws.m_o_t, ws.m_dh_t, wepi, dw_o, s));
+    MTL_TRY(mxgemm_pair("proj_bwd", mx_args(ws.m_o_t, ws.m_dh_t, wepi, dw_o),
+                        mx_args(ws.m_dh, ws.m_wo, EPI_BF16, ws.dout), s));
   } else if (f8) {
     // do = dh . w_o^T ; dw_o = o^T . dh
     if (keeps_codes(c)) {  // o's transposed codes and w_o's codes come from mtl_attn_fwd
@@ -1210,10 +1223,10 @@ mtl_status mtl_attn_bwd(const mtl_layer_cfg* c, const void* dh, const void* x, c
     MTL_TRY(mxq2(ws.dqkv, ws.m_dqkv, ws.m_dqkv_t, s));
     if (keeps_mx(c)) ws.m_wqkv = kp.m_wqkv;  // with x's column-blocked codes, from mtl_attn_fwd
     else MTL_TRY(mxq(w_qkv, ws.m_wqkv, s));
-    MTL_TRY(mxgemm("qkv_dgrad", ws.m_dqkv, ws.m_wqkv, EPI_BF16, dx_partial, s));
     if (keeps_mx(c)) ws.m_x_t = kp.m_x_t;
     else MTL_TRY(mxqt(x, ws.m_x_t, s));
-    MTL_TRY(mxgemm("qkv_wgrad", ws.m_x_t, ws.m_dqkv_t, wepi, dw_qkv, s));
+    MTL_TRY(mxgemm_pair("qkv_bwd", mx_args(ws.m_x_t, ws.m_dqkv_t, wepi, dw_qkv),
+                        mx_args(ws.m_dqkv, ws.m_wqkv, EPI_BF16, dx_partial), s));
     MTL_TRY(attn_bias_grads(d, ws, dh, db_qkv, db_o, accum, s));
     return MTL_OK;
   }

@@ -1167,12 +1167,9 @@ static hipError_t launch_mx(const GemmArgs& p, hipStream_t s) {
   return launch_cfg<128, 128, true, true, EPI, F8>(p, s);
 }
 
-hipError_t gemm_mxfp4_tiled(const Mxfp4GemmArgs& g, hipStream_t s) {
-  if (g.M <= 0 || g.N <= 0 || g.K <= 0) return hipSuccess;
-  if (g.K % 256) return hipErrorInvalidValue;
+// The GEMM arguments of an MXFP4 product (K, lda, ldb in code bytes).
+static GemmArgs mx_gemm_args(const Mxfp4GemmArgs& g) {
   const int64_t kb = g.K / 2;  // code bytes per row
-  if (((int64_t)g.M + 256) * kb >= ((int64_t)1 << 31) || ((int64_t)g.N + 256) * kb >= ((int64_t)1 << 31))
-    return hipErrorInvalidValue;
   GemmArgs p{};
   p.a = reinterpret_cast<const uint16_t*>(g.a);
   p.b = reinterpret_cast<const uint16_t*>(g.b);
@@ -1188,6 +1185,16 @@ hipError_t gemm_mxfp4_tiled(const Mxfp4GemmArgs& g, hipStream_t s) {
   p.mx_sa = g.sa;
   p.mx_sb = g.sb;
   p.keep_cached = g.keep_cached;
+  return p;
+}
+
+hipError_t gemm_mxfp4_tiled(const Mxfp4GemmArgs& g, hipStream_t s) {
+  if (g.M <= 0 || g.N <= 0 || g.K <= 0) return hipSuccess;
+  if (g.K % 256) return hipErrorInvalidValue;
+  const int64_t kb = g.K / 2;  // code bytes per row
+  if (((int64_t)g.M + 256) * kb >= ((int64_t)1 << 31) || ((int64_t)g.N + 256) * kb >= ((int64_t)1 << 31))
+    return hipErrorInvalidValue;
+  const GemmArgs p = mx_gemm_args(g);
   if (!g.scale_order) return g.epi == EPI_BF16 ? launch_mx<EPI_BF16, F8_MXFP4>(p, s) : hipErrorInvalidValue;
   if (g.M % 32 || g.N % 32) return hipErrorInvalidValue;
   switch (g.epi) {
@@ -1199,6 +1206,31 @@ hipError_t gemm_mxfp4_tiled(const Mxfp4GemmArgs& g, hipStream_t s) {
     case EPI_F32_ACC: return launch_mx<EPI_F32_ACC, F8_MXFP4_GO>(p, s);
   }
   return hipErrorInvalidValue;
+}
+
+hipError_t gemm_mxfp4_pair(const Mxfp4GemmArgs& gw, const Mxfp4GemmArgs& gd, hipStream_t s) {
+  // both on 256 x 256 tiles, GEMM-order scales: one launch (gemm_pair_kernel)
+  const auto fused = [](const Mxfp4GemmArgs& g) {
+    return g.M > 0 && g.N > 0 && g.K > 0 && g.K % 256 == 0 && g.M % 32 == 0 && g.N % 32 == 0 && g.scale_order &&
+           (long)((g.M + 255) / 256) * ((g.N + 255) / 256) >= 240 &&
+           ((int64_t)g.M + 256) * (g.K / 2) < ((int64_t)1 << 31) && ((int64_t)g.N + 256) * (g.K / 2) < ((int64_t)1 << 31);
+  };
+  if (fused(gw) && fused(gd) && (gw.epi == EPI_F32 || gw.epi == EPI_F32_ACC) &&
+      (gd.epi == EPI_BF16 || gd.epi == EPI_DGELU)) {
+    const GemmArgs pw = mx_gemm_args(gw), pd = mx_gemm_args(gd);
+    constexpr int G = F8_MXFP4_GO;
+    if (gw.epi == EPI_F32) {
+      using W = TileCfg<256, 256, true, true, EPI_F32, G>;
+      return gd.epi == EPI_DGELU ? launch_pair<W, TileCfg<256, 256, true, true, EPI_DGELU, G>>(pw, pd, s)
+                                 : launch_pair<W, TileCfg<256, 256, true, true, EPI_BF16, G>>(pw, pd, s);
+    }
+    using W = TileCfg<256, 256, true, true, EPI_F32_ACC, G>;
+    return gd.epi == EPI_DGELU ? launch_pair<W, TileCfg<256, 256, true, true, EPI_DGELU, G>>(pw, pd, s)
+                               : launch_pair<W, TileCfg<256, 256, true, true, EPI_BF16, G>>(pw, pd, s);
+  }
+  hipError_t e = gemm_mxfp4_tiled(gd, s);
+  if (e != hipSuccess) return e;
+  return gemm_mxfp4_tiled(gw, s);
 }
 
 hipError_t gemm_mxfp6_tiled(const Mxfp4GemmArgs& g, hipStream_t s) {

@@ -211,6 +211,10 @@ struct Mxfp4GemmArgs {
 // MXFP4 on the bf16 GEMM's pipeline (256 x 256, 256 x 192 or 128 x 128 tiles,
 // two slabs in flight), for K % 256 == 0.
 hipError_t gemm_mxfp4_tiled(const Mxfp4GemmArgs& g, hipStream_t s);
+// A weight gradient gw (EPI_F32 / EPI_F32_ACC) and a data gradient gd (EPI_BF16 /
+// EPI_DGELU) on MXFP4 operands in GEMM order: one launch on 256 x 256 tiles
+// when both fill the chip, else gd then gw.
+hipError_t gemm_mxfp4_pair(const Mxfp4GemmArgs& gw, const Mxfp4GemmArgs& gd, hipStream_t s);
 // MXFP4 quantisation of x [rows, cols] down its columns (blocks of 32 rows of
 // one column): codes of x^T, [cols, rows/2] bytes, and the scales of x^T,
 // plain [cols, rows/32] or in GEMM order (rows % 256 == 0, cols % 32 == 0)
