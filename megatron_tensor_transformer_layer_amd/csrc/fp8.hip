@@ -99,10 +99,22 @@ __global__ __launch_bounds__(256) void amax_stage1_multi(QuantArgs a) {
 }
 
 // Max of the stage-1 partials over a 256-thread block, returned to every
-// thread (a fixed order is not needed: max is order independent).
+// thread (a fixed order is not needed: max is order independent).  Each
+// thread keeps 16 loads in flight: the producers leave up to a few thousand
+// partials, and one load per round trip would make every cast block wait on
+// that many L2 latencies before its first conversion.  Indices past the end
+// read the last partial again (harmless for a max), so the loads carry no
+// branch and issue back to back.
 __device__ __forceinline__ uint32_t block_max_parts(const uint32_t* __restrict__ part, int nparts) {
+  constexpr int U = 16;
   uint32_t m = 0;
-  for (int i = threadIdx.x; i < nparts; i += blockDim.x) m = max(m, part[i]);
+  for (int i0 = 0; i0 < nparts; i0 += 256 * U) {
+    uint32_t v[U];
+#pragma unroll
+    for (int k = 0; k < U; ++k) v[k] = part[min(i0 + k * 256 + (int)threadIdx.x, nparts - 1)];
+#pragma unroll
+    for (int k = 0; k < U; ++k) m = max(m, v[k]);
+  }
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, off));
   __shared__ uint32_t sh[4];
