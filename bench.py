@@ -733,7 +733,9 @@ GROUP_KERNEL = {
 
 
 def traffic_file(workload, group, precision):
-    return os.path.join(HERE, "profiles", f"gemm_{group}{'_fp8' if precision == 'fp8' else ''}_{workload}_traffic.txt")
+    # each precision has its own kernels and counters: bf16 files carry no suffix
+    return os.path.join(HERE, "profiles",
+                        f"gemm_{group}{'' if precision == 'bf16' else '_' + precision}_{workload}_traffic.txt")
 
 
 def stored_traffic(workload, group, precision):
